@@ -1,0 +1,228 @@
+"""Plain CPU oracle for the MoLE hot path (ctypes wrapper over mole_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this module; the product path never
+does.  It shares no code with the HIP library.
+
+The arithmetic lives in ``mole_oracle.c`` (fp64, plain loops, OpenMP over
+rows/tokens); this module only compiles it with gcc, loads it and marshals
+numpy arrays.  bf16 tensors are passed as ``numpy.uint16`` bit patterns.
+
+Definitions followed (MoLE article, the "ICML 2025 Spotlight | MoLE" page):
+  * inference section -- LUT[v,e,:] = FFN_e(Emb[v]) over the whole
+    vocabulary, then retrieval of each token's rows by id;
+  * training section -- all routed experts active, router on the contextual
+    hidden state: gates = softmax(W_r h) over all N experts;
+  * results section -- the table compressed to 3 bits ("e.g. NF3").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mole_oracle.c")
+_LIB = os.path.join(_HERE, "libmole_oracle.so")
+
+F32, BF16 = 0, 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile mole_oracle.c with gcc (fp64, no fast-math, OpenMP)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P, I64, I, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        sig = {
+            "oracle_max_threads": (I, []),
+            "oracle_gelu": (D, [D]),
+            "oracle_normal_ppf": (D, [D]),
+            "oracle_build_lut_rows": (I, [P, P, P, I, I64, I64, I64, I64, P, I64, P, I]),
+            "oracle_router_gates": (I, [P, P, I, I64, I64, I64, P, I]),
+            "oracle_lookup_combine": (I, [P, P, P, I, P, I, I64, I64, I64, I64, P, I]),
+            "oracle_nf3_levels": (None, [P]),
+            "oracle_nf3_midpoints": (None, [P]),
+            "oracle_f32_to_f16_rne": (ctypes.c_uint16, [ctypes.c_float]),
+            "oracle_f16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
+            "oracle_pack_nf3": (I, [P, I, I64, I64, P, P, P, I]),
+            "oracle_unpack_nf3": (I, [P, I64, I64, P]),
+            "oracle_dequant_nf3": (I, [P, P, I64, I64, P]),
+            "oracle_lookup_combine_nf3": (I, [P, P, P, I, P, P, I64, I64, I64, I64, P, I]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle takes float32 or bf16-as-uint16 arrays, got %s" % a.dtype)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError("%s failed with oracle status %d" % (what, rc))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def gelu(u: float) -> float:
+    return float(_load().oracle_gelu(float(u)))
+
+
+def normal_ppf(p: float) -> float:
+    return float(_load().oracle_normal_ppf(float(p)))
+
+
+def build_lut_rows(emb, w_up, w_down, rows=None, nthreads: int = 0) -> np.ndarray:
+    """LUT rows in fp64: out[r, e, :] = W_down[e] . GELU(W_up[e] . Emb[rows[r]]).
+
+    emb [V,D], w_up [N,F,D], w_down [N,D,F], all float32 or all bf16 (uint16).
+    """
+    V, D = emb.shape
+    N, F, D2 = w_up.shape
+    assert D2 == D and w_down.shape == (N, D, F)
+    dt = _dtype_code(emb)
+    assert _dtype_code(w_up) == dt and _dtype_code(w_down) == dt
+    rows = np.arange(V, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, N, D), dtype=np.float64)
+    rc = _load().oracle_build_lut_rows(_ptr(emb), _ptr(w_up), _ptr(w_down), dt, V, D, F, N,
+                                       _ptr(rows), rows.size, _ptr(out), nthreads)
+    _check(rc, "build_lut_rows")
+    return out
+
+
+def router_gates(h, w_r, nthreads: int = 0) -> np.ndarray:
+    """gates[t, e] = softmax_e(W_r[e] . h[t]) in fp64.  h [T,D], w_r [N,D]."""
+    T, D = h.shape
+    N, D2 = w_r.shape
+    assert D2 == D
+    dt = _dtype_code(h)
+    assert _dtype_code(w_r) == dt
+    out = np.zeros((T, N), dtype=np.float64)
+    _check(_load().oracle_router_gates(_ptr(h), _ptr(w_r), dt, T, D, N, _ptr(out), nthreads),
+           "router_gates")
+    return out
+
+
+def lookup_combine(ids, h, w_r, lut, nthreads: int = 0) -> np.ndarray:
+    """y[t, :] = sum_e gates[t, e] * lut[ids[t], e, :] in fp64.  lut [V,N,D]."""
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    T = ids.size
+    V, N, D = lut.shape
+    assert h.shape == (T, D) and w_r.shape == (N, D)
+    dt = _dtype_code(h)
+    assert _dtype_code(w_r) == dt
+    y = np.zeros((T, D), dtype=np.float64)
+    rc = _load().oracle_lookup_combine(_ptr(ids), _ptr(h), _ptr(w_r), dt, _ptr(lut),
+                                       _dtype_code(lut), T, V, D, N, _ptr(y), nthreads)
+    _check(rc, "lookup_combine")
+    return y
+
+
+def nf3_levels() -> np.ndarray:
+    out = np.zeros(8, dtype=np.float32)
+    _load().oracle_nf3_levels(_ptr(out))
+    return out
+
+
+def nf3_midpoints() -> np.ndarray:
+    out = np.zeros(7, dtype=np.float32)
+    _load().oracle_nf3_midpoints(_ptr(out))
+    return out
+
+
+def f32_to_f16_rne(x: float) -> int:
+    return int(_load().oracle_f32_to_f16_rne(float(np.float32(x))))
+
+
+def f16_to_f32(bits: int) -> float:
+    return float(_load().oracle_f16_to_f32(int(bits)))
+
+
+def pack_nf3(table, nthreads: int = 0):
+    """Encode a [..., D] table to NF3.  Returns (codes uint8 [..., 3D/8],
+    scales uint16 (fp16 bits) [..., D/64], number of saturated blocks)."""
+    D = table.shape[-1]
+    lead = table.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    t2 = np.ascontiguousarray(table.reshape(rows, D))
+    codes = np.zeros((rows, 3 * D // 8), dtype=np.uint8)
+    scales = np.zeros((rows, D // 64), dtype=np.uint16)
+    nsat = ctypes.c_int64(0)
+    rc = _load().oracle_pack_nf3(_ptr(t2), _dtype_code(t2), rows, D, _ptr(codes), _ptr(scales),
+                                 ctypes.addressof(nsat), nthreads)
+    _check(rc, "pack_nf3")
+    return codes.reshape(*lead, 3 * D // 8), scales.reshape(*lead, D // 64), int(nsat.value)
+
+
+def unpack_nf3(codes, D: int) -> np.ndarray:
+    lead = codes.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    c2 = np.ascontiguousarray(codes.reshape(rows, 3 * D // 8))
+    out = np.zeros((rows, D), dtype=np.uint8)
+    _check(_load().oracle_unpack_nf3(_ptr(c2), rows, D, _ptr(out)), "unpack_nf3")
+    return out.reshape(*lead, D)
+
+
+def dequant_nf3(codes, scales, D: int) -> np.ndarray:
+    lead = codes.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    c2 = np.ascontiguousarray(codes.reshape(rows, 3 * D // 8))
+    s2 = np.ascontiguousarray(scales.reshape(rows, D // 64))
+    out = np.zeros((rows, D), dtype=np.float64)
+    _check(_load().oracle_dequant_nf3(_ptr(c2), _ptr(s2), rows, D, _ptr(out)), "dequant_nf3")
+    return out.reshape(*lead, D)
+
+
+def lookup_combine_nf3(ids, h, w_r, codes, scales, nthreads: int = 0) -> np.ndarray:
+    """y[t, d] = sum_e gates[t, e] * level[code] * scale over the NF3 table.
+    codes [V,N,3D/8] uint8, scales [V,N,D/64] uint16 (fp16 bits)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    T = ids.size
+    V, N, CB = codes.shape
+    D = CB * 8 // 3
+    assert scales.shape == (V, N, D // 64)
+    assert h.shape == (T, D) and w_r.shape == (N, D)
+    dt = _dtype_code(h)
+    y = np.zeros((T, D), dtype=np.float64)
+    rc = _load().oracle_lookup_combine_nf3(_ptr(ids), _ptr(h), _ptr(w_r), dt, _ptr(codes),
+                                           _ptr(scales), T, V, D, N, _ptr(y), nthreads)
+    _check(rc, "lookup_combine_nf3")
+    return y
