@@ -1,0 +1,185 @@
+/*
+ * mole.h -- C ABI of libmole.so, the MI355X (gfx950) hot path of
+ * Mixture-of-Lookup-Experts (MoLE) inference.
+ *
+ * MoLE's routed experts read the token embedding instead of the previous
+ * layer's output, so before inference every expert can be run once over the
+ * whole vocabulary and replaced by a table indexed by token id; at inference
+ * each token fetches its N expert outputs by id and mixes them with the
+ * router's gates.  (MoLE article, "ICML 2025 Spotlight | MoLE" page:
+ * sections "思考" (motivation), "训练阶段" (training), "推理阶段"
+ * (inference) and "实验结果" (results, 3-bit table).)
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers are device pointers (hipMalloc / torch CUDA tensors) unless
+ *    the argument name ends in _host.  The caller owns every buffer; the
+ *    library allocates no device memory.
+ *  - Tensors are dense row-major with the shapes given below.  Element
+ *    types: dtype MOLE_F32 = IEEE binary32, MOLE_BF16 = bfloat16.  The
+ *    combine output y is always fp32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and the call returns without waiting, except where a function
+ *    says otherwise.  Inputs must stay valid until the work has run.
+ *  - Every function returns MOLE_OK (0) or a negative status; argument
+ *    errors are detected on the host before anything is enqueued.  After
+ *    MOLE_ERR_HIP, mole_last_hip_error() gives the hipError_t (per thread).
+ *  - Device pointers must be 16-byte aligned (MOLE_ERR_ALIGN otherwise).
+ *  - Token ids must lie in [0, V); the GPU entry points do not check ids
+ *    stored in device memory (an out-of-range id reads outside the table).
+ *  - Entry points hold no state between calls and may be called from
+ *    several threads; calls that write the same buffers must be ordered by
+ *    the caller.
+ */
+#ifndef MOLE_H
+#define MOLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOLE_OK 0
+#define MOLE_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MOLE_ERR_DIM (-2)         /* a size is negative, zero where it must not be, or inconsistent */
+#define MOLE_ERR_DTYPE (-3)       /* unknown dtype code */
+#define MOLE_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
+#define MOLE_ERR_WORKSPACE (-5)   /* workspace smaller than the minimum */
+#define MOLE_ERR_UNSUPPORTED (-6) /* a valid but unsupported shape (e.g. N > 256) */
+#define MOLE_ERR_HIP (-7)         /* a HIP runtime call or kernel launch failed */
+#define MOLE_ERR_ID (-8)          /* a host-side token id is outside [0, V) */
+
+#define MOLE_F32 0
+#define MOLE_BF16 1
+
+/* Static text for a status code. */
+const char* mole_status_string(int status);
+
+/* The hipError_t of the last failing HIP call on this thread (0 if none). */
+int mole_last_hip_error(void);
+
+/* ABI version of this header (increments on any signature change). */
+int mole_abi_version(void);
+
+/*
+ * Copy the 8 NF3 reconstruction levels used by the library's kernels (fp32,
+ * ascending, code c -> levels[c]) to host memory.  Host-only; no GPU call.
+ */
+int mole_nf3_levels(float* levels_host);
+
+/* ------------------------------------------------------------------------
+ * LUT reparameterisation (inference section: the embedding weight matrix is
+ * fed to every routed expert, giving the complete token-id -> expert-output
+ * table):
+ *
+ *   LUT[v][e][:] = W_down[e] . GELU(W_up[e] . Emb[v])     for all v < V, e < N
+ *
+ * with GELU(u) = u * Phi(u) (erf form) and no biases.
+ *   emb    [V][D]      w_up [N][F][D]     w_down [N][D][F]     lut [V][N][D]
+ * (w_up and w_down are stored output-major, like a linear layer's weight.)
+ * dtype MOLE_F32: everything fp32, fp32 arithmetic.
+ * dtype MOLE_BF16: bf16 inputs and output; bf16 matrix-core products with
+ *   fp32 accumulation; the hidden activation GELU(.) is rounded to bf16
+ *   between the two products; LUT rounded to bf16 (nearest even).
+ * Needs D % 8 == 0 and F % 8 == 0 for MOLE_BF16.
+ *
+ * workspace: device scratch for the bf16 hidden activations of a block of
+ * vocabulary rows (ignored for MOLE_F32, may be NULL there).  Any size at
+ * or above the minimum works; larger blocks mean fewer launches.
+ * mole_build_lut_workspace_size() returns the minimum in *min_bytes and a
+ * recommended size in *rec_bytes (either pointer may be NULL).
+ * ------------------------------------------------------------------------ */
+int mole_build_lut_workspace_size(int64_t V, int64_t D, int64_t F, int64_t N, int dtype,
+                                  size_t* min_bytes, size_t* rec_bytes);
+
+int mole_build_lut(const void* emb, const void* w_up, const void* w_down, void* lut,
+                   int64_t V, int64_t D, int64_t F, int64_t N, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Lookup-combine (inference section: each token's expert outputs are
+ * fetched by token id; training section: the router reads the contextual
+ * hidden state and every routed expert is active):
+ *
+ *   g[t][:] = softmax_e( sum_d h[t][d] * w_r[e][d] )       (all N experts)
+ *   y[t][d] = sum_e g[t][e] * LUT[ids[t]][e][d]
+ *
+ *   ids [T] int64      h [T][D]      w_r [N][D]      lut [V][N][D]
+ *   y   [T][D] fp32 (written, never read)
+ * h, w_r and lut share `dtype`.  Router dot products, softmax and the
+ * combine accumulate in fp32.  T == 0 is a no-op.  1 <= N <= 256.
+ * ------------------------------------------------------------------------ */
+int mole_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut,
+                        float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * NF3 table compression (results section: the table still works at 3 bits,
+ * e.g. NF3).  Per row r = v*N + e and block b of 64 consecutive elements:
+ *   a = max |x| (fp32);  s = fp16(min(a, 65504)) rounded to nearest even;
+ *   scales[r][b] = s (fp16 bits);
+ *   code = #{ j : x > fp32(mid[j] * s) } for the 7 midpoints of the levels
+ *          (strict: an exact tie takes the lower code); code 3 if s == 0;
+ *   code i of row r sits at bits [3i, 3i+3) of the row's little-endian bit
+ *   stream, LSB first (3D/8 bytes per row).
+ * Levels: the NormalFloat construction at 3 bits (see mole_nf3_levels).
+ *   lut [V][N][D] (dtype)   codes [V][N][3D/8] u8   scales [V][N][D/64] u16
+ * Needs D % 64 == 0.  Codes and scales are bit-exact functions of the table.
+ * ------------------------------------------------------------------------ */
+int mole_pack_nf3(const void* lut, uint8_t* codes, uint16_t* scales,
+                  int64_t V, int64_t N, int64_t D, int dtype, void* stream);
+
+/*
+ *   y[t][d] = sum_e g[t][e] * levels[code(ids[t], e, d)] * s(ids[t], e, d/64)
+ * with g as in mole_lookup_combine; codes/scales laid out as produced by
+ * mole_pack_nf3 for a table of V rows.  dtype_h is the dtype of h and w_r.
+ * Needs D % 64 == 0.
+ */
+int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
+                            const uint8_t* codes, const uint16_t* scales, float* y,
+                            int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host-resident NF3 table (inference section: after reparameterisation the
+ * table lives in lower-tier storage such as CPU memory, each token's
+ * entries are looked up there and only the retrieved vectors are loaded
+ * into GPU memory).
+ *
+ * mole_gather_nf3_host: host-only.  Deduplicates ids_host[0..T) (first
+ * occurrence order), copies the U distinct rows' codes and scales into
+ * codes_stage_host [U][N][3D/8] / scales_stage_host [U][N][D/64] and writes
+ * remap_host[t] = index of ids_host[t] among the distinct ids, so that
+ * row remap_host[t] of the staged table is row ids_host[t] of the full one.
+ * *n_unique receives U.  nthreads <= 0 picks the hardware concurrency.
+ * Returns MOLE_ERR_ID if an id is outside [0, V).
+ *
+ * mole_lookup_combine_nf3_host: gather on the calling thread as above into
+ * the pinned staging buffers (hipHostMalloc'ed, >= T rows; remap_stage_host
+ * pinned int64 [T]), then enqueue on `stream` the host->device copies of
+ * the U staged rows and the T remapped ids into codes_dev / scales_dev /
+ * remap_dev (device, >= T rows), then the NF3 combine over the staged rows.
+ * Because the staging buffers are rewritten on the host, this function
+ * first waits for `stream` to drain (hipStreamSynchronize); the rest is
+ * asynchronous.  *n_unique (may be NULL) receives U.
+ * ------------------------------------------------------------------------ */
+int mole_gather_nf3_host(const int64_t* ids_host, int64_t T, const uint8_t* codes_host,
+                         const uint16_t* scales_host, int64_t V, int64_t N, int64_t D,
+                         uint8_t* codes_stage_host, uint16_t* scales_stage_host,
+                         int64_t* remap_host, int64_t* n_unique, int nthreads);
+
+int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const void* w_r,
+                                 const uint8_t* codes_host, const uint16_t* scales_host,
+                                 uint8_t* codes_stage_host, uint16_t* scales_stage_host,
+                                 int64_t* remap_stage_host, uint8_t* codes_dev,
+                                 uint16_t* scales_dev, int64_t* remap_dev, float* y,
+                                 int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                                 int nthreads, int64_t* n_unique, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOLE_H */

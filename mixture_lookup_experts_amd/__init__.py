@@ -1,0 +1,38 @@
+"""MoLE (Mixture-of-Lookup-Experts) inference hot path for AMD MI355X.
+
+Thin Python binding over the C ABI of ``libmole.so`` (declared in
+``include/mole.h``).  Every computation runs in the library's HIP kernels;
+this module only turns torch tensors into pointers and sizes and raises
+:class:`MoleError` on a non-zero status.  torch supplies device memory and
+streams.
+
+The native library is loaded on first use; if it has not been built the
+first call raises ``MoleLibraryMissing`` (build it with
+``python -m mixture_lookup_experts_amd.build``).
+"""
+from __future__ import annotations
+
+from ._native import (  # noqa: F401
+    MOLE_BF16,
+    MOLE_F32,
+    MoleError,
+    MoleLibraryMissing,
+    library,
+    library_path,
+    mole_build_lut,
+    mole_build_lut_workspace_size,
+    mole_gather_nf3_host,
+    mole_lookup_combine,
+    mole_lookup_combine_nf3,
+    mole_lookup_combine_nf3_host,
+    mole_nf3_levels,
+    mole_pack_nf3,
+    mole_status_string,
+)
+
+__all__ = [
+    "MOLE_F32", "MOLE_BF16", "MoleError", "MoleLibraryMissing", "library", "library_path",
+    "mole_build_lut", "mole_build_lut_workspace_size", "mole_lookup_combine", "mole_pack_nf3",
+    "mole_lookup_combine_nf3", "mole_gather_nf3_host", "mole_lookup_combine_nf3_host",
+    "mole_nf3_levels", "mole_status_string",
+]

@@ -1,0 +1,232 @@
+"""ctypes marshalling for libmole.so (argument marshalling only).
+
+Each ``mole_*`` function here has the name of the C entry point it calls and
+takes torch tensors (device tensors unless the name says host).  Shapes,
+dtypes and the stream are read off the tensors; the C library validates
+sizes, pointers and alignment and every status other than MOLE_OK raises
+MoleError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "libmole.so")
+
+MOLE_F32, MOLE_BF16 = 0, 1
+_DTYPE = {torch.float32: MOLE_F32, torch.bfloat16: MOLE_BF16}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MoleError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = "%s: status %d (%s)" % (fn, status, mole_status_string(status))
+        if hip_error:
+            msg += ", hipError %d" % hip_error
+        super().__init__(msg)
+
+
+class MoleLibraryMissing(ImportError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """Load libmole.so (once).  Raises MoleLibraryMissing if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise MoleLibraryMissing(
+                "libmole.so not found at %s; build it with "
+                "`python -m mixture_lookup_experts_amd.build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        sig = {
+            "mole_status_string": (ctypes.c_char_p, [I]),
+            "mole_last_hip_error": (I, []),
+            "mole_abi_version": (I, []),
+            "mole_nf3_levels": (I, [P]),
+            "mole_build_lut_workspace_size": (I, [I64, I64, I64, I64, I, P, P]),
+            "mole_build_lut": (I, [P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
+            "mole_lookup_combine": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P]),
+            "mole_pack_nf3": (I, [P, P, P, I64, I64, I64, I, P]),
+            "mole_lookup_combine_nf3": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
+            "mole_gather_nf3_host": (I, [P, I64, P, P, I64, I64, I64, P, P, P, P, I]),
+            "mole_lookup_combine_nf3_host": (I, [P, P, P, P, P, P, P, P, P, P, P, P,
+                                                 I64, I64, I64, I64, I, I, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def mole_status_string(status: int) -> str:
+    try:
+        return library().mole_status_string(int(status)).decode()
+    except MoleLibraryMissing:
+        return "library not loaded"
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise MoleError(fn, rc, library().mole_last_hip_error() if rc == -7 else 0)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        return -1  # rejected by the library as MOLE_ERR_DTYPE
+
+
+def _need(cond: bool, what: str) -> None:
+    if not cond:
+        raise ValueError(what)
+
+
+def mole_nf3_levels() -> list:
+    out = (ctypes.c_float * 8)()
+    _check("mole_nf3_levels", library().mole_nf3_levels(ctypes.addressof(out)))
+    return list(out)
+
+
+def mole_build_lut_workspace_size(V: int, D: int, F: int, N: int, dtype=torch.bfloat16):
+    """(minimum, recommended) workspace bytes for mole_build_lut."""
+    mn, rec = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    code = _DTYPE.get(dtype, -1) if not isinstance(dtype, int) else dtype
+    _check("mole_build_lut_workspace_size",
+           library().mole_build_lut_workspace_size(V, D, F, N, code, ctypes.addressof(mn),
+                                                   ctypes.addressof(rec)))
+    return int(mn.value), int(rec.value)
+
+
+def mole_build_lut(emb, w_up, w_down, lut, workspace=None, stream=None) -> None:
+    """lut[V,N,D] = W_down[e] . GELU(W_up[e] . emb[v]) for all v, e.
+    emb [V,D], w_up [N,F,D], w_down [N,D,F]; workspace: a uint8 device tensor
+    (bf16 only; see mole_build_lut_workspace_size)."""
+    _need(emb.dim() == 2 and w_up.dim() == 3 and w_down.dim() == 3 and lut.dim() == 3,
+          "emb [V,D], w_up [N,F,D], w_down [N,D,F], lut [V,N,D]")
+    V, D = emb.shape
+    N, F, D2 = w_up.shape
+    _need(D2 == D and tuple(w_down.shape) == (N, D, F) and tuple(lut.shape) == (V, N, D),
+          "inconsistent shapes")
+    for t in (emb, w_up, w_down, lut):
+        _need(t.is_contiguous() and t.dtype == emb.dtype, "tensors must be contiguous, one dtype")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mole_build_lut", library().mole_build_lut(
+        _ptr(emb), _ptr(w_up), _ptr(w_down), _ptr(lut), V, D, F, N, _dtype(emb),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mole_lookup_combine(ids, h, w_r, lut, y, stream=None) -> None:
+    """y[t,:] = sum_e softmax(w_r . h[t])[e] * lut[ids[t], e, :] (fp32 y)."""
+    V, N, D = lut.shape
+    T = ids.numel()
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "ids [T], h [T,D], w_r [N,D], lut [V,N,D], y [T,D]")
+    _need(ids.dtype == torch.int64 and y.dtype == torch.float32, "ids int64, y float32")
+    _need(h.dtype == lut.dtype == w_r.dtype, "h, w_r and lut share one dtype")
+    for t in (ids, h, w_r, lut, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_lookup_combine", library().mole_lookup_combine(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut), _ptr(y), T, V, D, N, _dtype(lut),
+        _stream(stream)))
+
+
+def mole_pack_nf3(lut, codes, scales, stream=None) -> None:
+    """NF3-encode lut [V,N,D] into codes [V,N,3D/8] (uint8) and scales
+    [V,N,D/64] (fp16 bits, int16/uint16 tensor)."""
+    V, N, D = lut.shape
+    _need(D % 64 == 0, "D must be a multiple of 64")
+    _need(tuple(codes.shape) == (V, N, 3 * D // 8) and codes.dtype == torch.uint8, "codes [V,N,3D/8] uint8")
+    _need(tuple(scales.shape) == (V, N, D // 64) and scales.element_size() == 2, "scales [V,N,D/64] 16-bit")
+    for t in (lut, codes, scales):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_pack_nf3", library().mole_pack_nf3(
+        _ptr(lut), _ptr(codes), _ptr(scales), V, N, D, _dtype(lut), _stream(stream)))
+
+
+def mole_lookup_combine_nf3(ids, h, w_r, codes, scales, y, stream=None) -> None:
+    V, N, CB = codes.shape
+    D = CB * 8 // 3
+    T = ids.numel()
+    _need(tuple(scales.shape) == (V, N, D // 64), "scales [V,N,D/64]")
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "ids [T], h [T,D], w_r [N,D], y [T,D]")
+    _need(ids.dtype == torch.int64 and y.dtype == torch.float32 and h.dtype == w_r.dtype,
+          "ids int64, y float32, h and w_r one dtype")
+    for t in (ids, h, w_r, codes, scales, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_lookup_combine_nf3", library().mole_lookup_combine_nf3(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(codes), _ptr(scales), _ptr(y), T, V, D, N,
+        _dtype(h), _stream(stream)))
+
+
+def mole_gather_nf3_host(ids_host, codes_host, scales_host, codes_stage, scales_stage, remap,
+                         nthreads: int = 0) -> int:
+    """Host-only dedupe + gather of the requested NF3 rows; returns the number
+    of distinct ids U (rows 0..U-1 of the staging buffers are written)."""
+    V, N, CB = codes_host.shape
+    D = CB * 8 // 3
+    T = ids_host.numel()
+    for t in (ids_host, codes_host, scales_host, codes_stage, scales_stage, remap):
+        _need(t.device.type == "cpu" and t.is_contiguous(), "host tensors, contiguous")
+    _need(codes_stage.numel() >= T * N * CB and scales_stage.numel() >= T * N * (D // 64)
+          and remap.numel() >= T, "staging buffers hold at least T rows")
+    u = ctypes.c_int64(0)
+    _check("mole_gather_nf3_host", library().mole_gather_nf3_host(
+        _ptr(ids_host), T, _ptr(codes_host), _ptr(scales_host), V, N, D, _ptr(codes_stage),
+        _ptr(scales_stage), _ptr(remap), ctypes.addressof(u), nthreads))
+    return int(u.value)
+
+
+def mole_lookup_combine_nf3_host(ids_host, h, w_r, codes_host, scales_host, codes_stage,
+                                 scales_stage, remap_stage, codes_dev, scales_dev, remap_dev, y,
+                                 nthreads: int = 0, stream=None) -> int:
+    """Host-resident NF3 table: gather the requested rows on the host into
+    pinned staging, copy them to the device buffers and combine.  Returns U."""
+    V, N, CB = codes_host.shape
+    D = CB * 8 // 3
+    T = ids_host.numel()
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "h [T,D], w_r [N,D], y [T,D]")
+    _need(codes_stage.numel() >= T * N * CB and codes_dev.numel() >= T * N * CB
+          and scales_stage.numel() >= T * N * (D // 64) and scales_dev.numel() >= T * N * (D // 64)
+          and remap_stage.numel() >= T and remap_dev.numel() >= T, "staging buffers hold T rows")
+    u = ctypes.c_int64(0)
+    _check("mole_lookup_combine_nf3_host", library().mole_lookup_combine_nf3_host(
+        _ptr(ids_host), _ptr(h), _ptr(w_r), _ptr(codes_host), _ptr(scales_host),
+        _ptr(codes_stage), _ptr(scales_stage), _ptr(remap_stage), _ptr(codes_dev),
+        _ptr(scales_dev), _ptr(remap_dev), _ptr(y), T, V, D, N, _dtype(h), nthreads,
+        ctypes.addressof(u), _stream(stream)))
+    return int(u.value)

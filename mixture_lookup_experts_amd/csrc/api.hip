@@ -1,0 +1,254 @@
+// extern "C" entry points of libmole.so: argument checks on the host, then
+// kernel dispatch on the caller's stream.  Declarations and contracts are in
+// include/mole.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <thread>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/mole.h"
+#include "mole_kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t err) {
+  if (err == hipSuccess) return MOLE_OK;
+  g_last_hip_error = (int)err;
+  return MOLE_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+bool dtype_ok(int dt) { return dt == MOLE_F32 || dt == MOLE_BF16; }
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // sizes handed to kernels as int
+constexpr int64_t kMaxExperts = 64;             // combine kernels keep N gates in registers
+
+int check_combine_common(int64_t T, int64_t V, int64_t D, int64_t N) {
+  if (T < 0 || V <= 0 || D <= 0 || N <= 0) return MOLE_ERR_DIM;
+  if (D > kMaxDim || T > kMaxDim) return MOLE_ERR_DIM;
+  if (N > kMaxExperts) return MOLE_ERR_UNSUPPORTED;
+  return MOLE_OK;
+}
+
+// Deduplicate ids in first-occurrence order.  Returns MOLE_ERR_ID on a bad id.
+int dedupe(const int64_t* ids, int64_t T, int64_t V, std::vector<int64_t>& uniq, int64_t* remap) {
+  std::unordered_map<int64_t, int64_t> pos;
+  pos.reserve((size_t)T * 2 + 1);
+  uniq.clear();
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t id = ids[t];
+    if (id < 0 || id >= V) return MOLE_ERR_ID;
+    auto it = pos.find(id);
+    if (it == pos.end()) {
+      const int64_t u = (int64_t)uniq.size();
+      pos.emplace(id, u);
+      uniq.push_back(id);
+      remap[t] = u;
+    } else {
+      remap[t] = it->second;
+    }
+  }
+  return MOLE_OK;
+}
+
+void gather_rows(const std::vector<int64_t>& uniq, const uint8_t* codes, const uint16_t* scales,
+                 int64_t N, int64_t D, uint8_t* codes_out, uint16_t* scales_out, int nthreads) {
+  const size_t crow = (size_t)(N * 3 * D / 8), srow = (size_t)(N * (D / 64));
+  const int64_t U = (int64_t)uniq.size();
+  auto work = [&](int64_t lo, int64_t hi) {
+    for (int64_t u = lo; u < hi; ++u) {
+      std::memcpy(codes_out + (size_t)u * crow, codes + (size_t)uniq[u] * crow, crow);
+      std::memcpy(scales_out + (size_t)u * srow, scales + (size_t)uniq[u] * srow, srow * 2);
+    }
+  };
+  int nt = nthreads > 0 ? nthreads : (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
+  const size_t bytes = (size_t)U * (crow + 2 * srow);
+  if (bytes < ((size_t)1 << 20)) nt = 1;  // threads are not worth it below ~1 MB
+  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(U, 1));
+  if (nt <= 1) {
+    work(0, U);
+    return;
+  }
+  std::vector<std::thread> pool;
+  const int64_t per = (U + nt - 1) / nt;
+  for (int i = 0; i < nt; ++i) {
+    const int64_t lo = i * per, hi = std::min<int64_t>(U, lo + per);
+    if (lo < hi) pool.emplace_back(work, lo, hi);
+  }
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mole_status_string(int status) {
+  switch (status) {
+    case MOLE_OK: return "ok";
+    case MOLE_ERR_NULL: return "a required pointer is NULL";
+    case MOLE_ERR_DIM: return "invalid or inconsistent size";
+    case MOLE_ERR_DTYPE: return "unknown dtype";
+    case MOLE_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MOLE_ERR_WORKSPACE: return "workspace too small";
+    case MOLE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOLE_ERR_HIP: return "HIP runtime error (see mole_last_hip_error)";
+    case MOLE_ERR_ID: return "token id outside [0, V)";
+    default: return "unknown status";
+  }
+}
+
+int mole_last_hip_error(void) { return g_last_hip_error; }
+
+int mole_abi_version(void) { return 1; }
+
+int mole_nf3_levels(float* levels_host) {
+  if (!levels_host) return MOLE_ERR_NULL;
+  mole::nf3_levels_host(levels_host);
+  return MOLE_OK;
+}
+
+int mole_build_lut_workspace_size(int64_t V, int64_t D, int64_t F, int64_t N, int dtype,
+                                  size_t* min_bytes, size_t* rec_bytes) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  if (V <= 0 || D <= 0 || F <= 0 || N <= 0 || D > kMaxDim || F > kMaxDim ||
+      N * F > kMaxDim)
+    return MOLE_ERR_DIM;
+  size_t mn = 0, rec = 0;
+  if (dtype == MOLE_BF16) {
+    mn = mole::build_lut_min_workspace(D, F, N);
+    rec = mole::build_lut_rec_workspace(V, D, F, N);
+  }
+  if (min_bytes) *min_bytes = mn;
+  if (rec_bytes) *rec_bytes = rec;
+  return MOLE_OK;
+}
+
+int mole_build_lut(const void* emb, const void* w_up, const void* w_down, void* lut, int64_t V,
+                   int64_t D, int64_t F, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  if (!emb || !w_up || !w_down || !lut) return MOLE_ERR_NULL;
+  if (V <= 0 || D <= 0 || F <= 0 || N <= 0 || D > kMaxDim || F > kMaxDim ||
+      N * F > kMaxDim || V > kMaxDim)
+    return MOLE_ERR_DIM;
+  if (!aligned16(emb) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(lut)) return MOLE_ERR_ALIGN;
+  if (dtype == MOLE_F32) {
+    if (D + F > mole::kBuildF32MaxLds) return MOLE_ERR_UNSUPPORTED;
+    return hip_status(mole::launch_build_lut_f32((const float*)emb, (const float*)w_up,
+                                                 (const float*)w_down, (float*)lut, V, D, F, N,
+                                                 as_stream(stream)));
+  }
+  if (D % 8 != 0 || F % 8 != 0) return MOLE_ERR_DIM;
+  if (!workspace) return MOLE_ERR_NULL;
+  if (!aligned16(workspace)) return MOLE_ERR_ALIGN;
+  if (workspace_bytes < mole::build_lut_min_workspace(D, F, N)) return MOLE_ERR_WORKSPACE;
+  return hip_status(mole::launch_build_lut_bf16((const uint16_t*)emb, (const uint16_t*)w_up,
+                                                (const uint16_t*)w_down, (uint16_t*)lut, V, D, F, N,
+                                                workspace, workspace_bytes, as_stream(stream)));
+}
+
+int mole_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut, float* y,
+                        int64_t T, int64_t V, int64_t D, int64_t N, int dtype, void* stream) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (T == 0) return MOLE_OK;
+  if (!ids || !h || !w_r || !lut || !y) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(lut) || !aligned16(y))
+    return MOLE_ERR_ALIGN;
+  return hip_status(mole::launch_lookup_combine(ids, h, w_r, lut, y, T, D, N, dtype, true,
+                                                as_stream(stream)));
+}
+
+int mole_pack_nf3(const void* lut, uint8_t* codes, uint16_t* scales, int64_t V, int64_t N, int64_t D,
+                  int dtype, void* stream) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  if (V <= 0 || N <= 0 || D <= 0 || D > kMaxDim) return MOLE_ERR_DIM;
+  if (D % 64 != 0) return MOLE_ERR_DIM;
+  if (!lut || !codes || !scales) return MOLE_ERR_NULL;
+  if (!aligned16(lut) || !aligned16(codes) || !aligned16(scales)) return MOLE_ERR_ALIGN;
+  return hip_status(mole::launch_pack_nf3(lut, codes, scales, V * N, D, dtype, as_stream(stream)));
+}
+
+int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
+                            const uint16_t* scales, float* y, int64_t T, int64_t V, int64_t D,
+                            int64_t N, int dtype_h, void* stream) {
+  if (!dtype_ok(dtype_h)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (D % 64 != 0) return MOLE_ERR_DIM;
+  if (T == 0) return MOLE_OK;
+  if (!ids || !h || !w_r || !codes || !scales || !y) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(codes) || !aligned16(scales) ||
+      !aligned16(y))
+    return MOLE_ERR_ALIGN;
+  return hip_status(mole::launch_lookup_combine_nf3(ids, h, w_r, codes, scales, y, T, D, N, dtype_h,
+                                                    as_stream(stream)));
+}
+
+int mole_gather_nf3_host(const int64_t* ids_host, int64_t T, const uint8_t* codes_host,
+                         const uint16_t* scales_host, int64_t V, int64_t N, int64_t D,
+                         uint8_t* codes_stage_host, uint16_t* scales_stage_host, int64_t* remap_host,
+                         int64_t* n_unique, int nthreads) {
+  if (T < 0 || V <= 0 || N <= 0 || D <= 0 || D % 64 != 0) return MOLE_ERR_DIM;
+  if (T > 0 && (!ids_host || !codes_host || !scales_host || !codes_stage_host || !scales_stage_host ||
+                !remap_host))
+    return MOLE_ERR_NULL;
+  if (!n_unique) return MOLE_ERR_NULL;
+  std::vector<int64_t> uniq;
+  int rc = dedupe(ids_host, T, V, uniq, remap_host);
+  if (rc != MOLE_OK) return rc;
+  gather_rows(uniq, codes_host, scales_host, N, D, codes_stage_host, scales_stage_host, nthreads);
+  *n_unique = (int64_t)uniq.size();
+  return MOLE_OK;
+}
+
+int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const void* w_r,
+                                 const uint8_t* codes_host, const uint16_t* scales_host,
+                                 uint8_t* codes_stage_host, uint16_t* scales_stage_host,
+                                 int64_t* remap_stage_host, uint8_t* codes_dev, uint16_t* scales_dev,
+                                 int64_t* remap_dev, float* y, int64_t T, int64_t V, int64_t D,
+                                 int64_t N, int dtype_h, int nthreads, int64_t* n_unique,
+                                 void* stream) {
+  if (!dtype_ok(dtype_h)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (D % 64 != 0) return MOLE_ERR_DIM;
+  if (T == 0) {
+    if (n_unique) *n_unique = 0;
+    return MOLE_OK;
+  }
+  if (!ids_host || !h || !w_r || !codes_host || !scales_host || !codes_stage_host ||
+      !scales_stage_host || !remap_stage_host || !codes_dev || !scales_dev || !remap_dev || !y)
+    return MOLE_ERR_NULL;
+  if (!aligned16(h) || !aligned16(w_r) || !aligned16(codes_dev) || !aligned16(scales_dev) ||
+      !aligned8(remap_dev) || !aligned16(y))
+    return MOLE_ERR_ALIGN;
+  hipStream_t s = as_stream(stream);
+  rc = hip_status(hipStreamSynchronize(s));
+  if (rc != MOLE_OK) return rc;
+  int64_t U = 0;
+  rc = mole_gather_nf3_host(ids_host, T, codes_host, scales_host, V, N, D, codes_stage_host,
+                            scales_stage_host, remap_stage_host, &U, nthreads);
+  if (rc != MOLE_OK) return rc;
+  const size_t cbytes = (size_t)U * (size_t)(N * 3 * D / 8);
+  const size_t sbytes = (size_t)U * (size_t)(N * (D / 64)) * 2u;
+  rc = hip_status(hipMemcpyAsync(codes_dev, codes_stage_host, cbytes, hipMemcpyHostToDevice, s));
+  if (rc == MOLE_OK) rc = hip_status(hipMemcpyAsync(scales_dev, scales_stage_host, sbytes, hipMemcpyHostToDevice, s));
+  if (rc == MOLE_OK)
+    rc = hip_status(hipMemcpyAsync(remap_dev, remap_stage_host, (size_t)T * 8u, hipMemcpyHostToDevice, s));
+  if (rc == MOLE_OK)
+    rc = hip_status(mole::launch_lookup_combine_nf3(remap_dev, h, w_r, codes_dev, scales_dev, y, T, D,
+                                                    N, dtype_h, s));
+  if (rc == MOLE_OK && n_unique) *n_unique = U;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,406 @@
+// Lookup-combine kernels: router softmax + gather of each token's N x D
+// table slab + gate-weighted sum, for a bf16/fp32 table and for the 3-bit
+// NF3 table.  (MoLE article, inference section: retrieve each token's
+// expert outputs by token id; training section: the router reads the
+// contextual hidden state and all routed experts are active.)
+//
+// Work decomposition (one launch, no inter-block communication):
+//   * a "group" of G lanes (G a power of two) owns one token; a 256-thread
+//     block holds 256/G tokens;
+//   * router: lanes split D into 16-byte chunks, form per-expert partial
+//     dot products in fp32, reduce them across the group with a wavefront
+//     reduce-scatter (xor shuffles) plus one LDS exchange, and every lane
+//     evaluates the max-subtracted softmax redundantly;
+//   * gather/combine: lane `l` of the group streams chunks l, l+G, ... of
+//     every expert row of the token's contiguous slab LUT[id] with 16-byte
+//     loads (the first batch of slab loads is issued before the router so
+//     the two latencies overlap) and accumulates in fp32.
+#include "mole_device.hpp"
+#include "mole_kernels.hpp"
+
+namespace mole {
+
+// NF3 reconstruction levels: the NormalFloat construction at 3 bits (levels
+// Phi^-1 of evenly spaced probabilities, 4 positive, 3 negative, an exact
+// zero, normalised to [-1, 1]), rounded to fp32.  Bit patterns:
+__constant__ uint32_t kNf3LevelBits[8] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
+                                          0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
+
+// ---------------------------------------------------------------------------
+// Router: per-lane partial logits over the lane's 16-byte chunks of D.
+// ---------------------------------------------------------------------------
+template <typename T, int NP, bool VECTOR>
+__device__ __forceinline__ void router_partials(const T* __restrict__ h_row, const T* __restrict__ w_r,
+                                                int D, int N, int lig, int G, bool valid,
+                                                float* part) {
+#pragma unroll
+  for (int e = 0; e < NP; ++e) part[e] = 0.f;
+  if (!valid) return;
+  if constexpr (VECTOR) {
+    constexpr int V = Elem<T>::kVec;
+    const int C = D / V;
+    for (int r = lig; r < C; r += G) {
+      float hv[V];
+      Elem<T>::unpack(ldg16(h_row + (int64_t)r * V), hv);
+#pragma unroll
+      for (int e = 0; e < NP; ++e) {
+        if (e < N) {
+          float wv[V];
+          Elem<T>::unpack(ldg16(w_r + (int64_t)e * D + (int64_t)r * V), wv);
+#pragma unroll
+          for (int j = 0; j < V; ++j) part[e] = fmaf(hv[j], wv[j], part[e]);
+        }
+      }
+    }
+  } else {
+    for (int d = lig; d < D; d += G) {
+      const float hv = Elem<T>::load1(h_row, d);
+#pragma unroll
+      for (int e = 0; e < NP; ++e)
+        if (e < N) part[e] = fmaf(hv, Elem<T>::load1(w_r, (int64_t)e * D + d), part[e]);
+    }
+  }
+}
+
+// Reduce the partial logits of a token group and turn them into softmax
+// gates held (identically) by every lane of the group.  Must be reached by
+// every thread of the block (it contains a barrier).
+template <int NP, int G>
+__device__ __forceinline__ void group_gates(float* part, float* gate, int N, int lig,
+                                            float* red /* [WG][NP] of this group */) {
+  constexpr int W = G < kWave ? G : kWave;
+  constexpr int WG = G > kWave ? G / kWave : 1;
+  using RS = ReduceScatter<NP, W>;
+  const int lane_w = lig % W, wig = lig / W;
+  RS::run(part, lane_w);
+  constexpr int kWriters = NP < W ? NP : W;
+  if (lane_w < kWriters) {
+    const int off = RS::offset(lane_w);
+#pragma unroll
+    for (int i = 0; i < RS::kLeft; ++i) red[wig * NP + off + i] = part[i];
+  }
+  __syncthreads();
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    float z = 0.f;
+#pragma unroll
+    for (int w = 0; w < WG; ++w) z += red[w * NP + e];
+    gate[e] = z;
+    if (e < N) zmax = fmaxf(zmax, z);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    const float p = (e < N) ? expf(gate[e] - zmax) : 0.f;
+    gate[e] = p;
+    sum += p;
+  }
+  const float inv = 1.f / sum;
+#pragma unroll
+  for (int e = 0; e < NP; ++e) gate[e] *= inv;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 / fp32 table
+// ---------------------------------------------------------------------------
+template <typename T, int NP, int G, bool VECTOR>
+__global__ __launch_bounds__(256) void lookup_combine_kernel(
+    const int64_t* __restrict__ ids, const T* __restrict__ h, const T* __restrict__ w_r,
+    const T* __restrict__ lut, float* __restrict__ y, int64_t T_, int D, int N) {
+  constexpr int WG = G > kWave ? G / kWave : 1;
+  constexpr int TPB = 256 / G;
+  constexpr int CH = VECTOR ? Elem<T>::kVec : 1;  // elements per chunk
+  constexpr int EC = NP < 16 ? NP : 16;           // experts per batch of slab loads
+  __shared__ float red[TPB * WG * NP];
+
+  const int tid = threadIdx.x;
+  const int grp = tid / G, lig = tid % G;
+  const int64_t t = (int64_t)blockIdx.x * TPB + grp;
+  const bool valid = t < T_;
+  const int64_t tt = valid ? t : 0;
+  const int C = D / CH;
+  const int64_t id = valid ? ids[tt] : 0;
+  const T* slab = lut + id * (int64_t)N * D;
+
+  // First batch of slab loads (chunk lig, experts 0..EC-1), before the router.
+  uint4 sv[EC];
+  float sf[EC];
+  const bool have0 = valid && lig < C;
+  if (have0) {
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      if (e < N) {
+        if constexpr (VECTOR) sv[e] = ldg16(slab + (int64_t)e * D + (int64_t)lig * CH);
+        else sf[e] = Elem<T>::load1(slab, (int64_t)e * D + lig);
+      }
+    }
+  }
+
+  float part[NP];
+  router_partials<T, NP, VECTOR>(h + tt * D, w_r, D, N, lig, G, valid, part);
+  float gate[NP];
+  group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+  if (!valid) return;
+
+  for (int k = 0; k * G + lig < C; ++k) {
+    const int c = k * G + lig;
+    float acc[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int e0 = 0; e0 < NP; e0 += EC) {
+      if (k != 0 || e0 != 0) {
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {
+          if (e0 + e < N) {
+            if constexpr (VECTOR) sv[e] = ldg16(slab + (int64_t)(e0 + e) * D + (int64_t)c * CH);
+            else sf[e] = Elem<T>::load1(slab, (int64_t)(e0 + e) * D + c);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        if (e0 + e < N) {
+          const float g = gate[e0 + e];
+          if constexpr (VECTOR) {
+            float v[CH];
+            Elem<T>::unpack(sv[e], v);
+#pragma unroll
+            for (int j = 0; j < CH; ++j) acc[j] = fmaf(g, v[j], acc[j]);
+          } else {
+            acc[0] = fmaf(g, sf[e], acc[0]);
+          }
+        }
+      }
+    }
+    float* yo = y + tt * D + (int64_t)c * CH;
+    if constexpr (VECTOR) {
+#pragma unroll
+      for (int j = 0; j < CH; j += 4)
+        *reinterpret_cast<float4*>(yo + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+    } else {
+      yo[0] = acc[0];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NF3 table: 32 codes (12 bytes) per chunk, one fp16 scale per 64 elements.
+// ---------------------------------------------------------------------------
+template <typename TH, int NP, int G>
+__global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
+    const int64_t* __restrict__ ids, const TH* __restrict__ h, const TH* __restrict__ w_r,
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    float* __restrict__ y, int64_t T_, int D, int N) {
+  constexpr int WG = G > kWave ? G / kWave : 1;
+  constexpr int TPB = 256 / G;
+  constexpr int EC = NP < 8 ? NP : 8;
+  __shared__ float red[TPB * WG * NP];
+  __shared__ float lv[8];
+
+  const int tid = threadIdx.x;
+  if (tid < 8) lv[tid] = __uint_as_float(kNf3LevelBits[tid]);
+  const int grp = tid / G, lig = tid % G;
+  const int64_t t = (int64_t)blockIdx.x * TPB + grp;
+  const bool valid = t < T_;
+  const int64_t tt = valid ? t : 0;
+  const int C = D / 32;                     // 32-element chunks per row
+  const int64_t row_bytes = 3 * (int64_t)D / 8, nblk = D / 64;
+  const int64_t id = valid ? ids[tt] : 0;
+  const uint8_t* crow0 = codes + id * (int64_t)N * row_bytes;
+  const uint16_t* srow0 = scales + id * (int64_t)N * nblk;
+
+  uint3 cw[EC];
+  uint32_t sc[EC];
+  const bool have0 = valid && lig < C;
+  if (have0) {
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      if (e < N) {
+        cw[e] = *reinterpret_cast<const uint3*>(crow0 + (int64_t)e * row_bytes + (int64_t)lig * 12);
+        sc[e] = srow0[(int64_t)e * nblk + (lig >> 1)];
+      }
+    }
+  }
+
+  float part[NP];
+  router_partials<TH, NP, true>(h + tt * D, w_r, D, N, lig, G, valid, part);
+  float gate[NP];
+  group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+  if (!valid) return;
+
+  for (int k = 0; k * G + lig < C; ++k) {
+    const int c = k * G + lig;
+    float acc[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int e0 = 0; e0 < NP; e0 += EC) {
+      if (k != 0 || e0 != 0) {
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {
+          if (e0 + e < N) {
+            cw[e] = *reinterpret_cast<const uint3*>(crow0 + (int64_t)(e0 + e) * row_bytes +
+                                                    (int64_t)c * 12);
+            sc[e] = srow0[(int64_t)(e0 + e) * nblk + (c >> 1)];
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        if (e0 + e < N) {
+          const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[e]);
+          const float ws = gate[e0 + e] * s;
+          const uint32_t w[3] = {cw[e].x, cw[e].y, cw[e].z};
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const int pos = 3 * i, wd = pos >> 5, off = pos & 31;
+            uint32_t code;
+            if (off <= 29) code = (w[wd] >> off) & 7u;
+            else code = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off) & 7u;
+            acc[i] = fmaf(ws, lv[code], acc[i]);
+          }
+        }
+      }
+    }
+    float* yo = y + tt * D + (int64_t)c * 32;
+#pragma unroll
+    for (int j = 0; j < 32; j += 4)
+      *reinterpret_cast<float4*>(yo + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+static int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Lanes per token: the power of two in [lo, 256] that wastes the fewest
+// lanes over the row's C chunks (ties: the larger group).
+static int pick_group(int C, int lo, int hi) {
+  int best = hi, best_waste = 1 << 30;
+  for (int G = hi; G >= lo; G >>= 1) {
+    const int cpl = (C + G - 1) / G;
+    const int waste = G * cpl - C;
+    if (waste < best_waste) { best_waste = waste; best = G; }
+  }
+  return best;
+}
+
+template <typename E, int NP, int G, bool VEC>
+static hipError_t launch_dense(const int64_t* ids, const void* h, const void* w_r, const void* lut,
+                               float* y, int64_t T, int D, int N, hipStream_t s) {
+  constexpr int TPB = 256 / G;
+  const int64_t blocks = (T + TPB - 1) / TPB;
+  hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N);
+  return hipGetLastError();
+}
+
+template <typename E, int NP, bool VEC>
+static hipError_t dispatch_dense_g(int G, const int64_t* ids, const void* h, const void* w_r,
+                                   const void* lut, float* y, int64_t T, int D, int N, hipStream_t s) {
+  switch (G) {
+    case 16: return launch_dense<E, NP, 16, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    case 32: return launch_dense<E, NP, 32, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    case 64: return launch_dense<E, NP, 64, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    case 128: return launch_dense<E, NP, 128, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    default: return launch_dense<E, NP, 256, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+  }
+}
+
+template <typename E, bool VEC>
+static hipError_t dispatch_dense_np(int NP, int G, const int64_t* ids, const void* h, const void* w_r,
+                                    const void* lut, float* y, int64_t T, int D, int N, hipStream_t s) {
+  switch (NP) {
+    case 1: return dispatch_dense_g<E, 1, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 2: return dispatch_dense_g<E, 2, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 4: return dispatch_dense_g<E, 4, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 8: return dispatch_dense_g<E, 8, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 16: return dispatch_dense_g<E, 16, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 32: return dispatch_dense_g<E, 32, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    default: return dispatch_dense_g<E, 64, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+  }
+}
+
+hipError_t launch_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut,
+                                 float* y, int64_t T, int64_t D, int64_t N, int dtype, bool vector_ok,
+                                 hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int NP = next_pow2((int)N);
+  const int elem_bytes = dtype == kF32 ? 4 : 2;
+  const int vec = 16 / elem_bytes;
+  const bool vector = vector_ok && (D % vec == 0);
+  const int C = vector ? (int)(D / vec) : (int)D;
+  const int G = pick_group(C, 16, 256);
+  if (dtype == kF32)
+    return vector ? dispatch_dense_np<float, true>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s)
+                  : dispatch_dense_np<float, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s);
+  return vector ? dispatch_dense_np<uint16_t, true>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s)
+                : dispatch_dense_np<uint16_t, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s);
+}
+
+template <typename TH, int NP, int G>
+static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
+                             const uint16_t* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
+  constexpr int TPB = 256 / G;
+  const int64_t blocks = (T + TPB - 1) / TPB;
+  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, G>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N);
+  return hipGetLastError();
+}
+
+template <typename TH, int NP>
+static hipError_t dispatch_nf3_g(int G, const int64_t* ids, const void* h, const void* w_r,
+                                 const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                 int D, int N, hipStream_t s) {
+  switch (G) {
+    case 8: return launch_nf3<TH, NP, 8>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 16: return launch_nf3<TH, NP, 16>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 32: return launch_nf3<TH, NP, 32>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    default: return launch_nf3<TH, NP, 64>(ids, h, w_r, codes, scales, y, T, D, N, s);
+  }
+}
+
+template <typename TH>
+static hipError_t dispatch_nf3_np(int NP, int G, const int64_t* ids, const void* h, const void* w_r,
+                                  const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                  int D, int N, hipStream_t s) {
+  switch (NP) {
+    case 1: return dispatch_nf3_g<TH, 1>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 2: return dispatch_nf3_g<TH, 2>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 4: return dispatch_nf3_g<TH, 4>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 8: return dispatch_nf3_g<TH, 8>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 16: return dispatch_nf3_g<TH, 16>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 32: return dispatch_nf3_g<TH, 32>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
+    default: return dispatch_nf3_g<TH, 64>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
+  }
+}
+
+hipError_t launch_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
+                                     const uint8_t* codes, const uint16_t* scales, float* y,
+                                     int64_t T, int64_t D, int64_t N, int dtype_h, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int NP = next_pow2((int)N);
+  const int G = pick_group((int)(D / 32), 8, 64);
+  if (dtype_h == kF32)
+    return dispatch_nf3_np<float>(NP, G, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
+  return dispatch_nf3_np<uint16_t>(NP, G, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
+}
+
+void nf3_levels_host(float* out) {
+  static const uint32_t bits[8] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
+                                   0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
+  for (int i = 0; i < 8; ++i) {
+    union { uint32_t u; float f; } cv;
+    cv.u = bits[i];
+    out[i] = cv.f;
+  }
+}
+
+}  // namespace mole

@@ -1,0 +1,87 @@
+// Device-side helpers shared by the libmole kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mole {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ---- bf16 <-> fp32 -----------------------------------------------------------
+// bf16 is the upper half of an fp32 bit pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---- element access for the two storage types ---------------------------------
+// A "chunk" is 16 bytes of a row: 8 bf16 or 4 fp32 values.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ __forceinline__ static float load1(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void unpack(const uint4& q, float* out) {
+    out[0] = __uint_as_float(q.x); out[1] = __uint_as_float(q.y);
+    out[2] = __uint_as_float(q.z); out[3] = __uint_as_float(q.w);
+  }
+};
+template <> struct Elem<uint16_t> {  // bf16 bit patterns
+  static constexpr int kVec = 8;
+  __device__ __forceinline__ static float load1(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void unpack(const uint4& q, float* out) {
+    out[0] = bf16_lo(q.x); out[1] = bf16_hi(q.x); out[2] = bf16_lo(q.y); out[3] = bf16_hi(q.y);
+    out[4] = bf16_lo(q.z); out[5] = bf16_hi(q.z); out[6] = bf16_lo(q.w); out[7] = bf16_hi(q.w);
+  }
+};
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---- cross-lane reductions ----------------------------------------------------
+// Reduce-scatter of NP per-lane partial sums over the W lanes (W a power of
+// two, W <= 64) of a lane group: at the step with xor-mask m the lane keeps
+// one half of its vector (the upper half when bit m of its lane id is set)
+// and adds the partner's copy of that half.  After min(log2 NP, log2 W)
+// steps each lane holds CNT = NP / min(NP, W) sums, for experts
+// offset(lane) + i, i < CNT; the remaining masks (if W > NP) finish the sum.
+template <int NP, int W, int M = 1, int CNT = NP>
+struct ReduceScatter {
+  __device__ __forceinline__ static void run(float* v, int lane) {
+    if constexpr (M < W) {
+      if constexpr (CNT > 1) {
+        constexpr int H = CNT / 2;
+        const bool hi = (lane & M) != 0;
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+          const float keep = hi ? v[i + H] : v[i];
+          const float send = hi ? v[i] : v[i + H];
+          v[i] = keep + __shfl_xor(send, M, kWave);
+        }
+        ReduceScatter<NP, W, M * 2, H>::run(v, lane);
+      } else {
+        v[0] += __shfl_xor(v[0], M, kWave);
+        ReduceScatter<NP, W, M * 2, 1>::run(v, lane);
+      }
+    }
+  }
+  // Number of values left per lane and the expert index of value 0.
+  static constexpr int kLeft = NP / (NP < W ? NP : W);
+  __device__ __forceinline__ static int offset(int lane) {
+    int off = 0;
+#pragma unroll
+    for (int b = 0, span = NP / 2; span >= kLeft && (1 << b) < W && span > 0; ++b, span /= 2)
+      if (lane & (1 << b)) off += span;
+    return off;
+  }
+};
+
+}  // namespace mole

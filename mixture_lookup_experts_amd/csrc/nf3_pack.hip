@@ -1,0 +1,109 @@
+// NF3 encoder: blocks of 64 consecutive elements of a table row, fp16
+// absmax scale, 3-bit codes by threshold count, LSB-first bit stream.
+// (MoLE article, results section: the lookup table keeps the model's
+// quality when compressed to 3 bits, e.g. NF3.)
+//
+// Eight lanes own one 64-element block (8 elements = 16 bytes of bf16
+// each), so a wavefront encodes 8 consecutive blocks from 1 KB of
+// contiguous input with coalesced 16-byte loads.  Each lane forms the 24
+// code bits of its 8 elements; lanes 0..5 of the group then assemble the
+// block's six output dwords from two neighbours' bits with lane shuffles.
+#include "mole_device.hpp"
+#include "mole_kernels.hpp"
+
+namespace mole {
+
+// Decision thresholds between neighbouring NF3 levels: fp32 nearest-even
+// rounding of the exact midpoint of the two fp32 levels.
+__constant__ uint32_t kNf3MidBits[7] = {0xbf447ba0u, 0xbec82e26u, 0xbdfcdb98u, 0x3dbbbcd2u,
+                                        0x3e90b990u, 0x3f00a32cu, 0x3f4fbdffu};
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* x);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* x) {
+  Elem<uint16_t>::unpack(ldg16(p), x);
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float* x) {
+  Elem<float>::unpack(ldg16(p), x);
+  Elem<float>::unpack(ldg16(p + 4), x + 4);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void pack_nf3_kernel(const T* __restrict__ lut,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint16_t* __restrict__ scales,
+                                                       int64_t nblocks, int D) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 7;
+  const int nblk_row = D / 64;
+  const int64_t row_bytes = 3 * (int64_t)D / 8;
+  float mid[7];
+#pragma unroll
+  for (int j = 0; j < 7; ++j) mid[j] = __uint_as_float(kNf3MidBits[j]);
+
+  const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x / 64);
+  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  for (int64_t base = wave_id * 8; base < nblocks; base += waves_total * 8) {
+    const int64_t b = base + (lane >> 3);   // this group's block
+    const bool valid = b < nblocks;
+    const int64_t row = valid ? b / nblk_row : 0;
+    const int bi = valid ? (int)(b - row * nblk_row) : 0;
+    float x[8];
+    if (valid) load8<T>(lut + row * D + bi * 64 + sub * 8, x);
+    else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));
+    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    a = fmaxf(a, __shfl_xor(a, 4, 64));
+    a = fminf(a, 65504.f);
+    const _Float16 s16 = (_Float16)a;  // v_cvt_f16_f32: round to nearest even
+    const float s = (float)s16;
+    float thr[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) thr[j] = __fmul_rn(mid[j], s);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < 7; ++j) c += (x[i] > thr[j]) ? 1u : 0u;
+      if (s == 0.f) c = 3u;
+      bits |= c << (3 * i);
+    }
+    // Output dword k of the block = stream bits [32k, 32k+32), taken from the
+    // 24-bit pieces of lanes j0 = 32k/24 and j0+1.
+    const int k = sub < 6 ? sub : 5;
+    const int j0 = (32 * k) / 24, off = 32 * k - 24 * j0;
+    const int gbase = lane & ~7;
+    const uint32_t a0 = (uint32_t)__shfl((int)bits, gbase + j0, 64);
+    const uint32_t a1 = (uint32_t)__shfl((int)bits, gbase + j0 + 1, 64);
+    const uint32_t dw = (a0 >> off) | (a1 << (24 - off));
+    if (valid && sub < 6)
+      *reinterpret_cast<uint32_t*>(codes + row * row_bytes + (int64_t)bi * 24 + 4 * sub) = dw;
+    if (valid && sub == 0) scales[b] = __builtin_bit_cast(uint16_t, s16);
+  }
+}
+
+hipError_t launch_pack_nf3(const void* lut, uint8_t* codes, uint16_t* scales, int64_t rows,
+                           int64_t D, int dtype, hipStream_t s) {
+  const int64_t nblocks = rows * (D / 64);
+  if (nblocks == 0) return hipSuccess;
+  const int64_t need = (nblocks + 31) / 32;  // 32 blocks per 256-thread workgroup
+  const unsigned grid = (unsigned)(need < 8192 ? need : 8192);
+  if (dtype == kF32)
+    hipLaunchKernelGGL((pack_nf3_kernel<float>), dim3(grid), dim3(256), 0, s, (const float*)lut,
+                       codes, scales, nblocks, (int)D);
+  else
+    hipLaunchKernelGGL((pack_nf3_kernel<uint16_t>), dim3(grid), dim3(256), 0, s,
+                       (const uint16_t*)lut, codes, scales, nblocks, (int)D);
+  return hipGetLastError();
+}
+
+}  // namespace mole

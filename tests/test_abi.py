@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: libmole.so loads, exports every function
+include/mole.h declares, and rejects bad arguments on the host (no kernel
+is launched on any of these paths)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mixture_lookup_experts_amd as mole
+from mixture_lookup_experts_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mole.h")
+
+OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mole_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mole.library()
+
+
+def test_header_declares_the_hot_path():
+    names = declared_functions()
+    for fn in ("mole_build_lut", "mole_lookup_combine", "mole_pack_nf3", "mole_lookup_combine_nf3",
+               "mole_build_lut_workspace_size", "mole_gather_nf3_host",
+               "mole_lookup_combine_nf3_host", "mole_status_string", "mole_last_hip_error",
+               "mole_nf3_levels", "mole_abi_version"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.mole_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID):
+        assert mole.mole_status_string(code) not in ("", "unknown status")
+    assert mole.mole_status_string(12345) == "unknown status"
+
+
+def test_library_codebook_is_the_nf3_construction(lib):
+    """The kernels' level table equals the oracle's NormalFloat levels."""
+    import oracle
+    np.testing.assert_array_equal(np.array(mole.mole_nf3_levels(), np.float32), oracle.nf3_levels())
+
+
+def test_workspace_size(lib):
+    mn, rec = mole.mole_build_lut_workspace_size(50304, 1024, 4096, 16)
+    assert mn == 256 * 16 * 4096 * 2
+    assert rec >= mn and rec % (16 * 4096 * 2) == 0
+    mn, rec = mole.mole_build_lut_workspace_size(512, 64, 256, 4, dtype=0)
+    assert mn == 0 and rec == 0
+    with pytest.raises(mole.MoleError) as e:
+        mole.mole_build_lut_workspace_size(0, 64, 256, 4)
+    assert e.value.status == DIM
+    with pytest.raises(mole.MoleError) as e:
+        mole.mole_build_lut_workspace_size(8, 64, 256, 4, dtype=7)
+    assert e.value.status == DTYPE
+
+
+def P(x):
+    return ctypes.c_void_p(x)
+
+
+def test_combine_argument_errors(lib):
+    a = 0x1000  # never dereferenced: every case fails validation first
+    f = lib.mole_lookup_combine
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, 64, 4, 2, None) == DTYPE
+    assert f(None, P(a), P(a), P(a), P(a), 4, 10, 64, 4, 1, None) == NULL
+    assert f(P(a), P(a), P(a), P(a), P(a), -1, 10, 64, 4, 1, None) == DIM
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, 0, 64, 4, 1, None) == DIM
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, 0, 4, 1, None) == DIM
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, 64, 65, 1, None) == UNSUP
+    assert f(P(a), P(a + 4), P(a), P(a), P(a), 4, 10, 64, 4, 1, None) == ALIGN
+    assert f(None, None, None, None, None, 0, 10, 64, 4, 1, None) == OK  # empty batch: no-op
+
+
+def test_nf3_argument_errors(lib):
+    a = 0x1000
+    assert lib.mole_pack_nf3(P(a), P(a), P(a), 10, 4, 96, 1, None) == DIM
+    assert lib.mole_pack_nf3(None, P(a), P(a), 10, 4, 128, 1, None) == NULL
+    assert lib.mole_pack_nf3(P(a), P(a), P(a + 2), 10, 4, 128, 1, None) == ALIGN
+    g = lib.mole_lookup_combine_nf3
+    assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 96, 4, 1, None) == DIM
+    assert g(P(a), P(a), P(a), P(a), None, P(a), 4, 10, 128, 4, 1, None) == NULL
+    assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 128, 4, 5, None) == DTYPE
+
+
+def test_build_argument_errors(lib):
+    a = 0x1000
+    b = lib.mole_build_lut
+    assert b(P(a), P(a), P(a), P(a), 8, 64, 256, 4, 1, P(a), 10, None) == WS
+    assert b(P(a), P(a), P(a), P(a), 8, 60, 256, 4, 1, P(a), 1 << 40, None) == DIM
+    assert b(P(a), P(a), P(a), P(a), 8, 64, 256, 4, 1, None, 1 << 40, None) == NULL
+    assert b(P(a), P(a), P(a), P(a + 8), 8, 64, 256, 4, 1, P(a), 1 << 40, None) == ALIGN
+    assert b(P(a), P(a), P(a), P(a), 8, 64, 20000, 4, 0, None, 0, None) == UNSUP
+    assert b(P(a), P(a), P(a), P(a), 8, 64, 256, 4, 3, None, 0, None) == DTYPE
+
+
+def gather_inputs(seed, V=50, N=3, D=128, T=40):
+    r = np.random.Generator(np.random.PCG64(seed))
+    codes = r.integers(0, 256, size=(V, N, 3 * D // 8), dtype=np.uint8)
+    scales = r.integers(0, 1 << 15, size=(V, N, D // 64), dtype=np.uint16)
+    ids = r.integers(0, V, size=T).astype(np.int64)
+    return codes, scales, ids
+
+
+def test_host_gather_dedupes_and_copies_rows(lib):
+    import torch
+    codes, scales, ids = gather_inputs(7)
+    T, (V, N, CB) = ids.size, codes.shape
+    cs = torch.zeros(T * N * CB, dtype=torch.uint8)
+    ss = torch.zeros(T * N * 2, dtype=torch.int16)
+    remap = torch.zeros(T, dtype=torch.int64)
+    U = mole.mole_gather_nf3_host(torch.from_numpy(ids), torch.from_numpy(codes),
+                                  torch.from_numpy(scales.view(np.int16)), cs, ss, remap)
+    uniq = np.unique(ids)
+    assert U == uniq.size
+    r = remap.numpy()
+    cs = cs.numpy().reshape(T, N, CB)
+    ss = ss.numpy().view(np.uint16).reshape(T, N, 2)
+    # staged row remap[t] is table row ids[t]; first-occurrence order
+    for t in range(T):
+        np.testing.assert_array_equal(cs[r[t]], codes[ids[t]])
+        np.testing.assert_array_equal(ss[r[t]], scales[ids[t]])
+    first = [int(x) for x in dict.fromkeys(ids.tolist())]
+    assert [int(ids[list(r).index(u)]) for u in range(U)] == first
+
+
+def test_host_gather_rejects_bad_id(lib):
+    import torch
+    codes, scales, ids = gather_inputs(8, V=10, T=5)
+    ids[3] = 10
+    T, (V, N, CB) = ids.size, codes.shape
+    with pytest.raises(mole.MoleError) as e:
+        mole.mole_gather_nf3_host(torch.from_numpy(ids), torch.from_numpy(codes),
+                                  torch.from_numpy(scales.view(np.int16)),
+                                  torch.zeros(T * N * CB, dtype=torch.uint8),
+                                  torch.zeros(T * N * 2, dtype=torch.int16),
+                                  torch.zeros(T, dtype=torch.int64))
+    assert e.value.status == BADID
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_native, "_lib", None)
+    monkeypatch.setattr(_native, "_LIB_PATH", str(tmp_path / "libmole.so"))
+    with pytest.raises(mole.MoleLibraryMissing):
+        _native.library()

@@ -1,0 +1,361 @@
+"""GPU parity: every libmole entry point (through the C ABI) against the CPU
+oracle on identical seeded inputs.
+
+Bars (written in each test):
+  * lookup-combine (bf16 or fp32 table): per token max_d |y - y_ref| /
+    max_d |y_ref| <= 2e-5 (fp32 accumulation vs fp64);
+  * NF3 codes and scales: bit-exact;
+  * NF3 combine: same 2e-5 bar against the fp64 decode of the same codes;
+  * bf16 LUT build: relative L2 error <= 1e-2 vs the fp64 oracle over the
+    checked rows; fp32 build: <= 1e-5.
+No oracle input or expected value comes from the GPU: tables fed to the
+combine and NF3 tests are seeded synthetic arrays (or the oracle's own NF3
+encoding), never a GPU-built LUT.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_lookup_experts_amd as mole
+import oracle
+from mixture_lookup_experts_amd import synth
+from tests.gpu_util import bf16_to_f64, combine_rel_err, dev, host, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+COMBINE_TOL = 2e-5
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def rand_table(seed, V, N, D, dtype, std=0.05, rows=None):
+    """Seeded synthetic table; if `rows` is given only those rows are drawn
+    (the rest stay zero), which keeps full-vocabulary tables cheap."""
+    r = rng(seed)
+    conv = synth.f32_to_bf16_bits if dtype == "bf16" else (lambda a: a)
+    if rows is None:
+        return conv(r.standard_normal((V, N, D), dtype=np.float32) * np.float32(std))
+    out = np.zeros((V, N, D), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    out[rows] = conv(r.standard_normal((len(rows), N, D), dtype=np.float32) * np.float32(std))
+    return out
+
+
+def rand_hw(seed, T, N, D, dtype, wstd=0.02):
+    r = rng(seed)
+    h = r.standard_normal((T, D), dtype=np.float32)
+    w_r = r.standard_normal((N, D), dtype=np.float32) * np.float32(wstd)
+    if dtype == "bf16":
+        return synth.f32_to_bf16_bits(h), synth.f32_to_bf16_bits(w_r)
+    return h, w_r
+
+
+def run_combine(ids, h, w_r, lut):
+    y = torch.empty((ids.size, lut.shape[2]), dtype=torch.float32, device="cuda")
+    mole.mole_lookup_combine(dev(ids), dev(h), dev(w_r), dev(lut), y)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+# ----------------------------------------------------------------------------
+# lookup-combine, dense table
+# ----------------------------------------------------------------------------
+
+COMBINE_CASES = [
+    # V, N, D, T, dtype
+    (512, 4, 64, 64, "f32"),      # tiny workload
+    (512, 4, 64, 1, "f32"),
+    (300, 4, 768, 300, "bf16"),   # 160M-class width, ragged token tile
+    (300, 16, 1024, 257, "bf16"),
+    (200, 16, 2048, 33, "bf16"),
+    (100, 1, 128, 17, "bf16"),
+    (100, 3, 136, 19, "bf16"),    # N padded to 4, D not a power of two
+    (64, 64, 256, 9, "bf16"),     # largest N
+    (64, 32, 512, 40, "f32"),
+    (50, 5, 60, 21, "bf16"),      # D % 8 != 0: element-wise path
+    (50, 2, 30, 7, "f32"),
+    (20, 4, 8, 70, "bf16"),       # tiny D: one chunk per row
+]
+
+
+@pytest.mark.parametrize("V,N,D,T,dtype", COMBINE_CASES)
+def test_combine_matches_oracle(V, N, D, T, dtype):
+    seed = 1000 + V + N + D + T
+    lut = rand_table(seed, V, N, D, dtype)
+    h, w_r = rand_hw(seed + 1, T, N, D, dtype, wstd=0.3)
+    ids = rng(seed + 2).integers(0, V, T).astype(np.int64)
+    y = run_combine(ids, h, w_r, lut)
+    y_ref = oracle.lookup_combine(ids, h, w_r, lut)
+    assert combine_rel_err(y, y_ref) <= COMBINE_TOL
+
+
+def test_combine_empty_batch_is_noop():
+    lut = dev(rand_table(1, 10, 4, 64, "bf16"))
+    h = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    w_r = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros(0, dtype=torch.int64, device="cuda")
+    y = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
+    mole.mole_lookup_combine(ids, h, w_r, lut, y)
+    torch.cuda.synchronize()
+
+
+def test_combine_one_hot_gate_is_exact_row():
+    """Logit gap of 1000 makes the softmax exactly one-hot in fp32, so y is
+    the selected expert's row bit for bit."""
+    V, N, D, T = 40, 4, 256, 12
+    lut = rand_table(2, V, N, D, "bf16")
+    ids = rng(3).integers(0, V, T).astype(np.int64)
+    h = np.zeros((T, D), np.float32)
+    h[:, 0] = 1.0
+    for e_star in range(N):
+        w_r = np.zeros((N, D), np.float32)
+        w_r[e_star, 0] = 1000.0
+        y = run_combine(ids, synth.f32_to_bf16_bits(h), synth.f32_to_bf16_bits(w_r), lut)
+        np.testing.assert_array_equal(y, bf16_to_f64(lut[ids, e_star]).astype(np.float32))
+
+
+def test_combine_zero_router_is_slab_mean():
+    V, N, D, T = 40, 16, 1024, 20
+    lut = rand_table(4, V, N, D, "bf16")
+    ids = rng(5).integers(0, V, T).astype(np.int64)
+    h, _ = rand_hw(6, T, N, D, "bf16")
+    y = run_combine(ids, h, np.zeros((N, D), np.uint16), lut)
+    assert combine_rel_err(y, bf16_to_f64(lut[ids]).mean(axis=1)) <= COMBINE_TOL
+
+
+@pytest.mark.parametrize("name,T", [("160m", 1), ("160m", 8), ("160m", 64), ("160m", 256),
+                                    ("410m", 256), ("410m", 1024), ("410m", 4096),
+                                    ("1b", 1), ("1b", 16), ("1b", 128), ("1b", 1024)])
+def test_combine_full_size_zipf(name, T):
+    """Full vocabulary, workload widths, Zipf(1.1) ids, every token checked."""
+    w = synth.WORKLOADS[name]
+    ids = synth.make_ids(w, T, step=0)
+    lut = rand_table(77 + w.index, w.V, w.N, w.D, "bf16", rows=np.unique(ids))
+    h = synth.make_hidden(w, T)
+    w_r = synth.make_router(w)
+    y = run_combine(ids, h, w_r, lut)
+    y_ref = oracle.lookup_combine(ids, h, w_r, lut)
+    assert combine_rel_err(y, y_ref) <= COMBINE_TOL
+
+
+# ----------------------------------------------------------------------------
+# NF3 pack
+# ----------------------------------------------------------------------------
+
+def run_pack(table):
+    lut = dev(table)
+    V, N, D = table.shape
+    codes = torch.empty((V, N, 3 * D // 8), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((V, N, D // 64), dtype=torch.int16, device="cuda")
+    mole.mole_pack_nf3(lut, codes, scales)
+    torch.cuda.synchronize()
+    return host(codes), host(scales)
+
+
+@pytest.mark.parametrize("V,N,D,dtype,std", [(512, 4, 64, "f32", 0.02), (300, 4, 768, "bf16", 0.02),
+                                             (100, 16, 1024, "bf16", 1.0), (33, 3, 2048, "bf16", 1e-3),
+                                             (7, 1, 128, "f32", 3.0)])
+def test_pack_nf3_bit_exact(V, N, D, dtype, std):
+    table = rand_table(10 + D + V, V, N, D, dtype, std=std)
+    codes, scales = run_pack(table)
+    c_ref, s_ref, _ = oracle.pack_nf3(table)
+    np.testing.assert_array_equal(scales, s_ref)
+    np.testing.assert_array_equal(codes, c_ref)
+
+
+def test_pack_nf3_edge_cases_bit_exact():
+    """Exact threshold ties (strict compare keeps the lower code), the
+    neighbouring float above each tie, zero and tiny blocks (code 3),
+    fp16-subnormal scales and saturation at 65504."""
+    mid = oracle.nf3_midpoints()
+    lv = oracle.nf3_levels()
+    rows = []
+    tie = np.zeros(64, np.float32)
+    tie[0] = 1.0                                   # absmax 1 -> scale exactly 1.0
+    tie[1:8] = mid
+    tie[8:15] = np.nextafter(mid, np.float32(2))
+    tie[15:22] = np.nextafter(mid, np.float32(-2))
+    tie[22:30] = lv
+    tie[30] = -1.0
+    rows.append(tie)
+    rows.append(np.zeros(64, np.float32))
+    rows.append(np.full(64, 1e-9, np.float32))
+    sub = np.linspace(-3e-6, 2e-6, 64).astype(np.float32)
+    rows.append(sub)
+    sat = np.linspace(-1e5, 7e4, 64).astype(np.float32)
+    rows.append(sat)
+    half = np.linspace(-1, 1, 64).astype(np.float32) * np.float32(65519.0)
+    rows.append(half)
+    table = np.stack(rows).reshape(len(rows), 1, 64)
+    codes, scales = run_pack(table)
+    c_ref, s_ref, nsat = oracle.pack_nf3(table)
+    assert nsat == 2
+    np.testing.assert_array_equal(scales, s_ref)
+    np.testing.assert_array_equal(codes, c_ref)
+
+
+def test_pack_nf3_full_size_sampled_rows():
+    """410M-class table (50304 x 16 x 1024) packed on the GPU in one launch;
+    2048 seeded rows plus the first and last are re-encoded by the oracle."""
+    w = synth.WORKLOADS["410m"]
+    sample = np.unique(np.concatenate([[0, w.V - 1], rng(11).integers(0, w.V, 2048)]))
+    table = rand_table(12, w.V, w.N, w.D, "bf16", std=0.02, rows=sample)
+    codes, scales = run_pack(table)
+    c_ref, s_ref, _ = oracle.pack_nf3(table[sample])
+    np.testing.assert_array_equal(scales[sample], s_ref)
+    np.testing.assert_array_equal(codes[sample], c_ref)
+    other = np.setdiff1d(np.arange(w.V), sample)[:500]   # all-zero rows: scale 0, code 3
+    assert np.all(scales[other] == 0)
+    assert np.all(codes[other][..., 0::3] == 0xDB)
+
+
+# ----------------------------------------------------------------------------
+# NF3 combine (device table and host-resident table)
+# ----------------------------------------------------------------------------
+
+def run_nf3(ids, h, w_r, codes, scales):
+    y = torch.empty((ids.size, h.shape[1]), dtype=torch.float32, device="cuda")
+    mole.mole_lookup_combine_nf3(dev(ids), dev(h), dev(w_r), dev(codes), dev(scales.view(np.int16)), y)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+@pytest.mark.parametrize("V,N,D,T,dtype", [(512, 4, 64, 64, "f32"), (300, 4, 768, 200, "bf16"),
+                                           (300, 16, 1024, 257, "bf16"), (100, 16, 2048, 33, "bf16"),
+                                           (64, 64, 128, 10, "bf16"), (50, 3, 192, 17, "f32"),
+                                           (40, 1, 64, 5, "bf16")])
+def test_combine_nf3_matches_oracle(V, N, D, T, dtype):
+    seed = 2000 + V + N + D
+    table = rand_table(seed, V, N, D, "bf16")
+    codes, scales, _ = oracle.pack_nf3(table)
+    h, w_r = rand_hw(seed + 1, T, N, D, dtype, wstd=0.3)
+    ids = rng(seed + 2).integers(0, V, T).astype(np.int64)
+    y = run_nf3(ids, h, w_r, codes, scales)
+    y_ref = oracle.lookup_combine_nf3(ids, h, w_r, codes, scales)
+    assert combine_rel_err(y, y_ref) <= COMBINE_TOL
+
+
+@pytest.mark.parametrize("T", [256, 1024, 4096])
+def test_combine_nf3_full_size_zipf(T):
+    w = synth.WORKLOADS["410m-nf3"]
+    ids = synth.make_ids(w, T)
+    uniq = np.unique(ids)
+    table = rand_table(91, w.V, w.N, w.D, "bf16", std=0.02, rows=uniq)
+    codes, scales, _ = oracle.pack_nf3(table)
+    h = synth.make_hidden(w, T)
+    w_r = synth.make_router(w)
+    y = run_nf3(ids, h, w_r, codes, scales)
+    assert combine_rel_err(y, oracle.lookup_combine_nf3(ids, h, w_r, codes, scales)) <= COMBINE_TOL
+
+
+@pytest.mark.parametrize("T", [1, 256, 4096])
+def test_combine_nf3_host_resident(T):
+    """Table in pinned host memory; only the distinct requested rows cross
+    PCIe.  Equal bit for bit to the device-resident combine, and to the
+    oracle within the combine bar."""
+    w = synth.WORKLOADS["410m-nf3"]
+    V, N, D = w.V, w.N, w.D
+    ids = synth.make_ids(w, T, step=3)
+    uniq = np.unique(ids)
+    table = rand_table(92, V, N, D, "bf16", std=0.02, rows=uniq)
+    codes, scales, _ = oracle.pack_nf3(table)
+    h = synth.make_hidden(w, T, step=3)
+    w_r = synth.make_router(w)
+    codes_h = torch.from_numpy(codes).pin_memory()
+    scales_h = torch.from_numpy(scales.view(np.int16)).pin_memory()
+    CB, SB = 3 * D // 8, D // 64
+    cs = torch.empty(T * N * CB, dtype=torch.uint8, pin_memory=True)
+    ss = torch.empty(T * N * SB, dtype=torch.int16, pin_memory=True)
+    rs = torch.empty(T, dtype=torch.int64, pin_memory=True)
+    cd = torch.empty(T * N * CB, dtype=torch.uint8, device="cuda")
+    sd = torch.empty(T * N * SB, dtype=torch.int16, device="cuda")
+    rd = torch.empty(T, dtype=torch.int64, device="cuda")
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    U = mole.mole_lookup_combine_nf3_host(torch.from_numpy(ids), dev(h), dev(w_r), codes_h, scales_h,
+                                          cs, ss, rs, cd, sd, rd, y)
+    torch.cuda.synchronize()
+    assert U == uniq.size
+    y_host = host(y)
+    np.testing.assert_array_equal(y_host, run_nf3(ids, h, w_r, codes, scales))
+    assert combine_rel_err(y_host, oracle.lookup_combine_nf3(ids, h, w_r, codes, scales)) <= COMBINE_TOL
+
+
+# ----------------------------------------------------------------------------
+# LUT build
+# ----------------------------------------------------------------------------
+
+def run_build(layer, ws_bytes=None):
+    emb, w_up, w_down = dev(layer.emb), dev(layer.w_up), dev(layer.w_down)
+    V, D = layer.emb.shape
+    N, F, _ = layer.w_up.shape
+    lut = torch.empty((V, N, D), dtype=emb.dtype, device="cuda")
+    ws = None
+    if emb.dtype == torch.bfloat16:
+        mn, rec = mole.mole_build_lut_workspace_size(V, D, F, N)
+        ws = torch.empty(ws_bytes or rec, dtype=torch.uint8, device="cuda")
+    mole.mole_build_lut(emb, w_up, w_down, lut, workspace=ws)
+    torch.cuda.synchronize()
+    return lut
+
+
+def test_build_tiny_f32_all_rows():
+    w = synth.WORKLOADS["tiny"]
+    layer = synth.make_layer(w)
+    lut = host(run_build(layer))
+    ref = oracle.build_lut_rows(layer.emb, layer.w_up, layer.w_down)
+    assert rel_l2(lut, ref) <= 1e-5
+
+
+def test_build_tiny_f32_unit_scale_nonlinear():
+    """Unit-scale weights put GELU in its nonlinear range (|u| ~ 1), where
+    the erf and tanh forms differ by ~1e-4: the 1e-5 bar tells them apart."""
+    r = rng(21)
+    V, D, F, N = 512, 64, 256, 4
+    layer = synth.Layer(r.standard_normal((V, D), dtype=np.float32),
+                        (r.standard_normal((N, F, D)) / np.sqrt(D)).astype(np.float32),
+                        (r.standard_normal((N, D, F)) / np.sqrt(F)).astype(np.float32),
+                        np.zeros((N, D), np.float32))
+    lut = host(run_build(layer))
+    assert rel_l2(lut, oracle.build_lut_rows(layer.emb, layer.w_up, layer.w_down)) <= 1e-5
+
+
+def bf16_layer(seed, V, D, F, N, std=0.02):
+    r = rng(seed)
+    f = lambda shape, s: synth.f32_to_bf16_bits(r.standard_normal(shape, dtype=np.float32) * np.float32(s))
+    return synth.Layer(f((V, D), std), f((N, F, D), std), f((N, D, F), std), f((N, D), std))
+
+
+@pytest.mark.parametrize("V,D,F,N,std", [(600, 256, 512, 2, 0.02), (333, 72, 136, 3, 0.5),
+                                         (256, 512, 256, 1, 0.1), (1000, 128, 1024, 4, 0.02)])
+def test_build_bf16_small_all_rows(V, D, F, N, std):
+    layer = bf16_layer(V + D + F + N, V, D, F, N, std)
+    lut = host(run_build(layer))
+    ref = oracle.build_lut_rows(layer.emb, layer.w_up, layer.w_down)
+    assert rel_l2(bf16_to_f64(lut), ref) <= 1e-2
+
+
+def test_build_bf16_min_workspace_equals_recommended():
+    """Chunking over vocabulary rows does not change the arithmetic."""
+    layer = bf16_layer(5, 1300, 256, 512, 2, 0.05)
+    mn, _ = mole.mole_build_lut_workspace_size(1300, 256, 512, 2)
+    a = host(run_build(layer, ws_bytes=mn))
+    b = host(run_build(layer))
+    np.testing.assert_array_equal(a, b)
+    # and a zero embedding row gives an exactly zero table row
+    layer.emb[17] = 0
+    assert np.all(host(run_build(layer))[17] == 0)
+
+
+@pytest.mark.parametrize("name,nrows", [("160m", 48), ("410m", 24), ("1b", 8)])
+def test_build_full_size_sampled_rows(name, nrows):
+    w = synth.WORKLOADS[name]
+    layer = synth.make_layer(w)
+    lut = run_build(layer)
+    rows = np.unique(np.concatenate([[0, w.V - 1], rng(31).integers(0, w.V, nrows)]))
+    got = host(lut[torch.from_numpy(rows).cuda()])
+    del lut
+    ref = oracle.build_lut_rows(layer.emb, layer.w_up, layer.w_down, rows=rows)
+    assert rel_l2(bf16_to_f64(got), ref) <= 1e-2
+    per_row = [rel_l2(bf16_to_f64(got[i]), ref[i]) for i in range(len(rows))]
+    assert max(per_row) <= 2e-2
