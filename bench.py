@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoLE hot path on one MI355X.
+
+One *step* is one pass of every row of the hot path over one batch of
+synthetic input, in the order a deployment runs them:
+
+  1. mole_build_lut            reparameterise the N routed experts into the
+                               token-id table LUT[V][N][D] (bf16 MFMA GEMMs);
+  2. mole_pack_nf3             compress the table to 3-bit NF3 codes + scales;
+  3. mole_lookup_combine       router softmax + gather + combine of T tokens
+                               from the bf16 table in HBM;
+  4. mole_lookup_combine_nf3   the same from the NF3 table in HBM;
+  5. mole_lookup_combine_nf3_host  the same with the NF3 table in pinned host
+                               memory: host dedupe/gather, PCIe copy of the
+                               distinct rows, combine.
+
+Default workload: the 160M-class layer (V=50304, D=768, N=4 experts of
+768->3072->768, bf16) with a batch of T=256 Zipf(1.1) token ids.  All inputs
+are seeded synthetic arrays already resident in HBM (or pinned host memory
+for row 5) before the timed region; 8 pre-drawn (ids, h) batches are cycled.
+
+Printed: ONE JSON line.  `value` is whole-step throughput (T tokens per
+step / measured step time); per-row figures (build TFLOP/s, combine
+tokens/s and GB/s, ...) are in `rows`; `roofline` describes the dominant
+kernel of the step (the LUT build) and `roofline_combine` the combine.
+The CPU oracle is timed on a bounded sample on this host (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="160m", help="160m | 410m | 1b | tiny")
+    p.add_argument("--tokens", type=int, default=256)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="budget for the CPU-oracle baseline (0 disables it)")
+    p.add_argument("--no-scale-probe", action="store_true",
+                   help="skip the 410M-class combine measurement at T=1024/4096")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
+              "multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_lookup_experts_amd as mole
+    from mixture_lookup_experts_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    V, D, N, F, T = w.V, w.D, w.N, w.F, args.tokens
+    bf16 = w.dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    # ---------------- inputs (host draws -> HBM), outside the timed region,
+    # produced on `stream` (the stream every kernel below runs on)
+    torch.cuda.set_stream(stream)
+    layer = synth.make_layer(w)
+    emb, w_up, w_down, w_r = (to_dev(x) for x in (layer.emb, layer.w_up, layer.w_down, layer.w_r))
+    perm = synth.rank_permutation(w)
+    NB = 8
+    ids_h = [synth.make_ids(w, T, step=s, perm=perm) for s in range(NB)]
+    batches = [(to_dev(ids_h[s]), to_dev(synth.make_hidden(w, T, step=s))) for s in range(NB)]
+    uniq = [np.unique(x).size for x in ids_h]
+
+    lut = torch.empty((V, N, D), dtype=tdt, device=dev)
+    ws = None
+    if bf16:
+        # one vocabulary block: a single launch of each build GEMM per step
+        ws_bytes = V * N * F * 2
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    nf3 = D % 64 == 0
+    CB, SB = 3 * D // 8, D // 64
+    codes = torch.empty((V, N, CB), dtype=torch.uint8, device=dev)
+    scales = torch.empty((V, N, SB), dtype=torch.int16, device=dev)
+    y = torch.empty((T, D), dtype=torch.float32, device=dev)
+    y3 = torch.empty((T, D), dtype=torch.float32, device=dev)
+    y5 = torch.empty((T, D), dtype=torch.float32, device=dev)
+    # host-resident NF3 table (filled from the first pack, before timing)
+    codes_h = torch.empty((V, N, CB), dtype=torch.uint8, pin_memory=True)
+    scales_h = torch.empty((V, N, SB), dtype=torch.int16, pin_memory=True)
+    cs = torch.empty(T * N * CB, dtype=torch.uint8, pin_memory=True)
+    ss = torch.empty(T * N * SB, dtype=torch.int16, pin_memory=True)
+    rs = torch.empty(T, dtype=torch.int64, pin_memory=True)
+    cd = torch.empty(T * N * CB, dtype=torch.uint8, device=dev)
+    sd = torch.empty(T * N * SB, dtype=torch.int16, device=dev)
+    rd = torch.empty(T, dtype=torch.int64, device=dev)
+    ids_cpu = [torch.from_numpy(x) for x in ids_h]
+
+    ROWS = ["build", "pack_nf3", "combine", "combine_nf3", "combine_nf3_host"]
+    n_unique_host = []
+
+    def step(k, evs=None):
+        ids, h = batches[k % NB]
+        rec = (lambda i: evs[i].record(stream)) if evs is not None else (lambda i: None)
+        rec(0)
+        mole.mole_build_lut(emb, w_up, w_down, lut, workspace=ws, stream=stream)
+        rec(1)
+        if nf3:
+            mole.mole_pack_nf3(lut, codes, scales, stream=stream)
+        rec(2)
+        mole.mole_lookup_combine(ids, h, w_r, lut, y, stream=stream)
+        rec(3)
+        if nf3:
+            mole.mole_lookup_combine_nf3(ids, h, w_r, codes, scales, y3, stream=stream)
+        rec(4)
+        if nf3:
+            n_unique_host.append(mole.mole_lookup_combine_nf3_host(
+                ids_cpu[k % NB], h, w_r, codes_h, scales_h, cs, ss, rs, cd, sd, rd, y5,
+                stream=stream))
+        rec(5)
+
+    with torch.cuda.stream(stream):
+        # fill the host-resident table once
+        mole.mole_build_lut(emb, w_up, w_down, lut, workspace=ws, stream=stream)
+        if nf3:
+            mole.mole_pack_nf3(lut, codes, scales, stream=stream)
+            stream.synchronize()
+            codes_h.copy_(codes.cpu())
+            scales_h.copy_(scales.cpu())
+        for k in range(args.warmup):
+            step(k)
+        torch.cuda.synchronize()
+
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for k in range(args.steps):
+            step(k, evs[k])
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    row_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+              for i, name in enumerate(ROWS)}
+
+    # ---------------- per-row algorithmic work
+    bL = 2 if bf16 else 4
+    bh = bL
+    mean_u = float(np.mean(uniq))
+    build_flops = 4.0 * V * N * D * F
+    pack_bytes = V * N * D * bL + V * N * (CB + 2 * SB)
+    comb_bytes = T * (N * D * bL + D * bh + 4 * D + 8) + D * N * bh
+    comb_uniq = comb_bytes - (T - mean_u) * N * D * bL
+    nf3_row = N * (CB + 2 * SB)
+    nf3_bytes = T * (nf3_row + D * bh + 4 * D + 8) + D * N * bh
+    host_pcie = float(np.mean(n_unique_host)) * nf3_row if n_unique_host else 0.0
+
+    def rate(bytes_, ms):
+        return bytes_ / (ms * 1e-3) / 1e9
+
+    rows = {
+        "build": {"ms": row_ms["build"], "tflops": build_flops / (row_ms["build"] * 1e-3) / 1e12,
+                  "mfma_frac": build_flops / (row_ms["build"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                  "flops": build_flops},
+        "pack_nf3": {"ms": row_ms["pack_nf3"], "gbs": rate(pack_bytes, row_ms["pack_nf3"]),
+                     "hbm_frac": rate(pack_bytes, row_ms["pack_nf3"]) / HBM_PEAK_GBS},
+        "combine": {"us": row_ms["combine"] * 1e3, "tokens_per_s": T / (row_ms["combine"] * 1e-3),
+                    "gbs": rate(comb_bytes, row_ms["combine"]),
+                    "hbm_frac": rate(comb_bytes, row_ms["combine"]) / HBM_PEAK_GBS,
+                    "gbs_unique": rate(comb_uniq, row_ms["combine"]), "bytes": comb_bytes,
+                    "mean_unique_ids": mean_u},
+        "combine_nf3": {"us": row_ms["combine_nf3"] * 1e3,
+                        "tokens_per_s": T / (row_ms["combine_nf3"] * 1e-3),
+                        "gbs": rate(nf3_bytes, row_ms["combine_nf3"]),
+                        "hbm_frac": rate(nf3_bytes, row_ms["combine_nf3"]) / HBM_PEAK_GBS},
+        "combine_nf3_host": {"us": row_ms["combine_nf3_host"] * 1e3,
+                             "tokens_per_s": T / (row_ms["combine_nf3_host"] * 1e-3),
+                             "pcie_bytes": host_pcie,
+                             "pcie_gbs_effective": rate(host_pcie, row_ms["combine_nf3_host"])
+                             if host_pcie else 0.0},
+    }
+
+    result = {
+        "metric": "lookup-combine tokens/s + HBM GB/s (% peak); LUT-build TFLOP/s (% MFMA peak)",
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) h, Zipf(1.1) ids)",
+        "config": {"workload": "%s-class MoLE layer V=%d D=%d N=%d F=%d, T=%d %s ids; step = "
+                               "build + NF3 pack + combine + NF3 combine + host-resident NF3 combine"
+                               % (w.name, V, D, N, F, T, "Zipf(1.1)" if w.zipf else "uniform"),
+                   "V": V, "D": D, "N": N, "F": F, "tokens": T, "parallelism": "single GPU"},
+        "rows": rows,
+        "roofline": {"kernel": "mole_build_lut (gemm_nt_bf16 GELU + store, one launch each)",
+                     "bound": "mfma", "achieved": rows["build"]["tflops"], "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": rows["build"]["mfma_frac"], "traffic": None},
+        "roofline_combine": {"kernel": "lookup_combine_kernel", "bound": "hbm",
+                             "achieved": rows["combine"]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": rows["combine"]["hbm_frac"], "traffic": None},
+        "wall_s_timed": wall,
+    }
+
+    if not args.no_scale_probe and bf16:
+        torch.cuda.synchronize()
+        result["combine_at_scale"] = scale_probe(torch, mole, synth, dev, stream)
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(args, w, layer, ids_h[0], synth, T)
+
+    print(json.dumps(result), flush=True)
+
+
+def scale_probe(torch, mole, synth, dev, stream):
+    """Combine throughput where one launch moves tens of MB: the 410M-class
+    table (50304 x 16 x 1024 bf16 and its NF3 form) at T = 1024 and 4096,
+    Zipf ids and a distinct-id control (gathered bytes = unique bytes)."""
+    w = synth.WORKLOADS["410m"]
+    V, D, N = w.V, w.D, w.N
+    # every input is produced on `stream`, the stream the kernels run on
+    ctx = torch.cuda.stream(stream)
+    ctx.__enter__()
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.seed(w, 60))
+    lut = (torch.randn((V, N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    codes = torch.empty((V, N, 3 * D // 8), dtype=torch.uint8, device=dev)
+    scales = torch.empty((V, N, D // 64), dtype=torch.int16, device=dev)
+    w_r = (torch.randn((N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    mole.mole_pack_nf3(lut, codes, scales, stream=stream)
+    out = {"workload": "410M-class table V=50304 D=1024 N=16 (bf16 %.2f GB, NF3 %.2f GB)"
+           % (V * N * D * 2 / 1e9, V * N * (3 * D // 8 + D // 32) / 1e9)}
+    perm = synth.rank_permutation(w)
+    for T in (1024, 4096):
+        for kind in ("zipf", "distinct"):
+            ids_l = [torch.from_numpy(synth.make_ids(w, T, step=s, kind=kind, perm=perm)).to(dev)
+                     for s in range(8)]
+            h_l = [torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(8)]
+            y = torch.empty((T, D), dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            res = {}
+            for name, fn, row in (
+                    ("bf16", lambda i: mole.mole_lookup_combine(ids_l[i % 8], h_l[i % 8], w_r, lut, y,
+                                                                stream=stream), N * D * 2),
+                    ("nf3", lambda i: mole.mole_lookup_combine_nf3(ids_l[i % 8], h_l[i % 8], w_r, codes,
+                                                                   scales, y, stream=stream),
+                     N * (3 * D // 8 + D // 32))):
+                with torch.cuda.stream(stream):
+                    for i in range(5):
+                        fn(i)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    reps = 50
+                    e0.record(stream)
+                    for i in range(reps):
+                        fn(i)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                byts = T * (row + D * 2 + 4 * D + 8) + D * N * 2
+                res[name] = {"us": us, "tokens_per_s": T / (us * 1e-6), "gbs": byts / (us * 1e-6) / 1e9,
+                             "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes": byts}
+            out["T%d_%s" % (T, kind)] = res
+    torch.cuda.synchronize()
+    ctx.__exit__(None, None, None)
+    del lut, codes, scales
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(args, w, layer, ids, synth, T):
+    """The CPU oracle (plain fp64 C, OpenMP) on this host: the build on a
+    sample of vocabulary rows and the NF3 encoder on a sample of table rows,
+    both extrapolated linearly to the whole vocabulary, plus the two
+    combines on the whole batch.  value = T / (extrapolated step time)."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    budget = args.cpu_seconds
+    h = synth.make_hidden(w, T)
+    t0 = time.perf_counter()
+    nrow = 1
+    while True:
+        rows = np.arange(nrow, dtype=np.int64) * (w.V // nrow)
+        t1 = time.perf_counter()
+        lut_rows = oracle.build_lut_rows(layer.emb, layer.w_up, layer.w_down, rows=rows, nthreads=cores)
+        dt = time.perf_counter() - t1
+        if dt > 0.4 * budget or nrow >= w.V or time.perf_counter() - t0 > 0.6 * budget:
+            break
+        nrow = min(w.V, nrow * 4)
+    build_s = dt * w.V / nrow
+    table = synth.f32_to_bf16_bits(lut_rows.astype(np.float32)) if w.dtype == "bf16" else lut_rows.astype(np.float32)
+    t1 = time.perf_counter()
+    reps = 0
+    while True:
+        codes, scales, _ = oracle.pack_nf3(table, nthreads=cores) if w.D % 64 == 0 else (None, None, 0)
+        reps += 1
+        if time.perf_counter() - t1 > 0.5 or reps >= 50:
+            break
+    pack_s = (time.perf_counter() - t1) / reps * w.V / nrow
+    # combine on the whole batch: ids remapped into the sampled rows (same work per token)
+    ids_s = (np.asarray(ids) % nrow).astype(np.int64)
+    t1 = time.perf_counter()
+    oracle.lookup_combine(ids_s, h, layer.w_r, table, nthreads=cores)
+    comb_s = time.perf_counter() - t1
+    nf3_s = 0.0
+    if codes is not None:
+        t1 = time.perf_counter()
+        oracle.lookup_combine_nf3(ids_s, h, layer.w_r, codes, scales, nthreads=cores)
+        nf3_s = time.perf_counter() - t1
+    step_s = build_s + pack_s + comb_s + 2 * nf3_s
+    return {"value": T / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "build on %d of %d vocabulary rows and NF3 pack of those rows, extrapolated "
+                      "linearly to V; combine and NF3 combine (counted twice, device and host "
+                      "table) on the full batch of %d tokens" % (nrow, w.V, T),
+            "build_s_extrapolated": build_s, "pack_s_extrapolated": pack_s,
+            "combine_tokens_per_s": T / comb_s, "combine_nf3_tokens_per_s": T / nf3_s if nf3_s else None,
+            "measured_s": time.perf_counter() - t0}
+
+
+if __name__ == "__main__":
+    main()

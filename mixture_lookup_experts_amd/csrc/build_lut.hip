@@ -180,8 +180,11 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
                                  void* ws, size_t ws_bytes, hipStream_t s) {
   const int64_t NF = N * F;
   const int64_t row_bytes = NF * 2;
-  int64_t vc = (int64_t)(ws_bytes / (size_t)row_bytes) / kBM * kBM;
-  if (vc > V) vc = V;
+  // Vocabulary rows per block: all of V when the workspace holds them,
+  // otherwise a whole number of row tiles.
+  int64_t vc = (int64_t)(ws_bytes / (size_t)row_bytes);
+  if (vc >= V) vc = V;
+  else vc = vc / kBM * kBM;
   uint16_t* G = static_cast<uint16_t*>(ws);
   for (int64_t v0 = 0; v0 < V; v0 += vc) {
     const int64_t mc = (V - v0 < vc) ? (V - v0) : vc;

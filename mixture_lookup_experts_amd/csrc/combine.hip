@@ -5,12 +5,17 @@
 // contextual hidden state and all routed experts are active.)
 //
 // Work decomposition (one launch, no inter-block communication):
-//   * a "group" of G lanes (G a power of two) owns one token; a 256-thread
-//     block holds 256/G tokens;
-//   * router: lanes split D into 16-byte chunks, form per-expert partial
-//     dot products in fp32, reduce them across the group with a wavefront
-//     reduce-scatter (xor shuffles) plus one LDS exchange, and every lane
-//     evaluates the max-subtracted softmax redundantly;
+//   * a "group" of G lanes (G a power of two) owns one token; a block holds
+//     up to 16 tokens, fewer when the batch is small so that the grid still
+//     covers the 256 compute units;
+//   * router, bf16: the block's logits [tokens x experts] come from
+//     v_mfma_f32_16x16x32_bf16 tiles (tokens x 16 experts, K = 32 per
+//     instruction), the waves splitting D, so W_r is read once per block;
+//     partial tiles meet in LDS and one thread per token does the
+//     max-subtracted softmax;
+//   * router, fp32 or unaligned: lanes split D into chunks, form per-expert
+//     partial dot products, reduce them across the group with a wavefront
+//     reduce-scatter (xor shuffles) plus one LDS exchange;
 //   * gather/combine: lane `l` of the group streams chunks l, l+G, ... of
 //     every expert row of the token's contiguous slab LUT[id] with 16-byte
 //     loads (the first batch of slab loads is issued before the router so
@@ -62,6 +67,89 @@ __device__ __forceinline__ void router_partials(const T* __restrict__ h_row, con
   }
 }
 
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxTokPerBlock = 16;  // one 16-row MFMA tile of tokens
+
+// Router on the matrix cores for the block's `tpb` (<= 16) tokens starting
+// at t0: logits[t][e] = sum_d h[t0+t][d] * w_r[e][d] (bf16 products, fp32
+// accumulation), then gates = softmax over e < N into gsh[t][NP].  Lane l
+// of a wave supplies token row l%16 (A) and expert column l%16 (B) with the
+// 8 consecutive d values of k-group l/16; the waves take every nw-th 32-wide
+// K step.  Contains barriers: every thread of the block must call it.
+template <int NP>
+__device__ __forceinline__ void router_mfma_bf16(const uint16_t* __restrict__ h,
+                                                 const uint16_t* __restrict__ w_r, int64_t t0,
+                                                 int64_t T_, int tpb, int D, int N,
+                                                 float* red /* [4][16][NPAD] */,
+                                                 float* gsh /* [16][NP] */) {
+  constexpr int NT = (NP + 15) / 16, NPAD = NT * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int64_t tok = t0 + row;
+  const bool tok_ok = row < tpb && tok < T_;
+  const uint16_t* hrow = h + (tok_ok ? tok : 0) * (int64_t)D;
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int ksteps = (D + 31) / 32;
+  // Batches of UB K-steps per wave: all their loads are issued before the
+  // MFMAs that consume them, so a batch costs one memory round trip.
+  constexpr int UB = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
+  for (int base = wave; base < ksteps; base += UB * nw) {
+    uint4 a[UB], b[UB][NT];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int ks = base + u * nw;
+      const int k = ks * 32 + kg * 8;
+      const bool kok = ks < ksteps && k < D;
+      a[u] = (tok_ok && kok) ? ldg16(hrow + k) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int e = nt * 16 + row;
+        b[u][nt] = (e < N && kok) ? ldg16(w_r + (int64_t)e * D + k) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[u]),
+                                                          __builtin_bit_cast(bf16x8_t, b[u][nt]), acc[nt],
+                                                          0, 0, 0);
+  }
+  // lane l holds logits of tokens 4*(l/16) + r, expert nt*16 + l%16
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kg + r) * NPAD + nt * 16 + row] = acc[nt][r];
+  __syncthreads();
+  if ((int)threadIdx.x < tpb) {
+    const int tk = threadIdx.x;
+    float z[NP];
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      float s = 0.f;
+      for (int w = 0; w < nw; ++w) s += red[(w * 16 + tk) * NPAD + e];
+      z[e] = s;
+      if (e < N) zmax = fmaxf(zmax, s);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      z[e] = (e < N) ? expf(z[e] - zmax) : 0.f;
+      sum += z[e];
+    }
+    const float inv = 1.f / sum;
+#pragma unroll
+    for (int e = 0; e < NP; ++e) gsh[tk * NP + e] = z[e] * inv;
+  }
+  __syncthreads();
+}
+
 // Reduce the partial logits of a token group and turn them into softmax
 // gates held (identically) by every lane of the group.  Must be reached by
 // every thread of the block (it contains a barrier).
@@ -109,14 +197,19 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
     const int64_t* __restrict__ ids, const T* __restrict__ h, const T* __restrict__ w_r,
     const T* __restrict__ lut, float* __restrict__ y, int64_t T_, int D, int N) {
   constexpr int WG = G > kWave ? G / kWave : 1;
-  constexpr int TPB = 256 / G;
+  constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
   constexpr int CH = VECTOR ? Elem<T>::kVec : 1;  // elements per chunk
   constexpr int EC = NP < 16 ? NP : 16;           // experts per batch of slab loads
-  __shared__ float red[TPB * WG * NP];
+  constexpr bool kMfmaRouter = VECTOR && sizeof(T) == 2;
+  constexpr int NPAD = ((NP + 15) / 16) * 16;
+  __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * WG * NP];
+  __shared__ float gsh[kMfmaRouter ? kMaxTokPerBlock * NP : 1];
 
   const int tid = threadIdx.x;
+  const int tpb = blockDim.x / G;
   const int grp = tid / G, lig = tid % G;
-  const int64_t t = (int64_t)blockIdx.x * TPB + grp;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  const int64_t t = t0 + grp;
   const bool valid = t < T_;
   const int64_t tt = valid ? t : 0;
   const int C = D / CH;
@@ -137,10 +230,17 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
     }
   }
 
-  float part[NP];
-  router_partials<T, NP, VECTOR>(h + tt * D, w_r, D, N, lig, G, valid, part);
   float gate[NP];
-  group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+  if constexpr (kMfmaRouter) {
+    router_mfma_bf16<NP>(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r),
+                         t0, T_, tpb, D, N, red, gsh);
+#pragma unroll
+    for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
+  } else {
+    float part[NP];
+    router_partials<T, NP, VECTOR>(h + tt * D, w_r, D, N, lig, G, valid, part);
+    group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+  }
   if (!valid) return;
 
   for (int k = 0; k * G + lig < C; ++k) {
@@ -178,9 +278,9 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
     if constexpr (VECTOR) {
 #pragma unroll
       for (int j = 0; j < CH; j += 4)
-        *reinterpret_cast<float4*>(yo + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+        stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
     } else {
-      yo[0] = acc[0];
+      __builtin_nontemporal_store(acc[0], yo);
     }
   }
 }
@@ -194,15 +294,20 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     float* __restrict__ y, int64_t T_, int D, int N) {
   constexpr int WG = G > kWave ? G / kWave : 1;
-  constexpr int TPB = 256 / G;
+  constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
   constexpr int EC = NP < 8 ? NP : 8;
-  __shared__ float red[TPB * WG * NP];
+  constexpr bool kMfmaRouter = sizeof(TH) == 2;
+  constexpr int NPAD = ((NP + 15) / 16) * 16;
+  __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * WG * NP];
+  __shared__ float gsh[kMfmaRouter ? kMaxTokPerBlock * NP : 1];
   __shared__ float lv[8];
 
   const int tid = threadIdx.x;
   if (tid < 8) lv[tid] = __uint_as_float(kNf3LevelBits[tid]);
+  const int tpb = blockDim.x / G;
   const int grp = tid / G, lig = tid % G;
-  const int64_t t = (int64_t)blockIdx.x * TPB + grp;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  const int64_t t = t0 + grp;
   const bool valid = t < T_;
   const int64_t tt = valid ? t : 0;
   const int C = D / 32;                     // 32-element chunks per row
@@ -224,10 +329,17 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
     }
   }
 
-  float part[NP];
-  router_partials<TH, NP, true>(h + tt * D, w_r, D, N, lig, G, valid, part);
   float gate[NP];
-  group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+  if constexpr (kMfmaRouter) {
+    router_mfma_bf16<NP>(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r),
+                         t0, T_, tpb, D, N, red, gsh);
+#pragma unroll
+    for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
+  } else {
+    float part[NP];
+    router_partials<TH, NP, true>(h + tt * D, w_r, D, N, lig, G, valid, part);
+    group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+  }
   if (!valid) return;
 
   for (int k = 0; k * G + lig < C; ++k) {
@@ -267,7 +379,7 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
     float* yo = y + tt * D + (int64_t)c * 32;
 #pragma unroll
     for (int j = 0; j < 32; j += 4)
-      *reinterpret_cast<float4*>(yo + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+      stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
   }
 }
 
@@ -280,24 +392,31 @@ static int next_pow2(int x) {
   return p;
 }
 
-// Lanes per token: the power of two in [lo, 256] that wastes the fewest
-// lanes over the row's C chunks (ties: the larger group).
+// Lanes per token: the smallest power of two in [lo, hi] covering the C
+// chunks of a row (so each lane streams one chunk per expert row when it can).
 static int pick_group(int C, int lo, int hi) {
-  int best = hi, best_waste = 1 << 30;
-  for (int G = hi; G >= lo; G >>= 1) {
-    const int cpl = (C + G - 1) / G;
-    const int waste = G * cpl - C;
-    if (waste < best_waste) { best_waste = waste; best = G; }
-  }
-  return best;
+  int G = lo;
+  while (G < C && G < hi) G <<= 1;
+  return G;
+}
+
+// Tokens per block: up to 16 (one MFMA tile of router rows) and at most 256
+// threads, halved while the grid would have fewer than two blocks per
+// compute unit -- small decode batches then spread over the whole chip --
+// but never below one full wavefront per block.
+static int pick_tokens_per_block(int64_t T, int G) {
+  int tpb = 256 / G < 16 ? 256 / G : 16;
+  const int min_tpb = G >= 64 ? 1 : 64 / G;
+  while (tpb > min_tpb && (T + tpb - 1) / tpb < 512) tpb >>= 1;
+  return tpb;
 }
 
 template <typename E, int NP, int G, bool VEC>
 static hipError_t launch_dense(const int64_t* ids, const void* h, const void* w_r, const void* lut,
                                float* y, int64_t T, int D, int N, hipStream_t s) {
-  constexpr int TPB = 256 / G;
-  const int64_t blocks = (T + TPB - 1) / TPB;
-  hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC>), dim3((unsigned)blocks), dim3(256), 0, s,
+  const int tpb = pick_tokens_per_block(T, G);
+  const int64_t blocks = (T + tpb - 1) / tpb;
+  hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC>), dim3((unsigned)blocks), dim3(G * tpb), 0, s,
                      ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N);
   return hipGetLastError();
 }
@@ -348,9 +467,9 @@ hipError_t launch_lookup_combine(const int64_t* ids, const void* h, const void* 
 template <typename TH, int NP, int G>
 static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
                              const uint16_t* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
-  constexpr int TPB = 256 / G;
-  const int64_t blocks = (T + TPB - 1) / TPB;
-  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, G>), dim3((unsigned)blocks), dim3(256), 0, s,
+  const int tpb = pick_tokens_per_block(T, G);
+  const int64_t blocks = (T + tpb - 1) / tpb;
+  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, G>), dim3((unsigned)blocks), dim3(G * tpb), 0, s,
                      ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N);
   return hipGetLastError();
 }
@@ -360,6 +479,7 @@ static hipError_t dispatch_nf3_g(int G, const int64_t* ids, const void* h, const
                                  const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
                                  int D, int N, hipStream_t s) {
   switch (G) {
+    case 4: return launch_nf3<TH, NP, 4>(ids, h, w_r, codes, scales, y, T, D, N, s);
     case 8: return launch_nf3<TH, NP, 8>(ids, h, w_r, codes, scales, y, T, D, N, s);
     case 16: return launch_nf3<TH, NP, 16>(ids, h, w_r, codes, scales, y, T, D, N, s);
     case 32: return launch_nf3<TH, NP, 32>(ids, h, w_r, codes, scales, y, T, D, N, s);
@@ -387,7 +507,7 @@ hipError_t launch_lookup_combine_nf3(const int64_t* ids, const void* h, const vo
                                      int64_t T, int64_t D, int64_t N, int dtype_h, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int NP = next_pow2((int)N);
-  const int G = pick_group((int)(D / 32), 8, 64);
+  const int G = pick_group((int)(D / 32), 4, 64);
   if (dtype_h == kF32)
     return dispatch_nf3_np<float>(NP, G, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
   return dispatch_nf3_np<uint16_t>(NP, G, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);

@@ -46,6 +46,13 @@ template <> struct Elem<uint16_t> {  // bf16 bit patterns
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte streaming store (non-temporal: the output is not re-read here).
+typedef float f32x4_vec_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void stg16_nt(float* p, float a, float b, float c, float d) {
+  const f32x4_vec_t v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_vec_t*>(p));
+}
+
 // ---- cross-lane reductions ----------------------------------------------------
 // Reduce-scatter of NP per-lane partial sums over the W lanes (W a power of
 // two, W <= 64) of a lane group: at the step with xor-mask m the lane keeps
