@@ -14,9 +14,18 @@
 // output tile per 256-thread workgroup, 4 waves in a 2x2 arrangement, each
 // owning a 128x128 sub-tile of v_mfma_f32_32x32x16_bf16 accumulators; the
 // K loop streams 64-wide slices of A and B through a double-buffered LDS
-// ring (row = 128 bytes, 16-byte segments XOR-swizzled by row so both the
-// staging writes and the fragment reads are bank-conflict free), with the
-// next slice's global loads in flight during the current slice's MFMAs.
+// ring (row = 128 bytes; 16-byte segment s of row r stored at s ^ ((r/2) & 7):
+// the LDS serves 256 bytes (64 banks) per cycle, so the 16 lanes of one
+// ds_read_b128 pass -- 16 consecutive rows -- and the 16 lanes of a staging
+// write -- 2 rows x 8 segments -- each hit 16 distinct 16-byte bank groups),
+// with the
+// next slice's global loads and the next K step's fragment reads in flight
+// during the current MFMAs (an explicit interleave of MFMA, LDS and global
+// instructions).  Operands are read through buffer resources, so rows past
+// the matrix edge read zeros and the K loop has no branches.  Tiles are
+// ordered per GEMM (see tile_of_block).  The
+// GEMM-1 epilogue evaluates GELU with a polynomial normal CDF (see
+// gelu_poly).
 //
 // fp32 path (small tables): one workgroup per (v, e) row: stage Emb[v] in
 // LDS, each thread forms hidden units u[f] with fp32 FMAs and exact-form
@@ -29,58 +38,165 @@ namespace mole {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// GELU(u) = u * Phi(u) = u/2 * (1 + erf(u / sqrt 2)).
+// GELU(u) = u * Phi(u) = u/2 * (1 + erf(u / sqrt 2)), with the C library's
+// erff (fp32 path).
 __device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
+
+// GELU for the bf16 path: u * Phi(u) with Phi - 1/2 (an odd function)
+// replaced on [-4, 4] by the odd polynomial s*(c0 + c1 s^2 + ... + c9 s^18),
+// s = u/4, a least-squares fit to the normal CDF on Chebyshev nodes
+// (gelu_poly_fit.py next to this file derives and checks it): |error| <=
+// 6e-6 in fp32, and Phi is clamped to [0, 1] outside (1 - Phi(4) = 3.2e-5).
+// The hidden activation is rounded to bf16 (relative 2^-9) right after, so
+// the approximation is invisible there; it costs ~14 full-rate VALU slots and
+// no transcendental, which matters because this epilogue runs once per
+// hidden unit and vocabulary row.
+__device__ __forceinline__ float gelu_poly(float u) {
+  const float s = __builtin_amdgcn_fmed3f(u, -4.0f, 4.0f) * 0.25f;
+  const float s2 = s * s;
+  float p = -1.005731821e+00f;
+  p = fmaf(p, s2, 6.118065357e+00f);
+  p = fmaf(p, s2, -1.688562202e+01f);
+  p = fmaf(p, s2, 2.834799385e+01f);
+  p = fmaf(p, s2, -3.288965607e+01f);
+  p = fmaf(p, s2, 2.843501091e+01f);
+  p = fmaf(p, s2, -1.914556694e+01f);
+  p = fmaf(p, s2, 1.018382359e+01f);
+  p = fmaf(p, s2, -4.254103661e+00f);
+  p = fmaf(p, s2, 1.595752358e+00f);
+  const float phi = __builtin_amdgcn_fmed3f(fmaf(s, p, 0.5f), 0.0f, 1.0f);
+  return u * phi;
+}
 
 enum { kEpiStore = 0, kEpiGelu = 1 };
 
-constexpr int kBK = 64;  // K slice per LDS stage (64 bf16 = 128 bytes per row)
+constexpr int kBK = 64;     // K slice per LDS stage (64 bf16 = 128 bytes per row)
+constexpr int kXcds = 8;    // MI355X: 8 accelerator complex dies, each with its own L2
+constexpr int kGroupM = 8;  // row tiles per raster band
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every record: loads read 0, stores drop
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
+struct GemmArgs {
+  const uint16_t* A; int64_t lda, sAz;
+  const uint16_t* B; int64_t ldb, sBz;
+  uint16_t* C; int64_t ldc, sCz;
+  int M, N, K;
+  int tiles_m, tiles_n, batch;
+  int xcd_order;  // 1: XCD-banded tile order, 0: row-major tile order
+};
+
+// Map the hardware workgroup id to an output tile.
+//  * xcd_order = 0: row-major over tiles (n fastest).  Concurrent workgroups
+//    then cover one or two full rows of tiles: they share the A row panel
+//    and write one contiguous stripe of C.  Used for the wide GEMM-1, whose
+//    C (the hidden activations, up to several GB) must be written in long
+//    runs -- a scattered order made the memory system write every output
+//    line several times over.
+//  * xcd_order = 1: workgroups go to the XCDs round-robin (id % 8), so
+//    consecutive ids land on different L2 caches; renumbering gives each XCD
+//    a contiguous run of logical tiles, walked in bands of kGroupM row tiles
+//    column by column, so the tiles an XCD runs together share A row panels
+//    and B column panels in its L2.  Used for GEMM-2 (narrow N = D).
+__device__ __forceinline__ void tile_of_block(const GemmArgs& p, int& z, int& tm, int& tn) {
+  const int b = blockIdx.x;
+  if (!p.xcd_order) {
+    tn = b % p.tiles_n;
+    tm = (b / p.tiles_n) % p.tiles_m;
+    z = b / (p.tiles_n * p.tiles_m);
+    return;
+  }
+  const int total = p.tiles_m * p.tiles_n * p.batch;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int xcd = b % kXcds, loc = b / kXcds;
+  const int logical = xcd < rem ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+  const int per_z = p.tiles_m * p.tiles_n;
+  z = logical / per_z;
+  const int r = logical - z * per_z;
+  const int band = r / (kGroupM * p.tiles_n);
+  const int first_m = band * kGroupM;
+  const int gm = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
+  const int rin = r - band * kGroupM * p.tiles_n;
+  tm = first_m + rin % gm;
+  tn = rin / gm;
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// Scheduling-group masks (LLVM AMDGPU sched_group_barrier).
+constexpr int kSgMfma = 0x008, kSgVmemRd = 0x020, kSgDsRd = 0x100, kSgDsWr = 0x200;
+
+// C[m][n] = epi( sum_k A[m*lda + k] * B[n*ldb + k] ), bf16 in, fp32
+// accumulation, bf16 out; batch index z offsets A, B, C by sAz, sBz, sCz.
+// Requires K % 8 == 0 and N % 4 == 0 (16-byte K segments, 8-byte stores).
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, int64_t sAz,
-    const uint16_t* __restrict__ B, int64_t ldb, int64_t sBz,
-    uint16_t* __restrict__ C, int64_t ldc, int64_t sCz, int M, int N, int K) {
+__global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;     // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;   // MFMA tiles per wave
   constexpr int SA = BM * 8 / 256, SB = BN * 8 / 256;  // 16-byte segments per thread
+  constexpr int KS = kBK / 16;                // MFMA K steps per LDS stage
+  static_assert(KS == 4, "the software pipeline below is written for 4 K steps per stage");
   __shared__ uint4 smem[2][(BM + BN) * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int z = blockIdx.z;
-  A += z * sAz;
-  B += z * sBz;
-  C += z * sCz;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const int seg = tid & 7;  // staging segment (constant per thread)
+  int z, tm, tn;
+  tile_of_block(p, z, tm, tn);
+  const int M = p.M, N = p.N, K = p.K;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_a = M - m0 < BM ? M - m0 : BM;
+  const int rows_b = N - n0 < BN ? N - n0 : BN;
+  // Buffer resources over this tile's A and B row panels: a load past the
+  // panel (a row beyond M or N) returns zeros without a branch.
+  const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.A + z * p.sAz + (int64_t)m0 * p.lda), (short)0, (int)(rows_a * p.lda * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.B + z * p.sBz + (int64_t)n0 * p.ldb), (short)0, (int)(rows_b * p.ldb * 2), kRsrcWord3);
+
+  // Staging: thread t moves 16-byte segment (t & 7) of rows t/8 + 32 i.
+  const int seg = tid & 7;
+  const int srow = tid >> 3;
+  const int pseg = seg ^ ((srow >> 1) & 7);  // XOR swizzle ((row >> 1) & 7 is the same for all i)
+  uint32_t offa[SA], offb[SB];
+#pragma unroll
+  for (int i = 0; i < SA; ++i) {
+    const int row = srow + 32 * i;
+    offa[i] = row < rows_a ? (uint32_t)(row * p.lda * 2 + seg * 16) : kOob;
+  }
+#pragma unroll
+  for (int i = 0; i < SB; ++i) {
+    const int row = srow + 32 * i;
+    offb[i] = row < rows_b ? (uint32_t)(row * p.ldb * 2 + seg * 16) : kOob;
+  }
 
   uint4 ra[SA], rb[SB];
   auto gload = [&](int k0) {
-    const int kk = k0 + seg * 8;
+    const bool kok = k0 + seg * 8 < K;
 #pragma unroll
-    for (int i = 0; i < SA; ++i) {
-      const int row = (tid + i * 256) >> 3;
-      const int gm = m0 + row;
-      ra[i] = (gm < M && kk < K) ? ldg16(A + (int64_t)gm * lda + kk) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < SA; ++i) ra[i] = buf_load16(ra_rs, kok ? offa[i] + k0 * 2 : kOob);
 #pragma unroll
-    for (int i = 0; i < SB; ++i) {
-      const int row = (tid + i * 256) >> 3;
-      const int gn = n0 + row;
-      rb[i] = (gn < N && kk < K) ? ldg16(B + (int64_t)gn * ldb + kk) : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < SB; ++i) rb[i] = buf_load16(rb_rs, kok ? offb[i] + k0 * 2 : kOob);
   };
   auto swrite = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < SA; ++i) {
-      const int row = (tid + i * 256) >> 3;
-      smem[st][row * 8 + (seg ^ (row & 7))] = ra[i];
+    for (int i = 0; i < SA; ++i) smem[st][(srow + 32 * i) * 8 + pseg] = ra[i];
+#pragma unroll
+    for (int i = 0; i < SB; ++i) smem[st][(BM + srow + 32 * i) * 8 + pseg] = rb[i];
+  };
+  // Fragments of one 16-wide K step: lane l reads row l%32 of each 32-row
+  // MFMA tile, 8 consecutive k at 8*(l/32) (swizzled segment).
+  auto fload = [&](int st, int ks, uint4* a, uint4* b) {
+    const int sg = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WM + i * 32 + (lane & 31);
+      a[i] = smem[st][r * 8 + (sg ^ ((r >> 1) & 7))];
     }
 #pragma unroll
-    for (int i = 0; i < SB; ++i) {
-      const int row = (tid + i * 256) >> 3;
-      smem[st][(BM + row) * 8 + (seg ^ (row & 7))] = rb[i];
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * WN + j * 32 + (lane & 31);
+      b[j] = smem[st][(BM + r) * 8 + (sg ^ ((r >> 1) & 7))];
     }
   };
 
@@ -92,48 +208,77 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Operands swapped (B tile as the matrix-core "A"): lane l then holds
+  // C[m = l%32][n = 8*(r/4) + 4*(l/32) + r%4] in accumulator r, i.e. four
+  // consecutive n per group of four registers.
+  auto mfmas = [&](const uint4* a, const uint4* b) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
+                                                             __builtin_bit_cast(bf16x8_t, a[i]),
+                                                             acc[i][j], 0, 0, 0);
+  };
+
   const int nk = (K + kBK - 1) / kBK;
   gload(0);
   swrite(0);
   __syncthreads();
+  uint4 fa[2][TM], fb[2][TN];
+  fload(0, 0, fa[0], fb[0]);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    // Loads of the next stage (past K they read zeros, so the last
+    // iteration needs no branch); fragments of K step s+1 are read while
+    // the MFMAs of step s run; the staged next slice is written to the other
+    // LDS buffer during the last step.
+    gload((kt + 1) * kBK);
+    fload(st, 1, fa[1], fb[1]);
+    mfmas(fa[0], fb[0]);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int sg = 2 * ks + (lane >> 5);   // 16-byte segment holding this lane's 8 k values
-      uint4 a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + (lane & 31);
-        a[i] = smem[st][r * 8 + (sg ^ (r & 7))];
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * WN + j * 32 + (lane & 31);
-        b[j] = smem[st][(BM + r) * 8 + (sg ^ (r & 7))];
-      }
-      // Operands swapped (B tile as the matrix-core "A"): lane l then holds
-      // C[m = l%32][n = 8*(r/4) + 4*(l/32) + r%4] in accumulator r, i.e.
-      // four consecutive n per group of four registers.
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
-                                                               __builtin_bit_cast(bf16x8_t, a[i]),
-                                                               acc[i][j], 0, 0, 0);
+    for (int i = 0; i < TM + TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRd, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVmemRd, (SA + SB) / (TM + TN), 0);
     }
-    if (kt + 1 < nk) swrite(st ^ 1);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, TM * TN - (TM + TN), 0);
+    fload(st, 2, fa[0], fb[0]);
+    mfmas(fa[1], fb[1]);
+#pragma unroll
+    for (int i = 0; i < TM + TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRd, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, TM * TN - (TM + TN), 0);
+    fload(st, 3, fa[1], fb[1]);
+    mfmas(fa[0], fb[0]);
+#pragma unroll
+    for (int i = 0; i < TM + TN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRd, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, TM * TN - (TM + TN), 0);
+    swrite(st ^ 1);
+    mfmas(fa[1], fb[1]);
+#pragma unroll
+    for (int i = 0; i < SA + SB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsWr, 1, 0);
+    }
     __syncthreads();
+    fload(st ^ 1, 0, fa[0], fb[0]);
   }
 
-  // Epilogue: (GELU), round to bf16, 8-byte stores of 4 consecutive columns.
+  // Epilogue: (GELU), round to bf16, 8-byte stores of 4 consecutive columns
+  // through a buffer resource over this tile's rows (rows past M and column
+  // groups past N take an out-of-range offset and are dropped).
+  const int rows_c = M - m0 < BM ? M - m0 : BM;
+  const __amdgpu_buffer_rsrc_t rc_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.C + z * p.sCz + (int64_t)m0 * p.ldc), (short)0, (int)(rows_c * p.ldc * 2), kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int m = m0 + wm * WM + i * 32 + (lane & 31);
-    if (m >= M) continue;
-    uint16_t* crow = C + (int64_t)m * ldc;
+    const int mr = wm * WM + i * 32 + (lane & 31);  // row within the tile
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -143,18 +288,30 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           v[q] = acc[i][j][4 * g + q];
-          if constexpr (EPI == kEpiGelu) v[q] = gelu_erf(v[q]);
+          if constexpr (EPI == kEpiGelu) v[q] = gelu_poly(v[q]);
         }
-        if (n + 3 < N) {
-          *reinterpret_cast<uint2*>(crow + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < N) crow[n + q] = (uint16_t)f32_to_bf16_rne(v[q]);
-        }
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+        const uint32_t off = (mr < rows_c && n < N) ? (uint32_t)(mr * p.ldc * 2 + n * 2) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
+                                                                 make_uint2(lo, hi)),
+                                              rc_rs, (int)off, 0, 0);
       }
     }
   }
+}
+
+template <int BM, int BN, int EPI>
+static hipError_t launch_gemm(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
+                              int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, int M, int N, int K,
+                              int batch, int xcd_order, hipStream_t s) {
+  GemmArgs p{A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, (M + BM - 1) / BM, (N + BN - 1) / BN, batch,
+             xcd_order};
+  const int64_t total = (int64_t)p.tiles_m * p.tiles_n * batch;
+  hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EPI>), dim3((unsigned)total), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 constexpr int kBM = kBuildTileM, kBN = 256;
@@ -188,17 +345,11 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
   uint16_t* G = static_cast<uint16_t*>(ws);
   for (int64_t v0 = 0; v0 < V; v0 += vc) {
     const int64_t mc = (V - v0 < vc) ? (V - v0) : vc;
-    dim3 g1((unsigned)((NF + kBN - 1) / kBN), (unsigned)((mc + kBM - 1) / kBM), 1);
-    hipLaunchKernelGGL((gemm_nt_bf16_kernel<kBM, kBN, kEpiGelu>), g1, dim3(256), 0, s,
-                       emb + v0 * D, D, (int64_t)0, w_up, D, (int64_t)0, G, NF, (int64_t)0,
-                       (int)mc, (int)NF, (int)D);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_gemm<kBM, kBN, kEpiGelu>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc,
+                                                      (int)NF, (int)D, 1, /*xcd_order=*/0, s);
     if (err != hipSuccess) return err;
-    dim3 g2((unsigned)((D + kBN - 1) / kBN), (unsigned)((mc + kBM - 1) / kBM), (unsigned)N);
-    hipLaunchKernelGGL((gemm_nt_bf16_kernel<kBM, kBN, kEpiStore>), g2, dim3(256), 0, s,
-                       (const uint16_t*)G, NF, F, w_down, F, D * F, lut + v0 * N * D, N * D, D,
-                       (int)mc, (int)D, (int)F);
-    err = hipGetLastError();
+    err = launch_gemm<kBM, kBN, kEpiStore>(G, NF, F, w_down, F, D * F, lut + v0 * N * D, N * D, D,
+                                           (int)mc, (int)D, (int)F, (int)N, /*xcd_order=*/1, s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
