@@ -50,7 +50,30 @@ def parse():
                    help="budget for the CPU-oracle baseline (0 disables it)")
     p.add_argument("--no-scale-probe", action="store_true",
                    help="skip the 410M-class combine measurement at T=1024/4096")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one 256 MiB device-to-device copy first (the reference kernel "
+                        "that scales FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return p.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_build_lut_160m.txt")
+BUILD_SRC = os.path.join(ROOT, "mixture_lookup_experts_amd", "csrc", "build_lut.hip")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per build call from the committed counter summary, if it
+    was taken on this workload with the current build kernel source."""
+    import hashlib
+    try:
+        kv = dict(l.split("=", 1) for l in open(TRAFFIC_FILE).read().split("\n")
+                  if "=" in l and not l.startswith("#"))
+        src = hashlib.sha256(open(BUILD_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if kv.get("workload", "").strip() != workload or kv.get("build_lut_sha256", "").strip() != src:
+        return None
+    return float(kv["bytes_per_build"])
 
 
 def main():
@@ -138,6 +161,12 @@ def main():
         rec(5)
 
     with torch.cuda.stream(stream):
+        if args.copy_calibration:
+            src_c = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+            dst_c = torch.empty_like(src_c)
+            dst_c.copy_(src_c)
+            torch.cuda.synchronize()
+            del src_c, dst_c
         # fill the host-resident table once
         mole.mole_build_lut(emb, w_up, w_down, lut, workspace=ws, stream=stream)
         if nf3:
@@ -222,7 +251,8 @@ def main():
         "rows": rows,
         "roofline": {"kernel": "mole_build_lut (gemm_nt_bf16 GELU + store, one launch each)",
                      "bound": "mfma", "achieved": rows["build"]["tflops"], "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": rows["build"]["mfma_frac"], "traffic": None},
+                     "unit": "TFLOP/s", "frac": rows["build"]["mfma_frac"],
+                     "traffic": measured_traffic(args.workload) if T == 256 else None},
         "roofline_combine": {"kernel": "lookup_combine_kernel", "bound": "hbm",
                              "achieved": rows["combine"]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": rows["combine"]["hbm_frac"], "traffic": None},
