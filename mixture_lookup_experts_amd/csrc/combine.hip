@@ -287,30 +287,70 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
 
 // ---------------------------------------------------------------------------
 // NF3 table: 32 codes (12 bytes) per chunk, one fp16 scale per 64 elements.
+// A token is owned by G = CP*S lanes: lane (s, c) = s*CP + c decodes chunk c
+// (and c + CP, ... when a row has more than CP chunks) for the experts
+// e = s, s + S, s + 2S, ...; the S partial sums of a chunk then meet in a
+// reduce-scatter over the lanes c, c + CP, ..., so each lane stores 32/S of
+// the chunk's outputs.  Splitting the experts across lanes keeps a full
+// wavefront busy per token at the 160M/410M widths (24-32 chunks per row)
+// and lets every lane issue all of its code loads in one batch.
 // ---------------------------------------------------------------------------
-template <typename TH, int NP, int G>
+
+// Halving reduce-scatter of the 32 per-lane sums over the S expert splits:
+// at step b (xor mask CP << b) a lane keeps the half its split bit b
+// selects and adds the partner's copy of it.  Afterwards the lane holds the
+// 32/S sums of elements off(s) .. off(s) + 32/S - 1 of its chunk.
+template <int CP, int S, int B = 0, int CNT = 32>
+struct SplitReduce {
+  __device__ __forceinline__ static void run(float* acc, int sp) {
+    if constexpr ((1 << B) < S) {
+      constexpr int H = CNT / 2;
+      const bool hi = ((sp >> B) & 1) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float keep = hi ? acc[i + H] : acc[i];
+        const float send = hi ? acc[i] : acc[i + H];
+        acc[i] = keep + __shfl_xor(send, CP << B, kWave);
+      }
+      SplitReduce<CP, S, B + 1, H>::run(acc, sp);
+    }
+  }
+  __device__ __forceinline__ static int offset(int sp) {
+    int off = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) < S; ++b)
+      if ((sp >> b) & 1) off += 16 >> b;
+    return off;
+  }
+};
+
+template <typename TH, int NP, int CP, int S>
 __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
     const int64_t* __restrict__ ids, const TH* __restrict__ h, const TH* __restrict__ w_r,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     float* __restrict__ y, int64_t T_, int D, int N) {
-  constexpr int WG = G > kWave ? G / kWave : 1;
+  constexpr int G = CP * S;                        // lanes per token (<= 64)
+  static_assert(G <= kWave, "a token's lanes must share one wavefront");
   constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
-  constexpr int EC = NP < 8 ? NP : 8;
+  constexpr int EPL = (NP + S - 1) / S;            // experts per lane
+  constexpr int EC = EPL < 8 ? EPL : 8;            // experts per batch of code loads
+  constexpr int OUT = 32 / S;                      // outputs stored per lane and chunk
   constexpr bool kMfmaRouter = sizeof(TH) == 2;
   constexpr int NPAD = ((NP + 15) / 16) * 16;
-  __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * WG * NP];
-  __shared__ float gsh[kMfmaRouter ? kMaxTokPerBlock * NP : 1];
+  __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * NP];
+  __shared__ float gsh[kMaxTokPerBlock * NP];
   __shared__ float lv[8];
 
   const int tid = threadIdx.x;
   if (tid < 8) lv[tid] = __uint_as_float(kNf3LevelBits[tid]);
   const int tpb = blockDim.x / G;
   const int grp = tid / G, lig = tid % G;
+  const int sp = lig / CP, ch = lig % CP;          // expert split, chunk
   const int64_t t0 = (int64_t)blockIdx.x * tpb;
   const int64_t t = t0 + grp;
   const bool valid = t < T_;
   const int64_t tt = valid ? t : 0;
-  const int C = D / 32;                     // 32-element chunks per row
+  const int C = D / 32;                            // 32-element chunks per row
   const int64_t row_bytes = 3 * (int64_t)D / 8, nblk = D / 64;
   const int64_t id = valid ? ids[tt] : 0;
   const uint8_t* crow0 = codes + id * (int64_t)N * row_bytes;
@@ -318,53 +358,51 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
 
   uint3 cw[EC];
   uint32_t sc[EC];
-  const bool have0 = valid && lig < C;
-  if (have0) {
+  auto load_batch = [&](int c, int j0) {
 #pragma unroll
-    for (int e = 0; e < EC; ++e) {
+    for (int j = 0; j < EC; ++j) {
+      const int e = (j0 + j) * S + sp;
       if (e < N) {
-        cw[e] = *reinterpret_cast<const uint3*>(crow0 + (int64_t)e * row_bytes + (int64_t)lig * 12);
-        sc[e] = srow0[(int64_t)e * nblk + (lig >> 1)];
+        cw[j] = *reinterpret_cast<const uint3*>(crow0 + (int64_t)e * row_bytes + (int64_t)c * 12);
+        sc[j] = srow0[(int64_t)e * nblk + (c >> 1)];
       }
     }
-  }
+  };
+  // First batch of code loads before the router, so the two latencies overlap.
+  if (valid && ch < C) load_batch(ch, 0);
 
-  float gate[NP];
+  // Gates of the block's tokens into gsh[token][expert].
   if constexpr (kMfmaRouter) {
     router_mfma_bf16<NP>(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r),
                          t0, T_, tpb, D, N, red, gsh);
-#pragma unroll
-    for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
   } else {
     float part[NP];
     router_partials<TH, NP, true>(h + tt * D, w_r, D, N, lig, G, valid, part);
-    group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+    float gate[NP];
+    group_gates<NP, G>(part, gate, N, lig, red + grp * NP);
+    if (lig == 0) {
+#pragma unroll
+      for (int e = 0; e < NP; ++e) gsh[grp * NP + e] = gate[e];
+    }
+    __syncthreads();
   }
   if (!valid) return;
 
-  for (int k = 0; k * G + lig < C; ++k) {
-    const int c = k * G + lig;
+  for (int k = 0; k * CP + ch < C; ++k) {
+    const int c = k * CP + ch;
     float acc[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) acc[j] = 0.f;
+    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int e0 = 0; e0 < NP; e0 += EC) {
-      if (k != 0 || e0 != 0) {
+    for (int j0 = 0; j0 < EPL; j0 += EC) {
+      if (k != 0 || j0 != 0) load_batch(c, j0);
 #pragma unroll
-        for (int e = 0; e < EC; ++e) {
-          if (e0 + e < N) {
-            cw[e] = *reinterpret_cast<const uint3*>(crow0 + (int64_t)(e0 + e) * row_bytes +
-                                                    (int64_t)c * 12);
-            sc[e] = srow0[(int64_t)(e0 + e) * nblk + (c >> 1)];
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < EC; ++e) {
-        if (e0 + e < N) {
-          const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[e]);
-          const float ws = gate[e0 + e] * s;
-          const uint32_t w[3] = {cw[e].x, cw[e].y, cw[e].z};
+      for (int j = 0; j < EC; ++j) {
+        const int e = (j0 + j) * S + sp;
+        if (e < N) {
+          const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j]);
+          const float ws = gsh[grp * NP + e] * sv;
+          const uint32_t w[3] = {cw[j].x, cw[j].y, cw[j].z};
 #pragma unroll
           for (int i = 0; i < 32; ++i) {
             const int pos = 3 * i, wd = pos >> 5, off = pos & 31;
@@ -376,10 +414,15 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
         }
       }
     }
-    float* yo = y + tt * D + (int64_t)c * 32;
+    SplitReduce<CP, S>::run(acc, sp);
+    float* yo = y + tt * D + (int64_t)c * 32 + SplitReduce<CP, S>::offset(sp);
+    if constexpr (OUT >= 4) {
 #pragma unroll
-    for (int j = 0; j < 32; j += 4)
-      stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+      for (int j = 0; j < OUT; j += 4) stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < OUT; ++j) __builtin_nontemporal_store(acc[j], yo + j);
+    }
   }
 }
 
@@ -464,22 +507,23 @@ hipError_t launch_lookup_combine(const int64_t* ids, const void* h, const void* 
                 : dispatch_dense_np<uint16_t, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s);
 }
 
-template <typename TH, int NP, int G>
+template <typename TH, int NP, int CP>
 static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
                              const uint16_t* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
+  constexpr int S = 64 / CP < NP ? 64 / CP : NP;  // expert splits per token
+  constexpr int G = CP * S;
   const int tpb = pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;
-  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, G>), dim3((unsigned)blocks), dim3(G * tpb), 0, s,
-                     ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N);
+  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S>), dim3((unsigned)blocks), dim3(G * tpb), 0,
+                     s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N);
   return hipGetLastError();
 }
 
 template <typename TH, int NP>
-static hipError_t dispatch_nf3_g(int G, const int64_t* ids, const void* h, const void* w_r,
-                                 const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
-                                 int D, int N, hipStream_t s) {
-  switch (G) {
-    case 4: return launch_nf3<TH, NP, 4>(ids, h, w_r, codes, scales, y, T, D, N, s);
+static hipError_t dispatch_nf3_cp(int CP, const int64_t* ids, const void* h, const void* w_r,
+                                  const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                  int D, int N, hipStream_t s) {
+  switch (CP) {
     case 8: return launch_nf3<TH, NP, 8>(ids, h, w_r, codes, scales, y, T, D, N, s);
     case 16: return launch_nf3<TH, NP, 16>(ids, h, w_r, codes, scales, y, T, D, N, s);
     case 32: return launch_nf3<TH, NP, 32>(ids, h, w_r, codes, scales, y, T, D, N, s);
@@ -488,17 +532,17 @@ static hipError_t dispatch_nf3_g(int G, const int64_t* ids, const void* h, const
 }
 
 template <typename TH>
-static hipError_t dispatch_nf3_np(int NP, int G, const int64_t* ids, const void* h, const void* w_r,
+static hipError_t dispatch_nf3_np(int NP, int CP, const int64_t* ids, const void* h, const void* w_r,
                                   const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
                                   int D, int N, hipStream_t s) {
   switch (NP) {
-    case 1: return dispatch_nf3_g<TH, 1>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 2: return dispatch_nf3_g<TH, 2>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 4: return dispatch_nf3_g<TH, 4>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 8: return dispatch_nf3_g<TH, 8>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 16: return dispatch_nf3_g<TH, 16>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 32: return dispatch_nf3_g<TH, 32>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
-    default: return dispatch_nf3_g<TH, 64>(G, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 1: return dispatch_nf3_cp<TH, 1>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 2: return dispatch_nf3_cp<TH, 2>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 4: return dispatch_nf3_cp<TH, 4>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 8: return dispatch_nf3_cp<TH, 8>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 16: return dispatch_nf3_cp<TH, 16>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 32: return dispatch_nf3_cp<TH, 32>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    default: return dispatch_nf3_cp<TH, 64>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
   }
 }
 
@@ -507,10 +551,10 @@ hipError_t launch_lookup_combine_nf3(const int64_t* ids, const void* h, const vo
                                      int64_t T, int64_t D, int64_t N, int dtype_h, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int NP = next_pow2((int)N);
-  const int G = pick_group((int)(D / 32), 4, 64);
+  const int CP = pick_group((int)(D / 32), 8, 64);  // lanes per expert split: chunks of a row
   if (dtype_h == kF32)
-    return dispatch_nf3_np<float>(NP, G, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
-  return dispatch_nf3_np<uint16_t>(NP, G, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
+    return dispatch_nf3_np<float>(NP, CP, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
+  return dispatch_nf3_np<uint16_t>(NP, CP, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
 }
 
 void nf3_levels_host(float* out) {
