@@ -12,20 +12,25 @@
 // Both are "NT" products C = A . B^T with A and B stored K-contiguous, so
 // the MFMA operands come straight from K-contiguous rows.  Kernel: 256x256
 // output tile per 256-thread workgroup, 4 waves in a 2x2 arrangement, each
-// owning a 128x128 sub-tile of v_mfma_f32_32x32x16_bf16 accumulators; the
+// owning a 128x128 sub-tile of v_mfma_f32_32x32x16_bf16 accumulators.  The
 // K loop streams 64-wide slices of A and B through a double-buffered LDS
 // ring (row = 128 bytes; 16-byte segment s of row r stored at s ^ ((r/2) & 7):
 // the LDS serves 256 bytes (64 banks) per cycle, so the 16 lanes of one
 // ds_read_b128 pass -- 16 consecutive rows -- and the 16 lanes of a staging
-// write -- 2 rows x 8 segments -- each hit 16 distinct 16-byte bank groups),
-// with the
-// next slice's global loads and the next K step's fragment reads in flight
-// during the current MFMAs (an explicit interleave of MFMA, LDS and global
-// instructions).  Operands are read through buffer resources, so rows past
-// the matrix edge read zeros and the K loop has no branches.  Tiles are
-// ordered per GEMM (see tile_of_block).  The
-// GEMM-1 epilogue evaluates GELU with a polynomial normal CDF (see
-// gelu_poly).
+// write -- 2 rows x 8 segments -- each hit 16 distinct 16-byte bank groups).
+// Each thread stages 16 segments per slice in registers; the software
+// pipeline writes one staged segment to LDS and at once re-issues its load
+// for the slice after next, spread over the MFMAs of a K step, so every
+// global load has a full slice of MFMA work to arrive, and the fragments of
+// K step s+1 are read from LDS while the MFMAs of step s run.  The order of
+// MFMA, LDS and global instructions is pinned with scheduling fences (left
+// to itself the compiler sank the loads to the end of the loop, exposing
+// their latency every slice).  Operands are read through buffer resources,
+// so rows past the matrix edge read zeros and the K loop has no branches.
+// Tiles are ordered per GEMM (see tile_of_block).  The GEMM-1 epilogue
+// evaluates GELU with a polynomial normal CDF (see gelu_poly); output tiles
+// whose rows lie far apart in memory (the LUT, row stride N*D) are staged in
+// LDS and written as whole row segments (see EpiMode).
 //
 // fp32 path (small tables): one workgroup per (v, e) row: stage Emb[v] in
 // LDS, each thread forms hidden units u[f] with fp32 FMAs and exact-form
@@ -68,7 +73,14 @@ __device__ __forceinline__ float gelu_poly(float u) {
   return u * phi;
 }
 
-enum { kEpiStore = 0, kEpiGelu = 1 };
+// Epilogue modes.  Direct: each lane stores 4 consecutive bf16 (8 bytes) of
+// one row; the 32 rows of a store instruction are merged into full cache
+// lines in L2 when rows are close together.  Staged: the tile goes through
+// LDS and each wave writes two whole 512-byte row segments per instruction;
+// measured faster once output rows are >= 16 KB apart (the LUT of the larger
+// configurations), slower for narrow rows (two extra barriers).
+enum { kEpiStore = 0, kEpiGelu = 1, kEpiStoreStaged = 2 };
+constexpr int64_t kStagedMinRowBytes = 16384;
 
 constexpr int kBK = 64;     // K slice per LDS stage (64 bf16 = 128 bytes per row)
 constexpr int kXcds = 8;    // MI355X: 8 accelerator complex dies, each with its own L2
@@ -124,20 +136,23 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// Scheduling-group masks (LLVM AMDGPU sched_group_barrier).
-constexpr int kSgMfma = 0x008, kSgVmemRd = 0x020, kSgDsRd = 0x100, kSgDsWr = 0x200;
-
 // C[m][n] = epi( sum_k A[m*lda + k] * B[n*ldb + k] ), bf16 in, fp32
 // accumulation, bf16 out; batch index z offsets A, B, C by sAz, sBz, sCz.
-// Requires K % 8 == 0 and N % 4 == 0 (16-byte K segments, 8-byte stores).
+// Requires K % 8 == 0 and N % 8 == 0 (16-byte K segments and output chunks).
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;     // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;   // MFMA tiles per wave
   constexpr int SA = BM * 8 / 256, SB = BN * 8 / 256;  // 16-byte segments per thread
+  constexpr int NS = SA + SB;                 // staging slots per thread
   constexpr int KS = kBK / 16;                // MFMA K steps per LDS stage
-  static_assert(KS == 4, "the software pipeline below is written for 4 K steps per stage");
-  __shared__ uint4 smem[2][(BM + BN) * 8];
+  static_assert(KS == 4 && TM == 4 && TN == 4 && NS == 16,
+                "the software pipeline below is written for 4 K steps of 4x4 MFMA tiles and 16 slots");
+  constexpr int kRing = (BM + BN) * 8;        // uint4 per LDS stage
+  constexpr int kCPitch = BN / 8 + 1;         // staged output row pitch in uint4 (16-byte pad)
+  constexpr int kLds = (EPI == kEpiStoreStaged && BM * kCPitch > 2 * kRing) ? BM * kCPitch : 2 * kRing;
+  __shared__ uint4 lds[kLds];
+  auto smem = reinterpret_cast<uint4(*)[kRing]>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -154,35 +169,31 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.B + z * p.sBz + (int64_t)n0 * p.ldb), (short)0, (int)(rows_b * p.ldb * 2), kRsrcWord3);
 
-  // Staging: thread t moves 16-byte segment (t & 7) of rows t/8 + 32 i.
+  // Staging slot s (0..15) of thread t: 16-byte segment (t & 7) of A row
+  // t/8 + 32 s (s < 8) or of B row t/8 + 32 (s - 8).
   const int seg = tid & 7;
   const int srow = tid >> 3;
-  const int pseg = seg ^ ((srow >> 1) & 7);  // XOR swizzle ((row >> 1) & 7 is the same for all i)
-  uint32_t offa[SA], offb[SB];
+  const int pseg = seg ^ ((srow >> 1) & 7);  // XOR swizzle ((row >> 1) & 7 is the same for all slots)
+  uint32_t off[NS];
 #pragma unroll
-  for (int i = 0; i < SA; ++i) {
-    const int row = srow + 32 * i;
-    offa[i] = row < rows_a ? (uint32_t)(row * p.lda * 2 + seg * 16) : kOob;
+  for (int s = 0; s < NS; ++s) {
+    const bool is_a = s < SA;
+    const int row = srow + 32 * (is_a ? s : s - SA);
+    const int lim = is_a ? rows_a : rows_b;
+    const int64_t ld = is_a ? p.lda : p.ldb;
+    off[s] = row < lim ? (uint32_t)(row * ld * 2 + seg * 16) : kOob;
   }
-#pragma unroll
-  for (int i = 0; i < SB; ++i) {
-    const int row = srow + 32 * i;
-    offb[i] = row < rows_b ? (uint32_t)(row * p.ldb * 2 + seg * 16) : kOob;
-  }
-
-  uint4 ra[SA], rb[SB];
-  auto gload = [&](int k0) {
-    const bool kok = k0 + seg * 8 < K;
-#pragma unroll
-    for (int i = 0; i < SA; ++i) ra[i] = buf_load16(ra_rs, kok ? offa[i] + k0 * 2 : kOob);
-#pragma unroll
-    for (int i = 0; i < SB; ++i) rb[i] = buf_load16(rb_rs, kok ? offb[i] + k0 * 2 : kOob);
+  uint4 rs[NS];
+  // Load slot s of K slice `slice` (past K: zeros).
+  auto lslot = [&](int s, int slice) {
+    const int k0 = slice * kBK;
+    const uint32_t o = (k0 + seg * 8 < K) ? off[s] + (uint32_t)k0 * 2u : kOob;
+    rs[s] = buf_load16(s < SA ? ra_rs : rb_rs, o);
   };
-  auto swrite = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < SA; ++i) smem[st][(srow + 32 * i) * 8 + pseg] = ra[i];
-#pragma unroll
-    for (int i = 0; i < SB; ++i) smem[st][(BM + srow + 32 * i) * 8 + pseg] = rb[i];
+  // Write slot s into LDS stage st.
+  auto wslot = [&](int s, int st) {
+    const int row = (s < SA ? 0 : BM) + srow + 32 * (s < SA ? s : s - SA);
+    smem[st][row * 8 + pseg] = rs[s];
   };
   // Fragments of one 16-wide K step: lane l reads row l%32 of each 32-row
   // MFMA tile, 8 consecutive k at 8*(l/32) (swizzled segment).
@@ -208,97 +219,131 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Operands swapped (B tile as the matrix-core "A"): lane l then holds
-  // C[m = l%32][n = 8*(r/4) + 4*(l/32) + r%4] in accumulator r, i.e. four
-  // consecutive n per group of four registers.
-  auto mfmas = [&](const uint4* a, const uint4* b) {
+  // The 16 MFMAs of one K step.  Operands swapped (B tile as the
+  // matrix-core "A"): lane l then holds C[m = l%32][n = 8*(r/4) + 4*(l/32) +
+  // r%4] in accumulator r, i.e. four consecutive n per group of four
+  // registers.  After MFMAs 1, 5, 9 and 13, staging slot s0 + q goes to LDS
+  // stage wst and is re-loaded from K slice `slice`.
+  auto mfma_step = [&](const uint4* a, const uint4* b, int s0, int wst, int slice) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
-                                                             __builtin_bit_cast(bf16x8_t, a[i]),
-                                                             acc[i][j], 0, 0, 0);
+    for (int x = 0; x < TM * TN; ++x) {
+      const int i = x / TN, j = x % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
+                                                           __builtin_bit_cast(bf16x8_t, a[i]), acc[i][j], 0, 0, 0);
+      if (x % 4 == 1) {
+        wslot(s0 + x / 4, wst);
+        lslot(s0 + x / 4, slice);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
+  // Pipeline invariant at the top of iteration kt (cur = kt & 1): LDS stage
+  // cur holds slice kt; LDS stage cur^1 holds slots 0-3 of slice kt+1; the
+  // registers of slots 4-15 hold (or are loading) slice kt+1 and those of
+  // slots 0-3 slice kt+2; fa[0]/fb[0] hold K step 0 of slice kt.  Slots
+  // 4-15 of slice kt+1 are written during K steps 0-2 (stage cur^1 was last
+  // read before the previous barrier); after the barrier, K step 3 writes
+  // slots 0-3 of slice kt+2 into stage cur, which every wave has finished
+  // reading.
   const int nk = (K + kBK - 1) / kBK;
-  gload(0);
-  swrite(0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) lslot(s, 0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) wslot(s, 0);
+#pragma unroll
+  for (int s = 0; s < NS; ++s) lslot(s, 1);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    wslot(s, 1);
+    lslot(s, 2);
+  }
   __syncthreads();
   uint4 fa[2][TM], fb[2][TN];
   fload(0, 0, fa[0], fb[0]);
+  __builtin_amdgcn_sched_barrier(0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    // Loads of the next stage (past K they read zeros, so the last
-    // iteration needs no branch); fragments of K step s+1 are read while
-    // the MFMAs of step s run; the staged next slice is written to the other
-    // LDS buffer during the last step.
-    gload((kt + 1) * kBK);
-    fload(st, 1, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
-#pragma unroll
-    for (int i = 0; i < TM + TN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRd, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgVmemRd, (SA + SB) / (TM + TN), 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, TM * TN - (TM + TN), 0);
-    fload(st, 2, fa[0], fb[0]);
-    mfmas(fa[1], fb[1]);
-#pragma unroll
-    for (int i = 0; i < TM + TN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRd, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, TM * TN - (TM + TN), 0);
-    fload(st, 3, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
-#pragma unroll
-    for (int i = 0; i < TM + TN; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRd, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, TM * TN - (TM + TN), 0);
-    swrite(st ^ 1);
-    mfmas(fa[1], fb[1]);
-#pragma unroll
-    for (int i = 0; i < SA + SB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsWr, 1, 0);
-    }
+    const int cur = kt & 1;
+    fload(cur, 1, fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(fa[0], fb[0], 4, cur ^ 1, kt + 2);
+    fload(cur, 2, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(fa[1], fb[1], 8, cur ^ 1, kt + 2);
+    fload(cur, 3, fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(fa[0], fb[0], 12, cur ^ 1, kt + 2);
     __syncthreads();
-    fload(st ^ 1, 0, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    fload(cur ^ 1, 0, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(fa[1], fb[1], 0, cur, kt + 3);
   }
 
-  // Epilogue: (GELU), round to bf16, 8-byte stores of 4 consecutive columns
-  // through a buffer resource over this tile's rows (rows past M and column
-  // groups past N take an out-of-range offset and are dropped).
   const int rows_c = M - m0 < BM ? M - m0 : BM;
   const __amdgpu_buffer_rsrc_t rc_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.C + z * p.sCz + (int64_t)m0 * p.ldc), (short)0, (int)(rows_c * p.ldc * 2), kRsrcWord3);
+  // (GELU,) round to bf16, pack 4 consecutive columns into 8 bytes.
+  auto packed = [&](int i, int j, int g) {
+    float v[4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int mr = wm * WM + i * 32 + (lane & 31);  // row within the tile
+    for (int q = 0; q < 4; ++q) {
+      v[q] = acc[i][j][4 * g + q];
+      if constexpr (EPI == kEpiGelu) v[q] = gelu_poly(v[q]);
+    }
+    const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v[0]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
+    const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)v[2]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
+    return make_uint2(lo, hi);
+  };
+  if constexpr (EPI != kEpiStoreStaged) {
+    // Direct: 8-byte stores through a buffer resource over this tile's rows
+    // (rows past M and column groups past N take an out-of-range offset and
+    // are dropped).
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int i = 0; i < TM; ++i) {
+      const int mr = wm * WM + i * 32 + (lane & 31);  // row within the tile
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-        float v[4];
+      for (int j = 0; j < TN; ++j) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = acc[i][j][4 * g + q];
-          if constexpr (EPI == kEpiGelu) v[q] = gelu_poly(v[q]);
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          const uint32_t o = (mr < rows_c && n < N) ? (uint32_t)(mr * p.ldc * 2 + n * 2) : kOob;
+          __builtin_amdgcn_raw_buffer_store_b64(
+              __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, packed(i, j, g)), rc_rs, (int)o,
+              0, 0);
         }
-        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v[0]) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
-        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)v[2]) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
-        const uint32_t off = (mr < rows_c && n < N) ? (uint32_t)(mr * p.ldc * 2 + n * 2) : kOob;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int,
-                                                                 make_uint2(lo, hi)),
-                                              rc_rs, (int)off, 0, 0);
       }
+    }
+  } else {
+    // Staged: the tile goes to LDS (row pitch BN*2 + 16 bytes), then each
+    // wave writes two whole tile rows per 16-byte store instruction.
+    __syncthreads();  // every wave is done with the operand ring
+    uint32_t* cs = reinterpret_cast<uint32_t*>(lds);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int mr = wm * WM + i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nc = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          *reinterpret_cast<uint2*>(cs + mr * (kCPitch * 4) + nc / 2) = packed(i, j, g);
+        }
+    }
+    __syncthreads();
+    constexpr int kChunks = BN / 8;  // 16-byte chunks per tile row
+    constexpr int kRowsPerPass = 256 / kChunks;
+    const int ch = tid % kChunks;
+    const int n = n0 + ch * 8;
+#pragma unroll 4
+    for (int r0 = 0; r0 < BM; r0 += kRowsPerPass) {
+      const int row = r0 + tid / kChunks;
+      const uint4 d = lds[row * kCPitch + ch];
+      const uint32_t o = (row < rows_c && n < N) ? (uint32_t)(row * p.ldc * 2 + n * 2) : kOob;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, d),
+                                             rc_rs, (int)o, 0, 0);
     }
   }
 }
@@ -348,8 +393,12 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
     hipError_t err = launch_gemm<kBM, kBN, kEpiGelu>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc,
                                                       (int)NF, (int)D, 1, /*xcd_order=*/0, s);
     if (err != hipSuccess) return err;
-    err = launch_gemm<kBM, kBN, kEpiStore>(G, NF, F, w_down, F, D * F, lut + v0 * N * D, N * D, D,
-                                           (int)mc, (int)D, (int)F, (int)N, /*xcd_order=*/1, s);
+    if (N * D * 2 >= kStagedMinRowBytes)
+      err = launch_gemm<kBM, kBN, kEpiStoreStaged>(G, NF, F, w_down, F, D * F, lut + v0 * N * D, N * D, D,
+                                                   (int)mc, (int)D, (int)F, (int)N, /*xcd_order=*/1, s);
+    else
+      err = launch_gemm<kBM, kBN, kEpiStore>(G, NF, F, w_down, F, D * F, lut + v0 * N * D, N * D, D,
+                                             (int)mc, (int)D, (int)F, (int)N, /*xcd_order=*/1, s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

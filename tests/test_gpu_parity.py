@@ -326,8 +326,12 @@ def bf16_layer(seed, V, D, F, N, std=0.02):
     return synth.Layer(f((V, D), std), f((N, F, D), std), f((N, D, F), std), f((N, D), std))
 
 
+# The last two cases have LUT rows >= 16 KB apart (N*D*2), which takes the
+# LDS-staged output path of the second GEMM; (520, 1000, 136, 9) also has
+# ragged row, column and K tiles in both GEMMs.
 @pytest.mark.parametrize("V,D,F,N,std", [(600, 256, 512, 2, 0.02), (333, 72, 136, 3, 0.5),
-                                         (256, 512, 256, 1, 0.1), (1000, 128, 1024, 4, 0.02)])
+                                         (256, 512, 256, 1, 0.1), (1000, 128, 1024, 4, 0.02),
+                                         (700, 1024, 256, 8, 0.03), (520, 1000, 136, 9, 0.1)])
 def test_build_bf16_small_all_rows(V, D, F, N, std):
     layer = bf16_layer(V + D + F + N, V, D, F, N, std)
     lut = host(run_build(layer))
