@@ -18,8 +18,10 @@
 //     reduce-scatter (xor shuffles) plus one LDS exchange;
 //   * gather/combine: lane `l` of the group streams chunks l, l+G, ... of
 //     every expert row of the token's contiguous slab LUT[id] with 16-byte
-//     loads (the first batch of slab loads is issued before the router so
-//     the two latencies overlap) and accumulates in fp32.
+//     loads and accumulates in fp32.  The router's operands are loaded
+//     first and the first batch of slab loads right after, so the router
+//     waits only for its own operands and the slab arrives during the
+//     router's arithmetic.
 #include "mole_device.hpp"
 #include "mole_kernels.hpp"
 
@@ -78,77 +80,118 @@ constexpr int kMaxTokPerBlock = 16;  // one 16-row MFMA tile of tokens
 // accumulation), then gates = softmax over e < N into gsh[t][NP].  Lane l
 // of a wave supplies token row l%16 (A) and expert column l%16 (B) with the
 // 8 consecutive d values of k-group l/16; the waves take every nw-th 32-wide
-// K step.  Contains barriers: every thread of the block must call it.
+// K step, in batches of UB steps whose loads are all issued before the
+// MFMAs that consume them (one memory round trip per batch).
+//
+// Two phases, because vector-memory counters retire in issue order: the
+// kernel calls load_first() before issuing its table loads, so the router
+// waits only for its own operands (not for the table rows queued behind
+// them), and finish() after; the table loads stay in flight through the
+// router's arithmetic and barriers.  finish() contains barriers: every
+// thread of the block must call it.
 template <int NP>
-__device__ __forceinline__ void router_mfma_bf16(const uint16_t* __restrict__ h,
-                                                 const uint16_t* __restrict__ w_r, int64_t t0,
-                                                 int64_t T_, int tpb, int D, int N,
-                                                 float* red /* [4][16][NPAD] */,
-                                                 float* gsh /* [16][NP] */) {
-  constexpr int NT = (NP + 15) / 16, NPAD = NT * 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int row = lane & 15, kg = lane >> 4;
-  const int64_t tok = t0 + row;
-  const bool tok_ok = row < tpb && tok < T_;
-  const uint16_t* hrow = h + (tok_ok ? tok : 0) * (int64_t)D;
+struct MfmaRouter {
+  static constexpr int NT = (NP + 15) / 16, NPAD = NT * 16;
+  static constexpr int UB = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
+  uint4 a[UB], b[UB][NT];
   f32x4_t acc[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int ksteps = (D + 31) / 32;
-  // Batches of UB K-steps per wave: all their loads are issued before the
-  // MFMAs that consume them, so a batch costs one memory round trip.
-  constexpr int UB = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
-  for (int base = wave; base < ksteps; base += UB * nw) {
-    uint4 a[UB], b[UB][NT];
+  const uint16_t* hrow;
+  const uint16_t* w_r;
+  int D, N, ksteps, nw, wave, row, kg;
+  bool tok_ok;
+
+  // Every load is issued unconditionally from an in-bounds (clamped)
+  // address and masked to zero only where it is consumed (mma, which
+  // recomputes the masks): loads under a divergent branch would leave the
+  // compiler unsure how many loads are outstanding at the join, and a select
+  // right after a load would make it wait there -- either way it would wait
+  // for the table rows issued after the router's operands.
+  __device__ __forceinline__ bool k_ok(int base, int u) const {
+    const int ks = base + u * nw;
+    return ks < ksteps && ks * 32 + kg * 8 < D;
+  }
+  __device__ __forceinline__ void load(int base) {
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
-      const int ks = base + u * nw;
-      const int k = ks * 32 + kg * 8;
-      const bool kok = ks < ksteps && k < D;
-      a[u] = (tok_ok && kok) ? ldg16(hrow + k) : make_uint4(0, 0, 0, 0);
+      const int kc = k_ok(base, u) ? (base + u * nw) * 32 + kg * 8 : 0;
+      a[u] = ldg16(hrow + kc);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int e = nt * 16 + row;
-        b[u][nt] = (e < N && kok) ? ldg16(w_r + (int64_t)e * D + k) : make_uint4(0, 0, 0, 0);
+        b[u][nt] = ldg16(w_r + (int64_t)(e < N ? e : N - 1) * D + kc);
       }
     }
+  }
+  __device__ __forceinline__ void mma(int base) {
+    const uint4 zero = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < UB; ++u)
+    for (int u = 0; u < UB; ++u) {
+      const bool kok = k_ok(base, u);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[u]),
-                                                          __builtin_bit_cast(bf16x8_t, b[u][nt]), acc[nt],
-                                                          0, 0, 0);
-  }
-  // lane l holds logits of tokens 4*(l/16) + r, expert nt*16 + l%16
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kg + r) * NPAD + nt * 16 + row] = acc[nt][r];
-  __syncthreads();
-  if ((int)threadIdx.x < tpb) {
-    const int tk = threadIdx.x;
-    float z[NP];
-    float zmax = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < NP; ++e) {
-      float s = 0.f;
-      for (int w = 0; w < nw; ++w) s += red[(w * 16 + tk) * NPAD + e];
-      z[e] = s;
-      if (e < N) zmax = fmaxf(zmax, s);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, (tok_ok && kok) ? a[u] : zero),
+            __builtin_bit_cast(bf16x8_t, (nt * 16 + row < N && kok) ? b[u][nt] : zero), acc[nt], 0, 0, 0);
     }
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < NP; ++e) {
-      z[e] = (e < N) ? expf(z[e] - zmax) : 0.f;
-      sum += z[e];
-    }
-    const float inv = 1.f / sum;
-#pragma unroll
-    for (int e = 0; e < NP; ++e) gsh[tk * NP + e] = z[e] * inv;
   }
-  __syncthreads();
-}
+  __device__ __forceinline__ void load_first(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
+                                             int64_t t0, int64_t T_, int tpb, int D_, int N_) {
+    lane_setup(h, w, t0, T_, tpb, D_, N_);
+    load(wave);
+  }
+  __device__ __forceinline__ void lane_setup(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
+                                             int64_t t0, int64_t T_, int tpb, int D_, int N_) {
+    const int lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    nw = blockDim.x >> 6;
+    row = lane & 15;
+    kg = lane >> 4;
+    D = D_;
+    N = N_;
+    w_r = w;
+    const int64_t tok = t0 + row;
+    tok_ok = row < tpb && tok < T_;
+    hrow = h + (tok_ok ? tok : 0) * (int64_t)D;
+    ksteps = (D + 31) / 32;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void finish(int tpb, float* red /* [4][16][NPAD] */, float* gsh /* [16][NP] */) {
+    mma(wave);
+    for (int base = wave + UB * nw; base < ksteps; base += UB * nw) {
+      load(base);
+      mma(base);
+    }
+    // lane l holds logits of tokens 4*(l/16) + r, expert nt*16 + l%16
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kg + r) * NPAD + nt * 16 + row] = acc[nt][r];
+    __syncthreads();
+    if ((int)threadIdx.x < tpb) {
+      const int tk = threadIdx.x;
+      float z[NP];
+      float zmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < NP; ++e) {
+        float s = 0.f;
+        for (int w = 0; w < nw; ++w) s += red[(w * 16 + tk) * NPAD + e];
+        z[e] = s;
+        if (e < N) zmax = fmaxf(zmax, s);
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < NP; ++e) {
+        z[e] = (e < N) ? expf(z[e] - zmax) : 0.f;
+        sum += z[e];
+      }
+      const float inv = 1.f / sum;
+#pragma unroll
+      for (int e = 0; e < NP; ++e) gsh[tk * NP + e] = z[e] * inv;
+    }
+    __syncthreads();
+  }
+};
 
 // Reduce the partial logits of a token group and turn them into softmax
 // gates held (identically) by every lane of the group.  Must be reached by
@@ -213,27 +256,37 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   const bool valid = t < T_;
   const int64_t tt = valid ? t : 0;
   const int C = D / CH;
-  const int64_t id = valid ? ids[tt] : 0;
+  const int64_t id_ld = ids[tt];  // unconditional (tt is clamped): see MfmaRouter::load
+  __builtin_amdgcn_sched_barrier(0);  // the id load goes out first: the table address waits on it alone
+  const int64_t id = valid ? id_ld : 0;
   const T* slab = lut + id * (int64_t)N * D;
 
-  // First batch of slab loads (chunk lig, experts 0..EC-1), before the router.
+  // Router operands first, then the first batch of slab loads (chunk lig,
+  // experts 0..EC-1); the router's arithmetic runs while the slab arrives.
+  MfmaRouter<NP> rt;
+  if constexpr (kMfmaRouter)
+    rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
+                  N);
+  __builtin_amdgcn_sched_barrier(0);
+  // (Unconditional loads from clamped chunk and expert indices; lanes past
+  // the row and experts past N read data they then ignore.)
   uint4 sv[EC];
   float sf[EC];
-  const bool have0 = valid && lig < C;
-  if (have0) {
+  {
+    const int c0 = lig < C ? lig : C - 1;
 #pragma unroll
     for (int e = 0; e < EC; ++e) {
-      if (e < N) {
-        if constexpr (VECTOR) sv[e] = ldg16(slab + (int64_t)e * D + (int64_t)lig * CH);
-        else sf[e] = Elem<T>::load1(slab, (int64_t)e * D + lig);
-      }
+      const int ec = e < N ? e : N - 1;
+      if constexpr (VECTOR) sv[e] = ldg16(slab + (int64_t)ec * D + (int64_t)c0 * CH);
+      else sf[e] = Elem<T>::load1(slab, (int64_t)ec * D + c0);
     }
   }
 
+  __builtin_amdgcn_sched_barrier(0);
+
   float gate[NP];
   if constexpr (kMfmaRouter) {
-    router_mfma_bf16<NP>(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r),
-                         t0, T_, tpb, D, N, red, gsh);
+    rt.finish(tpb, red, gsh);
 #pragma unroll
     for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
   } else {
@@ -368,13 +421,19 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
       }
     }
   };
-  // First batch of code loads before the router, so the two latencies overlap.
+  // First batch of code loads, then the router's operands.  (The reverse
+  // order, as in the dense kernel, needs branch-free code loads, which cost
+  // this kernel about 25 registers and one wave per SIMD of occupancy, more
+  // than the overlap gains: a token's codes are only N*(3D/8 + D/32) bytes.)
   if (valid && ch < C) load_batch(ch, 0);
+  MfmaRouter<NP> rt;
+  if constexpr (kMfmaRouter)
+    rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
+                  N);
 
   // Gates of the block's tokens into gsh[token][expert].
   if constexpr (kMfmaRouter) {
-    router_mfma_bf16<NP>(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r),
-                         t0, T_, tpb, D, N, red, gsh);
+    rt.finish(tpb, red, gsh);
   } else {
     float part[NP];
     router_partials<TH, NP, true>(h + tt * D, w_r, D, N, lig, G, valid, part);
