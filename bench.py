@@ -262,6 +262,7 @@ def main():
     if not args.no_scale_probe and bf16:
         torch.cuda.synchronize()
         result["combine_at_scale"] = scale_probe(torch, mole, synth, dev, stream)
+        result["decode_stack_1b"] = decode_stack_probe(torch, mole, synth, dev, stream)
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(args, w, layer, ids_h[0], synth, T)
@@ -320,6 +321,79 @@ def scale_probe(torch, mole, synth, dev, stream):
     torch.cuda.synchronize()
     ctx.__exit__(None, None, None)
     del lut, codes, scales
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_stack_probe(torch, mole, synth, dev, stream):
+    """Decode through the 1B-class stack: 16 layers, each with its own
+    50304 x 16 x 2048 bf16 table (3.3 GB, 52.7 GB in all) and router, the
+    same token ids at every layer and a fresh hidden state per layer.  One
+    step = the 16 lookup-combines; timed eagerly and as one HIP graph
+    replay, at T = 1, 16, 128 and 1024 Zipf(1.1) ids."""
+    w = synth.WORKLOADS["1b"]
+    V, D, N, L = w.V, w.D, w.N, w.layers
+    ctx = torch.cuda.stream(stream)
+    ctx.__enter__()
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.seed(w, 70))
+    luts, w_rs = [], []
+    for _ in range(L):
+        luts.append((torch.randn((V, N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+        w_rs.append((torch.randn((N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16))
+    perm = synth.rank_permutation(w)
+    out = {"workload": "1B-class stack: %d layers x table V=%d N=%d D=%d bf16 (%.1f GB in all)"
+           % (L, V, N, D, L * V * N * D * 2 / 1e9)}
+    for T in w.tokens:
+        NB = 4
+        ids_l = [torch.from_numpy(synth.make_ids(w, T, step=s, perm=perm)).to(dev) for s in range(NB)]
+        h_l = [[torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+               for _ in range(NB)]
+        y_l = [torch.empty((T, D), dtype=torch.float32, device=dev) for _ in range(L)]
+
+        def stack(b, st):
+            for l in range(L):
+                mole.mole_lookup_combine(ids_l[b], h_l[b][l], w_rs[l], luts[l], y_l[l], stream=st)
+
+        torch.cuda.synchronize()
+        for b in range(3):
+            stack(b % NB, stream)
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            stack(r % NB, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / reps
+        # the same 16 launches captured once per input batch, replayed
+        graphs = []
+        for b in range(NB):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                stack(b, torch.cuda.current_stream())
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        for b in range(NB):
+            graphs[b].replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for r in range(reps):
+            graphs[r % NB].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / reps
+        per_layer = T * (N * D * 2 + D * 2 + 4 * D + 8) + D * N * 2
+        best = min(eager_us, graph_us)
+        out["T%d" % T] = {"eager_us_per_step": eager_us, "graph_us_per_step": graph_us,
+                          "tokens_per_s": T / (best * 1e-6),
+                          "gbs": L * per_layer / (best * 1e-6) / 1e9,
+                          "hbm_frac": L * per_layer / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "bytes_per_step": L * per_layer}
+        del graphs
+    torch.cuda.synchronize()
+    ctx.__exit__(None, None, None)
+    del luts, w_rs
     torch.cuda.empty_cache()
     return out
 

@@ -1,0 +1,208 @@
+// Lookup-combine over a bf16/fp32 table: router softmax + gather of each
+// token's N x D table slab + gate-weighted sum.  (MoLE article, inference
+// section: retrieve each token's expert outputs by token id; training
+// section: the router reads the contextual hidden state and all routed
+// experts are active.)
+//
+// Work decomposition (one launch, no inter-block communication):
+//   * a "group" of G lanes (G a power of two) owns one token; a block holds
+//     up to 16 tokens, fewer when the batch is small so that the grid still
+//     covers the 256 compute units;
+//   * router, bf16: the block's logits [tokens x experts] come from
+//     v_mfma_f32_16x16x32_bf16 tiles (tokens x 16 experts, K = 32 per
+//     instruction), the waves splitting D, so W_r is read once per block;
+//     partial tiles meet in LDS and one thread per token does the
+//     max-subtracted softmax;
+//   * router, fp32 or unaligned: lanes split D into chunks, form per-expert
+//     partial dot products, reduce them across the group with a wavefront
+//     reduce-scatter (xor shuffles) plus one LDS exchange;
+//   * gather/combine: lane `l` of the group streams chunks l, l+G, ... of
+//     every expert row of the token's contiguous slab LUT[id] with 16-byte
+//     loads and accumulates in fp32.  The router's operands are loaded
+//     first and the first batch of slab loads right after, so the router
+//     waits only for its own operands and the slab arrives during the
+//     router's arithmetic.
+#include "combine_common.hpp"
+
+namespace mole {
+
+// ---------------------------------------------------------------------------
+// bf16 / fp32 table
+// ---------------------------------------------------------------------------
+template <typename T, int NP, int G, bool VECTOR, bool LANE>
+__global__ __launch_bounds__(256) void lookup_combine_kernel(
+    const int64_t* __restrict__ ids, const T* __restrict__ h, const T* __restrict__ w_r,
+    const T* __restrict__ lut, float* __restrict__ y, int64_t T_, int D, int N, int tpb) {
+  constexpr int WG = G > kWave ? G / kWave : 1;
+  constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
+  constexpr int CH = VECTOR ? Elem<T>::kVec : 1;  // elements per chunk
+  constexpr int EC = NP < 16 ? NP : 16;           // experts per batch of slab loads
+  // Router: on the matrix cores (bf16, several tokens per block), or on
+  // the vector units with its loads first (one token per block, or fp32),
+  // or element-wise (unaligned rows, or more than 16 experts in fp32).
+  constexpr bool kMfmaRouter = VECTOR && sizeof(T) == 2 && !LANE;
+  constexpr bool kLaneRouter = VECTOR && !kMfmaRouter && NP <= 16;
+  constexpr int NPAD = ((NP + 15) / 16) * 16;
+  __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * WG * NP];
+  __shared__ float gsh[kMfmaRouter ? kMaxTokPerBlock * NP : 1];
+
+  // tpb (tokens per block, = blockDim.x / G) comes as an argument: reading
+  // the block size costs a dependent load of the dispatch packet.
+  const int tid = threadIdx.x;
+  const int grp = tid / G, lig = tid % G;
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  const int64_t t = t0 + grp;
+  const bool valid = t < T_;
+  const int64_t tt = valid ? t : 0;
+  const int C = D / CH;
+  const int64_t id_ld = ids[tt];  // unconditional (tt is clamped): see MfmaRouter::load
+  __builtin_amdgcn_sched_barrier(0);  // the id load goes out first
+
+  // Router operands next, then the first batch of slab loads (chunk lig,
+  // experts 0..EC-1); the router's arithmetic runs while the slab arrives.
+  MfmaRouter<NP> rt;
+  LaneRouter<T, kLaneRouter ? NP : 1> lr;
+  if constexpr (kMfmaRouter)
+    rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
+                  N, (G * tpb) / kWave);
+  if constexpr (kLaneRouter) lr.load_first(h + tt * D, w_r, D, N, lig);
+  __builtin_amdgcn_sched_barrier(0);
+  const int64_t id = valid ? id_ld : 0;  // (the first wait on the id load is here)
+  const T* slab = lut + id * (int64_t)N * D;
+  // (Unconditional loads from clamped chunk and expert indices; lanes past
+  // the row and experts past N read data they then ignore.)
+  uint4 sv[EC];
+  float sf[EC];
+  {
+    const int c0 = lig < C ? lig : C - 1;
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      const int ec = e < N ? e : N - 1;
+      if constexpr (VECTOR) sv[e] = ldg16(slab + (int64_t)ec * D + (int64_t)c0 * CH);
+      else sf[e] = Elem<T>::load1(slab, (int64_t)ec * D + c0);
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  float gate[NP];
+  if constexpr (kMfmaRouter) {
+    rt.finish(tpb, red, gsh);
+#pragma unroll
+    for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
+  } else if constexpr (kLaneRouter) {
+    lr.template finish<G>(h + tt * D, w_r, D, N, lig, valid, gate, red + grp * WG * NP);
+  } else {
+    float part[NP];
+    router_partials<T, NP, VECTOR>(h + tt * D, w_r, D, N, lig, G, valid, part);
+    group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+  }
+  if (!valid) return;
+
+  for (int k = 0; k * G + lig < C; ++k) {
+    const int c = k * G + lig;
+    float acc[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int e0 = 0; e0 < NP; e0 += EC) {
+      if (k != 0 || e0 != 0) {
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {
+          if (e0 + e < N) {
+            if constexpr (VECTOR) sv[e] = ldg16(slab + (int64_t)(e0 + e) * D + (int64_t)c * CH);
+            else sf[e] = Elem<T>::load1(slab, (int64_t)(e0 + e) * D + c);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        if (e0 + e < N) {
+          const float g = gate[e0 + e];
+          if constexpr (VECTOR) {
+            float v[CH];
+            Elem<T>::unpack(sv[e], v);
+#pragma unroll
+            for (int j = 0; j < CH; ++j) acc[j] = fmaf(g, v[j], acc[j]);
+          } else {
+            acc[0] = fmaf(g, sf[e], acc[0]);
+          }
+        }
+      }
+    }
+    float* yo = y + tt * D + (int64_t)c * CH;
+    if constexpr (VECTOR) {
+#pragma unroll
+      for (int j = 0; j < CH; j += 4)
+        stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+    } else {
+      __builtin_nontemporal_store(acc[0], yo);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+template <typename E, int NP, int G, bool VEC>
+static hipError_t launch_dense(const int64_t* ids, const void* h, const void* w_r, const void* lut,
+                               float* y, int64_t T, int D, int N, hipStream_t s) {
+  const int tpb = pick_tokens_per_block(T, G);
+  const int64_t blocks = (T + tpb - 1) / tpb;
+  // One token per block: the vector-unit router (see LaneRouter).
+  if constexpr (VEC && sizeof(E) == 2 && NP <= 16 && G >= 64) {
+    if (tpb == 1) {
+      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, true>), dim3((unsigned)blocks), dim3(G), 0, s, ids,
+                         (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, 1);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, false>), dim3((unsigned)blocks), dim3(G * tpb), 0, s,
+                     ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, tpb);
+  return hipGetLastError();
+}
+
+template <typename E, int NP, bool VEC>
+static hipError_t dispatch_dense_g(int G, const int64_t* ids, const void* h, const void* w_r,
+                                   const void* lut, float* y, int64_t T, int D, int N, hipStream_t s) {
+  switch (G) {
+    case 16: return launch_dense<E, NP, 16, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    case 32: return launch_dense<E, NP, 32, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    case 64: return launch_dense<E, NP, 64, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    case 128: return launch_dense<E, NP, 128, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    default: return launch_dense<E, NP, 256, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+  }
+}
+
+template <typename E, bool VEC>
+static hipError_t dispatch_dense_np(int NP, int G, const int64_t* ids, const void* h, const void* w_r,
+                                    const void* lut, float* y, int64_t T, int D, int N, hipStream_t s) {
+  switch (NP) {
+    case 1: return dispatch_dense_g<E, 1, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 2: return dispatch_dense_g<E, 2, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 4: return dispatch_dense_g<E, 4, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 8: return dispatch_dense_g<E, 8, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 16: return dispatch_dense_g<E, 16, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 32: return dispatch_dense_g<E, 32, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    default: return dispatch_dense_g<E, 64, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+  }
+}
+
+hipError_t launch_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut,
+                                 float* y, int64_t T, int64_t D, int64_t N, int dtype, bool vector_ok,
+                                 hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int NP = next_pow2((int)N);
+  const int elem_bytes = dtype == kF32 ? 4 : 2;
+  const int vec = 16 / elem_bytes;
+  const bool vector = vector_ok && (D % vec == 0);
+  const int C = vector ? (int)(D / vec) : (int)D;
+  const int G = pick_group(C, 16, 256);
+  if (dtype == kF32)
+    return vector ? dispatch_dense_np<float, true>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s)
+                  : dispatch_dense_np<float, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s);
+  return vector ? dispatch_dense_np<uint16_t, true>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s)
+                : dispatch_dense_np<uint16_t, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s);
+}
+
+}  // namespace mole

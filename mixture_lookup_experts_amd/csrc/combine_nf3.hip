@@ -1,0 +1,227 @@
+// Lookup-combine over the 3-bit NF3 table: router softmax + decode of each
+// token's N x D codes (3 bits per element, one fp16 absmax scale per 64
+// elements) + gate-weighted sum.  (MoLE article, results section: the
+// table keeps the model's quality when compressed to 3 bits, e.g. NF3;
+// inference section: each token's expert outputs are fetched by token id.)
+// The routers and the launch-shape helpers are shared with the dense-table
+// kernel.
+#include "combine_common.hpp"
+
+namespace mole {
+
+// NF3 reconstruction levels: the NormalFloat construction at 3 bits (levels
+// Phi^-1 of evenly spaced probabilities, 4 positive, 3 negative, an exact
+// zero, normalised to [-1, 1]), rounded to fp32.  Bit patterns:
+__constant__ uint32_t kNf3LevelBits[8] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
+                                          0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
+
+// ---------------------------------------------------------------------------
+// NF3 table: 32 codes (12 bytes) per chunk, one fp16 scale per 64 elements.
+// A token is owned by G = CP*S lanes: lane (s, c) = s*CP + c decodes chunk c
+// (and c + CP, ... when a row has more than CP chunks) for the experts
+// e = s, s + S, s + 2S, ...; the S partial sums of a chunk then meet in a
+// reduce-scatter over the lanes c, c + CP, ..., so each lane stores 32/S of
+// the chunk's outputs.  Splitting the experts across lanes keeps a full
+// wavefront busy per token at the 160M/410M widths (24-32 chunks per row)
+// and lets every lane issue all of its code loads in one batch.
+// ---------------------------------------------------------------------------
+
+// Halving reduce-scatter of the 32 per-lane sums over the S expert splits:
+// at step b (xor mask CP << b) a lane keeps the half its split bit b
+// selects and adds the partner's copy of it.  Afterwards the lane holds the
+// 32/S sums of elements off(s) .. off(s) + 32/S - 1 of its chunk.
+template <int CP, int S, int B = 0, int CNT = 32>
+struct SplitReduce {
+  __device__ __forceinline__ static void run(float* acc, int sp) {
+    if constexpr ((1 << B) < S) {
+      constexpr int H = CNT / 2;
+      const bool hi = ((sp >> B) & 1) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float keep = hi ? acc[i + H] : acc[i];
+        const float send = hi ? acc[i] : acc[i + H];
+        acc[i] = keep + __shfl_xor(send, CP << B, kWave);
+      }
+      SplitReduce<CP, S, B + 1, H>::run(acc, sp);
+    }
+  }
+  __device__ __forceinline__ static int offset(int sp) {
+    int off = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) < S; ++b)
+      if ((sp >> b) & 1) off += 16 >> b;
+    return off;
+  }
+};
+
+template <typename TH, int NP, int CP, int S>
+__global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
+    const int64_t* __restrict__ ids, const TH* __restrict__ h, const TH* __restrict__ w_r,
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    float* __restrict__ y, int64_t T_, int D, int N, int tpb) {
+  constexpr int G = CP * S;                        // lanes per token (<= 64)
+  static_assert(G <= kWave, "a token's lanes must share one wavefront");
+  constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
+  constexpr int EPL = (NP + S - 1) / S;            // experts per lane
+  constexpr int EC = EPL < 8 ? EPL : 8;            // experts per batch of code loads
+  constexpr int OUT = 32 / S;                      // outputs stored per lane and chunk
+  constexpr bool kMfmaRouter = sizeof(TH) == 2;
+  constexpr int NPAD = ((NP + 15) / 16) * 16;
+  __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * NP];
+  __shared__ float gsh[kMaxTokPerBlock * NP];
+  __shared__ float lv[8];
+
+  const int tid = threadIdx.x;
+  if (tid < 8) lv[tid] = __uint_as_float(kNf3LevelBits[tid]);
+  const int grp = tid / G, lig = tid % G;  // tpb = blockDim.x / G, passed in
+  const int sp = lig / CP, ch = lig % CP;          // expert split, chunk
+  const int64_t t0 = (int64_t)blockIdx.x * tpb;
+  const int64_t t = t0 + grp;
+  const bool valid = t < T_;
+  const int64_t tt = valid ? t : 0;
+  const int C = D / 32;                            // 32-element chunks per row
+  const int64_t row_bytes = 3 * (int64_t)D / 8, nblk = D / 64;
+  const int64_t id = valid ? ids[tt] : 0;
+  const uint8_t* crow0 = codes + id * (int64_t)N * row_bytes;
+  const uint16_t* srow0 = scales + id * (int64_t)N * nblk;
+
+  uint3 cw[EC];
+  uint32_t sc[EC];
+  auto load_batch = [&](int c, int j0) {
+#pragma unroll
+    for (int j = 0; j < EC; ++j) {
+      const int e = (j0 + j) * S + sp;
+      if (e < N) {
+        cw[j] = *reinterpret_cast<const uint3*>(crow0 + (int64_t)e * row_bytes + (int64_t)c * 12);
+        sc[j] = srow0[(int64_t)e * nblk + (c >> 1)];
+      }
+    }
+  };
+  // First batch of code loads, then the router's operands.  (The reverse
+  // order, as in the dense kernel, needs branch-free code loads, which cost
+  // this kernel about 25 registers and one wave per SIMD of occupancy, more
+  // than the overlap gains: a token's codes are only N*(3D/8 + D/32) bytes.)
+  if (valid && ch < C) load_batch(ch, 0);
+  MfmaRouter<NP> rt;
+  if constexpr (kMfmaRouter)
+    rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
+                  N, (G * tpb) / kWave);
+
+  // Gates of the block's tokens into gsh[token][expert].
+  if constexpr (kMfmaRouter) {
+    rt.finish(tpb, red, gsh);
+  } else {
+    float part[NP];
+    router_partials<TH, NP, true>(h + tt * D, w_r, D, N, lig, G, valid, part);
+    float gate[NP];
+    group_gates<NP, G>(part, gate, N, lig, red + grp * NP);
+    if (lig == 0) {
+#pragma unroll
+      for (int e = 0; e < NP; ++e) gsh[grp * NP + e] = gate[e];
+    }
+    __syncthreads();
+  }
+  if (!valid) return;
+
+  for (int k = 0; k * CP + ch < C; ++k) {
+    const int c = k * CP + ch;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j0 = 0; j0 < EPL; j0 += EC) {
+      if (k != 0 || j0 != 0) load_batch(c, j0);
+#pragma unroll
+      for (int j = 0; j < EC; ++j) {
+        const int e = (j0 + j) * S + sp;
+        if (e < N) {
+          const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j]);
+          const float ws = gsh[grp * NP + e] * sv;
+          const uint32_t w[3] = {cw[j].x, cw[j].y, cw[j].z};
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const int pos = 3 * i, wd = pos >> 5, off = pos & 31;
+            uint32_t code;
+            if (off <= 29) code = (w[wd] >> off) & 7u;
+            else code = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off) & 7u;
+            acc[i] = fmaf(ws, lv[code], acc[i]);
+          }
+        }
+      }
+    }
+    SplitReduce<CP, S>::run(acc, sp);
+    float* yo = y + tt * D + (int64_t)c * 32 + SplitReduce<CP, S>::offset(sp);
+    if constexpr (OUT >= 4) {
+#pragma unroll
+      for (int j = 0; j < OUT; j += 4) stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < OUT; ++j) __builtin_nontemporal_store(acc[j], yo + j);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch
+// ---------------------------------------------------------------------------
+template <typename TH, int NP, int CP>
+static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
+                             const uint16_t* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
+  constexpr int S = 64 / CP < NP ? 64 / CP : NP;  // expert splits per token
+  constexpr int G = CP * S;
+  const int tpb = pick_tokens_per_block(T, G);
+  const int64_t blocks = (T + tpb - 1) / tpb;
+  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S>), dim3((unsigned)blocks), dim3(G * tpb), 0,
+                     s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, tpb);
+  return hipGetLastError();
+}
+
+template <typename TH, int NP>
+static hipError_t dispatch_nf3_cp(int CP, const int64_t* ids, const void* h, const void* w_r,
+                                  const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                  int D, int N, hipStream_t s) {
+  switch (CP) {
+    case 8: return launch_nf3<TH, NP, 8>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 16: return launch_nf3<TH, NP, 16>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 32: return launch_nf3<TH, NP, 32>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    default: return launch_nf3<TH, NP, 64>(ids, h, w_r, codes, scales, y, T, D, N, s);
+  }
+}
+
+template <typename TH>
+static hipError_t dispatch_nf3_np(int NP, int CP, const int64_t* ids, const void* h, const void* w_r,
+                                  const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                  int D, int N, hipStream_t s) {
+  switch (NP) {
+    case 1: return dispatch_nf3_cp<TH, 1>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 2: return dispatch_nf3_cp<TH, 2>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 4: return dispatch_nf3_cp<TH, 4>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 8: return dispatch_nf3_cp<TH, 8>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 16: return dispatch_nf3_cp<TH, 16>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 32: return dispatch_nf3_cp<TH, 32>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    default: return dispatch_nf3_cp<TH, 64>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+  }
+}
+
+hipError_t launch_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
+                                     const uint8_t* codes, const uint16_t* scales, float* y,
+                                     int64_t T, int64_t D, int64_t N, int dtype_h, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int NP = next_pow2((int)N);
+  const int CP = pick_group((int)(D / 32), 8, 64);  // lanes per expert split: chunks of a row
+  if (dtype_h == kF32)
+    return dispatch_nf3_np<float>(NP, CP, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
+  return dispatch_nf3_np<uint16_t>(NP, CP, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
+}
+
+void nf3_levels_host(float* out) {
+  static const uint32_t bits[8] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
+                                   0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
+  for (int i = 0; i < 8; ++i) {
+    union { uint32_t u; float f; } cv;
+    cv.u = bits[i];
+    out[i] = cv.f;
+  }
+}
+
+}  // namespace mole

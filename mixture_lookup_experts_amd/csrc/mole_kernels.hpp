@@ -10,7 +10,7 @@ namespace mole {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
-// combine.hip
+// combine_dense.hip, combine_nf3.hip
 hipError_t launch_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut,
                                  float* y, int64_t T, int64_t D, int64_t N, int dtype, bool vector_ok,
                                  hipStream_t s);
