@@ -54,7 +54,7 @@ struct SplitReduce {
   }
 };
 
-template <typename TH, int NP, int CP, int S>
+template <typename TH, int NP, int CP, int S, bool LANE>
 __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
     const int64_t* __restrict__ ids, const TH* __restrict__ h, const TH* __restrict__ w_r,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
@@ -65,7 +65,11 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   constexpr int EPL = (NP + S - 1) / S;            // experts per lane
   constexpr int EC = EPL < 8 ? EPL : 8;            // experts per batch of code loads
   constexpr int OUT = 32 / S;                      // outputs stored per lane and chunk
-  constexpr bool kMfmaRouter = sizeof(TH) == 2;
+  // Router: on the matrix cores (bf16 h, several tokens per block), else on
+  // the vector units (one token per block, or fp32 h; element-wise beyond
+  // 16 experts).
+  constexpr bool kMfmaRouter = sizeof(TH) == 2 && !LANE;
+  constexpr bool kLaneRouter = !kMfmaRouter && NP <= 16;
   constexpr int NPAD = ((NP + 15) / 16) * 16;
   __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * NP];
   __shared__ float gsh[kMaxTokPerBlock * NP];
@@ -103,13 +107,23 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   // than the overlap gains: a token's codes are only N*(3D/8 + D/32) bytes.)
   if (valid && ch < C) load_batch(ch, 0);
   MfmaRouter<NP> rt;
+  LaneRouter<TH, kLaneRouter ? NP : 1> lr;
   if constexpr (kMfmaRouter)
     rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
                   N, (G * tpb) / kWave);
+  if constexpr (kLaneRouter) lr.load_first(h + tt * D, w_r, D, N, lig);
 
   // Gates of the block's tokens into gsh[token][expert].
   if constexpr (kMfmaRouter) {
     rt.finish(tpb, red, gsh);
+  } else if constexpr (kLaneRouter) {
+    float gate[NP];
+    lr.template finish<G>(h + tt * D, w_r, D, N, lig, valid, gate, red + grp * NP);
+    if (lig == 0) {
+#pragma unroll
+      for (int e = 0; e < NP; ++e) gsh[grp * NP + e] = gate[e];
+    }
+    __syncthreads();
   } else {
     float part[NP];
     router_partials<TH, NP, true>(h + tt * D, w_r, D, N, lig, G, valid, part);
@@ -171,7 +185,15 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   constexpr int G = CP * S;
   const int tpb = pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;
-  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S>), dim3((unsigned)blocks), dim3(G * tpb), 0,
+  // One token per block: the vector-unit router (see LaneRouter).
+  if constexpr (sizeof(TH) == 2 && NP <= 16) {
+    if (tpb == 1) {
+      hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, true>), dim3((unsigned)blocks), dim3(G), 0, s,
+                         ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, 1);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, false>), dim3((unsigned)blocks), dim3(G * tpb), 0,
                      s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, tpb);
   return hipGetLastError();
 }
