@@ -129,12 +129,9 @@ def main():
     # host-resident NF3 table (filled from the first pack, before timing)
     codes_h = torch.empty((V, N, CB), dtype=torch.uint8, pin_memory=True)
     scales_h = torch.empty((V, N, SB), dtype=torch.int16, pin_memory=True)
-    cs = torch.empty(T * N * CB, dtype=torch.uint8, pin_memory=True)
-    ss = torch.empty(T * N * SB, dtype=torch.int16, pin_memory=True)
-    rs = torch.empty(T, dtype=torch.int64, pin_memory=True)
-    cd = torch.empty(T * N * CB, dtype=torch.uint8, device=dev)
-    sd = torch.empty(T * N * SB, dtype=torch.int16, device=dev)
-    rd = torch.empty(T, dtype=torch.int64, device=dev)
+    st_bytes = mole.mole_nf3_host_staging_size(T, N, D) if nf3 else 16
+    stage_h = torch.empty(st_bytes, dtype=torch.uint8, pin_memory=True)
+    stage_d = torch.empty(st_bytes, dtype=torch.uint8, device=dev)
     ids_cpu = [torch.from_numpy(x) for x in ids_h]
 
     ROWS = ["build", "pack_nf3", "combine", "combine_nf3", "combine_nf3_host"]
@@ -156,8 +153,7 @@ def main():
         rec(4)
         if nf3:
             n_unique_host.append(mole.mole_lookup_combine_nf3_host(
-                ids_cpu[k % NB], h, w_r, codes_h, scales_h, cs, ss, rs, cd, sd, rd, y5,
-                stream=stream))
+                ids_cpu[k % NB], h, w_r, codes_h, scales_h, stage_h, stage_d, y5, stream=stream))
         rec(5)
 
     with torch.cuda.stream(stream):
@@ -204,7 +200,7 @@ def main():
     comb_uniq = comb_bytes - (T - mean_u) * N * D * bL
     nf3_row = N * (CB + 2 * SB)
     nf3_bytes = T * (nf3_row + D * bh + 4 * D + 8) + D * N * bh
-    host_pcie = float(np.mean(n_unique_host)) * nf3_row if n_unique_host else 0.0
+    host_pcie = float(np.mean(n_unique_host)) * nf3_row + 8 * T if n_unique_host else 0.0
 
     def rate(bytes_, ms):
         return bytes_ / (ms * 1e-3) / 1e9

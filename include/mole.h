@@ -156,25 +156,40 @@ int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
  * *n_unique receives U.  nthreads <= 0 picks the hardware concurrency.
  * Returns MOLE_ERR_ID if an id is outside [0, V).
  *
+ * mole_nf3_host_staging_size: *bytes = size of the staging area that
+ * mole_lookup_combine_nf3_host needs for a batch of up to T tokens, both in
+ * pinned host memory and on the device.  Layout for a batch with U distinct
+ * ids, each section starting on a 16-byte boundary:
+ *     remap  int64 [T]          (row of the staged table for each token)
+ *     codes  uint8 [U][N][3D/8]
+ *     scales fp16  [U][N][D/64]
+ * Host-only; returns MOLE_ERR_DIM unless T >= 0, N > 0, D > 0, D % 64 == 0.
+ *
  * mole_lookup_combine_nf3_host: gather on the calling thread as above into
- * the pinned staging buffers (hipHostMalloc'ed, >= T rows; remap_stage_host
- * pinned int64 [T]), then enqueue on `stream` the host->device copies of
- * the U staged rows and the T remapped ids into codes_dev / scales_dev /
- * remap_dev (device, >= T rows), then the NF3 combine over the staged rows.
- * Because the staging buffers are rewritten on the host, this function
- * first waits for `stream` to drain (hipStreamSynchronize); the rest is
- * asynchronous.  *n_unique (may be NULL) receives U.
+ * stage_host (pinned, hipHostMalloc'ed; stage_bytes >= the staging size
+ * for T), then enqueue on `stream` one host->device copy of the used part
+ * of the staging area into stage_dev (device, 16-byte aligned, same size)
+ * and the NF3 combine over the staged rows.  Because stage_host is rewritten
+ * on the host, this function first waits (on the host) until the previous
+ * call's copy out of the same stage_host has finished -- not for the rest of
+ * the stream -- so the gather overlaps earlier GPU work; the rest is
+ * asynchronous.  Calls that share a staging area must be issued on one
+ * stream (stage_dev is then reused in stream order).  Not capturable in a
+ * HIP graph (the gather runs on the host at call time).  The caller keeps
+ * stage_host and stage_dev alive until the stream has passed the call.
+ * *n_unique (may be NULL) receives U.  Returns MOLE_ERR_WORKSPACE if
+ * stage_bytes is too small.
  * ------------------------------------------------------------------------ */
 int mole_gather_nf3_host(const int64_t* ids_host, int64_t T, const uint8_t* codes_host,
                          const uint16_t* scales_host, int64_t V, int64_t N, int64_t D,
                          uint8_t* codes_stage_host, uint16_t* scales_stage_host,
                          int64_t* remap_host, int64_t* n_unique, int nthreads);
 
+int mole_nf3_host_staging_size(int64_t T, int64_t N, int64_t D, size_t* bytes);
+
 int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const void* w_r,
                                  const uint8_t* codes_host, const uint16_t* scales_host,
-                                 uint8_t* codes_stage_host, uint16_t* scales_stage_host,
-                                 int64_t* remap_stage_host, uint8_t* codes_dev,
-                                 uint16_t* scales_dev, int64_t* remap_dev, float* y,
+                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
                                  int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
                                  int nthreads, int64_t* n_unique, void* stream);
 

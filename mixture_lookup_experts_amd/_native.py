@@ -65,7 +65,8 @@ def library():
             "mole_pack_nf3": (I, [P, P, P, I64, I64, I64, I, P]),
             "mole_lookup_combine_nf3": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_gather_nf3_host": (I, [P, I64, P, P, I64, I64, I64, P, P, P, P, I]),
-            "mole_lookup_combine_nf3_host": (I, [P, P, P, P, P, P, P, P, P, P, P, P,
+            "mole_nf3_host_staging_size": (I, [I64, I64, I64, P]),
+            "mole_lookup_combine_nf3_host": (I, [P, P, P, P, P, P, P, SZ, P,
                                                  I64, I64, I64, I64, I, I, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -210,23 +211,30 @@ def mole_gather_nf3_host(ids_host, codes_host, scales_host, codes_stage, scales_
     return int(u.value)
 
 
-def mole_lookup_combine_nf3_host(ids_host, h, w_r, codes_host, scales_host, codes_stage,
-                                 scales_stage, remap_stage, codes_dev, scales_dev, remap_dev, y,
+def mole_nf3_host_staging_size(T: int, N: int, D: int) -> int:
+    """Bytes of pinned host staging (and of the device buffer of the same
+    size) that mole_lookup_combine_nf3_host needs for up to T tokens."""
+    out = ctypes.c_size_t(0)
+    _check("mole_nf3_host_staging_size",
+           library().mole_nf3_host_staging_size(T, N, D, ctypes.addressof(out)))
+    return int(out.value)
+
+
+def mole_lookup_combine_nf3_host(ids_host, h, w_r, codes_host, scales_host, stage_host, stage_dev, y,
                                  nthreads: int = 0, stream=None) -> int:
     """Host-resident NF3 table: gather the requested rows on the host into
-    pinned staging, copy them to the device buffers and combine.  Returns U."""
+    the pinned staging area, copy its used part to the device buffer in one
+    transfer and combine.  Returns U, the number of distinct ids."""
     V, N, CB = codes_host.shape
     D = CB * 8 // 3
     T = ids_host.numel()
     _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
           "h [T,D], w_r [N,D], y [T,D]")
-    _need(codes_stage.numel() >= T * N * CB and codes_dev.numel() >= T * N * CB
-          and scales_stage.numel() >= T * N * (D // 64) and scales_dev.numel() >= T * N * (D // 64)
-          and remap_stage.numel() >= T and remap_dev.numel() >= T, "staging buffers hold T rows")
+    nbytes = stage_host.numel() * stage_host.element_size()
+    _need(stage_dev.numel() * stage_dev.element_size() >= nbytes, "device staging as large as the host one")
     u = ctypes.c_int64(0)
     _check("mole_lookup_combine_nf3_host", library().mole_lookup_combine_nf3_host(
         _ptr(ids_host), _ptr(h), _ptr(w_r), _ptr(codes_host), _ptr(scales_host),
-        _ptr(codes_stage), _ptr(scales_stage), _ptr(remap_stage), _ptr(codes_dev),
-        _ptr(scales_dev), _ptr(remap_dev), _ptr(y), T, V, D, N, _dtype(h), nthreads,
+        _ptr(stage_host), _ptr(stage_dev), nbytes, _ptr(y), T, V, D, N, _dtype(h), nthreads,
         ctypes.addressof(u), _stream(stream)))
     return int(u.value)

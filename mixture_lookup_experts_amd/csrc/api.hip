@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <thread>
 #include <unordered_map>
 #include <vector>
@@ -85,6 +86,40 @@ void gather_rows(const std::vector<int64_t>& uniq, const uint8_t* codes, const u
   for (auto& th : pool) th.join();
 }
 
+// One event per pinned staging area of the host-resident combine, recorded
+// after the copy out of it: the next call that reuses the area waits for
+// that copy only, not for everything queued on the stream.  Created on first
+// use and kept for the life of the process (a few bytes per distinct area).
+std::mutex g_stage_mu;
+std::unordered_map<const void*, hipEvent_t> g_stage_events;
+
+int stage_event(const void* stage_host, hipEvent_t* ev) {
+  std::lock_guard<std::mutex> lock(g_stage_mu);
+  auto it = g_stage_events.find(stage_host);
+  if (it != g_stage_events.end()) {
+    *ev = it->second;
+    return MOLE_OK;
+  }
+  const int rc = hip_status(hipEventCreateWithFlags(ev, hipEventDisableTiming));
+  if (rc == MOLE_OK) g_stage_events.emplace(stage_host, *ev);
+  return rc;
+}
+
+// Staging area of the host-resident combine for T tokens and U distinct
+// ids: remap int64[T] | codes [U][N][3D/8] | scales fp16 [U][N][D/64],
+// each section 16-byte aligned.  total = bytes in use.
+struct Nf3Staging {
+  size_t codes_off, scales_off, total;
+};
+inline size_t round16(size_t x) { return (x + 15u) & ~(size_t)15u; }
+Nf3Staging nf3_staging(int64_t T, int64_t U, int64_t N, int64_t D) {
+  Nf3Staging st;
+  st.codes_off = round16((size_t)T * 8u);
+  st.scales_off = st.codes_off + round16((size_t)U * (size_t)(N * 3 * D / 8));
+  st.total = st.scales_off + (size_t)U * (size_t)(N * (D / 64)) * 2u;
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,7 +141,7 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 1; }
+int mole_abi_version(void) { return 2; }
 
 int mole_nf3_levels(float* levels_host) {
   if (!levels_host) return MOLE_ERR_NULL;
@@ -210,13 +245,20 @@ int mole_gather_nf3_host(const int64_t* ids_host, int64_t T, const uint8_t* code
   return MOLE_OK;
 }
 
+int mole_nf3_host_staging_size(int64_t T, int64_t N, int64_t D, size_t* bytes) {
+  if (!bytes) return MOLE_ERR_NULL;
+  if (T < 0 || N <= 0 || D <= 0 || D % 64 != 0 || D > kMaxDim || T > kMaxDim || N > kMaxExperts)
+    return MOLE_ERR_DIM;
+  const Nf3Staging st = nf3_staging(T, T, N, D);
+  *bytes = st.total;
+  return MOLE_OK;
+}
+
 int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const void* w_r,
                                  const uint8_t* codes_host, const uint16_t* scales_host,
-                                 uint8_t* codes_stage_host, uint16_t* scales_stage_host,
-                                 int64_t* remap_stage_host, uint8_t* codes_dev, uint16_t* scales_dev,
-                                 int64_t* remap_dev, float* y, int64_t T, int64_t V, int64_t D,
-                                 int64_t N, int dtype_h, int nthreads, int64_t* n_unique,
-                                 void* stream) {
+                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
+                                 int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                                 int nthreads, int64_t* n_unique, void* stream) {
   if (!dtype_ok(dtype_h)) return MOLE_ERR_DTYPE;
   int rc = check_combine_common(T, V, D, N);
   if (rc != MOLE_OK) return rc;
@@ -225,28 +267,36 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
     if (n_unique) *n_unique = 0;
     return MOLE_OK;
   }
-  if (!ids_host || !h || !w_r || !codes_host || !scales_host || !codes_stage_host ||
-      !scales_stage_host || !remap_stage_host || !codes_dev || !scales_dev || !remap_dev || !y)
+  if (!ids_host || !h || !w_r || !codes_host || !scales_host || !stage_host || !stage_dev || !y)
     return MOLE_ERR_NULL;
-  if (!aligned16(h) || !aligned16(w_r) || !aligned16(codes_dev) || !aligned16(scales_dev) ||
-      !aligned8(remap_dev) || !aligned16(y))
+  if (!aligned16(h) || !aligned16(w_r) || !aligned16(stage_host) || !aligned16(stage_dev) || !aligned16(y))
     return MOLE_ERR_ALIGN;
+  if (stage_bytes < nf3_staging(T, T, N, D).total) return MOLE_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
-  rc = hip_status(hipStreamSynchronize(s));
+  hipEvent_t ev;
+  rc = stage_event(stage_host, &ev);
+  if (rc == MOLE_OK) rc = hip_status(hipEventSynchronize(ev));  // the last copy out of stage_host
   if (rc != MOLE_OK) return rc;
-  int64_t U = 0;
-  rc = mole_gather_nf3_host(ids_host, T, codes_host, scales_host, V, N, D, codes_stage_host,
-                            scales_stage_host, remap_stage_host, &U, nthreads);
+  // The remap section comes first (its size depends on T only); the codes
+  // and scales sections follow at offsets that depend on U, so the used part
+  // of the staging area is one contiguous range and moves in one copy.
+  std::vector<int64_t> uniq;
+  uint8_t* base_h = static_cast<uint8_t*>(stage_host);
+  int64_t* remap_h = reinterpret_cast<int64_t*>(base_h);
+  rc = dedupe(ids_host, T, V, uniq, remap_h);
   if (rc != MOLE_OK) return rc;
-  const size_t cbytes = (size_t)U * (size_t)(N * 3 * D / 8);
-  const size_t sbytes = (size_t)U * (size_t)(N * (D / 64)) * 2u;
-  rc = hip_status(hipMemcpyAsync(codes_dev, codes_stage_host, cbytes, hipMemcpyHostToDevice, s));
-  if (rc == MOLE_OK) rc = hip_status(hipMemcpyAsync(scales_dev, scales_stage_host, sbytes, hipMemcpyHostToDevice, s));
+  const int64_t U = (int64_t)uniq.size();
+  const Nf3Staging st = nf3_staging(T, U, N, D);
+  gather_rows(uniq, codes_host, scales_host, N, D, base_h + st.codes_off,
+              reinterpret_cast<uint16_t*>(base_h + st.scales_off), nthreads);
+  uint8_t* base_d = static_cast<uint8_t*>(stage_dev);
+  rc = hip_status(hipMemcpyAsync(base_d, base_h, st.total, hipMemcpyHostToDevice, s));
+  if (rc == MOLE_OK) rc = hip_status(hipEventRecord(ev, s));
   if (rc == MOLE_OK)
-    rc = hip_status(hipMemcpyAsync(remap_dev, remap_stage_host, (size_t)T * 8u, hipMemcpyHostToDevice, s));
-  if (rc == MOLE_OK)
-    rc = hip_status(mole::launch_lookup_combine_nf3(remap_dev, h, w_r, codes_dev, scales_dev, y, T, D,
-                                                    N, dtype_h, s));
+    rc = hip_status(mole::launch_lookup_combine_nf3(reinterpret_cast<const int64_t*>(base_d), h, w_r,
+                                                    base_d + st.codes_off,
+                                                    reinterpret_cast<const uint16_t*>(base_d + st.scales_off), y,
+                                                    T, D, N, dtype_h, s));
   if (rc == MOLE_OK && n_unique) *n_unique = U;
   return rc;
 }

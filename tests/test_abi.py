@@ -32,7 +32,8 @@ def test_header_declares_the_hot_path():
     names = declared_functions()
     for fn in ("mole_build_lut", "mole_lookup_combine", "mole_pack_nf3", "mole_lookup_combine_nf3",
                "mole_build_lut_workspace_size", "mole_gather_nf3_host",
-               "mole_lookup_combine_nf3_host", "mole_status_string", "mole_last_hip_error",
+               "mole_lookup_combine_nf3_host", "mole_nf3_host_staging_size", "mole_status_string",
+               "mole_last_hip_error",
                "mole_nf3_levels", "mole_abi_version"):
         assert fn in names
 
@@ -40,7 +41,7 @@ def test_header_declares_the_hot_path():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 1
+    assert lib.mole_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -95,6 +96,25 @@ def test_nf3_argument_errors(lib):
     assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 96, 4, 1, None) == DIM
     assert g(P(a), P(a), P(a), P(a), None, P(a), 4, 10, 128, 4, 1, None) == NULL
     assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 128, 4, 5, None) == DTYPE
+
+
+def test_host_staging_size_and_errors(lib):
+    """Staging layout of the host-resident combine: remap int64[T], then U
+    rows of codes and of fp16 scales, each section 16-byte aligned (sized
+    for U = T).  Errors are reported before any GPU call."""
+    T, N, D = 7, 3, 128
+    want = (T * 8 + 15) // 16 * 16 + (T * N * 3 * D // 8 + 15) // 16 * 16 + T * N * (D // 64) * 2
+    assert mole.mole_nf3_host_staging_size(T, N, D) == want
+    out = ctypes.c_size_t(0)
+    assert lib.mole_nf3_host_staging_size(T, N, 96, ctypes.addressof(out)) == DIM
+    assert lib.mole_nf3_host_staging_size(T, N, D, None) == NULL
+    a = 0x1000
+    f = lib.mole_lookup_combine_nf3_host
+    args = lambda stage_bytes, stage=P(a): (P(a), P(a), P(a), P(a), P(a), stage, P(a), stage_bytes, P(a),
+                                            T, 100, D, N, 1, 0, None, None)
+    assert f(*args(want - 1)) == WS  # too small: rejected before touching the stream
+    assert f(*args(want, None)) == NULL
+    assert f(*args(want, P(a + 8))) == ALIGN
 
 
 def test_build_argument_errors(lib):
