@@ -29,7 +29,12 @@ namespace mole {
 // ---------------------------------------------------------------------------
 // bf16 / fp32 table
 // ---------------------------------------------------------------------------
-template <typename T, int NP, int G, bool VECTOR, bool LANE>
+// Router placement (MODE): kRouterMfma / kRouterLane fused in this kernel,
+// kRouterStaged = gates computed by router_gates_kernel beforehand and staged
+// in the first N floats of each token's output row.
+enum { kRouterMfma = 0, kRouterLane = 1, kRouterStaged = 2 };
+
+template <typename T, int NP, int G, bool VECTOR, int MODE>
 __global__ __launch_bounds__(256) void lookup_combine_kernel(
     const int64_t* __restrict__ ids, const T* __restrict__ h, const T* __restrict__ w_r,
     const T* __restrict__ lut, float* __restrict__ y, int64_t T_, int D, int N, int tpb) {
@@ -40,8 +45,9 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   // Router: on the matrix cores (bf16, several tokens per block), or on
   // the vector units with its loads first (one token per block, or fp32),
   // or element-wise (unaligned rows, or more than 16 experts in fp32).
-  constexpr bool kMfmaRouter = VECTOR && sizeof(T) == 2 && !LANE;
-  constexpr bool kLaneRouter = VECTOR && !kMfmaRouter && NP <= 16;
+  constexpr bool kStaged = MODE == kRouterStaged;
+  constexpr bool kMfmaRouter = VECTOR && sizeof(T) == 2 && MODE == kRouterMfma;
+  constexpr bool kLaneRouter = VECTOR && !kMfmaRouter && !kStaged && NP <= 16;
   constexpr int NPAD = ((NP + 15) / 16) * 16;
   __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * WG * NP];
   __shared__ float gsh[kMfmaRouter ? kMaxTokPerBlock * NP : 1];
@@ -66,6 +72,14 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
     rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
                   N, (G * tpb) / kWave);
   if constexpr (kLaneRouter) lr.load_first(h + tt * D, w_r, D, N, lig);
+  // Staged gates: this token's N gates from the start of its own output row
+  // (every lane of the group reads the same 16-byte words).
+  constexpr int NG = kStaged ? (NP + 3) / 4 : 1;
+  uint4 gq[NG];
+  if constexpr (kStaged) {
+#pragma unroll
+    for (int q = 0; q < NG; ++q) gq[q] = ldg16(y + tt * D + 4 * q);
+  }
   __builtin_amdgcn_sched_barrier(0);
   const int64_t id = valid ? id_ld : 0;  // (the first wait on the id load is here)
   const T* slab = lut + id * (int64_t)N * D;
@@ -86,7 +100,18 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   __builtin_amdgcn_sched_barrier(0);
 
   float gate[NP];
-  if constexpr (kMfmaRouter) {
+  if constexpr (kStaged) {
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const float g4[4] = {__uint_as_float(gq[q].x), __uint_as_float(gq[q].y), __uint_as_float(gq[q].z),
+                           __uint_as_float(gq[q].w)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i < NP) gate[4 * q + i] = 4 * q + i < N ? g4[i] : 0.f;
+    }
+    // Every wave holds its tokens' gates before any wave overwrites the rows.
+    __syncthreads();
+  } else if constexpr (kMfmaRouter) {
     rt.finish(tpb, red, gsh);
 #pragma unroll
     for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
@@ -141,24 +166,65 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   }
 }
 
+// Gates for the staged-router mode: 16 tokens per block on the matrix cores
+// (a full MFMA tile, so W_r is read once per 16 tokens), written to the
+// first N floats of each token's output row, which the combine kernel reads
+// before it overwrites the row.
+template <int NP>
+__global__ __launch_bounds__(256) void router_gates_kernel(const uint16_t* __restrict__ h,
+                                                           const uint16_t* __restrict__ w_r, float* __restrict__ y,
+                                                           int64_t T_, int D, int N) {
+  constexpr int NPAD = ((NP + 15) / 16) * 16;
+  __shared__ float red[4 * 16 * NPAD];
+  __shared__ float gsh[kMaxTokPerBlock * NP];
+  const int64_t t0 = (int64_t)blockIdx.x * kMaxTokPerBlock;
+  MfmaRouter<NP> rt;
+  rt.load_first(h, w_r, t0, T_, kMaxTokPerBlock, D, N, 4);
+  rt.finish(kMaxTokPerBlock, red, gsh);
+  for (int i = threadIdx.x; i < kMaxTokPerBlock * N; i += blockDim.x) {
+    const int tk = i / N, e = i - tk * N;
+    if (t0 + tk < T_) y[(t0 + tk) * D + e] = gsh[tk * NP + e];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
+// Batches of at least this many tokens, at widths where a block holds
+// several tokens, route in a separate launch (see router_gates_kernel): the
+// fused MFMA router re-reads W_r for every 2-4 tokens and holds its operands
+// in registers through the gather, which at these sizes costs more than the
+// second launch (measured on the 410M-class table: T=4096 26.6 -> 21.0 us
+// with Zipf ids, neutral at T=1024).  With one token per block the vector
+// router stays fused: there the extra launch cost more than it saved
+// (1B-class table, T=1024: 12.4 -> 17.3 us).
+constexpr int64_t kStagedRouterMinT = 2048;
+
 template <typename E, int NP, int G, bool VEC>
 static hipError_t launch_dense(const int64_t* ids, const void* h, const void* w_r, const void* lut,
                                float* y, int64_t T, int D, int N, hipStream_t s) {
   const int tpb = pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;
-  // One token per block: the vector-unit router (see LaneRouter).
-  if constexpr (VEC && sizeof(E) == 2 && NP <= 16 && G >= 64) {
-    if (tpb == 1) {
-      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, true>), dim3((unsigned)blocks), dim3(G), 0, s, ids,
-                         (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, 1);
+  if constexpr (VEC && sizeof(E) == 2) {
+    if (T >= kStagedRouterMinT && tpb >= 2 && N <= D) {
+      const int64_t rblocks = (T + kMaxTokPerBlock - 1) / kMaxTokPerBlock;
+      hipLaunchKernelGGL((router_gates_kernel<NP>), dim3((unsigned)rblocks), dim3(256), 0, s, (const uint16_t*)h,
+                         (const uint16_t*)w_r, y, T, D, N);
+      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterStaged>), dim3((unsigned)blocks),
+                         dim3(G * tpb), 0, s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, tpb);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, false>), dim3((unsigned)blocks), dim3(G * tpb), 0, s,
-                     ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, tpb);
+  // One token per block: the vector-unit router (see LaneRouter).
+  if constexpr (VEC && sizeof(E) == 2 && NP <= 16 && G >= 64) {
+    if (tpb == 1) {
+      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterLane>), dim3((unsigned)blocks), dim3(G), 0,
+                         s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, 1);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterMfma>), dim3((unsigned)blocks), dim3(G * tpb),
+                     0, s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, tpb);
   return hipGetLastError();
 }
 

@@ -76,6 +76,11 @@ COMBINE_CASES = [
     (50, 5, 60, 21, "bf16"),      # D % 8 != 0: element-wise path
     (50, 2, 30, 7, "f32"),
     (20, 4, 8, 70, "bf16"),       # tiny D: one chunk per row
+    # T >= 2048 with several tokens per block: gates from a separate router
+    # launch, staged in the output rows
+    (300, 16, 1024, 2051, "bf16"),  # ragged last block and router tile
+    (200, 5, 256, 3001, "bf16"),    # N padded to 8
+    (100, 64, 512, 2048, "bf16"),   # largest N
 ]
 
 
