@@ -29,11 +29,6 @@ namespace mole {
 // ---------------------------------------------------------------------------
 // bf16 / fp32 table
 // ---------------------------------------------------------------------------
-// Router placement (MODE): kRouterMfma / kRouterLane fused in this kernel,
-// kRouterStaged = gates computed by router_gates_kernel beforehand and staged
-// in the first N floats of each token's output row.
-enum { kRouterMfma = 0, kRouterLane = 1, kRouterStaged = 2 };
-
 template <typename T, int NP, int G, bool VECTOR, int MODE>
 __global__ __launch_bounds__(256) void lookup_combine_kernel(
     const int64_t* __restrict__ ids, const T* __restrict__ h, const T* __restrict__ w_r,
@@ -166,39 +161,9 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   }
 }
 
-// Gates for the staged-router mode: 16 tokens per block on the matrix cores
-// (a full MFMA tile, so W_r is read once per 16 tokens), written to the
-// first N floats of each token's output row, which the combine kernel reads
-// before it overwrites the row.
-template <int NP>
-__global__ __launch_bounds__(256) void router_gates_kernel(const uint16_t* __restrict__ h,
-                                                           const uint16_t* __restrict__ w_r, float* __restrict__ y,
-                                                           int64_t T_, int D, int N) {
-  constexpr int NPAD = ((NP + 15) / 16) * 16;
-  __shared__ float red[4 * 16 * NPAD];
-  __shared__ float gsh[kMaxTokPerBlock * NP];
-  const int64_t t0 = (int64_t)blockIdx.x * kMaxTokPerBlock;
-  MfmaRouter<NP> rt;
-  rt.load_first(h, w_r, t0, T_, kMaxTokPerBlock, D, N, 4);
-  rt.finish(kMaxTokPerBlock, red, gsh);
-  for (int i = threadIdx.x; i < kMaxTokPerBlock * N; i += blockDim.x) {
-    const int tk = i / N, e = i - tk * N;
-    if (t0 + tk < T_) y[(t0 + tk) * D + e] = gsh[tk * NP + e];
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
-// Batches of at least this many tokens, at widths where a block holds
-// several tokens, route in a separate launch (see router_gates_kernel): the
-// fused MFMA router re-reads W_r for every 2-4 tokens and holds its operands
-// in registers through the gather, which at these sizes costs more than the
-// second launch (measured on the 410M-class table: T=4096 26.6 -> 21.0 us
-// with Zipf ids, neutral at T=1024).  With one token per block the vector
-// router stays fused: there the extra launch cost more than it saved
-// (1B-class table, T=1024: 12.4 -> 17.3 us).
-constexpr int64_t kStagedRouterMinT = 2048;
 
 template <typename E, int NP, int G, bool VEC>
 static hipError_t launch_dense(const int64_t* ids, const void* h, const void* w_r, const void* lut,

@@ -54,7 +54,7 @@ struct SplitReduce {
   }
 };
 
-template <typename TH, int NP, int CP, int S, bool LANE>
+template <typename TH, int NP, int CP, int S, int MODE>
 __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
     const int64_t* __restrict__ ids, const TH* __restrict__ h, const TH* __restrict__ w_r,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   // Router: on the matrix cores (bf16 h, several tokens per block), else on
   // the vector units (one token per block, or fp32 h; element-wise beyond
   // 16 experts).
-  constexpr bool kMfmaRouter = sizeof(TH) == 2 && !LANE;
+  static_assert(MODE != kRouterStaged, "the NF3 kernel routes in the same launch");
+  constexpr bool kMfmaRouter = sizeof(TH) == 2 && MODE == kRouterMfma;
   constexpr bool kLaneRouter = !kMfmaRouter && NP <= 16;
   constexpr int NPAD = ((NP + 15) / 16) * 16;
   __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * NP];
@@ -185,16 +186,19 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   constexpr int G = CP * S;
   const int tpb = pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;
+  // (No staged-router launch here: this kernel is bound by its decode
+  // arithmetic, and the extra launch measured slower -- 410M-class NF3
+  // table, T=4096: 20.1 -> 22.6 us.)
   // One token per block: the vector-unit router (see LaneRouter).
   if constexpr (sizeof(TH) == 2 && NP <= 16) {
     if (tpb == 1) {
-      hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, true>), dim3((unsigned)blocks), dim3(G), 0, s,
-                         ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, 1);
+      hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterLane>), dim3((unsigned)blocks), dim3(G),
+                         0, s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, 1);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, false>), dim3((unsigned)blocks), dim3(G * tpb), 0,
-                     s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, tpb);
+  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterMfma>), dim3((unsigned)blocks),
+                     dim3(G * tpb), 0, s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, tpb);
   return hipGetLastError();
 }
 

@@ -229,7 +229,10 @@ def run_nf3(ids, h, w_r, codes, scales):
 @pytest.mark.parametrize("V,N,D,T,dtype", [(512, 4, 64, 64, "f32"), (300, 4, 768, 200, "bf16"),
                                            (300, 16, 1024, 257, "bf16"), (100, 16, 2048, 33, "bf16"),
                                            (64, 64, 128, 10, "bf16"), (50, 3, 192, 17, "f32"),
-                                           (40, 1, 64, 5, "bf16")])
+                                           (40, 1, 64, 5, "bf16"),
+                                           # large batches with several tokens per block
+                                           (300, 16, 1024, 2051, "bf16"), (200, 5, 256, 3001, "bf16"),
+                                           (100, 64, 512, 2048, "bf16")])
 def test_combine_nf3_matches_oracle(V, N, D, T, dtype):
     seed = 2000 + V + N + D
     table = rand_table(seed, V, N, D, "bf16")
