@@ -201,6 +201,32 @@ def test_combine_depends_only_on_own_row_and_is_permutation_invariant():
     np.testing.assert_allclose(yp, y, rtol=1e-14, atol=1e-15)
 
 
+def test_combine_uses_every_expert_row_whatever_the_gates():
+    """All routed experts are active (no top-k): with every gate positive,
+    perturbing any single expert's row of a token's slab moves that token's
+    output by exactly gate[e] * delta, so every token reads all N rows and
+    the lookup cost is N*D per token however peaked the gates are."""
+    r = rng(26)
+    V, N, D, T = 9, 6, 16, 7
+    lut = r.standard_normal((V, N, D), dtype=np.float32)
+    h = r.standard_normal((T, D), dtype=np.float32)
+    # peaked but non-zero gates (logit gaps of a few units)
+    w_r = r.standard_normal((N, D), dtype=np.float32)
+    ids = np.array([0, 3, 3, 8, 5, 1, 0])
+    y = oracle.lookup_combine(ids, h, w_r, lut)
+    g = oracle.router_gates(h, w_r)
+    assert g.min() > 1e-8 and g.max() > 0.9  # peaked, yet every expert weighs in
+    for e in range(N):
+        lut2 = lut.copy()
+        delta = r.standard_normal(D).astype(np.float32)
+        lut2[:, e] += delta
+        y2 = oracle.lookup_combine(ids, h, w_r, lut2)
+        moved = (lut2.astype(np.float64)[ids, e] - lut.astype(np.float64)[ids, e])
+        # (fp64: each of y, y2 carries rounding ~1e-16 |y|, hence the absolute bar)
+        np.testing.assert_allclose(y2 - y, g[:, e:e + 1] * moved, rtol=1e-9, atol=1e-13)
+        assert (np.abs(y2 - y).max(axis=1) > 0).all()
+
+
 def test_combine_empty_batch_and_bad_id():
     lut = np.zeros((4, 2, 8), np.float32)
     w_r = np.zeros((2, 8), np.float32)
