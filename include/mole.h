@@ -83,7 +83,10 @@ int mole_nf3_levels(float* levels_host);
  * dtype MOLE_BF16: bf16 inputs and output; bf16 matrix-core products with
  *   fp32 accumulation; the hidden activation GELU(.) is rounded to bf16
  *   between the two products; LUT rounded to bf16 (nearest even).
- * Needs D % 8 == 0 and F % 8 == 0 for MOLE_BF16.
+ * Needs D % 8 == 0 and F % 8 == 0 for MOLE_BF16, and N*F and N*D at most
+ * 2^22 (the row strides of the hidden activations and of the table: each
+ * 256-row panel is addressed with 32-bit offsets); MOLE_ERR_UNSUPPORTED
+ * otherwise.  (The largest configurations here use N*F = 131072.)
  *
  * workspace: device scratch for the bf16 hidden activations of a block of
  * vocabulary rows (ignored for MOLE_F32, may be NULL there).  Any size at

@@ -30,6 +30,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // sizes handed to kernels as int
 constexpr int64_t kMaxExperts = 64;             // combine kernels keep N gates in registers
+constexpr int64_t kMaxPanelStride = (int64_t)1 << 22;  // bf16 build: row stride of G and of the LUT
 
 int check_combine_common(int64_t T, int64_t V, int64_t D, int64_t N) {
   if (T < 0 || V <= 0 || D <= 0 || N <= 0) return MOLE_ERR_DIM;
@@ -181,6 +182,9 @@ int mole_build_lut(const void* emb, const void* w_up, const void* w_down, void* 
                                                  as_stream(stream)));
   }
   if (D % 8 != 0 || F % 8 != 0) return MOLE_ERR_DIM;
+  // Each 256-row operand or output panel of the build GEMMs is addressed with
+  // 32-bit byte offsets (256 rows x stride x 2 bytes < 2^31).
+  if (N * F > kMaxPanelStride || N * D > kMaxPanelStride) return MOLE_ERR_UNSUPPORTED;
   if (!workspace) return MOLE_ERR_NULL;
   if (!aligned16(workspace)) return MOLE_ERR_ALIGN;
   if (workspace_bytes < mole::build_lut_min_workspace(D, F, N)) return MOLE_ERR_WORKSPACE;

@@ -126,6 +126,10 @@ def test_build_argument_errors(lib):
     assert b(P(a), P(a), P(a), P(a + 8), 8, 64, 256, 4, 1, P(a), 1 << 40, None) == ALIGN
     assert b(P(a), P(a), P(a), P(a), 8, 64, 20000, 4, 0, None, 0, None) == UNSUP
     assert b(P(a), P(a), P(a), P(a), 8, 64, 256, 4, 3, None, 0, None) == DTYPE
+    # bf16 panels are addressed with 32-bit offsets: N*F or N*D above 2^22 is refused
+    assert b(P(a), P(a), P(a), P(a), 8, 64, 1 << 17, 64, 1, P(a), 1 << 40, None) == UNSUP
+    assert b(P(a), P(a), P(a), P(a), 8, 1 << 17, 64, 64, 1, P(a), 1 << 40, None) == UNSUP
+    assert b(P(a), P(a), P(a), P(a), 8, 64, 1 << 16, 64, 1, P(a), 10, None) == WS  # 2^22 itself is fine
 
 
 def gather_inputs(seed, V=50, N=3, D=128, T=40):
