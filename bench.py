@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="160m", help="160m | 410m | 1b | tiny")
     p.add_argument("--tokens", type=int, default=256)
+    p.add_argument("--ids", default=None, choices=("zipf", "uniform", "distinct"),
+                   help="token-id law (default: the workload's own; 'distinct' = no repeats, "
+                        "so gathered bytes = unique bytes)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget for the CPU-oracle baseline (0 disables it)")
     p.add_argument("--no-scale-probe", action="store_true",
@@ -109,7 +112,7 @@ def main():
     emb, w_up, w_down, w_r = (to_dev(x) for x in (layer.emb, layer.w_up, layer.w_down, layer.w_r))
     perm = synth.rank_permutation(w)
     NB = 8
-    ids_h = [synth.make_ids(w, T, step=s, perm=perm) for s in range(NB)]
+    ids_h = [synth.make_ids(w, T, step=s, kind=args.ids, perm=perm) for s in range(NB)]
     batches = [(to_dev(ids_h[s]), to_dev(synth.make_hidden(w, T, step=s))) for s in range(NB)]
     uniq = [np.unique(x).size for x in ids_h]
 
@@ -239,10 +242,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
-        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) h, Zipf(1.1) ids)",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) h, %s ids)"
+                % {"zipf": "Zipf(1.1)", "uniform": "uniform", "distinct": "distinct"}[
+                    args.ids or ("zipf" if w.zipf else "uniform")],
         "config": {"workload": "%s-class MoLE layer V=%d D=%d N=%d F=%d, T=%d %s ids; step = "
                                "build + NF3 pack + combine + NF3 combine + host-resident NF3 combine"
-                               % (w.name, V, D, N, F, T, "Zipf(1.1)" if w.zipf else "uniform"),
+                               % (w.name, V, D, N, F, T, args.ids or ("Zipf(1.1)" if w.zipf else "uniform")),
                    "V": V, "D": D, "N": N, "F": F, "tokens": T, "parallelism": "single GPU"},
         "rows": rows,
         "roofline": {"kernel": "mole_build_lut (gemm_nt_bf16 GELU + store, one launch each)",
