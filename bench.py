@@ -264,6 +264,7 @@ def main():
         torch.cuda.synchronize()
         result["combine_at_scale"] = scale_probe(torch, mole, synth, dev, stream)
         result["decode_stack_1b"] = decode_stack_probe(torch, mole, synth, dev, stream)
+        result["host_stack_nf3"] = host_stack_probe(torch, mole, synth, dev, stream)
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(args, w, layer, ids_h[0], synth, T)
@@ -395,6 +396,100 @@ def decode_stack_probe(torch, mole, synth, dev, stream):
     torch.cuda.synchronize()
     ctx.__exit__(None, None, None)
     del luts, w_rs
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_stack_probe(torch, mole, synth, dev, stream):
+    """A 16-layer stack of 410M-class NF3 tables (V=50304 N=16 D=1024,
+    0.33 GB each, 5.3 GB in all) in pinned host memory.  One decode step
+    = the 16 layers' lookup-combines, run two ways: (a) per layer, the
+    host-resident call (gather + copy + combine, 16 transfers); (b) one
+    step-start prefetch of every layer's rows in a single transfer, then 16
+    device combines on the staged rows.  Also a pinned host->device copy of
+    256 MiB, the PCIe roofline measured in the same run.  The host tables are
+    left as allocated (zero pages): the combine's cost does not depend on the
+    code values."""
+    w = synth.WORKLOADS["410m-nf3"]
+    V, D, N, L = w.V, w.D, w.N, 16
+    CB, SB = 3 * D // 8, D // 64
+    ctx = torch.cuda.stream(stream)
+    ctx.__enter__()
+    codes_h = [torch.zeros((V, N, CB), dtype=torch.uint8, pin_memory=True) for _ in range(L)]
+    scales_h = [torch.zeros((V, N, SB), dtype=torch.int16, pin_memory=True) for _ in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.seed(w, 80))
+    w_rs = [(torch.randn((N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16) for _ in range(L)]
+    # PCIe roofline: one pinned 256 MiB host->device copy
+    src = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    h2d_gbs = 3 * (256 << 20) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    out = {"workload": "16-layer stack of 410M-class NF3 tables (V=50304 N=16 D=1024) in pinned host "
+                       "memory, %.1f GB" % (L * V * N * (CB + 2 * SB) / 1e9),
+           "pcie_h2d_gbs_measured": h2d_gbs}
+    perm = synth.rank_permutation(w)
+    for T in (256, 1024, 4096):
+        NB = 3
+        ids_l = [torch.from_numpy(synth.make_ids(w, T, step=s, perm=perm)) for s in range(NB)]
+        h_l = [[torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+               for _ in range(NB)]
+        y_l = [torch.empty((T, D), dtype=torch.float32, device=dev) for _ in range(L)]
+        one = mole.mole_nf3_host_staging_size(T, N, D)
+        st1_h = torch.empty(one, dtype=torch.uint8, pin_memory=True)
+        st1_d = torch.empty(one, dtype=torch.uint8, device=dev)
+        allb = mole.mole_nf3_host_stack_staging_size(T, L, N, D)
+        stL_h = torch.empty(allb, dtype=torch.uint8, pin_memory=True)
+        stL_d = torch.empty(allb, dtype=torch.uint8, device=dev)
+        uniq = []
+
+        def per_layer(b):
+            for l in range(L):
+                uniq.append(mole.mole_lookup_combine_nf3_host(ids_l[b], h_l[b][l], w_rs[l], codes_h[l],
+                                                              scales_h[l], st1_h, st1_d, y_l[l],
+                                                              stream=stream))
+
+        def prefetched(b):
+            remap, layers = mole.mole_prefetch_nf3_host_stack(ids_l[b], codes_h, scales_h, stL_h, stL_d,
+                                                              stream=stream)
+            for l in range(L):
+                mole.mole_lookup_combine_nf3(remap, h_l[b][l], w_rs[l], layers[l][0], layers[l][1], y_l[l],
+                                             stream=stream)
+
+        res = {}
+        for name, fn in (("per_layer", per_layer), ("prefetched", prefetched)):
+            for b in range(2):
+                fn(b % NB)
+            torch.cuda.synchronize()
+            reps = 5
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for r in range(reps):
+                fn(r % NB)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / reps
+            res[name + "_us_per_step"] = e0.elapsed_time(e1) * 1e3 / reps
+            res[name + "_wall_us_per_step"] = wall * 1e6
+        U = float(np.mean(uniq)) if uniq else 0.0
+        pcie = L * U * N * (CB + 2 * SB) + 8 * T
+        best = min(res["per_layer_us_per_step"], res["prefetched_us_per_step"])
+        res.update({"mean_unique_ids": U, "pcie_bytes_per_step": pcie,
+                    "pcie_gbs_effective_prefetched": pcie / (res["prefetched_us_per_step"] * 1e-6) / 1e9,
+                    "tokens_per_s": T / (best * 1e-6)})
+        out["T%d" % T] = res
+        del st1_h, st1_d, stL_h, stL_d, h_l, y_l
+    torch.cuda.synchronize()
+    ctx.__exit__(None, None, None)
+    del codes_h, scales_h, w_rs
     torch.cuda.empty_cache()
     return out
 

@@ -196,6 +196,44 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
                                  int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
                                  int nthreads, int64_t* n_unique, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Host-resident NF3 tables of a stack of L layers, prefetched at the start
+ * of a decode step (inference section: the table lives in lower-tier
+ * storage and only the retrieved vectors are loaded into GPU memory; a
+ * token's id is known before the first layer runs, so every layer's rows
+ * can be fetched in one transfer ahead of the layers that use them).
+ *
+ * mole_nf3_host_stack_staging_size: *bytes = staging size (pinned host and
+ * device alike) for up to T tokens and L layers.  Layout for a batch with U
+ * distinct ids, each section on a 16-byte boundary:
+ *     remap  int64 [T]
+ *     then for each layer l:  codes_l uint8 [U][N][3D/8],  scales_l fp16 [U][N][D/64]
+ *
+ * mole_prefetch_nf3_host_stack: dedupe ids_host once, gather the U distinct
+ * rows of every layer's host table (codes_host[l] [V][N][3D/8],
+ * scales_host[l] [V][N][D/64], l < L; pinned or pageable) into stage_host
+ * (pinned, 16-byte aligned), then enqueue on `stream` ONE host->device copy
+ * of the used part into stage_dev.  codes_off[l] / scales_off[l] (host
+ * arrays of L entries) receive the byte offsets of layer l's sections, so
+ * layer l's combine, issued on the same stream after this call, is
+ *     mole_lookup_combine_nf3(stage_dev, h_l, w_r_l,
+ *         stage_dev + codes_off[l], stage_dev + scales_off[l], y_l,
+ *         T, U, D, N, dtype_h, stream)
+ * (the remap section at the start of stage_dev serves as the ids, and U,
+ * the number of staged rows, as the vocabulary size).  Waiting and reuse rules as
+ * for mole_lookup_combine_nf3_host (the previous copy out of the same
+ * stage_host is waited for on the host; not capturable in a HIP graph).
+ * *n_unique receives U.  Errors: MOLE_ERR_ID for an id outside [0, V),
+ * MOLE_ERR_WORKSPACE if stage_bytes is below the staging size for T, L.
+ * ------------------------------------------------------------------------ */
+int mole_nf3_host_stack_staging_size(int64_t T, int64_t L, int64_t N, int64_t D, size_t* bytes);
+
+int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
+                                 const uint8_t* const* codes_host, const uint16_t* const* scales_host,
+                                 int64_t L, int64_t V, int64_t N, int64_t D, void* stage_host,
+                                 void* stage_dev, size_t stage_bytes, size_t* codes_off,
+                                 size_t* scales_off, int nthreads, int64_t* n_unique, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

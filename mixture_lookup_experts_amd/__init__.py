@@ -26,6 +26,8 @@ from ._native import (  # noqa: F401
     mole_lookup_combine_nf3,
     mole_lookup_combine_nf3_host,
     mole_nf3_host_staging_size,
+    mole_nf3_host_stack_staging_size,
+    mole_prefetch_nf3_host_stack,
     mole_nf3_levels,
     mole_pack_nf3,
     mole_status_string,
@@ -35,6 +37,6 @@ __all__ = [
     "MOLE_F32", "MOLE_BF16", "MoleError", "MoleLibraryMissing", "library", "library_path",
     "mole_build_lut", "mole_build_lut_workspace_size", "mole_lookup_combine", "mole_pack_nf3",
     "mole_lookup_combine_nf3", "mole_gather_nf3_host", "mole_lookup_combine_nf3_host",
-    "mole_nf3_host_staging_size",
+    "mole_nf3_host_staging_size", "mole_nf3_host_stack_staging_size", "mole_prefetch_nf3_host_stack",
     "mole_nf3_levels", "mole_status_string",
 ]

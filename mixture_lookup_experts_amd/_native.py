@@ -66,6 +66,9 @@ def library():
             "mole_lookup_combine_nf3": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_gather_nf3_host": (I, [P, I64, P, P, I64, I64, I64, P, P, P, P, I]),
             "mole_nf3_host_staging_size": (I, [I64, I64, I64, P]),
+            "mole_nf3_host_stack_staging_size": (I, [I64, I64, I64, I64, P]),
+            "mole_prefetch_nf3_host_stack": (I, [P, I64, P, P, I64, I64, I64, I64, P, P, SZ, P, P, I, P,
+                                                 P]),
             "mole_lookup_combine_nf3_host": (I, [P, P, P, P, P, P, P, SZ, P,
                                                  I64, I64, I64, I64, I, I, P, P]),
         }
@@ -218,6 +221,56 @@ def mole_nf3_host_staging_size(T: int, N: int, D: int) -> int:
     _check("mole_nf3_host_staging_size",
            library().mole_nf3_host_staging_size(T, N, D, ctypes.addressof(out)))
     return int(out.value)
+
+
+def mole_nf3_host_stack_staging_size(T: int, L: int, N: int, D: int) -> int:
+    """Bytes of pinned host staging (and of the device buffer of the same
+    size) that mole_prefetch_nf3_host_stack needs for T tokens, L layers."""
+    out = ctypes.c_size_t(0)
+    _check("mole_nf3_host_stack_staging_size",
+           library().mole_nf3_host_stack_staging_size(T, L, N, D, ctypes.addressof(out)))
+    return int(out.value)
+
+
+def mole_prefetch_nf3_host_stack(ids_host, codes_host, scales_host, stage_host, stage_dev,
+                                 nthreads: int = 0, stream=None):
+    """One decode step's NF3 rows for every layer of a stack, gathered on the
+    host from the L host tables (lists codes_host[l] [V,N,3D/8] uint8 and
+    scales_host[l] [V,N,D/64] int16) and moved in one host->device copy into
+    stage_dev.  Returns (remap [T] int64, [(codes_l [U,N,3D/8], scales_l
+    [U,N,D/64]) for each layer]) -- views into stage_dev to hand to
+    mole_lookup_combine_nf3 layer by layer on the same stream."""
+    L = len(codes_host)
+    _need(L > 0 and len(scales_host) == L, "one codes and one scales table per layer")
+    V, N, CB = codes_host[0].shape
+    D = CB * 8 // 3
+    SB = D // 64
+    T = ids_host.numel()
+    for c, sc in zip(codes_host, scales_host):
+        _need(tuple(c.shape) == (V, N, CB) and tuple(sc.shape) == (V, N, SB), "tables [V,N,3D/8] and [V,N,D/64]")
+        _need(c.device.type == "cpu" and sc.device.type == "cpu" and c.is_contiguous() and sc.is_contiguous(),
+              "host tables, contiguous")
+    _need(ids_host.device.type == "cpu" and ids_host.dtype == torch.int64, "ids_host: int64 on the host")
+    nbytes = stage_host.numel() * stage_host.element_size()
+    _need(stage_dev.numel() * stage_dev.element_size() >= nbytes and stage_dev.dtype == torch.uint8,
+          "device staging (uint8) as large as the host one")
+    cptrs = (ctypes.c_void_p * L)(*[c.data_ptr() for c in codes_host])
+    sptrs = (ctypes.c_void_p * L)(*[sc.data_ptr() for sc in scales_host])
+    coff = (ctypes.c_size_t * L)()
+    soff = (ctypes.c_size_t * L)()
+    u = ctypes.c_int64(0)
+    _check("mole_prefetch_nf3_host_stack", library().mole_prefetch_nf3_host_stack(
+        _ptr(ids_host), T, ctypes.addressof(cptrs), ctypes.addressof(sptrs), L, V, N, D, _ptr(stage_host),
+        _ptr(stage_dev), nbytes, ctypes.addressof(coff), ctypes.addressof(soff), nthreads,
+        ctypes.addressof(u), _stream(stream)))
+    U = int(u.value)
+    remap = stage_dev[:T * 8].view(torch.int64)
+    layers = []
+    for l in range(L):
+        c = stage_dev[coff[l]:coff[l] + U * N * CB].view(U, N, CB)
+        sc = stage_dev[soff[l]:soff[l] + U * N * SB * 2].view(torch.int16).view(U, N, SB)
+        layers.append((c, sc))
+    return remap, layers
 
 
 def mole_lookup_combine_nf3_host(ids_host, h, w_r, codes_host, scales_host, stage_host, stage_dev, y,

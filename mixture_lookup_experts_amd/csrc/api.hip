@@ -121,6 +121,53 @@ Nf3Staging nf3_staging(int64_t T, int64_t U, int64_t N, int64_t D) {
   return st;
 }
 
+// Staging area of the layer-stack prefetch for T tokens, U distinct ids and
+// L layers: remap int64[T], then per layer codes [U][N][3D/8] and scales
+// fp16 [U][N][D/64], each section 16-byte aligned.
+size_t nf3_stack_staging(int64_t T, int64_t U, int64_t L, int64_t N, int64_t D, size_t* codes_off,
+                         size_t* scales_off) {
+  size_t off = round16((size_t)T * 8u);
+  for (int64_t l = 0; l < L; ++l) {
+    if (codes_off) codes_off[l] = off;
+    off += round16((size_t)U * (size_t)(N * 3 * D / 8));
+    if (scales_off) scales_off[l] = off;
+    off += round16((size_t)U * (size_t)(N * (D / 64)) * 2u);
+  }
+  return off;
+}
+
+// Gather of the U distinct rows of L tables at once, split over threads by
+// flattened (layer, row) index, so a stack of small per-layer gathers still
+// spreads over the host cores.
+void gather_rows_stack(const std::vector<int64_t>& uniq, const uint8_t* const* codes, const uint16_t* const* scales,
+                       int64_t L, int64_t N, int64_t D, uint8_t* base, const size_t* codes_off,
+                       const size_t* scales_off, int nthreads) {
+  const size_t crow = (size_t)(N * 3 * D / 8), srow = (size_t)(N * (D / 64));
+  const int64_t U = (int64_t)uniq.size(), total = L * U;
+  auto work = [&](int64_t lo, int64_t hi) {
+    for (int64_t i = lo; i < hi; ++i) {
+      const int64_t l = i / U, u = i - l * U;
+      std::memcpy(base + codes_off[l] + (size_t)u * crow, codes[l] + (size_t)uniq[u] * crow, crow);
+      std::memcpy(reinterpret_cast<uint16_t*>(base + scales_off[l]) + (size_t)u * srow,
+                  scales[l] + (size_t)uniq[u] * srow, srow * 2);
+    }
+  };
+  int nt = nthreads > 0 ? nthreads : (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
+  if ((size_t)total * (crow + 2 * srow) < ((size_t)1 << 20)) nt = 1;  // threads are not worth it below ~1 MB
+  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(total, 1));
+  if (nt <= 1) {
+    work(0, total);
+    return;
+  }
+  std::vector<std::thread> pool;
+  const int64_t per = (total + nt - 1) / nt;
+  for (int i = 0; i < nt; ++i) {
+    const int64_t lo = i * per, hi = std::min<int64_t>(total, lo + per);
+    if (lo < hi) pool.emplace_back(work, lo, hi);
+  }
+  for (auto& th : pool) th.join();
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,7 +189,7 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 2; }
+int mole_abi_version(void) { return 3; }
 
 int mole_nf3_levels(float* levels_host) {
   if (!levels_host) return MOLE_ERR_NULL;
@@ -301,6 +348,52 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
                                                     base_d + st.codes_off,
                                                     reinterpret_cast<const uint16_t*>(base_d + st.scales_off), y,
                                                     T, D, N, dtype_h, s));
+  if (rc == MOLE_OK && n_unique) *n_unique = U;
+  return rc;
+}
+
+int mole_nf3_host_stack_staging_size(int64_t T, int64_t L, int64_t N, int64_t D, size_t* bytes) {
+  if (!bytes) return MOLE_ERR_NULL;
+  if (T < 0 || L <= 0 || N <= 0 || D <= 0 || D % 64 != 0 || D > kMaxDim || T > kMaxDim || N > kMaxExperts ||
+      L > kMaxDim)
+    return MOLE_ERR_DIM;
+  *bytes = nf3_stack_staging(T, T, L, N, D, nullptr, nullptr);
+  return MOLE_OK;
+}
+
+int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
+                                 const uint8_t* const* codes_host, const uint16_t* const* scales_host,
+                                 int64_t L, int64_t V, int64_t N, int64_t D, void* stage_host,
+                                 void* stage_dev, size_t stage_bytes, size_t* codes_off,
+                                 size_t* scales_off, int nthreads, int64_t* n_unique, void* stream) {
+  if (T < 0 || L <= 0 || V <= 0 || N <= 0 || D <= 0 || D % 64 != 0 || D > kMaxDim || T > kMaxDim ||
+      N > kMaxExperts || L > kMaxDim)
+    return MOLE_ERR_DIM;
+  if (!codes_host || !scales_host || !stage_host || !stage_dev || !codes_off || !scales_off) return MOLE_ERR_NULL;
+  for (int64_t l = 0; l < L; ++l)
+    if (!codes_host[l] || !scales_host[l]) return MOLE_ERR_NULL;
+  if (T > 0 && !ids_host) return MOLE_ERR_NULL;
+  if (!aligned16(stage_host) || !aligned16(stage_dev)) return MOLE_ERR_ALIGN;
+  if (stage_bytes < nf3_stack_staging(T, T, L, N, D, nullptr, nullptr)) return MOLE_ERR_WORKSPACE;
+  if (T == 0) {
+    nf3_stack_staging(0, 0, L, N, D, codes_off, scales_off);
+    if (n_unique) *n_unique = 0;
+    return MOLE_OK;
+  }
+  hipStream_t s = as_stream(stream);
+  hipEvent_t ev;
+  int rc = stage_event(stage_host, &ev);
+  if (rc == MOLE_OK) rc = hip_status(hipEventSynchronize(ev));  // the last copy out of stage_host
+  if (rc != MOLE_OK) return rc;
+  std::vector<int64_t> uniq;
+  uint8_t* base_h = static_cast<uint8_t*>(stage_host);
+  rc = dedupe(ids_host, T, V, uniq, reinterpret_cast<int64_t*>(base_h));
+  if (rc != MOLE_OK) return rc;
+  const int64_t U = (int64_t)uniq.size();
+  const size_t total = nf3_stack_staging(T, U, L, N, D, codes_off, scales_off);
+  gather_rows_stack(uniq, codes_host, scales_host, L, N, D, base_h, codes_off, scales_off, nthreads);
+  rc = hip_status(hipMemcpyAsync(stage_dev, stage_host, total, hipMemcpyHostToDevice, s));
+  if (rc == MOLE_OK) rc = hip_status(hipEventRecord(ev, s));
   if (rc == MOLE_OK && n_unique) *n_unique = U;
   return rc;
 }

@@ -41,7 +41,7 @@ def test_header_declares_the_hot_path():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 2
+    assert lib.mole_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -115,6 +115,31 @@ def test_host_staging_size_and_errors(lib):
     assert f(*args(want - 1)) == WS  # too small: rejected before touching the stream
     assert f(*args(want, None)) == NULL
     assert f(*args(want, P(a + 8))) == ALIGN
+
+
+def test_host_stack_staging_size_and_errors(lib):
+    """Layer-stack prefetch: remap int64[T], then per layer U rows of codes
+    and of fp16 scales, each section 16-byte aligned (sized for U = T).
+    Errors are reported before any GPU call."""
+    T, L, N, D = 5, 3, 4, 128
+    r16 = lambda x: (x + 15) // 16 * 16
+    want = r16(T * 8) + L * (r16(T * N * 3 * D // 8) + r16(T * N * (D // 64) * 2))
+    assert mole.mole_nf3_host_stack_staging_size(T, L, N, D) == want
+    out = ctypes.c_size_t(0)
+    assert lib.mole_nf3_host_stack_staging_size(T, 0, N, D, ctypes.addressof(out)) == DIM
+    assert lib.mole_nf3_host_stack_staging_size(T, L, N, 96, ctypes.addressof(out)) == DIM
+    a = 0x1000
+    tabs = (ctypes.c_void_p * L)(a, a, a)
+    nul = (ctypes.c_void_p * L)(a, None, a)
+    off = (ctypes.c_size_t * L)()
+    f = lib.mole_prefetch_nf3_host_stack
+    call = lambda codes=tabs, stage=P(a), nbytes=want, n=N: f(
+        P(a), T, ctypes.addressof(codes), ctypes.addressof(tabs), L, 100, n, D, stage, P(a), nbytes,
+        ctypes.addressof(off), ctypes.addressof(off), 0, None, None)
+    assert call(nbytes=want - 1) == WS
+    assert call(codes=nul) == NULL
+    assert call(stage=P(a + 4)) == ALIGN
+    assert call(n=65) == DIM
 
 
 def test_build_argument_errors(lib):

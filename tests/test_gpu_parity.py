@@ -290,6 +290,41 @@ def test_combine_nf3_host_resident(T):
         assert combine_rel_err(y_host, ref) <= COMBINE_TOL
 
 
+def test_nf3_host_stack_prefetch_matches_device_path():
+    """Three layers' NF3 tables in host memory, one step's rows prefetched in
+    one transfer; every layer's combine on the staged rows equals the
+    device-resident NF3 combine bit for bit, and the oracle within the
+    combine bar.  Two steps in a row through the same staging area."""
+    V, N, D, L = 700, 8, 512, 3
+    CB, SB = 3 * D // 8, D // 64
+    tabs = []
+    for l in range(L):
+        codes, scales, _ = oracle.pack_nf3(rand_table(300 + l, V, N, D, "bf16", std=0.02))
+        tabs.append((codes, scales))
+    codes_h = [torch.from_numpy(c).pin_memory() for c, _ in tabs]
+    scales_h = [torch.from_numpy(s.view(np.int16)).pin_memory() for _, s in tabs]
+    for step, T in enumerate((97, 40)):
+        ids = synth.zipf_ids(rng(400 + step), V, T, rng(401).permutation(V))
+        hws = [rand_hw(500 + 10 * step + l, T, N, D, "bf16", wstd=0.3) for l in range(L)]
+        nbytes = mole.mole_nf3_host_stack_staging_size(97, L, N, D)
+        if step == 0:
+            stage_h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+            stage_d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        remap, layers = mole.mole_prefetch_nf3_host_stack(torch.from_numpy(ids), codes_h, scales_h,
+                                                          stage_h, stage_d)
+        U = layers[0][0].shape[0]
+        assert U == np.unique(ids).size
+        for l in range(L):
+            h, w_r = hws[l]
+            y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+            mole.mole_lookup_combine_nf3(remap, dev(h), dev(w_r), layers[l][0], layers[l][1], y)
+            torch.cuda.synchronize()
+            got = host(y)
+            np.testing.assert_array_equal(got, run_nf3(ids, h, w_r, tabs[l][0], tabs[l][1]))
+            ref = oracle.lookup_combine_nf3(ids, h, w_r, tabs[l][0], tabs[l][1])
+            assert combine_rel_err(got, ref) <= COMBINE_TOL
+
+
 # ----------------------------------------------------------------------------
 # LUT build
 # ----------------------------------------------------------------------------
