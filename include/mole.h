@@ -212,8 +212,10 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
  * mole_prefetch_nf3_host_stack: dedupe ids_host once, gather the U distinct
  * rows of every layer's host table (codes_host[l] [V][N][3D/8],
  * scales_host[l] [V][N][D/64], l < L; pinned or pageable) into stage_host
- * (pinned, 16-byte aligned), then enqueue on `stream` ONE host->device copy
- * of the used part into stage_dev.  codes_off[l] / scales_off[l] (host
+ * (pinned, 16-byte aligned) and enqueue on `stream` the host->device copy
+ * of the used part into stage_dev -- in up to four pieces of consecutive
+ * layers, each enqueued as soon as its rows are gathered, so the bus moves
+ * one piece while the next is gathered.  codes_off[l] / scales_off[l] (host
  * arrays of L entries) receive the byte offsets of layer l's sections, so
  * layer l's combine, issued on the same stream after this call, is
  *     mole_lookup_combine_nf3(stage_dev, h_l, w_r_l,

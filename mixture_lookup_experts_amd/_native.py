@@ -236,8 +236,8 @@ def mole_prefetch_nf3_host_stack(ids_host, codes_host, scales_host, stage_host, 
                                  nthreads: int = 0, stream=None):
     """One decode step's NF3 rows for every layer of a stack, gathered on the
     host from the L host tables (lists codes_host[l] [V,N,3D/8] uint8 and
-    scales_host[l] [V,N,D/64] int16) and moved in one host->device copy into
-    stage_dev.  Returns (remap [T] int64, [(codes_l [U,N,3D/8], scales_l
+    scales_host[l] [V,N,D/64] int16) and moved to stage_dev (one copy, in up
+    to four pieces overlapped with the gather).  Returns (remap [T] int64, [(codes_l [U,N,3D/8], scales_l
     [U,N,D/64]) for each layer]) -- views into stage_dev to hand to
     mole_lookup_combine_nf3 layer by layer on the same stream."""
     L = len(codes_host)

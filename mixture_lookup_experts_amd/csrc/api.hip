@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <thread>
@@ -136,36 +137,64 @@ size_t nf3_stack_staging(int64_t T, int64_t U, int64_t L, int64_t N, int64_t D, 
   return off;
 }
 
-// Gather of the U distinct rows of L tables at once, split over threads by
-// flattened (layer, row) index, so a stack of small per-layer gathers still
-// spreads over the host cores.
-void gather_rows_stack(const std::vector<int64_t>& uniq, const uint8_t* const* codes, const uint16_t* const* scales,
-                       int64_t L, int64_t N, int64_t D, uint8_t* base, const size_t* codes_off,
-                       const size_t* scales_off, int nthreads) {
+// Gather of the U distinct rows of L tables, pipelined with the host->device
+// copy: the layers are cut into up to kStackChunks consecutive chunks; every
+// worker thread copies its share of chunk k's (layer, row) pairs, then
+// counts itself done with k; the calling thread enqueues chunk k's copy
+// (one contiguous byte range of the staging area) as soon as every worker
+// is done with it, so the bus moves chunk k while chunk k+1 is gathered.
+// Returns a mole status.
+constexpr int kStackChunks = 4;
+
+int gather_copy_stack(const std::vector<int64_t>& uniq, const uint8_t* const* codes, const uint16_t* const* scales,
+                      int64_t L, int64_t N, int64_t D, uint8_t* base_h, uint8_t* base_d,
+                      const size_t* codes_off, const size_t* scales_off, size_t total, int nthreads, hipStream_t s) {
   const size_t crow = (size_t)(N * 3 * D / 8), srow = (size_t)(N * (D / 64));
-  const int64_t U = (int64_t)uniq.size(), total = L * U;
-  auto work = [&](int64_t lo, int64_t hi) {
-    for (int64_t i = lo; i < hi; ++i) {
+  const int64_t U = (int64_t)uniq.size();
+  const int nchunks = (int)std::min<int64_t>(L, kStackChunks);
+  // chunk k = layers [l0(k), l0(k+1)); bytes [begin(k), begin(k+1)) of the staging area
+  auto l0 = [&](int k) { return (int64_t)k * L / nchunks; };
+  auto begin = [&](int k) { return k == 0 ? (size_t)0 : (k == nchunks ? total : codes_off[l0(k)]); };
+  auto gather = [&](int k, int64_t lo, int64_t hi) {  // flattened (layer, row) range within chunk k
+    const int64_t first = l0(k) * U;
+    for (int64_t i = first + lo; i < first + hi; ++i) {
       const int64_t l = i / U, u = i - l * U;
-      std::memcpy(base + codes_off[l] + (size_t)u * crow, codes[l] + (size_t)uniq[u] * crow, crow);
-      std::memcpy(reinterpret_cast<uint16_t*>(base + scales_off[l]) + (size_t)u * srow,
+      std::memcpy(base_h + codes_off[l] + (size_t)u * crow, codes[l] + (size_t)uniq[u] * crow, crow);
+      std::memcpy(reinterpret_cast<uint16_t*>(base_h + scales_off[l]) + (size_t)u * srow,
                   scales[l] + (size_t)uniq[u] * srow, srow * 2);
     }
   };
   int nt = nthreads > 0 ? nthreads : (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
-  if ((size_t)total * (crow + 2 * srow) < ((size_t)1 << 20)) nt = 1;  // threads are not worth it below ~1 MB
-  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(total, 1));
+  if ((size_t)(L * U) * (crow + 2 * srow) < ((size_t)1 << 20)) nt = 1;  // threads are not worth it below ~1 MB
+  int rc = MOLE_OK;
   if (nt <= 1) {
-    work(0, total);
-    return;
+    for (int k = 0; k < nchunks && rc == MOLE_OK; ++k) {
+      gather(k, 0, (l0(k + 1) - l0(k)) * U);
+      rc = hip_status(hipMemcpyAsync(base_d + begin(k), base_h + begin(k), begin(k + 1) - begin(k),
+                                     hipMemcpyHostToDevice, s));
+    }
+    return rc;
   }
+  std::vector<std::atomic<int>> done(nchunks);
+  for (auto& d : done) d.store(0);
+  auto worker = [&](int w) {
+    for (int k = 0; k < nchunks; ++k) {
+      const int64_t n = (l0(k + 1) - l0(k)) * U, per = (n + nt - 1) / nt;
+      const int64_t lo = std::min<int64_t>(n, w * per), hi = std::min<int64_t>(n, lo + per);
+      if (lo < hi) gather(k, lo, hi);
+      done[k].fetch_add(1, std::memory_order_release);
+    }
+  };
   std::vector<std::thread> pool;
-  const int64_t per = (total + nt - 1) / nt;
-  for (int i = 0; i < nt; ++i) {
-    const int64_t lo = i * per, hi = std::min<int64_t>(total, lo + per);
-    if (lo < hi) pool.emplace_back(work, lo, hi);
+  for (int w = 0; w < nt; ++w) pool.emplace_back(worker, w);
+  for (int k = 0; k < nchunks; ++k) {
+    while (done[k].load(std::memory_order_acquire) < nt) std::this_thread::yield();
+    if (rc == MOLE_OK)
+      rc = hip_status(hipMemcpyAsync(base_d + begin(k), base_h + begin(k), begin(k + 1) - begin(k),
+                                     hipMemcpyHostToDevice, s));
   }
   for (auto& th : pool) th.join();
+  return rc;
 }
 
 }  // namespace
@@ -391,8 +420,8 @@ int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
   if (rc != MOLE_OK) return rc;
   const int64_t U = (int64_t)uniq.size();
   const size_t total = nf3_stack_staging(T, U, L, N, D, codes_off, scales_off);
-  gather_rows_stack(uniq, codes_host, scales_host, L, N, D, base_h, codes_off, scales_off, nthreads);
-  rc = hip_status(hipMemcpyAsync(stage_dev, stage_host, total, hipMemcpyHostToDevice, s));
+  rc = gather_copy_stack(uniq, codes_host, scales_host, L, N, D, base_h, static_cast<uint8_t*>(stage_dev),
+                         codes_off, scales_off, total, nthreads, s);
   if (rc == MOLE_OK) rc = hip_status(hipEventRecord(ev, s));
   if (rc == MOLE_OK && n_unique) *n_unique = U;
   return rc;
