@@ -13,7 +13,11 @@ Definitions followed (MoLE article, the "ICML 2025 Spotlight | MoLE" page):
     vocabulary, then retrieval of each token's rows by id;
   * training section -- all routed experts active, router on the contextual
     hidden state: gates = softmax(W_r h) over all N experts;
-  * results section -- the table compressed to 3 bits ("e.g. NF3").
+  * results section -- the table compressed to 3 bits ("e.g. NF3");
+  * training section and complexity analysis -- shared experts keep reading
+    the contextual hidden state and are the only experts still computed at
+    inference, so a MoLE block adds shared FFN + routed lookup to the
+    residual stream (``shared_ffn``, ``layer_forward``).
 """
 from __future__ import annotations
 
@@ -71,6 +75,7 @@ def _load():
             "oracle_unpack_nf3": (I, [P, I64, I64, P]),
             "oracle_dequant_nf3": (I, [P, P, I64, I64, P]),
             "oracle_lookup_combine_nf3": (I, [P, P, P, I, P, P, I64, I64, I64, I64, P, I]),
+            "oracle_shared_ffn": (I, [P, P, P, I, I64, I64, I64, P, I]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -226,3 +231,30 @@ def lookup_combine_nf3(ids, h, w_r, codes, scales, nthreads: int = 0) -> np.ndar
                                            _ptr(scales), T, V, D, N, _ptr(y), nthreads)
     _check(rc, "lookup_combine_nf3")
     return y
+
+
+def shared_ffn(h, w_s_up, w_s_down, nthreads: int = 0) -> np.ndarray:
+    """out[t, :] = W_s_down . GELU(W_s_up . h[t]) in fp64 (exact-form GELU,
+    no biases).  h [T,D], w_s_up [F,D], w_s_down [D,F], one dtype."""
+    T, D = h.shape
+    F, D2 = w_s_up.shape
+    assert D2 == D and w_s_down.shape == (D, F)
+    dt = _dtype_code(h)
+    assert _dtype_code(w_s_up) == dt and _dtype_code(w_s_down) == dt
+    out = np.zeros((T, D), dtype=np.float64)
+    _check(_load().oracle_shared_ffn(_ptr(h), _ptr(w_s_up), _ptr(w_s_down), dt, T, D, F,
+                                     _ptr(out), nthreads), "shared_ffn")
+    return out
+
+
+def layer_forward(ids, h, w_r, lut, w_s_up, w_s_down, x=None, nthreads: int = 0) -> np.ndarray:
+    """One MoLE block at inference, in fp64:
+        out[t, :] = x[t, :] + shared_ffn(h)[t, :] + lookup_combine(ids, h, w_r, lut)[t, :]
+    (the residual stream x, fp32 [T,D], is taken as zero when None).  The
+    shared expert and the router read the contextual hidden state h; the
+    routed experts are the table lookups."""
+    out = shared_ffn(h, w_s_up, w_s_down, nthreads) + lookup_combine(ids, h, w_r, lut, nthreads)
+    if x is not None:
+        assert x.shape == out.shape and x.dtype == np.float32
+        out = out + x.astype(np.float64)
+    return out

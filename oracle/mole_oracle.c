@@ -429,3 +429,50 @@ int oracle_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r
   free(gates);
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Shared expert (training section: shared experts, like the router, keep   */
+/* reading the previous layer's output; complexity analysis: at inference   */
+/* the shared experts are the only experts still computed).                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One shared-expert FFN with the routed experts' form (D -> F -> D, GELU in
+ * its exact form, no biases), applied to every token's hidden state:
+ *   u[f] = sum_d h[t][d] * W_s_up[f][d];   g[f] = GELU(u[f]);
+ *   out[t][d] = sum_f g[f] * W_s_down[d][f].
+ * w_s_up [F][D], w_s_down [D][F], h [T][D], all of `dtype`; out [T][D] fp64.
+ */
+int oracle_shared_ffn(const void* h, const void* w_s_up, const void* w_s_down,
+                      int dtype, int64_t T, int64_t D, int64_t F, double* out,
+                      int nthreads) {
+  if (!dtype_ok(dtype) || T < 0 || D <= 0 || F <= 0) return OR_ERR_ARG;
+  set_threads(nthreads);
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* g = (double*)malloc((size_t)F * sizeof(double));
+    if (!g) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic)
+    for (int64_t t = 0; t < T; ++t) {
+      if (!g) continue;
+      for (int64_t f = 0; f < F; ++f) {
+        double u = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+          u += load_elem(h, dtype, t * D + d) * load_elem(w_s_up, dtype, f * D + d);
+        g[f] = oracle_gelu(u);
+      }
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t f = 0; f < F; ++f)
+          acc += g[f] * load_elem(w_s_down, dtype, d * F + f);
+        out[t * D + d] = acc;
+      }
+    }
+    free(g);
+  }
+  return failed ? OR_ERR_MEM : OR_OK;
+}
