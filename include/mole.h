@@ -146,6 +146,40 @@ int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
                             void* stream);
 
 /* ------------------------------------------------------------------------
+ * The MoLE block at inference (training section: shared experts and the
+ * router keep reading the previous layer's output; complexity analysis: at
+ * inference the shared experts are the only experts still computed, the
+ * routed ones having become table lookups):
+ *
+ *   x[t][:] += W_s_down . GELU(W_s_up . h[t]) + y[t][:]
+ *
+ * where y is mole_lookup_combine(ids, h, w_r, lut) and the shared expert
+ * has the routed experts' form (D -> F -> D, GELU(u) = u * Phi(u), no
+ * biases).  x is the residual stream, read and written in place; pass a
+ * zero-filled x to get the two expert terms alone.
+ *   ids [T] int64   h [T][D]   w_r [N][D]   lut [V][N][D]
+ *   w_s_up [F][D]   w_s_down [D][F]   (output-major, like the routed experts)
+ *   x [T][D] fp32 (read and written)
+ * dtype must be MOLE_BF16 (MOLE_ERR_UNSUPPORTED for MOLE_F32): bf16 inputs,
+ * fp32 accumulation, the hidden activation rounded to bf16 between the two
+ * products as in mole_build_lut, everything after the products in fp32.
+ * Needs D % 8 == 0, F % 8 == 0 (MOLE_ERR_DIM) and D, F <= 2^22
+ * (MOLE_ERR_UNSUPPORTED); 1 <= N <= 64.  T == 0 is a no-op.
+ *
+ * workspace: device scratch (16-byte aligned) of at least the size that
+ * mole_layer_workspace_size(T, D, F) returns (0 for T == 0): the routed y,
+ * the hidden activations and, for short batches, per-split partial sums.
+ * Contents on return are unspecified.  Enqueued on `stream`, asynchronous,
+ * no memset (capturable in a HIP graph).
+ * ------------------------------------------------------------------------ */
+int mole_layer_workspace_size(int64_t T, int64_t D, int64_t F, size_t* bytes);
+
+int mole_layer_forward(const int64_t* ids, const void* h, const void* w_r, const void* lut,
+                       const void* w_s_up, const void* w_s_down, float* x, int64_t T, int64_t V,
+                       int64_t D, int64_t N, int64_t F, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host-resident NF3 table (inference section: after reparameterisation the
  * table lives in lower-tier storage such as CPU memory, each token's
  * entries are looked up there and only the retrieved vectors are loaded

@@ -71,6 +71,8 @@ def library():
                                                  P]),
             "mole_lookup_combine_nf3_host": (I, [P, P, P, P, P, P, P, SZ, P,
                                                  I64, I64, I64, I64, I, I, P, P]),
+            "mole_layer_workspace_size": (I, [I64, I64, I64, P]),
+            "mole_layer_forward": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -291,3 +293,34 @@ def mole_lookup_combine_nf3_host(ids_host, h, w_r, codes_host, scales_host, stag
         _ptr(stage_host), _ptr(stage_dev), nbytes, _ptr(y), T, V, D, N, _dtype(h), nthreads,
         ctypes.addressof(u), _stream(stream)))
     return int(u.value)
+
+
+def mole_layer_workspace_size(T: int, D: int, F: int) -> int:
+    """Workspace bytes mole_layer_forward needs for T tokens (0 for T == 0)."""
+    out = ctypes.c_size_t(0)
+    _check("mole_layer_workspace_size",
+           library().mole_layer_workspace_size(T, D, F, ctypes.addressof(out)))
+    return int(out.value)
+
+
+def mole_layer_forward(ids, h, w_r, lut, w_s_up, w_s_down, x, workspace, stream=None) -> None:
+    """The MoLE block in place on the residual stream x [T,D] (fp32):
+    x += W_s_down . GELU(W_s_up . h) + sum_e softmax(w_r . h)[e] * lut[ids, e, :].
+    h [T,D], w_r [N,D], lut [V,N,D], w_s_up [F,D], w_s_down [D,F] (bf16);
+    workspace: a uint8 device tensor of mole_layer_workspace_size(T, D, F) bytes."""
+    V, N, D = lut.shape
+    T = ids.numel()
+    _need(w_s_up.dim() == 2 and w_s_down.dim() == 2, "w_s_up [F,D], w_s_down [D,F]")
+    F = w_s_up.shape[0]
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(x.shape) == (T, D)
+          and tuple(w_s_up.shape) == (F, D) and tuple(w_s_down.shape) == (D, F),
+          "ids [T], h [T,D], w_r [N,D], lut [V,N,D], w_s_up [F,D], w_s_down [D,F], x [T,D]")
+    _need(ids.dtype == torch.int64 and x.dtype == torch.float32, "ids int64, x float32")
+    _need(h.dtype == w_r.dtype == lut.dtype == w_s_up.dtype == w_s_down.dtype,
+          "h, w_r, lut and the shared weights share one dtype")
+    for t in (ids, h, w_r, lut, w_s_up, w_s_down, x):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mole_layer_forward", library().mole_layer_forward(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut), _ptr(w_s_up), _ptr(w_s_down), _ptr(x),
+        T, V, D, N, F, _dtype(h), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -218,7 +218,7 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 3; }
+int mole_abi_version(void) { return 4; }
 
 int mole_nf3_levels(float* levels_host) {
   if (!levels_host) return MOLE_ERR_NULL;
@@ -306,6 +306,35 @@ int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r, 
     return MOLE_ERR_ALIGN;
   return hip_status(mole::launch_lookup_combine_nf3(ids, h, w_r, codes, scales, y, T, D, N, dtype_h,
                                                     as_stream(stream)));
+}
+
+int mole_layer_workspace_size(int64_t T, int64_t D, int64_t F, size_t* bytes) {
+  if (!bytes) return MOLE_ERR_NULL;
+  if (T < 0 || D <= 0 || F <= 0 || T > kMaxDim || D > kMaxDim || F > kMaxDim) return MOLE_ERR_DIM;
+  *bytes = T == 0 ? 0 : mole::layer_plan(T, D, F).total;
+  return MOLE_OK;
+}
+
+int mole_layer_forward(const int64_t* ids, const void* h, const void* w_r, const void* lut, const void* w_s_up,
+                       const void* w_s_down, float* x, int64_t T, int64_t V, int64_t D, int64_t N, int64_t F,
+                       int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (F <= 0 || F > kMaxDim) return MOLE_ERR_DIM;
+  if (dtype != MOLE_BF16) return MOLE_ERR_UNSUPPORTED;
+  if (D % 8 != 0 || F % 8 != 0) return MOLE_ERR_DIM;
+  // The projections address 256-row operand panels with 32-bit byte offsets.
+  if (D > kMaxPanelStride || F > kMaxPanelStride) return MOLE_ERR_UNSUPPORTED;
+  if (T == 0) return MOLE_OK;
+  if (!ids || !h || !w_r || !lut || !w_s_up || !w_s_down || !x || !workspace) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(lut) || !aligned16(w_s_up) ||
+      !aligned16(w_s_down) || !aligned16(x) || !aligned16(workspace))
+    return MOLE_ERR_ALIGN;
+  if (workspace_bytes < mole::layer_plan(T, D, F).total) return MOLE_ERR_WORKSPACE;
+  return hip_status(mole::launch_layer_forward(ids, (const uint16_t*)h, (const uint16_t*)w_r, (const uint16_t*)lut,
+                                               (const uint16_t*)w_s_up, (const uint16_t*)w_s_down, x, T, D, N, F,
+                                               workspace, as_stream(stream)));
 }
 
 int mole_gather_nf3_host(const int64_t* ids_host, int64_t T, const uint8_t* codes_host,

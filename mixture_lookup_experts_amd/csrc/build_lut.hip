@@ -47,32 +47,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // erff (fp32 path).
 __device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f)); }
 
-// GELU for the bf16 path: u * Phi(u) with Phi - 1/2 (an odd function)
-// replaced on [-4, 4] by the odd polynomial s*(c0 + c1 s^2 + ... + c9 s^18),
-// s = u/4, a least-squares fit to the normal CDF on Chebyshev nodes
-// (gelu_poly_fit.py next to this file derives and checks it): |error| <=
-// 6e-6 in fp32, and Phi is clamped to [0, 1] outside (1 - Phi(4) = 3.2e-5).
-// The hidden activation is rounded to bf16 (relative 2^-9) right after, so
-// the approximation is invisible there; it costs ~14 full-rate VALU slots and
-// no transcendental, which matters because this epilogue runs once per
-// hidden unit and vocabulary row.
-__device__ __forceinline__ float gelu_poly(float u) {
-  const float s = __builtin_amdgcn_fmed3f(u, -4.0f, 4.0f) * 0.25f;
-  const float s2 = s * s;
-  float p = -1.005731821e+00f;
-  p = fmaf(p, s2, 6.118065357e+00f);
-  p = fmaf(p, s2, -1.688562202e+01f);
-  p = fmaf(p, s2, 2.834799385e+01f);
-  p = fmaf(p, s2, -3.288965607e+01f);
-  p = fmaf(p, s2, 2.843501091e+01f);
-  p = fmaf(p, s2, -1.914556694e+01f);
-  p = fmaf(p, s2, 1.018382359e+01f);
-  p = fmaf(p, s2, -4.254103661e+00f);
-  p = fmaf(p, s2, 1.595752358e+00f);
-  const float phi = __builtin_amdgcn_fmed3f(fmaf(s, p, 0.5f), 0.0f, 1.0f);
-  return u * phi;
-}
-
 // Epilogue modes.  Direct: each lane stores 4 consecutive bf16 (8 bytes) of
 // one row; the 32 rows of a store instruction are merged into full cache
 // lines in L2 when rows are close together.  Staged: the tile goes through
@@ -402,6 +376,13 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+// GELU(A . B^T) rounded to bf16, one 256x256 tile per workgroup (the
+// shared-expert up-projection of the MoLE block uses it for long batches).
+hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
+                                 int64_t ldc, int M, int N, int K, hipStream_t s) {
+  return launch_gemm<kBM, kBN, kEpiGelu>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
 }
 
 // ---------------------------------------------------------------------------

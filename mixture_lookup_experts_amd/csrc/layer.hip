@@ -1,0 +1,316 @@
+// The MoLE block at inference: residual stream x plus the shared expert's
+// FFN plus the router-weighted table rows,
+//
+//   x[t][:] += W_s_down . GELU(W_s_up . h[t]) + sum_e g[t][e] * LUT[id_t][e][:]
+//
+// (MoLE article, training section: shared experts and the router keep
+// reading the previous layer's output; complexity analysis: at inference
+// only the shared experts are still computed, the routed ones are lookups.)
+//
+// Launch sequence on one stream, all scratch in the caller's workspace:
+//   1. lookup-combine of the routed experts into yr (fp32 [T][D]);
+//   2. up-projection G = GELU(h . W_s_up^T), rounded to bf16 ([T][F]):
+//      long batches use the 256x256 build GEMM, shorter ones the mid-size
+//      GEMM below, split over K into fp32 partials plus a GELU reduction
+//      when the batch alone cannot fill the chip;
+//   3. down-projection of G, added with yr into x: in the GEMM epilogue when
+//      there is no K split, else fp32 partials and one reduction pass.
+//
+// Mid-size GEMM (C = A . B^T, A [M][lda] bf16 = activations, B [N][ldb]
+// bf16 = a weight matrix stored output-major): a 256-thread workgroup owns
+// a (32*RM) x 128 output tile; each wave owns 32 output columns and all
+// 32*RM rows, as RM v_mfma_f32_32x32x16_bf16 tiles.  Per 64-wide K slice
+// the A panel is staged once in LDS (shared by the four waves; rows of 128
+// bytes, 16-byte segment s of row r stored at s ^ ((r/2) & 7)) and each
+// wave streams its own 32 weight rows straight into registers, 64
+// contiguous bytes per lane.  Inside a slice the K order is permuted the
+// same way for both operands (lane half h, K step i covers k = 32h + 8i ..
+// 32h + 8i + 7), which leaves every dot product unchanged and lets a lane
+// fetch its 64 weight bytes in one run.  Double-buffered LDS, one barrier
+// per slice.  Operands are read through buffer resources, so rows past the
+// edge and K past the split's end read zeros.
+#include <algorithm>
+
+#include "mole_device.hpp"
+#include "mole_kernels.hpp"
+
+namespace mole {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every record: loads read 0
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kMidBN = 128;             // output columns per mid-size tile (4 waves x 32)
+constexpr int kTargetBlocks = 512;      // two workgroups per compute unit
+
+enum { kMidGelu = 0, kMidPartial = 1, kMidAccum = 2 };
+
+struct MidArgs {
+  const uint16_t* A; int64_t lda;  // [M][lda]
+  const uint16_t* B; int64_t ldb;  // [N][ldb]
+  void* C; int64_t ldc;            // GELU: bf16 [M][ldc]; partial: fp32 [splits][M][ldc]; accum: fp32 x [M][ldc]
+  int64_t sCz;                     // partial: elements between splits
+  const float* yadd;               // accum: fp32 [M][ldc] added to x with the product
+  int M, N, K, Ks, tiles_n;
+};
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+template <int RM, int EPI>
+__global__ __launch_bounds__(256) void gemm_mid_kernel(MidArgs p) {
+  constexpr int BM = 32 * RM;
+  __shared__ uint4 lds[2][BM * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int tm = blockIdx.x / p.tiles_n, tn = blockIdx.x % p.tiles_n;
+  const int m0 = tm * BM, n0 = tn * kMidBN;
+  const int kb = blockIdx.y * p.Ks;
+  const int ke = p.K - kb < p.Ks ? p.K : kb + p.Ks;
+  const int rows_a = p.M - m0 < BM ? p.M - m0 : BM;
+  const int rows_b = p.N - n0 < kMidBN ? p.N - n0 : kMidBN;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.A + (int64_t)m0 * p.lda), (short)0, (int)(rows_a * p.lda * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.B + (int64_t)n0 * p.ldb), (short)0, (int)(rows_b * p.ldb * 2), kRsrcWord3);
+
+  // A staging: thread t moves segment t % 8 of rows t / 8 + 32 i, i < RM.
+  const int aseg = tid & 7, arow0 = tid >> 3;
+  uint32_t aoff[RM];
+  int alds[RM];
+#pragma unroll
+  for (int i = 0; i < RM; ++i) {
+    const int row = arow0 + 32 * i;
+    aoff[i] = row < rows_a ? (uint32_t)(row * p.lda * 2 + aseg * 16) : kOob;
+    alds[i] = row * 8 + (aseg ^ ((row >> 1) & 7));
+  }
+  // Weight rows: lane l of wave w reads row 32 w + l % 32, K values 32 h .. 32 h + 31 of the slice.
+  const int brow = 32 * wave + l32;
+  const uint32_t boff = brow < rows_b ? (uint32_t)(brow * p.ldb * 2 + half * 64) : kOob;
+
+  uint4 astg[RM], bcur[4], bnxt[4];
+  auto load_slice = [&](int k0, uint4* bdst) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i) astg[i] = buf_load16(ra, k0 + aseg * 8 < ke ? aoff[i] + (uint32_t)k0 * 2u : kOob);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      bdst[c] = buf_load16(rb, k0 + 32 * half + 8 * c < ke ? boff + (uint32_t)(k0 + 8 * c) * 2u : kOob);
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i) lds[buf][alds[i]] = astg[i];
+  };
+
+  f32x16_t acc[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[r][q] = 0.f;
+
+  const int ns = ke > kb ? (ke - kb + 63) / 64 : 0;
+  if (ns > 0) {
+    load_slice(kb, bcur);
+    store_a(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < ns; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < ns) load_slice(kb + (s + 1) * 64, bnxt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sg = 4 * half + i;
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        const int row = 32 * r + l32;
+        const uint4 a = lds[buf][row * 8 + (sg ^ ((row >> 1) & 7))];
+        // Operands swapped (weights as the matrix-core "A"): lane l then holds
+        // C[m = l % 32][n = 8 (q / 4) + 4 (l / 32) + q % 4] in accumulator q.
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bcur[i]),
+                                                         __builtin_bit_cast(bf16x8_t, a), acc[r], 0, 0, 0);
+      }
+    }
+    if (s + 1 < ns) store_a(buf ^ 1);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bcur[c] = bnxt[c];
+  }
+
+  // Epilogue: lane l, accumulator group g (4 registers) = 4 consecutive columns.
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    const int m = m0 + 32 * r + l32;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int n = n0 + 32 * wave + 8 * g + 4 * half;
+      if (n >= p.N) continue;
+      const float v0 = acc[r][4 * g], v1 = acc[r][4 * g + 1], v2 = acc[r][4 * g + 2], v3 = acc[r][4 * g + 3];
+      const int64_t o = (int64_t)m * p.ldc + n;
+      if constexpr (EPI == kMidGelu) {
+        uint2 w;
+        w.x = pack_bf16x2(gelu_poly(v0), gelu_poly(v1));
+        w.y = pack_bf16x2(gelu_poly(v2), gelu_poly(v3));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + o) = w;
+      } else if constexpr (EPI == kMidPartial) {
+        float* dst = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.sCz + o;
+        *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
+      } else {
+        float* dst = static_cast<float*>(p.C) + o;
+        const float4 xv = *reinterpret_cast<const float4*>(dst);
+        const float4 yv = *reinterpret_cast<const float4*>(p.yadd + o);
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(xv.x + (v0 + yv.x), xv.y + (v1 + yv.y), xv.z + (v2 + yv.z), xv.w + (v3 + yv.w));
+      }
+    }
+  }
+}
+
+// G[i] = bf16(GELU(sum_s P[s][i])), four elements per thread and step.
+__global__ __launch_bounds__(256) void gelu_reduce_kernel(const float* __restrict__ P, int S, int64_t count,
+                                                          uint16_t* __restrict__ G) {
+  const int64_t n4 = count / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 a = reinterpret_cast<const float4*>(P)[i];
+    for (int s = 1; s < S; ++s) {
+      const float4 b = reinterpret_cast<const float4*>(P + (int64_t)s * count)[i];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    uint2 w;
+    w.x = pack_bf16x2(gelu_poly(a.x), gelu_poly(a.y));
+    w.y = pack_bf16x2(gelu_poly(a.z), gelu_poly(a.w));
+    reinterpret_cast<uint2*>(G)[i] = w;
+  }
+}
+
+// x[i] += yr[i] + sum_s P[s][i].
+__global__ __launch_bounds__(256) void add_reduce_kernel(const float* __restrict__ P, int S, int64_t count,
+                                                         const float* __restrict__ yr, float* __restrict__ x) {
+  const int64_t n4 = count / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4 a = reinterpret_cast<const float4*>(P)[i];
+    for (int s = 1; s < S; ++s) {
+      const float4 b = reinterpret_cast<const float4*>(P + (int64_t)s * count)[i];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    const float4 y = reinterpret_cast<const float4*>(yr)[i];
+    float4 v = reinterpret_cast<float4*>(x)[i];
+    v.x += a.x + y.x; v.y += a.y + y.y; v.z += a.z + y.z; v.w += a.w + y.w;
+    reinterpret_cast<float4*>(x)[i] = v;
+  }
+}
+
+template <int RM, int EPI>
+hipError_t launch_mid_rm(const MidArgs& p, int tiles_m, int splits, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_mid_kernel<RM, EPI>), dim3((unsigned)(tiles_m * p.tiles_n), (unsigned)splits), dim3(256),
+                     0, s, p);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_mid(int rm, const MidArgs& p, int splits, hipStream_t s) {
+  const int tiles_m = (p.M + 32 * rm - 1) / (32 * rm);
+  switch (rm) {
+    case 1: return launch_mid_rm<1, EPI>(p, tiles_m, splits, s);
+    case 2: return launch_mid_rm<2, EPI>(p, tiles_m, splits, s);
+    default: return launch_mid_rm<4, EPI>(p, tiles_m, splits, s);
+  }
+}
+
+// K splits for a projection with `tiles` output tiles: enough workgroups to
+// fill the chip, at least 128 of K per split, and partials no larger than
+// the weight matrix they come from (sp * T * out * 4 <= K * out * 2).
+int pick_splits(int64_t tiles, int64_t T, int64_t K) {
+  int64_t sp = (kTargetBlocks + tiles - 1) / tiles;
+  sp = std::min<int64_t>(sp, std::max<int64_t>(1, K / 128));
+  sp = std::min<int64_t>(sp, std::max<int64_t>(1, K / (2 * T)));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(sp, 16));
+}
+
+inline size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+// Workgroups for a grid-stride pass over n4 groups of four elements.
+unsigned grid_1d(int64_t n4) {
+  const int64_t b = (n4 + 255) / 256;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 4096));
+}
+
+}  // namespace
+
+LayerPlan layer_plan(int64_t T, int64_t D, int64_t F) {
+  LayerPlan pl{};
+  pl.rm = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
+  const int64_t bm = 32 * pl.rm;
+  const int64_t tiles_m = (T + bm - 1) / bm;
+  // The 256x256 GEMM needs a full chip's worth of tiles to beat the mid-size one.
+  pl.big_up = ((T + 255) / 256) * ((F + 255) / 256) >= 256;
+  pl.s_up = pl.big_up ? 1 : pick_splits(tiles_m * ((F + kMidBN - 1) / kMidBN), T, D);
+  pl.s_down = pick_splits(tiles_m * ((D + kMidBN - 1) / kMidBN), T, F);
+  pl.ks_up = ((D + pl.s_up - 1) / pl.s_up + 63) / 64 * 64;
+  pl.ks_down = ((F + pl.s_down - 1) / pl.s_down + 63) / 64 * 64;
+  pl.s_up = (int)((D + pl.ks_up - 1) / pl.ks_up);
+  pl.s_down = (int)((F + pl.ks_down - 1) / pl.ks_down);
+  const size_t yr = (size_t)T * (size_t)D * 4u;
+  const size_t g = (size_t)T * (size_t)F * 2u;
+  const size_t p_up = pl.s_up > 1 ? (size_t)pl.s_up * (size_t)T * (size_t)F * 4u : 0;
+  const size_t p_down = pl.s_down > 1 ? (size_t)pl.s_down * (size_t)T * (size_t)D * 4u : 0;
+  pl.yr_off = 0;
+  pl.g_off = round256(yr);
+  pl.p_off = pl.g_off + round256(g);
+  pl.total = pl.p_off + round256(std::max(p_up, p_down));
+  return pl;
+}
+
+hipError_t launch_layer_forward(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, const uint16_t* lut,
+                                const uint16_t* w_s_up, const uint16_t* w_s_down, float* x, int64_t T, int64_t D,
+                                int64_t N, int64_t F, void* ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const LayerPlan pl = layer_plan(T, D, F);
+  char* base = static_cast<char*>(ws);
+  float* yr = reinterpret_cast<float*>(base + pl.yr_off);
+  uint16_t* G = reinterpret_cast<uint16_t*>(base + pl.g_off);
+  float* P = reinterpret_cast<float*>(base + pl.p_off);
+
+  // 1. Routed experts: table lookup-combine.
+  hipError_t err = launch_lookup_combine(ids, h, w_r, lut, yr, T, D, N, kBF16, true, s);
+  if (err != hipSuccess) return err;
+
+  // 2. Shared expert, up-projection with GELU.
+  if (pl.big_up) {
+    err = launch_gemm_gelu_bf16(h, D, w_s_up, D, G, F, (int)T, (int)F, (int)D, s);
+  } else {
+    MidArgs a{h, D, w_s_up, D, nullptr, F, T * F, nullptr, (int)T, (int)F, (int)D, (int)pl.ks_up,
+              (int)((F + kMidBN - 1) / kMidBN)};
+    if (pl.s_up == 1) {
+      a.C = G;
+      err = launch_mid<kMidGelu>(pl.rm, a, 1, s);
+    } else {
+      a.C = P;
+      err = launch_mid<kMidPartial>(pl.rm, a, pl.s_up, s);
+      if (err == hipSuccess) {
+        hipLaunchKernelGGL(gelu_reduce_kernel, dim3(grid_1d(T * F / 4)), dim3(256), 0, s, P, pl.s_up, T * F, G);
+        err = hipGetLastError();
+      }
+    }
+  }
+  if (err != hipSuccess) return err;
+
+  // 3. Shared expert, down-projection, added with the routed output to x.
+  MidArgs b{G, F, w_s_down, F, nullptr, D, T * D, yr, (int)T, (int)D, (int)F, (int)pl.ks_down,
+            (int)((D + kMidBN - 1) / kMidBN)};
+  if (pl.s_down == 1) {
+    b.C = x;
+    return launch_mid<kMidAccum>(pl.rm, b, 1, s);
+  }
+  b.C = P;
+  err = launch_mid<kMidPartial>(pl.rm, b, pl.s_down, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(add_reduce_kernel, dim3(grid_1d(T * D / 4)), dim3(256), 0, s, P, pl.s_down, T * D, yr, x);
+  return hipGetLastError();
+}
+
+}  // namespace mole

@@ -33,5 +33,20 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
 hipError_t launch_build_lut_f32(const float* emb, const float* w_up, const float* w_down, float* lut,
                                 int64_t V, int64_t D, int64_t F, int64_t N, hipStream_t s);
 constexpr int64_t kBuildF32MaxLds = 16384;  // D + F floats staged in LDS by the fp32 build
+hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
+                                 int64_t ldc, int M, int N, int K, hipStream_t s);
+
+// layer.hip: the MoLE block at inference (shared expert + routed lookup + residual)
+struct LayerPlan {
+  bool big_up;          // up-projection on the 256x256 build GEMM
+  int rm;               // 32-row MFMA tiles per wave in the mid-size GEMM (tile height 32 * rm)
+  int s_up, s_down;     // K splits of the two projections (1 = none)
+  int64_t ks_up, ks_down;  // K range per split (multiple of 64)
+  size_t yr_off, g_off, p_off, total;  // workspace: routed y fp32 [T][D] | G bf16 [T][F] | partials fp32
+};
+LayerPlan layer_plan(int64_t T, int64_t D, int64_t F);
+hipError_t launch_layer_forward(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, const uint16_t* lut,
+                                const uint16_t* w_s_up, const uint16_t* w_s_down, float* x, int64_t T, int64_t D,
+                                int64_t N, int64_t F, void* ws, hipStream_t s);
 
 }  // namespace mole

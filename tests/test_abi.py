@@ -34,14 +34,15 @@ def test_header_declares_the_hot_path():
                "mole_build_lut_workspace_size", "mole_gather_nf3_host",
                "mole_lookup_combine_nf3_host", "mole_nf3_host_staging_size", "mole_status_string",
                "mole_last_hip_error",
-               "mole_nf3_levels", "mole_abi_version"):
+               "mole_nf3_levels", "mole_abi_version", "mole_layer_forward",
+               "mole_layer_workspace_size"):
         assert fn in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 3
+    assert lib.mole_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -206,3 +207,36 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_native, "_LIB_PATH", str(tmp_path / "libmole.so"))
     with pytest.raises(mole.MoleLibraryMissing):
         _native.library()
+
+
+def test_layer_workspace_size_and_errors(lib):
+    assert mole.mole_layer_workspace_size(0, 1024, 4096) == 0
+    # routed y (fp32) + hidden activations (bf16) at least, growing with T
+    for T in (1, 37, 256, 4096):
+        ws = mole.mole_layer_workspace_size(T, 1024, 4096)
+        assert ws >= T * 1024 * 4 + T * 4096 * 2
+    assert mole.mole_layer_workspace_size(4096, 1024, 4096) > mole.mole_layer_workspace_size(256, 1024, 4096)
+    out = ctypes.c_size_t(0)
+    assert lib.mole_layer_workspace_size(-1, 64, 64, ctypes.addressof(out)) == DIM
+    assert lib.mole_layer_workspace_size(4, 0, 64, ctypes.addressof(out)) == DIM
+    assert lib.mole_layer_workspace_size(4, 64, 64, None) == NULL
+
+    a = 0x1000
+    ws = mole.mole_layer_workspace_size(4, 64, 256)
+
+    def call(T=4, V=8, D=64, N=4, F=256, dtype=1, ids=P(a), x=P(a), wsp=P(a), wsb=ws, w_s_up=P(a)):
+        return lib.mole_layer_forward(ids, P(a), P(a), P(a), w_s_up, P(a), x, T, V, D, N, F, dtype,
+                                      wsp, wsb, None)
+    assert call(dtype=0) == UNSUP          # fp32 has no layer path
+    assert call(dtype=7) == DTYPE
+    assert call(D=60) == DIM               # 16-byte K segments
+    assert call(F=250) == DIM
+    assert call(F=0) == DIM
+    assert call(N=65) == UNSUP
+    assert call(D=1 << 23) == UNSUP        # 32-bit panel offsets
+    assert call(ids=None) == NULL
+    assert call(w_s_up=None) == NULL
+    assert call(wsp=None) == NULL
+    assert call(x=P(a + 4)) == ALIGN
+    assert call(wsb=ws - 1) == WS
+    assert call(T=0, ids=None, x=None, wsp=None, wsb=0) == OK   # empty batch: no-op

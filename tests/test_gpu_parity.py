@@ -451,3 +451,134 @@ def test_graph_replay_of_layer_stack_matches_eager_and_oracle():
             np.testing.assert_array_equal(host(ys[l]), eager[l])
         stack(None)  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# The MoLE block: residual + shared expert FFN + routed lookup (training
+# section: shared experts read the contextual hidden state; complexity
+# analysis: they are the only experts still computed at inference)
+# ----------------------------------------------------------------------------
+
+LAYER_TOL = 1e-2  # rel-L2 of the block's update, as for the bf16 build products
+
+
+def rand_shared(seed, D, F, std_up=0.02, std_down=0.02, zero=False):
+    """Shared-expert weights w_s_up [F,D], w_s_down [D,F] as bf16 bits."""
+    r = rng(seed)
+    if zero:
+        return np.zeros((F, D), np.uint16), np.zeros((D, F), np.uint16)
+    f = lambda shape, s: synth.f32_to_bf16_bits(r.standard_normal(shape, dtype=np.float32) * np.float32(s))
+    return f((F, D), std_up), f((D, F), std_down)
+
+
+def run_layer(ids, h, w_r, lut, wu, wd, x0):
+    T, D = h.shape
+    F = wu.shape[0]
+    ws = torch.empty(max(mole.mole_layer_workspace_size(T, D, F), 16), dtype=torch.uint8, device="cuda")
+    x = dev(x0)
+    mole.mole_layer_forward(dev(ids), dev(h), dev(w_r), dev(lut), dev(wu), dev(wd), x, ws)
+    torch.cuda.synchronize()
+    return host(x)
+
+
+# (V, N, D, F, T): every branch of the launch plan --
+#   T = 1: K splits on both projections (GELU reduction, add reduction);
+#   T = 37: two-tile-row MFMA blocks, ragged rows, columns and K (D = 264, F = 392), ragged last split;
+#   T = 200: unsplit up-projection with GELU in the epilogue, split down-projection;
+#   T = 512: no splits, residual update in the down-projection's epilogue;
+#   T = 2048, F = 8192: up-projection on the 256x256 build GEMM.
+LAYER_CASES = [(300, 4, 256, 512, 1), (500, 5, 264, 392, 37), (400, 16, 512, 1024, 200),
+               (256, 2, 256, 256, 512), (1000, 8, 128, 8192, 2048)]
+
+
+@pytest.mark.parametrize("V,N,D,F,T", LAYER_CASES)
+def test_layer_matches_oracle(V, N, D, F, T):
+    seed = V + N + D + F + T
+    lut = rand_table(seed, V, N, D, "bf16", std=0.05)
+    h, w_r = rand_hw(seed + 1, T, N, D, "bf16", wstd=0.05)
+    # unit-scale hidden units (|u| ~ 1, where GELU is nonlinear)
+    wu, wd = rand_shared(seed + 2, D, F, std_up=1.0 / np.sqrt(D), std_down=1.0 / np.sqrt(F))
+    ids = rng(seed + 3).integers(0, V, size=T).astype(np.int64)
+    x0 = rng(seed + 4).standard_normal((T, D), dtype=np.float32) * np.float32(3.0)
+    got = run_layer(ids, h, w_r, lut, wu, wd, x0)
+    upd = oracle.layer_forward(ids, h, w_r, lut, wu, wd, None)
+    assert rel_l2(got.astype(np.float64) - x0.astype(np.float64), upd) <= LAYER_TOL
+    per_tok = [rel_l2(got[t].astype(np.float64) - x0[t], upd[t]) for t in range(T)]
+    assert max(per_tok) <= 2 * LAYER_TOL
+
+
+@pytest.mark.parametrize("T", [1, 37, 512])
+def test_layer_zero_shared_weights_is_the_combine(T):
+    """With zero shared weights the block adds exactly the routed lookup, held
+    to the combine's 2e-5 bar (the shared path contributes exact zeros)."""
+    V, N, D, F = 300, 6, 256, 512
+    lut = rand_table(70 + T, V, N, D, "bf16")
+    h, w_r = rand_hw(71 + T, T, N, D, "bf16")
+    wu, wd = rand_shared(0, D, F, zero=True)
+    ids = rng(72 + T).integers(0, V, size=T).astype(np.int64)
+    got = run_layer(ids, h, w_r, lut, wu, wd, np.zeros((T, D), np.float32))
+    assert combine_rel_err(got, oracle.lookup_combine(ids, h, w_r, lut)) <= COMBINE_TOL
+
+
+def test_layer_empty_batch_is_noop():
+    D, F = 64, 128
+    x = torch.full((1, D), 7.0, device="cuda")
+    empty = torch.empty((0,), dtype=torch.int64, device="cuda")
+    z = torch.zeros((0, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((2, D), dtype=torch.bfloat16, device="cuda")
+    lut = torch.zeros((4, 2, D), dtype=torch.bfloat16, device="cuda")
+    wu = torch.zeros((F, D), dtype=torch.bfloat16, device="cuda")
+    wd = torch.zeros((D, F), dtype=torch.bfloat16, device="cuda")
+    mole.mole_layer_forward(empty, z, w, lut, wu, wd, x[:0], None)
+    torch.cuda.synchronize()
+    assert torch.all(x == 7.0)
+
+
+def test_layer_full_size_410m_sampled_tokens():
+    """410M-class block at prefill length (T = 4096, D = 1024, F = 4096,
+    N = 16, Zipf ids): every output row is computed; 48 sampled tokens are
+    checked against the oracle (its cost is per token)."""
+    w = synth.WORKLOADS["410m"]
+    T, D, F, N = 4096, w.D, w.F, w.N
+    ids = synth.make_ids(w, T)
+    rows = np.unique(ids)
+    lut = rand_table(81, w.V, N, D, "bf16", std=0.05, rows=rows)
+    h = synth.make_hidden(w, T)
+    w_r = synth.make_router(w)
+    wu, wd = rand_shared(82, D, F)
+    x0 = rng(83).standard_normal((T, D), dtype=np.float32)
+    got = run_layer(ids, h, w_r, lut, wu, wd, x0)
+    assert np.all(np.isfinite(got))
+    sample = np.unique(np.concatenate([[0, T - 1], rng(84).integers(0, T, 46)]))
+    upd = oracle.layer_forward(ids[sample], np.ascontiguousarray(h[sample]), w_r, lut, wu, wd, None)
+    assert rel_l2(got[sample].astype(np.float64) - x0[sample], upd) <= LAYER_TOL
+
+
+def test_layer_graph_replay_matches_eager():
+    """The block (five launches, no memset) captured once; each replay,
+    after eager work and a reset of the residual stream, equals the eager
+    result bit for bit."""
+    V, N, D, F, T = 300, 4, 256, 512, 37
+    lut = dev(rand_table(61, V, N, D, "bf16"))
+    h, w_r = (dev(a) for a in rand_hw(62, T, N, D, "bf16"))
+    wu, wd = (dev(a) for a in rand_shared(63, D, F, std_up=0.05, std_down=0.05))
+    ids = dev(rng(64).integers(0, V, size=T).astype(np.int64))
+    x0 = dev(rng(65).standard_normal((T, D), dtype=np.float32))
+    x = x0.clone()
+    ws = torch.empty(mole.mole_layer_workspace_size(T, D, F), dtype=torch.uint8, device="cuda")
+    mole.mole_layer_forward(ids, h, w_r, lut, wu, wd, x, ws)
+    torch.cuda.synchronize()
+    eager = host(x)
+    g = torch.cuda.CUDAGraph()
+    x.copy_(x0)
+    with torch.cuda.graph(g):
+        mole.mole_layer_forward(ids, h, w_r, lut, wu, wd, x, ws, stream=torch.cuda.current_stream())
+    for rep in range(3):
+        x.copy_(x0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(x), eager)
+        y = x0.clone()
+        mole.mole_layer_forward(ids, h, w_r, lut, wu, wd, y, ws)  # eager work between replays
+        torch.cuda.synchronize()
