@@ -51,6 +51,10 @@ def parse():
                         "so gathered bytes = unique bytes)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget for the CPU-oracle baseline (0 disables it)")
+    p.add_argument("--probes", default="scale,decode,host,layer",
+                   help="comma list of the extra measurements to run: scale (combine on the 410M-class "
+                        "table), decode (1B-class 16-layer stack), host (host-resident NF3 stack), "
+                        "layer (the full MoLE block: shared FFN + lookup + residual)")
     p.add_argument("--no-scale-probe", action="store_true",
                    help="skip the 410M-class combine measurement at T=1024/4096")
     p.add_argument("--copy-calibration", action="store_true",
@@ -260,11 +264,17 @@ def main():
         "wall_s_timed": wall,
     }
 
-    if not args.no_scale_probe and bf16:
+    probes = set() if args.no_scale_probe or not bf16 else set(args.probes.split(","))
+    if probes:
         torch.cuda.synchronize()
+    if "scale" in probes:
         result["combine_at_scale"] = scale_probe(torch, mole, synth, dev, stream)
+    if "decode" in probes:
         result["decode_stack_1b"] = decode_stack_probe(torch, mole, synth, dev, stream)
+    if "host" in probes:
         result["host_stack_nf3"] = host_stack_probe(torch, mole, synth, dev, stream)
+    if "layer" in probes:
+        result["layer_block"] = layer_probe(torch, mole, synth, dev, stream)
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(args, w, layer, ids_h[0], synth, T)
@@ -324,6 +334,64 @@ def scale_probe(torch, mole, synth, dev, stream):
     ctx.__exit__(None, None, None)
     del lut, codes, scales
     torch.cuda.empty_cache()
+    return out
+
+
+def layer_probe(torch, mole, synth, dev, stream):
+    """The full MoLE block at inference, x += shared FFN(h) + lookup(ids, h),
+    for the three bf16 configurations, with a shared expert of the routed
+    experts' size (D -> F -> D).  Per (configuration, T): event-timed block
+    time on `stream`, and the roofline it is held to -- the larger of its
+    bf16 FLOPs (4 T D F) at the MFMA peak and its algorithmic HBM bytes
+    (shared weights 4 D F, gathered table rows T N D 2, h, residual read and
+    write, ids, router) at the HBM peak."""
+    out = {"peaks": {"bf16_tflops": BF16_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS}}
+    ctx = torch.cuda.stream(stream)
+    ctx.__enter__()
+    for name, Ts in (("160m", (1, 64, 256)), ("410m", (256, 1024, 4096)), ("1b", (1, 128, 1024))):
+        w = synth.WORKLOADS[name]
+        V, D, N, F = w.V, w.D, w.N, w.F
+        g = torch.Generator(device=dev)
+        g.manual_seed(synth.seed(w, 80))
+        lut = (torch.randn((V, N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        w_r = (torch.randn((N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        wu = (torch.randn((F, D), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        wd = (torch.randn((D, F), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        perm = synth.rank_permutation(w)
+        for T in Ts:
+            NB = 4
+            ids_l = [torch.from_numpy(synth.make_ids(w, T, step=s, perm=perm)).to(dev) for s in range(NB)]
+            h_l = [torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(NB)]
+            x = torch.zeros((T, D), dtype=torch.float32, device=dev)
+            ws = torch.empty(mole.mole_layer_workspace_size(T, D, F), dtype=torch.uint8, device=dev)
+
+            def block(i):
+                mole.mole_layer_forward(ids_l[i % NB], h_l[i % NB], w_r, lut, wu, wd, x, ws, stream=stream)
+
+            for i in range(5):
+                block(i)
+            reps = 50 if T <= 256 else 20
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                block(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            flops = 4.0 * T * D * F
+            byts = 4.0 * D * F + T * (N * D * 2 + D * 2 + 8 * D + 8) + N * D * 2
+            roof_us = max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9)) * 1e6
+            out["%s_T%d" % (name, T)] = {
+                "us": us, "tokens_per_s": T / (us * 1e-6), "tflops": flops / (us * 1e-6) / 1e12,
+                "gbs": byts / (us * 1e-6) / 1e9, "roofline_us": roof_us,
+                "bound": "mfma" if flops / (BF16_PEAK_TFLOPS * 1e12) > byts / (HBM_PEAK_GBS * 1e9) else "hbm",
+                "roofline_frac": roof_us / us, "flops": flops, "bytes": byts,
+                "config": "V=%d D=%d N=%d F=%d (shared FFN D->F->D), Zipf(1.1) ids" % (V, D, N, F)}
+            del ws, x, h_l, ids_l
+        del lut, w_r, wu, wd
+        torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+    ctx.__exit__(None, None, None)
     return out
 
 

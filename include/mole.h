@@ -167,8 +167,9 @@ int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
  * (MOLE_ERR_UNSUPPORTED); 1 <= N <= 64.  T == 0 is a no-op.
  *
  * workspace: device scratch (16-byte aligned) of at least the size that
- * mole_layer_workspace_size(T, D, F) returns (0 for T == 0): the routed y,
- * the hidden activations and, for short batches, per-split partial sums.
+ * mole_layer_workspace_size(T, D, F) returns (0 for T == 0): router gates,
+ * the hidden activations and the down-projection's per-split fp32 partial
+ * sums, which the final lookup-combine pass adds to x with the table rows.
  * Contents on return are unspecified.  Enqueued on `stream`, asynchronous,
  * no memset (capturable in a HIP graph).
  * ------------------------------------------------------------------------ */

@@ -53,7 +53,9 @@ __device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + e
 // LDS and each wave writes two whole 512-byte row segments per instruction;
 // measured faster once output rows are >= 16 KB apart (the LUT of the larger
 // configurations), slower for narrow rows (two extra barriers).
-enum { kEpiStore = 0, kEpiGelu = 1, kEpiStoreStaged = 2 };
+// F32: the fp32 accumulators themselves, 16 bytes per lane (split-K partial
+// sums of the MoLE block's down-projection).
+enum { kEpiStore = 0, kEpiGelu = 1, kEpiStoreStaged = 2, kEpiF32 = 3 };
 constexpr int64_t kStagedMinRowBytes = 16384;
 
 constexpr int kBK = 64;     // K slice per LDS stage (64 bf16 = 128 bytes per row)
@@ -271,7 +273,28 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
                         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
     return make_uint2(lo, hi);
   };
-  if constexpr (EPI != kEpiStoreStaged) {
+  if constexpr (EPI == kEpiF32) {
+    // fp32 tile rows (buffer resource over rows_c rows of ldc floats).
+    float* cf = reinterpret_cast<float*>(p.C) + z * p.sCz + (int64_t)m0 * p.ldc;
+    const __amdgpu_buffer_rsrc_t rf_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)cf, (short)0, (int)(rows_c * p.ldc * 4), kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int mr = wm * WM + i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+          const uint32_t o = (mr < rows_c && n < N) ? (uint32_t)((mr * p.ldc + n) * 4) : kOob;
+          const uint4 v = make_uint4(__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
+                                     __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3]));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v),
+                                                 rf_rs, (int)o, 0, 0);
+        }
+      }
+    }
+  } else if constexpr (EPI != kEpiStoreStaged) {
     // Direct: 8-byte stores through a buffer resource over this tile's rows
     // (rows past M and column groups past N take an out-of-range offset and
     // are dropped).
@@ -383,6 +406,16 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
 hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
                                  int64_t ldc, int M, int N, int K, hipStream_t s) {
   return launch_gemm<kBM, kBN, kEpiGelu>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
+}
+
+// fp32 C = A . B^T per batch index z (split-K partial sums of the MoLE
+// block's down-projection: z selects a K range through sAz and sBz).
+// C rows of ldc floats; needs 256 * ldc * 4 < 2^31.
+hipError_t launch_gemm_f32_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
+                                int64_t sBz, float* C, int64_t ldc, int64_t sCz, int M, int N, int K, int batch,
+                                hipStream_t s) {
+  return launch_gemm<kBM, kBN, kEpiF32>(A, lda, sAz, B, ldb, sBz, reinterpret_cast<uint16_t*>(C), ldc, sCz, M, N, K,
+                                        batch, /*xcd_order=*/1, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -29,10 +29,16 @@ namespace mole {
 // ---------------------------------------------------------------------------
 // bf16 / fp32 table
 // ---------------------------------------------------------------------------
-template <typename T, int NP, int G, bool VECTOR, int MODE>
+// ADD (the MoLE block's last pass): y[t][d] += sum_s addp[s * add_stride + t * D + d]
+// + the routed combine, i.e. y is the residual stream, read and written.
+// Staged gates are read from `gates` (row stride D), which may be y itself:
+// neither pointer is restrict-qualified, so the gate loads stay ahead of the
+// barrier that precedes the first store.
+template <typename T, int NP, int G, bool VECTOR, int MODE, bool ADD = false>
 __global__ __launch_bounds__(256) void lookup_combine_kernel(
     const int64_t* __restrict__ ids, const T* __restrict__ h, const T* __restrict__ w_r,
-    const T* __restrict__ lut, float* __restrict__ y, int64_t T_, int D, int N, int tpb) {
+    const T* __restrict__ lut, float* y, int64_t T_, int D, int N, int tpb,
+    const float* gates, const float* __restrict__ addp, int nadd, int64_t add_stride) {
   constexpr int WG = G > kWave ? G / kWave : 1;
   constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
   constexpr int CH = VECTOR ? Elem<T>::kVec : 1;  // elements per chunk
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   uint4 gq[NG];
   if constexpr (kStaged) {
 #pragma unroll
-    for (int q = 0; q < NG; ++q) gq[q] = ldg16(y + tt * D + 4 * q);
+    for (int q = 0; q < NG; ++q) gq[q] = ldg16(gates + tt * D + 4 * q);
   }
   __builtin_amdgcn_sched_barrier(0);
   const int64_t id = valid ? id_ld : 0;  // (the first wait on the id load is here)
@@ -151,7 +157,40 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
       }
     }
     float* yo = y + tt * D + (int64_t)c * CH;
-    if constexpr (VECTOR) {
+    if constexpr (ADD) {
+      static_assert(VECTOR, "the block's final pass reads 16-byte chunks");
+      const int64_t o = tt * D + (int64_t)c * CH;
+      // Partial sums four splits at a time: the four loads of a batch go out
+      // together (indices clamped to the last split, the extra copies
+      // weighted by zero), so a pass over S splits waits ceil(S / 4) times.
+      float4 a[CH / 4];
+#pragma unroll
+      for (int j = 0; j < CH; j += 4) a[j / 4] = *reinterpret_cast<const float4*>(yo + j);
+      for (int s0 = 0; s0 < nadd; s0 += 4) {
+        float4 b[4][CH / 4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int sp = s0 + q < nadd ? s0 + q : nadd - 1;
+#pragma unroll
+          for (int j = 0; j < CH; j += 4) b[q][j / 4] = *reinterpret_cast<const float4*>(addp + sp * add_stride + o + j);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float wq = s0 + q < nadd ? 1.f : 0.f;
+#pragma unroll
+          for (int j = 0; j < CH / 4; ++j) {
+            a[j].x = fmaf(wq, b[q][j].x, a[j].x);
+            a[j].y = fmaf(wq, b[q][j].y, a[j].y);
+            a[j].z = fmaf(wq, b[q][j].z, a[j].z);
+            a[j].w = fmaf(wq, b[q][j].w, a[j].w);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CH; j += 4)
+        stg16_nt(yo + j, a[j / 4].x + acc[j], a[j / 4].y + acc[j + 1], a[j / 4].z + acc[j + 2],
+                 a[j / 4].w + acc[j + 3]);
+    } else if constexpr (VECTOR) {
 #pragma unroll
       for (int j = 0; j < CH; j += 4)
         stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
@@ -165,75 +204,100 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
 // Host-side dispatch
 // ---------------------------------------------------------------------------
 
-template <typename E, int NP, int G, bool VEC>
-static hipError_t launch_dense(const int64_t* ids, const void* h, const void* w_r, const void* lut,
-                               float* y, int64_t T, int D, int N, hipStream_t s) {
+struct CombineExtra {
+  float* gates_buf;    // where the staged router writes gates (row stride D); the combine's y if null
+  const float* addp;   // ADD pass: partial sums added to y (null: plain combine)
+  int nadd;
+  int64_t add_stride;
+};
+
+template <typename E, int NP, int G, bool VEC, bool ADD>
+static hipError_t launch_dense_add(const int64_t* ids, const void* h, const void* w_r, const void* lut, float* y,
+                                   int64_t T, int D, int N, const CombineExtra& ex, hipStream_t s) {
   const int tpb = pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;
+  float* gbuf = ex.gates_buf ? ex.gates_buf : y;
   if constexpr (VEC && sizeof(E) == 2) {
     if (T >= kStagedRouterMinT && tpb >= 2 && N <= D) {
       const int64_t rblocks = (T + kMaxTokPerBlock - 1) / kMaxTokPerBlock;
       hipLaunchKernelGGL((router_gates_kernel<NP>), dim3((unsigned)rblocks), dim3(256), 0, s, (const uint16_t*)h,
-                         (const uint16_t*)w_r, y, T, D, N);
-      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterStaged>), dim3((unsigned)blocks),
-                         dim3(G * tpb), 0, s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, tpb);
+                         (const uint16_t*)w_r, gbuf, T, D, N);
+      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterStaged, ADD>), dim3((unsigned)blocks),
+                         dim3(G * tpb), 0, s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, tpb,
+                         gbuf, ex.addp, ex.nadd, ex.add_stride);
       return hipGetLastError();
     }
   }
   // One token per block: the vector-unit router (see LaneRouter).
   if constexpr (VEC && sizeof(E) == 2 && NP <= 16 && G >= 64) {
     if (tpb == 1) {
-      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterLane>), dim3((unsigned)blocks), dim3(G), 0,
-                         s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, 1);
+      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterLane, ADD>), dim3((unsigned)blocks), dim3(G),
+                         0, s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, 1, gbuf, ex.addp,
+                         ex.nadd, ex.add_stride);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterMfma>), dim3((unsigned)blocks), dim3(G * tpb),
-                     0, s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, tpb);
+  hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterMfma, ADD>), dim3((unsigned)blocks),
+                     dim3(G * tpb), 0, s, ids, (const E*)h, (const E*)w_r, (const E*)lut, y, T, D, N, tpb, gbuf,
+                     ex.addp, ex.nadd, ex.add_stride);
   return hipGetLastError();
+}
+
+template <typename E, int NP, int G, bool VEC>
+static hipError_t launch_dense(const int64_t* ids, const void* h, const void* w_r, const void* lut, float* y,
+                               int64_t T, int D, int N, const CombineExtra& ex, hipStream_t s) {
+  if constexpr (VEC && sizeof(E) == 2) {
+    if (ex.addp) return launch_dense_add<E, NP, G, VEC, true>(ids, h, w_r, lut, y, T, D, N, ex, s);
+  }
+  return launch_dense_add<E, NP, G, VEC, false>(ids, h, w_r, lut, y, T, D, N, ex, s);
 }
 
 template <typename E, int NP, bool VEC>
 static hipError_t dispatch_dense_g(int G, const int64_t* ids, const void* h, const void* w_r,
-                                   const void* lut, float* y, int64_t T, int D, int N, hipStream_t s) {
+                                   const void* lut, float* y, int64_t T, int D, int N, const CombineExtra& ex,
+                                   hipStream_t s) {
   switch (G) {
-    case 16: return launch_dense<E, NP, 16, VEC>(ids, h, w_r, lut, y, T, D, N, s);
-    case 32: return launch_dense<E, NP, 32, VEC>(ids, h, w_r, lut, y, T, D, N, s);
-    case 64: return launch_dense<E, NP, 64, VEC>(ids, h, w_r, lut, y, T, D, N, s);
-    case 128: return launch_dense<E, NP, 128, VEC>(ids, h, w_r, lut, y, T, D, N, s);
-    default: return launch_dense<E, NP, 256, VEC>(ids, h, w_r, lut, y, T, D, N, s);
+    case 16: return launch_dense<E, NP, 16, VEC>(ids, h, w_r, lut, y, T, D, N, ex, s);
+    case 32: return launch_dense<E, NP, 32, VEC>(ids, h, w_r, lut, y, T, D, N, ex, s);
+    case 64: return launch_dense<E, NP, 64, VEC>(ids, h, w_r, lut, y, T, D, N, ex, s);
+    case 128: return launch_dense<E, NP, 128, VEC>(ids, h, w_r, lut, y, T, D, N, ex, s);
+    default: return launch_dense<E, NP, 256, VEC>(ids, h, w_r, lut, y, T, D, N, ex, s);
   }
 }
 
 template <typename E, bool VEC>
 static hipError_t dispatch_dense_np(int NP, int G, const int64_t* ids, const void* h, const void* w_r,
-                                    const void* lut, float* y, int64_t T, int D, int N, hipStream_t s) {
+                                    const void* lut, float* y, int64_t T, int D, int N, const CombineExtra& ex,
+                                    hipStream_t s) {
   switch (NP) {
-    case 1: return dispatch_dense_g<E, 1, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
-    case 2: return dispatch_dense_g<E, 2, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
-    case 4: return dispatch_dense_g<E, 4, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
-    case 8: return dispatch_dense_g<E, 8, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
-    case 16: return dispatch_dense_g<E, 16, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
-    case 32: return dispatch_dense_g<E, 32, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
-    default: return dispatch_dense_g<E, 64, VEC>(G, ids, h, w_r, lut, y, T, D, N, s);
+    case 1: return dispatch_dense_g<E, 1, VEC>(G, ids, h, w_r, lut, y, T, D, N, ex, s);
+    case 2: return dispatch_dense_g<E, 2, VEC>(G, ids, h, w_r, lut, y, T, D, N, ex, s);
+    case 4: return dispatch_dense_g<E, 4, VEC>(G, ids, h, w_r, lut, y, T, D, N, ex, s);
+    case 8: return dispatch_dense_g<E, 8, VEC>(G, ids, h, w_r, lut, y, T, D, N, ex, s);
+    case 16: return dispatch_dense_g<E, 16, VEC>(G, ids, h, w_r, lut, y, T, D, N, ex, s);
+    case 32: return dispatch_dense_g<E, 32, VEC>(G, ids, h, w_r, lut, y, T, D, N, ex, s);
+    default: return dispatch_dense_g<E, 64, VEC>(G, ids, h, w_r, lut, y, T, D, N, ex, s);
   }
 }
 
 hipError_t launch_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut,
                                  float* y, int64_t T, int64_t D, int64_t N, int dtype, bool vector_ok,
-                                 hipStream_t s) {
+                                 hipStream_t s, float* gates_buf, const float* addp, int nadd,
+                                 int64_t add_stride) {
   if (T == 0) return hipSuccess;
   const int NP = next_pow2((int)N);
   const int elem_bytes = dtype == kF32 ? 4 : 2;
   const int vec = 16 / elem_bytes;
   const bool vector = vector_ok && (D % vec == 0);
+  if (addp && (dtype == kF32 || !vector)) return hipErrorInvalidValue;  // the block's pass is bf16, 16-byte chunks
   const int C = vector ? (int)(D / vec) : (int)D;
   const int G = pick_group(C, 16, 256);
+  const CombineExtra ex{gates_buf, addp, nadd, add_stride};
   if (dtype == kF32)
-    return vector ? dispatch_dense_np<float, true>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s)
-                  : dispatch_dense_np<float, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s);
-  return vector ? dispatch_dense_np<uint16_t, true>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s)
-                : dispatch_dense_np<uint16_t, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, s);
+    return vector ? dispatch_dense_np<float, true>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, ex, s)
+                  : dispatch_dense_np<float, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, ex, s);
+  return vector ? dispatch_dense_np<uint16_t, true>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, ex, s)
+                : dispatch_dense_np<uint16_t, false>(NP, G, ids, h, w_r, lut, y, T, (int)D, (int)N, ex, s);
 }
 
 }  // namespace mole

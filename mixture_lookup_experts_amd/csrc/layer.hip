@@ -8,13 +8,16 @@
 // only the shared experts are still computed, the routed ones are lookups.)
 //
 // Launch sequence on one stream, all scratch in the caller's workspace:
-//   1. lookup-combine of the routed experts into yr (fp32 [T][D]);
-//   2. up-projection G = GELU(h . W_s_up^T), rounded to bf16 ([T][F]):
+//   1. up-projection G = GELU(h . W_s_up^T), rounded to bf16 ([T][F]):
 //      long batches use the 256x256 build GEMM, shorter ones the mid-size
 //      GEMM below, split over K into fp32 partials plus a GELU reduction
 //      when the batch alone cannot fill the chip;
-//   3. down-projection of G, added with yr into x: in the GEMM epilogue when
-//      there is no K split, else fp32 partials and one reduction pass.
+//   2. down-projection of G into fp32 partial sums P[s][T][D], one per K
+//      split (long batches: the 256x256 build GEMM over equal K splits);
+//   3. the routed lookup-combine as the block's final pass, reading x and
+//      adding the partial sums and the gate-weighted table rows:
+//      x += sum_s P[s] + sum_e g_e LUT[id, e]  (the shared expert's output
+//      never makes a separate trip through memory as a finished tensor).
 //
 // Mid-size GEMM (C = A . B^T, A [M][lda] bf16 = activations, B [N][ldb]
 // bf16 = a weight matrix stored output-major): a 256-thread workgroup owns
@@ -45,15 +48,15 @@ constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every record: load
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kMidBN = 128;             // output columns per mid-size tile (4 waves x 32)
 constexpr int kTargetBlocks = 512;      // two workgroups per compute unit
+constexpr int kMaxSplits = 16;          // K splits per projection
 
-enum { kMidGelu = 0, kMidPartial = 1, kMidAccum = 2 };
+enum { kMidGelu = 0, kMidPartial = 1 };
 
 struct MidArgs {
   const uint16_t* A; int64_t lda;  // [M][lda]
   const uint16_t* B; int64_t ldb;  // [N][ldb]
-  void* C; int64_t ldc;            // GELU: bf16 [M][ldc]; partial: fp32 [splits][M][ldc]; accum: fp32 x [M][ldc]
+  void* C; int64_t ldc;            // GELU: bf16 [M][ldc]; partial: fp32 [splits][M][ldc]
   int64_t sCz;                     // partial: elements between splits
-  const float* yadd;               // accum: fp32 [M][ldc] added to x with the product
   int M, N, K, Ks, tiles_n;
 };
 
@@ -156,51 +159,40 @@ __global__ __launch_bounds__(256) void gemm_mid_kernel(MidArgs p) {
         w.x = pack_bf16x2(gelu_poly(v0), gelu_poly(v1));
         w.y = pack_bf16x2(gelu_poly(v2), gelu_poly(v3));
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + o) = w;
-      } else if constexpr (EPI == kMidPartial) {
+      } else {
         float* dst = static_cast<float*>(p.C) + (int64_t)blockIdx.y * p.sCz + o;
         *reinterpret_cast<float4*>(dst) = make_float4(v0, v1, v2, v3);
-      } else {
-        float* dst = static_cast<float*>(p.C) + o;
-        const float4 xv = *reinterpret_cast<const float4*>(dst);
-        const float4 yv = *reinterpret_cast<const float4*>(p.yadd + o);
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(xv.x + (v0 + yv.x), xv.y + (v1 + yv.y), xv.z + (v2 + yv.z), xv.w + (v3 + yv.w));
       }
     }
   }
 }
 
-// G[i] = bf16(GELU(sum_s P[s][i])), four elements per thread and step.
+// sum_s P[s][i] for four consecutive i; all S loads are issued before the
+// first add, so a short pass waits for memory once, not S times.
+__device__ __forceinline__ float4 sum_splits(const float* __restrict__ P, int S, int64_t count, int64_t i) {
+  float4 v[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < S) v[s] = reinterpret_cast<const float4*>(P + (int64_t)s * count)[i];
+  float4 a = v[0];
+#pragma unroll
+  for (int s = 1; s < kMaxSplits; ++s)
+    if (s < S) {
+      a.x += v[s].x; a.y += v[s].y; a.z += v[s].z; a.w += v[s].w;
+    }
+  return a;
+}
+
+// G[i] = bf16(GELU(sum_s P[s][i])).
 __global__ __launch_bounds__(256) void gelu_reduce_kernel(const float* __restrict__ P, int S, int64_t count,
                                                           uint16_t* __restrict__ G) {
   const int64_t n4 = count / 4;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-    float4 a = reinterpret_cast<const float4*>(P)[i];
-    for (int s = 1; s < S; ++s) {
-      const float4 b = reinterpret_cast<const float4*>(P + (int64_t)s * count)[i];
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-    }
+    const float4 a = sum_splits(P, S, count, i);
     uint2 w;
     w.x = pack_bf16x2(gelu_poly(a.x), gelu_poly(a.y));
     w.y = pack_bf16x2(gelu_poly(a.z), gelu_poly(a.w));
     reinterpret_cast<uint2*>(G)[i] = w;
-  }
-}
-
-// x[i] += yr[i] + sum_s P[s][i].
-__global__ __launch_bounds__(256) void add_reduce_kernel(const float* __restrict__ P, int S, int64_t count,
-                                                         const float* __restrict__ yr, float* __restrict__ x) {
-  const int64_t n4 = count / 4;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-    float4 a = reinterpret_cast<const float4*>(P)[i];
-    for (int s = 1; s < S; ++s) {
-      const float4 b = reinterpret_cast<const float4*>(P + (int64_t)s * count)[i];
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-    }
-    const float4 y = reinterpret_cast<const float4*>(yr)[i];
-    float4 v = reinterpret_cast<float4*>(x)[i];
-    v.x += a.x + y.x; v.y += a.y + y.y; v.z += a.z + y.z; v.w += a.w + y.w;
-    reinterpret_cast<float4*>(x)[i] = v;
   }
 }
 
@@ -221,14 +213,26 @@ hipError_t launch_mid(int rm, const MidArgs& p, int splits, hipStream_t s) {
   }
 }
 
+// Mid-size tile height for a projection with `out` output columns: the
+// tallest tile (most reuse of each weight row) that still gives 128 tiles,
+// else the shortest.
+int pick_rm(int64_t T, int64_t out) {
+  const int64_t tn = (out + kMidBN - 1) / kMidBN;
+  for (int rm : {4, 2}) {
+    if (T <= 32 * (rm / 2)) continue;  // a taller tile than the batch wastes its rows
+    if (((T + 32 * rm - 1) / (32 * rm)) * tn >= 128) return rm;
+  }
+  return 1;
+}
+
 // K splits for a projection with `tiles` output tiles: enough workgroups to
-// fill the chip, at least 128 of K per split, and partials no larger than
-// the weight matrix they come from (sp * T * out * 4 <= K * out * 2).
+// fill the chip, at least 128 of K per split, and partial sums of at most
+// four times the weight matrix's bytes (sp * T * out * 4 <= 4 * K * out * 2).
 int pick_splits(int64_t tiles, int64_t T, int64_t K) {
   int64_t sp = (kTargetBlocks + tiles - 1) / tiles;
   sp = std::min<int64_t>(sp, std::max<int64_t>(1, K / 128));
-  sp = std::min<int64_t>(sp, std::max<int64_t>(1, K / (2 * T)));
-  return (int)std::max<int64_t>(1, std::min<int64_t>(sp, 16));
+  sp = std::min<int64_t>(sp, std::max<int64_t>(1, 2 * K / T));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
 }
 
 inline size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
@@ -243,21 +247,36 @@ unsigned grid_1d(int64_t n4) {
 
 LayerPlan layer_plan(int64_t T, int64_t D, int64_t F) {
   LayerPlan pl{};
-  pl.rm = T <= 32 ? 1 : (T <= 64 ? 2 : 4);
-  const int64_t bm = 32 * pl.rm;
-  const int64_t tiles_m = (T + bm - 1) / bm;
-  // The 256x256 GEMM needs a full chip's worth of tiles to beat the mid-size one.
+  // The 256x256 GEMM needs a full chip's worth of tiles (counting K splits)
+  // to beat the mid-size one.
   pl.big_up = ((T + 255) / 256) * ((F + 255) / 256) >= 256;
-  pl.s_up = pl.big_up ? 1 : pick_splits(tiles_m * ((F + kMidBN - 1) / kMidBN), T, D);
-  pl.s_down = pick_splits(tiles_m * ((D + kMidBN - 1) / kMidBN), T, F);
+  pl.rm_up = pick_rm(T, F);
+  pl.s_up = pl.big_up ? 1 : pick_splits(((T + 32 * pl.rm_up - 1) / (32 * pl.rm_up)) * ((F + kMidBN - 1) / kMidBN), T, D);
   pl.ks_up = ((D + pl.s_up - 1) / pl.s_up + 63) / 64 * 64;
-  pl.ks_down = ((F + pl.s_down - 1) / pl.s_down + 63) / 64 * 64;
   pl.s_up = (int)((D + pl.ks_up - 1) / pl.ks_up);
-  pl.s_down = (int)((F + pl.ks_down - 1) / pl.ks_down);
+  // Down-projection on the 256x256 GEMM: equal K splits (F / s, a multiple of
+  // 64) until the tiles fill the chip.
+  pl.big_down = false;
+  const int64_t tiles_big = ((T + 255) / 256) * ((D + 255) / 256);
+  if (T >= 2048 && D <= ((int64_t)1 << 20)) {
+    for (int sp = 1; sp <= 8; sp *= 2) {
+      if (F % (64 * sp) != 0) break;
+      pl.big_down = true;
+      pl.s_down = sp;
+      pl.ks_down = F / sp;
+      if (tiles_big * sp >= 256) break;
+    }
+  }
+  pl.rm_down = pick_rm(T, D);
+  if (!pl.big_down) {
+    pl.s_down = pick_splits(((T + 32 * pl.rm_down - 1) / (32 * pl.rm_down)) * ((D + kMidBN - 1) / kMidBN), T, F);
+    pl.ks_down = ((F + pl.s_down - 1) / pl.s_down + 63) / 64 * 64;
+    pl.s_down = (int)((F + pl.ks_down - 1) / pl.ks_down);
+  }
   const size_t yr = (size_t)T * (size_t)D * 4u;
   const size_t g = (size_t)T * (size_t)F * 2u;
   const size_t p_up = pl.s_up > 1 ? (size_t)pl.s_up * (size_t)T * (size_t)F * 4u : 0;
-  const size_t p_down = pl.s_down > 1 ? (size_t)pl.s_down * (size_t)T * (size_t)D * 4u : 0;
+  const size_t p_down = (size_t)pl.s_down * (size_t)T * (size_t)D * 4u;
   pl.yr_off = 0;
   pl.g_off = round256(yr);
   pl.p_off = pl.g_off + round256(g);
@@ -275,22 +294,19 @@ hipError_t launch_layer_forward(const int64_t* ids, const uint16_t* h, const uin
   uint16_t* G = reinterpret_cast<uint16_t*>(base + pl.g_off);
   float* P = reinterpret_cast<float*>(base + pl.p_off);
 
-  // 1. Routed experts: table lookup-combine.
-  hipError_t err = launch_lookup_combine(ids, h, w_r, lut, yr, T, D, N, kBF16, true, s);
-  if (err != hipSuccess) return err;
-
-  // 2. Shared expert, up-projection with GELU.
+  hipError_t err;
+  // 1. Shared expert, up-projection with GELU.
   if (pl.big_up) {
     err = launch_gemm_gelu_bf16(h, D, w_s_up, D, G, F, (int)T, (int)F, (int)D, s);
   } else {
-    MidArgs a{h, D, w_s_up, D, nullptr, F, T * F, nullptr, (int)T, (int)F, (int)D, (int)pl.ks_up,
+    MidArgs a{h, D, w_s_up, D, nullptr, F, T * F, (int)T, (int)F, (int)D, (int)pl.ks_up,
               (int)((F + kMidBN - 1) / kMidBN)};
     if (pl.s_up == 1) {
       a.C = G;
-      err = launch_mid<kMidGelu>(pl.rm, a, 1, s);
+      err = launch_mid<kMidGelu>(pl.rm_up, a, 1, s);
     } else {
       a.C = P;
-      err = launch_mid<kMidPartial>(pl.rm, a, pl.s_up, s);
+      err = launch_mid<kMidPartial>(pl.rm_up, a, pl.s_up, s);
       if (err == hipSuccess) {
         hipLaunchKernelGGL(gelu_reduce_kernel, dim3(grid_1d(T * F / 4)), dim3(256), 0, s, P, pl.s_up, T * F, G);
         err = hipGetLastError();
@@ -299,18 +315,20 @@ hipError_t launch_layer_forward(const int64_t* ids, const uint16_t* h, const uin
   }
   if (err != hipSuccess) return err;
 
-  // 3. Shared expert, down-projection, added with the routed output to x.
-  MidArgs b{G, F, w_s_down, F, nullptr, D, T * D, yr, (int)T, (int)D, (int)F, (int)pl.ks_down,
-            (int)((D + kMidBN - 1) / kMidBN)};
-  if (pl.s_down == 1) {
-    b.C = x;
-    return launch_mid<kMidAccum>(pl.rm, b, 1, s);
+  // 2. Shared expert, down-projection: fp32 partial sums per K split.
+  if (pl.big_down) {
+    err = launch_gemm_f32_bf16(G, F, pl.ks_down, w_s_down, F, pl.ks_down, P, D, T * D, (int)T, (int)D,
+                               (int)pl.ks_down, pl.s_down, s);
+  } else {
+    MidArgs b{G, F, w_s_down, F, P, D, T * D, (int)T, (int)D, (int)F, (int)pl.ks_down,
+              (int)((D + kMidBN - 1) / kMidBN)};
+    err = launch_mid<kMidPartial>(pl.rm_down, b, pl.s_down, s);
   }
-  b.C = P;
-  err = launch_mid<kMidPartial>(pl.rm, b, pl.s_down, s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(add_reduce_kernel, dim3(grid_1d(T * D / 4)), dim3(256), 0, s, P, pl.s_down, T * D, yr, x);
-  return hipGetLastError();
+
+  // 3. Routed lookup-combine, adding the shared expert's partial sums and the
+  //    table rows to the residual stream (staged router gates go to yr).
+  return launch_lookup_combine(ids, h, w_r, lut, x, T, D, N, kBF16, true, s, yr, P, pl.s_down, T * D);
 }
 
 }  // namespace mole

@@ -11,9 +11,13 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
 // combine_dense.hip, combine_nf3.hip
+// gates_buf: scratch for the staged router's gates (row stride D; y if null).
+// addp != null (bf16 only): y is read and the result added to it together with
+// the nadd arrays addp + k * add_stride (the MoLE block's final pass).
 hipError_t launch_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut,
                                  float* y, int64_t T, int64_t D, int64_t N, int dtype, bool vector_ok,
-                                 hipStream_t s);
+                                 hipStream_t s, float* gates_buf = nullptr, const float* addp = nullptr,
+                                 int nadd = 0, int64_t add_stride = 0);
 hipError_t launch_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
                                      const uint8_t* codes, const uint16_t* scales, float* y,
                                      int64_t T, int64_t D, int64_t N, int dtype_h, hipStream_t s);
@@ -36,13 +40,18 @@ constexpr int64_t kBuildF32MaxLds = 16384;  // D + F floats staged in LDS by the
 hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
                                  int64_t ldc, int M, int N, int K, hipStream_t s);
 
+hipError_t launch_gemm_f32_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
+                                int64_t sBz, float* C, int64_t ldc, int64_t sCz, int M, int N, int K, int batch,
+                                hipStream_t s);
+
 // layer.hip: the MoLE block at inference (shared expert + routed lookup + residual)
 struct LayerPlan {
   bool big_up;          // up-projection on the 256x256 build GEMM
-  int rm;               // 32-row MFMA tiles per wave in the mid-size GEMM (tile height 32 * rm)
+  bool big_down;        // down-projection on the 256x256 build GEMM (fp32 partials per K split)
+  int rm_up, rm_down;   // 32-row MFMA tiles per wave in the mid-size GEMM (tile height 32 * rm)
   int s_up, s_down;     // K splits of the two projections (1 = none)
   int64_t ks_up, ks_down;  // K range per split (multiple of 64)
-  size_t yr_off, g_off, p_off, total;  // workspace: routed y fp32 [T][D] | G bf16 [T][F] | partials fp32
+  size_t yr_off, g_off, p_off, total;  // workspace: router gates fp32 [T][D] | G bf16 [T][F] | partials fp32
 };
 LayerPlan layer_plan(int64_t T, int64_t D, int64_t F);
 hipError_t launch_layer_forward(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, const uint16_t* lut,

@@ -482,13 +482,18 @@ def run_layer(ids, h, w_r, lut, wu, wd, x0):
 
 
 # (V, N, D, F, T): every branch of the launch plan --
-#   T = 1: K splits on both projections (GELU reduction, add reduction);
-#   T = 37: two-tile-row MFMA blocks, ragged rows, columns and K (D = 264, F = 392), ragged last split;
-#   T = 200: unsplit up-projection with GELU in the epilogue, split down-projection;
-#   T = 512: no splits, residual update in the down-projection's epilogue;
-#   T = 2048, F = 8192: up-projection on the 256x256 build GEMM.
+#   T = 1, 37, 200: one-tile-row MFMA blocks, K splits on both projections (GELU
+#     reduction; several partial sums in the final pass); T = 37 has ragged
+#     rows, columns and K (D = 264, F = 392) and a ragged last split;
+#   T = 512: no splits (GELU in the up-projection's epilogue, one partial sum);
+#   T = 2048, F = 8192: both projections on the 256x256 build GEMM (8 equal K
+#     splits of fp32 partials for the down-projection), staged router gates;
+#   T = 256, F = 4096: two-tile-row blocks with GELU in the epilogue;
+#   T = 1024, D = 2048: four-tile-row blocks for the down-projection;
+#   T = 1024, F = 8192: four-tile-row blocks with GELU in the epilogue.
 LAYER_CASES = [(300, 4, 256, 512, 1), (500, 5, 264, 392, 37), (400, 16, 512, 1024, 200),
-               (256, 2, 256, 256, 512), (1000, 8, 128, 8192, 2048)]
+               (256, 2, 256, 256, 512), (1000, 8, 128, 8192, 2048), (300, 4, 128, 4096, 256),
+               (300, 4, 2048, 512, 1024), (300, 4, 256, 8192, 1024)]
 
 
 @pytest.mark.parametrize("V,N,D,F,T", LAYER_CASES)
@@ -534,15 +539,16 @@ def test_layer_empty_batch_is_noop():
     assert torch.all(x == 7.0)
 
 
-def test_layer_full_size_410m_sampled_tokens():
-    """410M-class block at prefill length (T = 4096, D = 1024, F = 4096,
-    N = 16, Zipf ids): every output row is computed; 48 sampled tokens are
-    checked against the oracle (its cost is per token)."""
-    w = synth.WORKLOADS["410m"]
-    T, D, F, N = 4096, w.D, w.F, w.N
+@pytest.mark.parametrize("name,T", [("160m", 1), ("160m", 256), ("410m", 1024), ("410m", 4096),
+                                    ("1b", 1024)])
+def test_layer_full_size_sampled_tokens(name, T):
+    """The block at the benchmark's configurations (shared expert of the
+    routed experts' size, Zipf ids): every output row is computed; up to 48
+    sampled tokens are checked against the oracle (its cost is per token)."""
+    w = synth.WORKLOADS[name]
+    D, F, N = w.D, w.F, w.N
     ids = synth.make_ids(w, T)
-    rows = np.unique(ids)
-    lut = rand_table(81, w.V, N, D, "bf16", std=0.05, rows=rows)
+    lut = rand_table(81, w.V, N, D, "bf16", std=0.05, rows=np.unique(ids))
     h = synth.make_hidden(w, T)
     w_r = synth.make_router(w)
     wu, wd = rand_shared(82, D, F)
