@@ -54,7 +54,9 @@ def parse():
     p.add_argument("--probes", default="scale,decode,host,layer",
                    help="comma list of the extra measurements to run: scale (combine on the 410M-class "
                         "table), decode (1B-class 16-layer stack), host (host-resident NF3 stack), "
-                        "layer (the full MoLE block: shared FFN + lookup + residual)")
+                        "layer (the full MoLE block: shared FFN + lookup + residual); not in the default "
+                        "list: vendor_gemm (the vendor GEMM library, via torch.matmul, on the build's GEMM "
+                        "shapes and two square ones, as a practical MFMA ceiling)")
     p.add_argument("--no-scale-probe", action="store_true",
                    help="skip the 410M-class combine measurement at T=1024/4096")
     p.add_argument("--copy-calibration", action="store_true",
@@ -275,6 +277,8 @@ def main():
         result["host_stack_nf3"] = host_stack_probe(torch, mole, synth, dev, stream)
     if "layer" in probes:
         result["layer_block"] = layer_probe(torch, mole, synth, dev, stream)
+    if "vendor_gemm" in probes:
+        result["vendor_gemm"] = vendor_gemm_probe(torch, dev, stream)
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(args, w, layer, ids_h[0], synth, T)
@@ -392,6 +396,38 @@ def layer_probe(torch, mole, synth, dev, stream):
         torch.cuda.empty_cache()
     torch.cuda.synchronize()
     ctx.__exit__(None, None, None)
+    return out
+
+
+def vendor_gemm_probe(torch, dev, stream):
+    """Reference point, not part of the hot path: bf16 GEMMs through the vendor
+    library (torch.matmul on 2-D contiguous operands, which dispatches to
+    hipBLASLt) on the build's GEMM shapes (one expert for GEMM-2) and on two
+    square shapes, event-timed on `stream`.  It bounds what a tuned library
+    reaches on this part at these shapes."""
+    out = {}
+    with torch.cuda.stream(stream):
+        for name, M, N, K in (("square_8192", 8192, 8192, 8192), ("16384x16384x4096", 16384, 16384, 4096),
+                              ("160m_gemm1", 50304, 12288, 768), ("160m_gemm2_one_expert", 50304, 768, 3072),
+                              ("410m_gemm2_one_expert", 50304, 1024, 4096)):
+            g = torch.Generator(device=dev)
+            g.manual_seed(7)
+            A = (torch.randn((M, K), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+            B = (torch.randn((K, N), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+            for _ in range(3):
+                torch.matmul(A, B)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record(stream)
+            for _ in range(reps):
+                torch.matmul(A, B)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            out[name] = {"ms": ms, "tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS}
+            del A, B
+            torch.cuda.empty_cache()
     return out
 
 

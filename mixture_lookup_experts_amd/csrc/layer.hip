@@ -64,10 +64,16 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-template <int RM, int EPI>
+// NSL == 0: the K loop above (double-buffered, one slice ahead).  NSL > 0
+// (short splits of at most NSL slices): every load of the split is issued
+// at once -- all A slices, then all weight slices, in straight-line code so
+// each wait covers only the loads it needs -- the A slices go to NSL LDS
+// buffers behind one barrier, and the MFMAs follow slice by slice as the
+// weights arrive.  One memory latency per split instead of one per slice.
+template <int RM, int EPI, int NSL>
 __global__ __launch_bounds__(256) void gemm_mid_kernel(MidArgs p) {
   constexpr int BM = 32 * RM;
-  __shared__ uint4 lds[2][BM * 8];
+  __shared__ uint4 lds[NSL > 2 ? NSL : 2][BM * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
@@ -96,24 +102,59 @@ __global__ __launch_bounds__(256) void gemm_mid_kernel(MidArgs p) {
   const int brow = 32 * wave + l32;
   const uint32_t boff = brow < rows_b ? (uint32_t)(brow * p.ldb * 2 + half * 64) : kOob;
 
-  uint4 astg[RM], bcur[4], bnxt[4];
-  auto load_slice = [&](int k0, uint4* bdst) {
-#pragma unroll
-    for (int i = 0; i < RM; ++i) astg[i] = buf_load16(ra, k0 + aseg * 8 < ke ? aoff[i] + (uint32_t)k0 * 2u : kOob);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      bdst[c] = buf_load16(rb, k0 + 32 * half + 8 * c < ke ? boff + (uint32_t)(k0 + 8 * c) * 2u : kOob);
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < RM; ++i) lds[buf][alds[i]] = astg[i];
-  };
-
   f32x16_t acc[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[r][q] = 0.f;
+  // MFMAs of one slice: A fragments from LDS buffer `buf`, weights from b[].
+  auto mfma_slice = [&](int buf, const uint4* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sg = 4 * half + i;
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        const int row = 32 * r + l32;
+        const uint4 a = lds[buf][row * 8 + (sg ^ ((row >> 1) & 7))];
+        // Operands swapped (weights as the matrix-core "A"): lane l then holds
+        // C[m = l % 32][n = 8 (q / 4) + 4 (l / 32) + q % 4] in accumulator q.
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[i]),
+                                                         __builtin_bit_cast(bf16x8_t, a), acc[r], 0, 0, 0);
+      }
+    }
+  };
+  auto a_off = [&](int i, int k0) { return k0 + aseg * 8 < ke ? aoff[i] + (uint32_t)k0 * 2u : kOob; };
+  auto b_off = [&](int c, int k0) { return k0 + 32 * half + 8 * c < ke ? boff + (uint32_t)(k0 + 8 * c) * 2u : kOob; };
+
+  if constexpr (NSL > 0) {
+    uint4 ast[NSL][RM], bst[NSL][4];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int i = 0; i < RM; ++i) ast[sl][i] = buf_load16(ra, a_off(i, kb + 64 * sl));
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bst[sl][c] = buf_load16(rb, b_off(c, kb + 64 * sl));
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int i = 0; i < RM; ++i) lds[sl][alds[i]] = ast[sl][i];
+    __syncthreads();
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) mfma_slice(sl, bst[sl]);
+  } else {
+  uint4 astg[RM], bcur[4], bnxt[4];
+  auto load_slice = [&](int k0, uint4* bdst) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i) astg[i] = buf_load16(ra, a_off(i, k0));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bdst[c] = buf_load16(rb, b_off(c, k0));
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < RM; ++i) lds[buf][alds[i]] = astg[i];
+  };
 
   const int ns = ke > kb ? (ke - kb + 63) / 64 : 0;
   if (ns > 0) {
@@ -124,23 +165,12 @@ __global__ __launch_bounds__(256) void gemm_mid_kernel(MidArgs p) {
   for (int s = 0; s < ns; ++s) {
     const int buf = s & 1;
     if (s + 1 < ns) load_slice(kb + (s + 1) * 64, bnxt);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sg = 4 * half + i;
-#pragma unroll
-      for (int r = 0; r < RM; ++r) {
-        const int row = 32 * r + l32;
-        const uint4 a = lds[buf][row * 8 + (sg ^ ((row >> 1) & 7))];
-        // Operands swapped (weights as the matrix-core "A"): lane l then holds
-        // C[m = l % 32][n = 8 (q / 4) + 4 (l / 32) + q % 4] in accumulator q.
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bcur[i]),
-                                                         __builtin_bit_cast(bf16x8_t, a), acc[r], 0, 0, 0);
-      }
-    }
+    mfma_slice(buf, bcur);
     if (s + 1 < ns) store_a(buf ^ 1);
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < 4; ++c) bcur[c] = bnxt[c];
+  }
   }
 
   // Epilogue: lane l, accumulator group g (4 registers) = 4 consecutive columns.
@@ -196,20 +226,31 @@ __global__ __launch_bounds__(256) void gelu_reduce_kernel(const float* __restric
   }
 }
 
-template <int RM, int EPI>
+template <int RM, int EPI, int NSL>
 hipError_t launch_mid_rm(const MidArgs& p, int tiles_m, int splits, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_mid_kernel<RM, EPI>), dim3((unsigned)(tiles_m * p.tiles_n), (unsigned)splits), dim3(256),
-                     0, s, p);
+  hipLaunchKernelGGL((gemm_mid_kernel<RM, EPI, NSL>), dim3((unsigned)(tiles_m * p.tiles_n), (unsigned)splits),
+                     dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
+// Short splits take the all-loads-at-once form for tile heights of 32 and
+// 64 rows when at most one of its slices would be padding (4 slices for
+// splits of 3-4, 8 for 7-8; measured: padding slices cost more than the
+// loop saves); taller tiles and other splits loop.
 template <int EPI>
 hipError_t launch_mid(int rm, const MidArgs& p, int splits, hipStream_t s) {
   const int tiles_m = (p.M + 32 * rm - 1) / (32 * rm);
+  const int ns = (p.Ks + 63) / 64;
   switch (rm) {
-    case 1: return launch_mid_rm<1, EPI>(p, tiles_m, splits, s);
-    case 2: return launch_mid_rm<2, EPI>(p, tiles_m, splits, s);
-    default: return launch_mid_rm<4, EPI>(p, tiles_m, splits, s);
+    case 1:
+      if (ns >= 3 && ns <= 4) return launch_mid_rm<1, EPI, 4>(p, tiles_m, splits, s);
+      if (ns >= 7 && ns <= 8) return launch_mid_rm<1, EPI, 8>(p, tiles_m, splits, s);
+      return launch_mid_rm<1, EPI, 0>(p, tiles_m, splits, s);
+    case 2:
+      if (ns >= 3 && ns <= 4) return launch_mid_rm<2, EPI, 4>(p, tiles_m, splits, s);
+      if (ns >= 7 && ns <= 8) return launch_mid_rm<2, EPI, 8>(p, tiles_m, splits, s);
+      return launch_mid_rm<2, EPI, 0>(p, tiles_m, splits, s);
+    default: return launch_mid_rm<4, EPI, 0>(p, tiles_m, splits, s);
   }
 }
 
@@ -230,6 +271,7 @@ int pick_rm(int64_t T, int64_t out) {
 // four times the weight matrix's bytes (sp * T * out * 4 <= 4 * K * out * 2).
 int pick_splits(int64_t tiles, int64_t T, int64_t K) {
   int64_t sp = (kTargetBlocks + tiles - 1) / tiles;
+  if (T <= 64 * 2) sp = std::max<int64_t>(sp, (K + 511) / 512);  // short splits load all at once
   sp = std::min<int64_t>(sp, std::max<int64_t>(1, K / 128));
   sp = std::min<int64_t>(sp, std::max<int64_t>(1, 2 * K / T));
   return (int)std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
