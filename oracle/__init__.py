@@ -14,6 +14,8 @@ Definitions followed (MoLE article, the "ICML 2025 Spotlight | MoLE" page):
   * training section -- all routed experts active, router on the contextual
     hidden state: gates = softmax(W_r h) over all N experts;
   * results section -- the table compressed to 3 bits ("e.g. NF3");
+  * results section ("redundancy remains at 3 bits") -- other table formats:
+    NF4 (the same construction at 4 bits) and int8 with one scale per row;
   * training section and complexity analysis -- shared experts keep reading
     the contextual hidden state and are the only experts still computed at
     inference, so a MoLE block adds shared FFN + routed lookup to the
@@ -76,6 +78,14 @@ def _load():
             "oracle_dequant_nf3": (I, [P, P, I64, I64, P]),
             "oracle_lookup_combine_nf3": (I, [P, P, P, I, P, P, I64, I64, I64, I64, P, I]),
             "oracle_shared_ffn": (I, [P, P, P, I, I64, I64, I64, P, I]),
+            "oracle_nf4_levels": (None, [P]),
+            "oracle_nf4_midpoints": (None, [P]),
+            "oracle_pack_nf4": (I, [P, I, I64, I64, P, P, P, I]),
+            "oracle_unpack_nf4": (I, [P, I64, I64, P]),
+            "oracle_dequant_nf4": (I, [P, P, I64, I64, P]),
+            "oracle_pack_int8": (I, [P, I, I64, I64, P, P, I]),
+            "oracle_dequant_int8": (I, [P, P, I64, I64, P]),
+            "oracle_lookup_combine_q": (I, [I, P, P, P, I, P, P, I64, I64, I64, I64, P, I]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -258,3 +268,102 @@ def layer_forward(ids, h, w_r, lut, w_s_up, w_s_down, x=None, nthreads: int = 0)
         assert x.shape == out.shape and x.dtype == np.float32
         out = out + x.astype(np.float64)
     return out
+
+
+def nf4_levels() -> np.ndarray:
+    out = np.zeros(16, dtype=np.float32)
+    _load().oracle_nf4_levels(_ptr(out))
+    return out
+
+
+def nf4_midpoints() -> np.ndarray:
+    out = np.zeros(15, dtype=np.float32)
+    _load().oracle_nf4_midpoints(_ptr(out))
+    return out
+
+
+def pack_nf4(table, nthreads: int = 0):
+    """Encode a [..., D] table to NF4.  Returns (codes uint8 [..., D/2],
+    scales uint16 (fp16 bits) [..., D/64], number of saturated blocks)."""
+    D = table.shape[-1]
+    lead = table.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    t2 = np.ascontiguousarray(table.reshape(rows, D))
+    codes = np.zeros((rows, D // 2), dtype=np.uint8)
+    scales = np.zeros((rows, D // 64), dtype=np.uint16)
+    nsat = ctypes.c_int64(0)
+    _check(_load().oracle_pack_nf4(_ptr(t2), _dtype_code(t2), rows, D, _ptr(codes), _ptr(scales),
+                                   ctypes.addressof(nsat), nthreads), "pack_nf4")
+    return codes.reshape(*lead, D // 2), scales.reshape(*lead, D // 64), int(nsat.value)
+
+
+def unpack_nf4(codes, D: int) -> np.ndarray:
+    lead = codes.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    c2 = np.ascontiguousarray(codes.reshape(rows, D // 2))
+    out = np.zeros((rows, D), dtype=np.uint8)
+    _check(_load().oracle_unpack_nf4(_ptr(c2), rows, D, _ptr(out)), "unpack_nf4")
+    return out.reshape(*lead, D)
+
+
+def dequant_nf4(codes, scales, D: int) -> np.ndarray:
+    lead = codes.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    c2 = np.ascontiguousarray(codes.reshape(rows, D // 2))
+    s2 = np.ascontiguousarray(scales.reshape(rows, D // 64))
+    out = np.zeros((rows, D), dtype=np.float64)
+    _check(_load().oracle_dequant_nf4(_ptr(c2), _ptr(s2), rows, D, _ptr(out)), "dequant_nf4")
+    return out.reshape(*lead, D)
+
+
+def pack_int8(table, nthreads: int = 0):
+    """Encode a [..., D] table to int8 with one fp32 scale per row.
+    Returns (codes int8 [..., D], scales float32 [...])."""
+    D = table.shape[-1]
+    lead = table.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    t2 = np.ascontiguousarray(table.reshape(rows, D))
+    codes = np.zeros((rows, D), dtype=np.int8)
+    scales = np.zeros(rows, dtype=np.float32)
+    _check(_load().oracle_pack_int8(_ptr(t2), _dtype_code(t2), rows, D, _ptr(codes), _ptr(scales),
+                                    nthreads), "pack_int8")
+    return codes.reshape(*lead, D), scales.reshape(lead)
+
+
+def dequant_int8(codes, scales) -> np.ndarray:
+    D = codes.shape[-1]
+    lead = codes.shape[:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    c2 = np.ascontiguousarray(codes.reshape(rows, D))
+    s2 = np.ascontiguousarray(scales.reshape(rows)).astype(np.float32)
+    out = np.zeros((rows, D), dtype=np.float64)
+    _check(_load().oracle_dequant_int8(_ptr(c2), _ptr(s2), rows, D, _ptr(out)), "dequant_int8")
+    return out.reshape(*lead, D)
+
+
+def _lookup_combine_q(fmt, ids, h, w_r, codes, scales, D, nthreads):
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    T = ids.size
+    V, N = codes.shape[:2]
+    assert h.shape == (T, D) and w_r.shape == (N, D)
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    y = np.zeros((T, D), dtype=np.float64)
+    _check(_load().oracle_lookup_combine_q(fmt, _ptr(ids), _ptr(h), _ptr(w_r), _dtype_code(h), _ptr(codes),
+                                           _ptr(scales), T, V, D, N, _ptr(y), nthreads),
+           "lookup_combine_q")
+    return y
+
+
+def lookup_combine_nf4(ids, h, w_r, codes, scales, nthreads: int = 0) -> np.ndarray:
+    """y over the NF4 table: codes [V,N,D/2] uint8, scales [V,N,D/64] uint16 (fp16 bits)."""
+    D = codes.shape[2] * 2
+    assert scales.shape == codes.shape[:2] + (D // 64,)
+    return _lookup_combine_q(4, ids, h, w_r, codes, scales.astype(np.uint16), D, nthreads)
+
+
+def lookup_combine_int8(ids, h, w_r, codes, scales, nthreads: int = 0) -> np.ndarray:
+    """y over the int8 table: codes [V,N,D] int8, scales [V,N] float32."""
+    D = codes.shape[2]
+    assert scales.shape == codes.shape[:2]
+    return _lookup_combine_q(8, ids, h, w_r, codes, scales.astype(np.float32), D, nthreads)

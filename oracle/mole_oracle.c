@@ -476,3 +476,191 @@ int oracle_shared_ffn(const void* h, const void* w_s_up, const void* w_s_down,
   }
   return failed ? OR_ERR_MEM : OR_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Other table formats (results section: the table still carries redundancy */
+/* at 3 bits).  NF4: the NormalFloat construction at k = 4, same blocks and  */
+/* scales as NF3.  int8: one fp32 absmax scale per (v, e) row.               */
+/* ------------------------------------------------------------------------ */
+
+/* NormalFloat levels at k = 4 bits (the same construction as at 3 bits:
+ * p* = 1 - (1/(2*15) + 1/(2*16))/2; Phi^-1 at 9 evenly spaced probabilities
+ * from p* down to 1/2 (1/2 dropped) for the 8 positive levels, -Phi^-1 at 8
+ * evenly spaced probabilities for the 7 negative ones, one exact zero,
+ * normalised by the maximum, sorted, rounded to fp32).  Zero is code 7. */
+void oracle_nf4_levels(float out[16]) {
+  const double pstar = 1.0 - 0.5 * (1.0 / 30.0 + 1.0 / 32.0);
+  double v[16];
+  int n = 0;
+  for (int i = 0; i < 8; ++i)            /* linspace(p*, 0.5, 9)[0..7] */
+    v[n++] = oracle_normal_ppf(pstar + (0.5 - pstar) * (double)i / 8.0);
+  for (int i = 0; i < 7; ++i)            /* linspace(p*, 0.5, 8)[0..6] */
+    v[n++] = -oracle_normal_ppf(pstar + (0.5 - pstar) * (double)i / 7.0);
+  v[n++] = 0.0;
+  double vmax = 0.0;
+  for (int i = 0; i < 16; ++i) if (v[i] > vmax) vmax = v[i];
+  for (int i = 0; i < 16; ++i) v[i] /= vmax;
+  for (int i = 1; i < 16; ++i)
+    for (int j = i; j > 0 && v[j - 1] > v[j]; --j) {
+      double tmp = v[j]; v[j] = v[j - 1]; v[j - 1] = tmp;
+    }
+  for (int i = 0; i < 16; ++i) out[i] = (float)v[i];
+}
+
+void oracle_nf4_midpoints(float out[15]) {
+  float lv[16];
+  oracle_nf4_levels(lv);
+  for (int j = 0; j < 15; ++j) out[j] = (float)(((double)lv[j] + (double)lv[j + 1]) / 2.0);
+}
+
+/*
+ * Encode a [rows][D] table into NF4: per block of 64 elements the fp16
+ * absmax scale exactly as for NF3; code = #{ j : x > fp32(mid[j] * s) }
+ * (strict), code 7 (zero) if s == 0; code i of a row in bits [4i, 4i+4) of
+ * the row's little-endian stream (low nibble first), D/2 bytes per row.
+ */
+int oracle_pack_nf4(const void* lut, int dtype, int64_t rows, int64_t D,
+                    uint8_t* codes, uint16_t* scales, int64_t* n_saturated,
+                    int nthreads) {
+  if (!dtype_ok(dtype) || rows < 0 || D <= 0 || D % 64 != 0) return OR_ERR_ARG;
+  float mid[15];
+  oracle_nf4_midpoints(mid);
+  const int64_t row_bytes = D / 2, nblk = D / 64;
+  int64_t nsat = 0;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(static) reduction(+ : nsat)
+  for (int64_t r = 0; r < rows; ++r) {
+    uint8_t* crow = codes + r * row_bytes;
+    memset(crow, 0, (size_t)row_bytes);
+    for (int64_t b = 0; b < nblk; ++b) {
+      float a = 0.0f;
+      for (int64_t i = 0; i < 64; ++i) {
+        float ax = fabsf((float)load_elem(lut, dtype, r * D + b * 64 + i));
+        if (ax > a) a = ax;
+      }
+      if (a > 65504.0f) { a = 65504.0f; nsat += 1; }
+      const uint16_t sbits = oracle_f32_to_f16_rne(a);
+      scales[r * nblk + b] = sbits;
+      const float s = oracle_f16_to_f32(sbits);
+      float thr[15];
+      for (int j = 0; j < 15; ++j) thr[j] = mid[j] * s;
+      for (int64_t i = 0; i < 64; ++i) {
+        float x = (float)load_elem(lut, dtype, r * D + b * 64 + i);
+        int code = 0;
+        if (s == 0.0f) code = 7;
+        else for (int j = 0; j < 15; ++j) if (x > thr[j]) code += 1;
+        const int64_t pos = 4 * (b * 64 + i);
+        for (int k = 0; k < 4; ++k) put_bit(crow, pos + k, (code >> k) & 1);
+      }
+    }
+  }
+  if (n_saturated) *n_saturated = nsat;
+  return OR_OK;
+}
+
+int oracle_unpack_nf4(const uint8_t* codes, int64_t rows, int64_t D, uint8_t* out) {
+  if (rows < 0 || D <= 0 || D % 64 != 0) return OR_ERR_ARG;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < D; ++i) {
+      const uint8_t* crow = codes + r * (D / 2);
+      int c = 0;
+      for (int k = 0; k < 4; ++k) c |= get_bit(crow, 4 * i + k) << k;
+      out[r * D + i] = (uint8_t)c;
+    }
+  return OR_OK;
+}
+
+int oracle_dequant_nf4(const uint8_t* codes, const uint16_t* scales, int64_t rows,
+                       int64_t D, double* out) {
+  if (rows < 0 || D <= 0 || D % 64 != 0) return OR_ERR_ARG;
+  float lv[16];
+  oracle_nf4_levels(lv);
+  const int64_t nblk = D / 64;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < D; ++i) {
+      const uint8_t* crow = codes + r * (D / 2);
+      int c = 0;
+      for (int k = 0; k < 4; ++k) c |= get_bit(crow, 4 * i + k) << k;
+      out[r * D + i] = (double)lv[c] * (double)oracle_f16_to_f32(scales[r * nblk + i / 64]);
+    }
+  return OR_OK;
+}
+
+/*
+ * Encode a [rows][D] table into int8 with one scale per row:
+ *   a = max |x| over the row (fp32);  s = fp32(a / 127) (one IEEE division);
+ *   q = rint(fp32(x / s)) (IEEE division, ties to even), clamped to
+ *   [-127, 127];  q = 0 for every element if s == 0.
+ * codes [rows][D] int8, scales [rows] fp32.
+ */
+int oracle_pack_int8(const void* lut, int dtype, int64_t rows, int64_t D, int8_t* codes,
+                     float* scales, int nthreads) {
+  if (!dtype_ok(dtype) || rows < 0 || D <= 0) return OR_ERR_ARG;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float a = 0.0f;
+    for (int64_t i = 0; i < D; ++i) {
+      float ax = fabsf((float)load_elem(lut, dtype, r * D + i));
+      if (ax > a) a = ax;
+    }
+    const float s = a / 127.0f;
+    scales[r] = s;
+    for (int64_t i = 0; i < D; ++i) {
+      int q = 0;
+      if (s != 0.0f) {
+        const float x = (float)load_elem(lut, dtype, r * D + i);
+        const float qf = rintf(x / s);
+        q = qf > 127.0f ? 127 : (qf < -127.0f ? -127 : (int)qf);
+      }
+      codes[r * D + i] = (int8_t)q;
+    }
+  }
+  return OR_OK;
+}
+
+int oracle_dequant_int8(const int8_t* codes, const float* scales, int64_t rows, int64_t D,
+                        double* out) {
+  if (rows < 0 || D <= 0) return OR_ERR_ARG;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < D; ++i) out[r * D + i] = (double)codes[r * D + i] * (double)scales[r];
+  return OR_OK;
+}
+
+/*
+ * Lookup-combine over an NF4 or int8 table, from the dequantised values:
+ *   y[t][d] = sum_e g[t][e] * xhat(id_t, e, d).
+ * fmt 4: codes [V][N][D/2], scales fp16 [V][N][D/64];
+ * fmt 8: codes int8 [V][N][D], scales fp32 [V][N].
+ */
+int oracle_lookup_combine_q(int fmt, const int64_t* ids, const void* h, const void* w_r,
+                            int dtype_hw, const void* codes, const void* scales, int64_t T,
+                            int64_t V, int64_t D, int64_t N, double* y, int nthreads) {
+  if ((fmt != 4 && fmt != 8) || !dtype_ok(dtype_hw) || T < 0 || V <= 0 || D <= 0 ||
+      D % 64 != 0 || N <= 0)
+    return OR_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t)
+    if (ids[t] < 0 || ids[t] >= V) return OR_ERR_ID;
+  double* gates = (double*)malloc((size_t)(T > 0 ? T : 1) * N * sizeof(double));
+  double* row = (double*)malloc((size_t)D * sizeof(double));
+  if (!gates || !row) { free(gates); free(row); return OR_ERR_MEM; }
+  int rc = oracle_router_gates(h, w_r, dtype_hw, T, D, N, gates, nthreads);
+  if (rc == OR_OK) {
+    for (int64_t t = 0; t < T; ++t) {
+      const int64_t v = ids[t];
+      for (int64_t d = 0; d < D; ++d) y[t * D + d] = 0.0;
+      for (int64_t e = 0; e < N; ++e) {
+        const int64_t r = v * N + e;
+        if (fmt == 4)
+          oracle_dequant_nf4((const uint8_t*)codes + r * (D / 2), (const uint16_t*)scales + r * (D / 64),
+                             1, D, row);
+        else
+          oracle_dequant_int8((const int8_t*)codes + r * D, (const float*)scales + r, 1, D, row);
+        for (int64_t d = 0; d < D; ++d) y[t * D + d] += gates[t * N + e] * row[d];
+      }
+    }
+  }
+  free(gates);
+  free(row);
+  return rc;
+}

@@ -534,3 +534,127 @@ def test_layer_forward_zero_shared_weights_reduce_to_lookup():
     zu, zd = np.zeros((F, D), np.float32), np.zeros((D, F), np.float32)
     assert np.array_equal(oracle.layer_forward(ids, h, w_r, lut, zu, zd, None),
                           oracle.lookup_combine(ids, h, w_r, lut))
+
+
+# ----------------------------------------------------------------------------
+# Other table formats (results section: redundancy remains at 3 bits): NF4
+# (the NormalFloat construction at 4 bits, same blocks and scales as NF3) and
+# int8 with one fp32 scale per (v, e) row.
+# ----------------------------------------------------------------------------
+
+def test_nf4_codebook_matches_stdlib_construction_and_published_values():
+    lv = oracle.nf4_levels()
+    np.testing.assert_array_equal(lv, nf_levels_stdlib(4))
+    assert lv[7] == 0.0 and lv[0] == -1.0 and lv[15] == 1.0 and np.all(np.diff(lv) > 0)
+    # the NF4 table as published with QLoRA (its probability grid was rounded
+    # to fp32, hence agreement to about 2e-7 rather than bit for bit)
+    np.testing.assert_allclose(lv[[1, 2, 3, 8, 13, 14]],
+                               [-0.6961928, -0.5250731, -0.3949175, 0.0795803, 0.5626170, 0.7229568], atol=2e-7)
+
+
+def test_nf4_midpoints_are_rne_of_exact_midpoints():
+    lv, mid = oracle.nf4_levels(), oracle.nf4_midpoints()
+    for j in range(15):
+        exact = (Fraction(float(lv[j])) + Fraction(float(lv[j + 1]))) / 2
+        assert mid[j] == np.float32(float(exact))  # one rounding of the exact value
+
+
+def test_nf4_pack_worked_example_codes_0_to_15():
+    # s = 1: each element equals a level, codes 0..15 four times; nibbles low
+    # first, so a pair (2k, 2k+1) packs into the byte 0x(2k+1)(2k).
+    lv = oracle.nf4_levels()
+    row = np.tile(lv, 4).astype(np.float32)[None, :]
+    codes, scales, nsat = oracle.pack_nf4(row)
+    assert nsat == 0 and scales[0, 0] == 0x3C00  # fp16 1.0
+    assert bytes(codes[0, :8]).hex() == "1032547698badcfe"
+    np.testing.assert_array_equal(oracle.unpack_nf4(codes, 64)[0], np.tile(np.arange(16), 4))
+    zero = np.zeros((1, 64), np.float32)
+    zc, zs, _ = oracle.pack_nf4(zero)
+    assert zs[0, 0] == 0 and np.all(zc == 0x77)  # code 7 = the zero level
+
+
+def test_nf4_codes_equal_bruteforce_nearest_level():
+    """Away from decision boundaries the threshold code is the nearest level
+    (levels from the stdlib construction; nibbles read in Python)."""
+    r = rng(401)
+    lv = nf_levels_stdlib(4).astype(np.float64)
+    x = (r.standard_normal((48, 128)) * r.choice([1e-3, 0.05, 3.0], size=(48, 1))).astype(np.float32)
+    codes, scales, _ = oracle.pack_nf4(x)
+    s = scales.astype(np.uint16).view(np.float16).astype(np.float64)
+    checked = 0
+    for row in range(48):
+        c = [(codes[row, i // 2] >> (4 * (i % 2))) & 15 for i in range(128)]
+        for i in range(128):
+            t = float(x[row, i]) / s[row, i // 64]
+            dist = np.abs(t - lv)
+            order = np.argsort(dist)
+            if dist[order[1]] - dist[order[0]] < 1e-5:
+                continue
+            assert c[i] == order[0], (row, i, t)
+            checked += 1
+    assert checked > 6000
+
+
+def test_nf4_roundtrip_requantises_and_error_bound():
+    r = rng(402)
+    x = (r.standard_normal((20, 256)) * 0.05).astype(np.float32)
+    codes, scales, _ = oracle.pack_nf4(x)
+    xh = oracle.dequant_nf4(codes, scales, 256)
+    c2, s2, _ = oracle.pack_nf4(xh.astype(np.float32))
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(s2, scales)
+    lv = oracle.nf4_levels().astype(np.float64)
+    half_gap = np.max(np.diff(lv)) / 2
+    s = np.repeat(np.array([[oracle.f16_to_f32(int(v)) for v in row] for row in scales]), 64, axis=1)
+    assert np.all(np.abs(xh - x) <= half_gap * s * (1 + 1e-6) + 1e-12)
+
+
+def test_int8_pack_worked_example_ties_to_even():
+    # absmax 127 -> s = 1 exactly; codes are x rounded half to even
+    row = np.array([[127.0, -127.0, 63.5, 62.5, 0.5, 1.5, -2.5, -0.49] + [0.0] * 56], np.float32)
+    codes, scales = oracle.pack_int8(row)
+    assert scales[0] == 1.0
+    assert codes[0, :8].tolist() == [127, -127, 64, 62, 0, 2, -2, 0]
+    zc, zs = oracle.pack_int8(np.zeros((2, 64), np.float32))
+    assert np.all(zs == 0) and np.all(zc == 0)
+
+
+def test_int8_pack_matches_numpy_ieee_division():
+    r = rng(403)
+    x = (r.standard_normal((30, 192)) * 0.04).astype(np.float32)
+    codes, scales = oracle.pack_int8(x)
+    s_ref = np.abs(x).max(axis=1) / np.float32(127.0)          # float32 IEEE division
+    q_ref = np.clip(np.rint(x / s_ref[:, None]), -127, 127)    # float32 division, rint ties to even
+    np.testing.assert_array_equal(scales, s_ref.astype(np.float32))
+    np.testing.assert_array_equal(codes.astype(np.float64), q_ref)
+    xh = oracle.dequant_int8(codes, scales)
+    assert np.all(np.abs(xh - x) <= scales[:, None].astype(np.float64) * (0.5 + 1e-6))
+    bf = synth.f32_to_bf16_bits(x)
+    cb, sb = oracle.pack_int8(bf)                                # bf16 input is upcast exactly
+    c32, s32 = oracle.pack_int8(synth.bf16_bits_to_f32(bf))
+    np.testing.assert_array_equal(cb, c32)
+    np.testing.assert_array_equal(sb, s32)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "int8"])
+def test_quantised_combine_matches_independent_decode(fmt):
+    r = rng(404)
+    V, N, D, T = 50, 3, 128, 11
+    table = (r.standard_normal((V, N, D)) * 0.05).astype(np.float32)
+    ids = r.integers(0, V, size=T, dtype=np.int64)
+    h = r.standard_normal((T, D), dtype=np.float32)
+    w_r = (r.standard_normal((N, D)) * 0.1).astype(np.float32)
+    g = scipy.special.softmax(as_f64(h) @ as_f64(w_r).T, axis=1)
+    if fmt == "nf4":
+        codes, scales, _ = oracle.pack_nf4(table)
+        lv = oracle.nf4_levels().astype(np.float64)
+        nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(V, N, D)   # independent nibble decode
+        s = np.array([[[oracle.f16_to_f32(int(v)) for v in row] for row in plane] for plane in scales])
+        xh = lv[nib] * np.repeat(s, 64, axis=2)
+        got = oracle.lookup_combine_nf4(ids, h, w_r, codes, scales)
+    else:
+        codes, scales = oracle.pack_int8(table)
+        xh = codes.astype(np.float64) * scales[..., None].astype(np.float64)
+        got = oracle.lookup_combine_int8(ids, h, w_r, codes, scales)
+    ref = np.einsum("te,ted->td", g, xh[ids])
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
