@@ -181,6 +181,45 @@ int mole_layer_forward(const int64_t* ids, const void* h, const void* w_r, const
                        size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Other table formats (results section: the table keeps the model's quality
+ * at 3 bits, so it still carries redundancy; these are the 4- and 8-bit
+ * points next to NF3, with the same combine contract as
+ * mole_lookup_combine_nf3).  Both need D % 64 == 0 (MOLE_ERR_DIM).
+ *
+ * NF4: the NormalFloat construction at 4 bits (16 levels, zero at code 7;
+ * mole_nf4_levels copies them to host memory), blocks of 64 elements with
+ * the fp16 absmax scale exactly as for NF3, code = number of the 15
+ * thresholds fp32(mid[j] * s) strictly below x (code 7 when s == 0), two
+ * codes per byte, element 2i in the low nibble of byte i (D/2 bytes a row).
+ *   lut [V][N][D] (dtype)   codes [V][N][D/2] u8   scales [V][N][D/64] fp16 bits
+ *
+ * int8: one fp32 scale per (v, e) row: a = max |x| over the row,
+ * s = a / 127 (IEEE division); code = rint(x / s) (IEEE division, ties to
+ * even) clamped to [-127, 127], 0 when s == 0; x is reconstructed as code * s.
+ *   lut [V][N][D] (dtype)   codes [V][N][D] int8   scales [V][N] fp32
+ * Codes and scales of both formats are bit-exact functions of the table.
+ * The combines compute y[t][d] = sum_e g[t][e] * xhat(ids[t], e, d) with g as
+ * in mole_lookup_combine; dtype_h is the dtype of h and w_r.
+ * ------------------------------------------------------------------------ */
+int mole_nf4_levels(float* levels_host);
+
+int mole_pack_nf4(const void* lut, uint8_t* codes, uint16_t* scales,
+                  int64_t V, int64_t N, int64_t D, int dtype, void* stream);
+
+int mole_lookup_combine_nf4(const int64_t* ids, const void* h, const void* w_r,
+                            const uint8_t* codes, const uint16_t* scales, float* y,
+                            int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                            void* stream);
+
+int mole_pack_int8(const void* lut, int8_t* codes, float* scales,
+                   int64_t V, int64_t N, int64_t D, int dtype, void* stream);
+
+int mole_lookup_combine_int8(const int64_t* ids, const void* h, const void* w_r,
+                             const int8_t* codes, const float* scales, float* y,
+                             int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
  * Host-resident NF3 table (inference section: after reparameterisation the
  * table lives in lower-tier storage such as CPU memory, each token's
  * entries are looked up there and only the retrieved vectors are loaded

@@ -23,6 +23,11 @@ from ._native import (  # noqa: F401
     mole_build_lut_workspace_size,
     mole_gather_nf3_host,
     mole_layer_forward,
+    mole_lookup_combine_int8,
+    mole_lookup_combine_nf4,
+    mole_nf4_levels,
+    mole_pack_int8,
+    mole_pack_nf4,
     mole_layer_workspace_size,
     mole_lookup_combine,
     mole_lookup_combine_nf3,
@@ -41,4 +46,5 @@ __all__ = [
     "mole_lookup_combine_nf3", "mole_gather_nf3_host", "mole_lookup_combine_nf3_host",
     "mole_nf3_host_staging_size", "mole_nf3_host_stack_staging_size", "mole_prefetch_nf3_host_stack",
     "mole_nf3_levels", "mole_status_string", "mole_layer_forward", "mole_layer_workspace_size",
+    "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4", "mole_pack_int8", "mole_lookup_combine_int8",
 ]

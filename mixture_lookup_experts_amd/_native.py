@@ -72,6 +72,11 @@ def library():
             "mole_lookup_combine_nf3_host": (I, [P, P, P, P, P, P, P, SZ, P,
                                                  I64, I64, I64, I64, I, I, P, P]),
             "mole_layer_workspace_size": (I, [I64, I64, I64, P]),
+            "mole_nf4_levels": (I, [P]),
+            "mole_pack_nf4": (I, [P, P, P, I64, I64, I64, I, P]),
+            "mole_lookup_combine_nf4": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
+            "mole_pack_int8": (I, [P, P, P, I64, I64, I64, I, P]),
+            "mole_lookup_combine_int8": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_layer_forward": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
@@ -324,3 +329,67 @@ def mole_layer_forward(ids, h, w_r, lut, w_s_up, w_s_down, x, workspace, stream=
     _check("mole_layer_forward", library().mole_layer_forward(
         _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut), _ptr(w_s_up), _ptr(w_s_down), _ptr(x),
         T, V, D, N, F, _dtype(h), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mole_nf4_levels() -> list:
+    out = (ctypes.c_float * 16)()
+    _check("mole_nf4_levels", library().mole_nf4_levels(ctypes.addressof(out)))
+    return list(out)
+
+
+def mole_pack_nf4(lut, codes, scales, stream=None) -> None:
+    """NF4-encode lut [V,N,D] into codes [V,N,D/2] (uint8) and scales
+    [V,N,D/64] (fp16 bits, int16/uint16 tensor)."""
+    V, N, D = lut.shape
+    _need(D % 64 == 0, "D must be a multiple of 64")
+    _need(tuple(codes.shape) == (V, N, D // 2) and codes.dtype == torch.uint8, "codes [V,N,D/2] uint8")
+    _need(tuple(scales.shape) == (V, N, D // 64) and scales.element_size() == 2, "scales [V,N,D/64] 16-bit")
+    for t in (lut, codes, scales):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_pack_nf4", library().mole_pack_nf4(
+        _ptr(lut), _ptr(codes), _ptr(scales), V, N, D, _dtype(lut), _stream(stream)))
+
+
+def mole_lookup_combine_nf4(ids, h, w_r, codes, scales, y, stream=None) -> None:
+    V, N, CB = codes.shape
+    D = CB * 2
+    T = ids.numel()
+    _need(tuple(scales.shape) == (V, N, D // 64), "scales [V,N,D/64]")
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "ids [T], h [T,D], w_r [N,D], y [T,D]")
+    _need(ids.dtype == torch.int64 and y.dtype == torch.float32 and h.dtype == w_r.dtype,
+          "ids int64, y float32, h and w_r one dtype")
+    for t in (ids, h, w_r, codes, scales, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_lookup_combine_nf4", library().mole_lookup_combine_nf4(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(codes), _ptr(scales), _ptr(y), T, V, D, N,
+        _dtype(h), _stream(stream)))
+
+
+def mole_pack_int8(lut, codes, scales, stream=None) -> None:
+    """int8-encode lut [V,N,D] into codes [V,N,D] (int8) and one fp32 scale
+    per row, scales [V,N]."""
+    V, N, D = lut.shape
+    _need(D % 64 == 0, "D must be a multiple of 64")
+    _need(tuple(codes.shape) == (V, N, D) and codes.dtype == torch.int8, "codes [V,N,D] int8")
+    _need(tuple(scales.shape) == (V, N) and scales.dtype == torch.float32, "scales [V,N] float32")
+    for t in (lut, codes, scales):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_pack_int8", library().mole_pack_int8(
+        _ptr(lut), _ptr(codes), _ptr(scales), V, N, D, _dtype(lut), _stream(stream)))
+
+
+def mole_lookup_combine_int8(ids, h, w_r, codes, scales, y, stream=None) -> None:
+    V, N, D = codes.shape
+    T = ids.numel()
+    _need(tuple(scales.shape) == (V, N) and scales.dtype == torch.float32, "scales [V,N] float32")
+    _need(codes.dtype == torch.int8, "codes int8")
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "ids [T], h [T,D], w_r [N,D], y [T,D]")
+    _need(ids.dtype == torch.int64 and y.dtype == torch.float32 and h.dtype == w_r.dtype,
+          "ids int64, y float32, h and w_r one dtype")
+    for t in (ids, h, w_r, codes, scales, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_lookup_combine_int8", library().mole_lookup_combine_int8(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(codes), _ptr(scales), _ptr(y), T, V, D, N,
+        _dtype(h), _stream(stream)))

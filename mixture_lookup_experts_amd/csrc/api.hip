@@ -218,11 +218,17 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 4; }
+int mole_abi_version(void) { return 5; }
 
 int mole_nf3_levels(float* levels_host) {
   if (!levels_host) return MOLE_ERR_NULL;
   mole::nf3_levels_host(levels_host);
+  return MOLE_OK;
+}
+
+int mole_nf4_levels(float* levels_host) {
+  if (!levels_host) return MOLE_ERR_NULL;
+  mole::nf4_levels_host(levels_host);
   return MOLE_OK;
 }
 
@@ -306,6 +312,54 @@ int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r, 
     return MOLE_ERR_ALIGN;
   return hip_status(mole::launch_lookup_combine_nf3(ids, h, w_r, codes, scales, y, T, D, N, dtype_h,
                                                     as_stream(stream)));
+}
+
+int mole_pack_nf4(const void* lut, uint8_t* codes, uint16_t* scales, int64_t V, int64_t N, int64_t D,
+                  int dtype, void* stream) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  if (V <= 0 || N <= 0 || D <= 0 || D > kMaxDim || D % 64 != 0) return MOLE_ERR_DIM;
+  if (!lut || !codes || !scales) return MOLE_ERR_NULL;
+  if (!aligned16(lut) || !aligned16(codes) || !aligned16(scales)) return MOLE_ERR_ALIGN;
+  return hip_status(mole::launch_pack_nf4(lut, codes, scales, V * N, D, dtype, as_stream(stream)));
+}
+
+int mole_pack_int8(const void* lut, int8_t* codes, float* scales, int64_t V, int64_t N, int64_t D, int dtype,
+                   void* stream) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  if (V <= 0 || N <= 0 || D <= 0 || D > kMaxDim || D % 64 != 0) return MOLE_ERR_DIM;
+  if (V * N > kMaxDim) return MOLE_ERR_DIM;  // four rows per workgroup, grid in 32 bits
+  if (!lut || !codes || !scales) return MOLE_ERR_NULL;
+  if (!aligned16(lut) || !aligned16(codes) || !aligned16(scales)) return MOLE_ERR_ALIGN;
+  return hip_status(mole::launch_pack_int8(lut, codes, scales, V * N, D, dtype, as_stream(stream)));
+}
+
+namespace {
+int combine_q(int fmt, const int64_t* ids, const void* h, const void* w_r, const void* codes, const void* scales,
+              float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h, void* stream) {
+  if (!dtype_ok(dtype_h)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (D % 64 != 0) return MOLE_ERR_DIM;
+  if (T == 0) return MOLE_OK;
+  if (!ids || !h || !w_r || !codes || !scales || !y) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(codes) || !aligned16(scales) ||
+      !aligned16(y))
+    return MOLE_ERR_ALIGN;
+  return hip_status(mole::launch_lookup_combine_q(fmt, ids, h, w_r, static_cast<const uint8_t*>(codes), scales, y,
+                                                  T, D, N, dtype_h, as_stream(stream)));
+}
+}  // namespace
+
+int mole_lookup_combine_nf4(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
+                            const uint16_t* scales, float* y, int64_t T, int64_t V, int64_t D, int64_t N,
+                            int dtype_h, void* stream) {
+  return combine_q(mole::kFmtNf4, ids, h, w_r, codes, scales, y, T, V, D, N, dtype_h, stream);
+}
+
+int mole_lookup_combine_int8(const int64_t* ids, const void* h, const void* w_r, const int8_t* codes,
+                             const float* scales, float* y, int64_t T, int64_t V, int64_t D, int64_t N,
+                             int dtype_h, void* stream) {
+  return combine_q(mole::kFmtI8, ids, h, w_r, codes, scales, y, T, V, D, N, dtype_h, stream);
 }
 
 int mole_layer_workspace_size(int64_t T, int64_t D, int64_t F, size_t* bytes) {

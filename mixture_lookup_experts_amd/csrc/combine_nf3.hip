@@ -1,10 +1,11 @@
-// Lookup-combine over the 3-bit NF3 table: router softmax + decode of each
-// token's N x D codes (3 bits per element, one fp16 absmax scale per 64
-// elements) + gate-weighted sum.  (MoLE article, results section: the
-// table keeps the model's quality when compressed to 3 bits, e.g. NF3;
-// inference section: each token's expert outputs are fetched by token id.)
-// The routers and the launch-shape helpers are shared with the dense-table
-// kernel.
+// Lookup-combine over a quantised table: router softmax + decode of each
+// token's N x D codes + gate-weighted sum.  Formats: NF3 (3 bits per
+// element, one fp16 absmax scale per 64 elements), NF4 (4 bits, same
+// scales) and int8 (one fp32 scale per table row).  (MoLE article, results
+// section: the table keeps the model's quality when compressed to 3 bits,
+// e.g. NF3, so it still carries redundancy; inference section: each token's
+// expert outputs are fetched by token id.)  The routers and the
+// launch-shape helpers are shared with the dense-table kernel.
 #include "combine_common.hpp"
 
 namespace mole {
@@ -14,9 +15,32 @@ namespace mole {
 // zero, normalised to [-1, 1]), rounded to fp32.  Bit patterns:
 __constant__ uint32_t kNf3LevelBits[8] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
                                           0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
+// NF4 levels: the same construction at 4 bits (8 positive, 7 negative, zero
+// at code 7), rounded to fp32.
+__constant__ uint32_t kNf4LevelBits[16] = {0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+                                           0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+                                           0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+
+// Per-format constants: bytes of codes per 32-element chunk, levels in the
+// decode table (0: the code is the value), experts per batch of code loads.
+template <int FMT> struct QFmt;
+template <> struct QFmt<kFmtNf3> {
+  static constexpr int kChunkBytes = 12, kLevels = 8, kBatch = 8;
+  static constexpr int64_t row_bytes(int64_t D) { return 3 * D / 8; }
+};
+template <> struct QFmt<kFmtNf4> {
+  static constexpr int kChunkBytes = 16, kLevels = 16, kBatch = 8;
+  static constexpr int64_t row_bytes(int64_t D) { return D / 2; }
+};
+template <> struct QFmt<kFmtI8> {
+  static constexpr int kChunkBytes = 32, kLevels = 0, kBatch = 4;
+  static constexpr int64_t row_bytes(int64_t D) { return D; }
+};
 
 // ---------------------------------------------------------------------------
-// NF3 table: 32 codes (12 bytes) per chunk, one fp16 scale per 64 elements.
+// A chunk is 32 elements of a row: 12 bytes of NF3 codes, 16 of NF4 or 32
+// of int8; NF3 and NF4 chunks take one fp16 scale per 64 elements, int8 one
+// fp32 scale per row.
 // A token is owned by G = CP*S lanes: lane (s, c) = s*CP + c decodes chunk c
 // (and c + CP, ... when a row has more than CP chunks) for the experts
 // e = s, s + S, s + 2S, ...; the S partial sums of a chunk then meet in a
@@ -54,16 +78,18 @@ struct SplitReduce {
   }
 };
 
-template <typename TH, int NP, int CP, int S, int MODE>
+template <typename TH, int NP, int CP, int S, int MODE, int FMT = kFmtNf3>
 __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
     const int64_t* __restrict__ ids, const TH* __restrict__ h, const TH* __restrict__ w_r,
-    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const uint8_t* __restrict__ codes, const void* __restrict__ scales_v,
     float* __restrict__ y, int64_t T_, int D, int N, int tpb) {
+  using Q = QFmt<FMT>;
   constexpr int G = CP * S;                        // lanes per token (<= 64)
   static_assert(G <= kWave, "a token's lanes must share one wavefront");
   constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
   constexpr int EPL = (NP + S - 1) / S;            // experts per lane
-  constexpr int EC = EPL < 8 ? EPL : 8;            // experts per batch of code loads
+  constexpr int EC = EPL < Q::kBatch ? EPL : Q::kBatch;  // experts per batch of code loads
+  constexpr int CW = Q::kChunkBytes / 4;           // code dwords per chunk
   constexpr int OUT = 32 / S;                      // outputs stored per lane and chunk
   // Router: on the matrix cores (bf16 h, several tokens per block), else on
   // the vector units (one token per block, or fp32 h; element-wise beyond
@@ -74,10 +100,14 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   constexpr int NPAD = ((NP + 15) / 16) * 16;
   __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * NP];
   __shared__ float gsh[kMaxTokPerBlock * NP];
-  __shared__ float lv[8];
+  __shared__ float lv[Q::kLevels > 0 ? Q::kLevels : 1];
 
   const int tid = threadIdx.x;
-  if (tid < 8) lv[tid] = __uint_as_float(kNf3LevelBits[tid]);
+  if constexpr (FMT == kFmtNf3) {
+    if (tid < 8) lv[tid] = __uint_as_float(kNf3LevelBits[tid]);
+  } else if constexpr (FMT == kFmtNf4) {
+    if (tid < 16) lv[tid] = __uint_as_float(kNf4LevelBits[tid]);
+  }
   const int grp = tid / G, lig = tid % G;  // tpb = blockDim.x / G, passed in
   const int sp = lig / CP, ch = lig % CP;          // expert split, chunk
   const int64_t t0 = (int64_t)blockIdx.x * tpb;
@@ -85,20 +115,32 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   const bool valid = t < T_;
   const int64_t tt = valid ? t : 0;
   const int C = D / 32;                            // 32-element chunks per row
-  const int64_t row_bytes = 3 * (int64_t)D / 8, nblk = D / 64;
+  const int64_t row_bytes = Q::row_bytes(D), nblk = D / 64;
   const int64_t id = valid ? ids[tt] : 0;
   const uint8_t* crow0 = codes + id * (int64_t)N * row_bytes;
-  const uint16_t* srow0 = scales + id * (int64_t)N * nblk;
+  const uint16_t* srow0 = static_cast<const uint16_t*>(scales_v) + id * (int64_t)N * nblk;  // NF3, NF4
+  const float* srowf = static_cast<const float*>(scales_v) + id * (int64_t)N;               // int8
 
-  uint3 cw[EC];
+  uint32_t cw[EC][CW];
   uint32_t sc[EC];
   auto load_batch = [&](int c, int j0) {
 #pragma unroll
     for (int j = 0; j < EC; ++j) {
       const int e = (j0 + j) * S + sp;
       if (e < N) {
-        cw[j] = *reinterpret_cast<const uint3*>(crow0 + (int64_t)e * row_bytes + (int64_t)c * 12);
-        sc[j] = srow0[(int64_t)e * nblk + (c >> 1)];
+        const uint8_t* src = crow0 + (int64_t)e * row_bytes + (int64_t)c * Q::kChunkBytes;
+        if constexpr (FMT == kFmtNf3) {
+          const uint3 v = *reinterpret_cast<const uint3*>(src);
+          cw[j][0] = v.x; cw[j][1] = v.y; cw[j][2] = v.z;
+        } else {
+#pragma unroll
+          for (int q = 0; q < CW / 4; ++q) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src + 16 * q);
+            cw[j][4 * q] = v.x; cw[j][4 * q + 1] = v.y; cw[j][4 * q + 2] = v.z; cw[j][4 * q + 3] = v.w;
+          }
+        }
+        if constexpr (FMT == kFmtI8) sc[j] = __float_as_uint(srowf[e]);
+        else sc[j] = srow0[(int64_t)e * nblk + (c >> 1)];
       }
     }
   };
@@ -150,16 +192,28 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
       for (int j = 0; j < EC; ++j) {
         const int e = (j0 + j) * S + sp;
         if (e < N) {
-          const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j]);
+          const float sv = FMT == kFmtI8 ? __uint_as_float(sc[j])
+                                         : (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j]);
           const float ws = gsh[grp * NP + e] * sv;
-          const uint32_t w[3] = {cw[j].x, cw[j].y, cw[j].z};
+          const uint32_t* w = cw[j];
+          if constexpr (FMT == kFmtNf3) {
 #pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const int pos = 3 * i, wd = pos >> 5, off = pos & 31;
-            uint32_t code;
-            if (off <= 29) code = (w[wd] >> off) & 7u;
-            else code = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off) & 7u;
-            acc[i] = fmaf(ws, lv[code], acc[i]);
+            for (int i = 0; i < 32; ++i) {
+              const int pos = 3 * i, wd = pos >> 5, off = pos & 31;
+              uint32_t code;
+              if (off <= 29) code = (w[wd] >> off) & 7u;
+              else code = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off) & 7u;
+              acc[i] = fmaf(ws, lv[code], acc[i]);
+            }
+          } else if constexpr (FMT == kFmtNf4) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) acc[i] = fmaf(ws, lv[(w[i >> 3] >> (4 * (i & 7))) & 15u], acc[i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+              const int q = (int)(w[i >> 2] << (24 - 8 * (i & 3))) >> 24;  // signed byte i
+              acc[i] = fmaf(ws, (float)q, acc[i]);
+            }
           }
         }
       }
@@ -179,9 +233,9 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
 // ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
-template <typename TH, int NP, int CP>
+template <typename TH, int NP, int CP, int FMT>
 static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
-                             const uint16_t* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
+                             const void* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
   constexpr int S = 64 / CP < NP ? 64 / CP : NP;  // expert splits per token
   constexpr int G = CP * S;
   const int tpb = pick_tokens_per_block(T, G);
@@ -192,58 +246,87 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   // One token per block: the vector-unit router (see LaneRouter).
   if constexpr (sizeof(TH) == 2 && NP <= 16) {
     if (tpb == 1) {
-      hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterLane>), dim3((unsigned)blocks), dim3(G),
-                         0, s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, 1);
+      hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterLane, FMT>), dim3((unsigned)blocks),
+                         dim3(G), 0, s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, 1);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterMfma>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterMfma, FMT>), dim3((unsigned)blocks),
                      dim3(G * tpb), 0, s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, tpb);
   return hipGetLastError();
 }
 
-template <typename TH, int NP>
+template <typename TH, int NP, int FMT>
 static hipError_t dispatch_nf3_cp(int CP, const int64_t* ids, const void* h, const void* w_r,
-                                  const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                  const uint8_t* codes, const void* scales, float* y, int64_t T,
                                   int D, int N, hipStream_t s) {
   switch (CP) {
-    case 8: return launch_nf3<TH, NP, 8>(ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 16: return launch_nf3<TH, NP, 16>(ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 32: return launch_nf3<TH, NP, 32>(ids, h, w_r, codes, scales, y, T, D, N, s);
-    default: return launch_nf3<TH, NP, 64>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 8: return launch_nf3<TH, NP, 8, FMT>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 16: return launch_nf3<TH, NP, 16, FMT>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 32: return launch_nf3<TH, NP, 32, FMT>(ids, h, w_r, codes, scales, y, T, D, N, s);
+    default: return launch_nf3<TH, NP, 64, FMT>(ids, h, w_r, codes, scales, y, T, D, N, s);
   }
 }
 
-template <typename TH>
+template <typename TH, int FMT>
 static hipError_t dispatch_nf3_np(int NP, int CP, const int64_t* ids, const void* h, const void* w_r,
-                                  const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                  const uint8_t* codes, const void* scales, float* y, int64_t T,
                                   int D, int N, hipStream_t s) {
   switch (NP) {
-    case 1: return dispatch_nf3_cp<TH, 1>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 2: return dispatch_nf3_cp<TH, 2>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 4: return dispatch_nf3_cp<TH, 4>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 8: return dispatch_nf3_cp<TH, 8>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 16: return dispatch_nf3_cp<TH, 16>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
-    case 32: return dispatch_nf3_cp<TH, 32>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
-    default: return dispatch_nf3_cp<TH, 64>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 1: return dispatch_nf3_cp<TH, 1, FMT>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 2: return dispatch_nf3_cp<TH, 2, FMT>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 4: return dispatch_nf3_cp<TH, 4, FMT>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 8: return dispatch_nf3_cp<TH, 8, FMT>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 16: return dispatch_nf3_cp<TH, 16, FMT>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    case 32: return dispatch_nf3_cp<TH, 32, FMT>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
+    default: return dispatch_nf3_cp<TH, 64, FMT>(CP, ids, h, w_r, codes, scales, y, T, D, N, s);
   }
+}
+
+template <int FMT>
+static hipError_t launch_q(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
+                           const void* scales, float* y, int64_t T, int64_t D, int64_t N, int dtype_h,
+                           hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int NP = next_pow2((int)N);
+  const int CP = pick_group((int)(D / 32), 8, 64);  // lanes per expert split: chunks of a row
+  if (dtype_h == kF32)
+    return dispatch_nf3_np<float, FMT>(NP, CP, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
+  return dispatch_nf3_np<uint16_t, FMT>(NP, CP, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
 }
 
 hipError_t launch_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
                                      const uint8_t* codes, const uint16_t* scales, float* y,
                                      int64_t T, int64_t D, int64_t N, int dtype_h, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const int NP = next_pow2((int)N);
-  const int CP = pick_group((int)(D / 32), 8, 64);  // lanes per expert split: chunks of a row
-  if (dtype_h == kF32)
-    return dispatch_nf3_np<float>(NP, CP, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
-  return dispatch_nf3_np<uint16_t>(NP, CP, ids, h, w_r, codes, scales, y, T, (int)D, (int)N, s);
+  return launch_q<kFmtNf3>(ids, h, w_r, codes, scales, y, T, D, N, dtype_h, s);
+}
+
+hipError_t launch_lookup_combine_q(int fmt, const int64_t* ids, const void* h, const void* w_r,
+                                   const uint8_t* codes, const void* scales, float* y, int64_t T, int64_t D,
+                                   int64_t N, int dtype_h, hipStream_t s) {
+  switch (fmt) {
+    case kFmtNf3: return launch_q<kFmtNf3>(ids, h, w_r, codes, scales, y, T, D, N, dtype_h, s);
+    case kFmtNf4: return launch_q<kFmtNf4>(ids, h, w_r, codes, scales, y, T, D, N, dtype_h, s);
+    case kFmtI8: return launch_q<kFmtI8>(ids, h, w_r, codes, scales, y, T, D, N, dtype_h, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 void nf3_levels_host(float* out) {
   static const uint32_t bits[8] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
                                    0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
   for (int i = 0; i < 8; ++i) {
+    union { uint32_t u; float f; } cv;
+    cv.u = bits[i];
+    out[i] = cv.f;
+  }
+}
+
+void nf4_levels_host(float* out) {
+  static const uint32_t bits[16] = {0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
+                                    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
+                                    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+  for (int i = 0; i < 16; ++i) {
     union { uint32_t u; float f; } cv;
     cv.u = bits[i];
     out[i] = cv.f;

@@ -35,14 +35,15 @@ def test_header_declares_the_hot_path():
                "mole_lookup_combine_nf3_host", "mole_nf3_host_staging_size", "mole_status_string",
                "mole_last_hip_error",
                "mole_nf3_levels", "mole_abi_version", "mole_layer_forward",
-               "mole_layer_workspace_size"):
+               "mole_layer_workspace_size", "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4",
+               "mole_pack_int8", "mole_lookup_combine_int8"):
         assert fn in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 4
+    assert lib.mole_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -240,3 +241,34 @@ def test_layer_workspace_size_and_errors(lib):
     assert call(x=P(a + 4)) == ALIGN
     assert call(wsb=ws - 1) == WS
     assert call(T=0, ids=None, x=None, wsp=None, wsb=0) == OK   # empty batch: no-op
+
+
+def test_library_nf4_codebook_is_the_construction(lib):
+    import oracle
+    np.testing.assert_array_equal(np.array(mole.mole_nf4_levels(), np.float32), oracle.nf4_levels())
+
+
+@pytest.mark.parametrize("fn", ["mole_pack_nf4", "mole_pack_int8"])
+def test_quant_pack_argument_errors(lib, fn):
+    a = 0x1000
+    f = getattr(lib, fn)
+    assert f(P(a), P(a), P(a), 8, 4, 96, 1, None) == DIM
+    assert f(P(a), P(a), P(a), 0, 4, 128, 1, None) == DIM
+    assert f(P(a), P(a), P(a), 8, 4, 128, 9, None) == DTYPE
+    assert f(None, P(a), P(a), 8, 4, 128, 1, None) == NULL
+    assert f(P(a), P(a + 4), P(a), 8, 4, 128, 1, None) == ALIGN
+
+
+@pytest.mark.parametrize("fn", ["mole_lookup_combine_nf4", "mole_lookup_combine_int8"])
+def test_quant_combine_argument_errors(lib, fn):
+    a = 0x1000
+    f = getattr(lib, fn)
+
+    def call(T=4, V=8, D=128, N=4, dt=1, ids=P(a), codes=P(a), y=P(a)):
+        return f(ids, P(a), P(a), codes, P(a), y, T, V, D, N, dt, None)
+    assert call(D=96) == DIM
+    assert call(N=65) == UNSUP
+    assert call(dt=5) == DTYPE
+    assert call(codes=None) == NULL
+    assert call(y=P(a + 4)) == ALIGN
+    assert call(T=0, ids=None, codes=None, y=None) == OK

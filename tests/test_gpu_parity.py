@@ -588,3 +588,142 @@ def test_layer_graph_replay_matches_eager():
         y = x0.clone()
         mole.mole_layer_forward(ids, h, w_r, lut, wu, wd, y, ws)  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# Other table formats: NF4 (NormalFloat at 4 bits) and int8 with one scale per
+# row (results section: the table still carries redundancy at 3 bits)
+# ----------------------------------------------------------------------------
+
+def run_pack_q(fmt, table):
+    lut = dev(table)
+    V, N, D = table.shape
+    if fmt == "nf4":
+        codes = torch.empty((V, N, D // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((V, N, D // 64), dtype=torch.int16, device="cuda")
+        mole.mole_pack_nf4(lut, codes, scales)
+    else:
+        codes = torch.empty((V, N, D), dtype=torch.int8, device="cuda")
+        scales = torch.empty((V, N), dtype=torch.float32, device="cuda")
+        mole.mole_pack_int8(lut, codes, scales)
+    torch.cuda.synchronize()
+    return host(codes), host(scales)
+
+
+def oracle_pack_q(fmt, table):
+    if fmt == "nf4":
+        c, s, _ = oracle.pack_nf4(table)
+        return c, s
+    return oracle.pack_int8(table)
+
+
+def run_combine_q(fmt, ids, h, w_r, codes, scales):
+    y = torch.empty((ids.size, h.shape[1]), dtype=torch.float32, device="cuda")
+    if fmt == "nf4":
+        mole.mole_lookup_combine_nf4(dev(ids), dev(h), dev(w_r), dev(codes), dev(scales.view(np.int16)), y)
+    else:
+        mole.mole_lookup_combine_int8(dev(ids), dev(h), dev(w_r), dev(codes), dev(scales), y)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def oracle_combine_q(fmt, ids, h, w_r, codes, scales):
+    if fmt == "nf4":
+        return oracle.lookup_combine_nf4(ids, h, w_r, codes, scales)
+    return oracle.lookup_combine_int8(ids, h, w_r, codes, scales)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "int8"])
+@pytest.mark.parametrize("V,N,D,dtype,std", [(512, 4, 64, "f32", 0.02), (300, 4, 768, "bf16", 0.02),
+                                             (100, 16, 1024, "bf16", 1.0), (33, 3, 2048, "bf16", 1e-3),
+                                             (7, 1, 128, "f32", 3.0), (20, 2, 4096, "bf16", 0.05)])
+def test_pack_q_bit_exact(fmt, V, N, D, dtype, std):
+    table = rand_table(20 + D + V, V, N, D, dtype, std=std)
+    codes, scales = run_pack_q(fmt, table)
+    c_ref, s_ref = oracle_pack_q(fmt, table)
+    np.testing.assert_array_equal(scales.view(s_ref.dtype), s_ref)
+    np.testing.assert_array_equal(codes.view(c_ref.dtype), c_ref)
+
+
+def test_pack_nf4_edge_cases_bit_exact():
+    """Exact threshold ties (strict compare keeps the lower code) and their
+    float neighbours, every level, zero and tiny blocks (code 7), fp16-subnormal
+    scales and saturation at 65504."""
+    mid, lv = oracle.nf4_midpoints(), oracle.nf4_levels()
+    tie = np.zeros(64, np.float32)
+    tie[0] = 1.0
+    tie[1:16] = mid
+    tie[16:31] = np.nextafter(mid, np.float32(2))
+    tie[31:46] = np.nextafter(mid, np.float32(-2))
+    tie[46:62] = lv
+    rows = [tie, np.zeros(64, np.float32), np.full(64, 1e-9, np.float32),
+            np.linspace(-3e-6, 2e-6, 64).astype(np.float32), np.linspace(-1e5, 7e4, 64).astype(np.float32)]
+    table = np.stack(rows).reshape(len(rows), 1, 64)
+    codes, scales = run_pack_q("nf4", table)
+    c_ref, s_ref, nsat = oracle.pack_nf4(table)
+    assert nsat == 1
+    np.testing.assert_array_equal(scales.view(np.uint16), s_ref)
+    np.testing.assert_array_equal(codes, c_ref)
+
+
+def test_pack_int8_edge_cases_bit_exact():
+    """Values at exact half-steps (ties to even), the absmax element on both
+    signs, an all-zero row, tiny and huge rows."""
+    half = (np.arange(64, dtype=np.float32) - 32) + np.float32(0.5)  # absmax 31.5 -> s = 31.5/127
+    unit = np.concatenate([[127.0, -127.0], np.arange(-31, 31) + 0.5]).astype(np.float32)  # s = 1 exactly
+    rows = [half, unit, np.zeros(64, np.float32), np.full(64, -1e-30, np.float32),
+            np.linspace(-3e38, 1e38, 64).astype(np.float32)]
+    table = np.stack(rows).reshape(len(rows), 1, 64)
+    codes, scales = run_pack_q("int8", table)
+    c_ref, s_ref = oracle.pack_int8(table)
+    np.testing.assert_array_equal(scales, s_ref)
+    np.testing.assert_array_equal(codes.view(np.int8), c_ref)
+    assert s_ref[1, 0] == 1.0 and c_ref[1, 0, 2:6].tolist() == [-30, -30, -28, -28]
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "int8"])
+@pytest.mark.parametrize("V,N,D,T,dtype", [(512, 4, 64, 64, "f32"), (300, 4, 768, 200, "bf16"),
+                                           (300, 16, 1024, 257, "bf16"), (100, 16, 2048, 33, "bf16"),
+                                           (64, 64, 128, 10, "bf16"), (50, 3, 192, 17, "f32"),
+                                           (40, 1, 64, 5, "bf16"), (300, 16, 1024, 2051, "bf16"),
+                                           (100, 64, 512, 2048, "bf16")])
+def test_combine_q_matches_oracle(fmt, V, N, D, T, dtype):
+    seed = 3000 + V + N + D
+    table = rand_table(seed, V, N, D, "bf16")
+    codes, scales = oracle_pack_q(fmt, table)
+    h, w_r = rand_hw(seed + 1, T, N, D, dtype, wstd=0.3)
+    ids = rng(seed + 2).integers(0, V, T).astype(np.int64)
+    y = run_combine_q(fmt, ids, h, w_r, codes, scales)
+    assert combine_rel_err(y, oracle_combine_q(fmt, ids, h, w_r, codes, scales)) <= COMBINE_TOL
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "int8"])
+@pytest.mark.parametrize("T", [1, 256, 4096])
+def test_combine_q_full_size_zipf(fmt, T):
+    """410M-class table (V=50304, N=16, D=1024), Zipf ids: codes from the
+    oracle's encoding of the rows the batch touches."""
+    w = synth.WORKLOADS["410m"]
+    ids = synth.make_ids(w, T)
+    uniq = np.unique(ids)
+    table = rand_table(92, w.V, w.N, w.D, "bf16", std=0.02, rows=uniq)
+    codes, scales = oracle_pack_q(fmt, table)
+    h = synth.make_hidden(w, T)
+    w_r = synth.make_router(w)
+    y = run_combine_q(fmt, ids, h, w_r, codes, scales)
+    assert combine_rel_err(y, oracle_combine_q(fmt, ids, h, w_r, codes, scales)) <= COMBINE_TOL
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "int8"])
+def test_pack_q_full_size_sampled_rows(fmt):
+    """410M-class table packed on the GPU in one launch; 1024 seeded rows plus
+    the first and last are re-encoded by the oracle; untouched rows are zero."""
+    w = synth.WORKLOADS["410m"]
+    sample = np.unique(np.concatenate([[0, w.V - 1], rng(13).integers(0, w.V, 1024)]))
+    table = rand_table(14, w.V, w.N, w.D, "bf16", std=0.02, rows=sample)
+    codes, scales = run_pack_q(fmt, table)
+    c_ref, s_ref = oracle_pack_q(fmt, table[sample])
+    np.testing.assert_array_equal(scales[sample].view(s_ref.dtype), s_ref)
+    np.testing.assert_array_equal(codes[sample].view(c_ref.dtype), c_ref)
+    other = np.setdiff1d(np.arange(w.V), sample)[:300]
+    assert np.all(scales[other] == 0)
+    assert np.all(codes[other] == (0x77 if fmt == "nf4" else 0))
