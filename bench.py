@@ -288,8 +288,9 @@ def main():
 
 def scale_probe(torch, mole, synth, dev, stream):
     """Combine throughput where one launch moves tens of MB: the 410M-class
-    table (50304 x 16 x 1024 bf16 and its NF3 form) at T = 1024 and 4096,
-    Zipf ids and a distinct-id control (gathered bytes = unique bytes)."""
+    table (50304 x 16 x 1024 bf16 and its NF3, NF4 and int8 forms) at
+    T = 1024 and 4096, Zipf ids and a distinct-id control (gathered bytes =
+    unique bytes); plus the NF4 and int8 encoders over the whole table."""
     w = synth.WORKLOADS["410m"]
     V, D, N = w.V, w.D, w.N
     # every input is produced on `stream`, the stream the kernels run on
@@ -302,8 +303,29 @@ def scale_probe(torch, mole, synth, dev, stream):
     scales = torch.empty((V, N, D // 64), dtype=torch.int16, device=dev)
     w_r = (torch.randn((N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16)
     mole.mole_pack_nf3(lut, codes, scales, stream=stream)
-    out = {"workload": "410M-class table V=50304 D=1024 N=16 (bf16 %.2f GB, NF3 %.2f GB)"
-           % (V * N * D * 2 / 1e9, V * N * (3 * D // 8 + D // 32) / 1e9)}
+    # the 4- and 8-bit formats of the same table
+    codes4 = torch.empty((V, N, D // 2), dtype=torch.uint8, device=dev)
+    scales4 = torch.empty((V, N, D // 64), dtype=torch.int16, device=dev)
+    codes8 = torch.empty((V, N, D), dtype=torch.int8, device=dev)
+    scales8 = torch.empty((V, N), dtype=torch.float32, device=dev)
+    out = {"workload": "410M-class table V=50304 D=1024 N=16 (bf16 %.2f GB, NF3 %.2f GB, NF4 %.2f GB, "
+           "int8 %.2f GB)" % (V * N * D * 2 / 1e9, V * N * (3 * D // 8 + D // 32) / 1e9,
+                              V * N * (D // 2 + D // 32) / 1e9, V * N * (D + 4) / 1e9)}
+    packs = {}
+    for name, fn, wbytes in (
+            ("nf4", lambda: mole.mole_pack_nf4(lut, codes4, scales4, stream=stream), V * N * (D // 2 + D // 32)),
+            ("int8", lambda: mole.mole_pack_int8(lut, codes8, scales8, stream=stream), V * N * (D + 4))):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        byts = V * N * D * 2 + wbytes
+        packs[name] = {"ms": ms, "gbs": byts / (ms * 1e-3) / 1e9, "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    out["pack"] = packs
     perm = synth.rank_permutation(w)
     for T in (1024, 4096):
         for kind in ("zipf", "distinct"):
@@ -318,7 +340,13 @@ def scale_probe(torch, mole, synth, dev, stream):
                                                                 stream=stream), N * D * 2),
                     ("nf3", lambda i: mole.mole_lookup_combine_nf3(ids_l[i % 8], h_l[i % 8], w_r, codes,
                                                                    scales, y, stream=stream),
-                     N * (3 * D // 8 + D // 32))):
+                     N * (3 * D // 8 + D // 32)),
+                    ("nf4", lambda i: mole.mole_lookup_combine_nf4(ids_l[i % 8], h_l[i % 8], w_r, codes4,
+                                                                   scales4, y, stream=stream),
+                     N * (D // 2 + D // 32)),
+                    ("int8", lambda i: mole.mole_lookup_combine_int8(ids_l[i % 8], h_l[i % 8], w_r, codes8,
+                                                                     scales8, y, stream=stream),
+                     N * (D + 4))):
                 with torch.cuda.stream(stream):
                     for i in range(5):
                         fn(i)

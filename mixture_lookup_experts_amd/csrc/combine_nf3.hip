@@ -29,7 +29,7 @@ template <> struct QFmt<kFmtNf3> {
   static constexpr int64_t row_bytes(int64_t D) { return 3 * D / 8; }
 };
 template <> struct QFmt<kFmtNf4> {
-  static constexpr int kChunkBytes = 16, kLevels = 16, kBatch = 8;
+  static constexpr int kChunkBytes = 16, kLevels = 16, kBatch = 4;
   static constexpr int64_t row_bytes(int64_t D) { return D / 2; }
 };
 template <> struct QFmt<kFmtI8> {
