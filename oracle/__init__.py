@@ -16,6 +16,9 @@ Definitions followed (MoLE article, the "ICML 2025 Spotlight | MoLE" page):
   * results section -- the table compressed to 3 bits ("e.g. NF3");
   * results section ("redundancy remains at 3 bits") -- other table formats:
     NF4 (the same construction at 4 bits) and int8 with one scale per row;
+  * training section -- the training-mode forward (every expert on the
+    token's embedding, dense gates) and its backward pass (``train_forward``,
+    ``train_backward``);
   * training section and complexity analysis -- shared experts keep reading
     the contextual hidden state and are the only experts still computed at
     inference, so a MoLE block adds shared FFN + routed lookup to the
@@ -86,6 +89,8 @@ def _load():
             "oracle_pack_int8": (I, [P, I, I64, I64, P, P, I]),
             "oracle_dequant_int8": (I, [P, P, I64, I64, P]),
             "oracle_lookup_combine_q": (I, [I, P, P, P, I, P, P, I64, I64, I64, I64, P, I]),
+            "oracle_train_forward": (I, [P, P, P, P, P, P, I, I64, I64, I64, I64, I64, P, I]),
+            "oracle_train_backward": (I, [P, P, P, P, P, P, I, P, I64, I64, I64, I64, I64, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -367,3 +372,38 @@ def lookup_combine_int8(ids, h, w_r, codes, scales, nthreads: int = 0) -> np.nda
     D = codes.shape[2]
     assert scales.shape == codes.shape[:2]
     return _lookup_combine_q(8, ids, h, w_r, codes, scales.astype(np.float32), D, nthreads)
+
+
+def train_forward(ids, emb, w_up, w_down, h, w_r, nthreads: int = 0) -> np.ndarray:
+    """y[t] = sum_e softmax(W_r . h[t])[e] * W_down[e] . GELU(W_up[e] . Emb[ids[t]]), fp64.
+    emb [V,D], w_up [N,F,D], w_down [N,D,F], h [T,D], w_r [N,D], one dtype."""
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    T = ids.size
+    V, D = emb.shape
+    N, F, _ = w_up.shape
+    dt = _dtype_code(emb)
+    for a in (w_up, w_down, h, w_r):
+        assert _dtype_code(a) == dt
+    y = np.zeros((T, D), dtype=np.float64)
+    _check(_load().oracle_train_forward(_ptr(ids), _ptr(emb), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(w_r), dt,
+                                        T, V, D, F, N, _ptr(y), nthreads), "train_forward")
+    return y
+
+
+def train_backward(ids, emb, w_up, w_down, h, w_r, dy):
+    """Gradients of sum(dy * train_forward(...)) in fp64: a dict with
+    d_w_up [N,F,D], d_w_down [N,D,F], d_w_r [N,D], d_h [T,D], d_emb [V,D]."""
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    T = ids.size
+    V, D = emb.shape
+    N, F, _ = w_up.shape
+    dt = _dtype_code(emb)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    assert dy.shape == (T, D)
+    out = {"d_w_up": np.zeros((N, F, D)), "d_w_down": np.zeros((N, D, F)), "d_w_r": np.zeros((N, D)),
+           "d_h": np.zeros((T, D)), "d_emb": np.zeros((V, D))}
+    _check(_load().oracle_train_backward(_ptr(ids), _ptr(emb), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(w_r), dt,
+                                         _ptr(dy), T, V, D, F, N, _ptr(out["d_w_up"]), _ptr(out["d_w_down"]),
+                                         _ptr(out["d_w_r"]), _ptr(out["d_h"]), _ptr(out["d_emb"])),
+           "train_backward")
+    return out

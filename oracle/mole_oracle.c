@@ -664,3 +664,152 @@ int oracle_lookup_combine_q(int fmt, const int64_t* ids, const void* h, const vo
   free(row);
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Training mode (training section: every routed expert reads the shallow  */
+/* embedding of the token, all experts are active, the router reads the    */
+/* contextual hidden state; inference section: the table is this forward   */
+/* pass evaluated for every vocabulary row).                                */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Forward: y[t][:] = sum_e g[t][e] * W_down[e] . GELU(W_up[e] . Emb[ids[t]]),
+ * g = softmax(W_r . h[t]) over all N.  y is [T][D] fp64.
+ */
+int oracle_train_forward(const int64_t* ids, const void* emb, const void* w_up, const void* w_down,
+                         const void* h, const void* w_r, int dtype, int64_t T, int64_t V, int64_t D,
+                         int64_t F, int64_t N, double* y, int nthreads) {
+  if (!dtype_ok(dtype) || T < 0 || V <= 0 || D <= 0 || F <= 0 || N <= 0) return OR_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t)
+    if (ids[t] < 0 || ids[t] >= V) return OR_ERR_ID;
+  double* gates = (double*)malloc((size_t)(T > 0 ? T : 1) * N * sizeof(double));
+  if (!gates) return OR_ERR_MEM;
+  int rc = oracle_router_gates(h, w_r, dtype, T, D, N, gates, nthreads);
+  int failed = 0;
+  if (rc == OR_OK) {
+#pragma omp parallel
+    {
+      double* g = (double*)malloc((size_t)F * sizeof(double));
+      if (!g) {
+#pragma omp atomic write
+        failed = 1;
+      }
+#pragma omp for schedule(dynamic)
+      for (int64_t t = 0; t < T; ++t) {
+        if (!g) continue;
+        const int64_t v = ids[t];
+        for (int64_t d = 0; d < D; ++d) y[t * D + d] = 0.0;
+        for (int64_t e = 0; e < N; ++e) {
+          for (int64_t f = 0; f < F; ++f) {
+            double u = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+              u += load_elem(emb, dtype, v * D + d) * load_elem(w_up, dtype, (e * F + f) * D + d);
+            g[f] = oracle_gelu(u);
+          }
+          for (int64_t d = 0; d < D; ++d) {
+            double o = 0.0;
+            for (int64_t f = 0; f < F; ++f) o += g[f] * load_elem(w_down, dtype, (e * D + d) * F + f);
+            y[t * D + d] += gates[t * N + e] * o;
+          }
+        }
+      }
+      free(g);
+    }
+  }
+  free(gates);
+  if (rc != OR_OK) return rc;
+  return failed ? OR_ERR_MEM : OR_OK;
+}
+
+/* d GELU / du = Phi(u) + u * phi(u). */
+static double gelu_grad(double u) {
+  const double phi = exp(-0.5 * u * u) / sqrt(2.0 * 3.14159265358979323846);
+  return 0.5 * (1.0 + erf(u / sqrt(2.0))) + u * phi;
+}
+
+/*
+ * Backward of oracle_train_forward for an upstream gradient dy [T][D]
+ * (fp64), by the chain rule written out per token and expert:
+ *   o_e = W_down[e] . G_e,  G_e = GELU(u_e),  u_e = W_up[e] . x,  x = Emb[id];
+ *   dg_e = dy . o_e;  dz_e = g_e (dg_e - sum_e' g_e' dg_e');
+ *   d W_r[e] += dz_e h;  dh += sum_e dz_e W_r[e];
+ *   d o_e = g_e dy;  d W_down[e] += d o_e (x) G_e;  d G_e = W_down[e]^T . d o_e;
+ *   d u_e = d G_e * GELU'(u_e);  d W_up[e] += d u_e (x) x;  d x += W_up[e]^T . d u_e;
+ *   d Emb[id] += d x.
+ * Outputs (fp64, overwritten): d_w_up [N][F][D], d_w_down [N][D][F],
+ * d_w_r [N][D], d_h [T][D], d_emb [V][D].  Serial over tokens (the weight
+ * gradients are sums over the batch).
+ */
+int oracle_train_backward(const int64_t* ids, const void* emb, const void* w_up, const void* w_down,
+                          const void* h, const void* w_r, int dtype, const double* dy, int64_t T,
+                          int64_t V, int64_t D, int64_t F, int64_t N, double* d_w_up, double* d_w_down,
+                          double* d_w_r, double* d_h, double* d_emb) {
+  if (!dtype_ok(dtype) || T < 0 || V <= 0 || D <= 0 || F <= 0 || N <= 0) return OR_ERR_ARG;
+  for (int64_t t = 0; t < T; ++t)
+    if (ids[t] < 0 || ids[t] >= V) return OR_ERR_ID;
+  memset(d_w_up, 0, (size_t)(N * F * D) * sizeof(double));
+  memset(d_w_down, 0, (size_t)(N * D * F) * sizeof(double));
+  memset(d_w_r, 0, (size_t)(N * D) * sizeof(double));
+  memset(d_h, 0, (size_t)(T * D) * sizeof(double));
+  memset(d_emb, 0, (size_t)(V * D) * sizeof(double));
+  double* gates = (double*)malloc((size_t)(T > 0 ? T : 1) * N * sizeof(double));
+  double* u = (double*)malloc((size_t)(N * F) * sizeof(double));
+  double* G = (double*)malloc((size_t)(N * F) * sizeof(double));
+  double* o = (double*)malloc((size_t)(N * D) * sizeof(double));
+  double* dg = (double*)malloc((size_t)N * sizeof(double));
+  double* dG = (double*)malloc((size_t)F * sizeof(double));
+  if (!gates || !u || !G || !o || !dg || !dG) {
+    free(gates); free(u); free(G); free(o); free(dg); free(dG);
+    return OR_ERR_MEM;
+  }
+  int rc = oracle_router_gates(h, w_r, dtype, T, D, N, gates, 1);
+  for (int64_t t = 0; rc == OR_OK && t < T; ++t) {
+    const int64_t v = ids[t];
+    const double* g = gates + t * N;
+    for (int64_t e = 0; e < N; ++e) {
+      for (int64_t f = 0; f < F; ++f) {
+        double s = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+          s += load_elem(emb, dtype, v * D + d) * load_elem(w_up, dtype, (e * F + f) * D + d);
+        u[e * F + f] = s;
+        G[e * F + f] = oracle_gelu(s);
+      }
+      for (int64_t d = 0; d < D; ++d) {
+        double s = 0.0;
+        for (int64_t f = 0; f < F; ++f) s += G[e * F + f] * load_elem(w_down, dtype, (e * D + d) * F + f);
+        o[e * D + d] = s;
+      }
+      double s = 0.0;
+      for (int64_t d = 0; d < D; ++d) s += dy[t * D + d] * o[e * D + d];
+      dg[e] = s;
+    }
+    double gdg = 0.0;
+    for (int64_t e = 0; e < N; ++e) gdg += g[e] * dg[e];
+    for (int64_t e = 0; e < N; ++e) {
+      const double dz = g[e] * (dg[e] - gdg);
+      for (int64_t d = 0; d < D; ++d) {
+        d_w_r[e * D + d] += dz * load_elem(h, dtype, t * D + d);
+        d_h[t * D + d] += dz * load_elem(w_r, dtype, e * D + d);
+      }
+    }
+    for (int64_t e = 0; e < N; ++e) {
+      for (int64_t f = 0; f < F; ++f) dG[f] = 0.0;
+      for (int64_t d = 0; d < D; ++d) {
+        const double dod = g[e] * dy[t * D + d];
+        for (int64_t f = 0; f < F; ++f) {
+          d_w_down[(e * D + d) * F + f] += dod * G[e * F + f];
+          dG[f] += load_elem(w_down, dtype, (e * D + d) * F + f) * dod;
+        }
+      }
+      for (int64_t f = 0; f < F; ++f) {
+        const double du = dG[f] * gelu_grad(u[e * F + f]);
+        for (int64_t d = 0; d < D; ++d) {
+          d_w_up[(e * F + f) * D + d] += du * load_elem(emb, dtype, v * D + d);
+          d_emb[v * D + d] += du * load_elem(w_up, dtype, (e * F + f) * D + d);
+        }
+      }
+    }
+  }
+  free(gates); free(u); free(G); free(o); free(dg); free(dG);
+  return rc;
+}

@@ -658,3 +658,90 @@ def test_quantised_combine_matches_independent_decode(fmt):
         got = oracle.lookup_combine_int8(ids, h, w_r, codes, scales)
     ref = np.einsum("te,ted->td", g, xh[ids])
     assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+# ----------------------------------------------------------------------------
+# Training mode (training section: each routed expert reads the token's
+# shallow embedding, every expert is active, the router reads h)
+# ----------------------------------------------------------------------------
+
+def train_inputs(seed, V=12, D=8, F=10, N=3, T=7):
+    r = rng(seed)
+    f = lambda shape, s: (r.standard_normal(shape) * s).astype(np.float32)
+    return (r.integers(0, V, size=T).astype(np.int64), f((V, D), 1.0), f((N, F, D), 0.4), f((N, D, F), 0.3),
+            f((T, D), 1.0), f((N, D), 0.5))
+
+
+def test_train_forward_matches_numpy_and_the_lookup_path():
+    ids, emb, wu, wd, h, wr = train_inputs(501)
+    y = oracle.train_forward(ids, emb, wu, wd, h, wr)
+    E = emb.astype(np.float64)[ids]
+    g = scipy.special.softmax(h.astype(np.float64) @ wr.astype(np.float64).T, axis=1)
+    ref = np.zeros_like(y)
+    for e in range(wu.shape[0]):
+        u = E @ wu[e].astype(np.float64).T
+        ref += g[:, e:e + 1] * ((0.5 * u * (1 + scipy.special.erf(u / np.sqrt(2)))) @ wd[e].astype(np.float64).T)
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+    # the inference path: the same function through the reparameterised table
+    lut = oracle.build_lut_rows(emb, wu, wd).astype(np.float32)
+    y_lut = oracle.lookup_combine(ids, h, wr, lut)
+    assert np.abs(y - y_lut).max() <= 1e-6 * np.abs(ref).max()  # the table is stored in fp32 here
+
+
+def torch_grads(ids, emb, wu, wd, h, wr, dy):
+    """Reference gradients from torch.autograd in float64 on the CPU."""
+    t = {k: torch.tensor(v.astype(np.float64), requires_grad=True)
+         for k, v in dict(emb=emb, wu=wu, wd=wd, h=h, wr=wr).items()}
+    x = t["emb"][torch.from_numpy(ids)]
+    g = torch.softmax(t["h"] @ t["wr"].T, dim=1)
+    y = 0
+    for e in range(wu.shape[0]):
+        u = x @ t["wu"][e].T
+        y = y + g[:, e:e + 1] * (torch.nn.functional.gelu(u) @ t["wd"][e].T)
+    (y * torch.from_numpy(dy)).sum().backward()
+    return {"d_emb": t["emb"].grad.numpy(), "d_w_up": t["wu"].grad.numpy(), "d_w_down": t["wd"].grad.numpy(),
+            "d_h": t["h"].grad.numpy(), "d_w_r": t["wr"].grad.numpy()}
+
+
+def test_train_backward_matches_torch_autograd():
+    ids, emb, wu, wd, h, wr = train_inputs(502)
+    ids[3] = ids[1]  # a repeated id: its embedding gradient sums over both tokens
+    dy = rng(503).standard_normal((ids.size, emb.shape[1]))
+    got = oracle.train_backward(ids, emb, wu, wd, h, wr, dy)
+    ref = torch_grads(ids, emb, wu, wd, h, wr, dy)
+    for k in ref:
+        assert np.abs(got[k] - ref[k]).max() <= 1e-10 * max(1.0, np.abs(ref[k]).max()), k
+
+
+def test_train_backward_matches_finite_differences():
+    """Central differences of the forward on a few coordinates of every input
+    (a step of 2^-10 applied to fp32 storage, divided by the step actually
+    taken)."""
+    ids, emb, wu, wd, h, wr = train_inputs(504, V=6, D=4, F=5, N=2, T=3)
+    dy = rng(505).standard_normal((ids.size, emb.shape[1]))
+    got = oracle.train_backward(ids, emb, wu, wd, h, wr, dy)
+    step = np.float32(2.0 ** -10)
+    def loss(**kw):
+        a = dict(emb=emb, wu=wu, wd=wd, h=h, wr=wr)
+        a.update(kw)
+        return float((oracle.train_forward(ids, a["emb"], a["wu"], a["wd"], a["h"], a["wr"]) * dy).sum())
+    for name, arr, gkey in (("emb", emb, "d_emb"), ("wu", wu, "d_w_up"), ("wd", wd, "d_w_down"),
+                            ("h", h, "d_h"), ("wr", wr, "d_w_r")):
+        flat = np.random.Generator(np.random.PCG64(506)).choice(arr.size, size=min(6, arr.size), replace=False)
+        if name == "emb":
+            flat = np.array([ids[0] * arr.shape[1] + 1, ids[2] * arr.shape[1]])  # rows the batch uses
+        for i in flat:
+            p, m = arr.copy(), arr.copy()
+            p.flat[i] += step
+            m.flat[i] -= step
+            fd = (loss(**{name: p}) - loss(**{name: m})) / (float(p.flat[i]) - float(m.flat[i]))
+            assert abs(fd - got[gkey].flat[i]) <= 1e-5 * max(1.0, abs(fd)), (name, i, fd, got[gkey].flat[i])
+
+
+def test_train_backward_zero_upstream_and_untouched_rows():
+    ids, emb, wu, wd, h, wr = train_inputs(507)
+    zero = oracle.train_backward(ids, emb, wu, wd, h, wr, np.zeros((ids.size, emb.shape[1])))
+    assert all(np.all(v == 0) for v in zero.values())
+    got = oracle.train_backward(ids, emb, wu, wd, h, wr, np.ones((ids.size, emb.shape[1])))
+    untouched = np.setdiff1d(np.arange(emb.shape[0]), ids)
+    assert np.all(got["d_emb"][untouched] == 0)
