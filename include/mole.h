@@ -220,6 +220,64 @@ int mole_lookup_combine_int8(const int64_t* ids, const void* h, const void* w_r,
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * Training mode of the routed experts (training section: every routed
+ * expert reads the token's shallow embedding Emb[id], all experts are
+ * active with dense softmax gates, the router reads the contextual hidden
+ * state h; the inference table is this forward pass on every vocabulary
+ * row -- here it is evaluated on the batch's distinct rows only):
+ *
+ *   y[t][:] = sum_e softmax(W_r . h[t])[e] * W_down[e] . GELU(W_up[e] . Emb[ids[t]])
+ *
+ * and its gradients for an upstream dy [T][D] (fp32): d_w_up [N][F][D],
+ * d_w_down [N][D][F], d_w_r [N][D], d_h [T][D] and d_x [U][D], the
+ * gradient of the embedding rows Emb[uniq[u]] (a row used by several tokens
+ * receives their sum; scatter-add it into the embedding gradient).
+ *
+ * mole_train_index: host-only.  Deduplicates ids_host[0..T) in first-
+ * occurrence order: uniq_host[0..U) = the distinct ids, remap_host[t] = the
+ * row of ids_host[t] among them, and the tokens of each row, grouped:
+ * tok_host[row_ptr_host[u] .. row_ptr_host[u+1]) in increasing t
+ * (row_ptr_host has U+1 entries; size it T+1).  *n_unique = U.
+ * MOLE_ERR_ID for an id outside [0, V).  Copy uniq, remap, row_ptr and tok
+ * to the device for the two calls below.
+ *
+ * mole_train_workspace_size: the forward workspace (kept by the caller from
+ * the forward to the backward call: the gathered rows, hidden activations
+ * and the batch's table rows) and the backward scratch, for T tokens and U
+ * distinct ids.
+ *
+ * mole_train_forward / mole_train_backward: bf16 only (MOLE_ERR_UNSUPPORTED
+ * for MOLE_F32), D % 8 == 0 and F % 8 == 0 (MOLE_ERR_DIM), D, N*F and T at
+ * most 2^20 and 1 <= N <= 64 (MOLE_ERR_UNSUPPORTED).  bf16 products with
+ * fp32 accumulation; as in mole_build_lut the hidden activation is rounded
+ * to bf16, and the backward pass rounds the row gradients, the hidden
+ * gradients and the recomputed pre-activations to bf16 for the matrix
+ * cores; all sums and every output are fp32.  Weight gradients are
+ * overwritten, not accumulated.  Deterministic (no atomics).
+ *   uniq [U] int64, remap [T] int64, row_ptr [U+1] int64, tok [T] int64 (device)
+ *   emb [V][D], w_up [N][F][D], w_down [N][D][F], h [T][D], w_r [N][D] (bf16)
+ *   y [T][D] fp32 (written)
+ * ------------------------------------------------------------------------ */
+int mole_train_index(const int64_t* ids_host, int64_t T, int64_t V, int64_t* uniq_host,
+                     int64_t* remap_host, int64_t* row_ptr_host, int64_t* tok_host,
+                     int64_t* n_unique);
+
+int mole_train_workspace_size(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N,
+                              size_t* fwd_bytes, size_t* bwd_bytes);
+
+int mole_train_forward(const int64_t* uniq, const int64_t* remap, const void* emb,
+                       const void* w_up, const void* w_down, const void* h, const void* w_r,
+                       float* y, int64_t T, int64_t U, int64_t V, int64_t D, int64_t F, int64_t N,
+                       int dtype, void* fwd_ws, size_t fwd_bytes, void* stream);
+
+int mole_train_backward(const int64_t* remap, const int64_t* row_ptr, const int64_t* tok,
+                        const void* w_up, const void* w_down, const void* h, const void* w_r,
+                        const float* dy, const void* fwd_ws, size_t fwd_bytes, void* bwd_ws,
+                        size_t bwd_bytes, float* d_w_up, float* d_w_down, float* d_w_r,
+                        float* d_h, float* d_x, int64_t T, int64_t U, int64_t V, int64_t D,
+                        int64_t F, int64_t N, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host-resident NF3 table (inference section: after reparameterisation the
  * table lives in lower-tier storage such as CPU memory, each token's
  * entries are looked up there and only the retrieved vectors are loaded

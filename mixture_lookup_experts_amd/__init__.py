@@ -38,6 +38,10 @@ from ._native import (  # noqa: F401
     mole_nf3_levels,
     mole_pack_nf3,
     mole_status_string,
+    mole_train_backward,
+    mole_train_forward,
+    mole_train_index,
+    mole_train_workspace_size,
 )
 
 __all__ = [
@@ -47,4 +51,5 @@ __all__ = [
     "mole_nf3_host_staging_size", "mole_nf3_host_stack_staging_size", "mole_prefetch_nf3_host_stack",
     "mole_nf3_levels", "mole_status_string", "mole_layer_forward", "mole_layer_workspace_size",
     "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4", "mole_pack_int8", "mole_lookup_combine_int8",
+    "mole_train_index", "mole_train_workspace_size", "mole_train_forward", "mole_train_backward",
 ]

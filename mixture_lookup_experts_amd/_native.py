@@ -77,6 +77,11 @@ def library():
             "mole_lookup_combine_nf4": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_pack_int8": (I, [P, P, P, I64, I64, I64, I, P]),
             "mole_lookup_combine_int8": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
+            "mole_train_index": (I, [P, I64, I64, P, P, P, P, P]),
+            "mole_train_workspace_size": (I, [I64, I64, I64, I64, I64, P, P]),
+            "mole_train_forward": (I, [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I, P, SZ, P]),
+            "mole_train_backward": (I, [P, P, P, P, P, P, P, P, P, SZ, P, SZ, P, P, P, P, P,
+                                        I64, I64, I64, I64, I64, I64, I, P]),
             "mole_layer_forward": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]),
         }
         for name, (res, args) in sig.items():
@@ -393,3 +398,63 @@ def mole_lookup_combine_int8(ids, h, w_r, codes, scales, y, stream=None) -> None
     _check("mole_lookup_combine_int8", library().mole_lookup_combine_int8(
         _ptr(ids), _ptr(h), _ptr(w_r), _ptr(codes), _ptr(scales), _ptr(y), T, V, D, N,
         _dtype(h), _stream(stream)))
+
+
+def mole_train_index(ids_host, V: int):
+    """Host-side batch index: (uniq [U], remap [T], row_ptr [U+1], tok [T]) as
+    int64 CPU tensors (distinct ids in first-occurrence order, each token's
+    row, and the tokens of each row grouped in token order)."""
+    ids_host = ids_host.contiguous()
+    _need(ids_host.dtype == torch.int64 and not ids_host.is_cuda, "ids_host: int64 CPU tensor")
+    T = ids_host.numel()
+    uniq = torch.empty(max(T, 1), dtype=torch.int64)
+    remap = torch.empty(max(T, 1), dtype=torch.int64)
+    row_ptr = torch.empty(T + 1, dtype=torch.int64)
+    tok = torch.empty(max(T, 1), dtype=torch.int64)
+    U = ctypes.c_int64(0)
+    _check("mole_train_index", library().mole_train_index(
+        _ptr(ids_host), T, V, _ptr(uniq), _ptr(remap), _ptr(row_ptr), _ptr(tok), ctypes.addressof(U)))
+    u = int(U.value)
+    return uniq[:u].clone(), remap[:T].clone(), row_ptr[:u + 1].clone(), tok[:T].clone()
+
+
+def mole_train_workspace_size(T: int, U: int, D: int, F: int, N: int):
+    """(forward workspace bytes, backward scratch bytes) for training mode."""
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mole_train_workspace_size", library().mole_train_workspace_size(
+        T, U, D, F, N, ctypes.addressof(f), ctypes.addressof(b)))
+    return int(f.value), int(b.value)
+
+
+def mole_train_forward(uniq, remap, emb, w_up, w_down, h, w_r, y, fwd_ws, stream=None) -> None:
+    """Training-mode forward: y[t] = sum_e softmax(w_r . h[t])[e] FFN_e(emb[ids[t]]), with the
+    batch given by (uniq, remap) on the device; fwd_ws keeps what the backward pass needs."""
+    V, D = emb.shape
+    N, F, _ = w_up.shape
+    T, U = remap.numel(), uniq.numel()
+    _need(tuple(w_down.shape) == (N, D, F) and tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D)
+          and tuple(y.shape) == (T, D), "emb [V,D], w_up [N,F,D], w_down [N,D,F], h [T,D], w_r [N,D], y [T,D]")
+    _need(y.dtype == torch.float32 and uniq.dtype == remap.dtype == torch.int64, "y float32, uniq/remap int64")
+    for t in (uniq, remap, emb, w_up, w_down, h, w_r, y, fwd_ws):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_train_forward", library().mole_train_forward(
+        _ptr(uniq), _ptr(remap), _ptr(emb), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(w_r), _ptr(y), T, U, V, D, F,
+        N, _dtype(emb), _ptr(fwd_ws), fwd_ws.numel() * fwd_ws.element_size(), _stream(stream)))
+
+
+def mole_train_backward(remap, row_ptr, tok, U: int, V: int, w_up, w_down, h, w_r, dy, fwd_ws, bwd_ws,
+                        d_w_up, d_w_down, d_w_r, d_h, d_x, stream=None) -> None:
+    """Training-mode backward for the upstream gradient dy [T,D]; outputs are fp32 tensors
+    d_w_up [N,F,D], d_w_down [N,D,F], d_w_r [N,D], d_h [T,D], d_x [U,D] (embedding rows)."""
+    N, F, D = w_up.shape
+    T = remap.numel()
+    _need(tuple(d_w_up.shape) == (N, F, D) and tuple(d_w_down.shape) == (N, D, F) and tuple(d_w_r.shape) == (N, D)
+          and tuple(d_h.shape) == (T, D) and tuple(d_x.shape) == (U, D) and tuple(dy.shape) == (T, D),
+          "gradient shapes")
+    for t in (remap, row_ptr, tok, w_up, w_down, h, w_r, dy, fwd_ws, bwd_ws, d_w_up, d_w_down, d_w_r, d_h, d_x):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_train_backward", library().mole_train_backward(
+        _ptr(remap), _ptr(row_ptr), _ptr(tok), _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(w_r), _ptr(dy),
+        _ptr(fwd_ws), fwd_ws.numel() * fwd_ws.element_size(), _ptr(bwd_ws), bwd_ws.numel() * bwd_ws.element_size(),
+        _ptr(d_w_up), _ptr(d_w_down), _ptr(d_w_r), _ptr(d_h), _ptr(d_x), T, U, V, D, F, N, _dtype(w_up),
+        _stream(stream)))

@@ -218,7 +218,7 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 5; }
+int mole_abi_version(void) { return 6; }
 
 int mole_nf3_levels(float* levels_host) {
   if (!levels_host) return MOLE_ERR_NULL;
@@ -360,6 +360,94 @@ int mole_lookup_combine_int8(const int64_t* ids, const void* h, const void* w_r,
                              const float* scales, float* y, int64_t T, int64_t V, int64_t D, int64_t N,
                              int dtype_h, void* stream) {
   return combine_q(mole::kFmtI8, ids, h, w_r, codes, scales, y, T, V, D, N, dtype_h, stream);
+}
+
+int mole_train_index(const int64_t* ids_host, int64_t T, int64_t V, int64_t* uniq_host, int64_t* remap_host,
+                     int64_t* row_ptr_host, int64_t* tok_host, int64_t* n_unique) {
+  if (T < 0 || V <= 0) return MOLE_ERR_DIM;
+  if (T > 0 && (!ids_host || !uniq_host || !remap_host || !row_ptr_host || !tok_host)) return MOLE_ERR_NULL;
+  if (!n_unique) return MOLE_ERR_NULL;
+  std::vector<int64_t> uniq;
+  int rc = dedupe(ids_host, T, V, uniq, remap_host);
+  if (rc != MOLE_OK) return rc;
+  const int64_t U = (int64_t)uniq.size();
+  std::copy(uniq.begin(), uniq.end(), uniq_host);
+  // Tokens grouped by row, in token order within a row (a counting sort).
+  if (row_ptr_host) {
+    std::fill(row_ptr_host, row_ptr_host + U + 1, (int64_t)0);
+    for (int64_t t = 0; t < T; ++t) row_ptr_host[remap_host[t] + 1] += 1;
+    for (int64_t u = 0; u < U; ++u) row_ptr_host[u + 1] += row_ptr_host[u];
+    std::vector<int64_t> next(row_ptr_host, row_ptr_host + U);
+    for (int64_t t = 0; t < T; ++t) tok_host[next[remap_host[t]]++] = t;
+  }
+  *n_unique = U;
+  return MOLE_OK;
+}
+
+namespace {
+constexpr int64_t kMaxTrainDim = (int64_t)1 << 20;  // 256-row fp32 panels of N*F, D stay under 2^31 bytes
+
+int check_train(int64_t T, int64_t U, int64_t V, int64_t D, int64_t F, int64_t N, int dtype) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  if (T < 0 || U < 0 || V <= 0 || D <= 0 || F <= 0 || N <= 0) return MOLE_ERR_DIM;
+  if (U > T || U > V || (T > 0 && U == 0)) return MOLE_ERR_DIM;
+  if (D % 8 != 0 || F % 8 != 0) return MOLE_ERR_DIM;
+  if (N > kMaxExperts) return MOLE_ERR_UNSUPPORTED;
+  if (dtype != MOLE_BF16) return MOLE_ERR_UNSUPPORTED;
+  if (D > kMaxTrainDim || N * F > kMaxTrainDim || T > kMaxTrainDim) return MOLE_ERR_UNSUPPORTED;
+  return MOLE_OK;
+}
+}  // namespace
+
+int mole_train_workspace_size(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N, size_t* fwd_bytes,
+                              size_t* bwd_bytes) {
+  if (T < 0 || U < 0 || U > T || D <= 0 || F <= 0 || N <= 0 || N * F > kMaxTrainDim || D > kMaxTrainDim ||
+      T > kMaxTrainDim)
+    return MOLE_ERR_DIM;
+  const mole::TrainPlan p = mole::train_plan(T, U, D, F, N);
+  if (fwd_bytes) *fwd_bytes = T == 0 ? 0 : p.fwd_total;
+  if (bwd_bytes) *bwd_bytes = T == 0 ? 0 : p.bwd_total;
+  return MOLE_OK;
+}
+
+int mole_train_forward(const int64_t* uniq, const int64_t* remap, const void* emb, const void* w_up,
+                       const void* w_down, const void* h, const void* w_r, float* y, int64_t T, int64_t U,
+                       int64_t V, int64_t D, int64_t F, int64_t N, int dtype, void* fwd_ws, size_t fwd_bytes,
+                       void* stream) {
+  int rc = check_train(T, U, V, D, F, N, dtype);
+  if (rc != MOLE_OK) return rc;
+  if (T == 0) return MOLE_OK;
+  if (!uniq || !remap || !emb || !w_up || !w_down || !h || !w_r || !y || !fwd_ws) return MOLE_ERR_NULL;
+  if (!aligned8(uniq) || !aligned8(remap) || !aligned16(emb) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(h) || !aligned16(w_r) || !aligned16(y) || !aligned16(fwd_ws))
+    return MOLE_ERR_ALIGN;
+  if (fwd_bytes < mole::train_plan(T, U, D, F, N).fwd_total) return MOLE_ERR_WORKSPACE;
+  return hip_status(mole::launch_train_forward(uniq, remap, (const uint16_t*)emb, (const uint16_t*)w_up,
+                                               (const uint16_t*)w_down, (const uint16_t*)h, (const uint16_t*)w_r, y,
+                                               fwd_ws, T, U, D, F, N, as_stream(stream)));
+}
+
+int mole_train_backward(const int64_t* remap, const int64_t* row_ptr, const int64_t* tok, const void* w_up,
+                        const void* w_down, const void* h, const void* w_r, const float* dy, const void* fwd_ws,
+                        size_t fwd_bytes, void* bwd_ws, size_t bwd_bytes, float* d_w_up, float* d_w_down,
+                        float* d_w_r, float* d_h, float* d_x, int64_t T, int64_t U, int64_t V, int64_t D, int64_t F,
+                        int64_t N, int dtype, void* stream) {
+  int rc = check_train(T, U, V, D, F, N, dtype);
+  if (rc != MOLE_OK) return rc;
+  if (T == 0) return MOLE_OK;
+  if (!remap || !row_ptr || !tok || !w_up || !w_down || !h || !w_r || !dy || !fwd_ws || !bwd_ws || !d_w_up ||
+      !d_w_down || !d_w_r || !d_h || !d_x)
+    return MOLE_ERR_NULL;
+  if (!aligned8(remap) || !aligned8(row_ptr) || !aligned8(tok) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(h) || !aligned16(w_r) || !aligned16(dy) || !aligned16(fwd_ws) || !aligned16(bwd_ws) ||
+      !aligned16(d_w_up) || !aligned16(d_w_down) || !aligned16(d_w_r) || !aligned16(d_h) || !aligned16(d_x))
+    return MOLE_ERR_ALIGN;
+  const mole::TrainPlan p = mole::train_plan(T, U, D, F, N);
+  if (fwd_bytes < p.fwd_total || bwd_bytes < p.bwd_total) return MOLE_ERR_WORKSPACE;
+  return hip_status(mole::launch_train_backward(nullptr, remap, row_ptr, tok, nullptr, (const uint16_t*)w_up,
+                                                (const uint16_t*)w_down, (const uint16_t*)h, (const uint16_t*)w_r,
+                                                dy, fwd_ws, bwd_ws, d_w_up, d_w_down, d_w_r, d_h, d_x, T, U, D, F, N,
+                                                as_stream(stream)));
 }
 
 int mole_layer_workspace_size(int64_t T, int64_t D, int64_t F, size_t* bytes) {

@@ -408,6 +408,12 @@ hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t*
   return launch_gemm<kBM, kBN, kEpiGelu>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
 }
 
+// bf16 C = A . B^T (no epilogue function), one 256x256 tile per workgroup.
+hipError_t launch_gemm_store_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
+                                  int64_t ldc, int M, int N, int K, hipStream_t s) {
+  return launch_gemm<kBM, kBN, kEpiStore>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
+}
+
 // fp32 C = A . B^T per batch index z (split-K partial sums of the MoLE
 // block's down-projection: z selects a K range through sAz and sBz).
 // C rows of ldc floats; needs 256 * ldc * 4 < 2^31.

@@ -52,9 +52,32 @@ constexpr int64_t kBuildF32MaxLds = 16384;  // D + F floats staged in LDS by the
 hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
                                  int64_t ldc, int M, int N, int K, hipStream_t s);
 
+hipError_t launch_gemm_store_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
+                                  int64_t ldc, int M, int N, int K, hipStream_t s);
 hipError_t launch_gemm_f32_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                 int64_t sBz, float* C, int64_t ldc, int64_t sCz, int M, int N, int K, int batch,
                                 hipStream_t s);
+
+// train.hip: training-mode forward and backward
+struct TrainPlan {
+  int64_t up;            // U rounded up to a multiple of 8 (K of the transposed products)
+  int dx_splits;         // K splits of the embedding-row gradient product
+  // forward state (kept by the caller between the two calls)
+  size_t x_off, g_off, o_off, fwd_total;
+  // backward scratch (a second workspace)
+  size_t gate_off, dz_off, do_off, dot_off, u_off, dg_off, du_off, dut_off, gt_off, xt_off, wdt_off, wut_off,
+      pdx_off, pwr_off, bwd_total;
+  int wr_chunks;         // token chunks of the router-weight gradient
+};
+TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N);
+hipError_t launch_train_forward(const int64_t* uniq, const int64_t* remap, const uint16_t* emb, const uint16_t* w_up,
+                                const uint16_t* w_down, const uint16_t* h, const uint16_t* w_r, float* y, void* fwd,
+                                int64_t T, int64_t U, int64_t D, int64_t F, int64_t N, hipStream_t s);
+hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, const int64_t* row_ptr, const int64_t* tok,
+                                 const uint16_t* emb, const uint16_t* w_up, const uint16_t* w_down, const uint16_t* h,
+                                 const uint16_t* w_r, const float* dy, const void* fwd, void* bwd, float* d_w_up,
+                                 float* d_w_down, float* d_w_r, float* d_h, float* d_x, int64_t T, int64_t U,
+                                 int64_t D, int64_t F, int64_t N, hipStream_t s);
 
 // layer.hip: the MoLE block at inference (shared expert + routed lookup + residual)
 struct LayerPlan {

@@ -36,14 +36,15 @@ def test_header_declares_the_hot_path():
                "mole_last_hip_error",
                "mole_nf3_levels", "mole_abi_version", "mole_layer_forward",
                "mole_layer_workspace_size", "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4",
-               "mole_pack_int8", "mole_lookup_combine_int8"):
+               "mole_pack_int8", "mole_lookup_combine_int8", "mole_train_index", "mole_train_workspace_size",
+               "mole_train_forward", "mole_train_backward"):
         assert fn in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 5
+    assert lib.mole_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -272,3 +273,45 @@ def test_quant_combine_argument_errors(lib, fn):
     assert call(codes=None) == NULL
     assert call(y=P(a + 4)) == ALIGN
     assert call(T=0, ids=None, codes=None, y=None) == OK
+
+
+def test_train_index_groups_tokens_by_row():
+    import torch
+    ids = torch.tensor([5, 2, 5, 9, 2, 5, 0], dtype=torch.int64)
+    uniq, remap, row_ptr, tok = mole.mole_train_index(ids, V=10)
+    assert uniq.tolist() == [5, 2, 9, 0]                   # first-occurrence order
+    assert remap.tolist() == [0, 1, 0, 2, 1, 0, 3]
+    assert row_ptr.tolist() == [0, 3, 5, 6, 7]
+    assert tok.tolist() == [0, 2, 5, 1, 4, 3, 6]            # each row's tokens, in token order
+    with pytest.raises(mole.MoleError):
+        mole.mole_train_index(torch.tensor([1, 10], dtype=torch.int64), V=10)
+    e_uniq, e_remap, e_ptr, e_tok = mole.mole_train_index(torch.empty(0, dtype=torch.int64), V=10)
+    assert e_uniq.numel() == 0 and e_ptr.tolist() == [0]
+
+
+def test_train_workspace_size_and_errors(lib):
+    f, b = mole.mole_train_workspace_size(256, 150, 768, 3072, 4)
+    assert f >= 150 * 768 * 2 + 150 * 4 * 3072 * 2 + 150 * 4 * 768 * 2   # X, G, table rows
+    assert b > f
+    assert mole.mole_train_workspace_size(0, 0, 768, 3072, 4) == (0, 0)
+    a = 0x1000
+    fwd = lib.mole_train_forward
+
+    def call(T=16, U=8, V=50, D=64, F=128, N=4, dt=1, uniq=P(a), ws=P(a), wsb=1 << 40):
+        return fwd(uniq, P(a), P(a), P(a), P(a), P(a), P(a), P(a), T, U, V, D, F, N, dt, ws, wsb, None)
+    assert call(dt=0) == UNSUP
+    assert call(dt=4) == DTYPE
+    assert call(U=17) == DIM              # more rows than tokens
+    assert call(U=0) == DIM
+    assert call(D=60) == DIM
+    assert call(N=65) == UNSUP
+    assert call(F=1 << 19, N=4) == UNSUP  # N*F above 2^20
+    assert call(uniq=None) == NULL
+    assert call(ws=P(a + 8)) == ALIGN
+    assert call(wsb=16) == WS
+    assert call(T=0, U=0, uniq=None, ws=None, wsb=0) == OK
+    bwd = lib.mole_train_backward
+    assert bwd(P(a), P(a), P(a), P(a), P(a), P(a), P(a), P(a), P(a), 1 << 40, P(a), 16, P(a), P(a), P(a), P(a),
+               P(a), 16, 8, 50, 64, 128, 4, 1, None) == WS
+    assert bwd(P(a), P(a), None, P(a), P(a), P(a), P(a), P(a), P(a), 1 << 40, P(a), 1 << 40, P(a), P(a), P(a),
+               P(a), P(a), 16, 8, 50, 64, 128, 4, 1, None) == NULL

@@ -727,3 +727,85 @@ def test_pack_q_full_size_sampled_rows(fmt):
     other = np.setdiff1d(np.arange(w.V), sample)[:300]
     assert np.all(scales[other] == 0)
     assert np.all(codes[other] == (0x77 if fmt == "nf4" else 0))
+
+
+# ----------------------------------------------------------------------------
+# Training mode: forward (every expert on the token's embedding, dense gates)
+# and backward (training section of the MoLE article)
+# ----------------------------------------------------------------------------
+
+TRAIN_TOL = 1e-2  # rel-L2, the bf16-product bar of the build
+
+
+def train_case(seed, V, D, F, N, T, zipf=False):
+    r = rng(seed)
+    f = lambda shape, s: synth.f32_to_bf16_bits(r.standard_normal(shape, dtype=np.float32) * np.float32(s))
+    emb = f((V, D), 1.0)
+    w_up = f((N, F, D), 1.0 / np.sqrt(D))     # unit-scale hidden units: GELU is nonlinear
+    w_down = f((N, D, F), 1.0 / np.sqrt(F))
+    w_r = f((N, D), 0.3 / np.sqrt(D))
+    h = f((T, D), 1.0)
+    if zipf:
+        ids = synth.zipf_ids(r, V, T, r.permutation(V))
+    else:
+        ids = r.integers(0, V, size=T).astype(np.int64)
+    dy = r.standard_normal((T, D)).astype(np.float32)
+    return ids, emb, w_up, w_down, h, w_r, dy
+
+
+def run_train(ids, emb, w_up, w_down, h, w_r, dy):
+    V, D = emb.shape
+    N, F, _ = w_up.shape
+    T = ids.size
+    uniq, remap, row_ptr, tok = mole.mole_train_index(torch.from_numpy(ids), V)
+    U = uniq.numel()
+    fb, bb = mole.mole_train_workspace_size(T, U, D, F, N)
+    fws = torch.empty(fb, dtype=torch.uint8, device="cuda")
+    bws = torch.empty(bb, dtype=torch.uint8, device="cuda")
+    d_uniq, d_remap, d_ptr, d_tok = (x.cuda() for x in (uniq, remap, row_ptr, tok))
+    t_w_up, t_w_down, t_h, t_w_r = dev(w_up), dev(w_down), dev(h), dev(w_r)
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    mole.mole_train_forward(d_uniq, d_remap, dev(emb), t_w_up, t_w_down, t_h, t_w_r, y, fws)
+    out = {k: torch.full(s, float("nan"), dtype=torch.float32, device="cuda")
+           for k, s in (("d_w_up", (N, F, D)), ("d_w_down", (N, D, F)), ("d_w_r", (N, D)), ("d_h", (T, D)),
+                        ("d_x", (U, D)))}
+    mole.mole_train_backward(d_remap, d_ptr, d_tok, U, V, t_w_up, t_w_down, t_h, t_w_r, dev(dy), fws, bws,
+                             out["d_w_up"], out["d_w_down"], out["d_w_r"], out["d_h"], out["d_x"])
+    torch.cuda.synchronize()
+    return host(y), {k: host(v) for k, v in out.items()}, uniq.numpy()
+
+
+# (V, N, D, F, T, zipf): ragged D/F/T, repeated ids (several tokens per row),
+# many experts, and a 160M-class width.
+TRAIN_CASES = [(300, 4, 128, 256, 100, False), (50, 3, 136, 200, 37, True), (400, 16, 256, 512, 64, True),
+               (40, 64, 64, 64, 20, False), (2000, 4, 768, 3072, 32, True)]
+
+
+@pytest.mark.parametrize("V,N,D,F,T,zipf", TRAIN_CASES)
+def test_train_forward_and_backward_match_oracle(V, N, D, F, T, zipf):
+    ids, emb, w_up, w_down, h, w_r, dy = train_case(V + N + D + F + T, V, D, F, N, T, zipf)
+    y, grads, uniq = run_train(ids, emb, w_up, w_down, h, w_r, dy)
+    y_ref = oracle.train_forward(ids, emb, w_up, w_down, h, w_r)
+    assert rel_l2(y, y_ref) <= TRAIN_TOL
+    ref = oracle.train_backward(ids, emb, w_up, w_down, h, w_r, dy.astype(np.float64))
+    for k in ("d_w_up", "d_w_down", "d_w_r", "d_h"):
+        assert np.all(np.isfinite(grads[k])), k
+        assert rel_l2(grads[k], ref[k]) <= TRAIN_TOL, (k, rel_l2(grads[k], ref[k]))
+    assert rel_l2(grads["d_x"], ref["d_emb"][uniq]) <= TRAIN_TOL
+
+
+def test_train_matches_the_lookup_path_on_the_built_table():
+    """The training forward equals the lookup-combine over the table that
+    mole_build_lut makes from the same weights (both round the hidden
+    activation and the table to bf16 the same way), up to fp32 summation order."""
+    V, N, D, F, T = 500, 4, 256, 512, 90
+    ids, emb, w_up, w_down, h, w_r, _ = train_case(77, V, D, F, N, T, zipf=True)
+    y, _, _ = run_train(ids, emb, w_up, w_down, h, w_r, np.zeros((T, D), np.float32))
+    lut = torch.empty((V, N, D), dtype=torch.bfloat16, device="cuda")
+    _, rec = mole.mole_build_lut_workspace_size(V, D, F, N)
+    mole.mole_build_lut(dev(emb), dev(w_up), dev(w_down), lut, workspace=torch.empty(rec, dtype=torch.uint8,
+                                                                                     device="cuda"))
+    y2 = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    mole.mole_lookup_combine(dev(ids), dev(h), dev(w_r), lut, y2)
+    torch.cuda.synchronize()
+    assert combine_rel_err(y, host(y2)) <= COMBINE_TOL
