@@ -51,10 +51,11 @@ def parse():
                         "so gathered bytes = unique bytes)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget for the CPU-oracle baseline (0 disables it)")
-    p.add_argument("--probes", default="scale,decode,host,layer",
+    p.add_argument("--probes", default="scale,decode,host,layer,train",
                    help="comma list of the extra measurements to run: scale (combine on the 410M-class "
                         "table), decode (1B-class 16-layer stack), host (host-resident NF3 stack), "
-                        "layer (the full MoLE block: shared FFN + lookup + residual); not in the default "
+                        "layer (the full MoLE block: shared FFN + lookup + residual), train (training-mode "
+                        "forward and backward of the routed experts); not in the default "
                         "list: vendor_gemm (the vendor GEMM library, via torch.matmul, on the build's GEMM "
                         "shapes and two square ones, as a practical MFMA ceiling)")
     p.add_argument("--no-scale-probe", action="store_true",
@@ -277,6 +278,8 @@ def main():
         result["host_stack_nf3"] = host_stack_probe(torch, mole, synth, dev, stream)
     if "layer" in probes:
         result["layer_block"] = layer_probe(torch, mole, synth, dev, stream)
+    if "train" in probes:
+        result["train"] = train_probe(torch, mole, synth, dev, stream)
     if "vendor_gemm" in probes:
         result["vendor_gemm"] = vendor_gemm_probe(torch, dev, stream)
 
@@ -424,6 +427,66 @@ def layer_probe(torch, mole, synth, dev, stream):
         torch.cuda.empty_cache()
     torch.cuda.synchronize()
     ctx.__exit__(None, None, None)
+    return out
+
+
+def train_probe(torch, mole, synth, dev, stream):
+    """Training mode of the routed experts: forward (every expert on the
+    batch's distinct embedding rows, dense gates) and backward (router,
+    hidden-state, embedding-row and expert-weight gradients), event-timed on
+    `stream` for the 160M-class layer at T = 256, the 410M-class layer at
+    T = 1024 and 4096 and the 1B-class layer at T = 1024 (Zipf ids, weights
+    N(0, 0.02)).  Roofline: the MFMA peak on the algorithmic flops, 4 U N D F
+    forward and 8 U N D F backward (U = distinct ids; the backward's recompute
+    of the hidden pre-activations is not counted)."""
+    out = {}
+    with torch.cuda.stream(stream):
+        for name, T in (("160m", 256), ("410m", 1024), ("410m", 4096), ("1b", 1024)):
+            w = synth.WORKLOADS[name]
+            V, D, N, F = w.V, w.D, w.N, w.F
+            g = torch.Generator(device=dev)
+            g.manual_seed(synth.seed(w, 90))
+            bf = lambda *shape: (torch.randn(shape, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            emb, w_up, w_down, w_r = bf(V, D), bf(N, F, D), bf(N, D, F), bf(N, D)
+            h = torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16)
+            dy = torch.randn((T, D), generator=g, device=dev)
+            ids = torch.from_numpy(synth.make_ids(w, T))
+            uniq, remap, row_ptr, tok = mole.mole_train_index(ids, V)
+            U = uniq.numel()
+            uniq, remap, row_ptr, tok = (x.to(dev) for x in (uniq, remap, row_ptr, tok))
+            fb, bb = mole.mole_train_workspace_size(T, U, D, F, N)
+            fws = torch.empty(fb, dtype=torch.uint8, device=dev)
+            bws = torch.empty(bb, dtype=torch.uint8, device=dev)
+            y = torch.empty((T, D), dtype=torch.float32, device=dev)
+            grads = [torch.empty(s, dtype=torch.float32, device=dev)
+                     for s in ((N, F, D), (N, D, F), (N, D), (T, D), (U, D))]
+
+            def fwd():
+                mole.mole_train_forward(uniq, remap, emb, w_up, w_down, h, w_r, y, fws, stream=stream)
+
+            def bwd():
+                mole.mole_train_backward(remap, row_ptr, tok, U, V, w_up, w_down, h, w_r, dy, fws, bws, *grads,
+                                         stream=stream)
+
+            res = {"tokens": T, "distinct_ids": U, "config": "V=%d D=%d N=%d F=%d" % (V, D, N, F)}
+            for lab, fn, fl in (("forward", fwd, 4.0 * U * N * D * F), ("backward", bwd, 8.0 * U * N * D * F)):
+                fwd()
+                for _ in range(2):
+                    fn()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 10
+                e0.record(stream)
+                for _ in range(reps):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                res[lab] = {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+                            "mfma_frac": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+            res["tokens_per_s_fwd_bwd"] = T / ((res["forward"]["ms"] + res["backward"]["ms"]) * 1e-3)
+            out["%s_T%d" % (name, T)] = res
+            del emb, w_up, w_down, w_r, h, dy, fws, bws, y, grads
+            torch.cuda.empty_cache()
     return out
 
 

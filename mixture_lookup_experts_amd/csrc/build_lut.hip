@@ -54,8 +54,12 @@ __device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + e
 // measured faster once output rows are >= 16 KB apart (the LUT of the larger
 // configurations), slower for narrow rows (two extra barriers).
 // F32: the fp32 accumulators themselves, 16 bytes per lane (split-K partial
-// sums of the MoLE block's down-projection).
-enum { kEpiStore = 0, kEpiGelu = 1, kEpiStoreStaged = 2, kEpiF32 = 3 };
+// sums of the MoLE block's down-projection, gradients).  GeluGrad: bf16 of
+// acc * GELU'(u) with u read from `aux` at the same position (the backward
+// pass of the experts' hidden activation).
+// F32Staged: the fp32 tile goes through LDS in four passes of 64 rows, and
+// every store writes a quarter of a 1 KB row segment (rows far apart).
+enum { kEpiStore = 0, kEpiGelu = 1, kEpiStoreStaged = 2, kEpiF32 = 3, kEpiGeluGrad = 4, kEpiF32Staged = 5 };
 constexpr int64_t kStagedMinRowBytes = 16384;
 
 constexpr int kBK = 64;     // K slice per LDS stage (64 bf16 = 128 bytes per row)
@@ -71,6 +75,7 @@ struct GemmArgs {
   int M, N, K;
   int tiles_m, tiles_n, batch;
   int xcd_order;  // 1: XCD-banded tile order, 0: row-major tile order
+  const uint16_t* aux;  // GELU-gradient epilogue: bf16 pre-activations, laid out like C
 };
 
 // Map the hardware workgroup id to an output tile.
@@ -259,13 +264,25 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   const int rows_c = M - m0 < BM ? M - m0 : BM;
   const __amdgpu_buffer_rsrc_t rc_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.C + z * p.sCz + (int64_t)m0 * p.ldc), (short)0, (int)(rows_c * p.ldc * 2), kRsrcWord3);
-  // (GELU,) round to bf16, pack 4 consecutive columns into 8 bytes.
+  // (GELU or its gradient,) round to bf16, pack 4 consecutive columns into 8 bytes.
   auto packed = [&](int i, int j, int g) {
     float v[4];
+    if constexpr (EPI == kEpiGeluGrad) {
+      // u at the same (row, column) as this accumulator group, 8 bytes
+      const int mr = wm * WM + i * 32 + (lane & 31);
+      const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+      uint2 uw = make_uint2(0u, 0u);
+      if (mr < rows_c && n < N)
+        uw = *reinterpret_cast<const uint2*>(p.aux + z * p.sCz + (int64_t)(m0 + mr) * p.ldc + n);
+      const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[q] = acc[i][j][4 * g + q];
-      if constexpr (EPI == kEpiGelu) v[q] = gelu_poly(v[q]);
+      for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] * gelu_grad_poly(uv[q]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = acc[i][j][4 * g + q];
+        if constexpr (EPI == kEpiGelu) v[q] = gelu_poly(v[q]);
+      }
     }
     const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v[0]) |
                         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[1]) << 16);
@@ -273,7 +290,46 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
                         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[3]) << 16);
     return make_uint2(lo, hi);
   };
-  if constexpr (EPI == kEpiF32) {
+  if constexpr (EPI == kEpiF32Staged) {
+    static_assert(BM == 256 && BN == 256, "four 64-row passes of a 256-column tile");
+    float* cf = reinterpret_cast<float*>(p.C) + z * p.sCz + (int64_t)m0 * p.ldc;
+    const __amdgpu_buffer_rsrc_t rf_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)cf, (short)0, (int)(rows_c * p.ldc * 4), kRsrcWord3);
+    constexpr int kPitch = BN + 4;  // floats per staged row (16-byte pad: conflict-free float4 writes)
+    float* cs = reinterpret_cast<float*>(lds);
+    __syncthreads();  // every wave is done with the operand ring
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      // rows [64 pass, 64 pass + 64) belong to the waves with wm = pass / 2, MFMA rows i = 2 (pass % 2) + 0, 1
+      if (wm == pass / 2) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * (pass % 2) + ii;
+          const int lr = ii * 32 + (lane & 31);  // row within the pass
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int nc = wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+              *reinterpret_cast<float4*>(cs + lr * kPitch + nc) =
+                  make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            }
+        }
+      }
+      __syncthreads();
+      const int c4 = tid & 63;  // 16-byte column group of the row
+#pragma unroll 4
+      for (int k = 0; k < 16; ++k) {
+        const int lr = (tid >> 6) + 4 * k;
+        const int row = 64 * pass + lr, n = n0 + 4 * c4;
+        const float4 v = *reinterpret_cast<const float4*>(cs + lr * kPitch + 4 * c4);
+        const uint32_t o = (row < rows_c && n < N) ? (uint32_t)((row * p.ldc + n) * 4) : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), rf_rs, (int)o, 0, 0);
+      }
+      __syncthreads();
+    }
+  } else if constexpr (EPI == kEpiF32) {
     // fp32 tile rows (buffer resource over rows_c rows of ldc floats).
     float* cf = reinterpret_cast<float*>(p.C) + z * p.sCz + (int64_t)m0 * p.ldc;
     const __amdgpu_buffer_rsrc_t rf_rs =
@@ -348,9 +404,9 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
 template <int BM, int BN, int EPI>
 static hipError_t launch_gemm(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                               int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, int M, int N, int K,
-                              int batch, int xcd_order, hipStream_t s) {
+                              int batch, int xcd_order, hipStream_t s, const uint16_t* aux = nullptr) {
   GemmArgs p{A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, (M + BM - 1) / BM, (N + BN - 1) / BN, batch,
-             xcd_order};
+             xcd_order, aux};
   const int64_t total = (int64_t)p.tiles_m * p.tiles_n * batch;
   hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EPI>), dim3((unsigned)total), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -414,12 +470,25 @@ hipError_t launch_gemm_store_bf16(const uint16_t* A, int64_t lda, const uint16_t
   return launch_gemm<kBM, kBN, kEpiStore>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
 }
 
+// bf16 C = (A . B^T) * GELU'(aux) per batch index z, aux laid out like C
+// (the gradient through the experts' hidden activation).
+hipError_t launch_gemm_gelu_grad_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
+                                      int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, const uint16_t* aux, int M,
+                                      int N, int K, int batch, hipStream_t s) {
+  return launch_gemm<kBM, kBN, kEpiGeluGrad>(A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, batch, /*xcd_order=*/1,
+                                             s, aux);
+}
+
 // fp32 C = A . B^T per batch index z (split-K partial sums of the MoLE
 // block's down-projection: z selects a K range through sAz and sBz).
 // C rows of ldc floats; needs 256 * ldc * 4 < 2^31.
 hipError_t launch_gemm_f32_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                 int64_t sBz, float* C, int64_t ldc, int64_t sCz, int M, int N, int K, int batch,
                                 hipStream_t s) {
+  // Rows 16 KB or more apart: stage through LDS and write whole row segments.
+  if (ldc * 4 >= kStagedMinRowBytes)
+    return launch_gemm<kBM, kBN, kEpiF32Staged>(A, lda, sAz, B, ldb, sBz, reinterpret_cast<uint16_t*>(C), ldc, sCz,
+                                                M, N, K, batch, /*xcd_order=*/1, s);
   return launch_gemm<kBM, kBN, kEpiF32>(A, lda, sAz, B, ldb, sBz, reinterpret_cast<uint16_t*>(C), ldc, sCz, M, N, K,
                                         batch, /*xcd_order=*/1, s);
 }

@@ -62,6 +62,28 @@ __device__ __forceinline__ void stg16_nt(float* p, float a, float b, float c, fl
 // the approximation is invisible there; it costs ~14 full-rate VALU slots and
 // no transcendental, which matters because a GEMM epilogue runs it once
 // per hidden unit and row.
+// Phi(u) from the same polynomial (gelu_poly(u) = u * phi_poly(u)).
+__device__ __forceinline__ float phi_poly(float u) {
+  const float s = __builtin_amdgcn_fmed3f(u, -4.0f, 4.0f) * 0.25f;
+  const float s2 = s * s;
+  float p = -1.005731821e+00f;
+  p = fmaf(p, s2, 6.118065357e+00f);
+  p = fmaf(p, s2, -1.688562202e+01f);
+  p = fmaf(p, s2, 2.834799385e+01f);
+  p = fmaf(p, s2, -3.288965607e+01f);
+  p = fmaf(p, s2, 2.843501091e+01f);
+  p = fmaf(p, s2, -1.914556694e+01f);
+  p = fmaf(p, s2, 1.018382359e+01f);
+  p = fmaf(p, s2, -4.254103661e+00f);
+  p = fmaf(p, s2, 1.595752358e+00f);
+  return __builtin_amdgcn_fmed3f(fmaf(s, p, 0.5f), 0.0f, 1.0f);
+}
+
+// d GELU / du = Phi(u) + u phi(u), phi(u) = exp(-u^2/2) / sqrt(2 pi).
+__device__ __forceinline__ float gelu_grad_poly(float u) {
+  return fmaf(u * 0.3989422804014327f, __expf(-0.5f * u * u), phi_poly(u));
+}
+
 __device__ __forceinline__ float gelu_poly(float u) {
   const float s = __builtin_amdgcn_fmed3f(u, -4.0f, 4.0f) * 0.25f;
   const float s2 = s * s;

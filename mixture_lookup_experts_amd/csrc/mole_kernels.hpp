@@ -54,6 +54,9 @@ hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t*
 
 hipError_t launch_gemm_store_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
                                   int64_t ldc, int M, int N, int K, hipStream_t s);
+hipError_t launch_gemm_gelu_grad_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
+                                      int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, const uint16_t* aux, int M,
+                                      int N, int K, int batch, hipStream_t s);
 hipError_t launch_gemm_f32_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                 int64_t sBz, float* C, int64_t ldc, int64_t sCz, int M, int N, int K, int batch,
                                 hipStream_t s);
@@ -65,7 +68,7 @@ struct TrainPlan {
   // forward state (kept by the caller between the two calls)
   size_t x_off, g_off, o_off, fwd_total;
   // backward scratch (a second workspace)
-  size_t gate_off, dz_off, do_off, dot_off, u_off, dg_off, du_off, dut_off, gt_off, xt_off, wdt_off, wut_off,
+  size_t gate_off, dz_off, do_off, dot_off, u_off, du_off, dut_off, gt_off, xt_off, wdt_off, wut_off,
       pdx_off, pwr_off, bwd_total;
   int wr_chunks;         // token chunks of the router-weight gradient
 };

@@ -16,7 +16,7 @@
 //                d_h = sum_e dz_e W_r[e]                     (gate_backward_kernel)
 //   router:      d_W_r = dz^T . h                            (two reduction passes)
 //   per row u:   dO[u][e] = sum_{t : remap t = u} g_te dy_t  (tokens grouped by row)
-//   experts:     dG_e = dO_e . W_down[e];  dU = dG * GELU'(X . W_up^T)
+//   experts:     dU_e = (dO_e . W_down[e]) * GELU'(X . W_up^T)   (one GEMM epilogue)
 //                d_W_down[e] = dO_e^T . G_e,  d_W_up[e] = dU_e^T . X,
 //                d_X = dU . W_up  (= the gradient of the rows Emb[uniq])
 // The five products run on the 256x256 MFMA GEMM (C = A . B^T with both
@@ -36,7 +36,7 @@ namespace mole {
 namespace {
 
 constexpr int kTile = 64;      // transpose tile edge
-constexpr int kWrChunk = 64;   // tokens per partial sum of the router-weight gradient
+constexpr int kWrChunk = 16;   // tokens per partial sum of the router-weight gradient
 
 inline size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 
@@ -52,25 +52,44 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
 }
 
 // out[b][c][r] = in[b][r][c] for r < R (zero for R <= r < Rpad), c < C; bf16.
+// Needs C, Rpad, ld_in, ld_out, bs_in, bs_out multiples of 8 (16-byte rows of
+// 8 elements both ways).  A 64 x 64 tile goes through LDS: 16-byte loads
+// along c, 16-byte stores along r, each assembled from 8 LDS reads.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ in, int64_t ld_in,
                                                         int64_t bs_in, uint16_t* __restrict__ out, int64_t ld_out,
                                                         int64_t bs_out, int R, int C, int Rpad) {
-  __shared__ uint16_t tile[kTile][kTile + 2];
+  __shared__ uint16_t tile[kTile][kTile + 8];  // row pitch 144 bytes
   const int r0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
   const int64_t b = blockIdx.z;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const uint16_t* src = in + b * bs_in;
   uint16_t* dst = out + b * bs_out;
-#pragma unroll 4
-  for (int i = ty; i < kTile; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? src[(int64_t)r * ld_in + c] : (uint16_t)0;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + 256 * k;            // 512 16-byte pieces: row q / 8, column group q % 8
+    const int i = q >> 3, cg = (q & 7) * 8;
+    const int r = r0 + i, c = c0 + cg;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * ld_in + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[i][cg + 2 * j] = (uint16_t)(w[j] & 0xFFFFu);
+      tile[i][cg + 2 * j + 1] = (uint16_t)(w[j] >> 16);
+    }
   }
   __syncthreads();
-#pragma unroll 4
-  for (int i = ty; i < kTile; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < C && r < Rpad) dst[(int64_t)c * ld_out + r] = tile[tx][i];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + 256 * k;            // output row c0 + q / 8, rows r0 + (q % 8) * 8 .. + 7
+    const int i = q >> 3, rg = (q & 7) * 8;
+    const int c = c0 + i, r = r0 + rg;
+    if (c < C && r < Rpad) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)tile[rg + 2 * j][i] | ((uint32_t)tile[rg + 2 * j + 1][i] << 16);
+      *reinterpret_cast<uint4*>(dst + (int64_t)c * ld_out + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
@@ -184,38 +203,52 @@ __global__ __launch_bounds__(256) void wr_partial_kernel(const float* __restrict
 }
 
 // dO[u][e][d] = bf16( sum over the tokens t of row u of g[t][e] * dy[t][d] ).
+// A workgroup owns 64 columns of one row; its four waves take every fourth
+// token of the row (Zipf batches give a few rows hundreds of tokens) and
+// meet in LDS.
 template <int NP>
 __global__ __launch_bounds__(256) void row_grad_kernel(const float* __restrict__ g, const float* __restrict__ dy,
                                                        const int64_t* __restrict__ row_ptr,
                                                        const int64_t* __restrict__ tok, uint16_t* __restrict__ dO,
                                                        int D, int N) {
+  __shared__ float part[3][NP][64];
   const int64_t u = blockIdx.x;
-  const int d = blockIdx.y * 256 + threadIdx.x;
-  if (d >= D) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int d = blockIdx.y * 64 + lane;
+  const bool ok = d < D;
   float acc[NP];
 #pragma unroll
   for (int e = 0; e < NP; ++e) acc[e] = 0.f;
-  for (int64_t k = row_ptr[u]; k < row_ptr[u + 1]; ++k) {
-    const int64_t t = tok[k];
-    const float yv = dy[t * D + d];
+  // Four tokens per wave and trip, their loads issued together (a hot row's
+  // walk is a chain of dependent loads otherwise).
+  const int64_t k0 = row_ptr[u], k1 = row_ptr[u + 1];
+  for (int64_t k = k0 + wave; k < k1; k += 16) {
+    int64_t t4[4];
+    float y4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t kq = k + 4 * q;
+      t4[q] = tok[kq < k1 ? kq : k1 - 1];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y4[q] = (ok && k + 4 * q < k1) ? dy[t4[q] * D + d] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < NP; ++e)
+        if (e < N) acc[e] = fmaf(g[t4[q] * N + e], y4[q], acc[e]);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < NP; ++e) part[wave - 1][e][lane] = acc[e];
+  }
+  __syncthreads();
+  if (wave == 0 && ok) {
+    uint16_t* out = dO + u * (int64_t)N * D + d;
 #pragma unroll
     for (int e = 0; e < NP; ++e)
-      if (e < N) acc[e] = fmaf(g[t * N + e], yv, acc[e]);
-  }
-  uint16_t* out = dO + u * (int64_t)N * D + d;
-#pragma unroll
-  for (int e = 0; e < NP; ++e)
-    if (e < N) out[(int64_t)e * D] = (uint16_t)f32_to_bf16_rne(acc[e]);
-}
-
-// dU = bf16(dG * GELU'(u)), GELU'(u) = Phi(u) + u phi(u) (exact form).
-__global__ __launch_bounds__(256) void gelu_grad_kernel(const float* __restrict__ dG, const uint16_t* __restrict__ u,
-                                                        uint16_t* __restrict__ dU, int64_t count) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
-    const float x = bf16_to_f32(u[i]);
-    const float phi = 0.3989422804014327f * expf(-0.5f * x * x);
-    const float dgelu = 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * phi;
-    dU[i] = (uint16_t)f32_to_bf16_rne(dG[i] * dgelu);
+      if (e < N) out[(int64_t)e * D] = (uint16_t)f32_to_bf16_rne(acc[e] + part[0][e][lane] + part[1][e][lane] +
+                                                                 part[2][e][lane]);
   }
 }
 
@@ -223,9 +256,13 @@ __global__ __launch_bounds__(256) void gelu_grad_kernel(const float* __restrict_
 __global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restrict__ P, int S, int64_t count,
                                                            float* __restrict__ out) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
-    float a = 0.f;
-    for (int s = 0; s < S; ++s) a += P[(int64_t)s * count + i];
-    out[i] = a;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains of loads
+    int sp = 0;
+    for (; sp + 4 <= S; sp += 4)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] += P[(int64_t)(sp + q) * count + i];
+    for (; sp < S; ++sp) a[0] += P[(int64_t)sp * count + i];
+    out[i] = (a[0] + a[1]) + (a[2] + a[3]);
   }
 }
 
@@ -284,7 +321,6 @@ TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N) {
   p.do_off = o; o += round256((size_t)U * N * D * 2);
   p.dot_off = o; o += round256((size_t)N * D * p.up * 2);
   p.u_off = o; o += round256((size_t)U * NF * 2);
-  p.dg_off = o; o += round256((size_t)U * NF * 4);
   p.du_off = o; o += round256((size_t)U * NF * 2);
   p.dut_off = o; o += round256((size_t)NF * p.up * 2);
   p.gt_off = o; o += round256((size_t)NF * p.up * 2);
@@ -335,7 +371,6 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
   uint16_t* dO = reinterpret_cast<uint16_t*>(bb + p.do_off);
   uint16_t* dOT = reinterpret_cast<uint16_t*>(bb + p.dot_off);
   uint16_t* Upre = reinterpret_cast<uint16_t*>(bb + p.u_off);
-  float* dG = reinterpret_cast<float*>(bb + p.dg_off);
   uint16_t* dU = reinterpret_cast<uint16_t*>(bb + p.du_off);
   uint16_t* dUT = reinterpret_cast<uint16_t*>(bb + p.dut_off);
   uint16_t* GT = reinterpret_cast<uint16_t*>(bb + p.gt_off);
@@ -359,7 +394,7 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
                      N * D, d_w_r);
   MOLE_TRY(hipGetLastError());
   // Gradient of the batch's table rows, dO[u][e] = sum_t g_te dy_t.
-  MOLE_NP_SWITCH(row_grad_kernel, dim3((unsigned)U, (unsigned)((D + 255) / 256)), s, (const float*)gate, dy, row_ptr,
+  MOLE_NP_SWITCH(row_grad_kernel, dim3((unsigned)U, (unsigned)((D + 63) / 64)), s, (const float*)gate, dy, row_ptr,
                  tok, dO, (int)D, (int)N);
   MOLE_TRY(hipGetLastError());
   // Transposed operands: dO_e^T [D][Up], G_e^T [F][Up], X^T [D][Up],
@@ -370,12 +405,10 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
   MOLE_TRY(transpose(w_down, F, D * F, WdT, D, F * D, D, F, D, N, s));
   MOLE_TRY(transpose(w_up, D, 0, WuT, NF, 0, NF, D, NF, 1, s));
   // Pre-activations again (not kept by the forward pass), then
-  // dG_e = dO_e . W_down[e] and dU = dG * GELU'(u).
+  // dU = (dO_e . W_down[e]) * GELU'(u) in one GEMM epilogue.
   MOLE_TRY(launch_gemm_store_bf16(X, D, w_up, D, Upre, NF, (int)U, (int)NF, (int)D, s));
-  MOLE_TRY(launch_gemm_f32_bf16(dO, N * D, D, WdT, D, F * D, dG, NF, F, (int)U, (int)F, (int)D, (int)N, s));
-  hipLaunchKernelGGL(gelu_grad_kernel, dim3(grid_for(U * NF)), dim3(256), 0, s, (const float*)dG,
-                     (const uint16_t*)Upre, dU, U * NF);
-  MOLE_TRY(hipGetLastError());
+  MOLE_TRY(launch_gemm_gelu_grad_bf16(dO, N * D, D, WdT, D, F * D, dU, NF, F, Upre, (int)U, (int)F, (int)D, (int)N,
+                                      s));
   MOLE_TRY(transpose(dU, NF, F, dUT, Up, F * Up, U, F, Up, N, s));
   // Weight gradients: d_W_down[e] = dO_e^T . G_e, d_W_up[e] = dU_e^T . X.
   MOLE_TRY(launch_gemm_f32_bf16(dOT, Up, D * Up, GT, Up, F * Up, d_w_down, F, D * F, (int)D, (int)F, (int)Up, (int)N,
