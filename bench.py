@@ -437,8 +437,7 @@ def train_probe(torch, mole, synth, dev, stream):
     `stream` for the 160M-class layer at T = 256, the 410M-class layer at
     T = 1024 and 4096 and the 1B-class layer at T = 1024 (Zipf ids, weights
     N(0, 0.02)).  Roofline: the MFMA peak on the algorithmic flops, 4 U N D F
-    forward and 8 U N D F backward (U = distinct ids; the backward's recompute
-    of the hidden pre-activations is not counted)."""
+    forward and 8 U N D F backward (U = distinct ids)."""
     out = {}
     with torch.cuda.stream(stream):
         for name, T in (("160m", 256), ("410m", 1024), ("410m", 4096), ("1b", 1024)):

@@ -59,7 +59,12 @@ __device__ __forceinline__ float gelu_erf(float u) { return 0.5f * u * (1.0f + e
 // pass of the experts' hidden activation).
 // F32Staged: the fp32 tile goes through LDS in four passes of 64 rows, and
 // every store writes a quarter of a 1 KB row segment (rows far apart).
-enum { kEpiStore = 0, kEpiGelu = 1, kEpiStoreStaged = 2, kEpiF32 = 3, kEpiGeluGrad = 4, kEpiF32Staged = 5 };
+// GeluPre: GELU(acc) to C and acc itself (bf16) to `pre`, laid out like C
+// (the training forward keeps the pre-activations for the backward pass).
+enum {
+  kEpiStore = 0, kEpiGelu = 1, kEpiStoreStaged = 2, kEpiF32 = 3, kEpiGeluGrad = 4, kEpiF32Staged = 5,
+  kEpiGeluPre = 6
+};
 constexpr int64_t kStagedMinRowBytes = 16384;
 
 constexpr int kBK = 64;     // K slice per LDS stage (64 bf16 = 128 bytes per row)
@@ -76,6 +81,7 @@ struct GemmArgs {
   int tiles_m, tiles_n, batch;
   int xcd_order;  // 1: XCD-banded tile order, 0: row-major tile order
   const uint16_t* aux;  // GELU-gradient epilogue: bf16 pre-activations, laid out like C
+  uint16_t* pre;        // GeluPre epilogue: bf16 pre-activations out, laid out like C
 };
 
 // Map the hardware workgroup id to an output tile.
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rc_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.C + z * p.sCz + (int64_t)m0 * p.ldc), (short)0, (int)(rows_c * p.ldc * 2), kRsrcWord3);
   // (GELU or its gradient,) round to bf16, pack 4 consecutive columns into 8 bytes.
-  auto packed = [&](int i, int j, int g) {
+  auto packed = [&](int i, int j, int g, bool raw = false) {
     float v[4];
     if constexpr (EPI == kEpiGeluGrad) {
       // u at the same (row, column) as this accumulator group, 8 bytes
@@ -281,7 +287,8 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[q] = acc[i][j][4 * g + q];
-        if constexpr (EPI == kEpiGelu) v[q] = gelu_poly(v[q]);
+        if constexpr (EPI == kEpiGelu || EPI == kEpiGeluPre)
+          if (!raw) v[q] = gelu_poly(v[q]);
       }
     }
     const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)v[0]) |
@@ -354,6 +361,10 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
     // Direct: 8-byte stores through a buffer resource over this tile's rows
     // (rows past M and column groups past N take an out-of-range offset and
     // are dropped).
+    __amdgpu_buffer_rsrc_t rp_rs = rc_rs;
+    if constexpr (EPI == kEpiGeluPre)
+      rp_rs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.pre + z * p.sCz + (int64_t)m0 * p.ldc), (short)0,
+                                                (int)(rows_c * p.ldc * 2), kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int mr = wm * WM + i * 32 + (lane & 31);  // row within the tile
@@ -366,6 +377,10 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
           __builtin_amdgcn_raw_buffer_store_b64(
               __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, packed(i, j, g)), rc_rs, (int)o,
               0, 0);
+          if constexpr (EPI == kEpiGeluPre)
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, packed(i, j, g, true)), rp_rs,
+                (int)o, 0, 0);
         }
       }
     }
@@ -404,9 +419,10 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
 template <int BM, int BN, int EPI>
 static hipError_t launch_gemm(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                               int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, int M, int N, int K,
-                              int batch, int xcd_order, hipStream_t s, const uint16_t* aux = nullptr) {
+                              int batch, int xcd_order, hipStream_t s, const uint16_t* aux = nullptr,
+                              uint16_t* pre = nullptr) {
   GemmArgs p{A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, (M + BM - 1) / BM, (N + BN - 1) / BN, batch,
-             xcd_order, aux};
+             xcd_order, aux, pre};
   const int64_t total = (int64_t)p.tiles_m * p.tiles_n * batch;
   hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EPI>), dim3((unsigned)total), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -432,7 +448,7 @@ size_t build_lut_rec_workspace(int64_t V, int64_t D, int64_t F, int64_t N) {
 
 hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, const uint16_t* w_down,
                                  uint16_t* lut, int64_t V, int64_t D, int64_t F, int64_t N,
-                                 void* ws, size_t ws_bytes, hipStream_t s) {
+                                 void* ws, size_t ws_bytes, hipStream_t s, uint16_t* pre) {
   const int64_t NF = N * F;
   const int64_t row_bytes = NF * 2;
   // Vocabulary rows per block: all of V when the workspace holds them,
@@ -443,8 +459,11 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
   uint16_t* G = static_cast<uint16_t*>(ws);
   for (int64_t v0 = 0; v0 < V; v0 += vc) {
     const int64_t mc = (V - v0 < vc) ? (V - v0) : vc;
-    hipError_t err = launch_gemm<kBM, kBN, kEpiGelu>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc,
-                                                      (int)NF, (int)D, 1, /*xcd_order=*/0, s);
+    hipError_t err =
+        pre ? launch_gemm<kBM, kBN, kEpiGeluPre>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc, (int)NF, (int)D,
+                                                 1, /*xcd_order=*/0, s, nullptr, pre + v0 * NF)
+            : launch_gemm<kBM, kBN, kEpiGelu>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc, (int)NF, (int)D, 1,
+                                              /*xcd_order=*/0, s);
     if (err != hipSuccess) return err;
     if (N * D * 2 >= kStagedMinRowBytes)
       err = launch_gemm<kBM, kBN, kEpiStoreStaged>(G, NF, F, w_down, F, D * F, lut + v0 * N * D, N * D, D,
@@ -462,12 +481,6 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
 hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
                                  int64_t ldc, int M, int N, int K, hipStream_t s) {
   return launch_gemm<kBM, kBN, kEpiGelu>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
-}
-
-// bf16 C = A . B^T (no epilogue function), one 256x256 tile per workgroup.
-hipError_t launch_gemm_store_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
-                                  int64_t ldc, int M, int N, int K, hipStream_t s) {
-  return launch_gemm<kBM, kBN, kEpiStore>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
 }
 
 // bf16 C = (A . B^T) * GELU'(aux) per batch index z, aux laid out like C

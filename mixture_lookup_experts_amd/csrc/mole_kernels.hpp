@@ -45,15 +45,13 @@ size_t build_lut_min_workspace(int64_t D, int64_t F, int64_t N);
 size_t build_lut_rec_workspace(int64_t V, int64_t D, int64_t F, int64_t N);
 hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, const uint16_t* w_down,
                                  uint16_t* lut, int64_t V, int64_t D, int64_t F, int64_t N,
-                                 void* ws, size_t ws_bytes, hipStream_t s);
+                                 void* ws, size_t ws_bytes, hipStream_t s, uint16_t* pre = nullptr);
 hipError_t launch_build_lut_f32(const float* emb, const float* w_up, const float* w_down, float* lut,
                                 int64_t V, int64_t D, int64_t F, int64_t N, hipStream_t s);
 constexpr int64_t kBuildF32MaxLds = 16384;  // D + F floats staged in LDS by the fp32 build
 hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
                                  int64_t ldc, int M, int N, int K, hipStream_t s);
 
-hipError_t launch_gemm_store_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
-                                  int64_t ldc, int M, int N, int K, hipStream_t s);
 hipError_t launch_gemm_gelu_grad_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                       int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, const uint16_t* aux, int M,
                                       int N, int K, int batch, hipStream_t s);
@@ -66,11 +64,14 @@ struct TrainPlan {
   int64_t up;            // U rounded up to a multiple of 8 (K of the transposed products)
   int dx_splits;         // K splits of the embedding-row gradient product
   // forward state (kept by the caller between the two calls)
-  size_t x_off, g_off, o_off, fwd_total;
-  // backward scratch (a second workspace)
-  size_t gate_off, dz_off, do_off, dot_off, u_off, du_off, dut_off, gt_off, xt_off, wdt_off, wut_off,
-      pdx_off, pwr_off, bwd_total;
+  size_t x_off, g_off, u_off, o_off, fwd_total;
+  // backward scratch (a second workspace); pwr_off also holds the row
+  // gradients' partial sums (used after the router-weight sums are done)
+  size_t gate_off, dz_off, do_off, dot_off, du_off, dut_off, gt_off, xt_off, wdt_off, wut_off, pdx_off, pwr_off,
+      bwd_total;
   int wr_chunks;         // token chunks of the router-weight gradient
+  int seg;               // token-list positions per row-gradient chunk
+  int64_t nseg;          // row-gradient chunks, ceil(T / seg)
 };
 TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N);
 hipError_t launch_train_forward(const int64_t* uniq, const int64_t* remap, const uint16_t* emb, const uint16_t* w_up,

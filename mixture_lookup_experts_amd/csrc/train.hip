@@ -7,9 +7,11 @@
 // Forward, for the U distinct ids of a batch (uniq) and the token -> row map
 // (remap):
 //   X = Emb[uniq]                                    (gather)
-//   G = GELU(X . W_up^T), O[:, e, :] = G_e . W_down[e]^T   (the build's two GEMMs)
+//   Upre = X . W_up^T, G = GELU(Upre), O[:, e, :] = G_e . W_down[e]^T
+//                                                    (the build's two GEMMs)
 //   y = sum_e softmax(W_r h)[e] O[remap, e, :]       (the lookup-combine)
-// X, G and O stay in the caller's forward workspace for the backward pass.
+// X, Upre, G and O stay in the caller's forward workspace for the backward
+// pass.
 //
 // Backward for an upstream gradient dy [T][D] (fp32):
 //   per token:   g = softmax(W_r h), dg_e = dy . O[remap, e], dz = g (dg - g.dg),
@@ -22,10 +24,11 @@
 // The five products run on the 256x256 MFMA GEMM (C = A . B^T with both
 // operands K-contiguous, fp32 output); products whose contraction runs over
 // rows (U) or over the weights' output dimension take LDS-tiled transposed
-// copies of their operands.  dO, dU and the recomputed pre-activations are
-// rounded to bf16 for the matrix cores; all sums are fp32.  The per-row
-// gradient sums walk a host-built list of each row's tokens, so no atomics
-// and the result does not depend on scheduling.
+// copies of their operands.  dO, dU and the pre-activations are rounded to
+// bf16 for the matrix cores; all sums are fp32.  The per-row gradient sums
+// walk a host-built list of the tokens grouped by row in fixed chunks and
+// add the pieces of rows that cross chunks in chunk order, so no atomics and
+// the result does not depend on scheduling.
 #include <algorithm>
 
 #include "mole_device.hpp"
@@ -37,6 +40,46 @@ namespace {
 
 constexpr int kTile = 64;      // transpose tile edge
 constexpr int kWrChunk = 16;   // tokens per partial sum of the router-weight gradient
+constexpr int kMaxSeg = 64;    // most token-list positions per row-gradient chunk
+
+// Columns per lane of the row-gradient walk: NP * CPL accumulators <= 64.
+template <int NP>
+struct RowGradCols {
+  static constexpr int kCpl = NP >= 64 ? 1 : (NP >= 32 ? 2 : 4);
+};
+
+template <int CPL>
+__device__ __forceinline__ void load_cols(const float* p, float* v) {
+  if constexpr (CPL == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else if constexpr (CPL == 2) {
+    const float2 q = *reinterpret_cast<const float2*>(p);
+    v[0] = q.x; v[1] = q.y;
+  } else {
+    v[0] = *p;
+  }
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_bf16_cols(uint16_t* p, const float* v) {
+  if constexpr (CPL == 4)
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  else if constexpr (CPL == 2)
+    *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v[0], v[1]);
+  else
+    *p = (uint16_t)f32_to_bf16_rne(v[0]);
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_f32_cols(float* p, const float* v) {
+  if constexpr (CPL == 4)
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  else if constexpr (CPL == 2)
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  else
+    *p = v[0];
+}
 
 inline size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 
@@ -93,88 +136,107 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
   }
 }
 
-// Per token t (one workgroup): router logits and dg_e = dy_t . O[remap_t][e]
-// as block sums, softmax and dz in LDS, then d_h[t] = sum_e dz_e W_r[e].
+// Per token t (one wavefront, 8 consecutive columns per lane and trip):
+// router logits z_e = h_t . W_r[e] and dg_e = dy_t . O[remap_t][e] as lane
+// sums, a reduce-scatter across the wavefront, the 2N totals through LDS to
+// every lane, softmax and dz, then d_h[t] = sum_e dz_e W_r[e].
 template <int NP>
 __global__ __launch_bounds__(256) void gate_backward_kernel(const uint16_t* __restrict__ h,
                                                             const uint16_t* __restrict__ w_r,
                                                             const uint16_t* __restrict__ O,
                                                             const int64_t* __restrict__ remap,
                                                             const float* __restrict__ dy, float* __restrict__ g_out,
-                                                            float* __restrict__ dz_out, float* __restrict__ d_h, int D,
-                                                            int N) {
-  __shared__ float red[4][2 * NP];
-  __shared__ float dzs[NP];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                            float* __restrict__ dz_out, float* __restrict__ d_h,
+                                                            int64_t T, int D, int N) {
+  using RS = ReduceScatter<2 * NP, kWave>;
+  __shared__ float tot[4][2 * NP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tw = (int64_t)blockIdx.x * 4 + wave;
+  const bool valid = tw < T;
+  const int64_t t = valid ? tw : T - 1;  // a wave past the end recomputes the last token and stores nothing
   const uint16_t* orow = O + remap[t] * (int64_t)N * D;
-  float z[NP], dg[NP];
+  float v[2 * NP];  // z_e, then dg_e
 #pragma unroll
-  for (int e = 0; e < NP; ++e) z[e] = dg[e] = 0.f;
-  for (int d = tid; d < D; d += 256) {
-    const float hv = bf16_to_f32(h[t * D + d]);
-    const float yv = dy[t * D + d];
+  for (int e = 0; e < 2 * NP; ++e) v[e] = 0.f;
+  for (int c = lane * 8; c < D; c += 512) {
+    float hv[8], yv[8];
+    Elem<uint16_t>::unpack(ldg16(h + t * D + c), hv);
+    Elem<float>::unpack(ldg16(dy + t * D + c), yv);
+    Elem<float>::unpack(ldg16(dy + t * D + c + 4), yv + 4);
 #pragma unroll
     for (int e = 0; e < NP; ++e) {
       if (e < N) {
-        z[e] = fmaf(hv, bf16_to_f32(w_r[(int64_t)e * D + d]), z[e]);
-        dg[e] = fmaf(yv, bf16_to_f32(orow[(int64_t)e * D + d]), dg[e]);
+        float wv[8], ov[8];
+        Elem<uint16_t>::unpack(ldg16(w_r + (int64_t)e * D + c), wv);
+        Elem<uint16_t>::unpack(ldg16(orow + (int64_t)e * D + c), ov);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[e] = fmaf(hv[i], wv[i], v[e]);
+          v[NP + e] = fmaf(yv[i], ov[i], v[NP + e]);
+        }
       }
     }
   }
+  RS::run(v, lane);
+  {
+    const int off = RS::offset(lane);
+#pragma unroll
+    for (int i = 0; i < RS::kLeft; ++i) tot[wave][off + i] = v[i];  // lanes with one offset hold one total
+  }
+  __syncthreads();
+  float zz[NP], dd[NP];
+  float zmax = -INFINITY;
 #pragma unroll
   for (int e = 0; e < NP; ++e) {
+    zz[e] = tot[wave][e];
+    dd[e] = tot[wave][NP + e];
+    if (e < N) zmax = fmaxf(zmax, zz[e]);
+  }
+  // (every lane computes the same softmax; loops over the compile-time
+  // bound NP keep the arrays in registers)
+  float sum = 0.f;
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      z[e] += __shfl_xor(z[e], m, 64);
-      dg[e] += __shfl_xor(dg[e], m, 64);
+  for (int e = 0; e < NP; ++e) {
+    zz[e] = e < N ? expf(zz[e] - zmax) : 0.f;
+    sum += zz[e];
+  }
+  float gdg = 0.f;
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    zz[e] /= sum;
+    gdg = fmaf(zz[e], dd[e], gdg);
+  }
+  float my_g = 0.f, my_dz = 0.f;
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    dd[e] = zz[e] * (dd[e] - gdg);  // dz_e
+    if (lane == e) {
+      my_g = zz[e];
+      my_dz = dd[e];
     }
   }
-  if (lane == 0) {
-#pragma unroll
-    for (int e = 0; e < NP; ++e) {
-      red[wave][e] = z[e];
-      red[wave][NP + e] = dg[e];
-    }
+  if (valid && lane < N) {
+    g_out[t * N + lane] = my_g;
+    dz_out[t * N + lane] = my_dz;
   }
-  __syncthreads();
-  if (tid == 0) {
-    // (loops over the compile-time bound NP keep the arrays in registers)
-    float zz[NP], gg[NP], dd[NP];
-    float zmax = -INFINITY;
+  for (int c = lane * 8; c < D; c += 512) {
+    float acc[8];
 #pragma unroll
-    for (int e = 0; e < NP; ++e) {
-      zz[e] = red[0][e] + red[1][e] + red[2][e] + red[3][e];
-      dd[e] = red[0][NP + e] + red[1][NP + e] + red[2][NP + e] + red[3][NP + e];
-      if (e < N) zmax = fmaxf(zmax, zz[e]);
-    }
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < NP; ++e) {
-      gg[e] = e < N ? expf(zz[e] - zmax) : 0.f;
-      sum += gg[e];
-    }
-    float gdg = 0.f;
-#pragma unroll
-    for (int e = 0; e < NP; ++e) {
-      gg[e] /= sum;
-      gdg = fmaf(gg[e], dd[e], gdg);
-    }
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int e = 0; e < NP; ++e) {
       if (e < N) {
-        const float dzv = gg[e] * (dd[e] - gdg);
-        g_out[t * N + e] = gg[e];
-        dz_out[t * N + e] = dzv;
-        dzs[e] = dzv;
+        float wv[8];
+        Elem<uint16_t>::unpack(ldg16(w_r + (int64_t)e * D + c), wv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(dd[e], wv[i], acc[i]);
       }
     }
-  }
-  __syncthreads();
-  for (int d = tid; d < D; d += 256) {
-    float acc = 0.f;
-    for (int e = 0; e < N; ++e) acc = fmaf(dzs[e], bf16_to_f32(w_r[(int64_t)e * D + d]), acc);
-    d_h[t * D + d] = acc;
+    if (valid) {
+      float4* o = reinterpret_cast<float4*>(d_h + t * D + c);
+      o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
   }
 }
 
@@ -202,53 +264,119 @@ __global__ __launch_bounds__(256) void wr_partial_kernel(const float* __restrict
     if (e < N) out[(int64_t)e * D + d] = acc[e];
 }
 
-// dO[u][e][d] = bf16( sum over the tokens t of row u of g[t][e] * dy[t][d] ).
-// A workgroup owns 64 columns of one row; its four waves take every fourth
-// token of the row (Zipf batches give a few rows hundreds of tokens) and
-// meet in LDS.
+// Row gradients dO[u][e][d] = bf16( sum over the tokens t of row u of
+// g[t][e] dy[t][d] ), by fixed chunks of `seg` positions of the token list
+// grouped by row (tok, row_ptr), so that a row with hundreds of tokens (the
+// head of a Zipf batch) is spread over many workgroups.  A row that lies
+// inside one chunk is summed and written there.  A row cut by a chunk
+// boundary leaves an fp32 partial sum per chunk it touches, in slot 0 of
+// that chunk when the row holds the chunk's first position and in slot 1
+// otherwise (it then starts inside the chunk and runs past its end);
+// row_grad_fix_kernel adds those in chunk order.  Each wave owns 64*CPL
+// columns and walks the chunk's positions in order.
 template <int NP>
 __global__ __launch_bounds__(256) void row_grad_kernel(const float* __restrict__ g, const float* __restrict__ dy,
+                                                       const int64_t* __restrict__ remap,
                                                        const int64_t* __restrict__ row_ptr,
                                                        const int64_t* __restrict__ tok, uint16_t* __restrict__ dO,
-                                                       int D, int N) {
-  __shared__ float part[3][NP][64];
-  const int64_t u = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int d = blockIdx.y * 64 + lane;
-  const bool ok = d < D;
-  float acc[NP];
-#pragma unroll
-  for (int e = 0; e < NP; ++e) acc[e] = 0.f;
-  // Four tokens per wave and trip, their loads issued together (a hot row's
-  // walk is a chain of dependent loads otherwise).
-  const int64_t k0 = row_ptr[u], k1 = row_ptr[u + 1];
-  for (int64_t k = k0 + wave; k < k1; k += 16) {
-    int64_t t4[4];
-    float y4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t kq = k + 4 * q;
-      t4[q] = tok[kq < k1 ? kq : k1 - 1];
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y4[q] = (ok && k + 4 * q < k1) ? dy[t4[q] * D + d] : 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < NP; ++e)
-        if (e < N) acc[e] = fmaf(g[t4[q] * N + e], y4[q], acc[e]);
+                                                       float* __restrict__ part, int64_t T, int seg, int D, int N) {
+  constexpr int CPL = RowGradCols<NP>::kCpl;
+  __shared__ float gs[kMaxSeg][NP];
+  __shared__ int64_t ts[kMaxSeg], rs[kMaxSeg + 1], k0s[kMaxSeg], k1s[kMaxSeg];
+  const int64_t p0 = (int64_t)blockIdx.x * seg;
+  const int len = (int)(T - p0 < seg ? T - p0 : seg);
+  const int tid = threadIdx.x;
+  if (tid < len) {
+    const int64_t t = tok[p0 + tid];
+    const int64_t r = remap[t];
+    ts[tid] = t;
+    rs[tid] = r;
+    k0s[tid] = row_ptr[r];
+    k1s[tid] = row_ptr[r + 1];
   }
-  if (wave > 0) {
-#pragma unroll
-    for (int e = 0; e < NP; ++e) part[wave - 1][e][lane] = acc[e];
+  if (tid == 0) rs[len] = -1;  // sentinel: the last position ends its row's run
+  __syncthreads();
+  for (int i = tid; i < len * NP; i += 256) {
+    const int q = i / NP, e = i % NP;
+    gs[q][e] = e < N ? g[ts[q] * N + e] : 0.f;
   }
   __syncthreads();
-  if (wave == 0 && ok) {
-    uint16_t* out = dO + u * (int64_t)N * D + d;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c0 = ((blockIdx.y * 4 + wave) * 64 + lane) * CPL;
+  if (c0 >= D) return;  // (no barrier follows)
+  const int64_t pend = p0 + len;
+  float acc[NP][CPL];
 #pragma unroll
-    for (int e = 0; e < NP; ++e)
-      if (e < N) out[(int64_t)e * D] = (uint16_t)f32_to_bf16_rne(acc[e] + part[0][e][lane] + part[1][e][lane] +
-                                                                 part[2][e][lane]);
+  for (int e = 0; e < NP; ++e)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[e][c] = 0.f;
+  for (int pb = 0; pb < len; pb += 4) {
+    float yv[4][CPL];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pq = pb + q < len ? pb + q : len - 1;
+      load_cols<CPL>(dy + ts[pq] * D + c0, yv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pq = pb + q;
+      if (pq < len) {
+#pragma unroll
+        for (int e = 0; e < NP; ++e) {
+          const float ge = gs[pq][e];
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[e][c] = fmaf(ge, yv[q][c], acc[e][c]);
+        }
+        const int64_t r = rs[pq];
+        if (rs[pq + 1] != r) {  // end of this row's run in the chunk
+          const int64_t k0 = k0s[pq], k1 = k1s[pq];
+          if (k0 >= p0 && k1 <= pend) {
+            uint16_t* out = dO + r * (int64_t)N * D + c0;
+#pragma unroll
+            for (int e = 0; e < NP; ++e)
+              if (e < N) store_bf16_cols<CPL>(out + (int64_t)e * D, acc[e]);
+          } else {
+            const int slot = k0 <= p0 ? 0 : 1;
+            float* out = part + ((int64_t)blockIdx.x * 2 + slot) * N * D + c0;
+#pragma unroll
+            for (int e = 0; e < NP; ++e)
+              if (e < N) store_f32_cols<CPL>(out + (int64_t)e * D, acc[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < NP; ++e)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[e][c] = 0.f;
+        }
+      }
+    }
+  }
+}
+
+// Rows cut by chunk boundaries: the chunk in which such a row starts (it
+// holds that chunk's last position and runs past it) sums the row's partials
+// over every chunk it touches, in chunk order, and writes the bf16 row.
+__global__ __launch_bounds__(256) void row_grad_fix_kernel(const float* __restrict__ part,
+                                                           const int64_t* __restrict__ remap,
+                                                           const int64_t* __restrict__ row_ptr,
+                                                           const int64_t* __restrict__ tok, uint16_t* __restrict__ dO,
+                                                           int64_t T, int seg, int64_t ND) {
+  const int64_t j = blockIdx.x;
+  const int64_t p0 = j * seg, pend = T - p0 < seg ? T : p0 + seg;
+  const int64_t r = remap[tok[pend - 1]];
+  const int64_t k0 = row_ptr[r], k1 = row_ptr[r + 1];
+  if (!(k0 >= p0 && k1 > pend)) return;
+  const int64_t jl = (k1 - 1) / seg;
+  for (int64_t i = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4; i < ND; i += (int64_t)gridDim.y * 1024) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t jj = j; jj <= jl; ++jj) {
+      const int slot = k0 <= jj * seg ? 0 : 1;
+      const float4 q = *reinterpret_cast<const float4*>(part + (jj * 2 + slot) * ND + i);
+      a[0] += q.x;
+      a[1] += q.y;
+      a[2] += q.z;
+      a[3] += q.w;
+    }
+    *reinterpret_cast<uint2*>(dO + r * ND + i) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
   }
 }
 
@@ -310,9 +438,14 @@ TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N) {
   p.dx_splits = 1;
   while (p.dx_splits < 16 && tiles * p.dx_splits < 256 && NF % (16 * p.dx_splits) == 0) p.dx_splits *= 2;
   p.wr_chunks = (int)((T + kWrChunk - 1) / kWrChunk);
+  // Row-gradient chunks: about 128 of them (a power-of-two size in [4, 64]).
+  p.seg = 4;
+  while (p.seg < kMaxSeg && (int64_t)p.seg * 128 < T) p.seg *= 2;
+  p.nseg = (T + p.seg - 1) / p.seg;
   size_t o = 0;
   p.x_off = o; o += round256((size_t)U * D * 2);
   p.g_off = o; o += round256((size_t)U * NF * 2);
+  p.u_off = o; o += round256((size_t)U * NF * 2);
   p.o_off = o; o += round256((size_t)U * N * D * 2);
   p.fwd_total = o;
   o = 0;
@@ -320,7 +453,6 @@ TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N) {
   p.dz_off = o; o += round256((size_t)T * N * 4);
   p.do_off = o; o += round256((size_t)U * N * D * 2);
   p.dot_off = o; o += round256((size_t)N * D * p.up * 2);
-  p.u_off = o; o += round256((size_t)U * NF * 2);
   p.du_off = o; o += round256((size_t)U * NF * 2);
   p.dut_off = o; o += round256((size_t)NF * p.up * 2);
   p.gt_off = o; o += round256((size_t)NF * p.up * 2);
@@ -328,7 +460,7 @@ TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N) {
   p.wdt_off = o; o += round256((size_t)NF * D * 2);
   p.wut_off = o; o += round256((size_t)D * NF * 2);
   p.pdx_off = o; o += round256((size_t)p.dx_splits * U * D * 4);
-  p.pwr_off = o; o += round256((size_t)p.wr_chunks * N * D * 4);
+  p.pwr_off = o; o += round256((size_t)std::max<int64_t>(p.wr_chunks, 2 * p.nseg) * N * D * 4);
   p.bwd_total = o;
   return p;
 }
@@ -341,12 +473,14 @@ hipError_t launch_train_forward(const int64_t* uniq, const int64_t* remap, const
   char* base = static_cast<char*>(fwd);
   uint16_t* X = reinterpret_cast<uint16_t*>(base + p.x_off);
   uint16_t* G = reinterpret_cast<uint16_t*>(base + p.g_off);
+  uint16_t* Upre = reinterpret_cast<uint16_t*>(base + p.u_off);
   uint16_t* O = reinterpret_cast<uint16_t*>(base + p.o_off);
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)U), dim3(256), 0, s, emb, uniq, X, (int)D);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // The build restricted to the batch's rows: G for all U rows in one block.
-  err = launch_build_lut_bf16(X, w_up, w_down, O, U, D, F, N, G, (size_t)U * N * F * 2, s);
+  // The build restricted to the batch's rows: G for all U rows in one block,
+  // with the pre-activations kept for the backward pass.
+  err = launch_build_lut_bf16(X, w_up, w_down, O, U, D, F, N, G, (size_t)U * N * F * 2, s, Upre);
   if (err != hipSuccess) return err;
   return launch_lookup_combine(remap, h, w_r, O, y, T, D, N, kBF16, true, s);
 }
@@ -364,13 +498,13 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
   const char* fb = static_cast<const char*>(fwd);
   const uint16_t* X = reinterpret_cast<const uint16_t*>(fb + p.x_off);
   const uint16_t* G = reinterpret_cast<const uint16_t*>(fb + p.g_off);
+  const uint16_t* Upre = reinterpret_cast<const uint16_t*>(fb + p.u_off);
   const uint16_t* O = reinterpret_cast<const uint16_t*>(fb + p.o_off);
   char* bb = static_cast<char*>(bwd);
   float* gate = reinterpret_cast<float*>(bb + p.gate_off);
   float* dz = reinterpret_cast<float*>(bb + p.dz_off);
   uint16_t* dO = reinterpret_cast<uint16_t*>(bb + p.do_off);
   uint16_t* dOT = reinterpret_cast<uint16_t*>(bb + p.dot_off);
-  uint16_t* Upre = reinterpret_cast<uint16_t*>(bb + p.u_off);
   uint16_t* dU = reinterpret_cast<uint16_t*>(bb + p.du_off);
   uint16_t* dUT = reinterpret_cast<uint16_t*>(bb + p.dut_off);
   uint16_t* GT = reinterpret_cast<uint16_t*>(bb + p.gt_off);
@@ -384,7 +518,8 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
 #define MOLE_TRY(x) do { err = (x); if (err != hipSuccess) return err; } while (0)
 
   // Gates: g, dz, d_h.
-  MOLE_NP_SWITCH(gate_backward_kernel, dim3((unsigned)T), s, h, w_r, O, remap, dy, gate, dz, d_h, (int)D, (int)N);
+  MOLE_NP_SWITCH(gate_backward_kernel, dim3((unsigned)((T + 3) / 4)), s, h, w_r, O, remap, dy, gate, dz, d_h, T,
+                 (int)D, (int)N);
   MOLE_TRY(hipGetLastError());
   // Router weights: chunked partial sums over tokens, then their sum.
   MOLE_NP_SWITCH(wr_partial_kernel, dim3((unsigned)((D + 255) / 256), (unsigned)p.wr_chunks), s, (const float*)dz,
@@ -393,10 +528,20 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
   hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(N * D)), dim3(256), 0, s, (const float*)Pwr, p.wr_chunks,
                      N * D, d_w_r);
   MOLE_TRY(hipGetLastError());
-  // Gradient of the batch's table rows, dO[u][e] = sum_t g_te dy_t.
-  MOLE_NP_SWITCH(row_grad_kernel, dim3((unsigned)U, (unsigned)((D + 63) / 64)), s, (const float*)gate, dy, row_ptr,
-                 tok, dO, (int)D, (int)N);
-  MOLE_TRY(hipGetLastError());
+  // Gradient of the batch's table rows, dO[u][e] = sum_t g_te dy_t, by
+  // chunks of the token list (partials of cut rows in the router-weight
+  // partials' region, which is free again), then the cut rows.
+  {
+    const int cpl = NP >= 64 ? 1 : (NP >= 32 ? 2 : 4);
+    const dim3 grid((unsigned)p.nseg, (unsigned)((D + 256 * cpl - 1) / (256 * cpl)));
+    MOLE_NP_SWITCH(row_grad_kernel, grid, s, (const float*)gate, dy, remap, row_ptr, tok, dO, Pwr, T, p.seg, (int)D,
+                   (int)N);
+    MOLE_TRY(hipGetLastError());
+    const int64_t gy = std::min<int64_t>((N * D + 1023) / 1024, 32);
+    hipLaunchKernelGGL(row_grad_fix_kernel, dim3((unsigned)p.nseg, (unsigned)gy), dim3(256), 0, s,
+                       (const float*)Pwr, remap, row_ptr, tok, dO, T, p.seg, N * D);
+    MOLE_TRY(hipGetLastError());
+  }
   // Transposed operands: dO_e^T [D][Up], G_e^T [F][Up], X^T [D][Up],
   // W_down[e]^T [F][D], W_up^T [D][N*F].
   MOLE_TRY(transpose(dO, N * D, D, dOT, Up, D * Up, U, D, Up, N, s));
@@ -404,9 +549,7 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
   MOLE_TRY(transpose(X, D, 0, XT, Up, 0, U, D, Up, 1, s));
   MOLE_TRY(transpose(w_down, F, D * F, WdT, D, F * D, D, F, D, N, s));
   MOLE_TRY(transpose(w_up, D, 0, WuT, NF, 0, NF, D, NF, 1, s));
-  // Pre-activations again (not kept by the forward pass), then
-  // dU = (dO_e . W_down[e]) * GELU'(u) in one GEMM epilogue.
-  MOLE_TRY(launch_gemm_store_bf16(X, D, w_up, D, Upre, NF, (int)U, (int)NF, (int)D, s));
+  // dU = (dO_e . W_down[e]) * GELU'(u) in one GEMM epilogue (u kept by the forward pass).
   MOLE_TRY(launch_gemm_gelu_grad_bf16(dO, N * D, D, WdT, D, F * D, dU, NF, F, Upre, (int)U, (int)F, (int)D, (int)N,
                                       s));
   MOLE_TRY(transpose(dU, NF, F, dUT, Up, F * Up, U, F, Up, N, s));

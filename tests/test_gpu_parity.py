@@ -776,9 +776,12 @@ def run_train(ids, emb, w_up, w_down, h, w_r, dy):
 
 
 # (V, N, D, F, T, zipf): ragged D/F/T, repeated ids (several tokens per row),
-# many experts, and a 160M-class width.
+# many experts, a 160M-class width, and long Zipf batches whose head rows run
+# over many chunks of the row-gradient walk (64-position chunks at T = 5000;
+# 32 experts take its two-columns-per-lane form).
 TRAIN_CASES = [(300, 4, 128, 256, 100, False), (50, 3, 136, 200, 37, True), (400, 16, 256, 512, 64, True),
-               (40, 64, 64, 64, 20, False), (2000, 4, 768, 3072, 32, True)]
+               (40, 64, 64, 64, 20, False), (2000, 4, 768, 3072, 32, True), (500, 16, 64, 64, 5000, True),
+               (300, 32, 64, 128, 700, True)]
 
 
 @pytest.mark.parametrize("V,N,D,F,T,zipf", TRAIN_CASES)
