@@ -242,17 +242,17 @@ int mole_lookup_combine_int8(const int64_t* ids, const void* h, const void* w_r,
  * to the device for the two calls below.
  *
  * mole_train_workspace_size: the forward workspace (kept by the caller from
- * the forward to the backward call: the gathered rows, hidden activations
- * and the batch's table rows) and the backward scratch, for T tokens and U
- * distinct ids.
+ * the forward to the backward call: the gathered rows, the hidden pre- and
+ * post-activations and the batch's table rows) and the backward scratch,
+ * for T tokens and U distinct ids.
  *
  * mole_train_forward / mole_train_backward: bf16 only (MOLE_ERR_UNSUPPORTED
- * for MOLE_F32), D % 8 == 0 and F % 8 == 0 (MOLE_ERR_DIM), D, N*F and T at
- * most 2^20 and 1 <= N <= 64 (MOLE_ERR_UNSUPPORTED).  bf16 products with
+ * for MOLE_F32), D % 8 == 0 and F % 8 == 0 (MOLE_ERR_DIM), N*D, N*F and T
+ * at most 2^20 and 1 <= N <= 64 (MOLE_ERR_UNSUPPORTED).  bf16 products with
  * fp32 accumulation; as in mole_build_lut the hidden activation is rounded
- * to bf16, and the backward pass rounds the row gradients, the hidden
- * gradients and the recomputed pre-activations to bf16 for the matrix
- * cores; all sums and every output are fp32.  Weight gradients are
+ * to bf16, the forward workspace keeps the bf16 pre-activations, and the
+ * backward pass rounds the row gradients and the hidden gradients to bf16
+ * for the matrix cores; all sums and every output are fp32.  Weight gradients are
  * overwritten, not accumulated.  Deterministic (no atomics).
  *   uniq [U] int64, remap [T] int64, row_ptr [U+1] int64, tok [T] int64 (device)
  *   emb [V][D], w_up [N][F][D], w_down [N][D][F], h [T][D], w_r [N][D] (bf16)

@@ -385,7 +385,9 @@ int mole_train_index(const int64_t* ids_host, int64_t T, int64_t V, int64_t* uni
 }
 
 namespace {
-constexpr int64_t kMaxTrainDim = (int64_t)1 << 20;  // 256-row fp32 panels of N*F, D stay under 2^31 bytes
+// 256-row fp32 panels of N*F and D, and 64-row slices of the MN-major
+// operands (row pitch N*D or N*F), stay under 2^31 bytes.
+constexpr int64_t kMaxTrainDim = (int64_t)1 << 20;
 
 int check_train(int64_t T, int64_t U, int64_t V, int64_t D, int64_t F, int64_t N, int dtype) {
   if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
@@ -394,14 +396,14 @@ int check_train(int64_t T, int64_t U, int64_t V, int64_t D, int64_t F, int64_t N
   if (D % 8 != 0 || F % 8 != 0) return MOLE_ERR_DIM;
   if (N > kMaxExperts) return MOLE_ERR_UNSUPPORTED;
   if (dtype != MOLE_BF16) return MOLE_ERR_UNSUPPORTED;
-  if (D > kMaxTrainDim || N * F > kMaxTrainDim || T > kMaxTrainDim) return MOLE_ERR_UNSUPPORTED;
+  if (N * D > kMaxTrainDim || N * F > kMaxTrainDim || T > kMaxTrainDim) return MOLE_ERR_UNSUPPORTED;
   return MOLE_OK;
 }
 }  // namespace
 
 int mole_train_workspace_size(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N, size_t* fwd_bytes,
                               size_t* bwd_bytes) {
-  if (T < 0 || U < 0 || U > T || D <= 0 || F <= 0 || N <= 0 || N * F > kMaxTrainDim || D > kMaxTrainDim ||
+  if (T < 0 || U < 0 || U > T || D <= 0 || F <= 0 || N <= 0 || N * F > kMaxTrainDim || N * D > kMaxTrainDim ||
       T > kMaxTrainDim)
     return MOLE_ERR_DIM;
   const mole::TrainPlan p = mole::train_plan(T, U, D, F, N);

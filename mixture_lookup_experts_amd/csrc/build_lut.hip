@@ -123,10 +123,16 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// C[m][n] = epi( sum_k A[m*lda + k] * B[n*ldb + k] ), bf16 in, fp32
-// accumulation, bf16 out; batch index z offsets A, B, C by sAz, sBz, sCz.
-// Requires K % 8 == 0 and N % 8 == 0 (16-byte K segments and output chunks).
-template <int BM, int BN, int EPI>
+__device__ __forceinline__ uint32_t dword_of(const uint4& q, int i) {
+  return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
+
+// C[m][n] = epi( sum_k A[m][k] * B[n][k] ), bf16 in, fp32 accumulation;
+// batch index z offsets A, B, C by sAz, sBz, sCz.  Requires N % 8 == 0
+// (16-byte output chunks) and, with a K-contiguous operand, K % 8 == 0
+// (16-byte K segments); an MN-major operand needs its M (or N) extent, ld
+// and batch offset to be multiples of 8 and 63 * ld + 256 < 2^30.
+template <int BM, int BN, int EPI, int OPS = kOpsKK>
 __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;     // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;   // MFMA tiles per wave
@@ -156,31 +162,96 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.B + z * p.sBz + (int64_t)n0 * p.ldb), (short)0, (int)(rows_b * p.ldb * 2), kRsrcWord3);
 
-  // Staging slot s (0..15) of thread t: 16-byte segment (t & 7) of A row
-  // t/8 + 32 s (s < 8) or of B row t/8 + 32 (s - 8).
+  // Staging slot s (0..15) of thread t, K-contiguous operand: 16-byte
+  // segment (t & 7) of A row t/8 + 32 s (s < 8) or of B row t/8 + 32 (s - 8).
+  // MN-major operand: slots in groups of four, group g (slots 4g .. 4g+3 of
+  // the operand) holds k rows 4 kq .. 4 kq + 3 of the slice, kq = (t & 7) +
+  // 8 (g % 2), at MN columns 8 (t/8) .. 8 (t/8) + 7; the group is transposed
+  // in registers just before it goes to LDS, so both storages leave the same
+  // LDS layout: row = M (or N) index, 64 k per row in 16-byte segments.
   const int seg = tid & 7;
   const int srow = tid >> 3;
   const int pseg = seg ^ ((srow >> 1) & 7);  // XOR swizzle ((row >> 1) & 7 is the same for all slots)
+  auto is_mn = [](int s) { return s < SA ? (OPS & kOpsAmn) != 0 : (OPS & kOpsBmn) != 0; };
   uint32_t off[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const bool is_a = s < SA;
-    const int row = srow + 32 * (is_a ? s : s - SA);
+    const int idx = is_a ? s : s - SA;
     const int lim = is_a ? rows_a : rows_b;
     const int64_t ld = is_a ? p.lda : p.ldb;
-    off[s] = row < lim ? (uint32_t)(row * ld * 2 + seg * 16) : kOob;
+    if (is_mn(s)) {
+      const int kr = 4 * (seg + 8 * ((idx >> 2) & 1)) + (idx & 3);  // k row within the slice
+      off[s] = (uint32_t)((kr * ld + srow * 8) * 2);
+    } else {
+      const int row = srow + 32 * idx;
+      off[s] = row < lim ? (uint32_t)(row * ld * 2 + seg * 16) : kOob;
+    }
   }
+  // MN-major operand: a buffer resource over the slice's k rows, clipped to
+  // the K rows left and, in the last row, to the tile's MN extent (reads
+  // past it return zeros; in earlier rows they only feed output rows or
+  // columns that are never stored).
+  auto mn_rsrc = [&](bool is_a, int slice) {
+    const int k0 = slice * kBK;
+    const int kr = K - k0 < kBK ? K - k0 : kBK;
+    const int64_t ld = is_a ? p.lda : p.ldb;
+    const int lim = is_a ? rows_a : rows_b;
+    const uint16_t* base = is_a ? p.A + z * p.sAz + m0 : p.B + z * p.sBz + n0;
+    const int nrec = kr > 0 ? (int)(((int64_t)(kr - 1) * ld + lim) * 2) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)(kr > 0 ? k0 : 0) * ld), (short)0, nrec,
+                                             kRsrcWord3);
+  };
   uint4 rs[NS];
   // Load slot s of K slice `slice` (past K: zeros).
   auto lslot = [&](int s, int slice) {
-    const int k0 = slice * kBK;
-    const uint32_t o = (k0 + seg * 8 < K) ? off[s] + (uint32_t)k0 * 2u : kOob;
-    rs[s] = buf_load16(s < SA ? ra_rs : rb_rs, o);
+    if (is_mn(s)) {
+      rs[s] = buf_load16(mn_rsrc(s < SA, slice), off[s]);
+    } else {
+      const int k0 = slice * kBK;
+      const uint32_t o = (k0 + seg * 8 < K) ? off[s] + (uint32_t)k0 * 2u : kOob;
+      rs[s] = buf_load16(s < SA ? ra_rs : rb_rs, o);
+    }
+  };
+  // MN-major group at slots s0 .. s0+3 (4 k rows of 8 MN values each) ->
+  // 8 MN rows of 4 k values: slot s0 + q then holds MN rows 2q and 2q + 1.
+  auto transpose_group = [&](int s0) {
+    if (!is_mn(s0)) return;
+    uint4 t[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * q + h;  // MN index within the block
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const uint32_t lo = dword_of(rs[s0 + 2 * pr], c >> 1), hi = dword_of(rs[s0 + 2 * pr + 1], c >> 1);
+          w[2 * h + pr] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+        }
+      }
+      t[q] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rs[s0 + q] = t[q];
   };
   // Write slot s into LDS stage st.
   auto wslot = [&](int s, int st) {
-    const int row = (s < SA ? 0 : BM) + srow + 32 * (s < SA ? s : s - SA);
-    smem[st][row * 8 + pseg] = rs[s];
+    const bool is_a = s < SA;
+    const int idx = is_a ? s : s - SA;
+    if (is_mn(s)) {
+      const int kq = seg + 8 * ((idx >> 2) & 1);
+      uint2* sm2 = reinterpret_cast<uint2*>(smem[st]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = srow * 8 + 2 * (idx & 3) + h;  // MN index within the tile
+        const int at = ((is_a ? 0 : BM) + row) * 8 + ((kq >> 1) ^ ((row >> 1) & 7));
+        sm2[at * 2 + (kq & 1)] = h ? make_uint2(rs[s].z, rs[s].w) : make_uint2(rs[s].x, rs[s].y);
+      }
+    } else {
+      const int row = (is_a ? 0 : BM) + srow + 32 * idx;
+      smem[st][row * 8 + pseg] = rs[s];
+    }
   };
   // Fragments of one 16-wide K step: lane l reads row l%32 of each 32-row
   // MFMA tile, 8 consecutive k at 8*(l/32) (swizzled segment).
@@ -217,6 +288,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
       const int i = x / TN, j = x % TN;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b[j]),
                                                            __builtin_bit_cast(bf16x8_t, a[i]), acc[i][j], 0, 0, 0);
+      if (x == 1) transpose_group(s0);
       if (x % 4 == 1) {
         wslot(s0 + x / 4, wst);
         lslot(s0 + x / 4, slice);
@@ -237,9 +309,12 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) lslot(s, 0);
 #pragma unroll
+  for (int s0 = 0; s0 < NS; s0 += 4) transpose_group(s0);
+#pragma unroll
   for (int s = 0; s < NS; ++s) wslot(s, 0);
 #pragma unroll
   for (int s = 0; s < NS; ++s) lslot(s, 1);
+  transpose_group(0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     wslot(s, 1);
@@ -416,7 +491,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, int OPS = kOpsKK>
 static hipError_t launch_gemm(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                               int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, int M, int N, int K,
                               int batch, int xcd_order, hipStream_t s, const uint16_t* aux = nullptr,
@@ -424,7 +499,7 @@ static hipError_t launch_gemm(const uint16_t* A, int64_t lda, int64_t sAz, const
   GemmArgs p{A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, (M + BM - 1) / BM, (N + BN - 1) / BN, batch,
              xcd_order, aux, pre};
   const int64_t total = (int64_t)p.tiles_m * p.tiles_n * batch;
-  hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EPI>), dim3((unsigned)total), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EPI, OPS>), dim3((unsigned)total), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -483,27 +558,54 @@ hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t*
   return launch_gemm<kBM, kBN, kEpiGelu>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
 }
 
+// Whether an MN-major operand fits the kernel's 32-bit slice offsets and
+// 16-byte loads (see the kernel's requirements).
+static bool mn_operand_ok(int64_t ld, int64_t sz, int64_t extent) {
+  return ld % 8 == 0 && sz % 8 == 0 && extent % 8 == 0 && 63 * ld + 256 < ((int64_t)1 << 30);
+}
+
+static bool ops_ok(int ops, int64_t lda, int64_t sAz, int M, int64_t ldb, int64_t sBz, int N, int K) {
+  if ((ops & kOpsAmn) && !mn_operand_ok(lda, sAz, M)) return false;
+  if ((ops & kOpsBmn) && !mn_operand_ok(ldb, sBz, N)) return false;
+  if (ops != kOpsMnMn && K % 8 != 0) return false;  // a K-contiguous operand reads 16-byte K segments
+  return N % 8 == 0;
+}
+
 // bf16 C = (A . B^T) * GELU'(aux) per batch index z, aux laid out like C
-// (the gradient through the experts' hidden activation).
+// (the gradient through the experts' hidden activation); B MN-major.
 hipError_t launch_gemm_gelu_grad_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                       int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, const uint16_t* aux, int M,
                                       int N, int K, int batch, hipStream_t s) {
-  return launch_gemm<kBM, kBN, kEpiGeluGrad>(A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, batch, /*xcd_order=*/1,
-                                             s, aux);
+  if (!ops_ok(kOpsBmn, lda, sAz, M, ldb, sBz, N, K)) return hipErrorInvalidValue;
+  return launch_gemm<kBM, kBN, kEpiGeluGrad, kOpsBmn>(A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, batch,
+                                                      /*xcd_order=*/1, s, aux);
+}
+
+template <int OPS>
+static hipError_t launch_f32(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb, int64_t sBz,
+                             float* C, int64_t ldc, int64_t sCz, int M, int N, int K, int batch, hipStream_t s) {
+  // Rows 16 KB or more apart: stage through LDS and write whole row segments.
+  if (ldc * 4 >= kStagedMinRowBytes)
+    return launch_gemm<kBM, kBN, kEpiF32Staged, OPS>(A, lda, sAz, B, ldb, sBz, reinterpret_cast<uint16_t*>(C), ldc,
+                                                     sCz, M, N, K, batch, /*xcd_order=*/1, s);
+  return launch_gemm<kBM, kBN, kEpiF32, OPS>(A, lda, sAz, B, ldb, sBz, reinterpret_cast<uint16_t*>(C), ldc, sCz, M,
+                                             N, K, batch, /*xcd_order=*/1, s);
 }
 
 // fp32 C = A . B^T per batch index z (split-K partial sums of the MoLE
-// block's down-projection: z selects a K range through sAz and sBz).
-// C rows of ldc floats; needs 256 * ldc * 4 < 2^31.
+// block's down-projection: z selects a K range through sAz and sBz; the
+// training gradients, with MN-major operands).  C rows of ldc floats; needs
+// 256 * ldc * 4 < 2^31.
 hipError_t launch_gemm_f32_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                 int64_t sBz, float* C, int64_t ldc, int64_t sCz, int M, int N, int K, int batch,
-                                hipStream_t s) {
-  // Rows 16 KB or more apart: stage through LDS and write whole row segments.
-  if (ldc * 4 >= kStagedMinRowBytes)
-    return launch_gemm<kBM, kBN, kEpiF32Staged>(A, lda, sAz, B, ldb, sBz, reinterpret_cast<uint16_t*>(C), ldc, sCz,
-                                                M, N, K, batch, /*xcd_order=*/1, s);
-  return launch_gemm<kBM, kBN, kEpiF32>(A, lda, sAz, B, ldb, sBz, reinterpret_cast<uint16_t*>(C), ldc, sCz, M, N, K,
-                                        batch, /*xcd_order=*/1, s);
+                                hipStream_t s, int ops) {
+  if (!ops_ok(ops, lda, sAz, M, ldb, sBz, N, K)) return hipErrorInvalidValue;
+  switch (ops) {
+    case kOpsKK: return launch_f32<kOpsKK>(A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, batch, s);
+    case kOpsBmn: return launch_f32<kOpsBmn>(A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, batch, s);
+    case kOpsMnMn: return launch_f32<kOpsMnMn>(A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, batch, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -52,23 +52,25 @@ constexpr int64_t kBuildF32MaxLds = 16384;  // D + F floats staged in LDS by the
 hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
                                  int64_t ldc, int M, int N, int K, hipStream_t s);
 
+// GEMM operand storage (bit 0 for A, bit 1 for B): K-contiguous, A[m][k] at
+// A[m*lda + k] (the default), or MN-major, A[m][k] at A[k*lda + m] (a
+// transposed matrix read in place).
+enum { kOpsKK = 0, kOpsAmn = 1, kOpsBmn = 2, kOpsMnMn = 3 };
 hipError_t launch_gemm_gelu_grad_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                       int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, const uint16_t* aux, int M,
                                       int N, int K, int batch, hipStream_t s);
 hipError_t launch_gemm_f32_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                 int64_t sBz, float* C, int64_t ldc, int64_t sCz, int M, int N, int K, int batch,
-                                hipStream_t s);
+                                hipStream_t s, int ops = kOpsKK);
 
 // train.hip: training-mode forward and backward
 struct TrainPlan {
-  int64_t up;            // U rounded up to a multiple of 8 (K of the transposed products)
   int dx_splits;         // K splits of the embedding-row gradient product
   // forward state (kept by the caller between the two calls)
   size_t x_off, g_off, u_off, o_off, fwd_total;
   // backward scratch (a second workspace); pwr_off also holds the row
   // gradients' partial sums (used after the router-weight sums are done)
-  size_t gate_off, dz_off, do_off, dot_off, du_off, dut_off, gt_off, xt_off, wdt_off, wut_off, pdx_off, pwr_off,
-      bwd_total;
+  size_t gate_off, dz_off, do_off, du_off, pdx_off, pwr_off, bwd_total;
   int wr_chunks;         // token chunks of the router-weight gradient
   int seg;               // token-list positions per row-gradient chunk
   int64_t nseg;          // row-gradient chunks, ceil(T / seg)

@@ -21,14 +21,15 @@
 //   experts:     dU_e = (dO_e . W_down[e]) * GELU'(X . W_up^T)   (one GEMM epilogue)
 //                d_W_down[e] = dO_e^T . G_e,  d_W_up[e] = dU_e^T . X,
 //                d_X = dU . W_up  (= the gradient of the rows Emb[uniq])
-// The five products run on the 256x256 MFMA GEMM (C = A . B^T with both
-// operands K-contiguous, fp32 output); products whose contraction runs over
-// rows (U) or over the weights' output dimension take LDS-tiled transposed
-// copies of their operands.  dO, dU and the pre-activations are rounded to
-// bf16 for the matrix cores; all sums are fp32.  The per-row gradient sums
-// walk a host-built list of the tokens grouped by row in fixed chunks and
-// add the pieces of rows that cross chunks in chunk order, so no atomics and
-// the result does not depend on scheduling.
+// The four products run on the 256x256 MFMA GEMM (C = A . B^T, fp32 or
+// fused-epilogue output); operands whose contraction index is not the
+// contiguous one (the rows U, or the weights' output dimension) are read in
+// place as MN-major operands and transposed in registers on their way to
+// LDS.  dO, dU and the pre-activations are rounded to bf16 for the matrix
+// cores; all sums are fp32.  The per-row gradient sums walk a host-built
+// list of the tokens grouped by row in fixed chunks and add the pieces of
+// rows that cross chunks in chunk order, so no atomics and the result does
+// not depend on scheduling.
 #include <algorithm>
 
 #include "mole_device.hpp"
@@ -38,7 +39,6 @@ namespace mole {
 
 namespace {
 
-constexpr int kTile = 64;      // transpose tile edge
 constexpr int kWrChunk = 16;   // tokens per partial sum of the router-weight gradient
 constexpr int kMaxSeg = 64;    // most token-list positions per row-gradient chunk
 
@@ -92,48 +92,6 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
   uint16_t* dst = X + u * D;
   for (int c = threadIdx.x; c < D / 8; c += 256)
     reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
-}
-
-// out[b][c][r] = in[b][r][c] for r < R (zero for R <= r < Rpad), c < C; bf16.
-// Needs C, Rpad, ld_in, ld_out, bs_in, bs_out multiples of 8 (16-byte rows of
-// 8 elements both ways).  A 64 x 64 tile goes through LDS: 16-byte loads
-// along c, 16-byte stores along r, each assembled from 8 LDS reads.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ in, int64_t ld_in,
-                                                        int64_t bs_in, uint16_t* __restrict__ out, int64_t ld_out,
-                                                        int64_t bs_out, int R, int C, int Rpad) {
-  __shared__ uint16_t tile[kTile][kTile + 8];  // row pitch 144 bytes
-  const int r0 = blockIdx.x * kTile, c0 = blockIdx.y * kTile;
-  const int64_t b = blockIdx.z;
-  const uint16_t* src = in + b * bs_in;
-  uint16_t* dst = out + b * bs_out;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = tid + 256 * k;            // 512 16-byte pieces: row q / 8, column group q % 8
-    const int i = q >> 3, cg = (q & 7) * 8;
-    const int r = r0 + i, c = c0 + cg;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * ld_in + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tile[i][cg + 2 * j] = (uint16_t)(w[j] & 0xFFFFu);
-      tile[i][cg + 2 * j + 1] = (uint16_t)(w[j] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = tid + 256 * k;            // output row c0 + q / 8, rows r0 + (q % 8) * 8 .. + 7
-    const int i = q >> 3, rg = (q & 7) * 8;
-    const int c = c0 + i, r = r0 + rg;
-    if (c < C && r < Rpad) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = (uint32_t)tile[rg + 2 * j][i] | ((uint32_t)tile[rg + 2 * j + 1][i] << 16);
-      *reinterpret_cast<uint4*>(dst + (int64_t)c * ld_out + r) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
 }
 
 // Per token t (one wavefront, 8 consecutive columns per lane and trip):
@@ -399,14 +357,6 @@ unsigned grid_for(int64_t n) {
   return (unsigned)std::max<int64_t>(1, std::min<int64_t>(b, 8192));
 }
 
-hipError_t transpose(const uint16_t* in, int64_t ld_in, int64_t bs_in, uint16_t* out, int64_t ld_out, int64_t bs_out,
-                     int64_t R, int64_t C, int64_t Rpad, int64_t batch, hipStream_t s) {
-  const dim3 grid((unsigned)((Rpad + kTile - 1) / kTile), (unsigned)((C + kTile - 1) / kTile), (unsigned)batch);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, in, ld_in, bs_in, out, ld_out, bs_out, (int)R, (int)C,
-                     (int)Rpad);
-  return hipGetLastError();
-}
-
 int next_pow2_int(int n) {
   int p = 1;
   while (p < n) p <<= 1;
@@ -431,7 +381,6 @@ int next_pow2_int(int n) {
 TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N) {
   TrainPlan p{};
   const int64_t NF = N * F;
-  p.up = std::max<int64_t>(8, (U + 7) / 8 * 8);
   // K splits of d_X = dU . W_up (K = N*F): enough 256x256 tiles to fill the
   // chip, each split a multiple of 8 of K.
   const int64_t tiles = ((U + 255) / 256) * ((D + 255) / 256);
@@ -452,13 +401,7 @@ TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N) {
   p.gate_off = o; o += round256((size_t)T * N * 4);
   p.dz_off = o; o += round256((size_t)T * N * 4);
   p.do_off = o; o += round256((size_t)U * N * D * 2);
-  p.dot_off = o; o += round256((size_t)N * D * p.up * 2);
   p.du_off = o; o += round256((size_t)U * NF * 2);
-  p.dut_off = o; o += round256((size_t)NF * p.up * 2);
-  p.gt_off = o; o += round256((size_t)NF * p.up * 2);
-  p.xt_off = o; o += round256((size_t)D * p.up * 2);
-  p.wdt_off = o; o += round256((size_t)NF * D * 2);
-  p.wut_off = o; o += round256((size_t)D * NF * 2);
   p.pdx_off = o; o += round256((size_t)p.dx_splits * U * D * 4);
   p.pwr_off = o; o += round256((size_t)std::max<int64_t>(p.wr_chunks, 2 * p.nseg) * N * D * 4);
   p.bwd_total = o;
@@ -494,7 +437,7 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
   (void)emb;
   if (T == 0) return hipSuccess;
   const TrainPlan p = train_plan(T, U, D, F, N);
-  const int64_t NF = N * F, Up = p.up;
+  const int64_t NF = N * F;
   const char* fb = static_cast<const char*>(fwd);
   const uint16_t* X = reinterpret_cast<const uint16_t*>(fb + p.x_off);
   const uint16_t* G = reinterpret_cast<const uint16_t*>(fb + p.g_off);
@@ -504,13 +447,7 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
   float* gate = reinterpret_cast<float*>(bb + p.gate_off);
   float* dz = reinterpret_cast<float*>(bb + p.dz_off);
   uint16_t* dO = reinterpret_cast<uint16_t*>(bb + p.do_off);
-  uint16_t* dOT = reinterpret_cast<uint16_t*>(bb + p.dot_off);
   uint16_t* dU = reinterpret_cast<uint16_t*>(bb + p.du_off);
-  uint16_t* dUT = reinterpret_cast<uint16_t*>(bb + p.dut_off);
-  uint16_t* GT = reinterpret_cast<uint16_t*>(bb + p.gt_off);
-  uint16_t* XT = reinterpret_cast<uint16_t*>(bb + p.xt_off);
-  uint16_t* WdT = reinterpret_cast<uint16_t*>(bb + p.wdt_off);
-  uint16_t* WuT = reinterpret_cast<uint16_t*>(bb + p.wut_off);
   float* Pdx = reinterpret_cast<float*>(bb + p.pdx_off);
   float* Pwr = reinterpret_cast<float*>(bb + p.pwr_off);
   const int NP = next_pow2_int((int)N);
@@ -542,24 +479,20 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
                        (const float*)Pwr, remap, row_ptr, tok, dO, T, p.seg, N * D);
     MOLE_TRY(hipGetLastError());
   }
-  // Transposed operands: dO_e^T [D][Up], G_e^T [F][Up], X^T [D][Up],
-  // W_down[e]^T [F][D], W_up^T [D][N*F].
-  MOLE_TRY(transpose(dO, N * D, D, dOT, Up, D * Up, U, D, Up, N, s));
-  MOLE_TRY(transpose(G, NF, F, GT, Up, F * Up, U, F, Up, N, s));
-  MOLE_TRY(transpose(X, D, 0, XT, Up, 0, U, D, Up, 1, s));
-  MOLE_TRY(transpose(w_down, F, D * F, WdT, D, F * D, D, F, D, N, s));
-  MOLE_TRY(transpose(w_up, D, 0, WuT, NF, 0, NF, D, NF, 1, s));
-  // dU = (dO_e . W_down[e]) * GELU'(u) in one GEMM epilogue (u kept by the forward pass).
-  MOLE_TRY(launch_gemm_gelu_grad_bf16(dO, N * D, D, WdT, D, F * D, dU, NF, F, Upre, (int)U, (int)F, (int)D, (int)N,
-                                      s));
-  MOLE_TRY(transpose(dU, NF, F, dUT, Up, F * Up, U, F, Up, N, s));
-  // Weight gradients: d_W_down[e] = dO_e^T . G_e, d_W_up[e] = dU_e^T . X.
-  MOLE_TRY(launch_gemm_f32_bf16(dOT, Up, D * Up, GT, Up, F * Up, d_w_down, F, D * F, (int)D, (int)F, (int)Up, (int)N,
-                                s));
-  MOLE_TRY(launch_gemm_f32_bf16(dUT, Up, F * Up, XT, Up, 0, d_w_up, D, F * D, (int)F, (int)D, (int)Up, (int)N, s));
-  // Embedding rows: d_X = dU . W_up over K = N*F, in equal K splits.
+  // dU = (dO_e . W_down[e]) * GELU'(u) in one GEMM epilogue (u kept by the
+  // forward pass); W_down[e] is [D][F], read MN-major.
+  MOLE_TRY(launch_gemm_gelu_grad_bf16(dO, N * D, D, w_down, F, D * F, dU, NF, F, Upre, (int)U, (int)F, (int)D,
+                                      (int)N, s));
+  // Weight gradients, contracted over the U rows with both operands read
+  // MN-major: d_W_down[e] = dO_e^T . G_e, d_W_up[e] = dU_e^T . X.
+  MOLE_TRY(launch_gemm_f32_bf16(dO, N * D, D, G, NF, F, d_w_down, F, D * F, (int)D, (int)F, (int)U, (int)N, s,
+                                kOpsMnMn));
+  MOLE_TRY(launch_gemm_f32_bf16(dU, NF, F, X, D, 0, d_w_up, D, F * D, (int)F, (int)D, (int)U, (int)N, s, kOpsMnMn));
+  // Embedding rows: d_X = dU . W_up over K = N*F in equal K splits, W_up
+  // ([N*F][D]) read MN-major.
   const int64_t ks = NF / p.dx_splits;
-  MOLE_TRY(launch_gemm_f32_bf16(dU, NF, ks, WuT, NF, ks, Pdx, D, U * D, (int)U, (int)D, (int)ks, p.dx_splits, s));
+  MOLE_TRY(launch_gemm_f32_bf16(dU, NF, ks, w_up, D, ks * D, Pdx, D, U * D, (int)U, (int)D, (int)ks, p.dx_splits, s,
+                                kOpsBmn));
   hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(U * D)), dim3(256), 0, s, (const float*)Pdx, p.dx_splits,
                      U * D, d_x);
   return hipGetLastError();
