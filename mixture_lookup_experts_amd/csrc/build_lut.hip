@@ -192,15 +192,22 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   // the K rows left and, in the last row, to the tile's MN extent (reads
   // past it return zeros; in earlier rows they only feed output rows or
   // columns that are never stored).
+  // (Branch-free: a slice past K gets zero records; its base is never read.)
+  const uint16_t* mn_base_a = p.A + z * p.sAz + m0;
+  const uint16_t* mn_base_b = p.B + z * p.sBz + n0;
+  const int ld_a = (int)p.lda, ld_b = (int)p.ldb;
+  // The values are uniform; readfirstlane keeps them in scalar registers
+  // (otherwise the compiler wraps each load in a loop over distinct
+  // descriptors).
   auto mn_rsrc = [&](bool is_a, int slice) {
     const int k0 = slice * kBK;
-    const int kr = K - k0 < kBK ? K - k0 : kBK;
-    const int64_t ld = is_a ? p.lda : p.ldb;
-    const int lim = is_a ? rows_a : rows_b;
-    const uint16_t* base = is_a ? p.A + z * p.sAz + m0 : p.B + z * p.sBz + n0;
-    const int nrec = kr > 0 ? (int)(((int64_t)(kr - 1) * ld + lim) * 2) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)(kr > 0 ? k0 : 0) * ld), (short)0, nrec,
-                                             kRsrcWord3);
+    const int ld = is_a ? ld_a : ld_b;
+    const int kr = max(0, min(kBK, K - k0));  // k rows of the slice that exist
+    const int nrec = __builtin_amdgcn_readfirstlane(max(0, (kr - 1) * ld + (is_a ? rows_a : rows_b)) * 2);
+    const uint64_t addr = reinterpret_cast<uint64_t>((is_a ? mn_base_a : mn_base_b) + (int64_t)k0 * ld);
+    const uint64_t base = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, nrec, kRsrcWord3);
   };
   uint4 rs[NS];
   // Load slot s of K slice `slice` (past K: zeros).
@@ -227,7 +234,8 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
           const uint32_t lo = dword_of(rs[s0 + 2 * pr], c >> 1), hi = dword_of(rs[s0 + 2 * pr + 1], c >> 1);
-          w[2 * h + pr] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+          // one byte permute: half (c & 1) of lo below the same half of hi
+          w[2 * h + pr] = __builtin_amdgcn_perm(hi, lo, (c & 1) ? 0x07060302u : 0x05040100u);
         }
       }
       t[q] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -345,16 +353,32 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   const int rows_c = M - m0 < BM ? M - m0 : BM;
   const __amdgpu_buffer_rsrc_t rc_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.C + z * p.sCz + (int64_t)m0 * p.ldc), (short)0, (int)(rows_c * p.ldc * 2), kRsrcWord3);
+  // GELU-gradient epilogue: the u values of one row block of accumulators
+  // (4 consecutive columns per group, 8 bytes) are loaded while the
+  // previous block is stored; loading them between stores instead made
+  // every wait for u also wait for the earlier stores (one counter).
+  uint2 ub[2][EPI == kEpiGeluGrad ? TN : 1][4];
+  __amdgpu_buffer_rsrc_t ru_rs = rc_rs;
+  if constexpr (EPI == kEpiGeluGrad)
+    ru_rs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.aux + z * p.sCz + (int64_t)m0 * p.ldc), (short)0,
+                                              (int)(rows_c * p.ldc * 2), kRsrcWord3);
+  auto aux_load = [&](int i, uint2 (*dst)[4]) {
+    const int mr = wm * WM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
+        const uint32_t o = (mr < rows_c && n < N) ? (uint32_t)(mr * p.ldc * 2 + n * 2) : kOob;
+        dst[j][g] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ru_rs, (int)o, 0, 0));
+      }
+  };
   // (GELU or its gradient,) round to bf16, pack 4 consecutive columns into 8 bytes.
   auto packed = [&](int i, int j, int g, bool raw = false) {
     float v[4];
     if constexpr (EPI == kEpiGeluGrad) {
-      // u at the same (row, column) as this accumulator group, 8 bytes
-      const int mr = wm * WM + i * 32 + (lane & 31);
-      const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-      uint2 uw = make_uint2(0u, 0u);
-      if (mr < rows_c && n < N)
-        uw = *reinterpret_cast<const uint2*>(p.aux + z * p.sCz + (int64_t)(m0 + mr) * p.ldc + n);
+      // u at the same (row, column) as this accumulator group
+      const uint2 uw = ub[i & 1][j][g];
       const float uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] * gelu_grad_poly(uv[q]);
@@ -440,8 +464,13 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
     if constexpr (EPI == kEpiGeluPre)
       rp_rs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.pre + z * p.sCz + (int64_t)m0 * p.ldc), (short)0,
                                                 (int)(rows_c * p.ldc * 2), kRsrcWord3);
+    if constexpr (EPI == kEpiGeluGrad) aux_load(0, ub[0]);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      if constexpr (EPI == kEpiGeluGrad) {
+        if (i + 1 < TM) aux_load(i + 1, ub[(i + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const int mr = wm * WM + i * 32 + (lane & 31);  // row within the tile
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
@@ -577,8 +606,10 @@ hipError_t launch_gemm_gelu_grad_bf16(const uint16_t* A, int64_t lda, int64_t sA
                                       int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, const uint16_t* aux, int M,
                                       int N, int K, int batch, hipStream_t s) {
   if (!ops_ok(kOpsBmn, lda, sAz, M, ldb, sBz, N, K)) return hipErrorInvalidValue;
+  // Row-major tile order: measured 5-10 % faster than the XCD-banded order
+  // on the 1B-class shape (U = 465, F = 8192, D = 2048), even on 410M-class.
   return launch_gemm<kBM, kBN, kEpiGeluGrad, kOpsBmn>(A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, batch,
-                                                      /*xcd_order=*/1, s, aux);
+                                                      /*xcd_order=*/0, s, aux);
 }
 
 template <int OPS>
