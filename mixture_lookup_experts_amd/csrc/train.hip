@@ -62,6 +62,19 @@ __device__ __forceinline__ void load_cols(const float* p, float* v) {
 }
 
 template <int CPL>
+__device__ __forceinline__ void load_bf16_cols(const uint16_t* p, float* v) {
+  if constexpr (CPL == 4) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+  } else if constexpr (CPL == 2) {
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = bf16_lo(q); v[1] = bf16_hi(q);
+  } else {
+    v[0] = bf16_to_f32(*p);
+  }
+}
+
+template <int CPL>
 __device__ __forceinline__ void store_bf16_cols(uint16_t* p, const float* v) {
   if constexpr (CPL == 4)
     *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -94,11 +107,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
     reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
 }
 
-// Per token t (one wavefront, 8 consecutive columns per lane and trip):
-// router logits z_e = h_t . W_r[e] and dg_e = dy_t . O[remap_t][e] as lane
-// sums, a reduce-scatter across the wavefront, the 2N totals through LDS to
-// every lane, softmax and dz, then d_h[t] = sum_e dz_e W_r[e].
-template <int NP>
+// Per token t (wpt = 1, 2 or 4 wavefronts of a workgroup, each over its
+// share of the columns, 8 consecutive columns per lane and trip): router
+// logits z_e = h_t . W_r[e] and dg_e = dy_t . O[remap_t][e] as lane sums, a
+// reduce-scatter across each wavefront, the token's 2N totals summed from
+// LDS in wave order by every lane, softmax and dz, then
+// d_h[t] = sum_e dz_e W_r[e] over each wave's columns.
+template <int NP, int WPT>
 __global__ __launch_bounds__(256) void gate_backward_kernel(const uint16_t* __restrict__ h,
                                                             const uint16_t* __restrict__ w_r,
                                                             const uint16_t* __restrict__ O,
@@ -106,17 +121,21 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(const uint16_t* __re
                                                             const float* __restrict__ dy, float* __restrict__ g_out,
                                                             float* __restrict__ dz_out, float* __restrict__ d_h,
                                                             int64_t T, int D, int N) {
+  constexpr int wpt = WPT;
   using RS = ReduceScatter<2 * NP, kWave>;
   __shared__ float tot[4][2 * NP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t tw = (int64_t)blockIdx.x * 4 + wave;
+  const int slot = wave / wpt, part = wave - slot * wpt;  // token slot of the workgroup, column share
+  const int64_t tw = (int64_t)blockIdx.x * (4 / wpt) + slot;
   const bool valid = tw < T;
-  const int64_t t = valid ? tw : T - 1;  // a wave past the end recomputes the last token and stores nothing
+  const int64_t t = valid ? tw : T - 1;  // a slot past the end recomputes the last token and stores nothing
+  const int span = (D / 8 + wpt - 1) / wpt * 8;
+  const int c_lo = part * span, c_hi = min(D, c_lo + span);
   const uint16_t* orow = O + remap[t] * (int64_t)N * D;
   float v[2 * NP];  // z_e, then dg_e
 #pragma unroll
   for (int e = 0; e < 2 * NP; ++e) v[e] = 0.f;
-  for (int c = lane * 8; c < D; c += 512) {
+  for (int c = c_lo + lane * 8; c < c_hi; c += 512) {
     float hv[8], yv[8];
     Elem<uint16_t>::unpack(ldg16(h + t * D + c), hv);
     Elem<float>::unpack(ldg16(dy + t * D + c), yv);
@@ -146,8 +165,13 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(const uint16_t* __re
   float zmax = -INFINITY;
 #pragma unroll
   for (int e = 0; e < NP; ++e) {
-    zz[e] = tot[wave][e];
-    dd[e] = tot[wave][NP + e];
+    zz[e] = tot[slot * wpt][e];
+    dd[e] = tot[slot * wpt][NP + e];
+#pragma unroll
+    for (int w = 1; w < wpt; ++w) {
+      zz[e] += tot[slot * wpt + w][e];
+      dd[e] += tot[slot * wpt + w][NP + e];
+    }
     if (e < N) zmax = fmaxf(zmax, zz[e]);
   }
   // (every lane computes the same softmax; loops over the compile-time
@@ -173,11 +197,11 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(const uint16_t* __re
       my_dz = dd[e];
     }
   }
-  if (valid && lane < N) {
+  if (valid && part == 0 && lane < N) {
     g_out[t * N + lane] = my_g;
     dz_out[t * N + lane] = my_dz;
   }
-  for (int c = lane * 8; c < D; c += 512) {
+  for (int c = c_lo + lane * 8; c < c_hi; c += 512) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -198,28 +222,68 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(const uint16_t* __re
   }
 }
 
+template <int NP> constexpr auto gate_backward_kernel_w1 = gate_backward_kernel<NP, 1>;
+template <int NP> constexpr auto gate_backward_kernel_w2 = gate_backward_kernel<NP, 2>;
+template <int NP> constexpr auto gate_backward_kernel_w4 = gate_backward_kernel<NP, 4>;
+
 // Partial router-weight gradient over one chunk of tokens:
-// P[chunk][e][d] = sum_{t in chunk} dz[t][e] h[t][d].
+// P[chunk][e][d] = sum_{t in chunk} dz[t][e] h[t][d].  A workgroup owns
+// 64*CPL columns; its four wavefronts take every fourth token of the chunk
+// and their sums are added in wave order through LDS.
 template <int NP>
 __global__ __launch_bounds__(256) void wr_partial_kernel(const float* __restrict__ dz, const uint16_t* __restrict__ h,
                                                          float* __restrict__ P, int64_t T, int D, int N) {
-  const int d = blockIdx.x * 256 + threadIdx.x;
+  constexpr int CPL = RowGradCols<NP>::kCpl;
+  __shared__ float part[3][NP * CPL][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c0 = (blockIdx.x * 64 + lane) * CPL;
+  const bool ok = c0 < D;
+  const int cc = ok ? c0 : 0;  // in-bounds column for the loads of an idle lane
   const int64_t t0 = (int64_t)blockIdx.y * kWrChunk;
-  if (d >= D) return;
-  float acc[NP];
-#pragma unroll
-  for (int e = 0; e < NP; ++e) acc[e] = 0.f;
   const int64_t t1 = T - t0 < kWrChunk ? T : t0 + kWrChunk;
-  for (int64_t t = t0; t < t1; ++t) {
-    const float hv = bf16_to_f32(h[t * D + d]);
-#pragma unroll
-    for (int e = 0; e < NP; ++e)
-      if (e < N) acc[e] = fmaf(dz[t * N + e], hv, acc[e]);
-  }
-  float* out = P + (int64_t)blockIdx.y * N * D;
+  float acc[NP][CPL];
 #pragma unroll
   for (int e = 0; e < NP; ++e)
-    if (e < N) out[(int64_t)e * D + d] = acc[e];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[e][c] = 0.f;
+  for (int64_t t = t0 + wave; t < t1; t += 16) {
+    float hv[4][CPL];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_bf16_cols<CPL>(h + (t + 4 * q < t1 ? t + 4 * q : t1 - 1) * D + cc, hv[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (t + 4 * q < t1) {
+#pragma unroll
+        for (int e = 0; e < NP; ++e) {
+          if (e < N) {
+            const float ze = dz[(t + 4 * q) * N + e];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[e][c] = fmaf(ze, hv[q][c], acc[e][c]);
+          }
+        }
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < NP; ++e)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) part[wave - 1][e * CPL + c][lane] = acc[e][c];
+  }
+  __syncthreads();
+  if (wave == 0 && ok) {
+    float* out = P + (int64_t)blockIdx.y * N * D + c0;
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      if (e < N) {
+        float v[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+          v[c] = acc[e][c] + part[0][e * CPL + c][lane] + part[1][e * CPL + c][lane] + part[2][e * CPL + c][lane];
+        store_f32_cols<CPL>(out + (int64_t)e * D, v);
+      }
+    }
+  }
 }
 
 // Row gradients dO[u][e][d] = bf16( sum over the tokens t of row u of
@@ -268,13 +332,18 @@ __global__ __launch_bounds__(256) void row_grad_kernel(const float* __restrict__
   for (int e = 0; e < NP; ++e)
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[e][c] = 0.f;
-  for (int pb = 0; pb < len; pb += 4) {
-    float yv[4][CPL];
+  // Positions in batches of four, double-buffered: the next batch's dy rows
+  // are loaded (clamped to the chunk, so always in bounds) while this one
+  // is summed.
+  float ya[4][CPL], yb[4][CPL];
+  auto load4 = [&](int pb, float (*y)[CPL]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int pq = pb + q < len ? pb + q : len - 1;
-      load_cols<CPL>(dy + ts[pq] * D + c0, yv[q]);
+      load_cols<CPL>(dy + ts[pq] * D + c0, y[q]);
     }
+  };
+  auto walk4 = [&](int pb, float (*y)[CPL]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int pq = pb + q;
@@ -283,7 +352,7 @@ __global__ __launch_bounds__(256) void row_grad_kernel(const float* __restrict__
         for (int e = 0; e < NP; ++e) {
           const float ge = gs[pq][e];
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) acc[e][c] = fmaf(ge, yv[q][c], acc[e][c]);
+          for (int c = 0; c < CPL; ++c) acc[e][c] = fmaf(ge, y[q][c], acc[e][c]);
         }
         const int64_t r = rs[pq];
         if (rs[pq + 1] != r) {  // end of this row's run in the chunk
@@ -307,6 +376,13 @@ __global__ __launch_bounds__(256) void row_grad_kernel(const float* __restrict__
         }
       }
     }
+  };
+  load4(0, ya);
+  for (int pb = 0; pb < len; pb += 8) {
+    load4(pb + 4, yb);
+    walk4(pb, ya);
+    load4(pb + 8, ya);
+    walk4(pb + 4, yb);
   }
 }
 
@@ -325,16 +401,27 @@ __global__ __launch_bounds__(256) void row_grad_fix_kernel(const float* __restri
   if (!(k0 >= p0 && k1 > pend)) return;
   const int64_t jl = (k1 - 1) / seg;
   for (int64_t i = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4; i < ND; i += (int64_t)gridDim.y * 1024) {
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t jj = j; jj <= jl; ++jj) {
-      const int slot = k0 <= jj * seg ? 0 : 1;
-      const float4 q = *reinterpret_cast<const float4*>(part + (jj * 2 + slot) * ND + i);
-      a[0] += q.x;
-      a[1] += q.y;
-      a[2] += q.z;
-      a[3] += q.w;
+    // chunks j, j+1, ... in four interleaved chains (a head row touches
+    // dozens of chunks), added in chain order at the end
+    float4 a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t jj = j; jj <= jl; jj += 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (jj + q <= jl) {
+          const int slot = k0 <= (jj + q) * seg ? 0 : 1;
+          const float4 x = *reinterpret_cast<const float4*>(part + ((jj + q) * 2 + slot) * ND + i);
+          a[q].x += x.x;
+          a[q].y += x.y;
+          a[q].z += x.z;
+          a[q].w += x.w;
+        }
+      }
     }
-    *reinterpret_cast<uint2*>(dO + r * ND + i) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    const float s0 = (a[0].x + a[1].x) + (a[2].x + a[3].x), s1 = (a[0].y + a[1].y) + (a[2].y + a[3].y);
+    const float s2 = (a[0].z + a[1].z) + (a[2].z + a[3].z), s3 = (a[0].w + a[1].w) + (a[2].w + a[3].w);
+    *reinterpret_cast<uint2*>(dO + r * ND + i) = make_uint2(pack_bf16x2(s0, s1), pack_bf16x2(s2, s3));
   }
 }
 
@@ -349,6 +436,42 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* __restri
       for (int q = 0; q < 4; ++q) a[q] += P[(int64_t)(sp + q) * count + i];
     for (; sp < S; ++sp) a[0] += P[(int64_t)sp * count + i];
     out[i] = (a[0] + a[1]) + (a[2] + a[3]);
+  }
+}
+
+// out[i] = sum_s P[s][i] for many partials (S > 16): a workgroup of 16
+// wavefronts owns 256 outputs (a float4 per lane); wavefront r sums the
+// partials s = r, r + 16, ... and the 16 sums are added in r order in LDS.
+// Needs count % 4 == 0.
+__global__ __launch_bounds__(1024) void sum_partials_wide_kernel(const float* __restrict__ P, int S, int64_t count,
+                                                                 float* __restrict__ out) {
+  __shared__ float4 red[16][64];
+  const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int64_t i = ((int64_t)blockIdx.x * 64 + lane) * 4;
+  const bool ok = i < count;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;  // two chains
+  int sp = r;
+  for (; sp + 16 < S; sp += 32) {
+    if (ok) {
+      const float4 x = *reinterpret_cast<const float4*>(P + (int64_t)sp * count + i);
+      const float4 y = *reinterpret_cast<const float4*>(P + (int64_t)(sp + 16) * count + i);
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+    }
+  }
+  if (sp < S && ok) {
+    const float4 x = *reinterpret_cast<const float4*>(P + (int64_t)sp * count + i);
+    a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+  }
+  red[r][lane] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+  __syncthreads();
+  if (r == 0 && ok) {
+    float4 t = red[0][lane];
+    for (int k = 1; k < 16; ++k) {
+      const float4 x = red[k][lane];
+      t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
+    }
+    *reinterpret_cast<float4*>(out + i) = t;
   }
 }
 
@@ -387,9 +510,9 @@ TrainPlan train_plan(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N) {
   p.dx_splits = 1;
   while (p.dx_splits < 16 && tiles * p.dx_splits < 256 && NF % (16 * p.dx_splits) == 0) p.dx_splits *= 2;
   p.wr_chunks = (int)((T + kWrChunk - 1) / kWrChunk);
-  // Row-gradient chunks: about 128 of them (a power-of-two size in [4, 64]).
+  // Row-gradient chunks: about 256 of them (a power-of-two size in [4, 64]).
   p.seg = 4;
-  while (p.seg < kMaxSeg && (int64_t)p.seg * 128 < T) p.seg *= 2;
+  while (p.seg < kMaxSeg && (int64_t)p.seg * 256 < T) p.seg *= 2;
   p.nseg = (T + p.seg - 1) / p.seg;
   size_t o = 0;
   p.x_off = o; o += round256((size_t)U * D * 2);
@@ -455,15 +578,34 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
 #define MOLE_TRY(x) do { err = (x); if (err != hipSuccess) return err; } while (0)
 
   // Gates: g, dz, d_h.
-  MOLE_NP_SWITCH(gate_backward_kernel, dim3((unsigned)((T + 3) / 4)), s, h, w_r, O, remap, dy, gate, dz, d_h, T,
-                 (int)D, (int)N);
+  // Waves per token: up to 4 while the batch has fewer than 4096 tokens
+  // and each wave keeps at least 256 columns.
+  int wpt = 1;
+  while (wpt < 4 && T * wpt < 4096 && D / (2 * wpt) >= 256) wpt *= 2;
+  {
+    const dim3 grid((unsigned)((T + 4 / wpt - 1) / (4 / wpt)));
+    if (wpt == 4) {
+      MOLE_NP_SWITCH(gate_backward_kernel_w4, grid, s, h, w_r, O, remap, dy, gate, dz, d_h, T, (int)D, (int)N);
+    } else if (wpt == 2) {
+      MOLE_NP_SWITCH(gate_backward_kernel_w2, grid, s, h, w_r, O, remap, dy, gate, dz, d_h, T, (int)D, (int)N);
+    } else {
+      MOLE_NP_SWITCH(gate_backward_kernel_w1, grid, s, h, w_r, O, remap, dy, gate, dz, d_h, T, (int)D, (int)N);
+    }
+  }
   MOLE_TRY(hipGetLastError());
   // Router weights: chunked partial sums over tokens, then their sum.
-  MOLE_NP_SWITCH(wr_partial_kernel, dim3((unsigned)((D + 255) / 256), (unsigned)p.wr_chunks), s, (const float*)dz,
-                 h, Pwr, T, (int)D, (int)N);
+  {
+    const int cpl = NP >= 64 ? 1 : (NP >= 32 ? 2 : 4);
+    MOLE_NP_SWITCH(wr_partial_kernel, dim3((unsigned)((D + 64 * cpl - 1) / (64 * cpl)), (unsigned)p.wr_chunks), s,
+                   (const float*)dz, h, Pwr, T, (int)D, (int)N);
+  }
   MOLE_TRY(hipGetLastError());
-  hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(N * D)), dim3(256), 0, s, (const float*)Pwr, p.wr_chunks,
-                     N * D, d_w_r);
+  if (p.wr_chunks > 16)
+    hipLaunchKernelGGL(sum_partials_wide_kernel, dim3((unsigned)((N * D + 255) / 256)), dim3(1024), 0, s,
+                       (const float*)Pwr, p.wr_chunks, N * D, d_w_r);
+  else
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(grid_for(N * D)), dim3(256), 0, s, (const float*)Pwr, p.wr_chunks,
+                       N * D, d_w_r);
   MOLE_TRY(hipGetLastError());
   // Gradient of the batch's table rows, dO[u][e] = sum_t g_te dy_t, by
   // chunks of the token list (partials of cut rows in the router-weight
