@@ -778,10 +778,11 @@ def run_train(ids, emb, w_up, w_down, h, w_r, dy):
 # (V, N, D, F, T, zipf): ragged D/F/T, repeated ids (several tokens per row),
 # many experts, a 160M-class width, and long Zipf batches whose head rows run
 # over many chunks of the row-gradient walk (64-position chunks at T = 5000;
-# 32 experts take its two-columns-per-lane form).
+# 32 experts take its two-columns-per-lane form), D = 1024 (four wavefronts
+# per token in the gate backward) and a single token with one expert.
 TRAIN_CASES = [(300, 4, 128, 256, 100, False), (50, 3, 136, 200, 37, True), (400, 16, 256, 512, 64, True),
                (40, 64, 64, 64, 20, False), (2000, 4, 768, 3072, 32, True), (500, 16, 64, 64, 5000, True),
-               (300, 32, 64, 128, 700, True)]
+               (300, 32, 64, 128, 700, True), (100, 4, 1024, 256, 64, True), (10, 1, 64, 64, 1, False)]
 
 
 @pytest.mark.parametrize("V,N,D,F,T,zipf", TRAIN_CASES)
@@ -793,6 +794,21 @@ def test_train_forward_and_backward_match_oracle(V, N, D, F, T, zipf):
     ref = oracle.train_backward(ids, emb, w_up, w_down, h, w_r, dy.astype(np.float64))
     for k in ("d_w_up", "d_w_down", "d_w_r", "d_h"):
         assert np.all(np.isfinite(grads[k])), k
+        assert rel_l2(grads[k], ref[k]) <= TRAIN_TOL, (k, rel_l2(grads[k], ref[k]))
+    assert rel_l2(grads["d_x"], ref["d_emb"][uniq]) <= TRAIN_TOL
+
+
+def test_train_one_row_for_every_token():
+    """Every token has the same id: one row of the table receives all T
+    tokens' gradients, through every chunk of the row-gradient walk."""
+    V, N, D, F, T = 30, 4, 64, 128, 700
+    ids, emb, w_up, w_down, h, w_r, dy = train_case(5, V, D, F, N, T)
+    ids[:] = 7
+    y, grads, uniq = run_train(ids, emb, w_up, w_down, h, w_r, dy)
+    assert uniq.tolist() == [7]
+    assert rel_l2(y, oracle.train_forward(ids, emb, w_up, w_down, h, w_r)) <= TRAIN_TOL
+    ref = oracle.train_backward(ids, emb, w_up, w_down, h, w_r, dy.astype(np.float64))
+    for k in ("d_w_up", "d_w_down", "d_w_r", "d_h"):
         assert rel_l2(grads[k], ref[k]) <= TRAIN_TOL, (k, rel_l2(grads[k], ref[k]))
     assert rel_l2(grads["d_x"], ref["d_emb"][uniq]) <= TRAIN_TOL
 
