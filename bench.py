@@ -51,10 +51,10 @@ def parse():
                         "so gathered bytes = unique bytes)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget for the CPU-oracle baseline (0 disables it)")
-    p.add_argument("--probes", default="scale,decode,host,layer,train",
+    p.add_argument("--probes", default="scale,decode,host,disk,layer,train",
                    help="comma list of the extra measurements to run: scale (combine on the 410M-class "
                         "table), decode (1B-class 16-layer stack), host (host-resident NF3 stack), "
-                        "layer (the full MoLE block: shared FFN + lookup + residual), train (training-mode "
+                        "disk (NF3 table file, rows read per call), layer (the full MoLE block: shared FFN + lookup + residual), train (training-mode "
                         "forward and backward of the routed experts); not in the default "
                         "list: vendor_gemm (the vendor GEMM library, via torch.matmul, on the build's GEMM "
                         "shapes and two square ones, as a practical MFMA ceiling)")
@@ -276,6 +276,8 @@ def main():
         result["decode_stack_1b"] = decode_stack_probe(torch, mole, synth, dev, stream)
     if "host" in probes:
         result["host_stack_nf3"] = host_stack_probe(torch, mole, synth, dev, stream)
+    if "disk" in probes:
+        result["disk_nf3"] = disk_probe(torch, mole, synth, dev, stream)
     if "layer" in probes:
         result["layer_block"] = layer_probe(torch, mole, synth, dev, stream)
     if "train" in probes:
@@ -685,6 +687,92 @@ def host_stack_probe(torch, mole, synth, dev, stream):
     ctx.__exit__(None, None, None)
     del codes_h, scales_h, w_rs
     torch.cuda.empty_cache()
+    return out
+
+
+def _mount_of(path):
+    """(mount point, filesystem type) holding `path`, from /proc/mounts."""
+    best = ("/", "unknown")
+    try:
+        for line in open("/proc/mounts"):
+            parts = line.split()
+            mp, fs = parts[1], parts[2]
+            if (path == mp or path.startswith(mp.rstrip("/") + "/")) and len(mp) >= len(best[0]):
+                best = (mp, fs)
+    except OSError:
+        pass
+    return best
+
+
+def disk_probe(torch, mole, synth, dev, stream):
+    """The disk tier: one 410M-class NF3 table (V=50304 N=16 D=1024,
+    0.33 GB) written as a table file to the temporary directory, then
+    mole_lookup_combine_nf3_file at T = 256, 1024 and 4096 Zipf ids: the
+    distinct rows are read from the file (one positioned read each) into
+    pinned staging, copied to the device in one transfer and combined.
+    Timed per call (wall clock to the end of the combine) with the file in
+    the page cache, and after dropping the file's cached pages
+    (posix_fadvise DONTNEED) so the rows come from the device behind the
+    filesystem -- on a RAM-backed filesystem (tmpfs) the two are the same.
+    The table's code values do not change the cost."""
+    import tempfile
+    w = synth.WORKLOADS["410m-nf3"]
+    V, D, N = w.V, w.D, w.N
+    CB, SB = 3 * D // 8, D // 64
+    d = tempfile.mkdtemp(prefix="mole_disk_")
+    path = os.path.join(d, "table.molt")
+    out = {}
+    try:
+        t0 = time.perf_counter()
+        mole.mole_nf3_file_write(path, torch.zeros((V, N, CB), dtype=torch.uint8),
+                                 torch.zeros((V, N, SB), dtype=torch.int16))
+        mp, fs = _mount_of(os.path.realpath(d))
+        rec = N * (CB + 2 * SB)
+        out["workload"] = ("410M-class NF3 table file (V=50304 N=16 D=1024, %.2f GB, %d-byte records), %s "
+                           "filesystem at %s" % ((64 + V * rec) / 1e9, rec, fs, mp))
+        out["file_write_s"] = time.perf_counter() - t0
+        fd = os.open(path, os.O_RDONLY)
+        os.fsync(fd)  # written pages reach the device, so dropping them later works
+        g = torch.Generator(device=dev)
+        g.manual_seed(synth.seed(w, 85))
+        w_r = (torch.randn((N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        perm = synth.rank_permutation(w)
+        with torch.cuda.stream(stream):
+            for T in (256, 1024, 4096):
+                NB = 4
+                ids_l = [torch.from_numpy(synth.make_ids(w, T, step=s, perm=perm)) for s in range(NB)]
+                h = torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16)
+                y = torch.empty((T, D), dtype=torch.float32, device=dev)
+                nb = mole.mole_nf3_host_staging_size(T, N, D)
+                st_h = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+                st_d = torch.empty(nb, dtype=torch.uint8, device=dev)
+                res = {}
+                for mode in ("page_cache", "dropped"):
+                    times, uniq = [], []
+                    for r in range(2 + 6):
+                        if mode == "dropped":
+                            os.posix_fadvise(fd, 0, 0, os.POSIX_FADV_DONTNEED)
+                        torch.cuda.synchronize()
+                        t1 = time.perf_counter()
+                        U = mole.mole_lookup_combine_nf3_file(fd, ids_l[r % NB], h, w_r, V, st_h, st_d, y,
+                                                              stream=stream)
+                        torch.cuda.synchronize()
+                        if r >= 2:
+                            times.append(time.perf_counter() - t1)
+                            uniq.append(U)
+                    us = float(np.median(times)) * 1e6
+                    U = float(np.mean(uniq))
+                    res[mode] = {"us_per_call": us, "mean_unique_ids": U, "bytes_read": U * rec,
+                                 "read_gbs_effective": U * rec / (us * 1e-6) / 1e9, "tokens_per_s": T / (us * 1e-6)}
+                out["T%d" % T] = res
+                del st_h, st_d, h, y
+        os.close(fd)
+    finally:
+        try:
+            os.remove(path)
+            os.rmdir(d)
+        except OSError:
+            pass
     return out
 
 

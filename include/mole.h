@@ -50,6 +50,8 @@ extern "C" {
 #define MOLE_ERR_UNSUPPORTED (-6) /* a valid but unsupported shape (e.g. N > 256) */
 #define MOLE_ERR_HIP (-7)         /* a HIP runtime call or kernel launch failed */
 #define MOLE_ERR_ID (-8)          /* a host-side token id is outside [0, V) */
+#define MOLE_ERR_IO (-9)          /* a table file could not be read or written */
+#define MOLE_ERR_FORMAT (-10)     /* not a MoLE NF3 table file of this version */
 
 #define MOLE_F32 0
 #define MOLE_BF16 1
@@ -367,6 +369,59 @@ int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
                                  int64_t L, int64_t V, int64_t N, int64_t D, void* stage_host,
                                  void* stage_dev, size_t stage_bytes, size_t* codes_off,
                                  size_t* scales_off, int nthreads, int64_t* n_unique, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Disk tier: the NF3 table in a file (inference section: the table is kept
+ * in lower-tier storage and only the retrieved outputs are loaded into GPU
+ * memory; the offloading discussion names CPU memory and disk as such
+ * tiers).  The file holds one record per vocabulary row, so a token's row
+ * is one contiguous read:
+ *
+ *   bytes [0, 64): header, little-endian
+ *       char    magic[8]      "MOLENF3" and a zero byte
+ *       uint32  version       1
+ *       uint32  header_bytes  64
+ *       int64   V, N, D
+ *       int64   record_bytes  N*3D/8 + N*(D/64)*2
+ *       int64   data_offset   64
+ *       int64   reserved      0
+ *   record v at data_offset + v*record_bytes: the row's NF3 codes
+ *       [N][3D/8] (as mole_pack_nf3 writes codes[v]), then its fp16 scales
+ *       [N][D/64] (scales[v]).
+ *
+ * mole_nf3_file_write: host-only.  Creates (or truncates) `path` and writes
+ * the header and the V records from a packed table in host memory
+ * (codes_host [V][N][3D/8], scales_host [V][N][D/64]).  MOLE_ERR_IO if the
+ * file cannot be created or written.
+ *
+ * mole_nf3_file_shape: host-only.  Reads the header of the open file `fd`
+ * into *V, *N, *D.  MOLE_ERR_IO if it cannot be read, MOLE_ERR_FORMAT if it
+ * is not a version-1 table file.
+ *
+ * mole_gather_nf3_file: host-only.  As mole_gather_nf3_host, with the rows
+ * read from the open table file `fd` (one positioned read per distinct id,
+ * straight into the two staging sections; the caller's file offset is not
+ * used or moved).  MOLE_ERR_DIM if the header's V, N, D differ from the
+ * arguments; MOLE_ERR_IO on a failed or short read.
+ *
+ * mole_lookup_combine_nf3_file: as mole_lookup_combine_nf3_host, with the
+ * distinct rows read from the table file `fd` into the pinned staging area
+ * (same staging contract, mole_nf3_host_staging_size).  The reads happen on
+ * the calling thread before the copy is enqueued; y is written on `stream`.
+ * ------------------------------------------------------------------------ */
+int mole_nf3_file_write(const char* path, const uint8_t* codes_host, const uint16_t* scales_host,
+                        int64_t V, int64_t N, int64_t D);
+
+int mole_nf3_file_shape(int fd, int64_t* V, int64_t* N, int64_t* D);
+
+int mole_gather_nf3_file(int fd, const int64_t* ids_host, int64_t T, int64_t V, int64_t N,
+                         int64_t D, uint8_t* codes_stage_host, uint16_t* scales_stage_host,
+                         int64_t* remap_host, int64_t* n_unique, int nthreads);
+
+int mole_lookup_combine_nf3_file(int fd, const int64_t* ids_host, const void* h, const void* w_r,
+                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
+                                 int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                                 int nthreads, int64_t* n_unique, void* stream);
 
 #ifdef __cplusplus
 }

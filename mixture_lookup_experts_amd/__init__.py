@@ -35,6 +35,10 @@ from ._native import (  # noqa: F401
     mole_nf3_host_staging_size,
     mole_nf3_host_stack_staging_size,
     mole_prefetch_nf3_host_stack,
+    mole_gather_nf3_file,
+    mole_lookup_combine_nf3_file,
+    mole_nf3_file_shape,
+    mole_nf3_file_write,
     mole_nf3_levels,
     mole_pack_nf3,
     mole_status_string,
@@ -52,4 +56,5 @@ __all__ = [
     "mole_nf3_levels", "mole_status_string", "mole_layer_forward", "mole_layer_workspace_size",
     "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4", "mole_pack_int8", "mole_lookup_combine_int8",
     "mole_train_index", "mole_train_workspace_size", "mole_train_forward", "mole_train_backward",
+    "mole_nf3_file_write", "mole_nf3_file_shape", "mole_gather_nf3_file", "mole_lookup_combine_nf3_file",
 ]

@@ -83,6 +83,10 @@ def library():
             "mole_train_backward": (I, [P, P, P, P, P, P, P, P, P, SZ, P, SZ, P, P, P, P, P,
                                         I64, I64, I64, I64, I64, I64, I, P]),
             "mole_layer_forward": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]),
+            "mole_nf3_file_write": (I, [ctypes.c_char_p, P, P, I64, I64, I64]),
+            "mole_nf3_file_shape": (I, [I, P, P, P]),
+            "mole_gather_nf3_file": (I, [I, P, I64, I64, I64, I64, P, P, P, P, I]),
+            "mole_lookup_combine_nf3_file": (I, [I, P, P, P, P, P, SZ, P, I64, I64, I64, I64, I, I, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -302,6 +306,61 @@ def mole_lookup_combine_nf3_host(ids_host, h, w_r, codes_host, scales_host, stag
         _ptr(ids_host), _ptr(h), _ptr(w_r), _ptr(codes_host), _ptr(scales_host),
         _ptr(stage_host), _ptr(stage_dev), nbytes, _ptr(y), T, V, D, N, _dtype(h), nthreads,
         ctypes.addressof(u), _stream(stream)))
+    return int(u.value)
+
+
+def mole_nf3_file_write(path: str, codes_host, scales_host) -> None:
+    """Write a packed NF3 table (codes [V,N,3D/8] uint8, scales [V,N,D/64]
+    fp16 bits, host tensors) to `path` as a table file: a 64-byte header,
+    then one record (codes, then scales) per vocabulary row."""
+    V, N, CB = codes_host.shape
+    D = CB * 8 // 3
+    for t in (codes_host, scales_host):
+        _need(t.device.type == "cpu" and t.is_contiguous(), "host tensors, contiguous")
+    _need(tuple(scales_host.shape) == (V, N, D // 64), "scales [V,N,D/64]")
+    _check("mole_nf3_file_write", library().mole_nf3_file_write(
+        os.fsencode(path), _ptr(codes_host), _ptr(scales_host), V, N, D))
+
+
+def mole_nf3_file_shape(fd: int):
+    """(V, N, D) from the header of an open table file."""
+    V, N, D = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check("mole_nf3_file_shape", library().mole_nf3_file_shape(
+        int(fd), ctypes.addressof(V), ctypes.addressof(N), ctypes.addressof(D)))
+    return int(V.value), int(N.value), int(D.value)
+
+
+def mole_gather_nf3_file(fd: int, ids_host, V: int, N: int, D: int, codes_stage, scales_stage, remap,
+                         nthreads: int = 0) -> int:
+    """As mole_gather_nf3_host, with the rows read from the open table file
+    `fd`; returns the number of distinct ids U."""
+    T = ids_host.numel()
+    for t in (ids_host, codes_stage, scales_stage, remap):
+        _need(t.device.type == "cpu" and t.is_contiguous(), "host tensors, contiguous")
+    _need(codes_stage.numel() >= T * N * (3 * D // 8) and scales_stage.numel() >= T * N * (D // 64)
+          and remap.numel() >= T, "staging buffers hold at least T rows")
+    u = ctypes.c_int64(0)
+    _check("mole_gather_nf3_file", library().mole_gather_nf3_file(
+        int(fd), _ptr(ids_host), T, V, N, D, _ptr(codes_stage), _ptr(scales_stage), _ptr(remap),
+        ctypes.addressof(u), nthreads))
+    return int(u.value)
+
+
+def mole_lookup_combine_nf3_file(fd: int, ids_host, h, w_r, V: int, stage_host, stage_dev, y,
+                                 nthreads: int = 0, stream=None) -> int:
+    """Disk-resident NF3 table: read the requested rows from the open table
+    file `fd` into the pinned staging area, copy its used part to the device
+    buffer in one transfer and combine.  Returns U, the number of distinct
+    ids."""
+    T, D = h.shape
+    N = w_r.shape[0]
+    _need(tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D), "h [T,D], w_r [N,D], y [T,D]")
+    nbytes = stage_host.numel() * stage_host.element_size()
+    _need(stage_dev.numel() * stage_dev.element_size() >= nbytes, "device staging as large as the host one")
+    u = ctypes.c_int64(0)
+    _check("mole_lookup_combine_nf3_file", library().mole_lookup_combine_nf3_file(
+        int(fd), _ptr(ids_host), _ptr(h), _ptr(w_r), _ptr(stage_host), _ptr(stage_dev), nbytes, _ptr(y), T, V,
+        D, N, _dtype(h), nthreads, ctypes.addressof(u), _stream(stream)))
     return int(u.value)
 
 

@@ -3,9 +3,16 @@
 // include/mole.h.
 #include <hip/hip_runtime.h>
 
+#include <fcntl.h>
+#include <sys/uio.h>
+#include <unistd.h>
+
 #include <algorithm>
 #include <atomic>
+#include <cerrno>
+#include <condition_variable>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <thread>
 #include <unordered_map>
@@ -61,6 +68,87 @@ int dedupe(const int64_t* ids, int64_t T, int64_t V, std::vector<int64_t>& uniq,
   return MOLE_OK;
 }
 
+// Host worker threads for the gathers, created on first use and kept for
+// the life of the process (spawning a thread per worker and call cost
+// about 10 us each, more than a small batch's copies).  start(n, fn) runs
+// fn(0) .. fn(n-1) on n pool threads and returns at once; wait() returns
+// when all have finished.  One job at a time: a second caller's start()
+// blocks until the first caller's wait().
+class WorkerPool {
+ public:
+  static constexpr int kMaxWorkers = 64;
+  static WorkerPool& instance() {
+    static WorkerPool* p = new WorkerPool();  // never destroyed: its threads outlive static destructors
+    return *p;
+  }
+  void start(int n, std::function<void(int)> fn) {
+    job_mu_.lock();
+    std::unique_lock<std::mutex> lk(mu_);
+    while (nthreads_ < n) {
+      std::thread(&WorkerPool::loop, this).detach();
+      ++nthreads_;
+    }
+    fn_ = std::move(fn);
+    want_ = n;
+    claimed_ = 0;
+    pending_ = n;
+    ++gen_;
+    lk.unlock();
+    cv_.notify_all();
+  }
+  void wait() {
+    {
+      std::unique_lock<std::mutex> lk(mu_);
+      done_cv_.wait(lk, [&] { return pending_ == 0; });
+      fn_ = nullptr;
+    }
+    job_mu_.unlock();
+  }
+
+ private:
+  void loop() {
+    uint64_t seen = 0;
+    std::unique_lock<std::mutex> lk(mu_);
+    for (;;) {
+      cv_.wait(lk, [&] { return gen_ != seen; });
+      seen = gen_;
+      if (claimed_ >= want_) continue;  // this job needs fewer workers
+      const int idx = claimed_++;
+      std::function<void(int)>* fn = &fn_;
+      lk.unlock();
+      (*fn)(idx);  // fn_ is not replaced before pending_ reaches 0
+      lk.lock();
+      if (--pending_ == 0) done_cv_.notify_all();
+    }
+  }
+  std::mutex job_mu_, mu_;
+  std::condition_variable cv_, done_cv_;
+  std::function<void(int)> fn_;
+  int nthreads_ = 0, want_ = 0, claimed_ = 0, pending_ = 0;
+  uint64_t gen_ = 0;
+};
+
+int default_threads(int nthreads, int cap) {
+  const int hw = (int)std::max(1u, std::thread::hardware_concurrency());
+  return std::min(WorkerPool::kMaxWorkers, nthreads > 0 ? nthreads : std::min(cap, hw));
+}
+
+// work(lo, hi) over [0, n) in nt equal ranges on the pool (inline for nt <= 1).
+void parallel_ranges(int64_t n, int nt, const std::function<void(int64_t, int64_t)>& work) {
+  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(n, 1));
+  if (nt <= 1) {
+    work(0, n);
+    return;
+  }
+  const int64_t per = (n + nt - 1) / nt;
+  WorkerPool& pool = WorkerPool::instance();
+  pool.start(nt, [&](int w) {
+    const int64_t lo = std::min<int64_t>(n, w * per), hi = std::min<int64_t>(n, lo + per);
+    if (lo < hi) work(lo, hi);
+  });
+  pool.wait();
+}
+
 void gather_rows(const std::vector<int64_t>& uniq, const uint8_t* codes, const uint16_t* scales,
                  int64_t N, int64_t D, uint8_t* codes_out, uint16_t* scales_out, int nthreads) {
   const size_t crow = (size_t)(N * 3 * D / 8), srow = (size_t)(N * (D / 64));
@@ -71,21 +159,10 @@ void gather_rows(const std::vector<int64_t>& uniq, const uint8_t* codes, const u
       std::memcpy(scales_out + (size_t)u * srow, scales + (size_t)uniq[u] * srow, srow * 2);
     }
   };
-  int nt = nthreads > 0 ? nthreads : (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
+  int nt = default_threads(nthreads, 16);
   const size_t bytes = (size_t)U * (crow + 2 * srow);
-  if (bytes < ((size_t)1 << 20)) nt = 1;  // threads are not worth it below ~1 MB
-  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(U, 1));
-  if (nt <= 1) {
-    work(0, U);
-    return;
-  }
-  std::vector<std::thread> pool;
-  const int64_t per = (U + nt - 1) / nt;
-  for (int i = 0; i < nt; ++i) {
-    const int64_t lo = i * per, hi = std::min<int64_t>(U, lo + per);
-    if (lo < hi) pool.emplace_back(work, lo, hi);
-  }
-  for (auto& th : pool) th.join();
+  if (bytes < ((size_t)1 << 20)) nt = 1;  // workers are not worth it below ~1 MB
+  parallel_ranges(U, nt, work);
 }
 
 // One event per pinned staging area of the host-resident combine, recorded
@@ -164,8 +241,8 @@ int gather_copy_stack(const std::vector<int64_t>& uniq, const uint8_t* const* co
                   scales[l] + (size_t)uniq[u] * srow, srow * 2);
     }
   };
-  int nt = nthreads > 0 ? nthreads : (int)std::min(16u, std::max(1u, std::thread::hardware_concurrency()));
-  if ((size_t)(L * U) * (crow + 2 * srow) < ((size_t)1 << 20)) nt = 1;  // threads are not worth it below ~1 MB
+  int nt = default_threads(nthreads, 16);
+  if ((size_t)(L * U) * (crow + 2 * srow) < ((size_t)1 << 20)) nt = 1;  // workers are not worth it below ~1 MB
   int rc = MOLE_OK;
   if (nt <= 1) {
     for (int k = 0; k < nchunks && rc == MOLE_OK; ++k) {
@@ -185,15 +262,15 @@ int gather_copy_stack(const std::vector<int64_t>& uniq, const uint8_t* const* co
       done[k].fetch_add(1, std::memory_order_release);
     }
   };
-  std::vector<std::thread> pool;
-  for (int w = 0; w < nt; ++w) pool.emplace_back(worker, w);
+  WorkerPool& pool = WorkerPool::instance();
+  pool.start(nt, worker);
   for (int k = 0; k < nchunks; ++k) {
     while (done[k].load(std::memory_order_acquire) < nt) std::this_thread::yield();
     if (rc == MOLE_OK)
       rc = hip_status(hipMemcpyAsync(base_d + begin(k), base_h + begin(k), begin(k + 1) - begin(k),
                                      hipMemcpyHostToDevice, s));
   }
-  for (auto& th : pool) th.join();
+  pool.wait();
   return rc;
 }
 
@@ -212,13 +289,15 @@ const char* mole_status_string(int status) {
     case MOLE_ERR_UNSUPPORTED: return "unsupported shape";
     case MOLE_ERR_HIP: return "HIP runtime error (see mole_last_hip_error)";
     case MOLE_ERR_ID: return "token id outside [0, V)";
+    case MOLE_ERR_IO: return "table file read or write failed";
+    case MOLE_ERR_FORMAT: return "not a MoLE NF3 table file of this version";
     default: return "unknown status";
   }
 }
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 6; }
+int mole_abi_version(void) { return 7; }
 
 int mole_nf3_levels(float* levels_host) {
   if (!levels_host) return MOLE_ERR_NULL;
@@ -507,11 +586,16 @@ int mole_nf3_host_staging_size(int64_t T, int64_t N, int64_t D, size_t* bytes) {
   return MOLE_OK;
 }
 
-int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const void* w_r,
-                                 const uint8_t* codes_host, const uint16_t* scales_host,
-                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
-                                 int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
-                                 int nthreads, int64_t* n_unique, void* stream) {
+extern "C++" {  // (a template inside the C-linkage block)
+namespace {
+// The host-resident NF3 combine with a row source: gather(uniq, codes_out,
+// scales_out) copies the distinct rows into the pinned staging area and
+// returns a status; source_ok says whether the source's own pointers or
+// handle are present (checked with the other arguments).
+template <typename Gather>
+int combine_nf3_staged(const int64_t* ids_host, const void* h, const void* w_r, void* stage_host, void* stage_dev,
+                       size_t stage_bytes, float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                       int64_t* n_unique, void* stream, bool source_ok, Gather gather) {
   if (!dtype_ok(dtype_h)) return MOLE_ERR_DTYPE;
   int rc = check_combine_common(T, V, D, N);
   if (rc != MOLE_OK) return rc;
@@ -520,8 +604,7 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
     if (n_unique) *n_unique = 0;
     return MOLE_OK;
   }
-  if (!ids_host || !h || !w_r || !codes_host || !scales_host || !stage_host || !stage_dev || !y)
-    return MOLE_ERR_NULL;
+  if (!ids_host || !h || !w_r || !source_ok || !stage_host || !stage_dev || !y) return MOLE_ERR_NULL;
   if (!aligned16(h) || !aligned16(w_r) || !aligned16(stage_host) || !aligned16(stage_dev) || !aligned16(y))
     return MOLE_ERR_ALIGN;
   if (stage_bytes < nf3_staging(T, T, N, D).total) return MOLE_ERR_WORKSPACE;
@@ -540,8 +623,8 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
   if (rc != MOLE_OK) return rc;
   const int64_t U = (int64_t)uniq.size();
   const Nf3Staging st = nf3_staging(T, U, N, D);
-  gather_rows(uniq, codes_host, scales_host, N, D, base_h + st.codes_off,
-              reinterpret_cast<uint16_t*>(base_h + st.scales_off), nthreads);
+  rc = gather(uniq, base_h + st.codes_off, reinterpret_cast<uint16_t*>(base_h + st.scales_off));
+  if (rc != MOLE_OK) return rc;
   uint8_t* base_d = static_cast<uint8_t*>(stage_dev);
   rc = hip_status(hipMemcpyAsync(base_d, base_h, st.total, hipMemcpyHostToDevice, s));
   if (rc == MOLE_OK) rc = hip_status(hipEventRecord(ev, s));
@@ -552,6 +635,202 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
                                                     T, D, N, dtype_h, s));
   if (rc == MOLE_OK && n_unique) *n_unique = U;
   return rc;
+}
+}  // namespace
+}  // extern "C++"
+
+int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const void* w_r,
+                                 const uint8_t* codes_host, const uint16_t* scales_host,
+                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
+                                 int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                                 int nthreads, int64_t* n_unique, void* stream) {
+  return combine_nf3_staged(ids_host, h, w_r, stage_host, stage_dev, stage_bytes, y, T, V, D, N, dtype_h, n_unique,
+                            stream, codes_host && scales_host,
+                            [&](const std::vector<int64_t>& uniq, uint8_t* codes_out, uint16_t* scales_out) {
+                              gather_rows(uniq, codes_host, scales_host, N, D, codes_out, scales_out, nthreads);
+                              return (int)MOLE_OK;
+                            });
+}
+
+// ---------------------------------------------------------------------------
+// Disk tier: the NF3 table in a file, one record per vocabulary row
+// ---------------------------------------------------------------------------
+namespace {
+constexpr char kNf3FileMagic[8] = {'M', 'O', 'L', 'E', 'N', 'F', '3', '\0'};
+constexpr uint32_t kNf3FileVersion = 1;
+
+// 64-byte header, little-endian; records follow at data_offset.
+struct Nf3FileHeader {
+  char magic[8];
+  uint32_t version;
+  uint32_t header_bytes;
+  int64_t V, N, D;
+  int64_t record_bytes;  // N*3D/8 code bytes, then N*(D/64) fp16 scales
+  int64_t data_offset;
+  int64_t reserved;
+};
+static_assert(sizeof(Nf3FileHeader) == 64, "the file header is 64 bytes");
+
+int64_t nf3_record_bytes(int64_t N, int64_t D) { return N * 3 * D / 8 + N * (D / 64) * 2; }
+
+// pread / pwrite of exactly n bytes (retrying short transfers and EINTR).
+bool read_full(int fd, void* buf, size_t n, int64_t off) {
+  char* p = static_cast<char*>(buf);
+  while (n > 0) {
+    const ssize_t r = pread(fd, p, n, (off_t)off);
+    if (r < 0 && errno == EINTR) continue;
+    if (r <= 0) return false;
+    p += r;
+    n -= (size_t)r;
+    off += r;
+  }
+  return true;
+}
+
+bool write_full(int fd, const void* buf, size_t n, int64_t off) {
+  const char* p = static_cast<const char*>(buf);
+  while (n > 0) {
+    const ssize_t r = pwrite(fd, p, n, (off_t)off);
+    if (r < 0 && errno == EINTR) continue;
+    if (r <= 0) return false;
+    p += r;
+    n -= (size_t)r;
+    off += r;
+  }
+  return true;
+}
+
+int read_nf3_header(int fd, Nf3FileHeader* hd) {
+  if (fd < 0) return MOLE_ERR_IO;
+  if (!read_full(fd, hd, sizeof(*hd), 0)) return MOLE_ERR_IO;
+  if (std::memcmp(hd->magic, kNf3FileMagic, 8) != 0 || hd->version != kNf3FileVersion ||
+      hd->header_bytes != sizeof(Nf3FileHeader))
+    return MOLE_ERR_FORMAT;
+  if (hd->V <= 0 || hd->N <= 0 || hd->D <= 0 || hd->D % 64 != 0 || hd->N > kMaxExperts || hd->D > kMaxDim ||
+      hd->record_bytes != nf3_record_bytes(hd->N, hd->D) || hd->data_offset < (int64_t)sizeof(Nf3FileHeader))
+    return MOLE_ERR_FORMAT;
+  return MOLE_OK;
+}
+
+// Rows uniq[u] of the file into codes_out [U][N][3D/8] and scales_out
+// [U][N][D/64]: one preadv per row (two segments, straight into the two
+// staging sections), split over threads for larger batches.
+int gather_rows_file(int fd, const Nf3FileHeader& hd, const std::vector<int64_t>& uniq, uint8_t* codes_out,
+                     uint16_t* scales_out, int nthreads) {
+  const size_t crow = (size_t)(hd.N * 3 * hd.D / 8), srow = (size_t)(hd.N * (hd.D / 64)) * 2;
+  const int64_t U = (int64_t)uniq.size();
+  std::atomic<int> failed{0};
+  auto work = [&](int64_t lo, int64_t hi) {
+    for (int64_t u = lo; u < hi && !failed.load(std::memory_order_relaxed); ++u) {
+      const int64_t off = hd.data_offset + uniq[u] * hd.record_bytes;
+      uint8_t* cp = codes_out + (size_t)u * crow;
+      uint8_t* sp = reinterpret_cast<uint8_t*>(scales_out) + (size_t)u * srow;
+      struct iovec iov[2] = {{cp, crow}, {sp, srow}};
+      ssize_t r;
+      do r = preadv(fd, iov, 2, (off_t)off); while (r < 0 && errno == EINTR);
+      if (r == (ssize_t)(crow + srow)) continue;
+      // a short read: finish the record with plain reads
+      const size_t got = r > 0 ? (size_t)r : 0;
+      bool ok = r >= 0;
+      if (ok && got < crow) ok = read_full(fd, cp + got, crow - got, off + (int64_t)got);
+      const size_t sgot = got > crow ? got - crow : 0;
+      if (ok) ok = read_full(fd, sp + sgot, srow - sgot, off + (int64_t)(crow + sgot));
+      if (!ok) failed.store(1);
+    }
+  };
+  // Reads mostly wait on the device: more workers than cores keep more of
+  // them in flight (32 by default, at least 4 rows each).
+  int nt = nthreads > 0 ? std::min(nthreads, WorkerPool::kMaxWorkers) : 32;
+  nt = (int)std::min<int64_t>(nt, std::max<int64_t>(1, U / 4));
+  parallel_ranges(U, nt, work);
+  return failed.load() ? MOLE_ERR_IO : MOLE_OK;
+}
+
+int check_nf3_file(int fd, int64_t V, int64_t N, int64_t D, Nf3FileHeader* hd) {
+  const int rc = read_nf3_header(fd, hd);
+  if (rc != MOLE_OK) return rc;
+  if (hd->V != V || hd->N != N || hd->D != D) return MOLE_ERR_DIM;
+  return MOLE_OK;
+}
+}  // namespace
+
+int mole_nf3_file_write(const char* path, const uint8_t* codes_host, const uint16_t* scales_host, int64_t V,
+                        int64_t N, int64_t D) {
+  if (!path || !codes_host || !scales_host) return MOLE_ERR_NULL;
+  if (V <= 0 || N <= 0 || D <= 0 || D % 64 != 0 || D > kMaxDim) return MOLE_ERR_DIM;
+  if (N > kMaxExperts) return MOLE_ERR_UNSUPPORTED;
+  Nf3FileHeader hd;
+  std::memset(&hd, 0, sizeof(hd));
+  std::memcpy(hd.magic, kNf3FileMagic, 8);
+  hd.version = kNf3FileVersion;
+  hd.header_bytes = sizeof(Nf3FileHeader);
+  hd.V = V;
+  hd.N = N;
+  hd.D = D;
+  hd.record_bytes = nf3_record_bytes(N, D);
+  hd.data_offset = sizeof(Nf3FileHeader);
+  const int fd = open(path, O_CREAT | O_TRUNC | O_WRONLY, 0644);
+  if (fd < 0) return MOLE_ERR_IO;
+  bool ok = write_full(fd, &hd, sizeof(hd), 0);
+  // records assembled in blocks of rows (about 4 MB per write)
+  const size_t crow = (size_t)(N * 3 * D / 8), srow = (size_t)(N * (D / 64)) * 2;
+  const int64_t rows_per = std::max<int64_t>(1, ((int64_t)4 << 20) / hd.record_bytes);
+  std::vector<uint8_t> buf((size_t)(rows_per * hd.record_bytes));
+  for (int64_t v0 = 0; ok && v0 < V; v0 += rows_per) {
+    const int64_t nr = std::min(rows_per, V - v0);
+    for (int64_t i = 0; i < nr; ++i) {
+      uint8_t* rec = buf.data() + (size_t)(i * hd.record_bytes);
+      std::memcpy(rec, codes_host + (size_t)(v0 + i) * crow, crow);
+      std::memcpy(rec + crow, reinterpret_cast<const uint8_t*>(scales_host) + (size_t)(v0 + i) * srow, srow);
+    }
+    ok = write_full(fd, buf.data(), (size_t)(nr * hd.record_bytes), hd.data_offset + v0 * hd.record_bytes);
+  }
+  if (close(fd) != 0) ok = false;
+  return ok ? MOLE_OK : MOLE_ERR_IO;
+}
+
+int mole_nf3_file_shape(int fd, int64_t* V, int64_t* N, int64_t* D) {
+  if (!V || !N || !D) return MOLE_ERR_NULL;
+  Nf3FileHeader hd;
+  const int rc = read_nf3_header(fd, &hd);
+  if (rc != MOLE_OK) return rc;
+  *V = hd.V;
+  *N = hd.N;
+  *D = hd.D;
+  return MOLE_OK;
+}
+
+int mole_gather_nf3_file(int fd, const int64_t* ids_host, int64_t T, int64_t V, int64_t N, int64_t D,
+                         uint8_t* codes_stage_host, uint16_t* scales_stage_host, int64_t* remap_host,
+                         int64_t* n_unique, int nthreads) {
+  if (T < 0 || V <= 0 || N <= 0 || D <= 0 || D % 64 != 0) return MOLE_ERR_DIM;
+  if (T > 0 && (!ids_host || !codes_stage_host || !scales_stage_host || !remap_host)) return MOLE_ERR_NULL;
+  if (!n_unique) return MOLE_ERR_NULL;
+  Nf3FileHeader hd;
+  int rc = check_nf3_file(fd, V, N, D, &hd);
+  if (rc != MOLE_OK) return rc;
+  std::vector<int64_t> uniq;
+  rc = dedupe(ids_host, T, V, uniq, remap_host);
+  if (rc != MOLE_OK) return rc;
+  rc = gather_rows_file(fd, hd, uniq, codes_stage_host, scales_stage_host, nthreads);
+  if (rc != MOLE_OK) return rc;
+  *n_unique = (int64_t)uniq.size();
+  return MOLE_OK;
+}
+
+int mole_lookup_combine_nf3_file(int fd, const int64_t* ids_host, const void* h, const void* w_r,
+                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y, int64_t T,
+                                 int64_t V, int64_t D, int64_t N, int dtype_h, int nthreads, int64_t* n_unique,
+                                 void* stream) {
+  Nf3FileHeader hd;
+  int hdr = MOLE_OK;
+  if (T > 0) hdr = check_nf3_file(fd, V, N, D, &hd);
+  return combine_nf3_staged(ids_host, h, w_r, stage_host, stage_dev, stage_bytes, y, T, V, D, N, dtype_h, n_unique,
+                            stream, true,
+                            [&](const std::vector<int64_t>& uniq, uint8_t* codes_out, uint16_t* scales_out) {
+                              if (hdr != MOLE_OK) return hdr;
+                              return gather_rows_file(fd, hd, uniq, codes_out, scales_out, nthreads);
+                            });
 }
 
 int mole_nf3_host_stack_staging_size(int64_t T, int64_t L, int64_t N, int64_t D, size_t* bytes) {

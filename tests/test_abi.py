@@ -14,7 +14,7 @@ from mixture_lookup_experts_amd import _native
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mole.h")
 
-OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
 
 
 def declared_functions():
@@ -37,18 +37,19 @@ def test_header_declares_the_hot_path():
                "mole_nf3_levels", "mole_abi_version", "mole_layer_forward",
                "mole_layer_workspace_size", "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4",
                "mole_pack_int8", "mole_lookup_combine_int8", "mole_train_index", "mole_train_workspace_size",
-               "mole_train_forward", "mole_train_backward"):
+               "mole_train_forward", "mole_train_backward", "mole_nf3_file_write", "mole_nf3_file_shape",
+               "mole_gather_nf3_file", "mole_lookup_combine_nf3_file"):
         assert fn in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 6
+    assert lib.mole_abi_version() == 7
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID):
+    for code in (OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT):
         assert mole.mole_status_string(code) not in ("", "unknown status")
     assert mole.mole_status_string(12345) == "unknown status"
 
@@ -315,3 +316,156 @@ def test_train_workspace_size_and_errors(lib):
                P(a), 16, 8, 50, 64, 128, 4, 1, None) == WS
     assert bwd(P(a), P(a), None, P(a), P(a), P(a), P(a), P(a), P(a), 1 << 40, P(a), 1 << 40, P(a), P(a), P(a),
                P(a), P(a), 16, 8, 50, 64, 128, 4, 1, None) == NULL
+
+
+# ----------------------------------------------------------------------------
+# Disk tier: the NF3 table file
+# ----------------------------------------------------------------------------
+
+def write_table_file(path, codes, scales):
+    import torch
+    mole.mole_nf3_file_write(str(path), torch.from_numpy(codes), torch.from_numpy(scales.view(np.int16)))
+
+
+def test_table_file_layout_is_the_documented_one(tmp_path):
+    """The file is the 64-byte header the header file documents followed by
+    one record per row (that row's codes, then its scales), byte for byte."""
+    import struct
+    codes, scales, _ = gather_inputs(11, V=9)
+    V, N, CB = codes.shape
+    D = CB * 8 // 3
+    p = tmp_path / "t.molt"
+    write_table_file(p, codes, scales)
+    rec = N * CB + N * (D // 64) * 2
+    want = struct.pack("<8sII6q", b"MOLENF3\0", 1, 64, V, N, D, rec, 64, 0)
+    want += b"".join(codes[v].tobytes() + scales[v].astype("<u2").tobytes() for v in range(V))
+    assert p.read_bytes() == want
+    fd = os.open(p, os.O_RDONLY)
+    try:
+        assert mole.mole_nf3_file_shape(fd) == (V, N, D)
+    finally:
+        os.close(fd)
+
+
+def test_file_gather_equals_host_gather(tmp_path):
+    """Rows read from the file are the rows the host-memory gather copies,
+    with the same remap and count, whatever the thread split."""
+    import torch
+    codes, scales, ids = gather_inputs(12, V=300, T=200)
+    T, (V, N, CB) = ids.size, codes.shape
+    D = CB * 8 // 3
+    p = tmp_path / "t.molt"
+    write_table_file(p, codes, scales)
+    bufs = lambda: (torch.zeros(T * N * CB, dtype=torch.uint8), torch.zeros(T * N * (D // 64), dtype=torch.int16),
+                    torch.zeros(T, dtype=torch.int64))
+    hc, hs, hr = bufs()
+    Uh = mole.mole_gather_nf3_host(torch.from_numpy(ids), torch.from_numpy(codes),
+                                   torch.from_numpy(scales.view(np.int16)), hc, hs, hr)
+    fd = os.open(p, os.O_RDONLY)
+    try:
+        for nthreads in (1, 4):
+            fc, fs, fr = bufs()
+            Uf = mole.mole_gather_nf3_file(fd, torch.from_numpy(ids), V, N, D, fc, fs, fr, nthreads=nthreads)
+            assert Uf == Uh
+            assert torch.equal(fr, hr)
+            assert torch.equal(fc[:Uf * N * CB], hc[:Uh * N * CB])
+            assert torch.equal(fs[:Uf * N * (D // 64)], hs[:Uh * N * (D // 64)])
+    finally:
+        os.close(fd)
+
+
+def test_table_file_errors(tmp_path):
+    import torch
+    codes, scales, ids = gather_inputs(13, V=10, T=5)
+    T, (V, N, CB) = ids.size, codes.shape
+    D = CB * 8 // 3
+    p = tmp_path / "t.molt"
+    write_table_file(p, codes, scales)
+    bufs = (torch.zeros(T * N * CB, dtype=torch.uint8), torch.zeros(T * N * (D // 64), dtype=torch.int16),
+            torch.zeros(T, dtype=torch.int64))
+
+    def status(fd, ids_=ids, V_=V):
+        try:
+            mole.mole_gather_nf3_file(fd, torch.from_numpy(ids_), V_, N, D, *bufs)
+            return OK
+        except mole.MoleError as e:
+            return e.status
+
+    fd = os.open(p, os.O_RDONLY)
+    try:
+        assert status(fd) == OK
+        assert status(fd, V_=V + 1) == DIM                       # header shape differs
+        bad = ids.copy()
+        bad[2] = V
+        assert status(fd, ids_=bad) == BADID
+    finally:
+        os.close(fd)
+    assert status(-1) == IO                                     # no open file
+    raw = bytearray(p.read_bytes())
+    raw[0:1] = b"X"
+    q = tmp_path / "bad_magic.molt"
+    q.write_bytes(bytes(raw))
+    fd = os.open(q, os.O_RDONLY)
+    try:
+        assert status(fd) == FORMAT
+    finally:
+        os.close(fd)
+    r = tmp_path / "short.molt"                                 # records cut off
+    r.write_bytes(p.read_bytes()[:64 + 3])
+    fd = os.open(r, os.O_RDONLY)
+    try:
+        ids_last = np.array([V - 1], np.int64)
+        assert status(fd, ids_=ids_last) == IO
+    finally:
+        os.close(fd)
+    with pytest.raises(mole.MoleError) as e:
+        mole.mole_nf3_file_write(str(tmp_path / "no_such_dir" / "t.molt"), torch.from_numpy(codes),
+                                 torch.from_numpy(scales.view(np.int16)))
+    assert e.value.status == IO
+
+
+def test_gathers_from_several_threads_share_the_worker_pool(tmp_path):
+    """Host gathers run on one persistent worker pool; calls from several
+    threads at once (memory and file sources mixed) each get their own
+    rows."""
+    import threading
+    import torch
+    codes, scales, _ = gather_inputs(14, V=400, N=4, D=256, T=10)
+    V, N, CB = codes.shape
+    D = CB * 8 // 3
+    p = tmp_path / "t.molt"
+    write_table_file(p, codes, scales)
+    fd = os.open(p, os.O_RDONLY)
+    errors = []
+
+    def job(k):
+        try:
+            r = np.random.Generator(np.random.PCG64(100 + k))
+            for it in range(20):
+                ids = r.integers(0, V, size=600).astype(np.int64)
+                T = ids.size
+                cs = torch.zeros(T * N * CB, dtype=torch.uint8)
+                ss = torch.zeros(T * N * (D // 64), dtype=torch.int16)
+                rm = torch.zeros(T, dtype=torch.int64)
+                if (k + it) % 2:
+                    U = mole.mole_gather_nf3_file(fd, torch.from_numpy(ids), V, N, D, cs, ss, rm, nthreads=8)
+                else:
+                    U = mole.mole_gather_nf3_host(torch.from_numpy(ids), torch.from_numpy(codes),
+                                                  torch.from_numpy(scales.view(np.int16)), cs, ss, rm,
+                                                  nthreads=8)
+                r_ = rm.numpy()
+                c = cs.numpy()[:U * N * CB].reshape(U, N, CB)
+                assert U == np.unique(ids).size
+                for t in range(0, T, 37):
+                    np.testing.assert_array_equal(c[r_[t]], codes[ids[t]])
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=job, args=(k,)) for k in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    os.close(fd)
+    assert not any(th.is_alive() for th in threads), "a gather did not return"
+    assert not errors, errors

@@ -12,6 +12,8 @@ No oracle input or expected value comes from the GPU: tables fed to the
 combine and NF3 tests are seeded synthetic arrays (or the oracle's own NF3
 encoding), never a GPU-built LUT.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -288,6 +290,40 @@ def test_combine_nf3_host_resident(T):
         y_host = host(y)
         np.testing.assert_array_equal(y_host, ref_dev)
         assert combine_rel_err(y_host, ref) <= COMBINE_TOL
+
+
+@pytest.mark.parametrize("T", [1, 256, 2048])
+def test_combine_nf3_from_table_file(T, tmp_path):
+    """Table in a file (the disk tier); only the distinct requested rows are
+    read and cross PCIe.  Equal bit for bit to the device-resident combine,
+    twice in a row through the same staging area."""
+    V, N, D = 4096, 16, 1024
+    r = rng(93)
+    ids = synth.zipf_ids(r, V, T, r.permutation(V))
+    uniq = np.unique(ids)
+    table = rand_table(94, V, N, D, "bf16", std=0.02, rows=uniq)
+    codes, scales, _ = oracle.pack_nf3(table)
+    h, w_r = rand_hw(95, T, N, D, "bf16", wstd=0.3)
+    path = tmp_path / "table.molt"
+    mole.mole_nf3_file_write(str(path), torch.from_numpy(codes), torch.from_numpy(scales.view(np.int16)))
+    nbytes = mole.mole_nf3_host_staging_size(T, N, D)
+    stage_h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    stage_d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    ref_dev = run_nf3(ids, h, w_r, codes, scales)
+    fd = os.open(path, os.O_RDONLY)
+    try:
+        assert mole.mole_nf3_file_shape(fd) == (V, N, D)
+        for _ in range(2):
+            y.fill_(float("nan"))
+            U = mole.mole_lookup_combine_nf3_file(fd, torch.from_numpy(ids), dev(h), dev(w_r), V, stage_h, stage_d,
+                                                  y)
+            torch.cuda.synchronize()
+            assert U == uniq.size
+            np.testing.assert_array_equal(host(y), ref_dev)
+    finally:
+        os.close(fd)
+    assert combine_rel_err(host(y), oracle.lookup_combine_nf3(ids, h, w_r, codes, scales)) <= COMBINE_TOL
 
 
 def test_nf3_host_stack_prefetch_matches_device_path():
