@@ -295,7 +295,10 @@ def scale_probe(torch, mole, synth, dev, stream):
     """Combine throughput where one launch moves tens of MB: the 410M-class
     table (50304 x 16 x 1024 bf16 and its NF3, NF4 and int8 forms) at
     T = 1024 and 4096, Zipf ids and a distinct-id control (gathered bytes =
-    unique bytes); plus the NF4 and int8 encoders over the whole table."""
+    unique bytes); the bf16 combine also in its grouped form (tokens grouped
+    by distinct id on the host, each slab read once per run; the index time
+    is reported, outside the timed region); plus the NF4 and int8 encoders
+    over the whole table."""
     w = synth.WORKLOADS["410m"]
     V, D, N = w.V, w.D, w.N
     # every input is produced on `stream`, the stream the kernels run on
@@ -334,13 +337,20 @@ def scale_probe(torch, mole, synth, dev, stream):
     perm = synth.rank_permutation(w)
     for T in (1024, 4096):
         for kind in ("zipf", "distinct"):
-            ids_l = [torch.from_numpy(synth.make_ids(w, T, step=s, kind=kind, perm=perm)).to(dev)
-                     for s in range(8)]
+            ids_host = [torch.from_numpy(synth.make_ids(w, T, step=s, kind=kind, perm=perm)) for s in range(8)]
+            ids_l = [x.to(dev) for x in ids_host]
+            # the grouped form's host index (tokens grouped by distinct id), built before the timed region
+            t_idx = time.perf_counter()
+            idx = [mole.mole_grouped_index(x, V) for x in ids_host]
+            index_us = (time.perf_counter() - t_idx) / len(ids_host) * 1e6
+            grp = [(r.to(dev), tk.to(dev)) for (r, tk) in idx]
             h_l = [torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(8)]
             y = torch.empty((T, D), dtype=torch.float32, device=dev)
             torch.cuda.synchronize()
             res = {}
             for name, fn, row in (
+                    ("bf16_grouped", lambda i: mole.mole_lookup_combine_grouped(*grp[i % 8], h_l[i % 8], w_r, lut, y,
+                                                                                stream=stream), N * D * 2),
                     ("bf16", lambda i: mole.mole_lookup_combine(ids_l[i % 8], h_l[i % 8], w_r, lut, y,
                                                                 stream=stream), N * D * 2),
                     ("nf3", lambda i: mole.mole_lookup_combine_nf3(ids_l[i % 8], h_l[i % 8], w_r, codes,
@@ -366,6 +376,8 @@ def scale_probe(torch, mole, synth, dev, stream):
                 byts = T * (row + D * 2 + 4 * D + 8) + D * N * 2
                 res[name] = {"us": us, "tokens_per_s": T / (us * 1e-6), "gbs": byts / (us * 1e-6) / 1e9,
                              "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes": byts}
+            res["bf16_grouped"]["host_index_us"] = index_us
+            res["bf16_grouped"]["mean_unique_ids"] = float(np.mean([torch.unique(r).numel() for (r, _) in idx]))
             out["T%d_%s" % (T, kind)] = res
     torch.cuda.synchronize()
     ctx.__exit__(None, None, None)

@@ -371,6 +371,28 @@ int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
                                  size_t* scales_off, int nthreads, int64_t* n_unique, void* stream);
 
 /* ------------------------------------------------------------------------
+ * mole_lookup_combine_grouped: the combine of mole_lookup_combine over a
+ * batch grouped by distinct id (inference section: each token's expert
+ * outputs are fetched by its id; a prefill batch of natural text repeats
+ * ids, and every token of one id reads the same N x D table slab).  The
+ * grouping comes from mole_train_index: tok [T] = the tokens grouped by
+ * distinct id (its tok_host), rows [T] = the table row of each grouped
+ * position (rows[p] = uniq[remap[tok[p]]]), both copied to the device.  Each
+ * slab is read once per run of equal rows in a chunk of the grouped list (a
+ * row with many tokens is split over chunks) instead of once per token.  y
+ * [T][D] fp32 as from mole_lookup_combine, up to fp32 summation order.
+ * bf16 h, w_r and table only, N <= 16, N <= D and D % 8 == 0
+ * (MOLE_ERR_UNSUPPORTED otherwise).  Device-resident rows are not
+ * range-checked.  Two launches on `stream`: the router (its gates are parked
+ * in the first N floats of each y row) and the grouped combine.
+ *   rows, tok: int64 [T], 8-byte aligned; h [T][D], w_r [N][D],
+ *   lut [V][N][D] bf16; y [T][D] fp32
+ * ------------------------------------------------------------------------ */
+int mole_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const void* h,
+                                const void* w_r, const void* lut, float* y, int64_t T, int64_t V,
+                                int64_t D, int64_t N, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Disk tier: the NF3 table in a file (inference section: the table is kept
  * in lower-tier storage and only the retrieved outputs are loaded into GPU
  * memory; the offloading discussion names CPU memory and disk as such

@@ -36,6 +36,8 @@ from ._native import (  # noqa: F401
     mole_nf3_host_stack_staging_size,
     mole_prefetch_nf3_host_stack,
     mole_gather_nf3_file,
+    mole_grouped_index,
+    mole_lookup_combine_grouped,
     mole_lookup_combine_nf3_file,
     mole_nf3_file_shape,
     mole_nf3_file_write,
@@ -57,4 +59,5 @@ __all__ = [
     "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4", "mole_pack_int8", "mole_lookup_combine_int8",
     "mole_train_index", "mole_train_workspace_size", "mole_train_forward", "mole_train_backward",
     "mole_nf3_file_write", "mole_nf3_file_shape", "mole_gather_nf3_file", "mole_lookup_combine_nf3_file",
+    "mole_lookup_combine_grouped", "mole_grouped_index",
 ]

@@ -83,6 +83,7 @@ def library():
             "mole_train_backward": (I, [P, P, P, P, P, P, P, P, P, SZ, P, SZ, P, P, P, P, P,
                                         I64, I64, I64, I64, I64, I64, I, P]),
             "mole_layer_forward": (I, [P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I, P, SZ, P]),
+            "mole_lookup_combine_grouped": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_nf3_file_write": (I, [ctypes.c_char_p, P, P, I64, I64, I64]),
             "mole_nf3_file_shape": (I, [I, P, P, P]),
             "mole_gather_nf3_file": (I, [I, P, I64, I64, I64, I64, P, P, P, P, I]),
@@ -307,6 +308,30 @@ def mole_lookup_combine_nf3_host(ids_host, h, w_r, codes_host, scales_host, stag
         _ptr(stage_host), _ptr(stage_dev), nbytes, _ptr(y), T, V, D, N, _dtype(h), nthreads,
         ctypes.addressof(u), _stream(stream)))
     return int(u.value)
+
+
+def mole_grouped_index(ids_host, V: int):
+    """Host-side grouping for mole_lookup_combine_grouped: (rows [T], tok [T])
+    int64 CPU tensors -- the tokens grouped by distinct id (mole_train_index's
+    tok) and the table row of each grouped position."""
+    uniq, remap, _, tok = mole_train_index(ids_host, V)
+    return uniq[remap[tok]].contiguous(), tok
+
+
+def mole_lookup_combine_grouped(rows, tok, h, w_r, lut, y, stream=None) -> None:
+    """The combine over a batch grouped by distinct id (rows, tok from
+    mole_grouped_index, on the device): each table slab is read once per run
+    of a row's tokens instead of once per token."""
+    V, N, D = lut.shape
+    T = h.shape[0]
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "h [T,D], w_r [N,D], y [T,D]")
+    _need(rows.numel() == T and tok.numel() == T, "rows and tok hold T entries")
+    _need(h.dtype == lut.dtype == w_r.dtype and y.dtype == torch.float32, "h, w_r, lut share one dtype; y float32")
+    for t in (rows, tok, h, w_r, lut, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_lookup_combine_grouped", library().mole_lookup_combine_grouped(
+        _ptr(rows), _ptr(tok), _ptr(h), _ptr(w_r), _ptr(lut), _ptr(y), T, V, D, N, _dtype(lut), _stream(stream)))
 
 
 def mole_nf3_file_write(path: str, codes_host, scales_host) -> None:

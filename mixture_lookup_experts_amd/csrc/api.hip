@@ -480,6 +480,22 @@ int check_train(int64_t T, int64_t U, int64_t V, int64_t D, int64_t F, int64_t N
 }
 }  // namespace
 
+int mole_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const void* h, const void* w_r,
+                                const void* lut, float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
+                                void* stream) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (dtype != MOLE_BF16 || N > 16 || N > D || D % 8 != 0) return MOLE_ERR_UNSUPPORTED;
+  if (T == 0) return MOLE_OK;
+  if (!rows || !tok || !h || !w_r || !lut || !y) return MOLE_ERR_NULL;
+  if (!aligned8(rows) || !aligned8(tok) || !aligned16(h) || !aligned16(w_r) || !aligned16(lut) || !aligned16(y))
+    return MOLE_ERR_ALIGN;
+  return hip_status(mole::launch_lookup_combine_grouped(rows, tok, (const uint16_t*)h, (const uint16_t*)w_r,
+                                                        (const uint16_t*)lut, y, T, (int)D, (int)N,
+                                                        as_stream(stream)));
+}
+
 int mole_train_workspace_size(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N, size_t* fwd_bytes,
                               size_t* bwd_bytes) {
   if (T < 0 || U < 0 || U > T || D <= 0 || F <= 0 || N <= 0 || N * F > kMaxTrainDim || N * D > kMaxTrainDim ||

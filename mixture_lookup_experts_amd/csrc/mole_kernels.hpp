@@ -39,6 +39,12 @@ hipError_t launch_pack_int8(const void* lut, int8_t* codes, float* scales, int64
 hipError_t launch_pack_nf3(const void* lut, uint8_t* codes, uint16_t* scales, int64_t rows,
                            int64_t D, int dtype, hipStream_t s);
 
+// combine_grouped.hip: the combine over a batch grouped by distinct id
+int grouped_chunk(int64_t T);
+hipError_t launch_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const uint16_t* h,
+                                         const uint16_t* w_r, const uint16_t* lut, float* y, int64_t T, int D, int N,
+                                         hipStream_t s);
+
 // build_lut.hip
 constexpr int kBuildTileM = 256;  // vocabulary rows per GEMM tile
 size_t build_lut_min_workspace(int64_t D, int64_t F, int64_t N);

@@ -38,7 +38,7 @@ def test_header_declares_the_hot_path():
                "mole_layer_workspace_size", "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4",
                "mole_pack_int8", "mole_lookup_combine_int8", "mole_train_index", "mole_train_workspace_size",
                "mole_train_forward", "mole_train_backward", "mole_nf3_file_write", "mole_nf3_file_shape",
-               "mole_gather_nf3_file", "mole_lookup_combine_nf3_file"):
+               "mole_gather_nf3_file", "mole_lookup_combine_nf3_file", "mole_lookup_combine_grouped"):
         assert fn in names
 
 
@@ -469,3 +469,32 @@ def test_gathers_from_several_threads_share_the_worker_pool(tmp_path):
     os.close(fd)
     assert not any(th.is_alive() for th in threads), "a gather did not return"
     assert not errors, errors
+
+
+def test_grouped_combine_argument_errors(lib):
+    """The grouped combine checks sizes, dtype and its limits before any
+    launch (no GPU is touched: every call here fails on the host)."""
+    dummy = ctypes.c_void_p(16)  # never dereferenced: the calls fail before
+
+    def call(T=8, V=100, D=64, N=4, dtype=_native.MOLE_BF16, ptr=dummy):
+        return lib.mole_lookup_combine_grouped(ptr, ptr, ptr, ptr, ptr, ptr, T, V, D, N, dtype, None)
+
+    assert call(dtype=7) == DTYPE
+    assert call(D=0) == DIM
+    assert call(T=-1) == DIM
+    assert call(dtype=_native.MOLE_F32) == UNSUP
+    assert call(N=17) == UNSUP
+    assert call(N=8, D=4) == UNSUP       # N > D
+    assert call(D=60) == UNSUP           # D % 8
+    assert call(T=0) == OK               # empty batch: no-op
+    assert call(ptr=None) == NULL
+
+
+def test_grouped_index_orders_rows_by_id():
+    """The grouping puts each id's tokens together, in token order, and
+    rows[p] is the table row of grouped position p."""
+    import torch
+    ids = torch.tensor([7, 3, 7, 9, 3, 7], dtype=torch.int64)
+    rows, tok = mole.mole_grouped_index(ids, 10)
+    assert tok.tolist() == [0, 2, 5, 1, 4, 3]
+    assert rows.tolist() == [7, 7, 7, 3, 3, 9]

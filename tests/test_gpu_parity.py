@@ -246,6 +246,59 @@ def test_combine_nf3_matches_oracle(V, N, D, T, dtype):
     assert combine_rel_err(y, y_ref) <= COMBINE_TOL
 
 
+# ----------------------------------------------------------------------------
+# lookup-combine over a batch grouped by distinct id
+# ----------------------------------------------------------------------------
+
+def run_grouped(ids, h, w_r, lut):
+    rows, tok = mole.mole_grouped_index(torch.from_numpy(ids), lut.shape[0])
+    y = torch.full((ids.size, lut.shape[2]), float("nan"), dtype=torch.float32, device="cuda")
+    mole.mole_lookup_combine_grouped(rows.cuda(), tok.cuda(), dev(h), dev(w_r), dev(lut), y)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def grouped_ids(r, V, T, law):
+    if law == "zipf":
+        return synth.zipf_ids(r, V, T, r.permutation(V))
+    if law == "one":
+        return np.full(T, V // 2, np.int64)
+    return r.integers(0, V, T).astype(np.int64)
+
+
+# (V, N, D, T, ids): ragged T and D, N padded to a power of two, one token,
+# runs of a hot id over many chunks (T = 3000 and 5000: 8- and 16-position
+# chunks), a single id for every token.
+GROUPED_CASES = [(300, 4, 768, 300, "uniform"), (300, 16, 1024, 257, "zipf"), (200, 16, 2048, 33, "zipf"),
+                 (100, 1, 128, 17, "uniform"), (100, 3, 136, 19, "zipf"), (50, 16, 1024, 3000, "zipf"),
+                 (20, 8, 64, 5000, "one"), (1000, 16, 1024, 1, "uniform")]
+
+
+@pytest.mark.parametrize("V,N,D,T,law", GROUPED_CASES)
+def test_grouped_combine_matches_oracle(V, N, D, T, law):
+    seed = 2000 + V + N + D + T
+    lut = rand_table(seed, V, N, D, "bf16")
+    h, w_r = rand_hw(seed + 1, T, N, D, "bf16", wstd=0.3)
+    ids = grouped_ids(rng(seed + 2), V, T, law)
+    y = run_grouped(ids, h, w_r, lut)
+    assert np.all(np.isfinite(y))
+    assert combine_rel_err(y, oracle.lookup_combine(ids, h, w_r, lut)) <= COMBINE_TOL
+    # the per-token combine on the same inputs, up to fp32 summation order
+    assert combine_rel_err(y, run_combine(ids, h, w_r, lut).astype(np.float64)) <= COMBINE_TOL
+
+
+@pytest.mark.parametrize("T", [1024, 4096])
+def test_grouped_combine_full_size_zipf(T):
+    """410M-class table, full vocabulary, Zipf(1.1) ids, every token checked."""
+    w = synth.WORKLOADS["410m"]
+    ids = synth.make_ids(w, T, step=0)
+    lut = rand_table(78, w.V, w.N, w.D, "bf16", rows=np.unique(ids))
+    h = synth.make_hidden(w, T)
+    w_r = synth.make_router(w)
+    y = run_grouped(ids, h, w_r, lut)
+    assert combine_rel_err(y, oracle.lookup_combine(ids, h, w_r, lut)) <= COMBINE_TOL
+
+
 @pytest.mark.parametrize("T", [256, 1024, 4096])
 def test_combine_nf3_full_size_zipf(T):
     w = synth.WORKLOADS["410m-nf3"]
