@@ -99,13 +99,14 @@ __global__ __launch_bounds__(kGroupedThreads) void lookup_combine_grouped_kernel
   }
 }
 
-}  // namespace
-
+// Chunk size: about 1024 chunks, a power of two in [4, 64].
 int grouped_chunk(int64_t T) {
-  int seg = 4;  // about 1024 chunks, a power of two in [4, 64]
+  int seg = 4;
   while (seg < kMaxSegG && (int64_t)seg * 1024 < T) seg *= 2;
   return seg;
 }
+
+}  // namespace
 
 hipError_t launch_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const uint16_t* h,
                                          const uint16_t* w_r, const uint16_t* lut, float* y, int64_t T, int D, int N,

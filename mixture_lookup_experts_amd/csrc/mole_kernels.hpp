@@ -40,7 +40,6 @@ hipError_t launch_pack_nf3(const void* lut, uint8_t* codes, uint16_t* scales, in
                            int64_t D, int dtype, hipStream_t s);
 
 // combine_grouped.hip: the combine over a batch grouped by distinct id
-int grouped_chunk(int64_t T);
 hipError_t launch_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const uint16_t* h,
                                          const uint16_t* w_r, const uint16_t* lut, float* y, int64_t T, int D, int N,
                                          hipStream_t s);
