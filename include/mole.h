@@ -52,6 +52,7 @@ extern "C" {
 #define MOLE_ERR_ID (-8)          /* a host-side token id is outside [0, V) */
 #define MOLE_ERR_IO (-9)          /* a table file could not be read or written */
 #define MOLE_ERR_FORMAT (-10)     /* not a MoLE NF3 table file of this version */
+#define MOLE_ERR_HOST (-11)       /* a host-side allocation or thread creation failed */
 
 #define MOLE_F32 0
 #define MOLE_BF16 1

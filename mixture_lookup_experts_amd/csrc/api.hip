@@ -70,10 +70,12 @@ int dedupe(const int64_t* ids, int64_t T, int64_t V, std::vector<int64_t>& uniq,
 
 // Host worker threads for the gathers, created on first use and kept for
 // the life of the process (spawning a thread per worker and call cost
-// about 10 us each, more than a small batch's copies).  start(n, fn) runs
-// fn(0) .. fn(n-1) on n pool threads and returns at once; wait() returns
-// when all have finished.  One job at a time: a second caller's start()
-// blocks until the first caller's wait().
+// about 10 us each, more than a small batch's copies).  reserve(n) makes
+// sure up to n workers exist and returns how many do (fewer if the system
+// refuses more threads, 0 if none).  start(n, fn), n <= reserve's answer,
+// runs fn(0) .. fn(n-1) on n pool threads and returns at once; wait()
+// returns when all have finished.  One job at a time: a second caller's
+// start() blocks until the first caller's wait().
 class WorkerPool {
  public:
   static constexpr int kMaxWorkers = 64;
@@ -81,13 +83,21 @@ class WorkerPool {
     static WorkerPool* p = new WorkerPool();  // never destroyed: its threads outlive static destructors
     return *p;
   }
+  int reserve(int n) {
+    std::lock_guard<std::mutex> lk(mu_);
+    while (nthreads_ < n) {
+      try {
+        std::thread(&WorkerPool::loop, this).detach();
+      } catch (...) {
+        break;  // no more threads: run with those there are
+      }
+      ++nthreads_;
+    }
+    return std::min(n, nthreads_);
+  }
   void start(int n, std::function<void(int)> fn) {
     job_mu_.lock();
     std::unique_lock<std::mutex> lk(mu_);
-    while (nthreads_ < n) {
-      std::thread(&WorkerPool::loop, this).detach();
-      ++nthreads_;
-    }
     fn_ = std::move(fn);
     want_ = n;
     claimed_ = 0;
@@ -133,15 +143,17 @@ int default_threads(int nthreads, int cap) {
   return std::min(WorkerPool::kMaxWorkers, nthreads > 0 ? nthreads : std::min(cap, hw));
 }
 
-// work(lo, hi) over [0, n) in nt equal ranges on the pool (inline for nt <= 1).
+// work(lo, hi) over [0, n) in nt equal ranges on the pool (inline for nt <= 1
+// or when no worker thread can be had).
 void parallel_ranges(int64_t n, int nt, const std::function<void(int64_t, int64_t)>& work) {
   nt = (int)std::min<int64_t>(nt, std::max<int64_t>(n, 1));
+  WorkerPool& pool = WorkerPool::instance();
+  if (nt > 1) nt = pool.reserve(nt);
   if (nt <= 1) {
     work(0, n);
     return;
   }
   const int64_t per = (n + nt - 1) / nt;
-  WorkerPool& pool = WorkerPool::instance();
   pool.start(nt, [&](int w) {
     const int64_t lo = std::min<int64_t>(n, w * per), hi = std::min<int64_t>(n, lo + per);
     if (lo < hi) work(lo, hi);
@@ -243,6 +255,8 @@ int gather_copy_stack(const std::vector<int64_t>& uniq, const uint8_t* const* co
   };
   int nt = default_threads(nthreads, 16);
   if ((size_t)(L * U) * (crow + 2 * srow) < ((size_t)1 << 20)) nt = 1;  // workers are not worth it below ~1 MB
+  WorkerPool& pool = WorkerPool::instance();
+  if (nt > 1) nt = pool.reserve(nt);
   int rc = MOLE_OK;
   if (nt <= 1) {
     for (int k = 0; k < nchunks && rc == MOLE_OK; ++k) {
@@ -262,7 +276,6 @@ int gather_copy_stack(const std::vector<int64_t>& uniq, const uint8_t* const* co
       done[k].fetch_add(1, std::memory_order_release);
     }
   };
-  WorkerPool& pool = WorkerPool::instance();
   pool.start(nt, worker);
   for (int k = 0; k < nchunks; ++k) {
     while (done[k].load(std::memory_order_acquire) < nt) std::this_thread::yield();
@@ -272,6 +285,18 @@ int gather_copy_stack(const std::vector<int64_t>& uniq, const uint8_t* const* co
   }
   pool.wait();
   return rc;
+}
+
+
+// Host-side entry points allocate (maps, vectors, file buffers) and start
+// threads; an exception must not cross the C ABI, so it becomes a status.
+template <typename F>
+int guarded(F f) {
+  try {
+    return f();
+  } catch (...) {
+    return MOLE_ERR_HOST;
+  }
 }
 
 }  // namespace
@@ -291,6 +316,7 @@ const char* mole_status_string(int status) {
     case MOLE_ERR_ID: return "token id outside [0, V)";
     case MOLE_ERR_IO: return "table file read or write failed";
     case MOLE_ERR_FORMAT: return "not a MoLE NF3 table file of this version";
+    case MOLE_ERR_HOST: return "host memory or thread allocation failed";
     default: return "unknown status";
   }
 }
@@ -441,8 +467,8 @@ int mole_lookup_combine_int8(const int64_t* ids, const void* h, const void* w_r,
   return combine_q(mole::kFmtI8, ids, h, w_r, codes, scales, y, T, V, D, N, dtype_h, stream);
 }
 
-int mole_train_index(const int64_t* ids_host, int64_t T, int64_t V, int64_t* uniq_host, int64_t* remap_host,
-                     int64_t* row_ptr_host, int64_t* tok_host, int64_t* n_unique) {
+static int mole_train_index_impl(const int64_t* ids_host, int64_t T, int64_t V, int64_t* uniq_host, int64_t* remap_host,
+                                 int64_t* row_ptr_host, int64_t* tok_host, int64_t* n_unique) {
   if (T < 0 || V <= 0) return MOLE_ERR_DIM;
   if (T > 0 && (!ids_host || !uniq_host || !remap_host || !row_ptr_host || !tok_host)) return MOLE_ERR_NULL;
   if (!n_unique) return MOLE_ERR_NULL;
@@ -461,6 +487,13 @@ int mole_train_index(const int64_t* ids_host, int64_t T, int64_t V, int64_t* uni
   }
   *n_unique = U;
   return MOLE_OK;
+}
+
+int mole_train_index(const int64_t* ids_host, int64_t T, int64_t V, int64_t* uniq_host, int64_t* remap_host,
+                     int64_t* row_ptr_host, int64_t* tok_host, int64_t* n_unique) {
+  return guarded([&] {
+    return mole_train_index_impl(ids_host, T, V, uniq_host, remap_host, row_ptr_host, tok_host, n_unique);
+  });
 }
 
 namespace {
@@ -576,10 +609,10 @@ int mole_layer_forward(const int64_t* ids, const void* h, const void* w_r, const
                                                workspace, as_stream(stream)));
 }
 
-int mole_gather_nf3_host(const int64_t* ids_host, int64_t T, const uint8_t* codes_host,
-                         const uint16_t* scales_host, int64_t V, int64_t N, int64_t D,
-                         uint8_t* codes_stage_host, uint16_t* scales_stage_host, int64_t* remap_host,
-                         int64_t* n_unique, int nthreads) {
+static int mole_gather_nf3_host_impl(const int64_t* ids_host, int64_t T, const uint8_t* codes_host,
+                                     const uint16_t* scales_host, int64_t V, int64_t N, int64_t D,
+                                     uint8_t* codes_stage_host, uint16_t* scales_stage_host, int64_t* remap_host,
+                                     int64_t* n_unique, int nthreads) {
   if (T < 0 || V <= 0 || N <= 0 || D <= 0 || D % 64 != 0) return MOLE_ERR_DIM;
   if (T > 0 && (!ids_host || !codes_host || !scales_host || !codes_stage_host || !scales_stage_host ||
                 !remap_host))
@@ -591,6 +624,16 @@ int mole_gather_nf3_host(const int64_t* ids_host, int64_t T, const uint8_t* code
   gather_rows(uniq, codes_host, scales_host, N, D, codes_stage_host, scales_stage_host, nthreads);
   *n_unique = (int64_t)uniq.size();
   return MOLE_OK;
+}
+
+int mole_gather_nf3_host(const int64_t* ids_host, int64_t T, const uint8_t* codes_host,
+                         const uint16_t* scales_host, int64_t V, int64_t N, int64_t D,
+                         uint8_t* codes_stage_host, uint16_t* scales_stage_host, int64_t* remap_host,
+                         int64_t* n_unique, int nthreads) {
+  return guarded([&] {
+    return mole_gather_nf3_host_impl(ids_host, T, codes_host, scales_host, V, N, D, codes_stage_host,
+        scales_stage_host, remap_host, n_unique, nthreads);
+  });
 }
 
 int mole_nf3_host_staging_size(int64_t T, int64_t N, int64_t D, size_t* bytes) {
@@ -655,17 +698,28 @@ int combine_nf3_staged(const int64_t* ids_host, const void* h, const void* w_r, 
 }  // namespace
 }  // extern "C++"
 
-int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const void* w_r,
-                                 const uint8_t* codes_host, const uint16_t* scales_host,
-                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
-                                 int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
-                                 int nthreads, int64_t* n_unique, void* stream) {
+static int mole_lookup_combine_nf3_host_impl(const int64_t* ids_host, const void* h, const void* w_r,
+                                             const uint8_t* codes_host, const uint16_t* scales_host,
+                                             void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
+                                             int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                                             int nthreads, int64_t* n_unique, void* stream) {
   return combine_nf3_staged(ids_host, h, w_r, stage_host, stage_dev, stage_bytes, y, T, V, D, N, dtype_h, n_unique,
                             stream, codes_host && scales_host,
                             [&](const std::vector<int64_t>& uniq, uint8_t* codes_out, uint16_t* scales_out) {
                               gather_rows(uniq, codes_host, scales_host, N, D, codes_out, scales_out, nthreads);
                               return (int)MOLE_OK;
                             });
+}
+
+int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const void* w_r,
+                                 const uint8_t* codes_host, const uint16_t* scales_host,
+                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
+                                 int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                                 int nthreads, int64_t* n_unique, void* stream) {
+  return guarded([&] {
+    return mole_lookup_combine_nf3_host_impl(ids_host, h, w_r, codes_host, scales_host, stage_host, stage_dev,
+        stage_bytes, y, T, V, D, N, dtype_h, nthreads, n_unique, stream);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -770,8 +824,8 @@ int check_nf3_file(int fd, int64_t V, int64_t N, int64_t D, Nf3FileHeader* hd) {
 }
 }  // namespace
 
-int mole_nf3_file_write(const char* path, const uint8_t* codes_host, const uint16_t* scales_host, int64_t V,
-                        int64_t N, int64_t D) {
+static int mole_nf3_file_write_impl(const char* path, const uint8_t* codes_host, const uint16_t* scales_host, int64_t V,
+                                    int64_t N, int64_t D) {
   if (!path || !codes_host || !scales_host) return MOLE_ERR_NULL;
   if (V <= 0 || N <= 0 || D <= 0 || D % 64 != 0 || D > kMaxDim) return MOLE_ERR_DIM;
   if (N > kMaxExperts) return MOLE_ERR_UNSUPPORTED;
@@ -805,7 +859,12 @@ int mole_nf3_file_write(const char* path, const uint8_t* codes_host, const uint1
   return ok ? MOLE_OK : MOLE_ERR_IO;
 }
 
-int mole_nf3_file_shape(int fd, int64_t* V, int64_t* N, int64_t* D) {
+int mole_nf3_file_write(const char* path, const uint8_t* codes_host, const uint16_t* scales_host, int64_t V,
+                        int64_t N, int64_t D) {
+  return guarded([&] { return mole_nf3_file_write_impl(path, codes_host, scales_host, V, N, D); });
+}
+
+static int mole_nf3_file_shape_impl(int fd, int64_t* V, int64_t* N, int64_t* D) {
   if (!V || !N || !D) return MOLE_ERR_NULL;
   Nf3FileHeader hd;
   const int rc = read_nf3_header(fd, &hd);
@@ -816,9 +875,13 @@ int mole_nf3_file_shape(int fd, int64_t* V, int64_t* N, int64_t* D) {
   return MOLE_OK;
 }
 
-int mole_gather_nf3_file(int fd, const int64_t* ids_host, int64_t T, int64_t V, int64_t N, int64_t D,
-                         uint8_t* codes_stage_host, uint16_t* scales_stage_host, int64_t* remap_host,
-                         int64_t* n_unique, int nthreads) {
+int mole_nf3_file_shape(int fd, int64_t* V, int64_t* N, int64_t* D) {
+  return guarded([&] { return mole_nf3_file_shape_impl(fd, V, N, D); });
+}
+
+static int mole_gather_nf3_file_impl(int fd, const int64_t* ids_host, int64_t T, int64_t V, int64_t N, int64_t D,
+                                     uint8_t* codes_stage_host, uint16_t* scales_stage_host, int64_t* remap_host,
+                                     int64_t* n_unique, int nthreads) {
   if (T < 0 || V <= 0 || N <= 0 || D <= 0 || D % 64 != 0) return MOLE_ERR_DIM;
   if (T > 0 && (!ids_host || !codes_stage_host || !scales_stage_host || !remap_host)) return MOLE_ERR_NULL;
   if (!n_unique) return MOLE_ERR_NULL;
@@ -834,10 +897,19 @@ int mole_gather_nf3_file(int fd, const int64_t* ids_host, int64_t T, int64_t V, 
   return MOLE_OK;
 }
 
-int mole_lookup_combine_nf3_file(int fd, const int64_t* ids_host, const void* h, const void* w_r,
-                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y, int64_t T,
-                                 int64_t V, int64_t D, int64_t N, int dtype_h, int nthreads, int64_t* n_unique,
-                                 void* stream) {
+int mole_gather_nf3_file(int fd, const int64_t* ids_host, int64_t T, int64_t V, int64_t N, int64_t D,
+                         uint8_t* codes_stage_host, uint16_t* scales_stage_host, int64_t* remap_host,
+                         int64_t* n_unique, int nthreads) {
+  return guarded([&] {
+    return mole_gather_nf3_file_impl(fd, ids_host, T, V, N, D, codes_stage_host, scales_stage_host, remap_host,
+        n_unique, nthreads);
+  });
+}
+
+static int mole_lookup_combine_nf3_file_impl(int fd, const int64_t* ids_host, const void* h, const void* w_r,
+                                             void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
+                                             int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h, int nthreads,
+                                             int64_t* n_unique, void* stream) {
   Nf3FileHeader hd;
   int hdr = MOLE_OK;
   if (T > 0) hdr = check_nf3_file(fd, V, N, D, &hd);
@@ -849,6 +921,16 @@ int mole_lookup_combine_nf3_file(int fd, const int64_t* ids_host, const void* h,
                             });
 }
 
+int mole_lookup_combine_nf3_file(int fd, const int64_t* ids_host, const void* h, const void* w_r,
+                                 void* stage_host, void* stage_dev, size_t stage_bytes, float* y, int64_t T,
+                                 int64_t V, int64_t D, int64_t N, int dtype_h, int nthreads, int64_t* n_unique,
+                                 void* stream) {
+  return guarded([&] {
+    return mole_lookup_combine_nf3_file_impl(fd, ids_host, h, w_r, stage_host, stage_dev, stage_bytes, y, T, V, D, N,
+        dtype_h, nthreads, n_unique, stream);
+  });
+}
+
 int mole_nf3_host_stack_staging_size(int64_t T, int64_t L, int64_t N, int64_t D, size_t* bytes) {
   if (!bytes) return MOLE_ERR_NULL;
   if (T < 0 || L <= 0 || N <= 0 || D <= 0 || D % 64 != 0 || D > kMaxDim || T > kMaxDim || N > kMaxExperts ||
@@ -858,11 +940,11 @@ int mole_nf3_host_stack_staging_size(int64_t T, int64_t L, int64_t N, int64_t D,
   return MOLE_OK;
 }
 
-int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
-                                 const uint8_t* const* codes_host, const uint16_t* const* scales_host,
-                                 int64_t L, int64_t V, int64_t N, int64_t D, void* stage_host,
-                                 void* stage_dev, size_t stage_bytes, size_t* codes_off,
-                                 size_t* scales_off, int nthreads, int64_t* n_unique, void* stream) {
+static int mole_prefetch_nf3_host_stack_impl(const int64_t* ids_host, int64_t T,
+                                             const uint8_t* const* codes_host, const uint16_t* const* scales_host,
+                                             int64_t L, int64_t V, int64_t N, int64_t D, void* stage_host,
+                                             void* stage_dev, size_t stage_bytes, size_t* codes_off,
+                                             size_t* scales_off, int nthreads, int64_t* n_unique, void* stream) {
   if (T < 0 || L <= 0 || V <= 0 || N <= 0 || D <= 0 || D % 64 != 0 || D > kMaxDim || T > kMaxDim ||
       N > kMaxExperts || L > kMaxDim)
     return MOLE_ERR_DIM;
@@ -893,6 +975,17 @@ int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
   if (rc == MOLE_OK) rc = hip_status(hipEventRecord(ev, s));
   if (rc == MOLE_OK && n_unique) *n_unique = U;
   return rc;
+}
+
+int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
+                                 const uint8_t* const* codes_host, const uint16_t* const* scales_host,
+                                 int64_t L, int64_t V, int64_t N, int64_t D, void* stage_host,
+                                 void* stage_dev, size_t stage_bytes, size_t* codes_off,
+                                 size_t* scales_off, int nthreads, int64_t* n_unique, void* stream) {
+  return guarded([&] {
+    return mole_prefetch_nf3_host_stack_impl(ids_host, T, codes_host, scales_host, L, V, N, D, stage_host, stage_dev,
+        stage_bytes, codes_off, scales_off, nthreads, n_unique, stream);
+  });
 }
 
 }  // extern "C"

@@ -14,7 +14,7 @@ from mixture_lookup_experts_amd import _native
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mole.h")
 
-OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT, HOST = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11
 
 
 def declared_functions():
@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT):
+    for code in (OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT, HOST):
         assert mole.mole_status_string(code) not in ("", "unknown status")
     assert mole.mole_status_string(12345) == "unknown status"
 
