@@ -298,7 +298,8 @@ def scale_probe(torch, mole, synth, dev, stream):
     unique bytes); the bf16 combine also in its grouped form (tokens grouped
     by distinct id on the host, each slab read once per run; the index time
     is reported, outside the timed region); plus the NF4 and int8 encoders
-    over the whole table."""
+    over the whole table.  Fractions against the nominal 8 TB/s and against a
+    device-to-device copy measured in the same run."""
     w = synth.WORKLOADS["410m"]
     V, D, N = w.V, w.D, w.N
     # every input is produced on `stream`, the stream the kernels run on
@@ -334,6 +335,21 @@ def scale_probe(torch, mole, synth, dev, stream):
         byts = V * N * D * 2 + wbytes
         packs[name] = {"ms": ms, "gbs": byts / (ms * 1e-3) / 1e9, "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     out["pack"] = packs
+    # Measured HBM peak of this part in this run: a 1 GiB device-to-device
+    # copy (read + write bytes over its event time), the second roofline the
+    # combines are reported against.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    out["hbm_copy_gbs_measured"] = copy_gbs
+    del src, dst
     perm = synth.rank_permutation(w)
     for T in (1024, 4096):
         for kind in ("zipf", "distinct"):
@@ -375,7 +391,8 @@ def scale_probe(torch, mole, synth, dev, stream):
                 us = e0.elapsed_time(e1) * 1e3 / reps
                 byts = T * (row + D * 2 + 4 * D + 8) + D * N * 2
                 res[name] = {"us": us, "tokens_per_s": T / (us * 1e-6), "gbs": byts / (us * 1e-6) / 1e9,
-                             "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes": byts}
+                             "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                             "hbm_frac_measured": byts / (us * 1e-6) / 1e9 / copy_gbs, "bytes": byts}
             res["bf16_grouped"]["host_index_us"] = index_us
             res["bf16_grouped"]["mean_unique_ids"] = float(np.mean([torch.unique(r).numel() for (r, _) in idx]))
             out["T%d_%s" % (T, kind)] = res
