@@ -410,7 +410,8 @@ def layer_probe(torch, mole, synth, dev, stream):
     time on `stream`, and the roofline it is held to -- the larger of its
     bf16 FLOPs (4 T D F) at the MFMA peak and its algorithmic HBM bytes
     (shared weights 4 D F, gathered table rows T N D 2, h, residual read and
-    write, ids, router) at the HBM peak."""
+    write, ids, router) at the HBM peak.  Blocks of up to 128 tokens are also
+    timed as HIP-graph replays (graph_us)."""
     out = {"peaks": {"bf16_tflops": BF16_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS}}
     ctx = torch.cuda.stream(stream)
     ctx.__enter__()
@@ -444,6 +445,25 @@ def layer_probe(torch, mole, synth, dev, stream):
             e1.record(stream)
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps
+            graph_us = None
+            if T <= 128:
+                # decode-sized blocks as a decode loop would run them: eight
+                # consecutive blocks (different batches) captured once and
+                # replayed, so launch overhead is off the critical path
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    cur = torch.cuda.current_stream()
+                    for i in range(8):
+                        mole.mole_layer_forward(ids_l[i % NB], h_l[i % NB], w_r, lut, wu, wd, x, ws, stream=cur)
+                gr.replay()
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(10):
+                    gr.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                graph_us = e0.elapsed_time(e1) * 1e3 / 80
+                del gr
             flops = 4.0 * T * D * F
             byts = 4.0 * D * F + T * (N * D * 2 + D * 2 + 8 * D + 8) + N * D * 2
             roof_us = max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9)) * 1e6
@@ -451,7 +471,7 @@ def layer_probe(torch, mole, synth, dev, stream):
                 "us": us, "tokens_per_s": T / (us * 1e-6), "tflops": flops / (us * 1e-6) / 1e12,
                 "gbs": byts / (us * 1e-6) / 1e9, "roofline_us": roof_us,
                 "bound": "mfma" if flops / (BF16_PEAK_TFLOPS * 1e12) > byts / (HBM_PEAK_GBS * 1e9) else "hbm",
-                "roofline_frac": roof_us / us, "flops": flops, "bytes": byts,
+                "roofline_frac": roof_us / us, "flops": flops, "bytes": byts, "graph_us": graph_us,
                 "config": "V=%d D=%d N=%d F=%d (shared FFN D->F->D), Zipf(1.1) ids" % (V, D, N, F)}
             del ws, x, h_l, ids_l
         del lut, w_r, wu, wd
