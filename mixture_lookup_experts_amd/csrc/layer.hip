@@ -11,9 +11,11 @@
 //   1. up-projection G = GELU(h . W_s_up^T), rounded to bf16 ([T][F]):
 //      long batches use the 256x256 build GEMM, shorter ones the mid-size
 //      GEMM below, split over K into fp32 partials plus a GELU reduction
-//      when the batch alone cannot fill the chip;
+//      when the batch alone cannot fill the chip; decode batches (T <= 8)
+//      stream the weights through gemv_kernel, one wavefront per weight row;
 //   2. down-projection of G into fp32 partial sums P[s][T][D], one per K
-//      split (long batches: the 256x256 build GEMM over equal K splits);
+//      split (long batches: the 256x256 build GEMM over equal K splits;
+//      decode batches: gemv_kernel, one partial);
 //   3. the routed lookup-combine as the block's final pass, reading x and
 //      adding the partial sums and the gate-weighted table rows:
 //      x += sum_s P[s] + sum_e g_e LUT[id, e]  (the shared expert's output
@@ -49,6 +51,7 @@ constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kMidBN = 128;             // output columns per mid-size tile (4 waves x 32)
 constexpr int kTargetBlocks = 512;      // two workgroups per compute unit
 constexpr int kMaxSplits = 16;          // K splits per projection
+constexpr int64_t kGemvMaxT = 8;        // decode batches up to this many tokens stream the weights
 
 enum { kMidGelu = 0, kMidPartial = 1 };
 
@@ -226,6 +229,98 @@ __global__ __launch_bounds__(256) void gelu_reduce_kernel(const float* __restric
   }
 }
 
+// Decode-sized products: out[t][r] = epi( sum_k X[t][k] W[r][k] ) for
+// T <= TT tokens (X bf16 [T][ldx], W bf16 [R][ldw] output-major).  `wpr`
+// wavefronts (1, 2 or 4) of a workgroup share an output row: lanes stride
+// over K in 16-byte chunks, four chunks' loads in flight at a time, every
+// token's dot product in fp32, then a wavefront sum, and the row's wpr
+// sums are added in wave order through LDS.  One row per wavefront keeps
+// the most loads in flight across the chip (measured: four rows per
+// wavefront, sharing the token chunks, was slower).  EPI kMidGelu:
+// bf16(GELU) to C [T][ldc]; kMidPartial: fp32 to C [T][ldc].  Needs
+// K % 8 == 0.
+template <int TT, int EPI>
+__global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                   const uint16_t* __restrict__ W, int64_t ldw, void* C,
+                                                   int64_t ldc, int T, int R, int K, int wpr) {
+  __shared__ float part[4][TT];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = wave / wpr, share = wave - slot * wpr;
+  const int rr = blockIdx.x * (4 / wpr) + slot;
+  const bool valid = rr < R;
+  const int r = valid ? rr : R - 1;  // a slot past the end reads the last row and stores nothing
+  const uint16_t* wrow = W + (int64_t)r * ldw;
+  const int nchunk = K / 8, step = 64 * wpr;
+  float acc[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+  for (int c0 = share * 64 + lane; c0 < nchunk; c0 += 4 * step) {
+    // four chunks per trip, loads first (clamped in bounds, masked where used)
+    uint4 wv[4], xv[4][TT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + step * u < nchunk ? c0 + step * u : c0;
+      wv[u] = ldg16(wrow + c * 8);
+#pragma unroll
+      for (int t = 0; t < TT; ++t) xv[u][t] = ldg16(X + (int64_t)(t < T ? t : 0) * ldx + c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (c0 + step * u < nchunk) {
+        float wf[8];
+        Elem<uint16_t>::unpack(wv[u], wf);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          float xf[8];
+          Elem<uint16_t>::unpack(xv[u][t], xf);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[t] = fmaf(xf[i], wf[i], acc[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc[t] += __shfl_xor(acc[t], m, 64);
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t) part[wave][t] = acc[t];
+  }
+  __syncthreads();
+  if (share == 0 && lane < TT && valid) {
+    const int t = lane;
+    if (t < T) {
+      float v = part[wave][t];
+      for (int w = 1; w < wpr; ++w) v += part[wave + w][t];
+      if constexpr (EPI == kMidGelu)
+        static_cast<uint16_t*>(C)[t * ldc + r] = (uint16_t)f32_to_bf16_rne(gelu_poly(v));
+      else
+        static_cast<float*>(C)[t * ldc + r] = v;
+    }
+  }
+}
+
+// Wavefronts per row: enough that a lane has at most four chunks of the row
+// (one trip of loads), up to four.
+template <int EPI>
+hipError_t launch_gemv(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, void* C, int64_t ldc, int T,
+                       int R, int K, hipStream_t s) {
+  int wpr = 1;
+  while (wpr < 4 && K / 8 > 256 * wpr) wpr *= 2;
+  const int rows_per_block = 4 / wpr;
+  const dim3 grid((unsigned)((R + rows_per_block - 1) / rows_per_block));
+  if (T <= 1)
+    hipLaunchKernelGGL((gemv_kernel<1, EPI>), grid, dim3(256), 0, s, X, ldx, W, ldw, C, ldc, T, R, K, wpr);
+  else if (T <= 2)
+    hipLaunchKernelGGL((gemv_kernel<2, EPI>), grid, dim3(256), 0, s, X, ldx, W, ldw, C, ldc, T, R, K, wpr);
+  else if (T <= 4)
+    hipLaunchKernelGGL((gemv_kernel<4, EPI>), grid, dim3(256), 0, s, X, ldx, W, ldw, C, ldc, T, R, K, wpr);
+  else
+    hipLaunchKernelGGL((gemv_kernel<8, EPI>), grid, dim3(256), 0, s, X, ldx, W, ldw, C, ldc, T, R, K, wpr);
+  return hipGetLastError();
+}
+
 template <int RM, int EPI, int NSL>
 hipError_t launch_mid_rm(const MidArgs& p, int tiles_m, int splits, hipStream_t s) {
   hipLaunchKernelGGL((gemm_mid_kernel<RM, EPI, NSL>), dim3((unsigned)(tiles_m * p.tiles_n), (unsigned)splits),
@@ -289,6 +384,20 @@ unsigned grid_1d(int64_t n4) {
 
 LayerPlan layer_plan(int64_t T, int64_t D, int64_t F) {
   LayerPlan pl{};
+  if (T <= kGemvMaxT) {
+    // decode batch: both projections stream their weights (gemv_kernel),
+    // the down-projection as one partial
+    pl.gemv = true;
+    pl.s_up = pl.s_down = 1;
+    pl.ks_up = D;
+    pl.ks_down = F;
+    pl.rm_up = pl.rm_down = 1;
+    pl.yr_off = 0;
+    pl.g_off = round256((size_t)T * (size_t)D * 4u);
+    pl.p_off = pl.g_off + round256((size_t)T * (size_t)F * 2u);
+    pl.total = pl.p_off + round256((size_t)T * (size_t)D * 4u);
+    return pl;
+  }
   // The 256x256 GEMM needs a full chip's worth of tiles (counting K splits)
   // to beat the mid-size one.
   pl.big_up = ((T + 255) / 256) * ((F + 255) / 256) >= 256;
@@ -338,7 +447,9 @@ hipError_t launch_layer_forward(const int64_t* ids, const uint16_t* h, const uin
 
   hipError_t err;
   // 1. Shared expert, up-projection with GELU.
-  if (pl.big_up) {
+  if (pl.gemv) {
+    err = launch_gemv<kMidGelu>(h, D, w_s_up, D, G, F, (int)T, (int)F, (int)D, s);
+  } else if (pl.big_up) {
     err = launch_gemm_gelu_bf16(h, D, w_s_up, D, G, F, (int)T, (int)F, (int)D, s);
   } else {
     MidArgs a{h, D, w_s_up, D, nullptr, F, T * F, (int)T, (int)F, (int)D, (int)pl.ks_up,
@@ -358,7 +469,9 @@ hipError_t launch_layer_forward(const int64_t* ids, const uint16_t* h, const uin
   if (err != hipSuccess) return err;
 
   // 2. Shared expert, down-projection: fp32 partial sums per K split.
-  if (pl.big_down) {
+  if (pl.gemv) {
+    err = launch_gemv<kMidPartial>(G, F, w_s_down, F, P, D, (int)T, (int)D, (int)F, s);
+  } else if (pl.big_down) {
     err = launch_gemm_f32_bf16(G, F, pl.ks_down, w_s_down, F, pl.ks_down, P, D, T * D, (int)T, (int)D,
                                (int)pl.ks_down, pl.s_down, s);
   } else {

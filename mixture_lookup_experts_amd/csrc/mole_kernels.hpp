@@ -92,6 +92,7 @@ hipError_t launch_train_backward(const int64_t* uniq, const int64_t* remap, cons
 
 // layer.hip: the MoLE block at inference (shared expert + routed lookup + residual)
 struct LayerPlan {
+  bool gemv;            // decode batch: both projections as weight-streaming products
   bool big_up;          // up-projection on the 256x256 build GEMM
   bool big_down;        // down-projection on the 256x256 build GEMM (fp32 partials per K split)
   int rm_up, rm_down;   // 32-row MFMA tiles per wave in the mid-size GEMM (tile height 32 * rm)

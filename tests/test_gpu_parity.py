@@ -582,7 +582,10 @@ def run_layer(ids, h, w_r, lut, wu, wd, x0):
 #   T = 1024, F = 8192: four-tile-row blocks with GELU in the epilogue.
 LAYER_CASES = [(300, 4, 256, 512, 1), (500, 5, 264, 392, 37), (400, 16, 512, 1024, 200),
                (256, 2, 256, 256, 512), (1000, 8, 128, 8192, 2048), (300, 4, 128, 4096, 256),
-               (300, 4, 2048, 512, 1024), (300, 4, 256, 8192, 1024)]
+               (300, 4, 2048, 512, 1024), (300, 4, 256, 8192, 1024),
+               # decode batches (weight-streaming projections): ragged K tails,
+               # 1, 2, 4 and 8 tokens per wavefront, a long down-projection
+               (500, 5, 264, 392, 3), (400, 16, 1024, 8192, 8), (300, 3, 2048, 200, 5), (200, 4, 64, 136, 2)]
 
 
 @pytest.mark.parametrize("V,N,D,F,T", LAYER_CASES)
@@ -649,11 +652,12 @@ def test_layer_full_size_sampled_tokens(name, T):
     assert rel_l2(got[sample].astype(np.float64) - x0[sample], upd) <= LAYER_TOL
 
 
-def test_layer_graph_replay_matches_eager():
-    """The block (five launches, no memset) captured once; each replay,
-    after eager work and a reset of the residual stream, equals the eager
-    result bit for bit."""
-    V, N, D, F, T = 300, 4, 256, 512, 37
+@pytest.mark.parametrize("T", [37, 3])
+def test_layer_graph_replay_matches_eager(T):
+    """The block (no memset; T = 3 takes the weight-streaming decode path)
+    captured once; each replay, after eager work and a reset of the residual
+    stream, equals the eager result bit for bit."""
+    V, N, D, F = 300, 4, 256, 512
     lut = dev(rand_table(61, V, N, D, "bf16"))
     h, w_r = (dev(a) for a in rand_hw(62, T, N, D, "bf16"))
     wu, wd = (dev(a) for a in rand_shared(63, D, F, std_up=0.05, std_down=0.05))
