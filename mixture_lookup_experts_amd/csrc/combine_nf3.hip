@@ -100,13 +100,18 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   constexpr int NPAD = ((NP + 15) / 16) * 16;
   __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * NP];
   __shared__ float gsh[kMaxTokPerBlock * NP];
-  __shared__ float lv[Q::kLevels > 0 ? Q::kLevels : 1];
+  // Decode table indexed by two consecutive codes at once (6 bits for NF3,
+  // one byte for NF4): entry p holds the levels of codes p % L and p / L.
+  // One LDS read and one bit-field extraction then serve two elements.
+  __shared__ float2 lv2[Q::kLevels > 0 ? Q::kLevels * Q::kLevels : 1];
 
   const int tid = threadIdx.x;
   if constexpr (FMT == kFmtNf3) {
-    if (tid < 8) lv[tid] = __uint_as_float(kNf3LevelBits[tid]);
+    for (int i = tid; i < 64; i += blockDim.x)
+      lv2[i] = make_float2(__uint_as_float(kNf3LevelBits[i & 7]), __uint_as_float(kNf3LevelBits[i >> 3]));
   } else if constexpr (FMT == kFmtNf4) {
-    if (tid < 16) lv[tid] = __uint_as_float(kNf4LevelBits[tid]);
+    for (int i = tid; i < 256; i += blockDim.x)
+      lv2[i] = make_float2(__uint_as_float(kNf4LevelBits[i & 15]), __uint_as_float(kNf4LevelBits[i >> 4]));
   }
   const int grp = tid / G, lig = tid % G;  // tpb = blockDim.x / G, passed in
   const int sp = lig / CP, ch = lig % CP;          // expert split, chunk
@@ -197,17 +202,24 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
           const float ws = gsh[grp * NP + e] * sv;
           const uint32_t* w = cw[j];
           if constexpr (FMT == kFmtNf3) {
+            // code pair q = bits 6q .. 6q + 5 of the chunk's 96 bits
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
-              const int pos = 3 * i, wd = pos >> 5, off = pos & 31;
-              uint32_t code;
-              if (off <= 29) code = (w[wd] >> off) & 7u;
-              else code = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off) & 7u;
-              acc[i] = fmaf(ws, lv[code], acc[i]);
+            for (int q = 0; q < 16; ++q) {
+              const int pos = 6 * q, wd = pos >> 5, off = pos & 31;
+              uint32_t pr;
+              if (off <= 26) pr = (w[wd] >> off) & 63u;
+              else pr = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off) & 63u;
+              const float2 l = lv2[pr];
+              acc[2 * q] = fmaf(ws, l.x, acc[2 * q]);
+              acc[2 * q + 1] = fmaf(ws, l.y, acc[2 * q + 1]);
             }
           } else if constexpr (FMT == kFmtNf4) {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) acc[i] = fmaf(ws, lv[(w[i >> 3] >> (4 * (i & 7))) & 15u], acc[i]);
+            for (int q = 0; q < 16; ++q) {
+              const float2 l = lv2[(w[q >> 2] >> (8 * (q & 3))) & 255u];
+              acc[2 * q] = fmaf(ws, l.x, acc[2 * q]);
+              acc[2 * q + 1] = fmaf(ws, l.y, acc[2 * q + 1]);
+            }
           } else {
 #pragma unroll
             for (int i = 0; i < 32; ++i) {
