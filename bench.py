@@ -204,6 +204,8 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / args.steps
     row_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
               for i, name in enumerate(ROWS)}
+    sweep = batch_sweep(torch, mole, synth, w, perm, to_dev, lut, codes if nf3 else None,
+                        scales if nf3 else None, w_r, stream)
 
     # ---------------- per-row algorithmic work
     bL = 2 if bf16 else 4
@@ -270,6 +272,7 @@ def main():
                              "achieved": rows["combine"]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": rows["combine"]["hbm_frac"], "traffic": None},
         "wall_s_timed": wall,
+        "batch_sweep": sweep,
     }
 
     probes = set() if args.no_scale_probe or not bf16 else set(args.probes.split(","))
@@ -294,6 +297,45 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, w, layer, ids_h[0], synth, T)
 
     print(json.dumps(result), flush=True)
+
+
+def batch_sweep(torch, mole, synth, w, perm, to_dev, lut, codes, scales, w_r, stream):
+    """The combine and the NF3 combine on this workload's table at each of
+    its batch sizes (Zipf ids): event-timed over 50 launches that cycle
+    through 8 id batches, after 5 warm-up launches.  Bytes per launch as for
+    the headline combine (gathered rows + h + y + ids + W_r)."""
+    V, D, N = w.V, w.D, w.N
+    bL = 2 if w.dtype == "bf16" else 4
+    out = {}
+    for T in sorted(w.tokens):
+        ids_l = [to_dev(synth.make_ids(w, T, step=s, perm=perm)) for s in range(8)]
+        h_l = [to_dev(synth.make_hidden(w, T, step=s)) for s in range(8)]
+        y = torch.empty((T, D), dtype=torch.float32, device=lut.device)
+        res = {}
+        runs = [("bf16" if bL == 2 else "f32",
+                 lambda i: mole.mole_lookup_combine(ids_l[i % 8], h_l[i % 8], w_r, lut, y, stream=stream),
+                 N * D * bL)]
+        if codes is not None:
+            runs.append(("nf3", lambda i: mole.mole_lookup_combine_nf3(ids_l[i % 8], h_l[i % 8], w_r, codes,
+                                                                       scales, y, stream=stream),
+                         N * (3 * D // 8 + D // 32)))
+        for name, fn, row in runs:
+            with torch.cuda.stream(stream):
+                for i in range(5):
+                    fn(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 50
+                e0.record(stream)
+                for i in range(reps):
+                    fn(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            byts = T * (row + D * bL + 4 * D + 8) + D * N * bL
+            res[name] = {"us": us, "tokens_per_s": T / (us * 1e-6), "gbs": byts / (us * 1e-6) / 1e9,
+                         "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes": byts}
+        out["T%d" % T] = res
+    return out
 
 
 def scale_probe(torch, mole, synth, dev, stream):
@@ -356,7 +398,7 @@ def scale_probe(torch, mole, synth, dev, stream):
     out["hbm_copy_gbs_measured"] = copy_gbs
     del src, dst
     perm = synth.rank_permutation(w)
-    for T in (1024, 4096):
+    for T in (256, 1024, 4096):
         for kind in ("zipf", "distinct"):
             ids_host = [torch.from_numpy(synth.make_ids(w, T, step=s, kind=kind, perm=perm)) for s in range(8)]
             ids_l = [x.to(dev) for x in ids_host]
@@ -871,13 +913,59 @@ def cpu_baseline(args, w, layer, ids, synth, T):
         oracle.lookup_combine_nf3(ids_s, h, layer.w_r, codes, scales, nthreads=cores)
         nf3_s = time.perf_counter() - t1
     step_s = build_s + pack_s + comb_s + 2 * nf3_s
+    per_config = oracle_sweep(oracle, synth, cores)
     return {"value": T / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "build on %d of %d vocabulary rows and NF3 pack of those rows, extrapolated "
                       "linearly to V; combine and NF3 combine (counted twice, device and host "
                       "table) on the full batch of %d tokens" % (nrow, w.V, T),
             "build_s_extrapolated": build_s, "pack_s_extrapolated": pack_s,
             "combine_tokens_per_s": T / comb_s, "combine_nf3_tokens_per_s": T / nf3_s if nf3_s else None,
+            "per_config": per_config,
             "measured_s": time.perf_counter() - t0}
+
+
+def oracle_sweep(oracle, synth, cores):
+    """The oracle's combine (and NF3 combine on the NF3 workload) at every
+    batch size of the 160M-, 410M- and 1B-class workloads (one layer), on all
+    host cores and on one core, Zipf ids.  The tables are zero except the
+    rows the batch reads (random values there): the oracle touches only
+    those rows, and its time does not depend on the values."""
+    out = {}
+    for key in ("160m", "410m", "1b", "410m-nf3"):
+        w = synth.WORKLOADS[key]
+        V, D, N = w.V, w.D, w.N
+        rng = np.random.Generator(np.random.PCG64(20259999))
+        w_r = synth.make_router(w)
+        if w.nf3:
+            codes = np.zeros((V, N, 3 * D // 8), dtype=np.uint8)
+            scales = np.zeros((V, N, D // 64), dtype=np.uint16)
+        else:
+            table = np.zeros((V, N, D), dtype=np.uint16)
+        res = {}
+        for T in sorted(w.tokens):
+            ids = synth.make_ids(w, T)
+            h = synth.make_hidden(w, T)
+            rows = np.unique(ids)
+            if w.nf3:
+                codes[rows] = rng.integers(0, 256, size=(rows.size, N, 3 * D // 8), dtype=np.uint8)
+                scales[rows] = 0x2000  # fp16 2^-7
+                fn = lambda nt: oracle.lookup_combine_nf3(ids, h, w_r, codes, scales, nthreads=nt)
+            else:
+                table[rows] = synth.f32_to_bf16_bits(
+                    rng.standard_normal(size=(rows.size, N, D), dtype=np.float32) * np.float32(0.02))
+                fn = lambda nt: oracle.lookup_combine(ids, h, w_r, table, nthreads=nt)
+            r = {}
+            for label, nt in (("all_cores", cores), ("one_core", 1)):
+                reps, t1 = 0, time.perf_counter()
+                while True:
+                    fn(nt)
+                    reps += 1
+                    if time.perf_counter() - t1 > 0.05:
+                        break
+                r[label + "_tokens_per_s"] = T * reps / (time.perf_counter() - t1)
+            res["T%d" % T] = r
+        out[key] = res
+    return out
 
 
 if __name__ == "__main__":

@@ -48,6 +48,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxTokPerBlock = 16;  // one 16-row MFMA tile of tokens
+constexpr int64_t kSimdsPerChip = 1024;  // MI355X: 256 compute units x 4 SIMDs
 
 // Router on the matrix cores for the block's `tpb` (<= 16) tokens starting
 // at t0: logits[t][e] = sum_d h[t0+t][d] * w_r[e][d] (bf16 products, fp32

@@ -78,7 +78,13 @@ struct SplitReduce {
   }
 };
 
-template <typename TH, int NP, int CP, int S, int MODE, int FMT = kFmtNf3>
+// W > 1 (small batches, one token per block): the block's W wavefronts
+// share one token.  Wavefront w takes the experts ((j W + w) S + s), the W
+// of them route the token together (one lane group of 64 W lanes), and the
+// per-wavefront partial sums of a chunk meet in LDS; each wavefront then
+// stores a 1/W share of the chunk's outputs.  This spreads a decode-sized
+// batch over W times as many wavefronts.
+template <typename TH, int NP, int CP, int S, int MODE, int FMT = kFmtNf3, int W = 1>
 __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
     const int64_t* __restrict__ ids, const TH* __restrict__ h, const TH* __restrict__ w_r,
     const uint8_t* __restrict__ codes, const void* __restrict__ scales_v,
@@ -87,10 +93,13 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   constexpr int G = CP * S;                        // lanes per token (<= 64)
   static_assert(G <= kWave, "a token's lanes must share one wavefront");
   constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
-  constexpr int EPL = (NP + S - 1) / S;            // experts per lane
+  static_assert(W == 1 || (G == kWave && MODE == kRouterLane), "W > 1: one token per block, full wavefronts");
+  constexpr int EPL = (NP + S * W - 1) / (S * W);  // experts per lane
   constexpr int EC = EPL < Q::kBatch ? EPL : Q::kBatch;  // experts per batch of code loads
   constexpr int CW = Q::kChunkBytes / 4;           // code dwords per chunk
-  constexpr int OUT = 32 / S;                      // outputs stored per lane and chunk
+  constexpr int OUT = 32 / S;                      // sums per lane and chunk after the split reduce
+  static_assert(OUT % W == 0, "each wavefront stores a whole share of a lane's sums");
+  constexpr int OW = OUT / W;                      // outputs stored per lane and chunk
   // Router: on the matrix cores (bf16 h, several tokens per block), else on
   // the vector units (one token per block, or fp32 h; element-wise beyond
   // 16 experts).
@@ -104,6 +113,9 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   // one byte for NF4): entry p holds the levels of codes p % L and p / L.
   // One LDS read and one bit-field extraction then serve two elements.
   __shared__ float2 lv2[Q::kLevels > 0 ? Q::kLevels * Q::kLevels : 1];
+  // W > 1: the wavefronts' partial sums, [wavefront][sum][lane] (lane-minor:
+  // conflict-free writes and reads).
+  __shared__ float xw[W > 1 ? W * OUT * kWave : 1];
 
   const int tid = threadIdx.x;
   if constexpr (FMT == kFmtNf3) {
@@ -115,8 +127,9 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   }
   const int grp = tid / G, lig = tid % G;  // tpb = blockDim.x / G, passed in
   const int sp = lig / CP, ch = lig % CP;          // expert split, chunk
+  const int wsp = W > 1 ? grp : 0;                 // W > 1: this wavefront's share of the experts
   const int64_t t0 = (int64_t)blockIdx.x * tpb;
-  const int64_t t = t0 + grp;
+  const int64_t t = W > 1 ? t0 : t0 + grp;
   const bool valid = t < T_;
   const int64_t tt = valid ? t : 0;
   const int C = D / 32;                            // 32-element chunks per row
@@ -131,7 +144,7 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   auto load_batch = [&](int c, int j0) {
 #pragma unroll
     for (int j = 0; j < EC; ++j) {
-      const int e = (j0 + j) * S + sp;
+      const int e = ((j0 + j) * W + wsp) * S + sp;
       if (e < N) {
         const uint8_t* src = crow0 + (int64_t)e * row_bytes + (int64_t)c * Q::kChunkBytes;
         if constexpr (FMT == kFmtNf3) {
@@ -159,14 +172,17 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   if constexpr (kMfmaRouter)
     rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
                   N, (G * tpb) / kWave);
-  if constexpr (kLaneRouter) lr.load_first(h + tt * D, w_r, D, N, lig);
+  if constexpr (kLaneRouter) lr.load_first(h + tt * D, w_r, D, N, W > 1 ? tid : lig);
 
   // Gates of the block's tokens into gsh[token][expert].
   if constexpr (kMfmaRouter) {
     rt.finish(tpb, red, gsh);
   } else if constexpr (kLaneRouter) {
     float gate[NP];
-    lr.template finish<G>(h + tt * D, w_r, D, N, lig, valid, gate, red + grp * NP);
+    if constexpr (W > 1)
+      lr.template finish<G * W>(h + tt * D, w_r, D, N, tid, valid, gate, red);
+    else
+      lr.template finish<G>(h + tt * D, w_r, D, N, lig, valid, gate, red + grp * NP);
     if (lig == 0) {
 #pragma unroll
       for (int e = 0; e < NP; ++e) gsh[grp * NP + e] = gate[e];
@@ -185,18 +201,22 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   }
   if (!valid) return;
 
-  for (int k = 0; k * CP + ch < C; ++k) {
+  // Every lane walks the same number of chunk rounds (W > 1 has barriers
+  // inside); a lane whose chunk is past the row does no work in a round.
+  const int rounds = (C + CP - 1) / CP;
+  for (int k = 0; k < rounds; ++k) {
     const int c = k * CP + ch;
+    const bool act = c < C;
     float acc[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int j0 = 0; j0 < EPL; j0 += EC) {
-      if (k != 0 || j0 != 0) load_batch(c, j0);
+      if (act && (k != 0 || j0 != 0)) load_batch(c, j0);
 #pragma unroll
       for (int j = 0; j < EC; ++j) {
-        const int e = (j0 + j) * S + sp;
-        if (e < N) {
+        const int e = ((j0 + j) * W + wsp) * S + sp;
+        if (act && e < N) {
           const float sv = FMT == kFmtI8 ? __uint_as_float(sc[j])
                                          : (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j]);
           const float ws = gsh[grp * NP + e] * sv;
@@ -231,13 +251,29 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
       }
     }
     SplitReduce<CP, S>::run(acc, sp);
-    float* yo = y + tt * D + (int64_t)c * 32 + SplitReduce<CP, S>::offset(sp);
-    if constexpr (OUT >= 4) {
+    if constexpr (W > 1) {
+      // the W wavefronts' sums of this chunk meet in LDS (added in wavefront order)
 #pragma unroll
-      for (int j = 0; j < OUT; j += 4) stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
-    } else {
+      for (int j = 0; j < OUT; ++j) xw[(wsp * OUT + j) * kWave + lig] = acc[j];
+      __syncthreads();
 #pragma unroll
-      for (int j = 0; j < OUT; ++j) __builtin_nontemporal_store(acc[j], yo + j);
+      for (int q = 0; q < OW; ++q) {
+        float a = 0.f;
+#pragma unroll
+        for (int u = 0; u < W; ++u) a += xw[(u * OUT + wsp * OW + q) * kWave + lig];
+        acc[q] = a;
+      }
+      __syncthreads();  // xw is rewritten in the next round
+    }
+    if (act) {
+      float* yo = y + tt * D + (int64_t)c * 32 + SplitReduce<CP, S>::offset(sp) + wsp * OW;
+      if constexpr (OW >= 4) {
+#pragma unroll
+        for (int j = 0; j < OW; j += 4) stg16_nt(yo + j, acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < OW; ++j) __builtin_nontemporal_store(acc[j], yo + j);
+      }
     }
   }
 }
@@ -258,8 +294,21 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   // One token per block: the vector-unit router (see LaneRouter).
   if constexpr (sizeof(TH) == 2 && NP <= 16) {
     if (tpb == 1) {
-      hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterLane, FMT>), dim3((unsigned)blocks),
-                         dim3(G), 0, s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, 1);
+      // Wavefronts per token: doubled (up to 4) while the batch would still
+      // have at most one wavefront per SIMD and every wavefront keeps at
+      // least one expert per split.
+      int W = 1;
+      if constexpr (G == kWave)
+        while (W < 4 && 2 * W * S <= NP && T * 2 * W <= kSimdsPerChip) W *= 2;
+#define MOLE_NF3_W(WV)                                                                                     \
+  hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterLane, FMT, WV>), dim3((unsigned)blocks), \
+                     dim3(G * WV), 0, s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, 1)
+      if constexpr (G == kWave) {
+        if (W == 4) { MOLE_NF3_W(4); return hipGetLastError(); }
+        if (W == 2) { MOLE_NF3_W(2); return hipGetLastError(); }
+      }
+      MOLE_NF3_W(1);
+#undef MOLE_NF3_W
       return hipGetLastError();
     }
   }
