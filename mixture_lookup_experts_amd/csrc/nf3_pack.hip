@@ -81,9 +81,16 @@ __global__ __launch_bounds__(256) void pack_nf3_kernel(const T* __restrict__ lut
       uint32_t bits = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int j = 0; j < 7; ++j) c += (x[i] > thr[j]) ? 1u : 0u;
+        // The code is the number of thresholds below x; the thresholds are
+        // non-decreasing (ascending midpoints times one non-negative scale,
+        // each product rounded), so a branch-free binary search -- 3
+        // compares and 4 selects -- counts the same as 7 compares (a NaN x
+        // fails every compare either way).
+        const float v = x[i];
+        const bool b2 = v > thr[3];
+        const bool b1 = v > (b2 ? thr[5] : thr[1]);
+        const bool b0 = v > (b2 ? (b1 ? thr[6] : thr[4]) : (b1 ? thr[2] : thr[0]));
+        uint32_t c = (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
         if (sc == 0.f) c = 3u;
         bits |= c << (3 * i);
       }

@@ -83,9 +83,18 @@ __global__ __launch_bounds__(256) void pack_nf4_kernel(const T* __restrict__ lut
       uint32_t word = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int j = 0; j < 15; ++j) c += (x[i] > thr[j]) ? 1u : 0u;
+        // The code is the number of thresholds below x.  The thresholds are
+        // non-decreasing (ascending midpoints times one non-negative
+        // scale, each product rounded), so a branch-free binary search
+        // over the 15 of them -- 4 compares and 11 selects -- counts the
+        // same as 15 compares (a NaN x fails every compare either way).
+        const float v = x[i];
+        const bool b3 = v > thr[7];
+        const bool b2 = v > (b3 ? thr[11] : thr[3]);
+        const bool b1 = v > (b3 ? (b2 ? thr[13] : thr[9]) : (b2 ? thr[5] : thr[1]));
+        const bool b0 = v > (b3 ? (b2 ? (b1 ? thr[14] : thr[12]) : (b1 ? thr[10] : thr[8]))
+                                : (b2 ? (b1 ? thr[6] : thr[4]) : (b1 ? thr[2] : thr[0])));
+        uint32_t c = (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
         if (sc == 0.f) c = 7u;
         word |= c << (4 * i);
       }
