@@ -286,7 +286,14 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
                              const void* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
   constexpr int S = 64 / CP < NP ? 64 / CP : NP;  // expert splits per token
   constexpr int G = CP * S;
-  const int tpb = pick_tokens_per_block(T, G);
+  // Up to T = 1024 (bf16 h, NP <= 16, full-wavefront tokens): one token per
+  // workgroup with the vector-unit router, spread over W wavefronts below;
+  // measured on the 410M-class table at T = 1024: NF3 11.5 -> 8.7 us, NF4
+  // 11.5 -> 9.2 us, int8 11.1 -> 9.0 us.  At T = 4096 the matrix-core router
+  // over several tokens per workgroup stays ahead for NF3 and NF4 (18.2
+  // against 23.7 us).
+  const bool one_token = G == kWave && sizeof(TH) == 2 && NP <= 16 && T <= 1024;
+  const int tpb = one_token ? 1 : pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;
   // (No staged-router launch here: this kernel is bound by its decode
   // arithmetic, and the extra launch measured slower -- 410M-class NF3
@@ -295,11 +302,11 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   if constexpr (sizeof(TH) == 2 && NP <= 16) {
     if (tpb == 1) {
       // Wavefronts per token: doubled (up to 4) while the batch would still
-      // have at most one wavefront per SIMD and every wavefront keeps at
+      // have at most two wavefronts per SIMD and every wavefront keeps at
       // least one expert per split.
       int W = 1;
       if constexpr (G == kWave)
-        while (W < 4 && 2 * W * S <= NP && T * 2 * W <= kSimdsPerChip) W *= 2;
+        while (W < 4 && 2 * W * S <= NP && T * 2 * W <= 2 * kSimdsPerChip) W *= 2;
 #define MOLE_NF3_W(WV)                                                                                     \
   hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterLane, FMT, WV>), dim3((unsigned)blocks), \
                      dim3(G * WV), 0, s, ids, (const TH*)h, (const TH*)w_r, codes, scales, y, T, D, N, 1)
