@@ -291,8 +291,9 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   // measured on the 410M-class table at T = 1024: NF3 11.5 -> 8.7 us, NF4
   // 11.5 -> 9.2 us, int8 11.1 -> 9.0 us.  At T = 4096 the matrix-core router
   // over several tokens per workgroup stays ahead for NF3 and NF4 (18.2
-  // against 23.7 us).
-  const bool one_token = G == kWave && sizeof(TH) == 2 && NP <= 16 && T <= 1024;
+  // against 23.7 us), but not for int8, whose decode is lighter (one token
+  // per workgroup: 23.6 -> 20.5 us with Zipf ids, 28.7 -> 26.5 us distinct).
+  const bool one_token = G == kWave && sizeof(TH) == 2 && NP <= 16 && (T <= 1024 || FMT == kFmtI8);
   const int tpb = one_token ? 1 : pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;
   // (No staged-router launch here: this kernel is bound by its decode
