@@ -83,6 +83,9 @@ COMBINE_CASES = [
     (300, 16, 1024, 2051, "bf16"),  # ragged last block and router tile
     (200, 5, 256, 3001, "bf16"),    # N padded to 8
     (100, 64, 512, 2048, "bf16"),   # largest N
+    # either side of the one-token-per-workgroup limit (T = 1024)
+    (300, 16, 1024, 1024, "bf16"),
+    (300, 16, 1024, 1025, "bf16"),  # two tokens per workgroup, matrix-core router, ragged last block
 ]
 
 
@@ -234,7 +237,10 @@ def run_nf3(ids, h, w_r, codes, scales):
                                            (40, 1, 64, 5, "bf16"),
                                            # large batches with several tokens per block
                                            (300, 16, 1024, 2051, "bf16"), (200, 5, 256, 3001, "bf16"),
-                                           (100, 64, 512, 2048, "bf16")])
+                                           (100, 64, 512, 2048, "bf16"),
+                                           # either side of the one-token-per-workgroup limit
+                                           (300, 16, 1024, 1024, "bf16"), (300, 16, 1024, 1025, "bf16"),
+                                           (200, 8, 512, 600, "bf16")])
 def test_combine_nf3_matches_oracle(V, N, D, T, dtype):
     seed = 2000 + V + N + D
     table = rand_table(seed, V, N, D, "bf16")
