@@ -296,9 +296,8 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   const bool one_token = G == kWave && sizeof(TH) == 2 && NP <= 16 && (T <= 1024 || FMT == kFmtI8);
   const int tpb = one_token ? 1 : pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;
-  // (No staged-router launch here: this kernel is bound by its decode
-  // arithmetic, and the extra launch measured slower -- 410M-class NF3
-  // table, T=4096: 20.1 -> 22.6 us.)
+  // (No staged-router launch here: the extra launch measured slower --
+  // 410M-class NF3 table, T=4096: 20.1 -> 22.6 us.)
   // One token per block: the vector-unit router (see LaneRouter).
   if constexpr (sizeof(TH) == 2 && NP <= 16) {
     if (tpb == 1) {
