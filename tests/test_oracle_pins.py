@@ -745,3 +745,95 @@ def test_train_backward_zero_upstream_and_untouched_rows():
     got = oracle.train_backward(ids, emb, wu, wd, h, wr, np.ones((ids.size, emb.shape[1])))
     untouched = np.setdiff1d(np.arange(emb.shape[0]), ids)
     assert np.all(got["d_emb"][untouched] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Exact ties at the decision thresholds (results section: 3-bit table; the
+# threshold rule fixed for this build is code = #{j : x > fp32(mid_j * s)},
+# strict, so an element equal to a threshold takes the lower code).  Inputs
+# and expected bytes are literals: the fp32 bit patterns of the midpoints
+# (pinned against exact fractions by the midpoint tests above), of their
+# products with the fp16 scale 0x2E66 (= 0.0999755859375) rounded once to
+# fp32, and of their fp32 neighbours; the codes follow from the rule by
+# hand, and the bytes from packing those codes LSB-first.
+# ---------------------------------------------------------------------------
+def f32s(*hexes):
+    return [struct.unpack("<f", struct.pack("<I", h))[0] for h in hexes]
+
+
+def next_up(x):
+    return float(np.nextafter(np.float32(x), np.float32(np.inf)))
+
+
+def next_down(x):
+    return float(np.nextafter(np.float32(x), np.float32(-np.inf)))
+
+
+NF3_MID_S1 = f32s(0xbf447ba0, 0xbec82e26, 0xbdfcdb98, 0x3dbbbcd2, 0x3e90b990, 0x3f00a32c, 0x3f4fbdff)
+# fp32(mid_j * 0.0999755859375)
+NF3_THR_S = f32s(0xbd9d25e0, 0xbd201ae9, 0xbc4a3ca2, 0x3c162745, 0x3ce780d4, 0x3d4dc503, 0x3da62736)
+NF4_MID_S1 = f32s(0xbf591cd8, 0xbf1c5270, 0xbeeb847d, 0xbeadea74, 0xbe703cea, 0xbe0d38b9, 0xbd3a7869,
+                  0x3d22fb01, 0x3df64860, 0x3e5067dc, 0x3e9582d2, 0x3ec753f6, 0x3f006d02, 0x3f248dac,
+                  0x3f5c89d8)
+NF4_THR_S = f32s(0xbdada5d2, 0xbd7a0dde, 0xbd3c5e37, 0xbd0b1944, 0xbcc024b8, 0xbc61e63c, 0xbb9523ce,
+                 0x3b825a41, 0x3c44fa63, 0x3ca6af11, 0x3cef28c3, 0x3d1f6c67, 0x3d4d6e5f, 0x3d839c4f,
+                 0x3db06340)
+S_FP16_BITS = 0x2E66  # fp16 nearest to 0.1, exactly 0.0999755859375
+
+
+def tie_blocks(mid_s1, thr_s):
+    """Two 64-element blocks.  Block A: absmax 1.0 (scale 0x3C00, thresholds
+    = the midpoints), then for each j: mid_j, its upper and its lower fp32
+    neighbour.  Block B: absmax -0.0999755859375 (scale 0x2E66), then for
+    each j: the threshold fp32(mid_j * s) and its upper neighbour.  The rest
+    are zeros."""
+    a = [1.0]
+    for m in mid_s1:
+        a += [m, next_up(m), next_down(m)]
+    b = [-0.0999755859375]
+    for t in thr_s:
+        b += [t, next_up(t)]
+    a += [0.0] * (64 - len(a))
+    b += [0.0] * (64 - len(b))
+    return np.array([a + b], dtype=np.float32)
+
+
+def test_nf3_exact_threshold_ties_take_the_lower_code():
+    x = tie_blocks(NF3_MID_S1, NF3_THR_S)
+    assert x[0, 0] == 1.0 and abs(x[0, 64]) == np.float32(0.0999755859375)
+    codes, scales, nsat = oracle.pack_nf3(x)
+    assert nsat == 0 and scales.tolist() == [[0x3C00, S_FP16_BITS]]
+    c = read_codes_python(codes[0], 128)
+    # block A: 1.0 -> 7; (tie, above, below) at mid_j -> (j, j+1, j); zeros -> 3
+    assert c[:22] == [7, 0, 1, 0, 1, 2, 1, 2, 3, 2, 3, 4, 3, 4, 5, 4, 5, 6, 5, 6, 7, 6]
+    # block B: -s -> 0; (tie, above) at thr_j -> (j, j+1)
+    assert c[64:79] == [0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5, 6, 6, 7]
+    assert set(c[22:64]) == {3} and set(c[79:]) == {3}
+    assert bytes(codes[0]).hex() == (
+        "471045d33896757d6fdbb66ddbb66ddbb66ddbb66ddbb66d"
+        "40226d646b7fdbb66ddbb66ddbb66ddbb66ddbb66ddbb66d")
+
+
+def test_nf4_exact_threshold_ties_take_the_lower_code():
+    x = tie_blocks(NF4_MID_S1, NF4_THR_S)
+    codes, scales, nsat = oracle.pack_nf4(x)
+    assert nsat == 0 and scales.tolist() == [[0x3C00, S_FP16_BITS]]
+    c = [(int(codes[0, i // 2]) >> (4 * (i % 2))) & 15 for i in range(128)]
+    assert c[:46] == [15] + [v for j in range(15) for v in (j, j + 1, j)]
+    assert c[64:95] == [0] + [v for j in range(15) for v in (j, j + 1)]
+    assert set(c[46:64]) == {7} and set(c[95:]) == {7}
+    assert bytes(codes[0]).hex() == (
+        "0f01212123434345656567878789a9a9abcbcbcdededef777777777777777777"
+        "00112233445566778899aabbccddee7f77777777777777777777777777777777")
+
+
+def test_tie_literals_are_the_oracles_midpoints_and_products():
+    """The literal thresholds above are the midpoints the encoder uses and
+    their single-rounding fp32 products with the fp16 scale."""
+    s = np.float32(np.array([S_FP16_BITS], np.uint16).view(np.float16)[0])
+    for mids, lit_s1, lit_s in ((oracle.nf3_midpoints(), NF3_MID_S1, NF3_THR_S),
+                                (oracle.nf4_midpoints(), NF4_MID_S1, NF4_THR_S)):
+        np.testing.assert_array_equal(np.asarray(mids, np.float32), np.array(lit_s1, np.float32))
+        for m, t in zip(lit_s1, lit_s):
+            exact = Fraction(m) * Fraction(float(s))
+            assert np.float32(t) == np.float32(float(exact))  # one rounding of the exact product
