@@ -27,9 +27,13 @@
  *  - Device pointers must be 16-byte aligned (MOLE_ERR_ALIGN otherwise).
  *  - Token ids must lie in [0, V); the GPU entry points do not check ids
  *    stored in device memory (an out-of-range id reads outside the table).
- *  - Entry points hold no state between calls and may be called from
- *    several threads; calls that write the same buffers must be ordered by
- *    the caller.
+ *  - Entry points may be called from several threads; calls that write the
+ *    same buffers must be ordered by the caller.  Device-side entry points
+ *    keep no state between calls.  The host-side paths (host-resident and
+ *    file-backed tables) keep two pieces of process-wide state, created on
+ *    first use: a pool of up to 64 gather threads, and one HIP event per
+ *    distinct pinned staging area (the event that orders reuse of that
+ *    area).  mole_release_host_state() frees both.
  */
 #ifndef MOLE_H
 #define MOLE_H
@@ -47,7 +51,7 @@ extern "C" {
 #define MOLE_ERR_DTYPE (-3)       /* unknown dtype code */
 #define MOLE_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
 #define MOLE_ERR_WORKSPACE (-5)   /* workspace smaller than the minimum */
-#define MOLE_ERR_UNSUPPORTED (-6) /* a valid but unsupported shape (e.g. N > 256) */
+#define MOLE_ERR_UNSUPPORTED (-6) /* a valid but unsupported shape (e.g. N > 64) */
 #define MOLE_ERR_HIP (-7)         /* a HIP runtime call or kernel launch failed */
 #define MOLE_ERR_ID (-8)          /* a host-side token id is outside [0, V) */
 #define MOLE_ERR_IO (-9)          /* a table file could not be read or written */
@@ -67,10 +71,41 @@ int mole_last_hip_error(void);
 int mole_abi_version(void);
 
 /*
+ * Free the process-wide host state of the host-resident and file-backed
+ * paths: end the gather threads and destroy the staging-area events.  Call
+ * it only when no other thread is inside a libmole call and the streams
+ * have passed every host-resident call's copy (the events of the staging
+ * areas are destroyed).  Later calls recreate the state on first use.
+ * Returns MOLE_ERR_HIP if destroying an event fails (the rest is still
+ * released).
+ */
+int mole_release_host_state(void);
+
+/*
  * Copy the 8 NF3 reconstruction levels used by the library's kernels (fp32,
  * ascending, code c -> levels[c]) to host memory.  Host-only; no GPU call.
  */
 int mole_nf3_levels(float* levels_host);
+
+/*
+ * Copy the 7 NF3 decision thresholds of mole_pack_nf3 at unit scale (fp32,
+ * ascending: the nearest-even fp32 rounding of the exact midpoint of levels
+ * j and j+1) to host memory.  Host-only.  The kernels read the same array.
+ */
+int mole_nf3_midpoints(float* mid_host);
+
+/*
+ * The normal-CDF polynomial behind GELU(u) = u * Phi(u) in the bf16 kernels
+ * (the experts' activation; MoLE page, inference section: every expert runs
+ * over the embedding matrix).  On [-range, range], with s = u / range:
+ *     Phi(u) = 1/2 + s * (c[0] + c[1] s^2 + ... + c[9] s^18)   (fp32 Horner)
+ * clamped to [0, 1]; outside the interval u is clamped to +-range first
+ * (1 - Phi(4) = 3.2e-5 is the error there).  Copies the 10
+ * fp32 coefficients to coef_host (n >= 10, else MOLE_ERR_DIM) and the
+ * interval's half-width to *range.  Host-only; the kernels read the same
+ * array.
+ */
+int mole_gelu_phi_coefficients(float* coef_host, int n, float* range);
 
 /* ------------------------------------------------------------------------
  * LUT reparameterisation (inference section: the embedding weight matrix is
@@ -118,7 +153,9 @@ int mole_build_lut(const void* emb, const void* w_up, const void* w_down, void* 
  *   ids [T] int64      h [T][D]      w_r [N][D]      lut [V][N][D]
  *   y   [T][D] fp32 (written, never read)
  * h, w_r and lut share `dtype`.  Router dot products, softmax and the
- * combine accumulate in fp32.  T == 0 is a no-op.  1 <= N <= 256.
+ * combine accumulate in fp32.  T == 0 is a no-op.  1 <= N <= 64
+ * (MOLE_ERR_UNSUPPORTED above: the kernels keep a token's N gates in
+ * registers); the same limit holds for every combine below.
  * ------------------------------------------------------------------------ */
 int mole_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut,
                         float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
@@ -208,6 +245,9 @@ int mole_layer_forward(const int64_t* ids, const void* h, const void* w_r, const
  * in mole_lookup_combine; dtype_h is the dtype of h and w_r.
  * ------------------------------------------------------------------------ */
 int mole_nf4_levels(float* levels_host);
+
+/* The 15 NF4 decision thresholds at unit scale (as mole_nf3_midpoints). */
+int mole_nf4_midpoints(float* mid_host);
 
 int mole_pack_nf4(const void* lut, uint8_t* codes, uint16_t* scales,
                   int64_t V, int64_t N, int64_t D, int dtype, void* stream);

@@ -58,7 +58,11 @@ def library():
             "mole_status_string": (ctypes.c_char_p, [I]),
             "mole_last_hip_error": (I, []),
             "mole_abi_version": (I, []),
+            "mole_release_host_state": (I, []),
             "mole_nf3_levels": (I, [P]),
+            "mole_nf3_midpoints": (I, [P]),
+            "mole_nf4_midpoints": (I, [P]),
+            "mole_gelu_phi_coefficients": (I, [P, I, P]),
             "mole_build_lut_workspace_size": (I, [I64, I64, I64, I64, I, P, P]),
             "mole_build_lut": (I, [P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
             "mole_lookup_combine": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P]),

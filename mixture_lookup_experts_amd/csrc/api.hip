@@ -20,6 +20,7 @@
 
 #include "../../include/mole.h"
 #include "mole_kernels.hpp"
+#include "mole_tables.hpp"
 
 namespace {
 
@@ -114,6 +115,17 @@ class WorkerPool {
     }
     job_mu_.unlock();
   }
+  // Ends every worker thread (after any job in flight) and waits until they
+  // have left; a later reserve() starts new ones.
+  void shutdown() {
+    std::lock_guard<std::mutex> job(job_mu_);
+    std::unique_lock<std::mutex> lk(mu_);
+    stop_ = true;
+    ++gen_;
+    cv_.notify_all();
+    done_cv_.wait(lk, [&] { return nthreads_ == 0; });
+    stop_ = false;
+  }
 
  private:
   void loop() {
@@ -122,6 +134,10 @@ class WorkerPool {
     for (;;) {
       cv_.wait(lk, [&] { return gen_ != seen; });
       seen = gen_;
+      if (stop_) {
+        if (--nthreads_ == 0) done_cv_.notify_all();
+        return;
+      }
       if (claimed_ >= want_) continue;  // this job needs fewer workers
       const int idx = claimed_++;
       std::function<void(int)>* fn = &fn_;
@@ -136,6 +152,7 @@ class WorkerPool {
   std::function<void(int)> fn_;
   int nthreads_ = 0, want_ = 0, claimed_ = 0, pending_ = 0;
   uint64_t gen_ = 0;
+  bool stop_ = false;
 };
 
 int default_threads(int nthreads, int cap) {
@@ -323,17 +340,57 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 7; }
+int mole_abi_version(void) { return 8; }
+
+int mole_release_host_state(void) {
+  return guarded([&] {
+    WorkerPool::instance().shutdown();
+    std::lock_guard<std::mutex> lock(g_stage_mu);
+    int rc = MOLE_OK;
+    for (auto& kv : g_stage_events) {
+      const int r = hip_status(hipEventDestroy(kv.second));
+      if (rc == MOLE_OK) rc = r;
+    }
+    g_stage_events.clear();
+    return rc;
+  });
+}
+
+namespace {
+void copy_bits(const uint32_t* bits, int n, float* out) {
+  for (int i = 0; i < n; ++i) std::memcpy(out + i, bits + i, 4);
+}
+}  // namespace
 
 int mole_nf3_levels(float* levels_host) {
   if (!levels_host) return MOLE_ERR_NULL;
-  mole::nf3_levels_host(levels_host);
+  copy_bits(mole::kNf3LevelBits, 8, levels_host);
+  return MOLE_OK;
+}
+
+int mole_nf3_midpoints(float* mid_host) {
+  if (!mid_host) return MOLE_ERR_NULL;
+  copy_bits(mole::kNf3MidBits, 7, mid_host);
   return MOLE_OK;
 }
 
 int mole_nf4_levels(float* levels_host) {
   if (!levels_host) return MOLE_ERR_NULL;
-  mole::nf4_levels_host(levels_host);
+  copy_bits(mole::kNf4LevelBits, 16, levels_host);
+  return MOLE_OK;
+}
+
+int mole_nf4_midpoints(float* mid_host) {
+  if (!mid_host) return MOLE_ERR_NULL;
+  copy_bits(mole::kNf4MidBits, 15, mid_host);
+  return MOLE_OK;
+}
+
+int mole_gelu_phi_coefficients(float* coef_host, int n, float* range) {
+  if (n < mole::kPhiPolyTerms) return MOLE_ERR_DIM;
+  if (!coef_host || !range) return MOLE_ERR_NULL;
+  for (int i = 0; i < mole::kPhiPolyTerms; ++i) coef_host[i] = mole::kPhiPolyCoef[i];
+  *range = mole::kPhiPolyRange;
   return MOLE_OK;
 }
 

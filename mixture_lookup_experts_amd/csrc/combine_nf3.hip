@@ -10,16 +10,7 @@
 
 namespace mole {
 
-// NF3 reconstruction levels: the NormalFloat construction at 3 bits (levels
-// Phi^-1 of evenly spaced probabilities, 4 positive, 3 negative, an exact
-// zero, normalised to [-1, 1]), rounded to fp32.  Bit patterns:
-__constant__ uint32_t kNf3LevelBits[8] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
-                                          0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
-// NF4 levels: the same construction at 4 bits (8 positive, 7 negative, zero
-// at code 7), rounded to fp32.
-__constant__ uint32_t kNf4LevelBits[16] = {0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
-                                           0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
-                                           0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
+// Level tables: kNf3LevelBits / kNf4LevelBits (mole_tables.hpp).
 
 // Per-format constants: bytes of codes per 32-element chunk, levels in the
 // decode table (0: the code is the value), experts per batch of code loads.
@@ -377,27 +368,6 @@ hipError_t launch_lookup_combine_q(int fmt, const int64_t* ids, const void* h, c
     case kFmtNf4: return launch_q<kFmtNf4>(ids, h, w_r, codes, scales, y, T, D, N, dtype_h, s);
     case kFmtI8: return launch_q<kFmtI8>(ids, h, w_r, codes, scales, y, T, D, N, dtype_h, s);
     default: return hipErrorInvalidValue;
-  }
-}
-
-void nf3_levels_host(float* out) {
-  static const uint32_t bits[8] = {0xbf800000u, 0xbf08f740u, 0xbe7cdb98u, 0x00000000u,
-                                   0x3e3bbcd2u, 0x3ec394b6u, 0x3f1f7bfeu, 0x3f800000u};
-  for (int i = 0; i < 8; ++i) {
-    union { uint32_t u; float f; } cv;
-    cv.u = bits[i];
-    out[i] = cv.f;
-  }
-}
-
-void nf4_levels_host(float* out) {
-  static const uint32_t bits[16] = {0xbf800000u, 0xbf3239b1u, 0xbf066b2eu, 0xbeca329eu, 0xbe91a24bu, 0xbe3d353du,
-                                    0xbdba7869u, 0x00000000u, 0x3da2fb01u, 0x3e24cadfu, 0x3e7c04dau, 0x3ead0336u,
-                                    0x3ee1a4b5u, 0x3f1007a9u, 0x3f3913b0u, 0x3f800000u};
-  for (int i = 0; i < 16; ++i) {
-    union { uint32_t u; float f; } cv;
-    cv.u = bits[i];
-    out[i] = cv.f;
   }
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mole_tables.hpp"
+
 namespace mole {
 
 constexpr int kWave = 64;  // CDNA wavefront width
@@ -53,29 +55,16 @@ __device__ __forceinline__ void stg16_nt(float* p, float a, float b, float c, fl
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4_vec_t*>(p));
 }
 
-// GELU for the bf16 path: u * Phi(u) with Phi - 1/2 (an odd function)
-// replaced on [-4, 4] by the odd polynomial s*(c0 + c1 s^2 + ... + c9 s^18),
-// s = u/4, a least-squares fit to the normal CDF on Chebyshev nodes
-// (gelu_poly_fit.py next to this file derives and checks it): |error| <=
-// 6e-6 in fp32, and Phi is clamped to [0, 1] outside (1 - Phi(4) = 3.2e-5).
-// The hidden activation is rounded to bf16 (relative 2^-9) right after, so
-// the approximation is invisible there; it costs ~14 full-rate VALU slots and
-// no transcendental, which matters because a GEMM epilogue runs it once
-// per hidden unit and row.
-// Phi(u) from the same polynomial (gelu_poly(u) = u * phi_poly(u)).
+// GELU for the bf16 path: u * Phi(u), with Phi from the odd polynomial of
+// mole_tables.hpp (kPhiPolyCoef, Horner in fp32, u clamped to the fitted
+// interval, the result clamped to [0, 1]).  It costs ~14 full-rate VALU slots and no transcendental,
+// which matters because a GEMM epilogue runs it once per hidden unit and row.
 __device__ __forceinline__ float phi_poly(float u) {
-  const float s = __builtin_amdgcn_fmed3f(u, -4.0f, 4.0f) * 0.25f;
+  const float s = __builtin_amdgcn_fmed3f(u, -kPhiPolyRange, kPhiPolyRange) * (1.0f / kPhiPolyRange);
   const float s2 = s * s;
-  float p = -1.005731821e+00f;
-  p = fmaf(p, s2, 6.118065357e+00f);
-  p = fmaf(p, s2, -1.688562202e+01f);
-  p = fmaf(p, s2, 2.834799385e+01f);
-  p = fmaf(p, s2, -3.288965607e+01f);
-  p = fmaf(p, s2, 2.843501091e+01f);
-  p = fmaf(p, s2, -1.914556694e+01f);
-  p = fmaf(p, s2, 1.018382359e+01f);
-  p = fmaf(p, s2, -4.254103661e+00f);
-  p = fmaf(p, s2, 1.595752358e+00f);
+  float p = kPhiPolyCoef[kPhiPolyTerms - 1];
+#pragma unroll
+  for (int k = kPhiPolyTerms - 2; k >= 0; --k) p = fmaf(p, s2, kPhiPolyCoef[k]);
   return __builtin_amdgcn_fmed3f(fmaf(s, p, 0.5f), 0.0f, 1.0f);
 }
 
@@ -84,22 +73,7 @@ __device__ __forceinline__ float gelu_grad_poly(float u) {
   return fmaf(u * 0.3989422804014327f, __expf(-0.5f * u * u), phi_poly(u));
 }
 
-__device__ __forceinline__ float gelu_poly(float u) {
-  const float s = __builtin_amdgcn_fmed3f(u, -4.0f, 4.0f) * 0.25f;
-  const float s2 = s * s;
-  float p = -1.005731821e+00f;
-  p = fmaf(p, s2, 6.118065357e+00f);
-  p = fmaf(p, s2, -1.688562202e+01f);
-  p = fmaf(p, s2, 2.834799385e+01f);
-  p = fmaf(p, s2, -3.288965607e+01f);
-  p = fmaf(p, s2, 2.843501091e+01f);
-  p = fmaf(p, s2, -1.914556694e+01f);
-  p = fmaf(p, s2, 1.018382359e+01f);
-  p = fmaf(p, s2, -4.254103661e+00f);
-  p = fmaf(p, s2, 1.595752358e+00f);
-  const float phi = __builtin_amdgcn_fmed3f(fmaf(s, p, 0.5f), 0.0f, 1.0f);
-  return u * phi;
-}
+__device__ __forceinline__ float gelu_poly(float u) { return u * phi_poly(u); }
 
 // ---- cross-lane reductions ----------------------------------------------------
 // Reduce-scatter of NP per-lane partial sums over the W lanes (W a power of

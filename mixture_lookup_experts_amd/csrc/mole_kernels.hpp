@@ -21,8 +21,6 @@ hipError_t launch_lookup_combine(const int64_t* ids, const void* h, const void* 
 hipError_t launch_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
                                      const uint8_t* codes, const uint16_t* scales, float* y,
                                      int64_t T, int64_t D, int64_t N, int dtype_h, hipStream_t s);
-void nf3_levels_host(float* out);
-void nf4_levels_host(float* out);
 enum { kFmtNf3 = 3, kFmtNf4 = 4, kFmtI8 = 8 };  // quantised table formats (bits per element)
 // codes: NF3 [V][N][3D/8], NF4 [V][N][D/2], int8 [V][N][D]; scales: fp16
 // [V][N][D/64] for NF3/NF4, fp32 [V][N] for int8.

@@ -13,10 +13,7 @@
 
 namespace mole {
 
-// Decision thresholds between neighbouring NF3 levels: fp32 nearest-even
-// rounding of the exact midpoint of the two fp32 levels.
-__constant__ uint32_t kNf3MidBits[7] = {0xbf447ba0u, 0xbec82e26u, 0xbdfcdb98u, 0x3dbbbcd2u,
-                                        0x3e90b990u, 0x3f00a32cu, 0x3f4fbdffu};
+// Thresholds: kNf3MidBits (mole_tables.hpp).
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* x);

@@ -18,11 +18,7 @@
 
 namespace mole {
 
-// NF4 decision thresholds: fp32 nearest-even rounding of the exact midpoint
-// of two neighbouring fp32 levels (levels listed with the NF4 combine).
-__constant__ uint32_t kNf4MidBits[15] = {0xbf591cd8u, 0xbf1c5270u, 0xbeeb847du, 0xbeadea74u, 0xbe703ceau,
-                                         0xbe0d38b9u, 0xbd3a7869u, 0x3d22fb01u, 0x3df64860u, 0x3e5067dcu,
-                                         0x3e9582d2u, 0x3ec753f6u, 0x3f006d02u, 0x3f248dacu, 0x3f5c89d8u};
+// Thresholds: kNf4MidBits (mole_tables.hpp).
 
 namespace {
 

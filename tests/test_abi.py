@@ -45,7 +45,7 @@ def test_header_declares_the_hot_path():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 7
+    assert lib.mole_abi_version() == 8
 
 
 def test_status_strings(lib):
@@ -54,10 +54,119 @@ def test_status_strings(lib):
     assert mole.mole_status_string(12345) == "unknown status"
 
 
-def test_library_codebook_is_the_nf3_construction(lib):
-    """The kernels' level table equals the oracle's NormalFloat levels."""
+def nf_levels_stdlib(k):
+    """NormalFloat levels at k bits from the stdlib normal quantile: Phi^-1 at
+    2^(k-1) evenly spaced probabilities from p* down to 1/2 (1/2 dropped) for
+    the positive side, 2^(k-1) - 1 for the negative side, p* = 1 -
+    (1/(2(2^k - 1)) + 1/2^(k+1)) / 2, one exact zero, normalised by the
+    maximum, fp32."""
+    from statistics import NormalDist
+    nd = NormalDist()
+    half = 2 ** (k - 1)
+    p = 1 - 0.5 * (1 / (2 * (2 ** k - 1)) + 1 / (2 * 2 ** k))
+    pos = [nd.inv_cdf(x) for x in np.linspace(p, 0.5, half + 1)[:-1]]
+    neg = [-nd.inv_cdf(x) for x in np.linspace(p, 0.5, half)[:-1]]
+    v = sorted(pos + [0.0] + neg)
+    return np.array([x / max(v) for x in v], dtype=np.float32)
+
+
+def rne_midpoints(levels):
+    """fp32 nearest-even rounding of the exact midpoint of neighbouring levels."""
+    from fractions import Fraction
+    return np.array([float((Fraction(float(a)) + Fraction(float(b))) / 2) for a, b in zip(levels, levels[1:])],
+                    dtype=np.float32)
+
+
+@pytest.mark.parametrize("k", [3, 4])
+def test_library_codebooks_are_the_normalfloat_construction(lib, k):
+    """The level and threshold tables the kernels read (copied out by the
+    host helpers from the same arrays) against the construction done here
+    with the stdlib, and the thresholds against exact midpoints."""
+    levels = np.array(mole.mole_nf3_levels() if k == 3 else mole.mole_nf4_levels(), np.float32)
+    np.testing.assert_array_equal(levels, nf_levels_stdlib(k))
+    out = (ctypes.c_float * (2 ** k - 1))()
+    fn = lib.mole_nf3_midpoints if k == 3 else lib.mole_nf4_midpoints
+    assert fn(ctypes.addressof(out)) == OK
+    np.testing.assert_array_equal(np.array(list(out), np.float32), rne_midpoints(levels))
+    assert fn(None) == NULL
     import oracle
-    np.testing.assert_array_equal(np.array(mole.mole_nf3_levels(), np.float32), oracle.nf3_levels())
+    np.testing.assert_array_equal(levels, oracle.nf3_levels() if k == 3 else oracle.nf4_levels())
+
+
+def phi_fit():
+    """The least-squares fit behind the bf16 GELU: Phi(u) - 1/2 on 4000
+    Chebyshev nodes of [-4, 4] in the odd basis s^(2k+1), s = u/4, k < 10,
+    solved in fp64 and rounded to fp32."""
+    from scipy.special import ndtr
+    x = np.cos(np.pi * (np.arange(4000) + 0.5) / 4000) * 4.0
+    s = x / 4.0
+    basis = np.stack([s ** (2 * k + 1) for k in range(10)], axis=1)
+    c, *_ = np.linalg.lstsq(basis, ndtr(x) - 0.5, rcond=None)
+    return c
+
+
+def phi_poly_f32(u, c, rng_):
+    """fp32 evaluation as the kernels do it: clamp, Horner with fused
+    multiply-adds (one rounding each: the fp64 product of two fp32 values is
+    exact), clamp to [0, 1]."""
+    f32 = np.float32
+    s = np.clip(np.asarray(u, f32), -rng_, rng_) * f32(1.0 / rng_)
+    s2 = (s * s).astype(f32)
+    p = np.full_like(s, c[-1])
+    for k in range(len(c) - 2, -1, -1):
+        p = (p.astype(np.float64) * s2 + np.float64(c[k])).astype(f32)
+    return np.clip((s.astype(np.float64) * p + 0.5).astype(f32), 0, 1)
+
+
+def test_gelu_phi_coefficients_are_the_fit_and_within_bound(lib):
+    from scipy.special import ndtr
+    c = (ctypes.c_float * 10)()
+    r = ctypes.c_float(0)
+    assert lib.mole_gelu_phi_coefficients(ctypes.addressof(c), 9, ctypes.byref(r)) == DIM
+    assert lib.mole_gelu_phi_coefficients(None, 10, ctypes.byref(r)) == NULL
+    assert lib.mole_gelu_phi_coefficients(ctypes.addressof(c), 10, ctypes.byref(r)) == OK
+    coef = np.array(list(c), np.float32)
+    assert r.value == 4.0
+    # every coefficient is the fit's fp32 value, bit for bit
+    fit = phi_fit()
+    np.testing.assert_array_equal(coef, fit.astype(np.float32))
+    u = np.linspace(-4, 4, 400001).astype(np.float32)
+    err_in = np.abs(phi_poly_f32(u, coef, 4.0) - ndtr(u.astype(np.float64))).max()
+    assert err_in <= 1e-5, err_in
+    # outside: the argument is clamped, so the value is the one at +-4
+    out = np.concatenate([np.linspace(-30, -4, 1001), np.linspace(4, 30, 1001)]).astype(np.float32)
+    v = phi_poly_f32(out, coef, 4.0)
+    edge = phi_poly_f32(np.array([-4.0, 4.0], np.float32), coef, 4.0)
+    assert np.all(v[:1001] == edge[0]) and np.all(v[1001:] == edge[1])
+    assert np.abs(v - ndtr(out.astype(np.float64))).max() <= 3.6e-5  # 1 - Phi(4) + the fit's error at 4
+    # GELU = u * Phi(u) at textbook points (Phi(1) = 0.8413447460685429)
+    assert abs(float(phi_poly_f32(np.array([1.0], np.float32), coef, 4.0)[0]) - 0.8413447460685429) < 1e-5
+
+
+def test_release_host_state(lib):
+    """The gather pool and staging events are released and re-created on
+    use (host-only gathers, no GPU call)."""
+    assert lib.mole_release_host_state() == OK
+    V, N, D, T = 2048, 4, 256, 900
+    r = np.random.default_rng(5)
+    codes = r.integers(0, 256, (V, N, 3 * D // 8), dtype=np.uint8)
+    scales = r.integers(0, 2 ** 15, (V, N, D // 64), dtype=np.uint16)
+    ids = r.integers(0, V, T).astype(np.int64)
+    for _ in range(2):
+        cs = np.zeros((T, N, 3 * D // 8), np.uint8)
+        ss = np.zeros((T, N, D // 64), np.uint16)
+        remap = np.zeros(T, np.int64)
+        nu = ctypes.c_int64(0)
+        rc = lib.mole_gather_nf3_host(ids.ctypes.data, T, codes.ctypes.data, scales.ctypes.data, V, N, D,
+                                      cs.ctypes.data, ss.ctypes.data, remap.ctypes.data, ctypes.byref(nu), 8)
+        assert rc == OK
+        U = nu.value
+        uniq = np.array(list(dict.fromkeys(ids.tolist())), np.int64)
+        assert U == len(uniq)
+        np.testing.assert_array_equal(cs[:U], codes[uniq])
+        np.testing.assert_array_equal(ss[:U], scales[uniq])
+        np.testing.assert_array_equal(uniq[remap], ids)
+        assert lib.mole_release_host_state() == OK
 
 
 def test_workspace_size(lib):
