@@ -26,7 +26,9 @@
  *    MOLE_ERR_HIP, mole_last_hip_error() gives the hipError_t (per thread).
  *  - Device pointers must be 16-byte aligned (MOLE_ERR_ALIGN otherwise).
  *  - Token ids must lie in [0, V); the GPU entry points do not check ids
- *    stored in device memory (an out-of-range id reads outside the table).
+ *    stored in device memory (an out-of-range id reads outside the table);
+ *    mole_check_ids counts such ids on the device, for callers that want
+ *    the check.
  *  - Entry points may be called from several threads; calls that write the
  *    same buffers must be ordered by the caller.  Device-side entry points
  *    keep no state between calls.  The host-side paths (host-resident and
@@ -415,26 +417,46 @@ int mole_prefetch_nf3_host_stack(const int64_t* ids_host, int64_t T,
                                  size_t* scales_off, int nthreads, int64_t* n_unique, void* stream);
 
 /* ------------------------------------------------------------------------
- * mole_lookup_combine_grouped: the combine of mole_lookup_combine over a
- * batch grouped by distinct id (inference section: each token's expert
- * outputs are fetched by its id; a prefill batch of natural text repeats
- * ids, and every token of one id reads the same N x D table slab).  The
- * grouping comes from mole_train_index: tok [T] = the tokens grouped by
- * distinct id (its tok_host), rows [T] = the table row of each grouped
- * position (rows[p] = uniq[remap[tok[p]]]), both copied to the device.  Each
- * slab is read once per run of equal rows in a chunk of the grouped list (a
- * row with many tokens is split over chunks) instead of once per token.  y
- * [T][D] fp32 as from mole_lookup_combine, up to fp32 summation order.
- * bf16 h, w_r and table only, N <= 16, N <= D and D % 8 == 0
- * (MOLE_ERR_UNSUPPORTED otherwise).  Device-resident rows are not
- * range-checked.  Two launches on `stream`: the router (its gates are parked
- * in the first N floats of each y row) and the grouped combine.
- *   rows, tok: int64 [T], 8-byte aligned; h [T][D], w_r [N][D],
- *   lut [V][N][D] bf16; y [T][D] fp32
+ * mole_check_ids: optional device-side check of token ids (inference
+ * section: a token's rows are found by direct addressing on its id, and the
+ * combines do not check ids held in device memory).  Adds to *count (one
+ * int32 in device memory, 4-byte aligned; the caller zeroes it) the number
+ * of ids[0..T) outside [0, V).  One launch on `stream`, asynchronous; run it
+ * before a combine and read *count when convenient (e.g. in debug builds).
+ * T == 0 is a no-op.
  * ------------------------------------------------------------------------ */
-int mole_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const void* h,
-                                const void* w_r, const void* lut, float* y, int64_t T, int64_t V,
-                                int64_t D, int64_t N, int dtype, void* stream);
+int mole_check_ids(const int64_t* ids, int64_t T, int64_t V, int32_t* count, void* stream);
+
+/* ------------------------------------------------------------------------
+ * mole_lookup_combine_grouped: the combine of mole_lookup_combine with the
+ * batch grouped by token id on the device (inference section: each token's
+ * expert outputs are fetched by its id; results section: the table keeps
+ * redundancy -- a prefill batch of natural text repeats ids, and every
+ * token of one id reads the same N x D slab).  Two launches on `stream`:
+ * the first groups each chunk of 4096 tokens so that equal ids are
+ * adjacent (an LDS hash table and a scan) and, in other workgroups of the
+ * same grid, routes the tokens (bf16 matrix cores, fp32 softmax, as
+ * mole_lookup_combine), both into the workspace; the second reads each run
+ * of equal ids' slab once per 16 grouped positions instead of once per
+ * token.
+ *   ids [T] int64 (device, 8-byte aligned)   h [T][D]   w_r [N][D]
+ *   lut [V][N][D] (bf16)   y [T][D] fp32 (written)
+ * y equals mole_lookup_combine's up to fp32 summation order (each token's
+ * sum runs over its own gates and slab in expert order).  bf16 only, N <= 16,
+ * D % 8 == 0 and V < 2^31 (MOLE_ERR_UNSUPPORTED otherwise).  Device ids are
+ * not range-checked (see mole_check_ids).  T == 0 is a no-op.
+ *
+ * workspace: device scratch, 16-byte aligned, of at least the size that
+ * mole_lookup_combine_grouped_workspace_size(T) returns (72 bytes per
+ * token, each section rounded up to 256 bytes; 0 for T == 0): the grouped
+ * positions and every token's gates.  Contents on return are unspecified.  No memset and no host synchronisation (capturable in a HIP
+ * graph).
+ * ------------------------------------------------------------------------ */
+int mole_lookup_combine_grouped_workspace_size(int64_t T, size_t* bytes);
+
+int mole_lookup_combine_grouped(const int64_t* ids, const void* h, const void* w_r, const void* lut, float* y,
+                                int64_t T, int64_t V, int64_t D, int64_t N, int dtype, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Disk tier: the NF3 table in a file (inference section: the table is kept

@@ -570,19 +570,45 @@ int check_train(int64_t T, int64_t U, int64_t V, int64_t D, int64_t F, int64_t N
 }
 }  // namespace
 
-int mole_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const void* h, const void* w_r,
-                                const void* lut, float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
-                                void* stream) {
+int mole_check_ids(const int64_t* ids, int64_t T, int64_t V, int32_t* count, void* stream) {
+  if (T < 0 || V <= 0) return MOLE_ERR_DIM;
+  if (T == 0) return MOLE_OK;
+  if (!ids || !count) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || (reinterpret_cast<uintptr_t>(count) & 3u) != 0) return MOLE_ERR_ALIGN;
+  return hip_status(mole::launch_check_ids(ids, T, V, count, as_stream(stream)));
+}
+
+int mole_lookup_combine_grouped_workspace_size(int64_t T, size_t* bytes) {
+  if (T < 0 || T > kMaxDim) return MOLE_ERR_DIM;
+  if (!bytes) return MOLE_ERR_NULL;
+  *bytes = T == 0 ? 0 : mole::grouped_workspace_bytes(T);
+  return MOLE_OK;
+}
+
+namespace {
+int check_grouped(const int64_t* ids, const void* h, const void* w_r, const void* lut, float* y, int64_t T,
+                  int64_t V, int64_t D, int64_t N, int dtype) {
   if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
   int rc = check_combine_common(T, V, D, N);
   if (rc != MOLE_OK) return rc;
-  if (dtype != MOLE_BF16 || N > 16 || N > D || D % 8 != 0) return MOLE_ERR_UNSUPPORTED;
+  if (dtype != MOLE_BF16 || N > 16 || D % 8 != 0 || V > INT32_MAX) return MOLE_ERR_UNSUPPORTED;
   if (T == 0) return MOLE_OK;
-  if (!rows || !tok || !h || !w_r || !lut || !y) return MOLE_ERR_NULL;
-  if (!aligned8(rows) || !aligned8(tok) || !aligned16(h) || !aligned16(w_r) || !aligned16(lut) || !aligned16(y))
-    return MOLE_ERR_ALIGN;
-  return hip_status(mole::launch_lookup_combine_grouped(rows, tok, (const uint16_t*)h, (const uint16_t*)w_r,
-                                                        (const uint16_t*)lut, y, T, (int)D, (int)N,
+  if (!ids || !h || !w_r || !lut || !y) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(lut) || !aligned16(y)) return MOLE_ERR_ALIGN;
+  return MOLE_OK;
+}
+}  // namespace
+
+int mole_lookup_combine_grouped(const int64_t* ids, const void* h, const void* w_r, const void* lut, float* y,
+                                int64_t T, int64_t V, int64_t D, int64_t N, int dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  int rc = check_grouped(ids, h, w_r, lut, y, T, V, D, N, dtype);
+  if (rc != MOLE_OK || T == 0) return rc;
+  if (!workspace) return MOLE_ERR_NULL;
+  if (!aligned16(workspace)) return MOLE_ERR_ALIGN;
+  if (workspace_bytes < mole::grouped_workspace_bytes(T)) return MOLE_ERR_WORKSPACE;
+  return hip_status(mole::launch_lookup_combine_grouped(ids, (const uint16_t*)h, (const uint16_t*)w_r,
+                                                        (const uint16_t*)lut, y, T, (int)D, (int)N, workspace,
                                                         as_stream(stream)));
 }
 

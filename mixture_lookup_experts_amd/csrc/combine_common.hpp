@@ -116,8 +116,23 @@ struct MfmaRouter {
     lane_setup(h, w, t0, T_, tpb, D_, N_, nwaves);
     load(wave);
   }
+  // Router rows given by a token list (LDS): row r routes token tok_list[r]
+  // for r < ntok (the grouped combine's positions).
+  __device__ __forceinline__ void load_first_list(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
+                                                  const int* tok_list, int ntok, int D_, int N_, int nwaves) {
+    const int r = threadIdx.x & 15;
+    const bool ok = r < ntok;
+    lane_setup_tok(h, w, ok ? tok_list[r] : 0, ok, D_, N_, nwaves);
+    load(wave);
+  }
   __device__ __forceinline__ void lane_setup(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
                                              int64_t t0, int64_t T_, int tpb, int D_, int N_, int nwaves) {
+    const int r = threadIdx.x & 15;
+    const int64_t tok = t0 + r;
+    lane_setup_tok(h, w, tok, r < tpb && tok < T_, D_, N_, nwaves);
+  }
+  __device__ __forceinline__ void lane_setup_tok(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
+                                                 int64_t tok, bool ok, int D_, int N_, int nwaves) {
     const int lane = threadIdx.x & 63;
     wave = threadIdx.x >> 6;
     nw = nwaves;
@@ -126,8 +141,7 @@ struct MfmaRouter {
     D = D_;
     N = N_;
     w_r = w;
-    const int64_t tok = t0 + row;
-    tok_ok = row < tpb && tok < T_;
+    tok_ok = ok;
     hrow = h + (tok_ok ? tok : 0) * (int64_t)D;
     ksteps = (D + 31) / 32;
 #pragma unroll
@@ -234,12 +248,20 @@ struct LaneRouter {
   template <int G>
   __device__ __forceinline__ void finish(const T* __restrict__ h_row, const T* __restrict__ w_r, int D, int N,
                                          int lig, bool valid, float* gate, float* red /* [WG][NP] */) {
+    float part[NP];
+    partials<G>(h_row, w_r, D, N, lig, valid, part);
+    group_gates<NP, G>(part, gate, N, lig, red);
+  }
+  // The lane's partial logits (consumes the registers of load_first, so a
+  // caller can issue more loads between this and group_gates).
+  template <int G>
+  __device__ __forceinline__ void partials(const T* __restrict__ h_row, const T* __restrict__ w_r, int D, int N,
+                                           int lig, bool valid, float* part) {
     // The first chunk is consumed unconditionally and masked by a multiply
     // (a select or a branch would let the compiler sink the loads into the
     // branch below).  Masked lanes read finite in-bounds data of their own
     // token (or of token 0 for a token past the batch, whose gates are
     // unused), so the multiply by zero is exact.
-    float part[NP];
     const int C = D / V;
     const bool ok = valid && lig < C;
     const float okf = ok ? 1.f : 0.f;
@@ -271,7 +293,6 @@ struct LaneRouter {
         }
       }
     }
-    group_gates<NP, G>(part, gate, N, lig, red);
   }
 };
 

@@ -1,134 +1,289 @@
-// Lookup-combine over a batch grouped by distinct id (MoLE article,
-// inference section: each token's expert outputs are fetched by token id;
-// a prefill batch repeats ids -- Zipf-distributed text puts a few hundred
-// tokens on the commonest ids -- and every token of one id reads the same
-// N x D table slab).
+// Lookup-combine with the batch grouped by token id on the device (MoLE
+// article, inference section: each token's expert outputs are fetched by
+// token id; results section: the table keeps redundancy, and a prefill batch
+// of natural text repeats ids -- under Zipf(1.1) a third of a 4096-token
+// batch is distinct ids -- while every token of one id reads the same N x D
+// slab).
 //
-// The host index (the tokens grouped by distinct id, tok, and the table
-// row of each grouped position, rows) lets each slab be read once per run
-// of equal ids instead of once per token:
-//   * router_gates_kernel routes every token (16 per block, on the matrix
-//     cores) and leaves its N gates at the head of its output row;
-//   * a workgroup owns `seg` consecutive positions of the grouped token
-//     list; it stages their gates in LDS (before any row is overwritten --
-//     every token's row belongs to exactly one workgroup), then walks the
-//     runs of equal ids: the run's slab is loaded once (8 columns per lane,
-//     16-byte loads, N registers of 16 bytes) while the previous run is
-//     combined, and every token of the run is written from registers.
-// A row cut by a chunk boundary is loaded once per chunk it touches.
+// Two launches on the caller's stream, scratch in the caller's workspace:
+//   1. group_route_kernel, two kinds of workgroups in one grid:
+//      - grouping: one workgroup per chunk of kGroupChunk tokens puts the
+//        chunk's tokens in an order where equal ids are adjacent.  An LDS
+//        hash table (open addressing, twice as many slots as tokens) gives
+//        each distinct id a slot and each token its rank among the slot's
+//        tokens; an exclusive scan over the slot counts turns (slot, rank)
+//        into the token's position.  Written: pos_tok[p] (the token at
+//        position p) and pos_row[p] (its id).
+//      - routing: one workgroup per 16 tokens computes their gates on the
+//        matrix cores (one 16-row tile, the 16 wavefronts splitting D) and
+//        writes them to gates[t][NP] (fp32).
+//   2. lookup_combine_grouped_kernel: a workgroup owns 16 consecutive
+//      positions and one slice of the columns (grid.y).  It walks the runs
+//      of equal ids: each run's slab slice is read once -- the next run's
+//      loads in flight while the current run is combined -- and every token
+//      of the run gets its own gate-weighted sum.  Gates come from the
+//      workspace, so the column slices of a position never depend on each
+//      other.
+// The order of tokens inside a run depends on the order of the LDS atomics;
+// each token's output does not (its sum runs over its own gates and slab in
+// a fixed order).
 #include "combine_common.hpp"
 
 namespace mole {
 
 namespace {
 
-constexpr int kGroupedThreads = 128;  // 8 columns per lane: 1024 columns per workgroup
-constexpr int kMaxSegG = 64;
+constexpr int kGroupChunk = 4096;               // tokens grouped together (one workgroup)
+constexpr int kGroupSlots = 2 * kGroupChunk;    // LDS hash slots: a power of two, at least 2x the tokens
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupPerThread = kGroupSlots / kGroupThreads;  // slots scanned per thread
+constexpr int kTokPerThread = kGroupChunk / kGroupThreads;
+constexpr int kGroupedSeg = 16;                 // positions per combine workgroup
+constexpr int kGroupedLanes = 64;               // one wavefront per combine workgroup: 64 chunks of 8 columns
+
+__device__ __forceinline__ uint32_t slot_hash(uint32_t key) {
+  // multiplicative hashing (Knuth), top bits select the slot
+  return (key * 2654435761u) >> (32 - 13);
+}
+static_assert(kGroupSlots == 1 << 13, "slot_hash returns 13 bits");
+
+// Gates of 16 tokens [t0, t0 + 16) on the matrix cores, all 16 wavefronts
+// of the workgroup splitting D (one round of loads up to D = 2048 at 16
+// experts), written to gates[t][NP].
+template <int NP>
+__device__ __forceinline__ void route_tile(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_r,
+                                           float* __restrict__ gates, int64_t t0, int64_t T, int D, int N,
+                                           float* red, float* gsh) {
+  MfmaRouter<NP> rt;
+  rt.load_first(h, w_r, t0, T, kMaxTokPerBlock, D, N, kGroupThreads / kWave);
+  rt.finish(kMaxTokPerBlock, red, gsh);
+  const int tid = threadIdx.x;
+  if (tid < kMaxTokPerBlock * NP && t0 + tid / NP < T) gates[t0 * NP + tid] = gsh[tid];
+}
 
 template <int NP>
-__global__ __launch_bounds__(kGroupedThreads) void lookup_combine_grouped_kernel(
-    const int64_t* __restrict__ rows, const int64_t* __restrict__ tok, const uint16_t* __restrict__ lut, float* y,
-    int64_t T, int D, int N, int seg) {
-  __shared__ float gs[kMaxSegG][NP];
-  __shared__ int64_t ts[kMaxSegG], rowv[kMaxSegG];
-  __shared__ int runs[kMaxSegG + 1];
-  __shared__ int nruns_s;
-  const int64_t p0 = (int64_t)blockIdx.x * seg;
-  const int len = (int)(T - p0 < seg ? T - p0 : seg);
+__global__ __launch_bounds__(kGroupThreads) void group_route_kernel(const int64_t* __restrict__ ids,
+                                                                    const uint16_t* __restrict__ h,
+                                                                    const uint16_t* __restrict__ w_r, int64_t T,
+                                                                    int D, int N, int nchunks,
+                                                                    int* __restrict__ pos_tok,
+                                                                    int* __restrict__ pos_row,
+                                                                    float* __restrict__ gates) {
+  constexpr int NPAD = ((NP + 15) / 16) * 16;
+  __shared__ int keys[kGroupSlots];
+  __shared__ int cnt[kGroupSlots];
+  __shared__ int wsum[kGroupThreads / kWave];
+  static_assert(kGroupThreads / kWave * 16 * NPAD <= kGroupSlots && kMaxTokPerBlock * NP <= kGroupSlots,
+                "the router's partial tiles and gates fit the hash arrays");
+  if ((int)blockIdx.x >= nchunks) {
+    // routing workgroup: its LDS is the hash arrays' space
+    route_tile<NP>(h, w_r, gates, (int64_t)(blockIdx.x - nchunks) * kMaxTokPerBlock, T, D, N,
+                   reinterpret_cast<float*>(keys), reinterpret_cast<float*>(cnt));
+    return;
+  }
   const int tid = threadIdx.x;
-  if (tid < len) {
-    ts[tid] = tok[p0 + tid];
-    rowv[tid] = rows[p0 + tid];
+  const int64_t base = (int64_t)blockIdx.x * kGroupChunk;
+  const int len = (int)(T - base < kGroupChunk ? T - base : kGroupChunk);
+#pragma unroll
+  for (int i = 0; i < kGroupPerThread; ++i) {
+    keys[tid + i * kGroupThreads] = -1;
+    cnt[tid + i * kGroupThreads] = 0;
+  }
+  int key[kTokPerThread];
+#pragma unroll
+  for (int i = 0; i < kTokPerThread; ++i) {
+    const int q = tid + i * kGroupThreads;
+    key[i] = (int)ids[base + (q < len ? q : 0)];
   }
   __syncthreads();
-  if (tid == 0) {
+  // Insert: linear probing from the hashed slot.  At most kGroupChunk
+  // distinct keys in kGroupSlots slots, so every probe finds its key or an
+  // empty slot.  (An id of -1, invalid anyway, matches the empty marker and
+  // is grouped like any other.)
+  int slot[kTokPerThread], rank[kTokPerThread];
+#pragma unroll
+  for (int i = 0; i < kTokPerThread; ++i) {
+    const int q = tid + i * kGroupThreads;
+    slot[i] = 0;
+    rank[i] = 0;
+    if (q < len) {
+      uint32_t sl = slot_hash((uint32_t)key[i]);
+      for (int probe = 0; probe < kGroupSlots; ++probe) {
+        const int old = atomicCAS(&keys[sl], -1, key[i]);
+        if (old == -1 || old == key[i]) break;
+        sl = (sl + 1) & (kGroupSlots - 1);
+      }
+      slot[i] = (int)sl;
+      rank[i] = atomicAdd(&cnt[sl], 1);
+    }
+  }
+  __syncthreads();
+  // Exclusive scan of the slot counts: each thread owns kGroupPerThread
+  // consecutive slots; wavefront scans of the thread totals, then of the
+  // wavefront totals.
+  int c[kGroupPerThread], run = 0;
+#pragma unroll
+  for (int i = 0; i < kGroupPerThread; ++i) {
+    c[i] = cnt[tid * kGroupPerThread + i];
+    run += c[i];
+  }
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  int incl = run;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += wsum[w];
+  int off = wbase + incl - run;
+#pragma unroll
+  for (int i = 0; i < kGroupPerThread; ++i) {
+    cnt[tid * kGroupPerThread + i] = off;
+    off += c[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kTokPerThread; ++i) {
+    const int q = tid + i * kGroupThreads;
+    if (q < len) {
+      const int p = cnt[slot[i]] + rank[i];
+      pos_tok[base + p] = (int)(base + q);
+      pos_row[base + p] = key[i];
+    }
+  }
+}
+
+// One wavefront per workgroup: lane l of column slice blockIdx.y owns the
+// 16-byte chunk c = 64 * blockIdx.y + l (8 columns) of every grouped position
+// of the workgroup.
+template <int NP>
+__global__ __launch_bounds__(kGroupedLanes) void lookup_combine_grouped_kernel(
+    const int* __restrict__ pos_tok, const int* __restrict__ pos_row, const float* __restrict__ gates,
+    const uint16_t* __restrict__ lut, float* __restrict__ y, int64_t T, int D, int N) {
+  static_assert(NP <= 16, "gates and two slab slices in registers");
+  __shared__ float gsh[kGroupedSeg * NP];
+  __shared__ int ts[kGroupedSeg], rs[kGroupedSeg], runs[kGroupedSeg + 1];
+  __shared__ int nruns_s;
+  const int lane = threadIdx.x;
+  const int64_t p0 = (int64_t)blockIdx.x * kGroupedSeg;
+  const int len = (int)(T - p0 < kGroupedSeg ? T - p0 : kGroupedSeg);
+  const int C = D / 8;
+  const int c = blockIdx.y * kGroupedLanes + lane;
+  const int cc = c < C ? c : C - 1;
+  if (lane < len) {
+    ts[lane] = pos_tok[p0 + lane];
+    rs[lane] = pos_row[p0 + lane];
+  }
+  __syncthreads();
+  // the first run's slab slice goes out before the gates are staged
+  uint4 sa[NP], sb[NP];
+  {
+    const uint16_t* base = lut + (int64_t)rs[0] * N * D + (int64_t)cc * 8;
+#pragma unroll
+    for (int e = 0; e < NP; ++e) sa[e] = ldg16(base + (int64_t)(e < N ? e : N - 1) * D);
+  }
+  for (int i = lane; i < len * NP; i += kGroupedLanes) gsh[i] = gates[(int64_t)ts[i / NP] * NP + i % NP];
+  if (lane == 0) {
     int n = 0;
     for (int q = 0; q < len; ++q)
-      if (q == 0 || rowv[q] != rowv[q - 1]) runs[n++] = q;
+      if (q == 0 || rs[q] != rs[q - 1]) runs[n++] = q;
     runs[n] = len;
     nruns_s = n;
   }
-  // The first run's slab is requested before the gates are staged.
-  const int c0 = (blockIdx.y * kGroupedThreads + tid) * 8;
-  const int cc = c0 < D ? c0 : 0;  // an idle lane loads from column 0 and stores nothing
-  uint4 sa[NP], sb[NP];
-  {
-    const uint16_t* base = lut + rowv[0] * (int64_t)N * D + cc;
-#pragma unroll
-    for (int e = 0; e < NP; ++e) sa[e] = ldg16(base + (int64_t)(e < N ? e : 0) * D);
-  }
-  for (int i = tid; i < len * NP; i += kGroupedThreads) {
-    const int q = i / NP, e = i - (i / NP) * NP;
-    gs[q][e] = e < N ? y[ts[q] * D + e] : 0.f;  // the router's gates at the head of the row
-  }
   __syncthreads();
   const int nruns = nruns_s;
-  if (c0 >= D) return;  // (no barrier follows)
-  // Slab of run r (clamped to the last run, so the loads are unconditional).
-  auto load_slab = [&](int r, uint4* S) {
+  // slab slice of run r (clamped to the last run: the loads are unconditional)
+  auto load_run = [&](int r, uint4* S) {
     const int rr = r < nruns ? r : nruns - 1;
-    const uint16_t* base = lut + rowv[runs[rr]] * (int64_t)N * D + c0;
+    const uint16_t* base = lut + (int64_t)rs[runs[rr]] * N * D + (int64_t)cc * 8;
 #pragma unroll
-    for (int e = 0; e < NP; ++e) S[e] = ldg16(base + (int64_t)(e < N ? e : 0) * D);
+    for (int e = 0; e < NP; ++e) S[e] = ldg16(base + (int64_t)(e < N ? e : N - 1) * D);
   };
   auto combine_run = [&](int r, const uint4* S) {
+    if (c >= C) return;
     for (int q = runs[r]; q < runs[r + 1]; ++q) {
       float acc[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 #pragma unroll
       for (int e = 0; e < NP; ++e) {
         if (e < N) {
           float v[8];
           Elem<uint16_t>::unpack(S[e], v);
-          const float g = gs[q][e];
+          const float g = gsh[q * NP + e];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+          for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, v[j], acc[j]);
         }
       }
-      float* yo = y + ts[q] * D + c0;
+      float* yo = y + (int64_t)ts[q] * D + (int64_t)c * 8;
       stg16_nt(yo, acc[0], acc[1], acc[2], acc[3]);
       stg16_nt(yo + 4, acc[4], acc[5], acc[6], acc[7]);
     }
   };
   for (int r = 0; r < nruns; r += 2) {
-    load_slab(r + 1, sb);
+    load_run(r + 1, sb);
     combine_run(r, sa);
-    load_slab(r + 2, sa);
+    load_run(r + 2, sa);
     if (r + 1 < nruns) combine_run(r + 1, sb);
   }
 }
 
-// Chunk size: about 1024 chunks, a power of two in [4, 64].
-int grouped_chunk(int64_t T) {
-  int seg = 4;
-  while (seg < kMaxSegG && (int64_t)seg * 1024 < T) seg *= 2;
-  return seg;
+struct GroupedWs {
+  size_t tok_off, row_off, gate_off, total;
+};
+
+constexpr size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+constexpr GroupedWs grouped_ws(int64_t T) {
+  GroupedWs w{};
+  w.tok_off = 0;
+  w.row_off = round256((size_t)T * 4u);
+  w.gate_off = w.row_off + round256((size_t)T * 4u);
+  w.total = w.gate_off + round256((size_t)T * 16u * 4u);  // gates for up to 16 experts
+  return w;
+}
+
+template <int NP>
+hipError_t launch_grouped_np(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, const uint16_t* lut,
+                             float* y, int64_t T, int D, int N, void* ws, hipStream_t s) {
+  const GroupedWs lay = grouped_ws(T);
+  char* base = static_cast<char*>(ws);
+  int* pos_tok = reinterpret_cast<int*>(base + lay.tok_off);
+  int* pos_row = reinterpret_cast<int*>(base + lay.row_off);
+  float* gates = reinterpret_cast<float*>(base + lay.gate_off);
+  const int nchunks = (int)((T + kGroupChunk - 1) / kGroupChunk);
+  const int64_t rtiles = (T + kMaxTokPerBlock - 1) / kMaxTokPerBlock;
+  hipLaunchKernelGGL((group_route_kernel<NP>), dim3((unsigned)(nchunks + rtiles)), dim3(kGroupThreads), 0, s, ids,
+                     h, w_r, T, D, N, nchunks, pos_tok, pos_row, gates);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int C = D / 8;
+  const dim3 grid((unsigned)((T + kGroupedSeg - 1) / kGroupedSeg), (unsigned)((C + kGroupedLanes - 1) / kGroupedLanes));
+  hipLaunchKernelGGL((lookup_combine_grouped_kernel<NP>), grid, dim3(kGroupedLanes), 0, s, pos_tok, pos_row, gates,
+                     lut, y, T, D, N);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const uint16_t* h,
-                                         const uint16_t* w_r, const uint16_t* lut, float* y, int64_t T, int D, int N,
+size_t grouped_workspace_bytes(int64_t T) { return grouped_ws(T).total; }
+
+
+hipError_t launch_lookup_combine_grouped(const int64_t* ids, const uint16_t* h, const uint16_t* w_r,
+                                         const uint16_t* lut, float* y, int64_t T, int D, int N, void* ws,
                                          hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int NP = N <= 1 ? 1 : (N <= 2 ? 2 : (N <= 4 ? 4 : (N <= 8 ? 8 : 16)));
-  const unsigned rblocks = (unsigned)((T + kMaxTokPerBlock - 1) / kMaxTokPerBlock);
-  const int seg = grouped_chunk(T);
-  const dim3 grid((unsigned)((T + seg - 1) / seg), (unsigned)((D + 8 * kGroupedThreads - 1) / (8 * kGroupedThreads)));
-#define MOLE_GROUPED(NPV)                                                                                      \
-  hipLaunchKernelGGL((router_gates_kernel<NPV>), dim3(rblocks), dim3(256), 0, s, h, w_r, y, T, D, N);        \
-  hipLaunchKernelGGL((lookup_combine_grouped_kernel<NPV>), grid, dim3(kGroupedThreads), 0, s, rows, tok, lut, y, \
-                     T, D, N, seg)
   switch (NP) {
-    case 1: MOLE_GROUPED(1); break;
-    case 2: MOLE_GROUPED(2); break;
-    case 4: MOLE_GROUPED(4); break;
-    case 8: MOLE_GROUPED(8); break;
-    default: MOLE_GROUPED(16); break;
+    case 1: return launch_grouped_np<1>(ids, h, w_r, lut, y, T, D, N, ws, s);
+    case 2: return launch_grouped_np<2>(ids, h, w_r, lut, y, T, D, N, ws, s);
+    case 4: return launch_grouped_np<4>(ids, h, w_r, lut, y, T, D, N, ws, s);
+    case 8: return launch_grouped_np<8>(ids, h, w_r, lut, y, T, D, N, ws, s);
+    default: return launch_grouped_np<16>(ids, h, w_r, lut, y, T, D, N, ws, s);
   }
-#undef MOLE_GROUPED
-  return hipGetLastError();
 }
 
 }  // namespace mole

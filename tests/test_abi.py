@@ -38,7 +38,9 @@ def test_header_declares_the_hot_path():
                "mole_layer_workspace_size", "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4",
                "mole_pack_int8", "mole_lookup_combine_int8", "mole_train_index", "mole_train_workspace_size",
                "mole_train_forward", "mole_train_backward", "mole_nf3_file_write", "mole_nf3_file_shape",
-               "mole_gather_nf3_file", "mole_lookup_combine_nf3_file", "mole_lookup_combine_grouped"):
+               "mole_gather_nf3_file", "mole_lookup_combine_nf3_file", "mole_lookup_combine_grouped",
+               "mole_lookup_combine_grouped_workspace_size", "mole_check_ids", "mole_release_host_state",
+               "mole_nf3_midpoints", "mole_nf4_midpoints", "mole_gelu_phi_coefficients"):
         assert fn in names
 
 
@@ -581,29 +583,45 @@ def test_gathers_from_several_threads_share_the_worker_pool(tmp_path):
 
 
 def test_grouped_combine_argument_errors(lib):
-    """The grouped combine checks sizes, dtype and its limits before any
-    launch (no GPU is touched: every call here fails on the host)."""
+    """The grouped combine checks sizes, dtype, its limits and the workspace
+    before any launch (no GPU is touched: every call here fails on the host)."""
     dummy = ctypes.c_void_p(16)  # never dereferenced: the calls fail before
+    need = mole.mole_lookup_combine_grouped_workspace_size(8)
 
-    def call(T=8, V=100, D=64, N=4, dtype=_native.MOLE_BF16, ptr=dummy):
-        return lib.mole_lookup_combine_grouped(ptr, ptr, ptr, ptr, ptr, ptr, T, V, D, N, dtype, None)
+    def call(T=8, V=100, D=64, N=4, dtype=_native.MOLE_BF16, ptr=dummy, ws=dummy, ws_bytes=need):
+        return lib.mole_lookup_combine_grouped(ptr, ptr, ptr, ptr, ptr, T, V, D, N, dtype, ws, ws_bytes, None)
 
     assert call(dtype=7) == DTYPE
     assert call(D=0) == DIM
     assert call(T=-1) == DIM
     assert call(dtype=_native.MOLE_F32) == UNSUP
     assert call(N=17) == UNSUP
-    assert call(N=8, D=4) == UNSUP       # N > D
     assert call(D=60) == UNSUP           # D % 8
+    assert call(V=2 ** 31) == UNSUP      # rows are held as int32
     assert call(T=0) == OK               # empty batch: no-op
     assert call(ptr=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(ws_bytes=need - 1) == WS
+    assert call(ws=ctypes.c_void_p(24)) == ALIGN
 
 
-def test_grouped_index_orders_rows_by_id():
-    """The grouping puts each id's tokens together, in token order, and
-    rows[p] is the table row of grouped position p."""
-    import torch
-    ids = torch.tensor([7, 3, 7, 9, 3, 7], dtype=torch.int64)
-    rows, tok = mole.mole_grouped_index(ids, 10)
-    assert tok.tolist() == [0, 2, 5, 1, 4, 3]
-    assert rows.tolist() == [7, 7, 7, 3, 3, 9]
+def test_grouped_workspace_size():
+    """Three sections, each padded to 256 bytes: the grouped token and its
+    row (int32 [T] each) and the gates (fp32 [T][16])."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert mole.mole_lookup_combine_grouped_workspace_size(0) == 0
+    for T in (1, 64, 65, 4096, 5000):
+        assert mole.mole_lookup_combine_grouped_workspace_size(T) == 2 * r256(4 * T) + r256(64 * T)
+    with pytest.raises(mole.MoleError):
+        mole.mole_lookup_combine_grouped_workspace_size(-1)
+
+
+def test_check_ids_argument_errors(lib):
+    a = ctypes.c_void_p(0x1000)
+    assert lib.mole_check_ids(a, -1, 10, a, None) == DIM
+    assert lib.mole_check_ids(a, 4, 0, a, None) == DIM
+    assert lib.mole_check_ids(None, 4, 10, a, None) == NULL
+    assert lib.mole_check_ids(a, 4, 10, None, None) == NULL
+    assert lib.mole_check_ids(ctypes.c_void_p(0x1004), 4, 10, a, None) == ALIGN
+    assert lib.mole_check_ids(a, 4, 10, ctypes.c_void_p(0x1002), None) == ALIGN
+    assert lib.mole_check_ids(None, 0, 10, None, None) == OK

@@ -255,13 +255,15 @@ def test_combine_nf3_matches_oracle(V, N, D, T, dtype):
 
 
 # ----------------------------------------------------------------------------
-# lookup-combine over a batch grouped by distinct id
+# lookup-combine over a batch grouped by id on the device
 # ----------------------------------------------------------------------------
 
 def run_grouped(ids, h, w_r, lut):
-    rows, tok = mole.mole_grouped_index(torch.from_numpy(ids), lut.shape[0])
-    y = torch.full((ids.size, lut.shape[2]), float("nan"), dtype=torch.float32, device="cuda")
-    mole.mole_lookup_combine_grouped(rows.cuda(), tok.cuda(), dev(h), dev(w_r), dev(lut), y)
+    T = ids.size
+    y = torch.full((T, lut.shape[2]), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((max(mole.mole_lookup_combine_grouped_workspace_size(T), 16),), 0xAB, dtype=torch.uint8,
+                    device="cuda")  # stale contents: the kernels must not rely on a cleared workspace
+    mole.mole_lookup_combine_grouped(dev(ids), dev(h), dev(w_r), dev(lut), y, ws)
     torch.cuda.synchronize()
     return host(y)
 
@@ -271,15 +273,20 @@ def grouped_ids(r, V, T, law):
         return synth.zipf_ids(r, V, T, r.permutation(V))
     if law == "one":
         return np.full(T, V // 2, np.int64)
+    if law == "distinct":
+        return r.permutation(V)[:T].astype(np.int64)
     return r.integers(0, V, T).astype(np.int64)
 
 
 # (V, N, D, T, ids): ragged T and D, N padded to a power of two, one token,
-# runs of a hot id over many chunks (T = 3000 and 5000: 8- and 16-position
-# chunks), a single id for every token.
+# one 64-lane group (D = 64) and one to four wavefronts per workgroup, a
+# single id for every token, distinct ids only, and batches over several
+# 4096-token grouping chunks (5000, 8193: a one-token last chunk), with the
+# hot Zipf rows spread over many 16-position workgroups.
 GROUPED_CASES = [(300, 4, 768, 300, "uniform"), (300, 16, 1024, 257, "zipf"), (200, 16, 2048, 33, "zipf"),
                  (100, 1, 128, 17, "uniform"), (100, 3, 136, 19, "zipf"), (50, 16, 1024, 3000, "zipf"),
-                 (20, 8, 64, 5000, "one"), (1000, 16, 1024, 1, "uniform")]
+                 (20, 8, 64, 5000, "one"), (1000, 16, 1024, 1, "uniform"), (6000, 16, 256, 5000, "distinct"),
+                 (3000, 4, 512, 8193, "zipf"), (70, 16, 2048, 4096, "uniform")]
 
 
 @pytest.mark.parametrize("V,N,D,T,law", GROUPED_CASES)
@@ -295,16 +302,31 @@ def test_grouped_combine_matches_oracle(V, N, D, T, law):
     assert combine_rel_err(y, run_combine(ids, h, w_r, lut).astype(np.float64)) <= COMBINE_TOL
 
 
-@pytest.mark.parametrize("T", [1024, 4096])
-def test_grouped_combine_full_size_zipf(T):
-    """410M-class table, full vocabulary, Zipf(1.1) ids, every token checked."""
-    w = synth.WORKLOADS["410m"]
+@pytest.mark.parametrize("wl,T", [("410m", 1024), ("410m", 4096), ("1b", 1024), ("1b", 4096)])
+def test_grouped_combine_full_size_zipf(wl, T):
+    """410M- and 1B-class tables (D = 2048: one workgroup covers all columns),
+    full vocabulary, Zipf(1.1) ids, every token checked."""
+    w = synth.WORKLOADS[wl]
     ids = synth.make_ids(w, T, step=0)
     lut = rand_table(78, w.V, w.N, w.D, "bf16", rows=np.unique(ids))
     h = synth.make_hidden(w, T)
     w_r = synth.make_router(w)
     y = run_grouped(ids, h, w_r, lut)
     assert combine_rel_err(y, oracle.lookup_combine(ids, h, w_r, lut)) <= COMBINE_TOL
+
+
+def test_check_ids_counts_out_of_range():
+    """Direct addressing by id: the optional device check counts the ids
+    outside [0, V) (the count accumulates onto the caller's zeroed word)."""
+    V = 1000
+    ids = np.array([0, 999, 1000, -1, 5, 2 ** 40, 999, -(2 ** 40)] * 1000 + [3], np.int64)
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mole.mole_check_ids(dev(ids), V, cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 4000
+    mole.mole_check_ids(dev(np.arange(V, dtype=np.int64)), V, cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 4000
 
 
 @pytest.mark.parametrize("T", [256, 1024, 4096])
