@@ -35,6 +35,8 @@
 // fp32 path (small tables): one workgroup per (v, e) row: stage Emb[v] in
 // LDS, each thread forms hidden units u[f] with fp32 FMAs and exact-form
 // GELU (erff), then each thread forms output elements from the staged G.
+#include <algorithm>
+
 #include "mole_device.hpp"
 #include "mole_kernels.hpp"
 
@@ -68,6 +70,7 @@ enum {
 constexpr int64_t kStagedMinRowBytes = 16384;
 
 constexpr int kBK = 64;     // K slice per LDS stage (64 bf16 = 128 bytes per row)
+constexpr int kPanel = 256; // columns per panel of a panel-major operand (the build's hidden activations)
 constexpr int kXcds = 8;    // MI355X: 8 accelerator complex dies, each with its own L2
 constexpr int kGroupM = 8;  // row tiles per raster band
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every record: loads read 0, stores drop
@@ -82,6 +85,7 @@ struct GemmArgs {
   int xcd_order;  // 1: XCD-banded tile order, 0: row-major tile order
   const uint16_t* aux;  // GELU-gradient epilogue: bf16 pre-activations, laid out like C
   uint16_t* pre;        // GeluPre epilogue: bf16 pre-activations out, laid out like C
+  int64_t a_pstride, c_pstride;  // panel-major A / C: elements from one 256-column panel to the next
 };
 
 // Map the hardware workgroup id to an output tile.
@@ -157,8 +161,15 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   const int rows_b = N - n0 < BN ? N - n0 : BN;
   // Buffer resources over this tile's A and B row panels: a load past the
   // panel (a row beyond M or N) returns zeros without a branch.
-  const __amdgpu_buffer_rsrc_t ra_rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.A + z * p.sAz + (int64_t)m0 * p.lda), (short)0, (int)(rows_a * p.lda * 2), kRsrcWord3);
+  // Panel-major A: element (m, k) at A + (k / 256) * a_pstride + m * 256 + k % 256; the resource spans
+  // the tile's rows in every panel the K range touches.
+  constexpr bool kApanel = (OPS & kOpsApanel) != 0, kCpanel = (OPS & kOpsCpanel) != 0;
+  const __amdgpu_buffer_rsrc_t ra_rs =
+      kApanel ? __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(p.A + z * p.sAz + (int64_t)m0 * kPanel), (short)0,
+                    (int)(((K - 1) / kPanel) * p.a_pstride * 2 + (int64_t)rows_a * kPanel * 2), kRsrcWord3)
+              : __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + z * p.sAz + (int64_t)m0 * p.lda), (short)0,
+                                                  (int)(rows_a * p.lda * 2), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rb_rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.B + z * p.sBz + (int64_t)n0 * p.ldb), (short)0, (int)(rows_b * p.ldb * 2), kRsrcWord3);
 
@@ -185,7 +196,8 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
       off[s] = (uint32_t)((kr * ld + srow * 8) * 2);
     } else {
       const int row = srow + 32 * idx;
-      off[s] = row < lim ? (uint32_t)(row * ld * 2 + seg * 16) : kOob;
+      const int64_t pitch = (is_a && kApanel) ? kPanel : ld;
+      off[s] = row < lim ? (uint32_t)(row * pitch * 2 + seg * 16) : kOob;
     }
   }
   // MN-major operand: a buffer resource over the slice's k rows, clipped to
@@ -216,7 +228,11 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
       rs[s] = buf_load16(mn_rsrc(s < SA, slice), off[s]);
     } else {
       const int k0 = slice * kBK;
-      const uint32_t o = (k0 + seg * 8 < K) ? off[s] + (uint32_t)k0 * 2u : kOob;
+      const uint32_t kofs = (s < SA && kApanel)
+                                ? (uint32_t)((k0 / kPanel) * p.a_pstride * 2 + (k0 % kPanel) * 2)
+                                : (uint32_t)k0 * 2u;
+      // (a row past the tile has off = kOob; kOob + kofs stays below 2^32 and past every record)
+      const uint32_t o = (k0 + seg * 8 < K) ? off[s] + kofs : kOob;
       rs[s] = buf_load16(s < SA ? ra_rs : rb_rs, o);
     }
   };
@@ -351,8 +367,16 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   }
 
   const int rows_c = M - m0 < BM ? M - m0 : BM;
+  // Panel-major C (the tile is one 256-column panel): the tile's rows are a
+  // contiguous run of 512-byte rows at C + (n0 / 256) * c_pstride + m0 * 256.
+  static_assert(!kCpanel || (BN == kPanel && (EPI == kEpiGelu || EPI == kEpiStore)),
+                "panel-major C: one panel per tile, direct bf16 epilogue");
+  const int64_t ldc_t = kCpanel ? kPanel : p.ldc;  // row pitch of the tile's C rows
+  const int ncol0 = kCpanel ? n0 : 0;              // column of the tile's C base
   const __amdgpu_buffer_rsrc_t rc_rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.C + z * p.sCz + (int64_t)m0 * p.ldc), (short)0, (int)(rows_c * p.ldc * 2), kRsrcWord3);
+      kCpanel ? (void*)(p.C + z * p.sCz + (int64_t)(n0 / kPanel) * p.c_pstride + (int64_t)m0 * kPanel)
+              : (void*)(p.C + z * p.sCz + (int64_t)m0 * p.ldc),
+      (short)0, (int)(rows_c * ldc_t * 2), kRsrcWord3);
   // GELU-gradient epilogue: the u values of one row block of accumulators
   // (4 consecutive columns per group, 8 bytes) are loaded while the
   // previous block is stored; loading them between stores instead made
@@ -477,7 +501,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = n0 + wn * WN + j * 32 + 8 * g + 4 * (lane >> 5);
-          const uint32_t o = (mr < rows_c && n < N) ? (uint32_t)(mr * p.ldc * 2 + n * 2) : kOob;
+          const uint32_t o = (mr < rows_c && n < N) ? (uint32_t)(mr * ldc_t * 2 + (n - ncol0) * 2) : kOob;
           __builtin_amdgcn_raw_buffer_store_b64(
               __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, packed(i, j, g)), rc_rs, (int)o,
               0, 0);
@@ -524,9 +548,9 @@ template <int BM, int BN, int EPI, int OPS = kOpsKK>
 static hipError_t launch_gemm(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                               int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, int M, int N, int K,
                               int batch, int xcd_order, hipStream_t s, const uint16_t* aux = nullptr,
-                              uint16_t* pre = nullptr) {
+                              uint16_t* pre = nullptr, int64_t a_pstride = 0, int64_t c_pstride = 0) {
   GemmArgs p{A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, (M + BM - 1) / BM, (N + BN - 1) / BN, batch,
-             xcd_order, aux, pre};
+             xcd_order, aux, pre, a_pstride, c_pstride};
   const int64_t total = (int64_t)p.tiles_m * p.tiles_n * batch;
   hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EPI, OPS>), dim3((unsigned)total), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -550,26 +574,57 @@ size_t build_lut_rec_workspace(int64_t V, int64_t D, int64_t F, int64_t N) {
   return (size_t)rows * row_bytes;
 }
 
+// Tile order of GEMM-1 when its output is panel-major: the panels make every
+// output tile one contiguous 128 KB run whatever the order, so the order can
+// serve operand reuse (XCD bands: each XCD's concurrent tiles share W_up
+// column panels in its L2).
+constexpr int kGemm1PanelOrder = 1;
+
 hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, const uint16_t* w_down,
                                  uint16_t* lut, int64_t V, int64_t D, int64_t F, int64_t N,
                                  void* ws, size_t ws_bytes, hipStream_t s, uint16_t* pre) {
   const int64_t NF = N * F;
   const int64_t row_bytes = NF * 2;
+  // Hidden activations G of a block of vc vocabulary rows.  Panel-major
+  // (256-column panels, [N*F/256][vc][256]) when F is a whole number of
+  // panels: GEMM-1 then writes each output tile as one contiguous run and
+  // GEMM-2 reads expert e's K range from panels e*F/256 .. (e+1)*F/256 - 1.
+  // Row-major [vc][N*F] otherwise (and for the training forward, which keeps
+  // G and the pre-activations for its backward pass).
+  const bool panel = pre == nullptr && F % kPanel == 0;
   // Vocabulary rows per block: all of V when the workspace holds them,
-  // otherwise a whole number of row tiles.
+  // otherwise a whole number of row tiles; panel-major blocks keep an
+  // expert's K range under 2^31 bytes (32-bit buffer offsets).
   int64_t vc = (int64_t)(ws_bytes / (size_t)row_bytes);
+  if (panel) vc = std::min<int64_t>(vc, ((int64_t)1 << 30) / F / kBM * kBM);
   if (vc >= V) vc = V;
   else vc = vc / kBM * kBM;
   uint16_t* G = static_cast<uint16_t*>(ws);
+  const int64_t pstride = vc * kPanel;  // elements from one panel of G to the next
   for (int64_t v0 = 0; v0 < V; v0 += vc) {
     const int64_t mc = (V - v0 < vc) ? (V - v0) : vc;
-    hipError_t err =
-        pre ? launch_gemm<kBM, kBN, kEpiGeluPre>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc, (int)NF, (int)D,
-                                                 1, /*xcd_order=*/0, s, nullptr, pre + v0 * NF)
-            : launch_gemm<kBM, kBN, kEpiGelu>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc, (int)NF, (int)D, 1,
-                                              /*xcd_order=*/0, s);
+    hipError_t err;
+    if (pre)
+      err = launch_gemm<kBM, kBN, kEpiGeluPre>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc, (int)NF, (int)D, 1,
+                                               /*xcd_order=*/0, s, nullptr, pre + v0 * NF);
+    else if (panel)
+      err = launch_gemm<kBM, kBN, kEpiGelu, kOpsCpanel>(emb + v0 * D, D, 0, w_up, D, 0, G, kPanel, 0, (int)mc,
+                                                        (int)NF, (int)D, 1, kGemm1PanelOrder, s, nullptr, nullptr,
+                                                        0, pstride);
+    else
+      err = launch_gemm<kBM, kBN, kEpiGelu>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc, (int)NF, (int)D, 1,
+                                            /*xcd_order=*/0, s);
     if (err != hipSuccess) return err;
-    if (N * D * 2 >= kStagedMinRowBytes)
+    const bool staged = N * D * 2 >= kStagedMinRowBytes;
+    if (panel && staged)
+      err = launch_gemm<kBM, kBN, kEpiStoreStaged, kOpsApanel>(G, kPanel, (F / kPanel) * pstride, w_down, F, D * F,
+                                                               lut + v0 * N * D, N * D, D, (int)mc, (int)D, (int)F,
+                                                               (int)N, /*xcd_order=*/1, s, nullptr, nullptr, pstride);
+    else if (panel)
+      err = launch_gemm<kBM, kBN, kEpiStore, kOpsApanel>(G, kPanel, (F / kPanel) * pstride, w_down, F, D * F,
+                                                         lut + v0 * N * D, N * D, D, (int)mc, (int)D, (int)F, (int)N,
+                                                         /*xcd_order=*/1, s, nullptr, nullptr, pstride);
+    else if (staged)
       err = launch_gemm<kBM, kBN, kEpiStoreStaged>(G, NF, F, w_down, F, D * F, lut + v0 * N * D, N * D, D,
                                                    (int)mc, (int)D, (int)F, (int)N, /*xcd_order=*/1, s);
     else

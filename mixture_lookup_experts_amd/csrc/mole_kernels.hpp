@@ -37,9 +37,14 @@ hipError_t launch_pack_int8(const void* lut, int8_t* codes, float* scales, int64
 hipError_t launch_pack_nf3(const void* lut, uint8_t* codes, uint16_t* scales, int64_t rows,
                            int64_t D, int dtype, hipStream_t s);
 
-// combine_grouped.hip: the combine over a batch grouped by distinct id
-hipError_t launch_lookup_combine_grouped(const int64_t* rows, const int64_t* tok, const uint16_t* h,
-                                         const uint16_t* w_r, const uint16_t* lut, float* y, int64_t T, int D, int N,
+// check_ids.hip: *count += number of ids outside [0, V)
+hipError_t launch_check_ids(const int64_t* ids, int64_t T, int64_t V, int* count, hipStream_t s);
+
+// combine_grouped.hip: the combine over a batch grouped by id on the device;
+// ws holds the grouped positions (grouped_workspace_bytes(T) bytes).
+size_t grouped_workspace_bytes(int64_t T);
+hipError_t launch_lookup_combine_grouped(const int64_t* ids, const uint16_t* h, const uint16_t* w_r,
+                                         const uint16_t* lut, float* y, int64_t T, int D, int N, void* ws,
                                          hipStream_t s);
 
 // build_lut.hip
@@ -58,7 +63,10 @@ hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t*
 // GEMM operand storage (bit 0 for A, bit 1 for B): K-contiguous, A[m][k] at
 // A[m*lda + k] (the default), or MN-major, A[m][k] at A[k*lda + m] (a
 // transposed matrix read in place).
-enum { kOpsKK = 0, kOpsAmn = 1, kOpsBmn = 2, kOpsMnMn = 3 };
+// Bits 2 and 3 select panel-major storage for A and for C: element (m, k)
+// at base + (k / 256) * pstride + m * 256 + k % 256, so a 256-column panel
+// of a tile's rows is one contiguous run (the build's hidden activations).
+enum { kOpsKK = 0, kOpsAmn = 1, kOpsBmn = 2, kOpsMnMn = 3, kOpsApanel = 4, kOpsCpanel = 8 };
 hipError_t launch_gemm_gelu_grad_bf16(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                                       int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, const uint16_t* aux, int M,
                                       int N, int K, int batch, hipStream_t s);
