@@ -42,7 +42,13 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   constexpr int WG = G > kWave ? G / kWave : 1;
   constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
   constexpr int CH = VECTOR ? Elem<T>::kVec : 1;  // elements per chunk
-  constexpr int EC = NP < 16 ? NP : 16;           // experts per batch of slab loads
+  // Experts per batch of slab loads.  With the vector-unit router at 16
+  // experts the slab goes out in two halves: the first before the router's
+  // arithmetic, the second once the router's operand registers are free --
+  // all 16 rows at once with the router's operands held 146 registers, three
+  // wavefronts per SIMD instead of four.
+  constexpr bool kLaneSplit = VECTOR && sizeof(T) == 2 && MODE == kRouterLane && NP == 16;
+  constexpr int EC = kLaneSplit ? 8 : (NP < 16 ? NP : 16);
   // Router: on the matrix cores (bf16, several tokens per block), or on
   // the vector units with its loads first (one token per block, or fp32),
   // or element-wise (unaligned rows, or more than 16 experts in fp32).
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   // (Unconditional loads from clamped chunk and expert indices; lanes past
   // the row and experts past N read data they then ignore.)
   uint4 sv[EC];
+  uint4 sv2[kLaneSplit ? EC : 1];
   float sf[EC];
   {
     const int c0 = lig < C ? lig : C - 1;
@@ -117,7 +124,23 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
 #pragma unroll
     for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
   } else if constexpr (kLaneRouter) {
-    lr.template finish<G>(h + tt * D, w_r, D, N, lig, valid, gate, red + grp * WG * NP);
+    float part[NP];
+    lr.template partials<G>(h + tt * D, w_r, D, N, lig, valid, part);
+    if constexpr (kLaneSplit) {
+      // second half of the first chunk's expert rows (clamped as above)
+      const int c0 = lig < C ? lig : C - 1;
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        const int ec = EC + e < N ? EC + e : N - 1;
+        sv2[e] = ldg16(slab + (int64_t)ec * D + (int64_t)c0 * CH);
+      }
+    }
+    group_gates<NP, G>(part, gate, N, lig, red + grp * WG * NP);
+    if (tpb == 1) {
+      // one token per block: the gates are block-uniform, keep them in scalar registers
+#pragma unroll
+      for (int e = 0; e < NP; ++e) gate[e] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gate[e])));
+    }
   } else {
     float part[NP];
     router_partials<T, NP, VECTOR>(h + tt * D, w_r, D, N, lig, G, valid, part);
@@ -132,7 +155,10 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
     for (int j = 0; j < CH; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int e0 = 0; e0 < NP; e0 += EC) {
-      if (k != 0 || e0 != 0) {
+      if (kLaneSplit && k == 0 && e0 == EC) {
+#pragma unroll
+        for (int e = 0; e < EC; ++e) sv[e] = sv2[e];  // loaded during the router
+      } else if (k != 0 || e0 != 0) {
 #pragma unroll
         for (int e = 0; e < EC; ++e) {
           if (e0 + e < N) {
@@ -224,7 +250,9 @@ static hipError_t launch_dense_add(const int64_t* ids, const void* h, const void
   const int64_t blocks = (T + tpb - 1) / tpb;
   float* gbuf = ex.gates_buf ? ex.gates_buf : y;
   if constexpr (VEC && sizeof(E) == 2) {
-    if (T >= kStagedRouterMinT && tpb >= 2 && N <= D) {
+    // (The combine reads each token's gates as ceil(NP / 4) 16-byte words
+    // from the head of its row: NP <= D keeps them inside the row.)
+    if (T >= kStagedRouterMinT && tpb >= 2 && NP <= D) {
       const int64_t rblocks = (T + kMaxTokPerBlock - 1) / kMaxTokPerBlock;
       hipLaunchKernelGGL((router_gates_kernel<NP>), dim3((unsigned)rblocks), dim3(256), 0, s, (const uint16_t*)h,
                          (const uint16_t*)w_r, gbuf, T, D, N);
