@@ -459,6 +459,24 @@ int mole_lookup_combine_grouped(const int64_t* ids, const void* h, const void* w
                                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * mole_lookup_combine_grouped_noalloc: mole_lookup_combine_grouped for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments and
+ * result, minus the workspace: the library keeps it in a static device array
+ * of 4.5 MiB (each GPU it runs on holds one until the process ends), which
+ * serves batches of up to MOLE_GROUPED_NOALLOC_MAX_T tokens
+ * (MOLE_ERR_UNSUPPORTED above).  Allocates nothing.  Runs on the device of
+ * `stream` (the current device for the null stream).  Every call on one GPU
+ * shares that array: calls that overlap on one GPU (different streams, or
+ * threads) race and must be ordered by the caller, e.g. on one stream.
+ * ------------------------------------------------------------------------ */
+#define MOLE_GROUPED_NOALLOC_MAX_T 65536
+
+int mole_lookup_combine_grouped_noalloc(const int64_t* ids, const void* h, const void* w_r, const void* lut,
+                                        float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
+                                        void* stream);
+
+/* ------------------------------------------------------------------------
  * Disk tier: the NF3 table in a file (inference section: the table is kept
  * in lower-tier storage and only the retrieved outputs are loaded into GPU
  * memory; the offloading discussion names CPU memory and disk as such

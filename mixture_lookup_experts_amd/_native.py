@@ -90,6 +90,7 @@ def library():
             "mole_lookup_combine_grouped_workspace_size": (I, [I64, P]),
             "mole_check_ids": (I, [P, I64, I64, P, P]),
             "mole_lookup_combine_grouped": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
+            "mole_lookup_combine_grouped_noalloc": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_nf3_file_write": (I, [ctypes.c_char_p, P, P, I64, I64, I64]),
             "mole_nf3_file_shape": (I, [I, P, P, P]),
             "mole_gather_nf3_file": (I, [I, P, I64, I64, I64, I64, P, P, P, P, I]),
@@ -346,6 +347,24 @@ def mole_lookup_combine_grouped(ids, h, w_r, lut, y, workspace, stream=None) -> 
     _check("mole_lookup_combine_grouped", library().mole_lookup_combine_grouped(
         _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut), _ptr(y), T, V, D, N, _dtype(lut), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def mole_lookup_combine_grouped_noalloc(ids, h, w_r, lut, y, stream=None) -> None:
+    """mole_lookup_combine_grouped with the library's static device workspace
+    (no allocation; up to MOLE_GROUPED_NOALLOC_MAX_T tokens)."""
+    V, N, D = lut.shape
+    T = ids.numel()
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "h [T,D], w_r [N,D], y [T,D]")
+    _need(ids.dtype == torch.int64, "ids int64")
+    _need(h.dtype == lut.dtype == w_r.dtype and y.dtype == torch.float32, "h, w_r, lut share one dtype; y float32")
+    for t in (ids, h, w_r, lut, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_lookup_combine_grouped_noalloc", library().mole_lookup_combine_grouped_noalloc(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut), _ptr(y), T, V, D, N, _dtype(lut), _stream(stream)))
+
+
+MOLE_GROUPED_NOALLOC_MAX_T = 65536
 
 
 def mole_nf3_file_write(path: str, codes_host, scales_host) -> None:

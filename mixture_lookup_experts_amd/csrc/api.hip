@@ -612,6 +612,19 @@ int mole_lookup_combine_grouped(const int64_t* ids, const void* h, const void* w
                                                         as_stream(stream)));
 }
 
+int mole_lookup_combine_grouped_noalloc(const int64_t* ids, const void* h, const void* w_r, const void* lut,
+                                        float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
+                                        void* stream) {
+  int rc = check_grouped(ids, h, w_r, lut, y, T, V, D, N, dtype);
+  if (rc != MOLE_OK || T == 0) return rc;
+  if (T > MOLE_GROUPED_NOALLOC_MAX_T) return MOLE_ERR_UNSUPPORTED;
+  return hip_status(mole::launch_lookup_combine_grouped_noalloc(ids, (const uint16_t*)h, (const uint16_t*)w_r,
+                                                                (const uint16_t*)lut, y, T, (int)D, (int)N,
+                                                                as_stream(stream)));
+}
+
+static_assert(MOLE_GROUPED_NOALLOC_MAX_T == mole::kGroupedNoAllocMaxT, "header and library agree on the limit");
+
 int mole_train_workspace_size(int64_t T, int64_t U, int64_t D, int64_t F, int64_t N, size_t* fwd_bytes,
                               size_t* bwd_bytes) {
   if (T < 0 || U < 0 || U > T || D <= 0 || F <= 0 || N <= 0 || N * F > kMaxTrainDim || N * D > kMaxTrainDim ||

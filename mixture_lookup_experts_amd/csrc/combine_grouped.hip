@@ -27,6 +27,8 @@
 // The order of tokens inside a run depends on the order of the LDS atomics;
 // each token's output does not (its sum runs over its own gates and slab in
 // a fixed order).
+#include <mutex>
+
 #include "combine_common.hpp"
 
 namespace mole {
@@ -245,6 +247,7 @@ constexpr GroupedWs grouped_ws(int64_t T) {
   w.total = w.gate_off + round256((size_t)T * 16u * 4u);  // gates for up to 16 experts
   return w;
 }
+constexpr size_t grouped_ws_total_max() { return grouped_ws(kGroupedNoAllocMaxT).total; }
 
 template <int NP>
 hipError_t launch_grouped_np(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, const uint16_t* lut,
@@ -267,10 +270,63 @@ hipError_t launch_grouped_np(const int64_t* ids, const uint16_t* h, const uint16
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the workspace of up to kGroupedNoAllocMaxT tokens
+// in a static device array (each GPU the library runs on holds its own copy
+// until the process ends).  Host code never passes the array's name to a
+// kernel (in host code it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, looked up once per device with
+// that device current, and kept.  Every call on one GPU shares the array, so
+// calls that overlap on one GPU race; nothing in it needs clearing (each call
+// writes every position and gate it reads).
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[grouped_ws_total_max()];  // 4.5 MiB
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `s` (the current
+// device for the null stream).
+hipError_t scratch_address(hipStream_t s, void** out) {
+  int cur = 0;
+  hipError_t err = hipGetDevice(&cur);
+  if (err != hipSuccess) return err;
+  int dev = cur;
+  if (s != nullptr) {
+    err = hipStreamGetDevice(s, &dev);
+    if (err != hipSuccess) return err;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (err = hipSetDevice(dev)) != hipSuccess) return err;
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (err == hipSuccess) err = e2;
+    }
+    if (err != hipSuccess) return err;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 size_t grouped_workspace_bytes(int64_t T) { return grouped_ws(T).total; }
 
+hipError_t launch_lookup_combine_grouped_noalloc(const int64_t* ids, const uint16_t* h, const uint16_t* w_r,
+                                                 const uint16_t* lut, float* y, int64_t T, int D, int N,
+                                                 hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (T > kGroupedNoAllocMaxT) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t err = scratch_address(s, &ws);
+  if (err != hipSuccess) return err;
+  return launch_lookup_combine_grouped(ids, h, w_r, lut, y, T, D, N, ws, s);
+}
 
 hipError_t launch_lookup_combine_grouped(const int64_t* ids, const uint16_t* h, const uint16_t* w_r,
                                          const uint16_t* lut, float* y, int64_t T, int D, int N, void* ws,

@@ -46,6 +46,12 @@ size_t grouped_workspace_bytes(int64_t T);
 hipError_t launch_lookup_combine_grouped(const int64_t* ids, const uint16_t* h, const uint16_t* w_r,
                                          const uint16_t* lut, float* y, int64_t T, int D, int N, void* ws,
                                          hipStream_t s);
+// The same with the workspace in the library's static device array (T up to
+// kGroupedNoAllocMaxT; no allocation).
+constexpr int64_t kGroupedNoAllocMaxT = 65536;
+hipError_t launch_lookup_combine_grouped_noalloc(const int64_t* ids, const uint16_t* h, const uint16_t* w_r,
+                                                 const uint16_t* lut, float* y, int64_t T, int D, int N,
+                                                 hipStream_t s);
 
 // build_lut.hip
 constexpr int kBuildTileM = 256;  // vocabulary rows per GEMM tile
