@@ -17,13 +17,10 @@
 //      - routing: one workgroup per 16 tokens computes their gates on the
 //        matrix cores (one 16-row tile, the 16 wavefronts splitting D) and
 //        writes them to gates[t][NP] (fp32).
-//   2. lookup_combine_grouped_kernel: a workgroup owns 16 consecutive
-//      positions and one slice of the columns (grid.y).  It walks the runs
-//      of equal ids: each run's slab slice is read once -- the next run's
-//      loads in flight while the current run is combined -- and every token
-//      of the run gets its own gate-weighted sum.  Gates come from the
-//      workspace, so the column slices of a position never depend on each
-//      other.
+//   2. lookup_combine_grouped_kernel: one workgroup per grouped position,
+//      active where a run of equal ids starts (runs cut every 16
+//      positions): it reads the run's slab once and writes each token of
+//      the run.  Gates come from the workspace.
 // The order of tokens inside a run depends on the order of the LDS atomics;
 // each token's output does not (its sum runs over its own gates and slab in
 // a fixed order).
@@ -40,8 +37,7 @@ constexpr int kGroupSlots = 2 * kGroupChunk;    // LDS hash slots: a power of tw
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupPerThread = kGroupSlots / kGroupThreads;  // slots scanned per thread
 constexpr int kTokPerThread = kGroupChunk / kGroupThreads;
-constexpr int kGroupedSeg = 16;                 // positions per combine workgroup
-constexpr int kGroupedLanes = 64;               // one wavefront per combine workgroup: 64 chunks of 8 columns
+constexpr int kGroupedSeg = 16;                 // longest run chunk one combine workgroup writes
 
 __device__ __forceinline__ uint32_t slot_hash(uint32_t key) {
   // multiplicative hashing (Knuth), top bits select the slot
@@ -158,55 +154,47 @@ __global__ __launch_bounds__(kGroupThreads) void group_route_kernel(const int64_
   }
 }
 
-// One wavefront per workgroup: lane l of column slice blockIdx.y owns the
-// 16-byte chunk c = 64 * blockIdx.y + l (8 columns) of every grouped position
-// of the workgroup.
-template <int NP>
-__global__ __launch_bounds__(kGroupedLanes) void lookup_combine_grouped_kernel(
+// One workgroup per grouped position p, active only where a run chunk
+// starts: at p = 0, where the id changes, or at a multiple of kGroupedSeg
+// inside a run (long runs are cut so that no workgroup writes more than
+// kGroupedSeg rows).  An active workgroup reads its id's slab once -- lane l
+// holds the 16-byte chunk l (and l + LANES, ...) of every expert row -- and
+// writes the gate-weighted sum for each token of the run chunk.  The other
+// workgroups exit at once.  Gates come from the workspace.
+template <int NP, int LANES>
+__global__ __launch_bounds__(LANES) void lookup_combine_grouped_kernel(
     const int* __restrict__ pos_tok, const int* __restrict__ pos_row, const float* __restrict__ gates,
     const uint16_t* __restrict__ lut, float* __restrict__ y, int64_t T, int D, int N) {
-  static_assert(NP <= 16, "gates and two slab slices in registers");
+  static_assert(NP <= 16, "a lane holds one chunk of every expert row");
   __shared__ float gsh[kGroupedSeg * NP];
-  __shared__ int ts[kGroupedSeg], rs[kGroupedSeg], runs[kGroupedSeg + 1];
-  __shared__ int nruns_s;
+  __shared__ int ts[kGroupedSeg];
   const int lane = threadIdx.x;
-  const int64_t p0 = (int64_t)blockIdx.x * kGroupedSeg;
-  const int len = (int)(T - p0 < kGroupedSeg ? T - p0 : kGroupedSeg);
+  const int64_t p = blockIdx.x;
+  const int row = pos_row[p];
+  if (p != 0 && (p % kGroupedSeg) != 0 && pos_row[p - 1] == row) return;  // not a run-chunk start (uniform)
   const int C = D / 8;
-  const int c = blockIdx.y * kGroupedLanes + lane;
-  const int cc = c < C ? c : C - 1;
-  if (lane < len) {
-    ts[lane] = pos_tok[p0 + lane];
-    rs[lane] = pos_row[p0 + lane];
-  }
-  __syncthreads();
-  // the first run's slab slice goes out before the gates are staged
-  uint4 sa[NP], sb[NP];
+  const uint16_t* slab = lut + (int64_t)row * N * D;
+  // the slab's first chunk per lane goes out first
+  uint4 sv[NP];
   {
-    const uint16_t* base = lut + (int64_t)rs[0] * N * D + (int64_t)cc * 8;
+    const int cc = lane < C ? lane : C - 1;
 #pragma unroll
-    for (int e = 0; e < NP; ++e) sa[e] = ldg16(base + (int64_t)(e < N ? e : N - 1) * D);
+    for (int e = 0; e < NP; ++e) sv[e] = ldg16(slab + (int64_t)(e < N ? e : N - 1) * D + (int64_t)cc * 8);
   }
-  for (int i = lane; i < len * NP; i += kGroupedLanes) gsh[i] = gates[(int64_t)ts[i / NP] * NP + i % NP];
-  if (lane == 0) {
-    int n = 0;
-    for (int q = 0; q < len; ++q)
-      if (q == 0 || rs[q] != rs[q - 1]) runs[n++] = q;
-    runs[n] = len;
-    nruns_s = n;
-  }
+  // run chunk length: positions p .. p + len - 1 share the row (at most to the next multiple of kGroupedSeg)
+  const int64_t lim = ((p / kGroupedSeg) + 1) * kGroupedSeg < T ? ((p / kGroupedSeg) + 1) * kGroupedSeg : T;
+  int len = 1;
+  while (p + len < lim && pos_row[p + len] == row) ++len;
+  if (lane < len) ts[lane] = pos_tok[p + lane];
   __syncthreads();
-  const int nruns = nruns_s;
-  // slab slice of run r (clamped to the last run: the loads are unconditional)
-  auto load_run = [&](int r, uint4* S) {
-    const int rr = r < nruns ? r : nruns - 1;
-    const uint16_t* base = lut + (int64_t)rs[runs[rr]] * N * D + (int64_t)cc * 8;
+  for (int i = lane; i < len * NP; i += LANES) gsh[i] = gates[(int64_t)ts[i / NP] * NP + i % NP];
+  __syncthreads();
+  for (int c = lane; c < C; c += LANES) {
+    if (c != lane) {
 #pragma unroll
-    for (int e = 0; e < NP; ++e) S[e] = ldg16(base + (int64_t)(e < N ? e : N - 1) * D);
-  };
-  auto combine_run = [&](int r, const uint4* S) {
-    if (c >= C) return;
-    for (int q = runs[r]; q < runs[r + 1]; ++q) {
+      for (int e = 0; e < NP; ++e) sv[e] = ldg16(slab + (int64_t)(e < N ? e : N - 1) * D + (int64_t)c * 8);
+    }
+    for (int q = 0; q < len; ++q) {
       float acc[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = 0.f;
@@ -214,7 +202,7 @@ __global__ __launch_bounds__(kGroupedLanes) void lookup_combine_grouped_kernel(
       for (int e = 0; e < NP; ++e) {
         if (e < N) {
           float v[8];
-          Elem<uint16_t>::unpack(S[e], v);
+          Elem<uint16_t>::unpack(sv[e], v);
           const float g = gsh[q * NP + e];
 #pragma unroll
           for (int j = 0; j < 8; ++j) acc[j] = fmaf(g, v[j], acc[j]);
@@ -224,12 +212,6 @@ __global__ __launch_bounds__(kGroupedLanes) void lookup_combine_grouped_kernel(
       stg16_nt(yo, acc[0], acc[1], acc[2], acc[3]);
       stg16_nt(yo + 4, acc[4], acc[5], acc[6], acc[7]);
     }
-  };
-  for (int r = 0; r < nruns; r += 2) {
-    load_run(r + 1, sb);
-    combine_run(r, sa);
-    load_run(r + 2, sa);
-    if (r + 1 < nruns) combine_run(r + 1, sb);
   }
 }
 
@@ -263,10 +245,17 @@ hipError_t launch_grouped_np(const int64_t* ids, const uint16_t* h, const uint16
                      h, w_r, T, D, N, nchunks, pos_tok, pos_row, gates);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // lanes per workgroup: the 16-byte chunks of a row, 64 to 256
   const int C = D / 8;
-  const dim3 grid((unsigned)((T + kGroupedSeg - 1) / kGroupedSeg), (unsigned)((C + kGroupedLanes - 1) / kGroupedLanes));
-  hipLaunchKernelGGL((lookup_combine_grouped_kernel<NP>), grid, dim3(kGroupedLanes), 0, s, pos_tok, pos_row, gates,
-                     lut, y, T, D, N);
+  if (C <= 64)
+    hipLaunchKernelGGL((lookup_combine_grouped_kernel<NP, 64>), dim3((unsigned)T), dim3(64), 0, s, pos_tok, pos_row,
+                       gates, lut, y, T, D, N);
+  else if (C <= 128)
+    hipLaunchKernelGGL((lookup_combine_grouped_kernel<NP, 128>), dim3((unsigned)T), dim3(128), 0, s, pos_tok,
+                       pos_row, gates, lut, y, T, D, N);
+  else
+    hipLaunchKernelGGL((lookup_combine_grouped_kernel<NP, 256>), dim3((unsigned)T), dim3(256), 0, s, pos_tok,
+                       pos_row, gates, lut, y, T, D, N);
   return hipGetLastError();
 }
 
