@@ -133,9 +133,9 @@ int mole_gelu_phi_coefficients(float* coef_host, int n, float* range);
  * or above the minimum works; larger blocks mean fewer launches.
  * mole_build_lut_workspace_size() returns the minimum in *min_bytes and a
  * recommended size in *rec_bytes (either pointer may be NULL): blocks of
- * about 256 MB of hidden activations, the size of the last-level cache
- * (measured as fast as one block over the whole vocabulary on the
- * 160M-class layer, at a fifth of the memory).
+ * about 1 GB of hidden activations (every block re-reads the expert
+ * weights, so larger blocks move less; beyond about 1 GB the build time no
+ * longer changes).
  * ------------------------------------------------------------------------ */
 int mole_build_lut_workspace_size(int64_t V, int64_t D, int64_t F, int64_t N, int dtype,
                                   size_t* min_bytes, size_t* rec_bytes);

@@ -566,7 +566,11 @@ size_t build_lut_min_workspace(int64_t D, int64_t F, int64_t N) {
 size_t build_lut_rec_workspace(int64_t V, int64_t D, int64_t F, int64_t N) {
   (void)D;
   const size_t row_bytes = (size_t)(N * F) * 2u;
-  const size_t target = (size_t)256 << 20;  // about the size of the last-level (MALL) cache
+  // About 1 GB of hidden activations per block: each block re-reads both
+  // weight tensors, so larger blocks cut that traffic (1B-class layer, one
+  // build: 1024-row blocks 48.5 ms, 4096 rows 47.7 ms; 160M-class: 2.33 ->
+  // 2.16 ms), while blocks of a few GB gain nothing more.
+  const size_t target = (size_t)1 << 30;
   int64_t rows = (int64_t)(target / row_bytes) / kBM * kBM;
   if (rows < kBM) rows = kBM;
   const int64_t vpad = (V + kBM - 1) / kBM * kBM;
