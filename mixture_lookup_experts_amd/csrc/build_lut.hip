@@ -73,8 +73,6 @@ constexpr int kBK = 64;     // K slice per LDS stage (64 bf16 = 128 bytes per ro
 constexpr int kPanel = 256; // columns per panel of a panel-major operand (the build's hidden activations)
 constexpr int kXcds = 8;    // MI355X: 8 accelerator complex dies, each with its own L2
 constexpr int kGroupM = 8;  // row tiles per raster band
-constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every record: loads read 0, stores drop
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 struct GemmArgs {
   const uint16_t* A; int64_t lda, sAz;

@@ -64,10 +64,12 @@ constexpr int64_t kSimdsPerChip = 1024;  // MI355X: 256 compute units x 4 SIMDs
 // them), and finish() after; the table loads stay in flight through the
 // router's arithmetic and barriers.  finish() contains barriers: every
 // thread of the block must call it.
-template <int NP>
+template <int NP, int UBX = 0>
 struct MfmaRouter {
   static constexpr int NT = (NP + 15) / 16, NPAD = NT * 16;
-  static constexpr int UB = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
+  // K steps per wave and batch of loads (UBX overrides: wide blocks have
+  // fewer steps per wave)
+  static constexpr int UB = UBX > 0 ? UBX : (NT == 1 ? 8 : (NT == 2 ? 4 : 2));
   uint4 a[UB], b[UB][NT];
   f32x4_t acc[NT];
   const uint16_t* hrow;
@@ -179,6 +181,48 @@ struct MfmaRouter {
       const float inv = 1.f / sum;
 #pragma unroll
       for (int e = 0; e < NP; ++e) gsh[tk * NP + e] = z[e] * inv;
+    }
+    __syncthreads();
+  }
+  // finish() for blocks of many wavefronts (red: [nw][16][NPAD]): thread
+  // i < 16 NP sums the partial logits of token i / NP, expert i % NP over
+  // the waves, and each token's NP threads (consecutive lanes of one
+  // wavefront) form its softmax with shuffles.  Threads 0 .. 16 NP - 1 must
+  // exist (NP <= 16 and at least 4 wavefronts).
+  __device__ __forceinline__ void finish_wide(int tpb, float* red, float* gsh) {
+    compute();
+    reduce_wide(tpb, red, gsh);
+  }
+  // The matrix work alone (consumes the operand registers of load_first).
+  __device__ __forceinline__ void compute() {
+    mma(wave);
+    for (int base = wave + UB * nw; base < ksteps; base += UB * nw) {
+      load(base);
+      mma(base);
+    }
+  }
+  // The same when one batch covers the row (ceil(D / 32) <= UB * nwaves,
+  // checked by the caller's host code): no second batch of loads, so no
+  // second set of operand registers.
+  __device__ __forceinline__ void compute_one_batch() { mma(wave); }
+  __device__ __forceinline__ void reduce_wide(int tpb, float* red, float* gsh) {
+    static_assert(NP <= 16, "one 16-column tile");
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kg + r) * NPAD + row] = acc[0][r];
+    __syncthreads();
+    const int i = threadIdx.x;
+    if (i < 16 * NP) {
+      const int tk = i / NP, e = i % NP;
+      float z = 0.f;
+      for (int w = 0; w < nw; ++w) z += red[(w * 16 + tk) * NPAD + e];
+      float m = e < N ? z : -INFINITY;
+#pragma unroll
+      for (int o = 1; o < NP; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+      const float p = e < N ? expf(z - m) : 0.f;
+      float sum = p;
+#pragma unroll
+      for (int o = 1; o < NP; o <<= 1) sum += __shfl_xor(sum, o, kWave);
+      if (tk < tpb) gsh[tk * NP + e] = p * (1.f / sum);
     }
     __syncthreads();
   }
@@ -323,13 +367,13 @@ __global__ __launch_bounds__(256) void router_gates_kernel(const uint16_t* __res
 }
 
 // Batches of at least this many tokens, at widths where a block holds
-// several tokens, route in a separate launch (see router_gates_kernel): the
-// fused MFMA router re-reads W_r for every 2-4 tokens and holds its operands
-// in registers through the gather, which at these sizes costs more than the
-// second launch (measured on the 410M-class table: T=4096 26.6 -> 21.0 us
-// with Zipf ids, neutral at T=1024).  With one token per block the vector
-// router stays fused: there the extra launch cost more than it saved
-// (1B-class table, T=1024: 12.4 -> 17.3 us).
+// several tokens (below 128 lanes per token; wider tokens use the dense
+// kernel's four-token wide blocks instead), route in a separate launch (see
+// router_gates_kernel): the fused MFMA router of a 256-thread block re-reads
+// W_r for every 2-4 tokens and holds its operands in registers through the
+// gather, which at these sizes cost more than the second launch (measured
+// on the 410M-class table before the wide blocks: T=4096 26.6 -> 21.0 us
+// with Zipf ids, neutral at T=1024).
 constexpr int64_t kStagedRouterMinT = 2048;
 
 // ---------------------------------------------------------------------------

@@ -34,20 +34,25 @@ namespace mole {
 // Staged gates are read from `gates` (row stride D), which may be y itself:
 // neither pointer is restrict-qualified, so the gate loads stay ahead of the
 // barrier that precedes the first store.
-template <typename T, int NP, int G, bool VECTOR, int MODE, bool ADD = false>
-__global__ __launch_bounds__(256) void lookup_combine_kernel(
+template <typename T, int NP, int G, bool VECTOR, int MODE, bool ADD = false, int BT = 256>
+__global__ __launch_bounds__(BT) void lookup_combine_kernel(
     const int64_t* __restrict__ ids, const T* __restrict__ h, const T* __restrict__ w_r,
     const T* __restrict__ lut, float* y, int64_t T_, int D, int N, int tpb,
     const float* gates, const float* __restrict__ addp, int nadd, int64_t add_stride) {
   constexpr int WG = G > kWave ? G / kWave : 1;
-  constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
+  constexpr int MAXTPB = BT / G < kMaxTokPerBlock ? BT / G : kMaxTokPerBlock;
+  // BT > 256: wide blocks (MFMA router only): one router tile for the
+  // block's BT / G tokens, each wavefront taking at most 4 of its K steps
+  // (the host launches them only where ceil(D / 32) <= 4 BT / 64).
+  constexpr bool kWide = BT > 256;
+  static_assert(!kWide || (MODE == kRouterMfma && NP <= 16 && BT <= 1024), "wide blocks: MFMA router");
   constexpr int CH = VECTOR ? Elem<T>::kVec : 1;  // elements per chunk
   // Experts per batch of slab loads.  With the vector-unit router at 16
   // experts the slab goes out in two halves: the first before the router's
   // arithmetic, the second once the router's operand registers are free --
   // all 16 rows at once with the router's operands held 146 registers, three
   // wavefronts per SIMD instead of four.
-  constexpr bool kLaneSplit = VECTOR && sizeof(T) == 2 && MODE == kRouterLane && NP == 16;
+  constexpr bool kLaneSplit = VECTOR && sizeof(T) == 2 && (MODE == kRouterLane || BT > 256) && NP == 16;
   constexpr int EC = kLaneSplit ? 8 : (NP < 16 ? NP : 16);
   // Router: on the matrix cores (bf16, several tokens per block), or on
   // the vector units with its loads first (one token per block, or fp32),
@@ -56,7 +61,7 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
   constexpr bool kMfmaRouter = VECTOR && sizeof(T) == 2 && MODE == kRouterMfma;
   constexpr bool kLaneRouter = VECTOR && !kMfmaRouter && !kStaged && NP <= 16;
   constexpr int NPAD = ((NP + 15) / 16) * 16;
-  __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * WG * NP];
+  __shared__ float red[kMfmaRouter ? (BT / kWave) * 16 * NPAD : MAXTPB * WG * NP];
   __shared__ float gsh[kMfmaRouter ? kMaxTokPerBlock * NP : 1];
 
   // tpb (tokens per block, = blockDim.x / G) comes as an argument: reading
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
 
   // Router operands next, then the first batch of slab loads (chunk lig,
   // experts 0..EC-1); the router's arithmetic runs while the slab arrives.
-  MfmaRouter<NP> rt;
+  MfmaRouter<NP, kWide ? 4 : 0> rt;
   LaneRouter<T, kLaneRouter ? NP : 1> lr;
   if constexpr (kMfmaRouter)
     rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
@@ -120,7 +125,22 @@ __global__ __launch_bounds__(256) void lookup_combine_kernel(
     // Every wave holds its tokens' gates before any wave overwrites the rows.
     __syncthreads();
   } else if constexpr (kMfmaRouter) {
-    rt.finish(tpb, red, gsh);
+    if constexpr (kWide) {
+      rt.compute_one_batch();
+      if constexpr (kLaneSplit) {
+        // second half of the first chunk's expert rows, once the router's
+        // operand registers are free (clamped as above)
+        const int c0 = lig < C ? lig : C - 1;
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {
+          const int ec = EC + e < N ? EC + e : N - 1;
+          sv2[e] = ldg16(slab + (int64_t)ec * D + (int64_t)c0 * CH);
+        }
+      }
+      rt.reduce_wide(tpb, red, gsh);
+    } else {
+      rt.finish(tpb, red, gsh);
+    }
 #pragma unroll
     for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
   } else if constexpr (kLaneRouter) {
@@ -245,6 +265,27 @@ static hipError_t launch_dense_add(const int64_t* ids, const void* h, const void
   // core router over two; measured on the 410M-class table at T = 1024:
   // 10.95 -> 8.1 us with Zipf ids, 12.0 -> 10.0 us with distinct ids (no
   // change at T = 256, where a workgroup already holds one token).
+  //
+  // From T = 1024 on at widths of 128-256 lanes per token (D from 520 to
+  // 2048 bf16): four tokens per workgroup of 4 G threads, routed together
+  // on the matrix cores (each wavefront takes at most 4 of the K steps:
+  // ceil(D / 32) <= 8 G / 32 = 4 * (4 G / 64)), so W_r is read once per
+  // four tokens and the router's dot products leave the vector units.
+  // Measured with distinct ids: 1B-class T = 1024 17.97 -> 15.11 us, T =
+  // 4096 60.3 -> 58.0 us; 410M-class T = 1024 9.80 -> 8.27 us, T = 4096
+  // 32.7 -> 28.7 us (the staged router's two launches).  Not for the
+  // block's ADD pass, whose partial-sum loads do not fit the registers of
+  // 16 wavefronts per compute unit.
+  if constexpr (!ADD && VEC && sizeof(E) == 2 && NP <= 16 && G >= 128) {
+    if (T >= 1024) {
+      constexpr int kTok = 4, BT = kTok * G;
+      hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterMfma, ADD, BT>),
+                         dim3((unsigned)((T + kTok - 1) / kTok)), dim3(BT), 0, s, ids, (const E*)h,
+                         (const E*)w_r, (const E*)lut, y, T, D, N, kTok, (const float*)nullptr, ex.addp, ex.nadd,
+                         ex.add_stride);
+      return hipGetLastError();
+    }
+  }
   const bool one_token = VEC && sizeof(E) == 2 && NP <= 16 && G >= 64 && T <= 1024;
   const int tpb = one_token ? 1 : pick_tokens_per_block(T, G);
   const int64_t blocks = (T + tpb - 1) / tpb;

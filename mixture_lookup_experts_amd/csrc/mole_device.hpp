@@ -48,6 +48,12 @@ template <> struct Elem<uint16_t> {  // bf16 bit patterns
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Raw buffer resources: a buffer offset at or past a resource's byte count
+// reads 0 and drops stores, so kOob (past every record) masks a load or a
+// store without a branch.
+constexpr uint32_t kOob = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 // 16-byte streaming store (non-temporal: the output is not re-read here).
 typedef float f32x4_vec_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void stg16_nt(float* p, float a, float b, float c, float d) {

@@ -74,12 +74,16 @@ def lanes(blocks, threads):
 # routers (combine_common.hpp)
 # ----------------------------------------------------------------------------
 
-def mfma_router_loads(buf, b, tid, t0, T, tpb, D, N, NP, nwaves, clamp_expert=True):
+def mfma_router_loads(buf, b, tid, t0, T, tpb, D, N, NP, nwaves, clamp_expert=True, ub=0, one_batch=False):
     """MfmaRouter: lane l of wave w supplies token row l%16 and expert column
     l%16 with 8 consecutive d of k-group l/16; the waves take every nw-th
-    32-wide K step, UB steps per batch."""
+    32-wide K step, UB steps per batch (ub overrides, as the wide blocks'
+    router does; one_batch: only the first batch, which must then cover the
+    row)."""
     NT = (NP + 15) // 16
-    UB = 8 if NT == 1 else (4 if NT == 2 else 2)
+    UB = ub if ub else (8 if NT == 1 else (4 if NT == 2 else 2))
+    if one_batch:
+        assert (D + 31) // 32 <= UB * nwaves, "one batch of K steps must cover the row"
     lane = tid & 63
     wave = tid >> 6
     row, kg = lane & 15, lane >> 4
@@ -101,6 +105,8 @@ def mfma_router_loads(buf, b, tid, t0, T, tpb, D, N, NP, nwaves, clamp_expert=Tr
                 e = nt * 16 + row
                 ec = np.where(e < N, e, N - 1) if clamp_expert else e
                 buf.access("w_r", ((ec * D + kc) * BF16)[active], 16)
+        if one_batch:
+            break
         base = base + UB * nwaves
 
 
@@ -153,6 +159,9 @@ def dense_plan(T, D, N, esz):
     bf = esz == BF16
     one_token = vector and bf and NP <= 16 and G >= 64 and T <= 1024
     tpb = 1 if one_token else pick_tokens_per_block(T, G)
+    if vector and bf and NP <= 16 and G >= 128 and T >= 1024:
+        # four tokens per workgroup of 4 G threads, matrix-core router
+        return dict(NP=NP, vector=vector, C=C, G=G, tpb=4, mode="wide", CH=vec)
     if vector and bf and T >= 2048 and tpb >= 2 and NP <= D:
         mode = "staged"
     elif vector and bf and NP <= 16 and G >= 64 and tpb == 1:
@@ -180,6 +189,8 @@ def model_dense(T, V, D, N, esz, ids, clamp_expert=True):
     buf.access("ids", tt * 8, 8)
     if p["mode"] == "mfma":
         mfma_router_loads(buf, b, tid, t0, T, tpb, D, N, NP, (G * tpb) // WAVE, clamp_expert)
+    elif p["mode"] == "wide":
+        mfma_router_loads(buf, b, tid, t0, T, tpb, D, N, NP, (G * tpb) // WAVE, clamp_expert, ub=4, one_batch=True)
     elif p["mode"] == "lane":
         lane_router_loads(buf, tt, lig, G, D, N, NP, esz, valid)
     elif p["mode"] == "staged":
@@ -372,7 +383,7 @@ def ids_for(T, V, seed):
 
 NS = [1, 3, 4, 5, 8, 12, 16, 17, 33, 64]
 DS_BF16 = [8, 24, 136, 1000, 2048, 60, 30]
-TS = [1, 17, 1024, 1025, 2051]
+TS = [1, 17, 1023, 1024, 1025, 2051]
 
 
 @pytest.mark.parametrize("esz", [BF16, F32])
@@ -428,6 +439,6 @@ def test_router_without_expert_clamp_reads_past_w_r():
     T = 1025  # past the one-token limit: several tokens per block, matrix-core router
     ids = ids_for(T, V, 1)
     p, buf = model_dense(T, V, D, N, BF16, ids)
-    assert p["mode"] == "mfma" and p["tpb"] >= 2 and not buf.bad
+    assert p["mode"] in ("mfma", "wide") and p["tpb"] >= 2 and not buf.bad
     _, bad = model_dense(T, V, D, N, BF16, ids, clamp_expert=False)
     assert bad.bad and all(name == "w_r" for name, *_ in bad.bad)

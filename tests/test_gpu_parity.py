@@ -83,9 +83,18 @@ COMBINE_CASES = [
     (300, 16, 1024, 2051, "bf16"),  # ragged last block and router tile
     (200, 5, 256, 3001, "bf16"),    # N padded to 8
     (100, 64, 512, 2048, "bf16"),   # largest N
-    # either side of the one-token-per-workgroup limit (T = 1024)
+    # either side of the one-token-per-workgroup limit (T = 1024); from
+    # there on, tokens of 128-256 lanes go four to a workgroup of 4 G
+    # threads with the matrix-core router
+    (300, 16, 1024, 1023, "bf16"),
     (300, 16, 1024, 1024, "bf16"),
-    (300, 16, 1024, 1025, "bf16"),  # two tokens per workgroup, matrix-core router, ragged last block
+    (300, 16, 1024, 1025, "bf16"),  # ragged last workgroup (one token)
+    (300, 16, 2048, 1024, "bf16"),  # 1B-class width: 16 wavefronts, one K batch each
+    (300, 12, 2048, 1031, "bf16"),  # N padded to 16, ragged
+    (300, 16, 1000, 1026, "bf16"),  # D not a multiple of the 32-wide K step
+    (200, 8, 1536, 2050, "bf16"),   # N = 8, 192 chunks per row
+    (100, 1, 1024, 1024, "bf16"),   # one expert: every gate 1
+    (300, 16, 1024, 4099, "bf16"),  # 410M-class width, large batch
 ]
 
 
