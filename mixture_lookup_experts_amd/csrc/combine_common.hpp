@@ -72,90 +72,90 @@ struct MfmaRouter {
   static constexpr int UB = UBX > 0 ? UBX : (NT == 1 ? 8 : (NT == 2 ? 4 : 2));
   uint4 a[UB], b[UB][NT];
   f32x4_t acc[NT];
-  const uint16_t* hrow;
-  const uint16_t* w_r;
-  int D, N, ksteps, nw, wave, row, kg;
-  bool tok_ok;
+  // Operands through buffer resources: h over the rows of the block's
+  // tokens inside the batch, W_r over its N rows.  A lane's h offset is
+  // kOob for a token row outside the tile or the batch (and for a K step
+  // past the row), so its operand reads as zero without a select; W_r
+  // columns of experts >= N read the clamped row N - 1, whose logits the
+  // softmax ignores.
+  __amdgpu_buffer_rsrc_t rh, rw;
+  uint32_t hoff, woff[NT];
+  int D, ksteps, nw, wave, kg;
 
-  // Every load is issued unconditionally from an in-bounds (clamped)
-  // address and masked to zero only where it is consumed (mma, which
-  // recomputes the masks): loads under a divergent branch would leave the
-  // compiler unsure how many loads are outstanding at the join, and a select
-  // right after a load would make it wait there -- either way it would wait
-  // for the table rows issued after the router's operands.
-  __device__ __forceinline__ bool k_ok(int base, int u) const {
-    const int ks = base + u * nw;
-    return ks < ksteps && ks * 32 + kg * 8 < D;
-  }
+  // Every load is issued unconditionally: loads under a divergent branch
+  // would leave the compiler unsure how many loads are outstanding at the
+  // join, and a select right after a load would make it wait there --
+  // either way it would wait for the table rows issued after the router's
+  // operands.
   __device__ __forceinline__ void load(int base) {
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
-      const int kc = k_ok(base, u) ? (base + u * nw) * 32 + kg * 8 : 0;
-      a[u] = ldg16(hrow + kc);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int e = nt * 16 + row;
-        b[u][nt] = ldg16(w_r + (int64_t)(e < N ? e : N - 1) * D + kc);
-      }
-    }
-  }
-  __device__ __forceinline__ void mma(int base) {
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const bool kok = k_ok(base, u);
+      const int ks = base + u * nw;
+      const uint32_t kb = (uint32_t)(ks * 32 + kg * 8) * 2u;  // byte offset in a row
+      const bool kok = ks < ksteps && ks * 32 + kg * 8 < D;
+      a[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, (int)(kok ? hoff + kb : kOob), 0, 0));
+      // (past the row, A is zero: any finite W_r value will do, and the
+      // offset stays inside the resource or reads zero)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, (tok_ok && kok) ? a[u] : zero),
-            __builtin_bit_cast(bf16x8_t, (nt * 16 + row < N && kok) ? b[u][nt] : zero), acc[nt], 0, 0, 0);
+        b[u][nt] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(woff[nt] + (kok ? kb : 0u)), 0, 0));
     }
+  }
+  __device__ __forceinline__ void mma(int) {
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[u]),
+                                                          __builtin_bit_cast(bf16x8_t, b[u][nt]), acc[nt], 0, 0, 0);
   }
   // nwaves = the block's wavefronts (passed in: reading the block size
   // costs a dependent load of the dispatch packet).
   __device__ __forceinline__ void load_first(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
                                              int64_t t0, int64_t T_, int tpb, int D_, int N_, int nwaves) {
-    lane_setup(h, w, t0, T_, tpb, D_, N_, nwaves);
-    load(wave);
-  }
-  // Router rows given by a token list (LDS): row r routes token tok_list[r]
-  // for r < ntok (the grouped combine's positions).
-  __device__ __forceinline__ void load_first_list(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
-                                                  const int* tok_list, int ntok, int D_, int N_, int nwaves) {
-    const int r = threadIdx.x & 15;
-    const bool ok = r < ntok;
-    lane_setup_tok(h, w, ok ? tok_list[r] : 0, ok, D_, N_, nwaves);
-    load(wave);
-  }
-  __device__ __forceinline__ void lane_setup(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
-                                             int64_t t0, int64_t T_, int tpb, int D_, int N_, int nwaves) {
-    const int r = threadIdx.x & 15;
-    const int64_t tok = t0 + r;
-    lane_setup_tok(h, w, tok, r < tpb && tok < T_, D_, N_, nwaves);
-  }
-  __device__ __forceinline__ void lane_setup_tok(const uint16_t* __restrict__ h, const uint16_t* __restrict__ w,
-                                                 int64_t tok, bool ok, int D_, int N_, int nwaves) {
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, row = lane & 15;
     wave = threadIdx.x >> 6;
     nw = nwaves;
-    row = lane & 15;
     kg = lane >> 4;
     D = D_;
-    N = N_;
-    w_r = w;
-    tok_ok = ok;
-    hrow = h + (tok_ok ? tok : 0) * (int64_t)D;
     ksteps = (D + 31) / 32;
+    const int64_t left = T_ - t0;
+    const int rows = (int)(left < tpb ? left : tpb);  // token rows of the tile inside the batch (>= 1)
+    rh = __builtin_amdgcn_make_buffer_rsrc((void*)(h + t0 * D), (short)0, rows * D * 2, kRsrcWord3);
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, N_ * D * 2, kRsrcWord3);
+    hoff = row < rows ? (uint32_t)(row * D) * 2u : kOob;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = nt * 16 + row;
+      woff[nt] = (uint32_t)((e < N_ ? e : N_ - 1) * D) * 2u;
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    load(wave);
   }
-  __device__ __forceinline__ void finish(int tpb, float* red /* [4][16][NPAD] */, float* gsh /* [16][NP] */) {
+  // The matrix work alone (consumes the operand registers of load_first).
+  __device__ __forceinline__ void compute() {
     mma(wave);
     for (int base = wave + UB * nw; base < ksteps; base += UB * nw) {
       load(base);
       mma(base);
     }
+  }
+  // The same when one batch covers the row (ceil(D / 32) <= UB * nwaves,
+  // checked by the caller's host code): no second batch of loads, so no
+  // second set of operand registers.
+  __device__ __forceinline__ void compute_one_batch() { mma(wave); }
+
+  __device__ __forceinline__ void finish(int tpb, int N, float* red /* [nw][16][NPAD] */, float* gsh /* [16][NP] */) {
+    compute();
+    if constexpr (NP <= 16) {
+      if (nw * kWave >= 16 * NP) {
+        reduce_wide(tpb, N, red, gsh);
+        return;
+      }
+    }
     // lane l holds logits of tokens 4*(l/16) + r, expert nt*16 + l%16
+    const int row = threadIdx.x & 15;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -184,29 +184,13 @@ struct MfmaRouter {
     }
     __syncthreads();
   }
-  // finish() for blocks of many wavefronts (red: [nw][16][NPAD]): thread
-  // i < 16 NP sums the partial logits of token i / NP, expert i % NP over
-  // the waves, and each token's NP threads (consecutive lanes of one
-  // wavefront) form its softmax with shuffles.  Threads 0 .. 16 NP - 1 must
-  // exist (NP <= 16 and at least 4 wavefronts).
-  __device__ __forceinline__ void finish_wide(int tpb, float* red, float* gsh) {
-    compute();
-    reduce_wide(tpb, red, gsh);
-  }
-  // The matrix work alone (consumes the operand registers of load_first).
-  __device__ __forceinline__ void compute() {
-    mma(wave);
-    for (int base = wave + UB * nw; base < ksteps; base += UB * nw) {
-      load(base);
-      mma(base);
-    }
-  }
-  // The same when one batch covers the row (ceil(D / 32) <= UB * nwaves,
-  // checked by the caller's host code): no second batch of loads, so no
-  // second set of operand registers.
-  __device__ __forceinline__ void compute_one_batch() { mma(wave); }
-  __device__ __forceinline__ void reduce_wide(int tpb, float* red, float* gsh) {
+  // Softmax with one thread per (token, expert): thread i < 16 NP sums the
+  // partial logits of token i / NP, expert i % NP over the waves, and each
+  // token's NP threads (consecutive lanes of one wavefront) form its softmax
+  // with shuffles.  Needs NP <= 16 and at least 16 NP threads in the block.
+  __device__ __forceinline__ void reduce_wide(int tpb, int N, float* red, float* gsh) {
     static_assert(NP <= 16, "one 16-column tile");
+    const int row = threadIdx.x & 15;
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * kg + r) * NPAD + row] = acc[0][r];
     __syncthreads();
@@ -359,7 +343,7 @@ __global__ __launch_bounds__(256) void router_gates_kernel(const uint16_t* __res
   const int64_t t0 = (int64_t)blockIdx.x * kMaxTokPerBlock;
   MfmaRouter<NP> rt;
   rt.load_first(h, w_r, t0, T_, kMaxTokPerBlock, D, N, 4);
-  rt.finish(kMaxTokPerBlock, red, gsh);
+  rt.finish(kMaxTokPerBlock, N, red, gsh);
   for (int i = threadIdx.x; i < kMaxTokPerBlock * N; i += blockDim.x) {
     const int tk = i / N, e = i - tk * N;
     if (t0 + tk < T_) y[(t0 + tk) * D + e] = gsh[tk * NP + e];

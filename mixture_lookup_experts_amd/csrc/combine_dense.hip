@@ -137,12 +137,17 @@ __global__ __launch_bounds__(BT) void lookup_combine_kernel(
           sv2[e] = ldg16(slab + (int64_t)ec * D + (int64_t)c0 * CH);
         }
       }
-      rt.reduce_wide(tpb, red, gsh);
+      rt.reduce_wide(tpb, N, red, gsh);
     } else {
-      rt.finish(tpb, red, gsh);
+      rt.finish(tpb, N, red, gsh);
     }
 #pragma unroll
     for (int e = 0; e < NP; ++e) gate[e] = gsh[grp * NP + e];
+    if constexpr (G >= kWave) {
+      // a wavefront serves one token: its gates are wave-uniform
+#pragma unroll
+      for (int e = 0; e < NP; ++e) gate[e] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gate[e])));
+    }
   } else if constexpr (kLaneRouter) {
     float part[NP];
     lr.template partials<G>(h + tt * D, w_r, D, N, lig, valid, part);

@@ -54,7 +54,7 @@ __device__ __forceinline__ void route_tile(const uint16_t* __restrict__ h, const
                                            float* red, float* gsh) {
   MfmaRouter<NP> rt;
   rt.load_first(h, w_r, t0, T, kMaxTokPerBlock, D, N, kGroupThreads / kWave);
-  rt.finish(kMaxTokPerBlock, red, gsh);
+  rt.finish(kMaxTokPerBlock, N, red, gsh);
   const int tid = threadIdx.x;
   if (tid < kMaxTokPerBlock * NP && t0 + tid / NP < T) gates[t0 * NP + tid] = gsh[tid];
 }

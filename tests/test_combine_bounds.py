@@ -284,8 +284,22 @@ def model_q(fmt, T, V, D, N, esz, ids):
             else:
                 buf.access("scales", ((idv * N * (D // 64) + e * (D // 64) + (c >> 1)) * 2)[mm], 2)
 
-    load_batch(ch, 0, valid & (ch < C))
-    if p["mode"] == "mfma":
+    if p["mode"] == "mfma" and G == WAVE and W == 1:
+        # one token per wavefront: router operands first, then the first
+        # batch branch-free (expert and chunk clamped, every lane loads)
+        mfma_router_loads(buf, b, tid, t0, T, tpb, D, N, NP, (G * tpb) // WAVE)
+        cc = np.minimum(ch, C - 1)
+        for j in range(EC):
+            e = (j * W + wsp) * S + sp
+            ec = np.minimum(e, N - 1)
+            buf.access("codes", idv * N * rb + ec * rb + cc * chunk, chunk)
+            if fmt == "int8":
+                buf.access("scales", (idv * N + ec) * 4, 4)
+            else:
+                buf.access("scales", (idv * N * (D // 64) + ec * (D // 64) + (cc >> 1)) * 2, 2)
+    else:
+        load_batch(ch, 0, valid & (ch < C))
+    if p["mode"] == "mfma" and not (G == WAVE and W == 1):
         mfma_router_loads(buf, b, tid, t0, T, tpb, D, N, NP, (G * tpb) // WAVE)
     elif p["mode"] == "lane":
         lane_router_loads(buf, tt, tid if W > 1 else lig, G * W if W > 1 else G, D, N, NP, esz, valid)
