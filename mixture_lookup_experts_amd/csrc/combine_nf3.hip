@@ -314,15 +314,16 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
                              const void* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
   constexpr int S = 64 / CP < NP ? 64 / CP : NP;  // expert splits per token
   constexpr int G = CP * S;
-  // Up to T = 1024 (bf16 h, NP <= 16, full-wavefront tokens): one token per
-  // workgroup with the vector-unit router, spread over W wavefronts below;
-  // measured on the 410M-class table at T = 1024: NF3 11.5 -> 8.7 us, NF4
-  // 11.5 -> 9.2 us, int8 11.1 -> 9.0 us.  At T = 4096 the matrix-core router
-  // over several tokens per workgroup stays ahead for NF3 and NF4 (18.2
-  // against 23.7 us), but not for int8, whose decode is lighter (one token
-  // per workgroup: 23.6 -> 20.5 us with Zipf ids, 28.7 -> 26.5 us distinct).
-  const bool one_token = G == kWave && sizeof(TH) == 2 && NP <= 16 && (T <= 1024 || FMT == kFmtI8);
-  const int tpb = one_token ? 1 : pick_tokens_per_block(T, G);
+  // Below T = 1024 (bf16 h, NP <= 16, full-wavefront tokens): one token per
+  // workgroup with the vector-unit router, spread over W wavefronts below.
+  // From T = 1024 on, four tokens per workgroup (one per wavefront) with the
+  // matrix-core router, whose operands go out before the code loads; on the
+  // 410M-class table with distinct ids, against the one-token shapes: T =
+  // 1024 NF3 9.26 -> 8.51 us, NF4 9.83 -> 9.01 us, int8 10.2 -> 8.3 us;
+  // T = 4096 int8 26.4 -> 23.3 us.
+  const bool full_wave = G == kWave && sizeof(TH) == 2 && NP <= 16;
+  const bool one_token = full_wave && T < 1024;
+  const int tpb = one_token ? 1 : (full_wave ? 4 : pick_tokens_per_block(T, G));
   const int64_t blocks = (T + tpb - 1) / tpb;
   // (No staged-router launch here: the extra launch measured slower --
   // 410M-class NF3 table, T=4096: 20.1 -> 22.6 us.)

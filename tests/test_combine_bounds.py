@@ -235,8 +235,9 @@ def q_plan(fmt, T, D, N, esz):
     S = min(64 // CP, NP)
     G = CP * S
     bf = esz == BF16
-    one_token = G == WAVE and bf and NP <= 16 and (T <= 1024 or fmt == "int8")
-    tpb = 1 if one_token else pick_tokens_per_block(T, G)
+    full_wave = G == WAVE and bf and NP <= 16
+    one_token = full_wave and T < 1024
+    tpb = 1 if one_token else (4 if full_wave else pick_tokens_per_block(T, G))
     W = 1
     if bf and NP <= 16 and tpb == 1 and G == WAVE:
         while W < 4 and 2 * W * S <= NP and T * 2 * W <= 2 * 1024:
@@ -417,7 +418,7 @@ def test_quantised_combine_loads_stay_in_bounds(fmt):
     V = 41
     for N in NS:
         for D in (64, 192, 1024, 2048):
-            for T in (1, 17, 1024, 1025, 2049):
+            for T in (1, 17, 1023, 1024, 1025, 2049):
                 for esz in (BF16, F32):
                     if esz == F32 and T > 17:
                         continue

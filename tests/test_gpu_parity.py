@@ -248,8 +248,12 @@ def run_nf3(ids, h, w_r, codes, scales):
                                            (300, 16, 1024, 2051, "bf16"), (200, 5, 256, 3001, "bf16"),
                                            (100, 64, 512, 2048, "bf16"),
                                            # either side of the one-token-per-workgroup limit
-                                           (300, 16, 1024, 1024, "bf16"), (300, 16, 1024, 1025, "bf16"),
-                                           (200, 8, 512, 600, "bf16"),
+                                           # (from T = 1024: four tokens per workgroup, router
+                                           # operands before branch-free code loads)
+                                           (300, 16, 1024, 1023, "bf16"), (300, 16, 1024, 1024, "bf16"),
+                                           (300, 16, 1024, 1025, "bf16"), (200, 8, 512, 600, "bf16"),
+                                           (300, 12, 1024, 1030, "bf16"),  # N padded to 16, ragged
+                                           (300, 16, 2048, 1024, "bf16"),  # two batches of code loads
                                            # four wavefronts per token, some without an expert in a round
                                            (300, 12, 1024, 100, "bf16")])
 def test_combine_nf3_matches_oracle(V, N, D, T, dtype):
@@ -818,7 +822,9 @@ def test_pack_int8_edge_cases_bit_exact():
                                            (300, 16, 1024, 257, "bf16"), (100, 16, 2048, 33, "bf16"),
                                            (64, 64, 128, 10, "bf16"), (50, 3, 192, 17, "f32"),
                                            (40, 1, 64, 5, "bf16"), (300, 16, 1024, 2051, "bf16"),
-                                           (100, 64, 512, 2048, "bf16"), (300, 12, 1024, 100, "bf16")])
+                                           (100, 64, 512, 2048, "bf16"), (300, 12, 1024, 100, "bf16"),
+                                           (300, 16, 1024, 1023, "bf16"), (300, 16, 1024, 1024, "bf16"),
+                                           (300, 12, 2048, 1027, "bf16")])
 def test_combine_q_matches_oracle(fmt, V, N, D, T, dtype):
     seed = 3000 + V + N + D
     table = rand_table(seed, V, N, D, "bf16")
