@@ -107,6 +107,15 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   // W > 1: the wavefronts' partial sums, [wavefront][sum][lane] (lane-minor:
   // conflict-free writes and reads).
   __shared__ float xw[W > 1 ? W * OUT * kWave : 1];
+  // One token per wavefront: each round's outputs (CP chunks of 32) go
+  // through this wavefront's slice of LDS, so that every 16-byte store
+  // instruction writes 1 KB of the token's row (whole 128-byte lines).
+  // Stored straight from the lanes, each line was written in four pieces
+  // by four instructions and left L2 in parts: 25.4 MB written for the
+  // 16.8 MB of y (410M-class table, T = 4096).
+  constexpr bool kStageOut = W == 1 && G == kWave && OW >= 4;
+  // (one wavefront per block in the vector-router launches, up to four in the others)
+  __shared__ float ys[kStageOut ? (MODE == kRouterLane ? 1 : 256 / kWave) * CP * 32 : 1];
 
   const int tid = threadIdx.x;
   if constexpr (FMT == kFmtNf3) {
@@ -293,7 +302,26 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
       }
       __syncthreads();  // xw is rewritten in the next round
     }
-    if (act) {
+    if constexpr (kStageOut) {
+      // (lanes past the row write their unused sums too: those LDS words
+      // are never stored)
+      float* yw = ys + grp * (CP * 32);
+#pragma unroll
+      for (int j = 0; j < OW; j += 4)
+        *reinterpret_cast<float4*>(yw + ch * 32 + SplitReduce<CP, S>::offset(sp) + j) =
+            make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+      // the wavefront's LDS accesses complete in order; the fence keeps the
+      // compiler from moving the reads above the writes
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const int lane = lig;
+#pragma unroll
+      for (int q = 0; q < CP * 32 / 256; ++q) {
+        const int e = k * CP * 32 + 4 * lane + 256 * q;  // element of the token's row
+        const float4 v = *reinterpret_cast<const float4*>(yw + 4 * lane + 256 * q);
+        if (e < D) stg16_nt(y + tt * D + e, v.x, v.y, v.z, v.w);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the slice is rewritten next round
+    } else if (act) {
       float* yo = y + tt * D + (int64_t)c * 32 + SplitReduce<CP, S>::offset(sp) + wsp * OW;
       if constexpr (OW >= 4) {
 #pragma unroll
