@@ -46,8 +46,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr uint32_t kOob = 0x80000000u;  // buffer offset past every record: loads read 0
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kMidBN = 128;             // output columns per mid-size tile (4 waves x 32)
 constexpr int kTargetBlocks = 512;      // two workgroups per compute unit
 constexpr int kMaxSplits = 16;          // K splits per projection
