@@ -704,8 +704,14 @@ def host_stack_probe(torch, mole, synth, dev, stream):
     = the 16 layers' lookup-combines, run two ways: (a) per layer, the
     host-resident call (gather + copy + combine, 16 transfers); (b) one
     step-start prefetch of every layer's rows in a single transfer, then 16
-    device combines on the staged rows.  Also a pinned host->device copy of
-    256 MiB, the PCIe roofline measured in the same run.  The host tables are
+    device combines on the staged rows.  Then (c) the prefetch hidden behind
+    device work: the 16 layers' shared-expert FFNs (F = 4096, through
+    mole_layer_forward with a one-row zero table, so its own routed pass
+    reads one cached row) are enqueued on the compute stream first, the
+    prefetch's host gather and copy run meanwhile (the copy on a second
+    stream), and the 16 NF3 combines wait for the copy; against the same
+    work in order on one stream.  Also a pinned host->device copy of 256
+    MiB, the PCIe roofline measured in the same run.  The host tables are
     left as allocated (zero pages): the combine's cost does not depend on the
     code values."""
     w = synth.WORKLOADS["410m-nf3"]
@@ -718,6 +724,9 @@ def host_stack_probe(torch, mole, synth, dev, stream):
     g = torch.Generator(device=dev)
     g.manual_seed(synth.seed(w, 80))
     w_rs = [(torch.randn((N, D), generator=g, device=dev) * 0.02).to(torch.bfloat16) for _ in range(L)]
+    w_up = [(torch.randn((4 * D, D), generator=g, device=dev) * 0.02).to(torch.bfloat16) for _ in range(L)]
+    w_down = [(torch.randn((D, 4 * D), generator=g, device=dev) * 0.02).to(torch.bfloat16) for _ in range(L)]
+    copy_stream = torch.cuda.Stream(device=dev)
     # PCIe roofline: one pinned 256 MiB host->device copy
     src = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -762,8 +771,42 @@ def host_stack_probe(torch, mole, synth, dev, stream):
                 mole.mole_lookup_combine_nf3(remap, h_l[b][l], w_rs[l], layers[l][0], layers[l][1], y_l[l],
                                              stream=stream)
 
+        # (c) the shared experts' FFNs of the same 16 layers on the compute stream
+        F = 4 * D
+        ids0 = torch.zeros(T, dtype=torch.int64, device=dev)
+        lut0 = torch.zeros((1, N, D), dtype=torch.bfloat16, device=dev)
+        x_l = [torch.zeros((T, D), dtype=torch.float32, device=dev) for _ in range(L)]
+        ws_l = torch.empty(mole.mole_layer_workspace_size(T, D, F), dtype=torch.uint8, device=dev)
+
+        def ffns(b):
+            for l in range(L):
+                mole.mole_layer_forward(ids0, h_l[b][l], w_rs[l], lut0, w_up[l], w_down[l], x_l[l], ws_l,
+                                        stream=stream)
+
+        def serial(b):
+            ffns(b)
+            prefetched(b)
+
+        done = [torch.cuda.Event()]  # the previous step's combines, the last readers of stL_d
+        done[0].record(stream)
+
+        def overlapped(b):
+            ffns(b)
+            copy_stream.wait_event(done[0])  # the copy overwrites stL_d only after they end
+            remap, layers = mole.mole_prefetch_nf3_host_stack(ids_l[b], codes_h, scales_h, stL_h, stL_d,
+                                                              stream=copy_stream)
+            ev = torch.cuda.Event()
+            ev.record(copy_stream)
+            stream.wait_event(ev)
+            for l in range(L):
+                mole.mole_lookup_combine_nf3(remap, h_l[b][l], w_rs[l], layers[l][0], layers[l][1], y_l[l],
+                                             stream=stream)
+            done[0] = torch.cuda.Event()
+            done[0].record(stream)
+
         res = {}
-        for name, fn in (("per_layer", per_layer), ("prefetched", prefetched)):
+        for name, fn in (("per_layer", per_layer), ("prefetched", prefetched), ("ffn_only", ffns),
+                         ("ffn_then_prefetched", serial), ("ffn_overlapped_prefetch", overlapped)):
             for b in range(2):
                 fn(b % NB)
             torch.cuda.synchronize()
@@ -777,6 +820,10 @@ def host_stack_probe(torch, mole, synth, dev, stream):
             wall = (time.perf_counter() - t0) / reps
             res[name + "_us_per_step"] = e0.elapsed_time(e1) * 1e3 / reps
             res[name + "_wall_us_per_step"] = wall * 1e6
+        # hidden: FFNs and prefetched step run one after the other, minus the overlapped step
+        res["prefetch_hidden_us"] = (res["ffn_only_us_per_step"] + res["prefetched_us_per_step"]
+                                     - res["ffn_overlapped_prefetch_us_per_step"])
+        del x_l, ws_l
         U = float(np.mean(uniq)) if uniq else 0.0
         pcie = L * U * N * (CB + 2 * SB) + 8 * T
         best = min(res["per_layer_us_per_step"], res["prefetched_us_per_step"])
@@ -787,7 +834,7 @@ def host_stack_probe(torch, mole, synth, dev, stream):
         del st1_h, st1_d, stL_h, stL_d, h_l, y_l
     torch.cuda.synchronize()
     ctx.__exit__(None, None, None)
-    del codes_h, scales_h, w_rs
+    del codes_h, scales_h, w_rs, w_up, w_down
     torch.cuda.empty_cache()
     return out
 
