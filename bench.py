@@ -810,16 +810,18 @@ def host_stack_probe(torch, mole, synth, dev, stream):
             for b in range(2):
                 fn(b % NB)
             torch.cuda.synchronize()
-            reps = 5
-            t0 = time.perf_counter()
-            e0.record(stream)
+            # each step timed on its own (a host-bound step varies with the host's load): the median
+            reps, ev_us, wall_us = 7, [], []
             for r in range(reps):
+                t0 = time.perf_counter()
+                e0.record(stream)
                 fn(r % NB)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            wall = (time.perf_counter() - t0) / reps
-            res[name + "_us_per_step"] = e0.elapsed_time(e1) * 1e3 / reps
-            res[name + "_wall_us_per_step"] = wall * 1e6
+                e1.record(stream)
+                torch.cuda.synchronize()
+                wall_us.append((time.perf_counter() - t0) * 1e6)
+                ev_us.append(e0.elapsed_time(e1) * 1e3)
+            res[name + "_us_per_step"] = float(np.median(ev_us))
+            res[name + "_wall_us_per_step"] = float(np.median(wall_us))
         # hidden: FFNs and prefetched step run one after the other, minus the overlapped step
         res["prefetch_hidden_us"] = (res["ffn_only_us_per_step"] + res["prefetched_us_per_step"]
                                      - res["ffn_overlapped_prefetch_us_per_step"])
