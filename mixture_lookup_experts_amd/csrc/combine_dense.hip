@@ -6,16 +6,19 @@
 //
 // Work decomposition (one launch, no inter-block communication):
 //   * a "group" of G lanes (G a power of two) owns one token; a block holds
-//     up to 16 tokens, fewer when the batch is small so that the grid still
-//     covers the 256 compute units;
-//   * router, bf16: the block's logits [tokens x experts] come from
-//     v_mfma_f32_16x16x32_bf16 tiles (tokens x 16 experts, K = 32 per
-//     instruction), the waves splitting D, so W_r is read once per block;
-//     partial tiles meet in LDS and one thread per token does the
-//     max-subtracted softmax;
-//   * router, fp32 or unaligned: lanes split D into chunks, form per-expert
-//     partial dot products, reduce them across the group with a wavefront
-//     reduce-scatter (xor shuffles) plus one LDS exchange;
+//     one token (small bf16 batches), four (bf16 batches from 1024 tokens
+//     at 128-256 lanes per token, blocks of 4 G threads), or up to 16,
+//     fewer when the batch is small so that the grid still covers the 256
+//     compute units;
+//   * router, bf16 with several tokens per block: the block's logits
+//     [tokens x experts] come from v_mfma_f32_16x16x32_bf16 tiles (tokens x
+//     16 experts, K = 32 per instruction), the waves splitting D, so W_r is
+//     read once per block; partial tiles meet in LDS and the softmax runs
+//     on one lane per (token, expert) (MfmaRouter);
+//   * router, one token per block, fp32 or unaligned: lanes split D into
+//     chunks, form per-expert partial dot products, reduce them across the
+//     group with a wavefront reduce-scatter (xor shuffles) plus one LDS
+//     exchange;
 //   * gather/combine: lane `l` of the group streams chunks l, l+G, ... of
 //     every expert row of the token's contiguous slab LUT[id] with 16-byte
 //     loads and accumulates in fp32.  The router's operands are loaded
