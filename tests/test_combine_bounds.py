@@ -397,7 +397,7 @@ def ids_for(T, V, seed):
 
 
 NS = [1, 3, 4, 5, 8, 12, 16, 17, 33, 64]
-DS_BF16 = [8, 24, 136, 1000, 2048, 60, 30]
+DS_BF16 = [8, 24, 136, 1000, 1032, 2048, 60, 30]
 TS = [1, 17, 1023, 1024, 1025, 2051]
 
 

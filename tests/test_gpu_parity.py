@@ -92,6 +92,7 @@ COMBINE_CASES = [
     (300, 16, 2048, 1024, "bf16"),  # 1B-class width: 16 wavefronts, one K batch each
     (300, 12, 2048, 1031, "bf16"),  # N padded to 16, ragged
     (300, 16, 1000, 1026, "bf16"),  # D not a multiple of the 32-wide K step
+    (300, 16, 1032, 1024, "bf16"),  # 129 chunks in 256 lanes: lanes past the row, direct stores
     (200, 8, 1536, 2050, "bf16"),   # N = 8, 192 chunks per row
     (100, 1, 1024, 1024, "bf16"),   # one expert: every gate 1
     (300, 16, 1024, 4099, "bf16"),  # 410M-class width, large batch
