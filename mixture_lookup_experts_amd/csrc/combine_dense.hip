@@ -311,9 +311,10 @@ static hipError_t launch_dense_add(const int64_t* ids, const void* h, const void
   // 4096 60.3 -> 58.0 us; 410M-class T = 1024 9.80 -> 8.27 us, T = 4096
   // 32.7 -> 28.7 us (the staged router's two launches).  Not for the
   // block's ADD pass, whose partial-sum loads do not fit the registers of
-  // 16 wavefronts per compute unit.
+  // 16 wavefronts per compute unit, and not for rows wider than G chunks
+  // (D > 2048: G stops at 256), whose K steps would not fit the one batch.
   if constexpr (!ADD && VEC && sizeof(E) == 2 && NP <= 16 && G >= 128) {
-    if (T >= 1024) {
+    if (T >= 1024 && D <= 8 * G) {
       constexpr int kTok = 4, BT = kTok * G;
       hipLaunchKernelGGL((lookup_combine_kernel<E, NP, G, VEC, kRouterMfma, ADD, BT>),
                          dim3((unsigned)((T + kTok - 1) / kTok)), dim3(BT), 0, s, ids, (const E*)h,

@@ -159,7 +159,7 @@ def dense_plan(T, D, N, esz):
     bf = esz == BF16
     one_token = vector and bf and NP <= 16 and G >= 64 and T <= 1024
     tpb = 1 if one_token else pick_tokens_per_block(T, G)
-    if vector and bf and NP <= 16 and G >= 128 and T >= 1024:
+    if vector and bf and NP <= 16 and G >= 128 and T >= 1024 and C <= G:
         # four tokens per workgroup of 4 G threads, matrix-core router
         return dict(NP=NP, vector=vector, C=C, G=G, tpb=4, mode="wide", CH=vec)
     if vector and bf and T >= 2048 and tpb >= 2 and NP <= D:
@@ -397,7 +397,7 @@ def ids_for(T, V, seed):
 
 
 NS = [1, 3, 4, 5, 8, 12, 16, 17, 33, 64]
-DS_BF16 = [8, 24, 136, 1000, 1032, 2048, 60, 30]
+DS_BF16 = [8, 24, 136, 1000, 1032, 2048, 4096, 60, 30]
 TS = [1, 17, 1023, 1024, 1025, 2051]
 
 

@@ -96,6 +96,10 @@ COMBINE_CASES = [
     (200, 8, 1536, 2050, "bf16"),   # N = 8, 192 chunks per row
     (100, 1, 1024, 1024, "bf16"),   # one expert: every gate 1
     (300, 16, 1024, 4099, "bf16"),  # 410M-class width, large batch
+    # rows wider than 256 lanes (D > 2048): one token per workgroup with the
+    # vector router over several chunks per lane, at and past T = 1024
+    (100, 16, 4096, 1024, "bf16"),
+    (64, 12, 8192, 1100, "bf16"),
 ]
 
 
@@ -255,6 +259,7 @@ def run_nf3(ids, h, w_r, codes, scales):
                                            (300, 16, 1024, 1025, "bf16"), (200, 8, 512, 600, "bf16"),
                                            (300, 12, 1024, 1030, "bf16"),  # N padded to 16, ragged
                                            (300, 16, 2048, 1024, "bf16"),  # two batches of code loads
+                                           (100, 16, 4096, 1024, "bf16"),  # two chunk rounds per lane
                                            # four wavefronts per token, some without an expert in a round
                                            (300, 12, 1024, 100, "bf16")])
 def test_combine_nf3_matches_oracle(V, N, D, T, dtype):
@@ -825,7 +830,7 @@ def test_pack_int8_edge_cases_bit_exact():
                                            (40, 1, 64, 5, "bf16"), (300, 16, 1024, 2051, "bf16"),
                                            (100, 64, 512, 2048, "bf16"), (300, 12, 1024, 100, "bf16"),
                                            (300, 16, 1024, 1023, "bf16"), (300, 16, 1024, 1024, "bf16"),
-                                           (300, 12, 2048, 1027, "bf16")])
+                                           (300, 12, 2048, 1027, "bf16"), (100, 16, 4096, 1024, "bf16")])
 def test_combine_q_matches_oracle(fmt, V, N, D, T, dtype):
     seed = 3000 + V + N + D
     table = rand_table(seed, V, N, D, "bf16")
