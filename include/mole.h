@@ -155,9 +155,10 @@ int mole_build_lut(const void* emb, const void* w_up, const void* w_down, void* 
  *   ids [T] int64      h [T][D]      w_r [N][D]      lut [V][N][D]
  *   y   [T][D] fp32 (written, never read)
  * h, w_r and lut share `dtype`.  Router dot products, softmax and the
- * combine accumulate in fp32.  T == 0 is a no-op.  1 <= N <= 64
- * (MOLE_ERR_UNSUPPORTED above: the kernels keep a token's N gates in
- * registers); the same limit holds for every combine below.
+ * combine accumulate in fp32.  T == 0 is a no-op.  1 <= N <= 64 and
+ * D <= 2^20 (MOLE_ERR_UNSUPPORTED above: the kernels keep a token's N gates
+ * in registers, and the routers address the rows of h and w_r with 32-bit
+ * offsets); the same limits hold for every combine below.
  * ------------------------------------------------------------------------ */
 int mole_lookup_combine(const int64_t* ids, const void* h, const void* w_r, const void* lut,
                         float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
@@ -208,8 +209,9 @@ int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r,
  * dtype must be MOLE_BF16 (MOLE_ERR_UNSUPPORTED for MOLE_F32): bf16 inputs,
  * fp32 accumulation, the hidden activation rounded to bf16 between the two
  * products as in mole_build_lut, everything after the products in fp32.
- * Needs D % 8 == 0, F % 8 == 0 (MOLE_ERR_DIM) and D, F <= 2^22
- * (MOLE_ERR_UNSUPPORTED); 1 <= N <= 64.  T == 0 is a no-op.
+ * Needs D % 8 == 0, F % 8 == 0 (MOLE_ERR_DIM), D <= 2^20 (as for the
+ * combines) and F <= 2^22 (MOLE_ERR_UNSUPPORTED); 1 <= N <= 64.  T == 0 is
+ * a no-op.
  *
  * workspace: device scratch (16-byte aligned) of at least the size that
  * mole_layer_workspace_size(T, D, F) returns (0 for T == 0): router gates,

@@ -39,12 +39,13 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // sizes handed to kernels as int
 constexpr int64_t kMaxExperts = 64;             // combine kernels keep N gates in registers
+constexpr int64_t kMaxCombineDim = (int64_t)1 << 20;  // the routers address h and W_r rows with 32-bit offsets
 constexpr int64_t kMaxPanelStride = (int64_t)1 << 22;  // bf16 build: row stride of G and of the LUT
 
 int check_combine_common(int64_t T, int64_t V, int64_t D, int64_t N) {
   if (T < 0 || V <= 0 || D <= 0 || N <= 0) return MOLE_ERR_DIM;
   if (D > kMaxDim || T > kMaxDim) return MOLE_ERR_DIM;
-  if (N > kMaxExperts) return MOLE_ERR_UNSUPPORTED;
+  if (N > kMaxExperts || D > kMaxCombineDim) return MOLE_ERR_UNSUPPORTED;
   return MOLE_OK;
 }
 

@@ -198,6 +198,7 @@ def test_combine_argument_errors(lib):
     assert f(P(a), P(a), P(a), P(a), P(a), 4, 0, 64, 4, 1, None) == DIM
     assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, 0, 4, 1, None) == DIM
     assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, 64, 65, 1, None) == UNSUP
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, (1 << 20) + 8, 4, 1, None) == UNSUP
     assert f(P(a), P(a + 4), P(a), P(a), P(a), 4, 10, 64, 4, 1, None) == ALIGN
     assert f(None, None, None, None, None, 0, 10, 64, 4, 1, None) == OK  # empty batch: no-op
 
