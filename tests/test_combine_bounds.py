@@ -417,7 +417,7 @@ def test_dense_combine_loads_stay_in_bounds(esz):
 def test_quantised_combine_loads_stay_in_bounds(fmt):
     V = 41
     for N in NS:
-        for D in (64, 192, 1024, 2048):
+        for D in (64, 192, 1024, 2048, 4096):
             for T in (1, 17, 1023, 1024, 1025, 2049):
                 for esz in (BF16, F32):
                     if esz == F32 and T > 17:
@@ -429,7 +429,7 @@ def test_quantised_combine_loads_stay_in_bounds(fmt):
 def test_grouped_combine_loads_stay_in_bounds():
     V = 50
     for N in (1, 3, 4, 8, 16):
-        for D in (8, 64, 136, 1024, 2048):
+        for D in (8, 64, 136, 1024, 2048, 4096):
             for T in (1, 16, 17, 300, 4097):
                 buf = model_grouped(T, V, D, N, ids_for(T, V, N + D + T))
                 assert not buf.bad, (N, D, T, buf.bad[:3])
