@@ -75,15 +75,15 @@ struct SplitReduce {
 // per-wavefront partial sums of a chunk meet in LDS; each wavefront then
 // stores a 1/W share of the chunk's outputs.  This spreads a decode-sized
 // batch over W times as many wavefronts.
-template <typename TH, int NP, int CP, int S, int MODE, int FMT = kFmtNf3, int W = 1>
-__global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
+template <typename TH, int NP, int CP, int S, int MODE, int FMT = kFmtNf3, int W = 1, int BT = 256>
+__global__ __launch_bounds__(BT) void lookup_combine_nf3_kernel(
     const int64_t* __restrict__ ids, const TH* __restrict__ h, const TH* __restrict__ w_r,
     const uint8_t* __restrict__ codes, const void* __restrict__ scales_v,
     float* __restrict__ y, int64_t T_, int D, int N, int tpb) {
   using Q = QFmt<FMT>;
   constexpr int G = CP * S;                        // lanes per token (<= 64)
   static_assert(G <= kWave, "a token's lanes must share one wavefront");
-  constexpr int MAXTPB = 256 / G < kMaxTokPerBlock ? 256 / G : kMaxTokPerBlock;
+  constexpr int MAXTPB = BT / G < kMaxTokPerBlock ? BT / G : kMaxTokPerBlock;
   static_assert(W == 1 || (G == kWave && MODE == kRouterLane), "W > 1: one token per block, full wavefronts");
   constexpr int EPL = (NP + S * W - 1) / (S * W);  // experts per lane
   constexpr int EC = EPL < Q::kBatch ? EPL : Q::kBatch;  // experts per batch of code loads
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   constexpr bool kMfmaRouter = sizeof(TH) == 2 && MODE == kRouterMfma;
   constexpr bool kLaneRouter = !kMfmaRouter && NP <= 16;
   constexpr int NPAD = ((NP + 15) / 16) * 16;
-  __shared__ float red[kMfmaRouter ? 4 * 16 * NPAD : MAXTPB * NP];
+  __shared__ float red[kMfmaRouter ? (BT / kWave) * 16 * NPAD : MAXTPB * NP];
   __shared__ float gsh[kMaxTokPerBlock * NP];
   // Decode table indexed by two consecutive codes at once (6 bits for NF3,
   // one byte for NF4): entry p holds the levels of codes p % L and p / L.
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   // 16.8 MB of y (410M-class table, T = 4096).
   constexpr bool kStageOut = W == 1 && G == kWave && OW >= 4;
   // (one wavefront per block in the vector-router launches, up to four in the others)
-  __shared__ float ys[kStageOut ? (MODE == kRouterLane ? 1 : 256 / kWave) * CP * 32 : 1];
+  __shared__ float ys[kStageOut ? (MODE == kRouterLane ? 1 : BT / kWave) * CP * 32 : 1];
 
   const int tid = threadIdx.x;
   if constexpr (FMT == kFmtNf3) {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
   // clamped), so the router's matrix work waits only for its own operands.
   // Measured on the 410M-class NF3 table at T = 4096: 18.1 -> 16.3 us.
   constexpr bool kReorder = kMfmaRouter && G == kWave && W == 1;
-  MfmaRouter<NP> rt;
+  MfmaRouter<NP, (NP <= 16 && BT > 256) ? 2048 / BT : 0> rt;
   LaneRouter<TH, kLaneRouter ? NP : 1> lr;
   if constexpr (kReorder) {
     rt.load_first(reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_r), t0, T_, tpb, D,
@@ -337,6 +337,15 @@ __global__ __launch_bounds__(256) void lookup_combine_nf3_kernel(
 // ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
+// Tokens (wavefronts) per workgroup of the wide launch: 8 from T = 4096 on
+// (each workgroup streams W_r's K share once for twice as many tokens: 512
+// workgroups read 16 MB of W_r from L2 instead of 32 MB at T = 4096), 4
+// below (8 would leave half the compute units idle at T = 1024).  Measured
+// on the 410M-class NF3 table: T = 4096 distinct 15.0 -> 14.2 us, Zipf
+// 14.6 -> 13.1 us, T = 16384 distinct 48.3 -> 44.0 us; T = 1024 distinct
+// 7.9 us with 4 tokens, 8.5 us with 8.
+constexpr int64_t kQuantEightTokMinT = 4096;
+
 template <typename TH, int NP, int CP, int FMT>
 static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
                              const void* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
@@ -344,14 +353,15 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   constexpr int G = CP * S;
   // Below T = 1024 (bf16 h, NP <= 16, full-wavefront tokens): one token per
   // workgroup with the vector-unit router, spread over W wavefronts below.
-  // From T = 1024 on, four tokens per workgroup (one per wavefront) with the
+  // From T = 1024 on, four tokens per workgroup (one per wavefront; eight
+  // from T = 4096, see kQuantEightTokMinT) with the
   // matrix-core router, whose operands go out before the code loads; on the
   // 410M-class table with distinct ids, against the one-token shapes: T =
   // 1024 NF3 9.26 -> 8.51 us, NF4 9.83 -> 9.01 us, int8 10.2 -> 8.3 us;
   // T = 4096 int8 26.4 -> 23.3 us.
   const bool full_wave = G == kWave && sizeof(TH) == 2 && NP <= 16;
   const bool one_token = full_wave && T < 1024;
-  const int tpb = one_token ? 1 : (full_wave ? 4 : pick_tokens_per_block(T, G));
+  const int tpb = one_token ? 1 : (full_wave ? (T >= kQuantEightTokMinT ? 8 : 4) : pick_tokens_per_block(T, G));
   const int64_t blocks = (T + tpb - 1) / tpb;
   // (No staged-router launch here: the extra launch measured slower --
   // 410M-class NF3 table, T=4096: 20.1 -> 22.6 us.)
@@ -373,6 +383,14 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
       }
       MOLE_NF3_W(1);
 #undef MOLE_NF3_W
+      return hipGetLastError();
+    }
+  }
+  if constexpr (G == kWave && sizeof(TH) == 2 && NP <= 16) {
+    if (full_wave && tpb == 8) {
+      hipLaunchKernelGGL((lookup_combine_nf3_kernel<TH, NP, CP, S, kRouterMfma, FMT, 1, 8 * kWave>),
+                         dim3((unsigned)blocks), dim3(G * tpb), 0, s, ids, (const TH*)h, (const TH*)w_r, codes,
+                         scales, y, T, D, N, tpb);
       return hipGetLastError();
     }
   }
