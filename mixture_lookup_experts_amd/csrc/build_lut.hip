@@ -11,14 +11,15 @@
 //           (grid z = expert), written with row stride N*D.
 // Both are "NT" products C = A . B^T with A and B stored K-contiguous, so
 // the MFMA operands come straight from K-contiguous rows.  Kernel: 256x256
-// output tile per 256-thread workgroup, 4 waves in a 2x2 arrangement, each
-// owning a 128x128 sub-tile of v_mfma_f32_32x32x16_bf16 accumulators.  The
+// output tile per workgroup of 4 waves in a 2x2 arrangement, each owning a
+// 128x128 sub-tile of v_mfma_f32_32x32x16_bf16 accumulators, or (the build's
+// GEMMs) of 8 waves in a 2x4 arrangement with 128x64 sub-tiles.  The
 // K loop streams 64-wide slices of A and B through a double-buffered LDS
 // ring (row = 128 bytes; 16-byte segment s of row r stored at s ^ ((r/2) & 7):
 // the LDS serves 256 bytes (64 banks) per cycle, so the 16 lanes of one
 // ds_read_b128 pass -- 16 consecutive rows -- and the 16 lanes of a staging
 // write -- 2 rows x 8 segments -- each hit 16 distinct 16-byte bank groups).
-// Each thread stages 16 segments per slice in registers; the software
+// Each thread stages 16 (8) segments per slice in registers; the software
 // pipeline writes one staged segment to LDS and at once re-issues its load
 // for the slice after next, spread over the MFMAs of a K step, so every
 // global load has a full slice of MFMA work to arrive, and the fragments of
@@ -134,15 +135,23 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int i) {
 // (16-byte output chunks) and, with a K-contiguous operand, K % 8 == 0
 // (16-byte K segments); an MN-major operand needs its M (or N) extent, ld
 // and batch offset to be multiples of 8 and 63 * ld + 256 < 2^30.
-template <int BM, int BN, int EPI, int OPS = kOpsKK>
-__global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2;     // wave sub-tile
+template <int BM, int BN, int EPI, int OPS = kOpsKK, int NW = 4>
+__global__ __launch_bounds__(NW * 64) void gemm_nt_bf16_kernel(GemmArgs p) {
+  constexpr int NT = NW * 64;                 // threads
+  constexpr int WGN = NW / 2;                 // waves along N (two along M)
+  constexpr int WM = BM / 2, WN = BN / WGN;   // wave sub-tile
   constexpr int TM = WM / 32, TN = WN / 32;   // MFMA tiles per wave
-  constexpr int SA = BM * 8 / 256, SB = BN * 8 / 256;  // 16-byte segments per thread
+  constexpr int SA = BM * 8 / NT, SB = BN * 8 / NT;  // 16-byte segments per thread
   constexpr int NS = SA + SB;                 // staging slots per thread
+  constexpr int SPK = NS / 4;                 // slots written and re-loaded per K step
   constexpr int KS = kBK / 16;                // MFMA K steps per LDS stage
-  static_assert(KS == 4 && TM == 4 && TN == 4 && NS == 16,
-                "the software pipeline below is written for 4 K steps of 4x4 MFMA tiles and 16 slots");
+  // Four waves: 4x4 MFMA tiles per wave and 16 slots; eight waves (two per
+  // SIMD): 4x2 tiles and 8 slots.  Either way one slot is handled after
+  // every fourth MFMA of a K step, SPK per step.
+  static_assert(KS == 4 && TM == 4 && TM * TN == 4 * SPK && (NW == 4 || NW == 8),
+                "the software pipeline below is written for 4 K steps and one slot per 4 MFMAs");
+  static_assert(NW == 4 || ((OPS & (kOpsAmn | kOpsBmn)) == 0 && EPI != kEpiF32Staged),
+                "eight waves: K-contiguous operands and the direct or bf16-staged epilogues only");
   constexpr int kRing = (BM + BN) * 8;        // uint4 per LDS stage
   constexpr int kCPitch = BN / 8 + 1;         // staged output row pitch in uint4 (16-byte pad)
   constexpr int kLds = (EPI == kEpiStoreStaged && BM * kCPitch > 2 * kRing) ? BM * kCPitch : 2 * kRing;
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   auto smem = reinterpret_cast<uint4(*)[kRing]>(lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   int z, tm, tn;
   tile_of_block(p, z, tm, tn);
   const int M = p.M, N = p.N, K = p.K;
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
       const int kr = 4 * (seg + 8 * ((idx >> 2) & 1)) + (idx & 3);  // k row within the slice
       off[s] = (uint32_t)((kr * ld + srow * 8) * 2);
     } else {
-      const int row = srow + 32 * idx;
+      const int row = srow + (NT / 8) * idx;
       const int64_t pitch = (is_a && kApanel) ? kPanel : ld;
       off[s] = row < lim ? (uint32_t)(row * pitch * 2 + seg * 16) : kOob;
     }
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
         sm2[at * 2 + (kq & 1)] = h ? make_uint2(rs[s].z, rs[s].w) : make_uint2(rs[s].x, rs[s].y);
       }
     } else {
-      const int row = (is_a ? 0 : BM) + srow + 32 * idx;
+      const int row = (is_a ? 0 : BM) + srow + (NT / 8) * idx;
       smem[st][row * 8 + pseg] = rs[s];
     }
   };
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   for (int s = 0; s < NS; ++s) lslot(s, 1);
   transpose_group(0);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < SPK; ++s) {
     wslot(s, 1);
     lslot(s, 2);
   }
@@ -350,13 +359,13 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
     const int cur = kt & 1;
     fload(cur, 1, fa[1], fb[1]);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_step(fa[0], fb[0], 4, cur ^ 1, kt + 2);
+    mfma_step(fa[0], fb[0], SPK, cur ^ 1, kt + 2);
     fload(cur, 2, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_step(fa[1], fb[1], 8, cur ^ 1, kt + 2);
+    mfma_step(fa[1], fb[1], 2 * SPK, cur ^ 1, kt + 2);
     fload(cur, 3, fa[1], fb[1]);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_step(fa[0], fb[0], 12, cur ^ 1, kt + 2);
+    mfma_step(fa[0], fb[0], 3 * SPK, cur ^ 1, kt + 2);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     fload(cur ^ 1, 0, fa[0], fb[0]);
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
     }
     __syncthreads();
     constexpr int kChunks = BN / 8;  // 16-byte chunks per tile row
-    constexpr int kRowsPerPass = 256 / kChunks;
+    constexpr int kRowsPerPass = NT / kChunks;
     const int ch = tid % kChunks;
     const int n = n0 + ch * 8;
 #pragma unroll 4
@@ -542,7 +551,7 @@ __global__ __launch_bounds__(256) void gemm_nt_bf16_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int EPI, int OPS = kOpsKK>
+template <int BM, int BN, int EPI, int OPS = kOpsKK, int NW = 4>
 static hipError_t launch_gemm(const uint16_t* A, int64_t lda, int64_t sAz, const uint16_t* B, int64_t ldb,
                               int64_t sBz, uint16_t* C, int64_t ldc, int64_t sCz, int M, int N, int K,
                               int batch, int xcd_order, hipStream_t s, const uint16_t* aux = nullptr,
@@ -550,7 +559,7 @@ static hipError_t launch_gemm(const uint16_t* A, int64_t lda, int64_t sAz, const
   GemmArgs p{A, lda, sAz, B, ldb, sBz, C, ldc, sCz, M, N, K, (M + BM - 1) / BM, (N + BN - 1) / BN, batch,
              xcd_order, aux, pre, a_pstride, c_pstride};
   const int64_t total = (int64_t)p.tiles_m * p.tiles_n * batch;
-  hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EPI, OPS>), dim3((unsigned)total), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_nt_bf16_kernel<BM, BN, EPI, OPS, NW>), dim3((unsigned)total), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -582,6 +591,15 @@ size_t build_lut_rec_workspace(int64_t V, int64_t D, int64_t F, int64_t N) {
 // column panels in its L2).
 constexpr int kGemm1PanelOrder = 1;
 
+// Waves per workgroup of the build's two GEMMs: eight, two per SIMD, so that
+// one wave's matrix instructions issue while the other waits at the slice
+// barrier or for its LDS fragments (the 256x256 tile, the LDS ring and the
+// order of every accumulation are those of the four-wave form, so the
+// tables are bit-identical).  Measured on 1B-class builds: 47.7 -> 46.1 ms
+// and 50.2 -> 49.0 ms (two boxes; GEMM-2 1769 -> 1713 us and GEMM-1 2152 ->
+// 2133 us per 4096-row block); 160M-class 2.20 -> 2.03 ms.
+constexpr int kBuildWaves1 = 8, kBuildWaves2 = 8;
+
 hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, const uint16_t* w_down,
                                  uint16_t* lut, int64_t V, int64_t D, int64_t F, int64_t N,
                                  void* ws, size_t ws_bytes, hipStream_t s, uint16_t* pre) {
@@ -610,7 +628,7 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
       err = launch_gemm<kBM, kBN, kEpiGeluPre>(emb + v0 * D, D, 0, w_up, D, 0, G, NF, 0, (int)mc, (int)NF, (int)D, 1,
                                                /*xcd_order=*/0, s, nullptr, pre + v0 * NF);
     else if (panel)
-      err = launch_gemm<kBM, kBN, kEpiGelu, kOpsCpanel>(emb + v0 * D, D, 0, w_up, D, 0, G, kPanel, 0, (int)mc,
+      err = launch_gemm<kBM, kBN, kEpiGelu, kOpsCpanel, kBuildWaves1>(emb + v0 * D, D, 0, w_up, D, 0, G, kPanel, 0, (int)mc,
                                                         (int)NF, (int)D, 1, kGemm1PanelOrder, s, nullptr, nullptr,
                                                         0, pstride);
     else
@@ -619,11 +637,11 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
     if (err != hipSuccess) return err;
     const bool staged = N * D * 2 >= kStagedMinRowBytes;
     if (panel && staged)
-      err = launch_gemm<kBM, kBN, kEpiStoreStaged, kOpsApanel>(G, kPanel, (F / kPanel) * pstride, w_down, F, D * F,
+      err = launch_gemm<kBM, kBN, kEpiStoreStaged, kOpsApanel, kBuildWaves2>(G, kPanel, (F / kPanel) * pstride, w_down, F, D * F,
                                                                lut + v0 * N * D, N * D, D, (int)mc, (int)D, (int)F,
                                                                (int)N, /*xcd_order=*/1, s, nullptr, nullptr, pstride);
     else if (panel)
-      err = launch_gemm<kBM, kBN, kEpiStore, kOpsApanel>(G, kPanel, (F / kPanel) * pstride, w_down, F, D * F,
+      err = launch_gemm<kBM, kBN, kEpiStore, kOpsApanel, kBuildWaves2>(G, kPanel, (F / kPanel) * pstride, w_down, F, D * F,
                                                          lut + v0 * N * D, N * D, D, (int)mc, (int)D, (int)F, (int)N,
                                                          /*xcd_order=*/1, s, nullptr, nullptr, pstride);
     else if (staged)
@@ -641,7 +659,8 @@ hipError_t launch_build_lut_bf16(const uint16_t* emb, const uint16_t* w_up, cons
 // shared-expert up-projection of the MoLE block uses it for long batches).
 hipError_t launch_gemm_gelu_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C,
                                  int64_t ldc, int M, int N, int K, hipStream_t s) {
-  return launch_gemm<kBM, kBN, kEpiGelu>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1, /*xcd_order=*/0, s);
+  return launch_gemm<kBM, kBN, kEpiGelu, kOpsKK, kBuildWaves1>(A, lda, 0, B, ldb, 0, C, ldc, 0, M, N, K, 1,
+                                                              /*xcd_order=*/0, s);
 }
 
 // Whether an MN-major operand fits the kernel's 32-bit slice offsets and
