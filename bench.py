@@ -398,7 +398,8 @@ def layer410_probe(torch, mole, synth, dev, stream, to_dev):
     ids and a distinct-id control: the bf16 combine, the device-grouped bf16
     combine (index + combine, both launches timed), the NF3, NF4 and int8
     combines from HBM and the NF3 combine from pinned host memory (host
-    dedupe and gather, one PCIe copy of the distinct rows, combine).  50
+    dedupe and gather, one PCIe copy of the distinct rows, combine) and read in
+    place by the kernel from page-locked host memory.  50
     launches cycling 8 id batches per point; a 1 GiB device copy in the same
     run gives the measured HBM roofline, a 256 MiB pinned copy the PCIe one."""
     w = synth.WORKLOADS["410m"]
@@ -488,6 +489,11 @@ def layer410_probe(torch, mole, synth, dev, stream, to_dev):
             res["nf3_host"] = {"us": us, "tokens_per_s": T / (us * 1e-6), "pcie_bytes": pcie,
                                "pcie_gbs_effective": pcie / (us * 1e-6) / 1e9,
                                "wall_s": time.perf_counter() - t0}
+            # the same table read in place by the kernel (every token reads its own rows over PCIe)
+            us = time_launches(torch, stream, lambda i: mole.mole_lookup_combine_nf3_mapped(
+                ids_l[i % 8], h_l[i % 8], w_r, codes_h, scales_h, y, stream=stream), 20)
+            res["nf3_mapped"] = {"us": us, "tokens_per_s": T / (us * 1e-6), "pcie_bytes_requested": T * nf3_row,
+                                 "pcie_gbs_effective": T * nf3_row / (us * 1e-6) / 1e9}
             out["T%d_%s" % (T, kind)] = res
             del h_l, y, gws, st_h, st_d
     del lut, codes, scales, codes4, scales4, codes8, scales8, codes_h, scales_h
@@ -498,7 +504,8 @@ def layer410_probe(torch, mole, synth, dev, stream, to_dev):
 def layer160_probe(torch, mole, synth, dev, stream, to_dev):
     """The 160M-class layer (V=50304 D=768 N=4 F=3072): the build timed on
     its own, the NF3 pack, and the bf16 and NF3 combines at its decode
-    batches T = 1, 8, 64, 256 (Zipf ids; 50 launches cycling 8 batches).
+    batches T = 1, 8, 64, 256 (Zipf ids; 50 launches cycling 8 batches),
+    the NF3 one also with its table in page-locked host memory read in place.
     Every launch here moves under 3 MB: latency-bound."""
     w = synth.WORKLOADS["160m"]
     V, D, N, F = w.V, w.D, w.N, w.F
@@ -515,16 +522,25 @@ def layer160_probe(torch, mole, synth, dev, stream, to_dev):
     byts = V * N * D * 2 + V * N * (CB + 2 * SB)
     out["pack_nf3"] = {"ms": us / 1e3, "gbs": byts / (us * 1e-6) / 1e9,
                        "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    # the NF3 table in page-locked host memory, read in place at decode sizes
+    torch.cuda.synchronize()
+    codes_h = codes.cpu().pin_memory()
+    scales_h = scales.cpu().pin_memory()
+    nf3_row = N * (CB + 2 * SB)
     for T in w.tokens:
         ids_l = [to_dev(synth.make_ids(w, T, step=s)) for s in range(8)]
         h_l = [to_dev(synth.make_hidden(w, T, step=s)) for s in range(8)]
         y = torch.empty((T, D), dtype=torch.float32, device=dev)
+        us_m = time_launches(torch, stream, lambda i: mole.mole_lookup_combine_nf3_mapped(
+            ids_l[i % 8], h_l[i % 8], w_r, codes_h, scales_h, y, stream=stream), 50)
         out["T%d" % T] = {
             "bf16": combine_entry(T, time_launches(torch, stream, lambda i: mole.mole_lookup_combine(
                 ids_l[i % 8], h_l[i % 8], w_r, lut, y, stream=stream), 50), N * D * 2, D, N),
             "nf3": combine_entry(T, time_launches(torch, stream, lambda i: mole.mole_lookup_combine_nf3(
-                ids_l[i % 8], h_l[i % 8], w_r, codes, scales, y, stream=stream), 50), N * (CB + 2 * SB), D, N)}
-    del lut, codes, scales
+                ids_l[i % 8], h_l[i % 8], w_r, codes, scales, y, stream=stream), 50), nf3_row, D, N),
+            "nf3_mapped": {"us": us_m, "tokens_per_s": T / (us_m * 1e-6), "pcie_bytes_requested": T * nf3_row,
+                           "pcie_gbs_effective": T * nf3_row / (us_m * 1e-6) / 1e9}}
+    del lut, codes, scales, codes_h, scales_h
     torch.cuda.empty_cache()
     return out
 
@@ -710,7 +726,9 @@ def host_stack_probe(torch, mole, synth, dev, stream):
     reads one cached row) are enqueued on the compute stream first, the
     prefetch's host gather and copy run meanwhile (the copy on a second
     stream), and the 16 NF3 combines wait for the copy; against the same
-    work in order on one stream.  Also a pinned host->device copy of 256
+    work in order on one stream.  And (d) the 16 combines reading each
+    layer's host table in place (mole_lookup_combine_nf3_mapped: every token
+    reads its own rows over PCIe, no gather or staging).  Also a pinned host->device copy of 256
     MiB, the PCIe roofline measured in the same run.  The host tables are
     left as allocated (zero pages): the combine's cost does not depend on the
     code values."""
@@ -783,6 +801,14 @@ def host_stack_probe(torch, mole, synth, dev, stream):
                 mole.mole_layer_forward(ids0, h_l[b][l], w_rs[l], lut0, w_up[l], w_down[l], x_l[l], ws_l,
                                         stream=stream)
 
+        ids_dl = [x.to(dev) for x in ids_l]
+
+        def mapped(b):
+            # (d) each layer's table read in place by its combine: no gather, copy or staging
+            for l in range(L):
+                mole.mole_lookup_combine_nf3_mapped(ids_dl[b], h_l[b][l], w_rs[l], codes_h[l], scales_h[l],
+                                                    y_l[l], stream=stream)
+
         def serial(b):
             ffns(b)
             prefetched(b)
@@ -805,8 +831,9 @@ def host_stack_probe(torch, mole, synth, dev, stream):
             done[0].record(stream)
 
         res = {}
-        for name, fn in (("per_layer", per_layer), ("prefetched", prefetched), ("ffn_only", ffns),
-                         ("ffn_then_prefetched", serial), ("ffn_overlapped_prefetch", overlapped)):
+        for name, fn in (("per_layer", per_layer), ("prefetched", prefetched), ("mapped", mapped),
+                         ("ffn_only", ffns), ("ffn_then_prefetched", serial),
+                         ("ffn_overlapped_prefetch", overlapped)):
             for b in range(2):
                 fn(b % NB)
             torch.cuda.synchronize()
@@ -828,12 +855,12 @@ def host_stack_probe(torch, mole, synth, dev, stream):
         del x_l, ws_l
         U = float(np.mean(uniq)) if uniq else 0.0
         pcie = L * U * N * (CB + 2 * SB) + 8 * T
-        best = min(res["per_layer_us_per_step"], res["prefetched_us_per_step"])
+        best = min(res["per_layer_us_per_step"], res["prefetched_us_per_step"], res["mapped_us_per_step"])
         res.update({"mean_unique_ids": U, "pcie_bytes_per_step": pcie,
                     "pcie_gbs_effective_prefetched": pcie / (res["prefetched_us_per_step"] * 1e-6) / 1e9,
                     "tokens_per_s": T / (best * 1e-6)})
         out["T%d" % T] = res
-        del st1_h, st1_d, stL_h, stL_d, h_l, y_l
+        del st1_h, st1_d, stL_h, stL_d, h_l, y_l, ids_dl
     torch.cuda.synchronize()
     ctx.__exit__(None, None, None)
     del codes_h, scales_h, w_rs, w_up, w_down

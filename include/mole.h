@@ -59,6 +59,7 @@ extern "C" {
 #define MOLE_ERR_IO (-9)          /* a table file could not be read or written */
 #define MOLE_ERR_FORMAT (-10)     /* not a MoLE NF3 table file of this version */
 #define MOLE_ERR_HOST (-11)       /* a host-side allocation or thread creation failed */
+#define MOLE_ERR_MEMORY (-12)     /* a host table is not page-locked memory the device can read */
 
 #define MOLE_F32 0
 #define MOLE_BF16 1
@@ -377,6 +378,32 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
                                  void* stage_host, void* stage_dev, size_t stage_bytes, float* y,
                                  int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
                                  int nthreads, int64_t* n_unique, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host-resident NF3 table read in place (inference section: the table in
+ * lower-tier storage, only the retrieved vectors crossing into the GPU).
+ *
+ * mole_lookup_combine_nf3_mapped: the NF3 combine of mole_lookup_combine_nf3
+ * with the table left in page-locked host memory: the kernel reads each
+ * token's N rows of codes and scales over PCIe as it combines them, so a
+ * call is one launch -- no host-side dedupe or gather, no staging area, no
+ * wait on the host.  ids (int64 [T]), h, w_r and y are device memory as for
+ * mole_lookup_combine_nf3; codes_host [V][N][3D/8] and scales_host
+ * [V][N][D/64] must lie in page-locked host memory allocated through HIP
+ * (hipHostMalloc, or a pinned tensor of the framework) and must not be
+ * written while a call that reads them is in flight.  Both ranges are
+ * checked with the runtime's pointer attributes before anything is
+ * enqueued: pageable or unknown memory returns MOLE_ERR_MEMORY (a kernel
+ * reading it would fault).  Every token reads its own rows, so repeated
+ * ids cross PCIe again unless the GPU's caches still hold them; for large
+ * batches with repeated ids mole_lookup_combine_nf3_host (one copy of the
+ * distinct rows) moves fewer bytes.  Asynchronous on `stream`; capturable
+ * in a HIP graph (the checks run at call time, the launch is the device
+ * combine's).
+ * ------------------------------------------------------------------------ */
+int mole_lookup_combine_nf3_mapped(const int64_t* ids, const void* h, const void* w_r,
+                                   const uint8_t* codes_host, const uint16_t* scales_host, float* y,
+                                   int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h, void* stream);
 
 /* ------------------------------------------------------------------------
  * Host-resident NF3 tables of a stack of L layers, prefetched at the start

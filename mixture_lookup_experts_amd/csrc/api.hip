@@ -335,13 +335,14 @@ const char* mole_status_string(int status) {
     case MOLE_ERR_IO: return "table file read or write failed";
     case MOLE_ERR_FORMAT: return "not a MoLE NF3 table file of this version";
     case MOLE_ERR_HOST: return "host memory or thread allocation failed";
+    case MOLE_ERR_MEMORY: return "host table not in page-locked memory the device can read";
     default: return "unknown status";
   }
 }
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 8; }
+int mole_abi_version(void) { return 9; }
 
 int mole_release_host_state(void) {
   return guarded([&] {
@@ -474,6 +475,49 @@ int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r, 
       !aligned16(y))
     return MOLE_ERR_ALIGN;
   return hip_status(mole::launch_lookup_combine_nf3(ids, h, w_r, codes, scales, y, T, D, N, dtype_h,
+                                                    as_stream(stream)));
+}
+
+// The device address of the host range [p, p + bytes) if all of it lies in
+// one page-locked host allocation that the device can read, else null.  (A
+// failed query leaves an error behind in the runtime's last-error slot; it is
+// cleared so that the caller's next error check does not see it.)
+static const char* mapped_host_range(const void* p, size_t bytes) {
+  const char* first = static_cast<const char*>(p);
+  const char* last = first + bytes - 1;
+  const char* dev[2] = {nullptr, nullptr};
+  const char* q[2] = {first, last};
+  for (int i = 0; i < 2; ++i) {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, q[i]) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    if (a.type != hipMemoryTypeHost || !a.devicePointer || !a.hostPointer) return nullptr;
+    // (the runtime may report the allocation's base or the queried address
+    // itself; the offset from its host address covers both)
+    dev[i] = static_cast<const char*>(a.devicePointer) + (q[i] - static_cast<const char*>(a.hostPointer));
+  }
+  return dev[1] - dev[0] == (ptrdiff_t)(bytes - 1) ? dev[0] : nullptr;
+}
+
+int mole_lookup_combine_nf3_mapped(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes_host,
+                                   const uint16_t* scales_host, float* y, int64_t T, int64_t V, int64_t D,
+                                   int64_t N, int dtype_h, void* stream) {
+  if (!dtype_ok(dtype_h)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (D % 64 != 0) return MOLE_ERR_DIM;
+  if (T == 0) return MOLE_OK;
+  if (!ids || !h || !w_r || !codes_host || !scales_host || !y) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(codes_host) || !aligned16(scales_host) ||
+      !aligned16(y))
+    return MOLE_ERR_ALIGN;
+  const char* codes_d = mapped_host_range(codes_host, (size_t)(V * N * (3 * D / 8)));
+  const char* scales_d = mapped_host_range(scales_host, (size_t)(V * N * (D / 64)) * 2);
+  if (!codes_d || !scales_d) return MOLE_ERR_MEMORY;
+  return hip_status(mole::launch_lookup_combine_nf3(ids, h, w_r, reinterpret_cast<const uint8_t*>(codes_d),
+                                                    reinterpret_cast<const uint16_t*>(scales_d), y, T, D, N, dtype_h,
                                                     as_stream(stream)));
 }
 

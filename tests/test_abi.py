@@ -14,7 +14,8 @@ from mixture_lookup_experts_amd import _native
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mole.h")
 
-OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT, HOST = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11
+OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT, HOST, MEMORY = (0, -1, -2, -3, -4, -5, -6, -7, -8, -9,
+                                                                   -10, -11, -12)
 
 
 def declared_functions():
@@ -40,18 +41,19 @@ def test_header_declares_the_hot_path():
                "mole_train_forward", "mole_train_backward", "mole_nf3_file_write", "mole_nf3_file_shape",
                "mole_gather_nf3_file", "mole_lookup_combine_nf3_file", "mole_lookup_combine_grouped",
                "mole_lookup_combine_grouped_workspace_size", "mole_check_ids", "mole_release_host_state",
-               "mole_nf3_midpoints", "mole_nf4_midpoints", "mole_gelu_phi_coefficients"):
+               "mole_nf3_midpoints", "mole_nf4_midpoints", "mole_gelu_phi_coefficients",
+               "mole_lookup_combine_nf3_mapped"):
         assert fn in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 8
+    assert lib.mole_abi_version() == 9
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT, HOST):
+    for code in (OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT, HOST, MEMORY):
         assert mole.mole_status_string(code) not in ("", "unknown status")
     assert mole.mole_status_string(12345) == "unknown status"
 
@@ -212,6 +214,19 @@ def test_nf3_argument_errors(lib):
     assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 96, 4, 1, None) == DIM
     assert g(P(a), P(a), P(a), P(a), None, P(a), 4, 10, 128, 4, 1, None) == NULL
     assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 128, 4, 5, None) == DTYPE
+
+
+def test_mapped_nf3_argument_errors(lib):
+    """The in-place host-table combine validates like the device one before
+    it queries the table's memory (no HIP call on any of these paths)."""
+    a = 0x1000
+    g = lib.mole_lookup_combine_nf3_mapped
+    assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 96, 4, 1, None) == DIM
+    assert g(P(a), P(a), P(a), None, P(a), P(a), 4, 10, 128, 4, 1, None) == NULL
+    assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 128, 4, 5, None) == DTYPE
+    assert g(P(a), P(a), P(a), P(a + 8), P(a), P(a), 4, 10, 128, 4, 1, None) == ALIGN
+    assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 128, 65, 1, None) == UNSUP
+    assert g(None, None, None, None, None, None, 0, 10, 128, 4, 1, None) == OK  # empty batch: no-op
 
 
 def test_host_staging_size_and_errors(lib):

@@ -397,6 +397,65 @@ def test_combine_nf3_host_resident(T):
         assert combine_rel_err(y_host, ref) <= COMBINE_TOL
 
 
+@pytest.mark.parametrize("T", [1, 256, 1024, 4096])
+def test_combine_nf3_mapped_host_table(T):
+    """Table in page-locked host memory read in place by the kernel (one
+    launch, no staging).  Every launch shape of the NF3 combine (one token on
+    one or several wavefronts, four and eight tokens per workgroup) reads the
+    host rows; the codes sit at an offset inside their pinned allocation.
+    Equal bit for bit to the device-resident combine, and to the oracle
+    within the combine bar; twice in a row."""
+    w = synth.WORKLOADS["410m-nf3"]
+    V, N, D = w.V, w.N, w.D
+    ids = synth.make_ids(w, T, step=5)
+    table = rand_table(93, V, N, D, "bf16", std=0.02, rows=np.unique(ids))
+    codes, scales, _ = oracle.pack_nf3(table)
+    h = synth.make_hidden(w, T, step=5)
+    w_r = synth.make_router(w)
+    pool = torch.empty(codes.size + 256, dtype=torch.uint8, pin_memory=True)
+    codes_h = pool[256:].view(V, N, 3 * D // 8)
+    codes_h.copy_(torch.from_numpy(codes))
+    scales_h = torch.from_numpy(scales.view(np.int16)).pin_memory()
+    ref_dev = run_nf3(ids, h, w_r, codes, scales)
+    ref = oracle.lookup_combine_nf3(ids, h, w_r, codes, scales)
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        y.fill_(float("nan"))
+        mole.mole_lookup_combine_nf3_mapped(dev(ids), dev(h), dev(w_r), codes_h, scales_h, y)
+        torch.cuda.synchronize()
+        y_host = host(y)
+        np.testing.assert_array_equal(y_host, ref_dev)
+        assert combine_rel_err(y_host, ref) <= COMBINE_TOL
+
+
+def test_combine_nf3_mapped_refuses_unmapped_tables():
+    """Pageable host memory and device memory are refused on the host before
+    anything is enqueued (a kernel reading pageable memory would fault)."""
+    V, N, D, T = 64, 4, 128, 8
+    ids = dev(np.arange(T, dtype=np.int64))
+    h = torch.zeros((T, D), dtype=torch.bfloat16, device="cuda")
+    w_r = torch.zeros((N, D), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((T, D), dtype=torch.float32, device="cuda")
+    codes_p = torch.zeros((V, N, 3 * D // 8), dtype=torch.uint8)     # pageable
+    scales_p = torch.zeros((V, N, D // 64), dtype=torch.int16)
+    scales_pin = scales_p.pin_memory()
+    for c, sc in ((codes_p, scales_pin), (codes_p.pin_memory(), scales_p)):
+        with pytest.raises(mole.MoleError) as e:
+            mole.mole_lookup_combine_nf3_mapped(ids, h, w_r, c, sc, y)
+        assert e.value.status == -12
+    # device memory as the "host" table: the binding refuses it, and so does the C ABI
+    codes_d = codes_p.cuda()
+    rc = mole.library().mole_lookup_combine_nf3_mapped(ids.data_ptr(), h.data_ptr(), w_r.data_ptr(),
+                                                       codes_d.data_ptr(), scales_pin.data_ptr(), y.data_ptr(),
+                                                       T, V, D, N, 1, None)
+    assert rc == -12
+    torch.cuda.synchronize()
+    # the refused calls left no error behind for the next launch
+    mole.mole_lookup_combine_nf3_mapped(ids, h, w_r, codes_p.pin_memory(), scales_pin, y)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+
+
 @pytest.mark.parametrize("T", [1, 256, 2048])
 def test_combine_nf3_from_table_file(T, tmp_path):
     """Table in a file (the disk tier); only the distinct requested rows are
