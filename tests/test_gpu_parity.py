@@ -397,15 +397,17 @@ def test_combine_nf3_host_resident(T):
         assert combine_rel_err(y_host, ref) <= COMBINE_TOL
 
 
-@pytest.mark.parametrize("T", [1, 256, 1024, 4096])
-def test_combine_nf3_mapped_host_table(T):
+@pytest.mark.parametrize("wl,T", [("410m-nf3", 1), ("410m-nf3", 256), ("410m-nf3", 1024), ("410m-nf3", 4096),
+                                  ("160m", 64), ("160m", 1500)])
+def test_combine_nf3_mapped_host_table(wl, T):
     """Table in page-locked host memory read in place by the kernel (one
     launch, no staging).  Every launch shape of the NF3 combine (one token on
-    one or several wavefronts, four and eight tokens per workgroup) reads the
-    host rows; the codes sit at an offset inside their pinned allocation.
+    one or several wavefronts, four and eight tokens per workgroup; the
+    160M-class table's N = 4, D = 768) reads the host rows; the codes sit at
+    an offset inside their pinned allocation.
     Equal bit for bit to the device-resident combine, and to the oracle
     within the combine bar; twice in a row."""
-    w = synth.WORKLOADS["410m-nf3"]
+    w = synth.WORKLOADS[wl]
     V, N, D = w.V, w.N, w.D
     ids = synth.make_ids(w, T, step=5)
     table = rand_table(93, V, N, D, "bf16", std=0.02, rows=np.unique(ids))
