@@ -655,6 +655,49 @@ def test_graph_replay_of_layer_stack_matches_eager_and_oracle():
         torch.cuda.synchronize()
 
 
+def test_graph_replay_of_mapped_nf3_combines():
+    """Two layers whose NF3 tables sit in page-locked host memory, read in
+    place, captured as one HIP graph (the pointer checks run at capture
+    time; the graph holds only the kernels).  Every replay -- with eager
+    work in between -- reproduces the eager outputs bit for bit, and those
+    equal the device-resident combine."""
+    V, N, D, T, L = 400, 16, 1024, 1100, 2
+    ids = rng(93).integers(0, V, T).astype(np.int64)
+    layers = []
+    for l in range(L):
+        codes, scales, _ = oracle.pack_nf3(rand_table(960 + l, V, N, D, "bf16"))
+        h, w_r = rand_hw(970 + l, T, N, D, "bf16", wstd=0.3)
+        layers.append((codes, scales, h, w_r, torch.from_numpy(codes).pin_memory(),
+                       torch.from_numpy(scales.view(np.int16)).pin_memory(), dev(h), dev(w_r)))
+    d_ids = dev(ids)
+    ys = [torch.empty((T, D), dtype=torch.float32, device="cuda") for _ in range(L)]
+
+    def stack(st):
+        for l in range(L):
+            _, _, _, _, ch, sh, dh, dw = layers[l]
+            mole.mole_lookup_combine_nf3_mapped(d_ids, dh, dw, ch, sh, ys[l], stream=st)
+
+    stack(None)
+    torch.cuda.synchronize()
+    eager = [host(y) for y in ys]
+    for l in range(L):
+        codes, scales, h, w_r = layers[l][:4]
+        np.testing.assert_array_equal(eager[l], run_nf3(ids, h, w_r, codes, scales))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stack(torch.cuda.current_stream())
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            np.testing.assert_array_equal(host(ys[l]), eager[l])
+        stack(None)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # ----------------------------------------------------------------------------
 # The MoLE block: residual + shared expert FFN + routed lookup (training
 # section: shared experts read the contextual hidden state; complexity
