@@ -399,7 +399,7 @@ def layer410_probe(torch, mole, synth, dev, stream, to_dev):
     combine (index + combine, both launches timed), the NF3, NF4 and int8
     combines from HBM and the NF3 combine from pinned host memory (host
     dedupe and gather, one PCIe copy of the distinct rows, combine) and read in
-    place by the kernel from page-locked host memory.  50
+    place by the kernel from page-locked host memory, as is the bf16 table.  50
     launches cycling 8 id batches per point; a 1 GiB device copy in the same
     run gives the measured HBM roofline, a 256 MiB pinned copy the PCIe one."""
     w = synth.WORKLOADS["410m"]
@@ -447,6 +447,7 @@ def layer410_probe(torch, mole, synth, dev, stream, to_dev):
     torch.cuda.synchronize()
     codes_h.copy_(codes.cpu())
     scales_h.copy_(scales.cpu())
+    lut_h = lut.cpu().pin_memory()  # the bf16 table in page-locked host memory (1.65 GB)
     g = torch.Generator(device=dev)
     g.manual_seed(synth.seed(w, 60))
     nf3_row = N * (CB + 2 * SB)
@@ -489,14 +490,19 @@ def layer410_probe(torch, mole, synth, dev, stream, to_dev):
             res["nf3_host"] = {"us": us, "tokens_per_s": T / (us * 1e-6), "pcie_bytes": pcie,
                                "pcie_gbs_effective": pcie / (us * 1e-6) / 1e9,
                                "wall_s": time.perf_counter() - t0}
-            # the same table read in place by the kernel (every token reads its own rows over PCIe)
+            # the same tables read in place by the kernel (every token reads its own rows over PCIe)
             us = time_launches(torch, stream, lambda i: mole.mole_lookup_combine_nf3_mapped(
                 ids_l[i % 8], h_l[i % 8], w_r, codes_h, scales_h, y, stream=stream), 20)
             res["nf3_mapped"] = {"us": us, "tokens_per_s": T / (us * 1e-6), "pcie_bytes_requested": T * nf3_row,
                                  "pcie_gbs_effective": T * nf3_row / (us * 1e-6) / 1e9}
+            us = time_launches(torch, stream, lambda i: mole.mole_lookup_combine_mapped(
+                ids_l[i % 8], h_l[i % 8], w_r, lut_h, y, stream=stream), 10, warm=2)
+            res["bf16_mapped"] = {"us": us, "tokens_per_s": T / (us * 1e-6),
+                                  "pcie_bytes_requested": T * N * D * 2,
+                                  "pcie_gbs_effective": T * N * D * 2 / (us * 1e-6) / 1e9}
             out["T%d_%s" % (T, kind)] = res
             del h_l, y, gws, st_h, st_d
-    del lut, codes, scales, codes4, scales4, codes8, scales8, codes_h, scales_h
+    del lut, codes, scales, codes4, scales4, codes8, scales8, codes_h, scales_h, lut_h
     torch.cuda.empty_cache()
     return out
 
@@ -505,7 +511,7 @@ def layer160_probe(torch, mole, synth, dev, stream, to_dev):
     """The 160M-class layer (V=50304 D=768 N=4 F=3072): the build timed on
     its own, the NF3 pack, and the bf16 and NF3 combines at its decode
     batches T = 1, 8, 64, 256 (Zipf ids; 50 launches cycling 8 batches),
-    the NF3 one also with its table in page-locked host memory read in place.
+    both also with their tables in page-locked host memory read in place.
     Every launch here moves under 3 MB: latency-bound."""
     w = synth.WORKLOADS["160m"]
     V, D, N, F = w.V, w.D, w.N, w.F
@@ -526,6 +532,7 @@ def layer160_probe(torch, mole, synth, dev, stream, to_dev):
     torch.cuda.synchronize()
     codes_h = codes.cpu().pin_memory()
     scales_h = scales.cpu().pin_memory()
+    lut_h = lut.cpu().pin_memory()
     nf3_row = N * (CB + 2 * SB)
     for T in w.tokens:
         ids_l = [to_dev(synth.make_ids(w, T, step=s)) for s in range(8)]
@@ -533,14 +540,18 @@ def layer160_probe(torch, mole, synth, dev, stream, to_dev):
         y = torch.empty((T, D), dtype=torch.float32, device=dev)
         us_m = time_launches(torch, stream, lambda i: mole.mole_lookup_combine_nf3_mapped(
             ids_l[i % 8], h_l[i % 8], w_r, codes_h, scales_h, y, stream=stream), 50)
+        us_b = time_launches(torch, stream, lambda i: mole.mole_lookup_combine_mapped(
+            ids_l[i % 8], h_l[i % 8], w_r, lut_h, y, stream=stream), 50)
         out["T%d" % T] = {
             "bf16": combine_entry(T, time_launches(torch, stream, lambda i: mole.mole_lookup_combine(
                 ids_l[i % 8], h_l[i % 8], w_r, lut, y, stream=stream), 50), N * D * 2, D, N),
             "nf3": combine_entry(T, time_launches(torch, stream, lambda i: mole.mole_lookup_combine_nf3(
                 ids_l[i % 8], h_l[i % 8], w_r, codes, scales, y, stream=stream), 50), nf3_row, D, N),
             "nf3_mapped": {"us": us_m, "tokens_per_s": T / (us_m * 1e-6), "pcie_bytes_requested": T * nf3_row,
-                           "pcie_gbs_effective": T * nf3_row / (us_m * 1e-6) / 1e9}}
-    del lut, codes, scales, codes_h, scales_h
+                           "pcie_gbs_effective": T * nf3_row / (us_m * 1e-6) / 1e9},
+            "bf16_mapped": {"us": us_b, "tokens_per_s": T / (us_b * 1e-6), "pcie_bytes_requested": T * N * D * 2,
+                            "pcie_gbs_effective": T * N * D * 2 / (us_b * 1e-6) / 1e9}}
+    del lut, codes, scales, codes_h, scales_h, lut_h
     torch.cuda.empty_cache()
     return out
 

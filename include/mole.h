@@ -405,6 +405,16 @@ int mole_lookup_combine_nf3_mapped(const int64_t* ids, const void* h, const void
                                    const uint8_t* codes_host, const uint16_t* scales_host, float* y,
                                    int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h, void* stream);
 
+/* mole_lookup_combine_mapped: the same for the uncompressed table: the
+ * combine of mole_lookup_combine with lut_host [V][N][D] (dtype, as h and
+ * w_r) left in page-locked host memory allocated through HIP.  Each token
+ * reads its N x D slab over PCIe (2 N D bytes in bf16: 64 KB per token at
+ * N = 16, D = 2048).  Same checks, errors and graph behaviour as
+ * mole_lookup_combine_nf3_mapped. */
+int mole_lookup_combine_mapped(const int64_t* ids, const void* h, const void* w_r, const void* lut_host,
+                               float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
+                               void* stream);
+
 /* ------------------------------------------------------------------------
  * Host-resident NF3 tables of a stack of L layers, prefetched at the start
  * of a decode step (inference section: the table lives in lower-tier

@@ -69,6 +69,7 @@ def library():
             "mole_pack_nf3": (I, [P, P, P, I64, I64, I64, I, P]),
             "mole_lookup_combine_nf3": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_lookup_combine_nf3_mapped": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P]),
+            "mole_lookup_combine_mapped": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_gather_nf3_host": (I, [P, I64, P, P, I64, I64, I64, P, P, P, P, I]),
             "mole_nf3_host_staging_size": (I, [I64, I64, I64, P]),
             "mole_nf3_host_stack_staging_size": (I, [I64, I64, I64, I64, P]),
@@ -219,6 +220,22 @@ def mole_lookup_combine_nf3(ids, h, w_r, codes, scales, y, stream=None) -> None:
     _check("mole_lookup_combine_nf3", library().mole_lookup_combine_nf3(
         _ptr(ids), _ptr(h), _ptr(w_r), _ptr(codes), _ptr(scales), _ptr(y), T, V, D, N,
         _dtype(h), _stream(stream)))
+
+
+def mole_lookup_combine_mapped(ids, h, w_r, lut_host, y, stream=None) -> None:
+    """Lookup-combine reading the table in place from page-locked host memory
+    (lut_host: a pinned CPU tensor [V,N,D] of h's dtype); ids, h, w_r, y on the device."""
+    V, N, D = lut_host.shape
+    T = ids.numel()
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "ids [T], h [T,D], w_r [N,D], y [T,D]")
+    _need(ids.dtype == torch.int64 and y.dtype == torch.float32 and h.dtype == w_r.dtype == lut_host.dtype,
+          "ids int64, y float32, h, w_r and lut_host one dtype")
+    _need(not lut_host.is_cuda, "lut_host in host memory")
+    for t in (ids, h, w_r, lut_host, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    _check("mole_lookup_combine_mapped", library().mole_lookup_combine_mapped(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut_host), _ptr(y), T, V, D, N, _dtype(h), _stream(stream)))
 
 
 def mole_lookup_combine_nf3_mapped(ids, h, w_r, codes_host, scales_host, y, stream=None) -> None:

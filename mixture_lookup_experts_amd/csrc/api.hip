@@ -342,7 +342,7 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 9; }
+int mole_abi_version(void) { return 10; }
 
 int mole_release_host_state(void) {
   return guarded([&] {
@@ -519,6 +519,21 @@ int mole_lookup_combine_nf3_mapped(const int64_t* ids, const void* h, const void
   return hip_status(mole::launch_lookup_combine_nf3(ids, h, w_r, reinterpret_cast<const uint8_t*>(codes_d),
                                                     reinterpret_cast<const uint16_t*>(scales_d), y, T, D, N, dtype_h,
                                                     as_stream(stream)));
+}
+
+int mole_lookup_combine_mapped(const int64_t* ids, const void* h, const void* w_r, const void* lut_host, float* y,
+                               int64_t T, int64_t V, int64_t D, int64_t N, int dtype, void* stream) {
+  if (!dtype_ok(dtype)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (T == 0) return MOLE_OK;
+  if (!ids || !h || !w_r || !lut_host || !y) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(lut_host) || !aligned16(y))
+    return MOLE_ERR_ALIGN;
+  const size_t esz = dtype == MOLE_F32 ? 4 : 2;
+  const char* lut_d = mapped_host_range(lut_host, (size_t)(V * N * D) * esz);
+  if (!lut_d) return MOLE_ERR_MEMORY;
+  return hip_status(mole::launch_lookup_combine(ids, h, w_r, lut_d, y, T, D, N, dtype, true, as_stream(stream)));
 }
 
 int mole_pack_nf4(const void* lut, uint8_t* codes, uint16_t* scales, int64_t V, int64_t N, int64_t D,

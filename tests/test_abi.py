@@ -42,14 +42,14 @@ def test_header_declares_the_hot_path():
                "mole_gather_nf3_file", "mole_lookup_combine_nf3_file", "mole_lookup_combine_grouped",
                "mole_lookup_combine_grouped_workspace_size", "mole_check_ids", "mole_release_host_state",
                "mole_nf3_midpoints", "mole_nf4_midpoints", "mole_gelu_phi_coefficients",
-               "mole_lookup_combine_nf3_mapped"):
+               "mole_lookup_combine_nf3_mapped", "mole_lookup_combine_mapped"):
         assert fn in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 9
+    assert lib.mole_abi_version() == 10
 
 
 def test_status_strings(lib):
@@ -227,6 +227,13 @@ def test_mapped_nf3_argument_errors(lib):
     assert g(P(a), P(a), P(a), P(a + 8), P(a), P(a), 4, 10, 128, 4, 1, None) == ALIGN
     assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, 10, 128, 65, 1, None) == UNSUP
     assert g(None, None, None, None, None, None, 0, 10, 128, 4, 1, None) == OK  # empty batch: no-op
+    f = lib.mole_lookup_combine_mapped
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, 64, 4, 2, None) == DTYPE
+    assert f(P(a), P(a), P(a), None, P(a), 4, 10, 64, 4, 1, None) == NULL
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, 0, 64, 4, 1, None) == DIM
+    assert f(P(a), P(a), P(a), P(a + 8), P(a), 4, 10, 64, 4, 1, None) == ALIGN
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, 64, 65, 1, None) == UNSUP
+    assert f(None, None, None, None, None, 0, 10, 64, 4, 1, None) == OK
 
 
 def test_host_staging_size_and_errors(lib):

@@ -430,6 +430,34 @@ def test_combine_nf3_mapped_host_table(wl, T):
         assert combine_rel_err(y_host, ref) <= COMBINE_TOL
 
 
+@pytest.mark.parametrize("V,N,D,T,dtype", [(3000, 16, 2048, 1, "bf16"), (3000, 16, 2048, 128, "bf16"),
+                                           (3000, 16, 2048, 1030, "bf16"), (2000, 16, 1024, 4100, "bf16"),
+                                           (2000, 8, 512, 2100, "bf16"), (300, 4, 96, 70, "f32")])
+def test_combine_mapped_host_table(V, N, D, T, dtype):
+    """The uncompressed table in page-locked host memory, read in place
+    (one token per workgroup, the four-token wide blocks at two widths, the
+    staged router's two launches at 64 lanes per token, fp32): bit for bit
+    the device-resident combine, and within the oracle's bar."""
+    seed = 4000 + V + N + D + T
+    table = rand_table(seed, V, N, D, dtype)
+    h, w_r = rand_hw(seed + 1, T, N, D, dtype, wstd=0.3)
+    ids = rng(seed + 2).integers(0, V, T).astype(np.int64)
+    ref_dev = run_combine(ids, h, w_r, table)
+    lut_h = dev(table).cpu().pin_memory()
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        y.fill_(float("nan"))
+        mole.mole_lookup_combine_mapped(dev(ids), dev(h), dev(w_r), lut_h, y)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), ref_dev)
+    assert combine_rel_err(host(y), oracle.lookup_combine(ids, h, w_r, table)) <= COMBINE_TOL
+    pageable = lut_h.clone()
+    assert not pageable.is_pinned()
+    with pytest.raises(mole.MoleError) as e:  # the same table in pageable memory is refused
+        mole.mole_lookup_combine_mapped(dev(ids), dev(h), dev(w_r), pageable, y)
+    assert e.value.status == -12
+
+
 def test_combine_nf3_mapped_refuses_unmapped_tables():
     """Pageable host memory and device memory are refused on the host before
     anything is enqueued (a kernel reading pageable memory would fault)."""
