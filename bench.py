@@ -52,9 +52,10 @@ def parse():
                    help="token-id law of the headline step (a distinct-id control is always measured)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="budget for the CPU-oracle baseline (0 disables it)")
-    p.add_argument("--probes", default="sweep,410m,160m,host,disk,layer,train",
+    p.add_argument("--probes", default="sweep,host1b,410m,160m,host,disk,layer,train",
                    help="comma list of the measurements after the headline (or 'none'): sweep (1B-class "
-                        "decode batches), 410m (build, NF3 pack, quantised, host-resident and grouped "
+                        "decode batches), host1b (the same with 1B-class NF3 tables in page-locked host "
+                        "memory, read in place), 410m (build, NF3 pack, quantised, host-resident and grouped "
                         "combines), 160m (build and decode batches), host (16-layer host-resident NF3 stack), "
                         "disk (NF3 table file), layer (the MoLE block), train (training forward and backward); "
                         "opt-in: vendor_gemm (the vendor GEMM library on the build's shapes)")
@@ -248,6 +249,8 @@ def main():
 
     if "sweep" in probes:
         result["decode_sweep_1b"] = decode_sweep(torch, mole, synth, w, luts, w_rs, dev, stream, to_dev)
+    if "host1b" in probes:
+        result["decode_sweep_1b_nf3_host"] = host_decode_sweep(torch, mole, synth, w, w_rs, dev, stream, to_dev)
     del luts, w_rs, stack
     torch.cuda.empty_cache()
     if "410m" in probes:
@@ -358,6 +361,54 @@ def decode_sweep(torch, mole, synth, w, luts, w_rs, dev, stream, to_dev):
                           "hbm_frac": L * per_layer / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
                           "bytes_per_step": L * per_layer}
         del graphs, h_l, y_l
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_decode_sweep(torch, mole, synth, w, w_rs, dev, stream, to_dev):
+    """The same decode batches through a 16-layer stack of 1B-class NF3
+    tables (V=50304 N=16 D=2048: 0.67 GB each, 10.7 GB in all) left in
+    page-locked host memory and read in place by the combines
+    (mole_lookup_combine_nf3_mapped): one step = the L combines, eager and
+    as one HIP-graph replay.  The host tables hold zero codes and scales (the
+    combine's cost does not depend on their values)."""
+    V, D, N, L = w.V, w.D, w.N, len(w_rs)
+    CB, SB = 3 * D // 8, D // 64
+    codes_h = [torch.zeros((V, N, CB), dtype=torch.uint8, pin_memory=True) for _ in range(L)]
+    scales_h = [torch.zeros((V, N, SB), dtype=torch.int16, pin_memory=True) for _ in range(L)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.seed(w, 71))
+    out = {"workload": "16-layer stack of 1B-class NF3 tables (V=50304 N=16 D=2048) in page-locked host "
+                       "memory, %.1f GB, read in place" % (L * V * N * (CB + 2 * SB) / 1e9)}
+    row = N * (CB + 2 * SB)
+    for T in w.tokens:
+        NB = 4
+        ids_l = [to_dev(synth.make_ids(w, T, step=s)) for s in range(NB)]
+        h_l = [[torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(L)]
+               for _ in range(NB)]
+        y_l = [torch.empty((T, D), dtype=torch.float32, device=dev) for _ in range(L)]
+
+        def stack(b, st):
+            for l in range(L):
+                mole.mole_lookup_combine_nf3_mapped(ids_l[b % NB], h_l[b % NB][l], w_rs[l], codes_h[l],
+                                                    scales_h[l], y_l[l], stream=st)
+
+        eager_us = time_launches(torch, stream, lambda i: stack(i, stream), 20, warm=3)
+        with torch.cuda.stream(stream):
+            graphs = []
+            for b in range(NB):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    stack(b, torch.cuda.current_stream())
+                graphs.append(gr)
+        torch.cuda.synchronize()
+        graph_us = time_launches(torch, torch.cuda.current_stream(), lambda i: graphs[i % NB].replay(), 20, warm=NB)
+        best = min(eager_us, graph_us)
+        out["T%d" % T] = {"eager_us_per_step": eager_us, "graph_us_per_step": graph_us,
+                          "tokens_per_s": T / (best * 1e-6), "pcie_bytes_requested_per_step": L * T * row,
+                          "pcie_gbs_effective": L * T * row / (best * 1e-6) / 1e9}
+        del graphs, h_l, y_l
+    del codes_h, scales_h
     torch.cuda.empty_cache()
     return out
 
