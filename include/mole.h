@@ -497,6 +497,17 @@ int mole_lookup_combine_grouped(const int64_t* ids, const void* h, const void* w
                                 int64_t T, int64_t V, int64_t D, int64_t N, int dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* mole_lookup_combine_grouped_mapped: mole_lookup_combine_grouped with the
+ * table lut_host [V][N][D] (bf16) left in page-locked host memory allocated
+ * through HIP, read in place as in mole_lookup_combine_mapped (same checks
+ * and MOLE_ERR_MEMORY).  Each run of equal ids reads its slab over PCIe
+ * once, so a batch with repeated ids moves about its distinct rows instead
+ * of one slab per token; ids, h, w_r, y and the workspace are device memory
+ * as for mole_lookup_combine_grouped. */
+int mole_lookup_combine_grouped_mapped(const int64_t* ids, const void* h, const void* w_r, const void* lut_host,
+                                       float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * mole_lookup_combine_grouped_noalloc: mole_lookup_combine_grouped for
  * callers that cannot allocate device memory (code under HIP graph capture,

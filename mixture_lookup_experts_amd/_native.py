@@ -93,6 +93,7 @@ def library():
             "mole_check_ids": (I, [P, I64, I64, P, P]),
             "mole_lookup_combine_grouped": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
             "mole_lookup_combine_grouped_noalloc": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P]),
+            "mole_lookup_combine_grouped_mapped": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
             "mole_nf3_file_write": (I, [ctypes.c_char_p, P, P, I64, I64, I64]),
             "mole_nf3_file_shape": (I, [I, P, P, P]),
             "mole_gather_nf3_file": (I, [I, P, I64, I64, I64, I64, P, P, P, P, I]),
@@ -384,6 +385,25 @@ def mole_lookup_combine_grouped(ids, h, w_r, lut, y, workspace, stream=None) -> 
     _check("mole_lookup_combine_grouped", library().mole_lookup_combine_grouped(
         _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut), _ptr(y), T, V, D, N, _dtype(lut), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def mole_lookup_combine_grouped_mapped(ids, h, w_r, lut_host, y, workspace, stream=None) -> None:
+    """The grouped combine reading the table in place from page-locked host
+    memory (lut_host: a pinned bf16 CPU tensor [V,N,D]); the rest on the device."""
+    V, N, D = lut_host.shape
+    T = ids.numel()
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "h [T,D], w_r [N,D], y [T,D]")
+    _need(ids.dtype == torch.int64, "ids int64")
+    _need(h.dtype == lut_host.dtype == w_r.dtype and y.dtype == torch.float32,
+          "h, w_r, lut_host share one dtype; y float32")
+    _need(not lut_host.is_cuda, "lut_host in host memory")
+    for t in (ids, h, w_r, lut_host, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mole_lookup_combine_grouped_mapped", library().mole_lookup_combine_grouped_mapped(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut_host), _ptr(y), T, V, D, N, _dtype(h), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def mole_lookup_combine_grouped_noalloc(ids, h, w_r, lut, y, stream=None) -> None:

@@ -342,7 +342,7 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 10; }
+int mole_abi_version(void) { return 11; }
 
 int mole_release_host_state(void) {
   return guarded([&] {
@@ -670,6 +670,21 @@ int mole_lookup_combine_grouped(const int64_t* ids, const void* h, const void* w
   return hip_status(mole::launch_lookup_combine_grouped(ids, (const uint16_t*)h, (const uint16_t*)w_r,
                                                         (const uint16_t*)lut, y, T, (int)D, (int)N, workspace,
                                                         as_stream(stream)));
+}
+
+int mole_lookup_combine_grouped_mapped(const int64_t* ids, const void* h, const void* w_r, const void* lut_host,
+                                       float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_grouped(ids, h, w_r, lut_host, y, T, V, D, N, dtype);
+  if (rc != MOLE_OK || T == 0) return rc;
+  if (!workspace) return MOLE_ERR_NULL;
+  if (!aligned16(workspace)) return MOLE_ERR_ALIGN;
+  if (workspace_bytes < mole::grouped_workspace_bytes(T)) return MOLE_ERR_WORKSPACE;
+  const char* lut_d = mapped_host_range(lut_host, (size_t)(V * N * D) * 2);
+  if (!lut_d) return MOLE_ERR_MEMORY;
+  return hip_status(mole::launch_lookup_combine_grouped(ids, (const uint16_t*)h, (const uint16_t*)w_r,
+                                                        reinterpret_cast<const uint16_t*>(lut_d), y, T, (int)D,
+                                                        (int)N, workspace, as_stream(stream)));
 }
 
 int mole_lookup_combine_grouped_noalloc(const int64_t* ids, const void* h, const void* w_r, const void* lut,

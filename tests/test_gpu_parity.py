@@ -458,6 +458,30 @@ def test_combine_mapped_host_table(V, N, D, T, dtype):
     assert e.value.status == -12
 
 
+@pytest.mark.parametrize("V,N,D,T,law", [(3000, 16, 1024, 4096, "zipf"), (600, 16, 2048, 1030, "zipf"),
+                                         (300, 4, 768, 300, "uniform"), (20, 8, 64, 5000, "one")])
+def test_grouped_combine_mapped_host_table(V, N, D, T, law):
+    """The grouped combine with its bf16 table in page-locked host memory,
+    read in place: bit for bit the device-resident grouped combine (each
+    token's sum runs over its own gates and slab in a fixed order), and
+    within the oracle's bar."""
+    seed = 5000 + V + N + D + T
+    lut = rand_table(seed, V, N, D, "bf16")
+    h, w_r = rand_hw(seed + 1, T, N, D, "bf16", wstd=0.3)
+    ids = grouped_ids(rng(seed + 2), V, T, law)
+    ref_dev = run_grouped(ids, h, w_r, lut)
+    lut_h = dev(lut).cpu().pin_memory()
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    ws = torch.full((max(mole.mole_lookup_combine_grouped_workspace_size(T), 16),), 0xAB, dtype=torch.uint8,
+                    device="cuda")
+    for _ in range(2):
+        y.fill_(float("nan"))
+        mole.mole_lookup_combine_grouped_mapped(dev(ids), dev(h), dev(w_r), lut_h, y, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), ref_dev)
+    assert combine_rel_err(host(y), oracle.lookup_combine(ids, h, w_r, lut)) <= COMBINE_TOL
+
+
 def test_combine_nf3_mapped_refuses_unmapped_tables():
     """Pageable host memory and device memory are refused on the host before
     anything is enqueued (a kernel reading pageable memory would fault)."""
