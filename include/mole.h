@@ -31,11 +31,12 @@
  *    the check.
  *  - Entry points may be called from several threads; calls that write the
  *    same buffers must be ordered by the caller.  Device-side entry points
- *    keep no state between calls.  The host-side paths (host-resident and
- *    file-backed tables) keep two pieces of process-wide state, created on
- *    first use: a pool of up to 64 gather threads, and one HIP event per
- *    distinct pinned staging area (the event that orders reuse of that
- *    area).  mole_release_host_state() frees both.
+ *    keep no state between calls.  The staged host-side paths (host-resident
+ *    and file-backed tables copied through a staging area) keep two pieces
+ *    of process-wide state, created on first use: a pool of up to 64 gather
+ *    threads, and one HIP event per distinct pinned staging area (the event
+ *    that orders reuse of that area).  mole_release_host_state() frees both.
+ *    The read-in-place (_mapped) entry points keep none.
  */
 #ifndef MOLE_H
 #define MOLE_H
