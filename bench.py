@@ -551,6 +551,11 @@ def layer410_probe(torch, mole, synth, dev, stream, to_dev):
             res["bf16_mapped"] = {"us": us, "tokens_per_s": T / (us * 1e-6),
                                   "pcie_bytes_requested": T * N * D * 2,
                                   "pcie_gbs_effective": T * N * D * 2 / (us * 1e-6) / 1e9}
+            us = time_launches(torch, stream, lambda i: mole.mole_lookup_combine_nf3_grouped_mapped(
+                ids_l[i % 8], h_l[i % 8], w_r, codes_h, scales_h, y, gws, stream=stream), 20)
+            res["nf3_grouped_mapped"] = {"us": us, "tokens_per_s": T / (us * 1e-6),
+                                         "pcie_bytes_distinct_rows": U * nf3_row,
+                                         "pcie_gbs_effective_distinct": U * nf3_row / (us * 1e-6) / 1e9}
             # grouped by id on the device: each run of equal ids reads its slab over PCIe once
             us = time_launches(torch, stream, lambda i: mole.mole_lookup_combine_grouped_mapped(
                 ids_l[i % 8], h_l[i % 8], w_r, lut_h, y, gws, stream=stream), 10, warm=2)

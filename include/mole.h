@@ -509,6 +509,28 @@ int mole_lookup_combine_grouped_mapped(const int64_t* ids, const void* h, const 
                                        float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype,
                                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* mole_lookup_combine_nf3_grouped: the NF3 combine of mole_lookup_combine_nf3
+ * over the batch grouped by id on the device (the grouping and routing
+ * launch of mole_lookup_combine_grouped, then the NF3 decode with each
+ * position's token, row and gates from the workspace): tokens that share an
+ * id run on neighbouring workgroups, so their rows are read from memory
+ * about once.  bf16 h and w_r, N <= 16, D % 64 == 0 (MOLE_ERR_UNSUPPORTED /
+ * MOLE_ERR_DIM otherwise); the workspace is device memory of at least
+ * mole_lookup_combine_grouped_workspace_size(T) bytes, 16-byte aligned, and
+ * needs no clearing.
+ * mole_lookup_combine_nf3_grouped_mapped: the same with codes_host and
+ * scales_host in page-locked host memory, read in place as in
+ * mole_lookup_combine_nf3_mapped (same checks and MOLE_ERR_MEMORY).  For a
+ * batch with repeated ids this moves about its distinct rows over PCIe. */
+int mole_lookup_combine_nf3_grouped(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
+                                    const uint16_t* scales, float* y, int64_t T, int64_t V, int64_t D, int64_t N,
+                                    int dtype_h, void* workspace, size_t workspace_bytes, void* stream);
+
+int mole_lookup_combine_nf3_grouped_mapped(const int64_t* ids, const void* h, const void* w_r,
+                                           const uint8_t* codes_host, const uint16_t* scales_host, float* y,
+                                           int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * mole_lookup_combine_grouped_noalloc: mole_lookup_combine_grouped for
  * callers that cannot allocate device memory (code under HIP graph capture,

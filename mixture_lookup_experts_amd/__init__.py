@@ -35,6 +35,8 @@ from ._native import (  # noqa: F401
     mole_lookup_combine_nf3_mapped,
     mole_lookup_combine_mapped,
     mole_lookup_combine_grouped_mapped,
+    mole_lookup_combine_nf3_grouped,
+    mole_lookup_combine_nf3_grouped_mapped,
     mole_nf3_host_staging_size,
     mole_nf3_host_stack_staging_size,
     mole_prefetch_nf3_host_stack,
@@ -59,6 +61,7 @@ __all__ = [
     "mole_build_lut", "mole_build_lut_workspace_size", "mole_lookup_combine", "mole_pack_nf3",
     "mole_lookup_combine_nf3", "mole_gather_nf3_host", "mole_lookup_combine_nf3_host",
     "mole_lookup_combine_nf3_mapped", "mole_lookup_combine_mapped", "mole_lookup_combine_grouped_mapped",
+    "mole_lookup_combine_nf3_grouped", "mole_lookup_combine_nf3_grouped_mapped",
     "mole_nf3_host_staging_size", "mole_nf3_host_stack_staging_size", "mole_prefetch_nf3_host_stack",
     "mole_nf3_levels", "mole_status_string", "mole_layer_forward", "mole_layer_workspace_size",
     "mole_nf4_levels", "mole_pack_nf4", "mole_lookup_combine_nf4", "mole_pack_int8", "mole_lookup_combine_int8",

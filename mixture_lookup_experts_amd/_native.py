@@ -94,6 +94,8 @@ def library():
             "mole_lookup_combine_grouped": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
             "mole_lookup_combine_grouped_noalloc": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P]),
             "mole_lookup_combine_grouped_mapped": (I, [P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
+            "mole_lookup_combine_nf3_grouped": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
+            "mole_lookup_combine_nf3_grouped_mapped": (I, [P, P, P, P, P, P, I64, I64, I64, I64, I, P, SZ, P]),
             "mole_nf3_file_write": (I, [ctypes.c_char_p, P, P, I64, I64, I64]),
             "mole_nf3_file_shape": (I, [I, P, P, P]),
             "mole_gather_nf3_file": (I, [I, P, I64, I64, I64, I64, P, P, P, P, I]),
@@ -404,6 +406,36 @@ def mole_lookup_combine_grouped_mapped(ids, h, w_r, lut_host, y, workspace, stre
     _check("mole_lookup_combine_grouped_mapped", library().mole_lookup_combine_grouped_mapped(
         _ptr(ids), _ptr(h), _ptr(w_r), _ptr(lut_host), _ptr(y), T, V, D, N, _dtype(h), _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+def _nf3_grouped(fn, ids, h, w_r, codes, scales, y, workspace, stream):
+    V, N, CB = codes.shape
+    D = CB * 8 // 3
+    T = ids.numel()
+    _need(tuple(scales.shape) == (V, N, D // 64), "scales [V,N,D/64]")
+    _need(tuple(h.shape) == (T, D) and tuple(w_r.shape) == (N, D) and tuple(y.shape) == (T, D),
+          "ids [T], h [T,D], w_r [N,D], y [T,D]")
+    _need(ids.dtype == torch.int64 and y.dtype == torch.float32 and h.dtype == w_r.dtype,
+          "ids int64, y float32, h and w_r one dtype")
+    for t in (ids, h, w_r, codes, scales, y):
+        _need(t.is_contiguous(), "tensors must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn, getattr(library(), fn)(
+        _ptr(ids), _ptr(h), _ptr(w_r), _ptr(codes), _ptr(scales), _ptr(y), T, V, D, N, _dtype(h), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+
+
+def mole_lookup_combine_nf3_grouped(ids, h, w_r, codes, scales, y, workspace, stream=None) -> None:
+    """NF3 combine over the batch grouped by id on the device (workspace:
+    mole_lookup_combine_grouped_workspace_size(T) bytes on the device)."""
+    _nf3_grouped("mole_lookup_combine_nf3_grouped", ids, h, w_r, codes, scales, y, workspace, stream)
+
+
+def mole_lookup_combine_nf3_grouped_mapped(ids, h, w_r, codes_host, scales_host, y, workspace, stream=None) -> None:
+    """The same with the NF3 table in page-locked host memory, read in place."""
+    _need(not codes_host.is_cuda and not scales_host.is_cuda, "codes_host and scales_host in host memory")
+    _nf3_grouped("mole_lookup_combine_nf3_grouped_mapped", ids, h, w_r, codes_host, scales_host, y, workspace,
+                 stream)
 
 
 def mole_lookup_combine_grouped_noalloc(ids, h, w_r, lut, y, stream=None) -> None:

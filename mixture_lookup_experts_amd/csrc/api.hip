@@ -342,7 +342,7 @@ const char* mole_status_string(int status) {
 
 int mole_last_hip_error(void) { return g_last_hip_error; }
 
-int mole_abi_version(void) { return 11; }
+int mole_abi_version(void) { return 12; }
 
 int mole_release_host_state(void) {
   return guarded([&] {
@@ -685,6 +685,60 @@ int mole_lookup_combine_grouped_mapped(const int64_t* ids, const void* h, const 
   return hip_status(mole::launch_lookup_combine_grouped(ids, (const uint16_t*)h, (const uint16_t*)w_r,
                                                         reinterpret_cast<const uint16_t*>(lut_d), y, T, (int)D,
                                                         (int)N, workspace, as_stream(stream)));
+}
+
+namespace {
+// The NF3 combine over the batch grouped by id (codes and scales at device
+// addresses: device memory, or a page-locked host table's mapping).
+int nf3_grouped(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes, const uint16_t* scales,
+                float* y, int64_t T, int64_t D, int64_t N, void* workspace, hipStream_t s) {
+  const int* pos_tok;
+  const int* pos_row;
+  const float* gates;
+  hipError_t err = mole::launch_group_route(ids, (const uint16_t*)h, (const uint16_t*)w_r, T, (int)D, (int)N,
+                                            workspace, s, &pos_tok, &pos_row, &gates);
+  if (err != hipSuccess) return hip_status(err);
+  return hip_status(mole::launch_lookup_combine_nf3_grouped(pos_tok, pos_row, gates, codes, scales, y, T, D, N, s));
+}
+
+int check_nf3_grouped(const int64_t* ids, const void* h, const void* w_r, const void* codes, const void* scales,
+                      float* y, int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h, void* workspace,
+                      size_t workspace_bytes) {
+  if (!dtype_ok(dtype_h)) return MOLE_ERR_DTYPE;
+  int rc = check_combine_common(T, V, D, N);
+  if (rc != MOLE_OK) return rc;
+  if (D % 64 != 0) return MOLE_ERR_DIM;
+  if (dtype_h != MOLE_BF16 || N > 16 || V > INT32_MAX) return MOLE_ERR_UNSUPPORTED;
+  if (T == 0) return MOLE_OK;
+  if (!ids || !h || !w_r || !codes || !scales || !y || !workspace) return MOLE_ERR_NULL;
+  if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(codes) || !aligned16(scales) ||
+      !aligned16(y) || !aligned16(workspace))
+    return MOLE_ERR_ALIGN;
+  if (workspace_bytes < mole::grouped_workspace_bytes(T)) return MOLE_ERR_WORKSPACE;
+  return MOLE_OK;
+}
+}  // namespace
+
+int mole_lookup_combine_nf3_grouped(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
+                                    const uint16_t* scales, float* y, int64_t T, int64_t V, int64_t D, int64_t N,
+                                    int dtype_h, void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = check_nf3_grouped(ids, h, w_r, codes, scales, y, T, V, D, N, dtype_h, workspace, workspace_bytes);
+  if (rc != MOLE_OK || T == 0) return rc;
+  return nf3_grouped(ids, h, w_r, codes, scales, y, T, D, N, workspace, as_stream(stream));
+}
+
+int mole_lookup_combine_nf3_grouped_mapped(const int64_t* ids, const void* h, const void* w_r,
+                                           const uint8_t* codes_host, const uint16_t* scales_host, float* y,
+                                           int64_t T, int64_t V, int64_t D, int64_t N, int dtype_h,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc =
+      check_nf3_grouped(ids, h, w_r, codes_host, scales_host, y, T, V, D, N, dtype_h, workspace, workspace_bytes);
+  if (rc != MOLE_OK || T == 0) return rc;
+  const char* codes_d = mapped_host_range(codes_host, (size_t)(V * N * (3 * D / 8)));
+  const char* scales_d = mapped_host_range(scales_host, (size_t)(V * N * (D / 64)) * 2);
+  if (!codes_d || !scales_d) return MOLE_ERR_MEMORY;
+  return nf3_grouped(ids, h, w_r, reinterpret_cast<const uint8_t*>(codes_d),
+                     reinterpret_cast<const uint16_t*>(scales_d), y, T, D, N, workspace, as_stream(stream));
 }
 
 int mole_lookup_combine_grouped_noalloc(const int64_t* ids, const void* h, const void* w_r, const void* lut,

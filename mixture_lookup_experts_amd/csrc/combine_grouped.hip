@@ -232,18 +232,26 @@ constexpr GroupedWs grouped_ws(int64_t T) {
 constexpr size_t grouped_ws_total_max() { return grouped_ws(kGroupedNoAllocMaxT).total; }
 
 template <int NP>
-hipError_t launch_grouped_np(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, const uint16_t* lut,
-                             float* y, int64_t T, int D, int N, void* ws, hipStream_t s) {
+hipError_t group_route_np(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, int64_t T, int D, int N,
+                          void* ws, hipStream_t s, int** pos_tok, int** pos_row, float** gates) {
   const GroupedWs lay = grouped_ws(T);
   char* base = static_cast<char*>(ws);
-  int* pos_tok = reinterpret_cast<int*>(base + lay.tok_off);
-  int* pos_row = reinterpret_cast<int*>(base + lay.row_off);
-  float* gates = reinterpret_cast<float*>(base + lay.gate_off);
+  *pos_tok = reinterpret_cast<int*>(base + lay.tok_off);
+  *pos_row = reinterpret_cast<int*>(base + lay.row_off);
+  *gates = reinterpret_cast<float*>(base + lay.gate_off);
   const int nchunks = (int)((T + kGroupChunk - 1) / kGroupChunk);
   const int64_t rtiles = (T + kMaxTokPerBlock - 1) / kMaxTokPerBlock;
   hipLaunchKernelGGL((group_route_kernel<NP>), dim3((unsigned)(nchunks + rtiles)), dim3(kGroupThreads), 0, s, ids,
-                     h, w_r, T, D, N, nchunks, pos_tok, pos_row, gates);
-  hipError_t err = hipGetLastError();
+                     h, w_r, T, D, N, nchunks, *pos_tok, *pos_row, *gates);
+  return hipGetLastError();
+}
+
+template <int NP>
+hipError_t launch_grouped_np(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, const uint16_t* lut,
+                             float* y, int64_t T, int D, int N, void* ws, hipStream_t s) {
+  int *pos_tok, *pos_row;
+  float* gates;
+  hipError_t err = group_route_np<NP>(ids, h, w_r, T, D, N, ws, s, &pos_tok, &pos_row, &gates);
   if (err != hipSuccess) return err;
   // lanes per workgroup: the 16-byte chunks of a row, 64 to 256
   const int C = D / 8;
@@ -315,6 +323,26 @@ hipError_t launch_lookup_combine_grouped_noalloc(const int64_t* ids, const uint1
   const hipError_t err = scratch_address(s, &ws);
   if (err != hipSuccess) return err;
   return launch_lookup_combine_grouped(ids, h, w_r, lut, y, T, D, N, ws, s);
+}
+
+hipError_t launch_group_route(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, int64_t T, int D, int N,
+                              void* ws, hipStream_t s, const int** pos_tok, const int** pos_row,
+                              const float** gates) {
+  int *pt, *pr;
+  float* g;
+  const int NP = N <= 1 ? 1 : (N <= 2 ? 2 : (N <= 4 ? 4 : (N <= 8 ? 8 : 16)));
+  hipError_t err;
+  switch (NP) {
+    case 1: err = group_route_np<1>(ids, h, w_r, T, D, N, ws, s, &pt, &pr, &g); break;
+    case 2: err = group_route_np<2>(ids, h, w_r, T, D, N, ws, s, &pt, &pr, &g); break;
+    case 4: err = group_route_np<4>(ids, h, w_r, T, D, N, ws, s, &pt, &pr, &g); break;
+    case 8: err = group_route_np<8>(ids, h, w_r, T, D, N, ws, s, &pt, &pr, &g); break;
+    default: err = group_route_np<16>(ids, h, w_r, T, D, N, ws, s, &pt, &pr, &g); break;
+  }
+  *pos_tok = pt;
+  *pos_row = pr;
+  *gates = g;
+  return err;
 }
 
 hipError_t launch_lookup_combine_grouped(const int64_t* ids, const uint16_t* h, const uint16_t* w_r,

@@ -335,6 +335,148 @@ __global__ __launch_bounds__(BT) void lookup_combine_nf3_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// NF3 combine over a batch in grouped order (equal ids adjacent; see
+// combine_grouped.hip): position p holds token pos_tok[p], table row
+// pos_row[p], and the token's gates come precomputed in gates[token][NP].
+// One token per wavefront, four per workgroup, the per-token kernel's lane
+// layout, decode and staged stores.  Tokens that share an id run on
+// neighbouring workgroups of one pass, so their rows are fetched from memory
+// about once and then served from cache: this pays where every byte read is
+// expensive, as for a table read in place over PCIe.
+// ---------------------------------------------------------------------------
+template <int NP, int CP, int S>
+__global__ __launch_bounds__(256) void lookup_combine_nf3_grouped_kernel(
+    const int* __restrict__ pos_tok, const int* __restrict__ pos_row, const float* __restrict__ gates,
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, float* __restrict__ y, int64_t T_,
+    int D, int N) {
+  using Q = QFmt<kFmtNf3>;
+  static_assert(CP * S == kWave, "one token per wavefront");
+  constexpr int EPL = (NP + S - 1) / S;  // experts per lane
+  constexpr int EC = EPL < Q::kBatch ? EPL : Q::kBatch;
+  constexpr int OUT = 32 / S;
+  static_assert(OUT >= 4, "whole 16-byte pieces per lane");
+  __shared__ float2 lv2[64];
+  __shared__ float ys[4 * CP * 32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < 64; i += 256)
+    lv2[i] = make_float2(__uint_as_float(kNf3LevelBits[i & 7]), __uint_as_float(kNf3LevelBits[i >> 3]));
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * 4 + wave;
+  if (p >= T_) return;  // (wave-uniform; no barrier follows)
+  const int64_t tok = __builtin_amdgcn_readfirstlane(pos_tok[p]);
+  const int64_t id = __builtin_amdgcn_readfirstlane(pos_row[p]);
+  const int sp = lane / CP, ch = lane % CP;
+  const int C = D / 32, nblk = D / 64;
+  const int64_t row_bytes = Q::row_bytes(D);
+  const uint8_t* crow = codes + id * (int64_t)N * row_bytes;
+  const uint16_t* srow = scales + id * (int64_t)N * nblk;
+  float g[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = j * S + sp;
+    g[j] = e < N ? gates[tok * NP + e] : 0.f;
+  }
+  const int rounds = (C + CP - 1) / CP;
+  for (int k = 0; k < rounds; ++k) {
+    const int c = k * CP + ch;
+    const bool act = c < C;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j0 = 0; j0 < EPL; j0 += EC) {
+      uint32_t cw[EC][3], sc[EC];
+#pragma unroll
+      for (int j = 0; j < EC; ++j) {
+        const int e = (j0 + j) * S + sp;
+        if (act && e < N) {
+          const uint3 v = *reinterpret_cast<const uint3*>(crow + (int64_t)e * row_bytes + (int64_t)c * 12);
+          cw[j][0] = v.x; cw[j][1] = v.y; cw[j][2] = v.z;
+          sc[j] = srow[(int64_t)e * nblk + (c >> 1)];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < EC; ++j) {
+        const int e = (j0 + j) * S + sp;
+        if (act && e < N) {
+          const float ws = g[j0 + j] * (float)__builtin_bit_cast(_Float16, (uint16_t)sc[j]);
+          const uint32_t* w = cw[j];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int pos = 6 * q, wd = pos >> 5, off = pos & 31;
+            uint32_t pr;
+            if (off <= 26) pr = (w[wd] >> off) & 63u;
+            else pr = __builtin_amdgcn_alignbit(w[wd + 1], w[wd], off) & 63u;
+            const float2 l = lv2[pr];
+            acc[2 * q] = fmaf(ws, l.x, acc[2 * q]);
+            acc[2 * q + 1] = fmaf(ws, l.y, acc[2 * q + 1]);
+          }
+        }
+      }
+    }
+    SplitReduce<CP, S>::run(acc, sp);
+    float* yw = ys + wave * (CP * 32);
+#pragma unroll
+    for (int j = 0; j < OUT; j += 4)
+      *reinterpret_cast<float4*>(yw + ch * 32 + SplitReduce<CP, S>::offset(sp) + j) =
+          make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int q = 0; q < CP * 32 / 256; ++q) {
+      const int e = k * CP * 32 + 4 * lane + 256 * q;  // element of the token's row
+      const float4 v = *reinterpret_cast<const float4*>(yw + 4 * lane + 256 * q);
+      if (e < D) stg16_nt(y + tok * D + e, v.x, v.y, v.z, v.w);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the slice is rewritten next round
+  }
+}
+
+template <int NP, int CP>
+static hipError_t launch_nf3_grouped(const int* pos_tok, const int* pos_row, const float* gates, const uint8_t* codes,
+                                     const uint16_t* scales, float* y, int64_t T, int D, int N, hipStream_t s) {
+  constexpr int S = 64 / CP;
+  const int64_t blocks = (T + 3) / 4;
+  hipLaunchKernelGGL((lookup_combine_nf3_grouped_kernel<NP, CP, S>), dim3((unsigned)blocks), dim3(256), 0, s, pos_tok,
+                     pos_row, gates, codes, scales, y, T, D, N);
+  return hipGetLastError();
+}
+
+template <int NP>
+static hipError_t dispatch_nf3_grouped_cp(int CP, const int* pos_tok, const int* pos_row, const float* gates,
+                                          const uint8_t* codes, const uint16_t* scales, float* y, int64_t T, int D,
+                                          int N, hipStream_t s) {
+  // (64 / CP expert splits per token: at most NP, so that every split has an expert)
+  if constexpr (NP >= 8)
+    if (CP == 8) return launch_nf3_grouped<NP, 8>(pos_tok, pos_row, gates, codes, scales, y, T, D, N, s);
+  if constexpr (NP >= 4)
+    if (CP == 16) return launch_nf3_grouped<NP, 16>(pos_tok, pos_row, gates, codes, scales, y, T, D, N, s);
+  if constexpr (NP >= 2)
+    if (CP == 32) return launch_nf3_grouped<NP, 32>(pos_tok, pos_row, gates, codes, scales, y, T, D, N, s);
+  if (CP == 64) return launch_nf3_grouped<NP, 64>(pos_tok, pos_row, gates, codes, scales, y, T, D, N, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_lookup_combine_nf3_grouped(const int* pos_tok, const int* pos_row, const float* gates,
+                                             const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                             int64_t D, int64_t N, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int NP = next_pow2((int)N);
+  // lanes per expert split: the chunks of a row, at least 64 / NP so that a
+  // token fills its wavefront with every split holding an expert
+  int CP = pick_group((int)(D / 32), 8, 64);
+  while (CP * NP < 64) CP *= 2;
+  switch (NP) {
+    case 1: return dispatch_nf3_grouped_cp<1>(CP, pos_tok, pos_row, gates, codes, scales, y, T, (int)D, (int)N, s);
+    case 2: return dispatch_nf3_grouped_cp<2>(CP, pos_tok, pos_row, gates, codes, scales, y, T, (int)D, (int)N, s);
+    case 4: return dispatch_nf3_grouped_cp<4>(CP, pos_tok, pos_row, gates, codes, scales, y, T, (int)D, (int)N, s);
+    case 8: return dispatch_nf3_grouped_cp<8>(CP, pos_tok, pos_row, gates, codes, scales, y, T, (int)D, (int)N, s);
+    case 16: return dispatch_nf3_grouped_cp<16>(CP, pos_tok, pos_row, gates, codes, scales, y, T, (int)D, (int)N, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
 // Tokens (wavefronts) per workgroup of the wide launch: 8 from T = 4096 on

@@ -46,6 +46,17 @@ size_t grouped_workspace_bytes(int64_t T);
 hipError_t launch_lookup_combine_grouped(const int64_t* ids, const uint16_t* h, const uint16_t* w_r,
                                          const uint16_t* lut, float* y, int64_t T, int D, int N, void* ws,
                                          hipStream_t s);
+// The grouping-and-routing launch alone: positions in id order (pos_tok[p]
+// = the token at position p, pos_row[p] = its id) and each token's gates
+// (gates[t][NP], NP = N rounded up to a power of two, at most 16), all in ws.
+hipError_t launch_group_route(const int64_t* ids, const uint16_t* h, const uint16_t* w_r, int64_t T, int D, int N,
+                              void* ws, hipStream_t s, const int** pos_tok, const int** pos_row,
+                              const float** gates);
+// combine_nf3.hip: the NF3 combine over the grouped positions of
+// launch_group_route (bf16 h, N <= 16, D % 64 == 0).
+hipError_t launch_lookup_combine_nf3_grouped(const int* pos_tok, const int* pos_row, const float* gates,
+                                             const uint8_t* codes, const uint16_t* scales, float* y, int64_t T,
+                                             int64_t D, int64_t N, hipStream_t s);
 // The same with the workspace in the library's static device array (T up to
 // kGroupedNoAllocMaxT; no allocation).
 constexpr int64_t kGroupedNoAllocMaxT = 65536;

@@ -43,14 +43,15 @@ def test_header_declares_the_hot_path():
                "mole_lookup_combine_grouped_workspace_size", "mole_check_ids", "mole_release_host_state",
                "mole_nf3_midpoints", "mole_nf4_midpoints", "mole_gelu_phi_coefficients",
                "mole_lookup_combine_nf3_mapped", "mole_lookup_combine_mapped",
-               "mole_lookup_combine_grouped_mapped"):
+               "mole_lookup_combine_grouped_mapped", "mole_lookup_combine_nf3_grouped",
+               "mole_lookup_combine_nf3_grouped_mapped"):
         assert fn in names
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mole_abi_version() == 11
+    assert lib.mole_abi_version() == 12
 
 
 def test_status_strings(lib):

@@ -482,6 +482,57 @@ def test_grouped_combine_mapped_host_table(V, N, D, T, law):
     assert combine_rel_err(host(y), oracle.lookup_combine(ids, h, w_r, lut)) <= COMBINE_TOL
 
 
+@pytest.mark.parametrize("V,N,D,T,law", [(300, 16, 1024, 4096, "zipf"), (300, 4, 768, 300, "uniform"),
+                                         (100, 1, 128, 17, "uniform"), (20, 8, 64, 5000, "one"),
+                                         (100, 16, 4096, 1024, "zipf"), (50, 3, 192, 2000, "zipf")])
+def test_nf3_grouped_combine_matches_oracle(V, N, D, T, law):
+    """NF3 combine over the batch grouped by id on the device (ragged T, N
+    padded to a power of two, rows of one to 128 chunks with two chunk rounds
+    at D = 4096, a single id for 5000 tokens), against the oracle and the
+    per-token NF3 combine."""
+    seed = 6000 + V + N + D + T
+    table = rand_table(seed, V, N, D, "bf16")
+    codes, scales, _ = oracle.pack_nf3(table)
+    h, w_r = rand_hw(seed + 1, T, N, D, "bf16", wstd=0.3)
+    ids = grouped_ids(rng(seed + 2), V, T, law)
+    y = torch.full((T, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((max(mole.mole_lookup_combine_grouped_workspace_size(T), 16),), 0xAB, dtype=torch.uint8,
+                    device="cuda")
+    mole.mole_lookup_combine_nf3_grouped(dev(ids), dev(h), dev(w_r), dev(codes), dev(scales.view(np.int16)), y, ws)
+    torch.cuda.synchronize()
+    yh = host(y)
+    assert np.all(np.isfinite(yh))
+    assert combine_rel_err(yh, oracle.lookup_combine_nf3(ids, h, w_r, codes, scales)) <= COMBINE_TOL
+    assert combine_rel_err(yh, run_nf3(ids, h, w_r, codes, scales).astype(np.float64)) <= COMBINE_TOL
+
+
+@pytest.mark.parametrize("T", [1024, 4096])
+def test_nf3_grouped_combine_mapped_host_table(T):
+    """The grouped NF3 combine with its 410M-class table in page-locked host
+    memory, read in place: bit for bit the device-resident grouped NF3
+    combine (same gates, same kernel), and within the oracle's bar."""
+    w = synth.WORKLOADS["410m-nf3"]
+    V, N, D = w.V, w.N, w.D
+    ids = synth.make_ids(w, T, step=7)
+    table = rand_table(94, V, N, D, "bf16", std=0.02, rows=np.unique(ids))
+    codes, scales, _ = oracle.pack_nf3(table)
+    h = synth.make_hidden(w, T, step=7)
+    w_r = synth.make_router(w)
+    ws = torch.empty(mole.mole_lookup_combine_grouped_workspace_size(T), dtype=torch.uint8, device="cuda")
+    y_dev = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    mole.mole_lookup_combine_nf3_grouped(dev(ids), dev(h), dev(w_r), dev(codes), dev(scales.view(np.int16)), y_dev,
+                                         ws)
+    codes_h = torch.from_numpy(codes).pin_memory()
+    scales_h = torch.from_numpy(scales.view(np.int16)).pin_memory()
+    y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        y.fill_(float("nan"))
+        mole.mole_lookup_combine_nf3_grouped_mapped(dev(ids), dev(h), dev(w_r), codes_h, scales_h, y, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), host(y_dev))
+    assert combine_rel_err(host(y), oracle.lookup_combine_nf3(ids, h, w_r, codes, scales)) <= COMBINE_TOL
+
+
 def test_combine_nf3_mapped_refuses_unmapped_tables():
     """Pageable host memory and device memory are refused on the host before
     anything is enqueued (a kernel reading pageable memory would fault)."""
