@@ -333,10 +333,8 @@ def model_q(fmt, T, V, D, N, esz, ids):
 # grouped combine (combine_grouped.hip)
 # ----------------------------------------------------------------------------
 
-def model_grouped(T, V, D, N, ids):
-    NP = next_pow2(N)
-    buf = Buffers(ids=8 * T, h=T * D * 2, w_r=N * D * 2, lut=V * N * D * 2, y=T * D * 4,
-                  pos=4 * T, gates=T * 16 * 4)
+def group_route_accesses(buf, T, D, N, NP):
+    """The grouping and routing launch (group_route_kernel)."""
     # grouping workgroups: one per 4096-token chunk, 1024 threads, 4 tokens each
     nchunks = (T + 4095) // 4096
     b, tid = lanes(nchunks, 1024)
@@ -352,6 +350,13 @@ def model_grouped(T, V, D, N, ids):
     mfma_router_loads(buf, b, tid, b * 16, T, 16, D, N, NP, 16)
     gi = b * 16 * NP + tid
     buf.access("gates", (gi * 4)[(tid < 16 * NP) & (b * 16 + tid // NP < T)], 4)
+
+
+def model_grouped(T, V, D, N, ids):
+    NP = next_pow2(N)
+    buf = Buffers(ids=8 * T, h=T * D * 2, w_r=N * D * 2, lut=V * N * D * 2, y=T * D * 4,
+                  pos=4 * T, gates=T * 16 * 4)
+    group_route_accesses(buf, T, D, N, NP)
     # combine: one workgroup per position; positions hold a permutation of the tokens
     order = np.argsort(ids, kind="stable")
     rows = ids[order]
@@ -385,6 +390,49 @@ def model_grouped(T, V, D, N, ids):
                 break
             buf.access("y", ((tok * D + c * 8) * 4)[mc], 32)
             c = c + lanes_n
+    return buf
+
+
+def model_nf3_grouped(T, V, D, N, ids):
+    """The NF3 combine over the grouped positions (lookup_combine_nf3_grouped_kernel):
+    one position per wavefront, four per workgroup; lane (s, c) decodes chunk
+    c (+ CP per round) of experts s, s + S, ...; loads guarded by c < C and
+    e < N, gates at gates[token][NP], staged 16-byte stores of the row."""
+    NP = next_pow2(N)
+    rb, sb = 3 * D // 8, D // 64
+    buf = Buffers(ids=8 * T, h=T * D * 2, w_r=N * D * 2, codes=V * N * rb, scales=V * N * sb * 2, y=T * D * 4,
+                  pos=4 * T, gates=T * 16 * 4)
+    group_route_accesses(buf, T, D, N, NP)
+    C = D // 32
+    CP = pick_group(C, 8, 64)
+    while CP * NP < 64:
+        CP *= 2
+    S = 64 // CP
+    EPL = (NP + S - 1) // S
+    order = np.argsort(ids, kind="stable")
+    b, tid = lanes((T + 3) // 4, 256)
+    p = b * 4 + tid // 64
+    lane = tid % 64
+    live = p < T
+    pc = np.minimum(p, T - 1)
+    buf.access("pos", (pc * 4)[live], 4)
+    tok, row = order[pc], ids[order[pc]]
+    sp, ch = lane // CP, lane % CP
+    for j in range(EPL):
+        e = j * S + sp
+        buf.access("gates", ((tok * NP + e) * 4)[live & (e < N)], 4)
+    rounds = (C + CP - 1) // CP
+    for k in range(rounds):
+        c = k * CP + ch
+        act = live & (c < C)
+        for j in range(EPL):
+            e = j * S + sp
+            m = act & (e < N)
+            buf.access("codes", (row * N * rb + e * rb + c * 12)[m], 12)
+            buf.access("scales", ((row * N * sb + e * sb + (c >> 1)) * 2)[m], 2)
+        for q in range(max(CP * 32 // 256, 1)):
+            el = k * CP * 32 + 4 * lane + 256 * q
+            buf.access("y", ((tok * D + el) * 4)[live & (el < D)], 16)
     return buf
 
 
@@ -437,6 +485,15 @@ def test_grouped_combine_loads_stay_in_bounds():
         for D in (8, 64, 136, 1024, 2048, 4096):
             for T in (1, 16, 17, 300, 4097):
                 buf = model_grouped(T, V, D, N, ids_for(T, V, N + D + T))
+                assert not buf.bad, (N, D, T, buf.bad[:3])
+
+
+def test_nf3_grouped_combine_loads_stay_in_bounds():
+    V = 50
+    for N in (1, 2, 3, 4, 8, 16):
+        for D in (64, 192, 1024, 2048, 4096):
+            for T in (1, 5, 17, 300, 4097):
+                buf = model_nf3_grouped(T, V, D, N, ids_for(T, V, N + D + T))
                 assert not buf.bad, (N, D, T, buf.bad[:3])
 
 
