@@ -479,14 +479,21 @@ hipError_t launch_lookup_combine_nf3_grouped(const int* pos_tok, const int* pos_
 // ---------------------------------------------------------------------------
 // Host-side dispatch
 // ---------------------------------------------------------------------------
-// Tokens (wavefronts) per workgroup of the wide launch: 8 from T = 4096 on
-// (each workgroup streams W_r's K share once for twice as many tokens: 512
-// workgroups read 16 MB of W_r from L2 instead of 32 MB at T = 4096), 4
-// below (8 would leave half the compute units idle at T = 1024).  Measured
-// on the 410M-class NF3 table: T = 4096 distinct 15.0 -> 14.2 us, Zipf
-// 14.6 -> 13.1 us, T = 16384 distinct 48.3 -> 44.0 us; T = 1024 distinct
-// 7.9 us with 4 tokens, 8.5 us with 8.
-constexpr int64_t kQuantEightTokMinT = 4096;
+// Tokens (wavefronts) per workgroup of the wide launch: 8 where that needs
+// no more token slots per compute unit than 4 -- ceil(workgroups / 256 CUs)
+// rounds of 8 against rounds of 4 -- else 4.  With 8, each workgroup
+// streams W_r's K share once for twice as many tokens (at T = 4096, 16 MB
+// of W_r through L2 instead of 32 MB); with 4, a batch that does not fill
+// whole rounds of 8-token workgroups leaves fewer CUs idle.  Measured on
+// the 410M-class NF3 table, 4 -> 8 tokens: T = 2048 distinct 10.1 -> 9.4
+// us, Zipf 10.1 -> 9.0 us; T = 4096 distinct 15.0 -> 14.2 us, Zipf 14.6 ->
+// 13.1 us; T = 16384 distinct 48.3 -> 44.0 us; but T = 1024 distinct 7.9 ->
+// 8.5 us (128 workgroups for 256 CUs) and T = 3072 distinct 12.5 -> 13.0 us
+// (384 workgroups: two rounds where 4 tokens take three of half the size).
+static inline int quant_wide_tokens(int64_t T) {
+  const int64_t r8 = ((T + 7) / 8 + 255) / 256, r4 = ((T + 3) / 4 + 255) / 256;
+  return 8 * r8 <= 4 * r4 ? 8 : 4;
+}
 
 template <typename TH, int NP, int CP, int FMT>
 static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes,
@@ -495,15 +502,15 @@ static hipError_t launch_nf3(const int64_t* ids, const void* h, const void* w_r,
   constexpr int G = CP * S;
   // Below T = 1024 (bf16 h, NP <= 16, full-wavefront tokens): one token per
   // workgroup with the vector-unit router, spread over W wavefronts below.
-  // From T = 1024 on, four tokens per workgroup (one per wavefront; eight
-  // from T = 4096, see kQuantEightTokMinT) with the
+  // From T = 1024 on, four tokens per workgroup (one per wavefront; or
+  // eight, see quant_wide_tokens) with the
   // matrix-core router, whose operands go out before the code loads; on the
   // 410M-class table with distinct ids, against the one-token shapes: T =
   // 1024 NF3 9.26 -> 8.51 us, NF4 9.83 -> 9.01 us, int8 10.2 -> 8.3 us;
   // T = 4096 int8 26.4 -> 23.3 us.
   const bool full_wave = G == kWave && sizeof(TH) == 2 && NP <= 16;
   const bool one_token = full_wave && T < 1024;
-  const int tpb = one_token ? 1 : (full_wave ? (T >= kQuantEightTokMinT ? 8 : 4) : pick_tokens_per_block(T, G));
+  const int tpb = one_token ? 1 : (full_wave ? quant_wide_tokens(T) : pick_tokens_per_block(T, G));
   const int64_t blocks = (T + tpb - 1) / tpb;
   // (No staged-router launch here: the extra launch measured slower --
   // 410M-class NF3 table, T=4096: 20.1 -> 22.6 us.)

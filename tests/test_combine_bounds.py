@@ -237,8 +237,10 @@ def q_plan(fmt, T, D, N, esz):
     bf = esz == BF16
     full_wave = G == WAVE and bf and NP <= 16
     one_token = full_wave and T < 1024
-    # four tokens per workgroup of full wavefronts, eight from T = 4096
-    tpb = 1 if one_token else ((8 if T >= 4096 else 4) if full_wave else pick_tokens_per_block(T, G))
+    # four or eight tokens per workgroup of full wavefronts (eight where that
+    # takes no more rounds of token slots over the 256 compute units)
+    r8, r4 = ((T + 7) // 8 + 255) // 256, ((T + 3) // 4 + 255) // 256
+    tpb = 1 if one_token else ((8 if 8 * r8 <= 4 * r4 else 4) if full_wave else pick_tokens_per_block(T, G))
     W = 1
     if bf and NP <= 16 and tpb == 1 and G == WAVE:
         while W < 4 and 2 * W * S <= NP and T * 2 * W <= 2 * 1024:
@@ -469,11 +471,11 @@ def test_quantised_combine_loads_stay_in_bounds(fmt):
     V = 41
     for N in NS:
         for D in (64, 192, 1024, 2048, 4096):
-            for T in (1, 17, 1023, 1024, 1025, 2049, 4097):
+            for T in (1, 17, 1023, 1024, 1025, 2047, 2049, 4097):
                 for esz in (BF16, F32):
                     if esz == F32 and T > 17:
                         continue
-                    if T == 4097 and (D > 1024 or N not in (4, 12, 16)):
+                    if T in (2047, 4097) and (D > 1024 or N not in (4, 12, 16)):
                         continue  # the eight-token launch: a few shapes keep the CPU model quick
                     p, buf = model_q(fmt, T, V, D, N, esz, ids_for(T, V, N + D + T))
                     assert not buf.bad, (fmt, N, D, T, esz, p, buf.bad[:3])

@@ -262,9 +262,10 @@ def run_nf3(ids, h, w_r, codes, scales):
                                            (100, 16, 4096, 1024, "bf16"),  # two chunk rounds per lane
                                            # four wavefronts per token, some without an expert in a round
                                            (300, 12, 1024, 100, "bf16"),
-                                           # the streaming launch: several quads per workgroup, a
-                                           # ragged last quad, rows of 24 chunks in 32-lane groups
-                                           (300, 16, 1024, 9001, "bf16"), (300, 4, 768, 5003, "bf16")])
+                                           # large batches: four and eight tokens per workgroup with
+                                           # ragged last workgroups, rows of 24 chunks in 32-lane groups
+                                           (300, 16, 1024, 9001, "bf16"), (300, 4, 768, 5003, "bf16"),
+                                           (300, 12, 1024, 2047, "bf16"), (300, 16, 768, 4095, "bf16")])
 def test_combine_nf3_matches_oracle(V, N, D, T, dtype):
     seed = 2000 + V + N + D
     table = rand_table(seed, V, N, D, "bf16")
@@ -1041,7 +1042,8 @@ def test_pack_int8_edge_cases_bit_exact():
                                            (100, 64, 512, 2048, "bf16"), (300, 12, 1024, 100, "bf16"),
                                            (300, 16, 1024, 1023, "bf16"), (300, 16, 1024, 1024, "bf16"),
                                            (300, 12, 2048, 1027, "bf16"), (100, 16, 4096, 1024, "bf16"),
-                                           (300, 16, 1024, 9001, "bf16"), (300, 4, 768, 5003, "bf16")])
+                                           (300, 16, 1024, 9001, "bf16"), (300, 4, 768, 5003, "bf16"),
+                                           (300, 12, 1024, 2047, "bf16")])
 def test_combine_q_matches_oracle(fmt, V, N, D, T, dtype):
     seed = 3000 + V + N + D
     table = rand_table(seed, V, N, D, "bf16")
