@@ -630,6 +630,39 @@ def test_grouped_combine_argument_errors(lib):
     assert call(ws=ctypes.c_void_p(24)) == ALIGN
 
 
+def test_grouped_variant_argument_errors(lib):
+    """The grouped read-in-place and grouped NF3 entry points validate like
+    the grouped combine before any HIP call (the host-table checks, which
+    query the runtime, come only after these)."""
+    dummy = ctypes.c_void_p(16)
+    need = mole.mole_lookup_combine_grouped_workspace_size(8)
+
+    def gm(T=8, V=100, D=64, N=4, dtype=_native.MOLE_BF16, ptr=dummy, ws=dummy, ws_bytes=need):
+        return lib.mole_lookup_combine_grouped_mapped(ptr, ptr, ptr, ptr, ptr, T, V, D, N, dtype, ws, ws_bytes, None)
+
+    assert gm(dtype=7) == DTYPE
+    assert gm(dtype=_native.MOLE_F32) == UNSUP
+    assert gm(N=17) == UNSUP
+    assert gm(T=0) == OK
+    assert gm(ptr=None) == NULL
+    assert gm(ws=None) == NULL
+    assert gm(ws_bytes=need - 1) == WS
+    for fn in (lib.mole_lookup_combine_nf3_grouped, lib.mole_lookup_combine_nf3_grouped_mapped):
+        def ng(T=8, V=100, D=128, N=4, dtype=_native.MOLE_BF16, ptr=dummy, ws=dummy, ws_bytes=need):
+            return fn(ptr, ptr, ptr, ptr, ptr, ptr, T, V, D, N, dtype, ws, ws_bytes, None)
+
+        assert ng(dtype=7) == DTYPE
+        assert ng(D=96) == DIM               # D % 64
+        assert ng(dtype=_native.MOLE_F32) == UNSUP
+        assert ng(N=17) == UNSUP
+        assert ng(V=2 ** 31) == UNSUP
+        assert ng(T=0) == OK
+        assert ng(ptr=None) == NULL
+        assert ng(ws=None) == NULL
+        assert ng(ws_bytes=need - 1) == WS
+        assert ng(ws=ctypes.c_void_p(24)) == ALIGN
+
+
 def test_grouped_workspace_size():
     """Three sections, each padded to 256 bytes: the grouped token and its
     row (int32 [T] each) and the gates (fp32 [T][16])."""
