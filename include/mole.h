@@ -390,12 +390,13 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
  * call is one launch -- no host-side dedupe or gather, no staging area, no
  * wait on the host.  ids (int64 [T]), h, w_r and y are device memory as for
  * mole_lookup_combine_nf3; codes_host [V][N][3D/8] and scales_host
- * [V][N][D/64] must lie in page-locked host memory allocated through HIP
- * (hipHostMalloc, or a pinned tensor of the framework) and must not be
- * written while a call that reads them is in flight.  Both ranges are
- * checked with the runtime's pointer attributes before anything is
- * enqueued: pageable or unknown memory returns MOLE_ERR_MEMORY (a kernel
- * reading it would fault).  Every token reads its own rows, so repeated
+ * [V][N][D/64] must each lie inside one page-locked host allocation made
+ * through HIP (hipHostMalloc, or a pinned tensor of the framework) and must
+ * not be written while a call that reads them is in flight.  Both ranges
+ * are checked with the runtime's pointer attributes before anything is
+ * enqueued: pageable or unknown memory, or a range that runs past the end
+ * of the allocation holding its first byte, returns MOLE_ERR_MEMORY (a
+ * kernel reading it would fault).  Every token reads its own rows, so repeated
  * ids cross PCIe again unless the GPU's caches still hold them; for large
  * batches with repeated ids mole_lookup_combine_nf3_host (one copy of the
  * distinct rows) moves fewer bytes.  Asynchronous on `stream`; capturable

@@ -481,7 +481,11 @@ int mole_lookup_combine_nf3(const int64_t* ids, const void* h, const void* w_r, 
 // The device address of the host range [p, p + bytes) if all of it lies in
 // one page-locked host allocation that the device can read, else null.  (A
 // failed query leaves an error behind in the runtime's last-error slot; it is
-// cleared so that the caller's next error check does not see it.)
+// cleared so that the caller's next error check does not see it.)  Both ends
+// being mapped is not enough: a page-locked allocation's device address
+// equals its host address, so a range whose ends fall in two allocations
+// passes the end-to-end test with unmapped memory between them.  The range
+// must also fit inside the allocation that holds its first byte.
 static const char* mapped_host_range(const void* p, size_t bytes) {
   const char* first = static_cast<const char*>(p);
   const char* last = first + bytes - 1;
@@ -498,7 +502,19 @@ static const char* mapped_host_range(const void* p, size_t bytes) {
     // itself; the offset from its host address covers both)
     dev[i] = static_cast<const char*>(a.devicePointer) + (q[i] - static_cast<const char*>(a.hostPointer));
   }
-  return dev[1] - dev[0] == (ptrdiff_t)(bytes - 1) ? dev[0] : nullptr;
+  if (dev[1] - dev[0] != (ptrdiff_t)(bytes - 1)) return nullptr;
+  void* start = nullptr;
+  size_t size = 0;
+  void* q0 = const_cast<char*>(first);
+  if (hipPointerGetAttribute(&start, HIP_POINTER_ATTRIBUTE_RANGE_START_ADDR, q0) != hipSuccess ||
+      hipPointerGetAttribute(&size, HIP_POINTER_ATTRIBUTE_RANGE_SIZE, q0) != hipSuccess || !start) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  // (the start may come back as the allocation's host or device address)
+  const char* s0 = static_cast<const char*>(start);
+  auto fits = [&](const char* a) { return a >= s0 && (size_t)(a - s0) <= size && size - (size_t)(a - s0) >= bytes; };
+  return fits(first) || fits(dev[0]) ? dev[0] : nullptr;
 }
 
 int mole_lookup_combine_nf3_mapped(const int64_t* ids, const void* h, const void* w_r, const uint8_t* codes_host,

@@ -562,6 +562,48 @@ def test_combine_nf3_mapped_refuses_unmapped_tables():
     assert bool(torch.isfinite(y).all())
 
 
+def test_mapped_combines_refuse_a_range_across_two_allocations():
+    """A table range whose first byte lies in one page-locked allocation and
+    whose last byte lies in another (both ends mapped, the memory between them
+    not necessarily) is refused.  The ids touch only rows inside the first
+    allocation, so no read could leave it even if a call went through."""
+    T = 8
+    a = torch.zeros(1 << 20, dtype=torch.uint8).pin_memory()
+    b = torch.zeros(1 << 20, dtype=torch.uint8).pin_memory()
+    lo, hi = (a, b) if a.data_ptr() < b.data_ptr() else (b, a)
+    gap = hi.data_ptr() + 4096 - lo.data_ptr()      # from lo's first byte to a byte inside hi
+    ids = dev(np.arange(T, dtype=np.int64))
+    lib = mole.library()
+    for fmt in ("nf3", "bf16"):
+        D, N = 64, 1
+        row = N * (3 * D // 8) if fmt == "nf3" else N * D * 2
+        V = gap // row + 1                             # the range's last byte: 4096 .. 4096 + row - 1 into hi
+        if V * 2 > (1 << 30):
+            pytest.skip("the two allocations lie too far apart for a scale table of this size")
+        last = lo.data_ptr() + V * row - 1
+        assert hi.data_ptr() <= last < hi.data_ptr() + hi.numel()
+        h = torch.zeros((T, D), dtype=torch.bfloat16, device="cuda")
+        w_r = torch.zeros((N, D), dtype=torch.bfloat16, device="cuda")
+        y = torch.zeros((T, D), dtype=torch.float32, device="cuda")
+        if fmt == "nf3":
+            scales = torch.zeros((V, N, D // 64), dtype=torch.int16).pin_memory()
+            rc = lib.mole_lookup_combine_nf3_mapped(ids.data_ptr(), h.data_ptr(), w_r.data_ptr(), lo.data_ptr(),
+                                                    scales.data_ptr(), y.data_ptr(), T, V, D, N, 1, None)
+        else:
+            rc = lib.mole_lookup_combine_mapped(ids.data_ptr(), h.data_ptr(), w_r.data_ptr(), lo.data_ptr(),
+                                                y.data_ptr(), T, V, D, N, 1, None)
+        assert rc == -12, (fmt, rc)
+    torch.cuda.synchronize()
+    # the same first allocation with a range inside it goes through
+    V = lo.numel() // (3 * 64 // 8)
+    scales = torch.zeros((V, 1, 1), dtype=torch.int16).pin_memory()
+    y = torch.full((T, 64), float("nan"), dtype=torch.float32, device="cuda")
+    rc = lib.mole_lookup_combine_nf3_mapped(ids.data_ptr(), h.data_ptr(), w_r.data_ptr(), lo.data_ptr(),
+                                            scales.data_ptr(), y.data_ptr(), T, V, 64, 1, 1, None)
+    torch.cuda.synchronize()
+    assert rc == 0 and bool((y == 0).all())
+
+
 @pytest.mark.parametrize("T", [1, 256, 2048])
 def test_combine_nf3_from_table_file(T, tmp_path):
     """Table in a file (the disk tier); only the distinct requested rows are
