@@ -396,7 +396,8 @@ int mole_lookup_combine_nf3_host(const int64_t* ids_host, const void* h, const v
  * are checked with the runtime's pointer attributes before anything is
  * enqueued: pageable or unknown memory, or a range that runs past the end
  * of the allocation holding its first byte, returns MOLE_ERR_MEMORY (a
- * kernel reading it would fault).  Every token reads its own rows, so repeated
+ * kernel reading it would fault); a V whose table byte count overflows
+ * int64 returns MOLE_ERR_DIM.  Every token reads its own rows, so repeated
  * ids cross PCIe again unless the GPU's caches still hold them; for large
  * batches with repeated ids mole_lookup_combine_nf3_host (one copy of the
  * distinct rows) moves fewer bytes.  Asynchronous on `stream`; capturable

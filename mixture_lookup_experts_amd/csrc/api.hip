@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cerrno>
 #include <condition_variable>
+#include <cstdint>
 #include <cstring>
 #include <functional>
 #include <mutex>
@@ -529,6 +530,7 @@ int mole_lookup_combine_nf3_mapped(const int64_t* ids, const void* h, const void
   if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(codes_host) || !aligned16(scales_host) ||
       !aligned16(y))
     return MOLE_ERR_ALIGN;
+  if (V > INT64_MAX / (4 * N * D)) return MOLE_ERR_DIM;  // (the table's byte count must not wrap)
   const char* codes_d = mapped_host_range(codes_host, (size_t)(V * N * (3 * D / 8)));
   const char* scales_d = mapped_host_range(scales_host, (size_t)(V * N * (D / 64)) * 2);
   if (!codes_d || !scales_d) return MOLE_ERR_MEMORY;
@@ -547,6 +549,7 @@ int mole_lookup_combine_mapped(const int64_t* ids, const void* h, const void* w_
   if (!aligned8(ids) || !aligned16(h) || !aligned16(w_r) || !aligned16(lut_host) || !aligned16(y))
     return MOLE_ERR_ALIGN;
   const size_t esz = dtype == MOLE_F32 ? 4 : 2;
+  if (V > INT64_MAX / (4 * N * D)) return MOLE_ERR_DIM;  // (the table's byte count must not wrap)
   const char* lut_d = mapped_host_range(lut_host, (size_t)(V * N * D) * esz);
   if (!lut_d) return MOLE_ERR_MEMORY;
   return hip_status(mole::launch_lookup_combine(ids, h, w_r, lut_d, y, T, D, N, dtype, true, as_stream(stream)));

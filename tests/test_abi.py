@@ -236,6 +236,10 @@ def test_mapped_nf3_argument_errors(lib):
     assert f(P(a), P(a), P(a), P(a + 8), P(a), 4, 10, 64, 4, 1, None) == ALIGN
     assert f(P(a), P(a), P(a), P(a), P(a), 4, 10, 64, 65, 1, None) == UNSUP
     assert f(None, None, None, None, None, 0, 10, 64, 4, 1, None) == OK
+    # a vocabulary whose table byte count would wrap around int64
+    huge = 2 ** 62
+    assert g(P(a), P(a), P(a), P(a), P(a), P(a), 4, huge, 128, 4, 1, None) == DIM
+    assert f(P(a), P(a), P(a), P(a), P(a), 4, huge, 64, 4, 1, None) == DIM
 
 
 def test_host_staging_size_and_errors(lib):
