@@ -54,6 +54,21 @@ def test_library_exports_every_declared_symbol(lib):
     assert lib.mole_abi_version() == 12
 
 
+def test_every_exported_function_is_declared():
+    """The reverse of the export check: the library exports no mole_*
+    function that include/mole.h does not declare (nm over the built
+    library's dynamic symbol table)."""
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm is not installed")
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {f[2] for f in (line.split() for line in out.splitlines())
+                if len(f) == 3 and f[1] == "T" and f[2].startswith("mole_")}
+    assert exported == set(declared_functions())
+
+
 def test_status_strings(lib):
     for code in (OK, NULL, DIM, DTYPE, ALIGN, WS, UNSUP, HIP, BADID, IO, FORMAT, HOST, MEMORY):
         assert mole.mole_status_string(code) not in ("", "unknown status")
